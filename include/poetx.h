@@ -1,0 +1,165 @@
+/*
+ * libpoetx: the POET-X orthogonal-equivalence linear layer y = R W0 P x on
+ * AMD Instinct MI355X (gfx950), as hand-written HIP kernels behind a C ABI.
+ *
+ * Citations
+ *   [PX]   page "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
+ *          Transformation" (gist.science, French), section "Résumé technique".
+ *   [Pion] page "Pion：保持谱稳定的大语言模型训练优化器", section "数学原理".
+ *
+ * Mathematical conventions (shared with any independent checker)
+ *   Activations are row-major [T, features]. One token maps as y = R W0 P x,
+ *   i.e. Y = X P^T W0^T R^T for the whole batch.
+ *   P = Pi_P^T D_P Pi_P and R = Pi_R^T D_R Pi_R, where (Pi v)_i = v[pi[i]] and
+ *   D = blockdiag(Q_1, Q_2, ...) over contiguous blocks ([PX] §2.B, §2.C).
+ *   Each block Q = (I + S) * sum_{j=0..k} S^j: the Cayley transform
+ *   (I+S)(I-S)^{-1} with the inverse truncated to its Neumann series ([PX]
+ *   §2.D). S is skew; only its strict upper triangle is stored, row-major,
+ *   S[i][j] = theta, S[j][i] = -theta (b(b-1)/2 floats per block, [PX] §2.D),
+ *   blocks concatenated in order.
+ *   The weight is pre-merged with both permutations once per inner loop
+ *   ([PX] §2.B): Wt[i][j] = W0[pi_R[i]][pi_P[j]].
+ *
+ * Memory and threading
+ *   Every buffer is owned by the caller. Pointers marked "device" must be
+ *   device memory (e.g. from hipMalloc / torch); "host" arrays are read during
+ *   the call only. The library allocates no device memory: each call that needs
+ *   scratch takes a caller-provided workspace of poetx_workspace_size() bytes.
+ *   Calls are asynchronous on the given stream and never synchronise the host.
+ *   A plan is immutable after creation and may be shared by threads as long as
+ *   every concurrent call has its own workspace.
+ *
+ * Errors
+ *   Every call returns a poetx_status and never aborts. Arguments are checked on
+ *   the host before any launch; nothing is launched on error. Device pointers
+ *   must be 16-byte aligned. Permutation arrays must hold permutations; this is
+ *   the caller's guarantee and is not checked on the device.
+ */
+#ifndef POETX_H
+#define POETX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  POETX_OK = 0,
+  POETX_ERR_INVALID_ARG = 1,  /* NULL pointer, negative size, bad enum       */
+  POETX_ERR_SHAPE = 2,        /* block sizes do not sum to m or n, k range    */
+  POETX_ERR_DTYPE = 3,        /* unknown dtype                                */
+  POETX_ERR_ALIGNMENT = 4,    /* a device pointer is not 16-byte aligned      */
+  POETX_ERR_UNSUPPORTED = 5,  /* valid but not handled (see poetx_plan_create) */
+  POETX_ERR_HIP = 6,          /* a kernel launch failed                       */
+  POETX_ERR_WORKSPACE = 7     /* workspace NULL or smaller than required      */
+} poetx_status;
+
+typedef enum { POETX_FP32 = 0, POETX_BF16 = 1 } poetx_dtype;
+typedef enum { POETX_SIDE_R = 0, POETX_SIDE_P = 1 } poetx_side;
+typedef enum { POETX_WS_BUILD = 0, POETX_WS_FORWARD = 1, POETX_WS_BACKWARD = 2 } poetx_ws_kind;
+
+typedef struct poetx_plan poetx_plan;   /* opaque, immutable after create */
+
+typedef struct {
+  int32_t m, n;             /* W0 is [m, n] row-major (out x in)                   */
+  int32_t nb_R, nb_P;       /* number of blocks of R and of P                       */
+  const int32_t* bsz_R;     /* host, nb_R block sizes, summing to m                  */
+  const int32_t* bsz_P;     /* host, nb_P block sizes, summing to n                  */
+  int32_t k;                /* Neumann order, 0 <= k <= 32: powers S^0..S^k          */
+  int32_t dtype;            /* poetx_dtype of X, Y, W0, Wt, Q copies and gradients
+                               of X/Y. Skew parameters and their gradients are
+                               always fp32; accumulation is always fp32.            */
+} poetx_desc;
+
+/* Create a plan. Host only: no device call is made, so it works without a GPU.
+ * POETX_ERR_SHAPE: m or n < 1, a block size < 1, sums differ from m / n, or
+ *   k outside [0, 32].
+ * POETX_ERR_UNSUPPORTED: dtype BF16 with m, n or a block size not a multiple of
+ *   16 (fp32 plans take any sizes). */
+poetx_status poetx_plan_create(const poetx_desc* desc, poetx_plan** out);
+void poetx_plan_destroy(poetx_plan* plan);
+
+/* Number of packed skew parameters of one side: sum_i b_i (b_i - 1) / 2. */
+int64_t poetx_param_count(const poetx_plan* plan, int32_t side);
+/* Number of elements of one side's block array: sum_i b_i^2. */
+int64_t poetx_block_elems(const poetx_plan* plan, int32_t side);
+
+/* Workspace bytes needed by a call of the given kind for T tokens (T is
+ * ignored for POETX_WS_BUILD). Returns 0 for an invalid plan or kind. */
+size_t poetx_workspace_size(const poetx_plan* plan, int64_t T, int32_t kind);
+
+/* Short static description of a status code. */
+const char* poetx_status_string(poetx_status status);
+
+/* Pre-merge of the permutations into the frozen weight, once per inner loop
+ * ([PX] §2.B "Réduction": permutations folded into W ahead of time, leaving
+ * two index operations per step): Wt[i][j] = W0[pi_R[i]][pi_P[j]].
+ *   W0   device [m, n] (dtype)        pi_R device int32 [m]
+ *   pi_P device int32 [n]             Wt   device [m, n] (dtype), not aliasing W0
+ * Bit-exact copy. */
+poetx_status poetx_permute_weight(const poetx_plan* plan, const void* W0,
+                                  const int32_t* pi_R, const int32_t* pi_P,
+                                  void* Wt, void* stream);
+
+/* Cayley-Neumann blocks from packed skew parameters ([PX] §2.D).
+ *   theta  device fp32 [poetx_param_count(side)]
+ *   Q_f32  device fp32 [poetx_block_elems(side)]: block i row-major at offset
+ *          sum_{j<i} b_j^2; Q = I + sum_{j=1..k+1} c_j S^j, c_j = 2 for j <= k
+ *          and c_{k+1} = 1 (c_1 = 1 when k = 0)
+ *   Q_act  device [poetx_block_elems(side)] in the plan dtype (round to nearest
+ *          even for BF16), or NULL. FP32 plans may pass NULL and use Q_f32.
+ *   ws     device, poetx_workspace_size(plan, 0, POETX_WS_BUILD) bytes. */
+poetx_status poetx_build_orth(const poetx_plan* plan, int32_t side, const float* theta,
+                              float* Q_f32, void* Q_act, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Input-centric forward ([PX] §2.A): Y = R W0 P applied to the rows of X without
+ * forming R W0 P. Stages: gather X by pi_P, blocks of P, product with Wt,
+ * blocks of R, scatter by pi_R.
+ *   X        device [T, n] (dtype)       Wt  device [m, n] from poetx_permute_weight
+ *   pi_R, pi_P device int32              Q_R, Q_P device block arrays in the plan dtype
+ *   Y        device [T, m] (dtype)
+ *   Wa_saved device [T, m] (dtype) or NULL: the output of the Wt product, the
+ *            one extra activation kept for the backward (POET-Xfast, [PX] §2.E)
+ *   ws       device, poetx_workspace_size(plan, T, POETX_WS_FORWARD) bytes.
+ * T = 0 is a no-op. */
+poetx_status poetx_forward(const poetx_plan* plan, int64_t T, const void* X, const void* Wt,
+                           const int32_t* pi_R, const int32_t* pi_P,
+                           const void* Q_R, const void* Q_P,
+                           void* Y, void* Wa_saved, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of L = <G_Y, Y> w.r.t. X and both sides' skew parameters, for the
+ * truncated Q the forward used. W0 is frozen and gets no gradient.
+ *   X, Wt, pi_R, pi_P, Q_R, Q_P as in poetx_forward
+ *   theta_R, theta_P device fp32 packed parameters (rebuild S for the chain rule)
+ *   Wa_saved device [T, m] from poetx_forward (must not be NULL)
+ *   G_Y      device [T, m] (dtype)      G_X device [T, n] (dtype)
+ *   g_theta_R, g_theta_P device fp32 [param_count] (overwritten)
+ *   ws       device, poetx_workspace_size(plan, T, POETX_WS_BACKWARD) bytes.
+ * Deterministic: all reductions run in a fixed order. T = 0 writes zero
+ * parameter gradients. */
+poetx_status poetx_backward(const poetx_plan* plan, int64_t T, const void* X, const void* Wt,
+                            const int32_t* pi_R, const int32_t* pi_P,
+                            const float* theta_R, const float* theta_P,
+                            const void* Q_R, const void* Q_P, const void* Wa_saved,
+                            const void* G_Y, void* G_X, float* g_theta_R, float* g_theta_P,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Single index operations, exposed for testing and for callers that apply the
+ * permutations themselves ([PX] §2.B: index mapping, no permutation matrix).
+ *   poetx_gather_cols:  out[t][i] = in[t][idx[i]]      (out = in Pi^T)
+ *   poetx_scatter_cols: out[t][idx[i]] = in[t][i]      (out = in Pi)
+ * in/out device [T, dim] row-major in the plan dtype, not aliasing; idx device
+ * int32 [dim], a permutation of 0..dim-1. Bit-exact. */
+poetx_status poetx_gather_cols(const poetx_plan* plan, int64_t T, int32_t dim, const void* in,
+                               const int32_t* idx, void* out, void* stream);
+poetx_status poetx_scatter_cols(const poetx_plan* plan, int64_t T, int32_t dim, const void* in,
+                                const int32_t* idx, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POETX_H */

@@ -43,7 +43,7 @@ __all__ = [
     "skew_from_packed", "packed_upper", "neumann_cayley", "build_orth",
     "block_offsets", "apply_blocks_T", "apply_blocks", "permute_weight",
     "forward", "forward_rows", "cnp_backward", "backward", "cnp_coefficients",
-    "rel_fro", "layer_reference",
+    "rel_fro", "layer_reference", "backward_rows", "theta_grad_block",
 ]
 
 
@@ -228,3 +228,45 @@ def layer_reference(inp, k: int, backward_pass: bool = True):
                                          QR, QP, Wa, inp.G_Y, sp.bsz_R, sp.bsz_P, k)
         out.update(G_X=G_X, g_theta_R=gR, g_theta_P=gP, dQ_R=dQR, dQ_P=dQP)
     return out
+
+
+def backward_rows(G_Y_rows, Wt, pi_R, pi_P, QR, QP, bsz_R, bsz_P) -> np.ndarray:
+    """G_X for a subset of token rows: each row of G_X depends only on the same
+    row of G_Y (the backward steps of the activation path, restricted to rows)."""
+    G_Y_rows = np.asarray(G_Y_rows, dtype=np.float64)
+    G_Z = G_Y_rows[:, np.asarray(pi_R)]
+    G_Wa = apply_blocks(G_Z, QR, bsz_R)
+    G_V = G_Wa @ np.asarray(Wt, dtype=np.float64)
+    G_U = apply_blocks(G_V, QP, bsz_P)
+    G_X = np.empty_like(G_U)
+    G_X[:, np.asarray(pi_P)] = G_U
+    return G_X
+
+
+def theta_grad_block(side, j, X, Wt, pi_R, pi_P, theta_R, theta_P, QR, QP, G_Y, bsz_R, bsz_P, k):
+    """Packed gradient of one block (side "R" or "P", block index j) over all
+    tokens, computing only the columns that block's dL/dQ needs."""
+    X = np.asarray(X, dtype=np.float64)
+    Wt = np.asarray(Wt, dtype=np.float64)
+    G_Y = np.asarray(G_Y, dtype=np.float64)
+    pi_R = np.asarray(pi_R)
+    pi_P = np.asarray(pi_P)
+    if side == "R":
+        off, b = block_offsets(bsz_R)[j], bsz_R[j]
+        U = X[:, pi_P]
+        V = apply_blocks_T(U, QP, bsz_P)
+        Wa_blk = V @ Wt[off:off + b].T                  # columns of Wa in block j
+        G_Z_blk = G_Y[:, pi_R[off:off + b]]
+        dQ = G_Z_blk.T @ Wa_blk
+        theta, bsz = theta_R, bsz_R
+    else:
+        off, b = block_offsets(bsz_P)[j], bsz_P[j]
+        G_Wa = apply_blocks(G_Y[:, pi_R], QR, bsz_R)
+        G_V_blk = G_Wa @ Wt[:, off:off + b]             # columns of G_V in block j
+        U_blk = X[:, pi_P[off:off + b]]
+        dQ = G_V_blk.T @ U_blk
+        theta, bsz = theta_P, bsz_P
+    poff = sum(bb * (bb - 1) // 2 for bb in bsz[:j])
+    S = skew_from_packed(np.asarray(theta, dtype=np.float64)[poff:poff + b * (b - 1) // 2], b)
+    Sbar = cnp_backward(dQ, S, k)
+    return packed_upper(Sbar - Sbar.T)

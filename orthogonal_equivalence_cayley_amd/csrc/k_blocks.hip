@@ -1,0 +1,150 @@
+// Elementwise kernels on the per-block arrays of the Cayley-Neumann
+// parameterisation ([PX] = page "POET-X: Memory-efficient LLM Training by
+// Scaling Orthogonal Transformation", Résumé technique §2.D): unpack of the
+// stored upper triangle into the skew generator, packing of the parameter
+// gradient, dtype casts and the fixed-order split-K reduction.
+#include "poetx_internal.h"
+
+namespace poetx {
+namespace {
+
+constexpr int kThreads = 256;
+
+inline int grid1d(long long n) {
+  long long g = (n + kThreads - 1) / kThreads;
+  const long long cap = 256LL * 32;
+  return (int)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+// Offset of (i, j), i < j, in the row-major strict upper triangle of a b x b block.
+__device__ __forceinline__ long long tri_index(int i, int j, int b) {
+  return (long long)i * b - ((long long)i * (i + 1)) / 2 + (j - i - 1);
+}
+
+__global__ __launch_bounds__(kThreads) void unpack_skew_kernel(
+    const float* __restrict__ theta, int b, int count, long long q_off, long long p_off,
+    float* __restrict__ S, float* __restrict__ Q, float c1) {
+  const long long bb = (long long)b * b;
+  const long long np = (long long)b * (b - 1) / 2;
+  const long long total = bb * count;
+  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total;
+       e += (long long)gridDim.x * kThreads) {
+    const long long g = e / bb;
+    const int r = (int)((e - g * bb) / b);
+    const int c = (int)(e - g * bb - (long long)r * b);
+    const float* th = theta + p_off + g * np;
+    float v = 0.0f;
+    if (r < c) v = th[tri_index(r, c, b)];
+    else if (r > c) v = -th[tri_index(c, r, b)];
+    S[q_off + e] = v;
+    if (Q) Q[q_off + e] = (r == c ? 1.0f : 0.0f) + c1 * v;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void pack_antisym_kernel(
+    const float* __restrict__ Sbar, int b, int count, long long q_off, long long p_off,
+    float* __restrict__ g) {
+  const long long bb = (long long)b * b;
+  const long long np = (long long)b * (b - 1) / 2;
+  const long long total = bb * count;
+  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total;
+       e += (long long)gridDim.x * kThreads) {
+    const long long blk = e / bb;
+    const int r = (int)((e - blk * bb) / b);
+    const int c = (int)(e - blk * bb - (long long)r * b);
+    if (r < c) {
+      const float* M = Sbar + q_off + blk * bb;
+      g[p_off + blk * np + tri_index(r, c, b)] = M[(long long)r * b + c] - M[(long long)c * b + r];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const float* __restrict__ in,
+                                                             __bf16* __restrict__ out, long long n) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (long long)gridDim.x * kThreads)
+    out[i] = static_cast<__bf16>(in[i]);   // round to nearest even
+}
+
+__global__ __launch_bounds__(kThreads) void copy_f32_kernel(const float* __restrict__ in,
+                                                            float* __restrict__ out, long long n) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (long long)gridDim.x * kThreads)
+    out[i] = in[i];
+}
+
+__global__ __launch_bounds__(kThreads) void scale2_kernel(const float* __restrict__ in, float c,
+                                                          float* __restrict__ o1,
+                                                          float* __restrict__ o2, long long n) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (long long)gridDim.x * kThreads) {
+    const float v = c * in[i];
+    o1[i] = v;
+    if (o2) o2[i] = v;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void sum_splits_kernel(const float* __restrict__ part,
+                                                              int nsplit, long long stride,
+                                                              long long n, float* __restrict__ out) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (long long)gridDim.x * kThreads) {
+    float acc = 0.0f;
+    for (int s = 0; s < nsplit; ++s) acc += part[s * stride + i];
+    out[i] = acc;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void zero_kernel(float* __restrict__ out, long long n) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (long long)gridDim.x * kThreads)
+    out[i] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_unpack_skew(const float* theta, const Seg& g, float* S, float* Q, float c1,
+                              hipStream_t s) {
+  const long long total = (long long)g.b * g.b * g.count;
+  hipLaunchKernelGGL(unpack_skew_kernel, dim3(grid1d(total)), dim3(kThreads), 0, s, theta, g.b,
+                     g.count, g.q_off, g.p_off, S, Q, c1);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_antisym(const float* Sbar, const Seg& g, float* gtheta, hipStream_t s) {
+  const long long total = (long long)g.b * g.b * g.count;
+  hipLaunchKernelGGL(pack_antisym_kernel, dim3(grid1d(total)), dim3(kThreads), 0, s, Sbar, g.b,
+                     g.count, g.q_off, g.p_off, gtheta);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const float* in, void* out, long long n, int to_bf16, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (to_bf16)
+    hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid1d(n)), dim3(kThreads), 0, s, in, (__bf16*)out, n);
+  else
+    hipLaunchKernelGGL(copy_f32_kernel, dim3(grid1d(n)), dim3(kThreads), 0, s, in, (float*)out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale2(const float* in, float c, float* o1, float* o2, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scale2_kernel, dim3(grid1d(n)), dim3(kThreads), 0, s, in, c, o1, o2, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_splits(const float* part, int nsplit, long long stride, long long n,
+                             float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_splits_kernel, dim3(grid1d(n)), dim3(kThreads), 0, s, part, nsplit,
+                     stride, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float* out, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3(grid1d(n)), dim3(kThreads), 0, s, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace poetx

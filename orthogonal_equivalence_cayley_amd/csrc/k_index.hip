@@ -1,0 +1,200 @@
+// Index-mapping kernels: column gather / scatter inside each activation row and
+// the one-time weight pre-merge. Permutations stay index arrays and are never
+// formed as matrices ([PX] = page "POET-X: Memory-efficient LLM Training by
+// Scaling Orthogonal Transformation", Résumé technique §2.B).
+//
+// A permutation inside a row touches the whole row at random, so each workgroup
+// stages R whole rows in LDS with coalesced 16-byte global accesses and does the
+// random part of the access pattern in LDS. Every global read and write is then
+// a full-line, coalesced transfer; the index array is read once per R rows.
+#include "poetx_internal.h"
+
+namespace poetx {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLdsBudget = 64 * 1024;   // bytes of LDS for staged rows per workgroup
+
+template <typename E, int VEC>
+struct Vec { E v[VEC]; };
+
+template <typename E, bool VECTOR>
+__global__ __launch_bounds__(kThreads) void gather_cols_kernel(
+    const E* __restrict__ in, long long in_ld, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ idx, E* __restrict__ out, long long T, int dim, int R) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* lds = reinterpret_cast<E*>(smem);
+  constexpr int VEC = 16 / sizeof(E);
+  using V = Vec<E, VEC>;
+  for (long long t0 = (long long)blockIdx.x * R; t0 < T; t0 += (long long)gridDim.x * R) {
+    const int nr = (int)((T - t0) < R ? (T - t0) : R);
+    if (VECTOR) {
+      const int cpr = dim / VEC;   // chunks per row
+      for (int c = threadIdx.x; c < nr * cpr; c += kThreads) {
+        const int r = c / cpr, q = c - r * cpr;
+        const long long src_row = rows ? (long long)rows[t0 + r] : (t0 + r);
+        const V* src = reinterpret_cast<const V*>(in + src_row * in_ld);
+        reinterpret_cast<V*>(lds + (long long)r * dim)[q] = src[q];
+      }
+      __syncthreads();
+      for (int q = threadIdx.x; q < cpr; q += kThreads) {
+        int ix[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ix[e] = idx[q * VEC + e];
+        for (int r = 0; r < nr; ++r) {
+          V v;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v.v[e] = lds[r * dim + ix[e]];
+          reinterpret_cast<V*>(out + (t0 + r) * dim)[q] = v;
+        }
+      }
+    } else {
+      for (int c = threadIdx.x; c < nr * dim; c += kThreads) {
+        const int r = c / dim, q = c - r * dim;
+        const long long src_row = rows ? (long long)rows[t0 + r] : (t0 + r);
+        lds[(long long)r * dim + q] = in[src_row * in_ld + q];
+      }
+      __syncthreads();
+      for (int q = threadIdx.x; q < dim; q += kThreads) {
+        const int ix = idx[q];
+        for (int r = 0; r < nr; ++r) out[(t0 + r) * dim + q] = lds[r * dim + ix];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename E, bool VECTOR>
+__global__ __launch_bounds__(kThreads) void scatter_cols_kernel(
+    const E* __restrict__ in, const int32_t* __restrict__ idx, E* __restrict__ out,
+    long long T, int dim, int R) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* lds = reinterpret_cast<E*>(smem);
+  constexpr int VEC = 16 / sizeof(E);
+  using V = Vec<E, VEC>;
+  for (long long t0 = (long long)blockIdx.x * R; t0 < T; t0 += (long long)gridDim.x * R) {
+    const int nr = (int)((T - t0) < R ? (T - t0) : R);
+    if (VECTOR) {
+      const int cpr = dim / VEC;
+      for (int q = threadIdx.x; q < cpr; q += kThreads) {
+        int ix[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ix[e] = idx[q * VEC + e];
+        for (int r = 0; r < nr; ++r) {
+          const V v = reinterpret_cast<const V*>(in + (t0 + r) * dim)[q];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) lds[r * dim + ix[e]] = v.v[e];
+        }
+      }
+      __syncthreads();
+      for (int c = threadIdx.x; c < nr * cpr; c += kThreads) {
+        const int r = c / cpr, q = c - r * cpr;
+        reinterpret_cast<V*>(out + (t0 + r) * dim)[q] =
+            reinterpret_cast<const V*>(lds + (long long)r * dim)[q];
+      }
+    } else {
+      for (int q = threadIdx.x; q < dim; q += kThreads) {
+        const int ix = idx[q];
+        for (int r = 0; r < nr; ++r) lds[r * dim + ix] = in[(t0 + r) * dim + q];
+      }
+      __syncthreads();
+      for (int c = threadIdx.x; c < nr * dim; c += kThreads) {
+        const int r = c / dim, q = c - r * dim;
+        out[(t0 + r) * dim + q] = lds[(long long)r * dim + q];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Rows of `dim` elements too wide for LDS: plain per-element global access.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void gather_cols_direct(
+    const E* __restrict__ in, long long in_ld, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ idx, E* __restrict__ out, long long T, int dim) {
+  for (long long t = blockIdx.x; t < T; t += gridDim.x) {
+    const long long src_row = rows ? (long long)rows[t] : t;
+    for (int q = threadIdx.x; q < dim; q += kThreads) out[t * dim + q] = in[src_row * in_ld + idx[q]];
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void scatter_cols_direct(
+    const E* __restrict__ in, const int32_t* __restrict__ idx, E* __restrict__ out, long long T,
+    int dim) {
+  for (long long t = blockIdx.x; t < T; t += gridDim.x)
+    for (int q = threadIdx.x; q < dim; q += kThreads) out[t * dim + idx[q]] = in[t * dim + q];
+}
+
+inline int grid_for(long long units) {
+  const long long cap = 256LL * 16;   // 16 workgroups per CU on 256 CUs
+  return (int)(units < cap ? (units < 1 ? 1 : units) : cap);
+}
+
+template <typename E>
+hipError_t gather_typed(const void* in, long long in_ld, const int32_t* rows, const int32_t* idx,
+                        void* out, long long T, int dim, hipStream_t s) {
+  if (T <= 0 || dim <= 0) return hipSuccess;
+  const long long row_bytes = (long long)dim * sizeof(E);
+  constexpr int VEC = 16 / sizeof(E);
+  if (row_bytes > kLdsBudget) {
+    hipLaunchKernelGGL(gather_cols_direct<E>, dim3(grid_for(T)), dim3(kThreads), 0, s,
+                       (const E*)in, in_ld, rows, idx, (E*)out, T, dim);
+    return hipGetLastError();
+  }
+  int R = (int)(kLdsBudget / row_bytes);
+  if (R > 8) R = 8;
+  const size_t lds = (size_t)R * row_bytes;
+  const bool vec = (dim % VEC == 0) && (in_ld % VEC == 0) &&
+                   ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
+  const int grid = grid_for((T + R - 1) / R);
+  if (vec)
+    hipLaunchKernelGGL((gather_cols_kernel<E, true>), dim3(grid), dim3(kThreads), lds, s,
+                       (const E*)in, in_ld, rows, idx, (E*)out, T, dim, R);
+  else
+    hipLaunchKernelGGL((gather_cols_kernel<E, false>), dim3(grid), dim3(kThreads), lds, s,
+                       (const E*)in, in_ld, rows, idx, (E*)out, T, dim, R);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t scatter_typed(const void* in, const int32_t* idx, void* out, long long T, int dim,
+                         hipStream_t s) {
+  if (T <= 0 || dim <= 0) return hipSuccess;
+  const long long row_bytes = (long long)dim * sizeof(E);
+  constexpr int VEC = 16 / sizeof(E);
+  if (row_bytes > kLdsBudget) {
+    hipLaunchKernelGGL(scatter_cols_direct<E>, dim3(grid_for(T)), dim3(kThreads), 0, s,
+                       (const E*)in, idx, (E*)out, T, dim);
+    return hipGetLastError();
+  }
+  int R = (int)(kLdsBudget / row_bytes);
+  if (R > 8) R = 8;
+  const size_t lds = (size_t)R * row_bytes;
+  const bool vec = (dim % VEC == 0) && ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
+  const int grid = grid_for((T + R - 1) / R);
+  if (vec)
+    hipLaunchKernelGGL((scatter_cols_kernel<E, true>), dim3(grid), dim3(kThreads), lds, s,
+                       (const E*)in, idx, (E*)out, T, dim, R);
+  else
+    hipLaunchKernelGGL((scatter_cols_kernel<E, false>), dim3(grid), dim3(kThreads), lds, s,
+                       (const E*)in, idx, (E*)out, T, dim, R);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gather_cols(const void* in, long long in_ld, const int32_t* rows,
+                              const int32_t* idx, void* out, long long T, int dim, int elsize,
+                              hipStream_t s) {
+  if (elsize == 2) return gather_typed<uint16_t>(in, in_ld, rows, idx, out, T, dim, s);
+  return gather_typed<uint32_t>(in, in_ld, rows, idx, out, T, dim, s);
+}
+
+hipError_t launch_scatter_cols(const void* in, const int32_t* idx, void* out, long long T,
+                               int dim, int elsize, hipStream_t s) {
+  if (elsize == 2) return scatter_typed<uint16_t>(in, idx, out, T, dim, s);
+  return scatter_typed<uint32_t>(in, idx, out, T, dim, s);
+}
+
+}  // namespace poetx

@@ -1,0 +1,76 @@
+// Internal interface between the host dispatcher (poetx_host.cpp) and the HIP
+// kernels. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace poetx {
+
+// A run of consecutive blocks of equal size on one side.
+struct Seg {
+  int b;              // block size
+  int count;          // number of blocks in the run
+  int dim_off;        // first feature index of the run (permuted index space)
+  long long q_off;    // element offset of the run's first block in the b*b arrays
+  long long p_off;    // offset of its first packed parameter
+};
+
+// ---------------------------------------------------------------- index ops
+// out[t][i] = in[rows ? rows[t] : t][idx[i]]; in has row stride in_ld elements.
+hipError_t launch_gather_cols(const void* in, long long in_ld, const int32_t* rows,
+                              const int32_t* idx, void* out, long long T, int dim,
+                              int elsize, hipStream_t s);
+// out[t][idx[i]] = in[t][i]
+hipError_t launch_scatter_cols(const void* in, const int32_t* idx, void* out, long long T,
+                               int dim, int elsize, hipStream_t s);
+
+// ---------------------------------------------------------------- block helpers (fp32)
+// S = skew(theta) for every block of the run; if Q != nullptr also Q = I + c1 * S.
+hipError_t launch_unpack_skew(const float* theta, const Seg& g, float* S, float* Q, float c1,
+                              hipStream_t s);
+// g[(i,j)] = Sbar[i][j] - Sbar[j][i] for i < j, packed like theta.
+hipError_t launch_pack_antisym(const float* Sbar, const Seg& g, float* gtheta, hipStream_t s);
+// out = (to_bf16 ? bf16 : fp32) copy of n floats.
+hipError_t launch_cast(const float* in, void* out, long long n, int to_bf16, hipStream_t s);
+// out1 = c * in; out2 = c * in (out2 may be null)
+hipError_t launch_scale2(const float* in, float c, float* out1, float* out2, long long n,
+                         hipStream_t s);
+// out[i] = sum_{s < nsplit} part[s * stride + i], in order of s.
+hipError_t launch_sum_splits(const float* part, int nsplit, long long stride, long long n,
+                             float* out, hipStream_t s);
+hipError_t launch_zero(float* out, long long n, hipStream_t s);
+
+// ---------------------------------------------------------------- fp32 GEMM
+// C(m,n) = alpha * sum_k A(m,k) B(n,k) + beta * Cin(m,n) + gamma * [m == n];
+// optionally E(m,n) = sum_k A(m,k) B(n,k). General element strides, batched over
+// `groups` (group strides) and split over K (`splits`, partial outputs c_ss apart;
+// with splits > 1 only alpha applies).
+struct GemmF32 {
+  const float* A; const float* B; float* C; const float* Cin; float* E;
+  int M, N, K;
+  long long a_rs, a_cs, b_rs, b_cs, c_rs;
+  long long a_gs, b_gs, c_gs;
+  int groups, splits;
+  long long c_ss;
+  float alpha, beta, gamma;
+};
+hipError_t launch_gemm_f32(const GemmF32& p, hipStream_t s);
+
+// ---------------------------------------------------------------- bf16 MFMA GEMM
+// C(m,n) = sum_k A(m,k) B(n,k), bf16 inputs, fp32 accumulation.
+// A(m,k) = A[m*lda + k] when a_kmajor, else A[k*lda + m]; same for B with ldb.
+// Output bf16 (out_f32 = 0) or fp32; C(m,n) at C[m*ldc + n]. Batched over groups
+// and split over K like GemmF32.
+struct GemmBf16 {
+  const void* A; const void* B; void* C;
+  int M, N, K;
+  long long lda, ldb, ldc;
+  int a_kmajor, b_kmajor, out_f32;
+  long long a_gs, b_gs, c_gs;
+  int groups, splits;
+  long long c_ss;
+};
+hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
+
+}  // namespace poetx

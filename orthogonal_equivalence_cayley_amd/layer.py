@@ -1,0 +1,98 @@
+"""One POET-X linear layer on the GPU through libpoetx.
+
+Holds the device buffers of one layer (pre-merged weight, permutations, packed
+skew parameters, built blocks, workspaces) and calls the C ABI for build,
+forward and backward. torch provides memory and the current stream; all
+arithmetic runs in libpoetx's HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import poetx as _px
+
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
+_PX_DTYPE = {"bf16": _px.POETX_BF16, "f32": _px.POETX_FP32}
+
+
+class PoetxLayer:
+    def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
+                 dtype: str = "bf16", device: str = "cuda"):
+        if dtype not in _TORCH_DTYPE:
+            raise ValueError(f"dtype must be one of {sorted(_TORCH_DTYPE)}")
+        self.m, self.n, self.k, self.dtype = m, n, k, dtype
+        self.device = torch.device(device)
+        self.tdtype = _TORCH_DTYPE[dtype]
+        self.plan = _px.Plan(m, n, bsz_R, bsz_P, k, _PX_DTYPE[dtype])
+        self.nparam = (self.plan.param_count(_px.SIDE_R), self.plan.param_count(_px.SIDE_P))
+        self.nelem = (self.plan.block_elems(_px.SIDE_R), self.plan.block_elems(_px.SIDE_P))
+        self._ws = {}
+        self.Wt = None
+        self.pi_R = self.pi_P = None
+        self.theta = [None, None]
+        self.Q32 = [torch.empty(self.nelem[s], dtype=torch.float32, device=self.device) for s in (0, 1)]
+        if dtype == "bf16":
+            self.Qact = [torch.empty(self.nelem[s], dtype=torch.bfloat16, device=self.device) for s in (0, 1)]
+        else:
+            self.Qact = self.Q32
+        self.Wa = None
+
+    # ------------------------------------------------------------------ setup
+    def workspace(self, kind: int, T: int = 0) -> torch.Tensor:
+        need = self.plan.workspace_size(T, kind)
+        cur = self._ws.get(kind)
+        if cur is None or cur.numel() < need:
+            cur = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            self._ws[kind] = cur
+        return cur
+
+    def set_weight(self, W0: torch.Tensor, pi_R: torch.Tensor, pi_P: torch.Tensor) -> None:
+        """Pre-merge the permutations into W0 (once per inner loop)."""
+        assert W0.shape == (self.m, self.n) and W0.dtype == self.tdtype and W0.is_contiguous()
+        self.pi_R = pi_R.to(device=self.device, dtype=torch.int32).contiguous()
+        self.pi_P = pi_P.to(device=self.device, dtype=torch.int32).contiguous()
+        self.Wt = torch.empty_like(W0)
+        self.plan.permute_weight(W0, self.pi_R, self.pi_P, self.Wt)
+
+    def set_theta(self, theta_R: torch.Tensor, theta_P: torch.Tensor) -> None:
+        self.theta = [theta_R.to(device=self.device, dtype=torch.float32).contiguous(),
+                      theta_P.to(device=self.device, dtype=torch.float32).contiguous()]
+        assert self.theta[0].numel() == self.nparam[0] and self.theta[1].numel() == self.nparam[1]
+
+    # ------------------------------------------------------------------ calls
+    def build(self) -> None:
+        ws = self.workspace(_px.WS_BUILD)
+        for side in (_px.SIDE_R, _px.SIDE_P):
+            qa = self.Qact[side] if self.dtype == "bf16" else None
+            self.plan.build_orth(side, self.theta[side], self.Q32[side], qa, ws, ws.numel())
+
+    def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
+                Wa: Optional[torch.Tensor] = None, save: bool = True) -> torch.Tensor:
+        T = X.shape[0]
+        assert X.shape == (T, self.n) and X.dtype == self.tdtype and X.is_contiguous()
+        if Y is None:
+            Y = torch.empty(T, self.m, dtype=self.tdtype, device=self.device)
+        if save and Wa is None:
+            Wa = torch.empty(T, self.m, dtype=self.tdtype, device=self.device)
+        ws = self.workspace(_px.WS_FORWARD, T)
+        self.plan.forward(T, X, self.Wt, self.pi_R, self.pi_P, self.Qact[0], self.Qact[1], Y,
+                          Wa if save else None, ws, ws.numel())
+        self.Wa = Wa if save else None
+        return Y
+
+    def backward(self, X: torch.Tensor, G_Y: torch.Tensor, G_X: Optional[torch.Tensor] = None,
+                 g_theta: Optional[Sequence[torch.Tensor]] = None):
+        T = X.shape[0]
+        assert self.Wa is not None and self.Wa.shape[0] == T, "forward(save=True) first"
+        assert G_Y.shape == (T, self.m) and G_Y.dtype == self.tdtype and G_Y.is_contiguous()
+        if G_X is None:
+            G_X = torch.empty(T, self.n, dtype=self.tdtype, device=self.device)
+        if g_theta is None:
+            g_theta = [torch.empty(self.nparam[s], dtype=torch.float32, device=self.device) for s in (0, 1)]
+        ws = self.workspace(_px.WS_BACKWARD, T)
+        self.plan.backward(T, X, self.Wt, self.pi_R, self.pi_P, self.theta[0], self.theta[1],
+                           self.Qact[0], self.Qact[1], self.Wa, G_Y, G_X, g_theta[0], g_theta[1],
+                           ws, ws.numel())
+        return G_X, g_theta[0], g_theta[1]

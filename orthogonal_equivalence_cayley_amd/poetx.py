@@ -1,0 +1,181 @@
+"""ctypes binding of libpoetx (include/poetx.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libpoetx.so. torch supplies device memory (tensor data pointers) and the
+stream (torch.cuda.current_stream()). The module raises at import time if the
+built library is missing; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpoetx.so")
+
+POETX_OK = 0
+POETX_ERR_INVALID_ARG = 1
+POETX_ERR_SHAPE = 2
+POETX_ERR_DTYPE = 3
+POETX_ERR_ALIGNMENT = 4
+POETX_ERR_UNSUPPORTED = 5
+POETX_ERR_HIP = 6
+POETX_ERR_WORKSPACE = 7
+
+POETX_FP32 = 0
+POETX_BF16 = 1
+SIDE_R = 0
+SIDE_P = 1
+WS_BUILD = 0
+WS_FORWARD = 1
+WS_BACKWARD = 2
+
+EXPORTED = (
+    "poetx_plan_create", "poetx_plan_destroy", "poetx_param_count", "poetx_block_elems",
+    "poetx_workspace_size", "poetx_status_string", "poetx_permute_weight",
+    "poetx_build_orth", "poetx_forward", "poetx_backward", "poetx_gather_cols",
+    "poetx_scatter_cols",
+)
+
+
+class PoetxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("m", ctypes.c_int32), ("n", ctypes.c_int32),
+        ("nb_R", ctypes.c_int32), ("nb_P", ctypes.c_int32),
+        ("bsz_R", ctypes.POINTER(ctypes.c_int32)), ("bsz_P", ctypes.POINTER(ctypes.c_int32)),
+        ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libpoetx.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    st = ctypes.c_int
+    sig = {
+        "poetx_plan_create": (st, [ctypes.POINTER(Desc), ctypes.POINTER(vp)]),
+        "poetx_plan_destroy": (None, [vp]),
+        "poetx_param_count": (i64, [vp, i32]),
+        "poetx_block_elems": (i64, [vp, i32]),
+        "poetx_workspace_size": (sz, [vp, i64, i32]),
+        "poetx_status_string": (ctypes.c_char_p, [st]),
+        "poetx_permute_weight": (st, [vp, vp, vp, vp, vp, vp]),
+        "poetx_build_orth": (st, [vp, i32, vp, vp, vp, vp, sz, vp]),
+        "poetx_forward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "poetx_backward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                vp, sz, vp]),
+        "poetx_gather_cols": (st, [vp, i64, i32, vp, vp, vp, vp]),
+        "poetx_scatter_cols": (st, [vp, i64, i32, vp, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+def status_string(status: int) -> str:
+    return LIB.poetx_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != POETX_OK:
+        raise PoetxError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    """Device (or host) address of a tensor, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Plan:
+    """Owns a poetx_plan (host-only object; creating one needs no GPU)."""
+
+    def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
+                 dtype: int):
+        self.m, self.n, self.k, self.dtype = int(m), int(n), int(k), int(dtype)
+        self.bsz_R, self.bsz_P = tuple(int(b) for b in bsz_R), tuple(int(b) for b in bsz_P)
+        aR = (ctypes.c_int32 * max(1, len(self.bsz_R)))(*self.bsz_R)
+        aP = (ctypes.c_int32 * max(1, len(self.bsz_P)))(*self.bsz_P)
+        d = Desc(self.m, self.n, len(self.bsz_R), len(self.bsz_P), aR, aP, self.k, self.dtype)
+        h = ctypes.c_void_p()
+        self._h = None
+        _check(LIB.poetx_plan_create(ctypes.byref(d), ctypes.byref(h)), "poetx_plan_create")
+        self._h = h.value
+
+    @property
+    def handle(self) -> int:
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            LIB.poetx_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def param_count(self, side: int) -> int:
+        return int(LIB.poetx_param_count(self._h, side))
+
+    def block_elems(self, side: int) -> int:
+        return int(LIB.poetx_block_elems(self._h, side))
+
+    def workspace_size(self, T: int, kind: int) -> int:
+        return int(LIB.poetx_workspace_size(self._h, T, kind))
+
+    # ---- calls (tensors are torch tensors on the GPU, or raw int addresses)
+    def permute_weight(self, W0, pi_R, pi_P, Wt, stream=None) -> None:
+        _check(LIB.poetx_permute_weight(self._h, _ptr(W0), _ptr(pi_R), _ptr(pi_P), _ptr(Wt),
+                                        _stream(stream)), "poetx_permute_weight")
+
+    def build_orth(self, side: int, theta, Q_f32, Q_act, ws, ws_bytes: int, stream=None) -> None:
+        _check(LIB.poetx_build_orth(self._h, side, _ptr(theta), _ptr(Q_f32), _ptr(Q_act),
+                                    _ptr(ws), ws_bytes, _stream(stream)), "poetx_build_orth")
+
+    def forward(self, T: int, X, Wt, pi_R, pi_P, Q_R, Q_P, Y, Wa_saved, ws, ws_bytes: int,
+                stream=None) -> None:
+        _check(LIB.poetx_forward(self._h, T, _ptr(X), _ptr(Wt), _ptr(pi_R), _ptr(pi_P),
+                                 _ptr(Q_R), _ptr(Q_P), _ptr(Y), _ptr(Wa_saved), _ptr(ws),
+                                 ws_bytes, _stream(stream)), "poetx_forward")
+
+    def backward(self, T: int, X, Wt, pi_R, pi_P, theta_R, theta_P, Q_R, Q_P, Wa_saved, G_Y,
+                 G_X, g_theta_R, g_theta_P, ws, ws_bytes: int, stream=None) -> None:
+        _check(LIB.poetx_backward(self._h, T, _ptr(X), _ptr(Wt), _ptr(pi_R), _ptr(pi_P),
+                                  _ptr(theta_R), _ptr(theta_P), _ptr(Q_R), _ptr(Q_P),
+                                  _ptr(Wa_saved), _ptr(G_Y), _ptr(G_X), _ptr(g_theta_R),
+                                  _ptr(g_theta_P), _ptr(ws), ws_bytes, _stream(stream)),
+               "poetx_backward")
+
+    def gather_cols(self, T: int, dim: int, inp, idx, out, stream=None) -> None:
+        _check(LIB.poetx_gather_cols(self._h, T, dim, _ptr(inp), _ptr(idx), _ptr(out),
+                                     _stream(stream)), "poetx_gather_cols")
+
+    def scatter_cols(self, T: int, dim: int, inp, idx, out, stream=None) -> None:
+        _check(LIB.poetx_scatter_cols(self._h, T, dim, _ptr(inp), _ptr(idx), _ptr(out),
+                                      _stream(stream)), "poetx_scatter_cols")

@@ -1,0 +1,123 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments with the documented status codes before any
+device call (none of these calls reaches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from orthogonal_equivalence_cayley_amd import poetx as px
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "poetx.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(poetx_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(px.EXPORTED)
+    lib = ctypes.CDLL(px.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _plan(**kw):
+    args = dict(m=64, n=48, bsz_R=(32, 32), bsz_P=(16, 32), k=3, dtype=px.POETX_FP32)
+    args.update(kw)
+    return px.Plan(**args)
+
+
+def test_plan_counts():
+    p = _plan()
+    assert p.param_count(px.SIDE_R) == 2 * 32 * 31 // 2
+    assert p.param_count(px.SIDE_P) == 16 * 15 // 2 + 32 * 31 // 2
+    assert p.block_elems(px.SIDE_R) == 2 * 32 * 32
+    assert p.block_elems(px.SIDE_P) == 16 * 16 + 32 * 32
+    assert p.param_count(7) == -1
+
+
+@pytest.mark.parametrize("kw, status", [
+    (dict(bsz_R=(32, 31)), px.POETX_ERR_SHAPE),
+    (dict(bsz_P=(48, 0)), px.POETX_ERR_SHAPE),
+    (dict(k=-1), px.POETX_ERR_SHAPE),
+    (dict(k=33), px.POETX_ERR_SHAPE),
+    (dict(dtype=5), px.POETX_ERR_DTYPE),
+    (dict(dtype=px.POETX_BF16, bsz_P=(24, 24)), px.POETX_ERR_UNSUPPORTED),
+    (dict(dtype=px.POETX_BF16, m=40, bsz_R=(40,)), px.POETX_ERR_UNSUPPORTED),
+])
+def test_plan_rejects(kw, status):
+    with pytest.raises(px.PoetxError) as e:
+        _plan(**kw)
+    assert e.value.status == status
+
+
+def test_plan_accepts_ragged_fp32_and_bf16_multiples_of_16():
+    _plan(bsz_R=(5, 27, 32), dtype=px.POETX_FP32)
+    _plan(bsz_R=(48, 16), bsz_P=(16, 32), dtype=px.POETX_BF16)
+
+
+def test_null_desc():
+    h = ctypes.c_void_p()
+    assert px.LIB.poetx_plan_create(None, ctypes.byref(h)) == px.POETX_ERR_INVALID_ARG
+
+
+def test_workspace_sizes():
+    p = _plan()
+    b = p.workspace_size(0, px.WS_BUILD)
+    assert b >= 3 * 4 * p.block_elems(px.SIDE_P)
+    f1, f2 = p.workspace_size(10, px.WS_FORWARD), p.workspace_size(1000, px.WS_FORWARD)
+    assert 0 < f1 < f2
+    assert p.workspace_size(10, px.WS_BACKWARD) > 0
+    assert p.workspace_size(10, 9) == 0
+    assert p.workspace_size(-1, px.WS_FORWARD) == 0
+
+
+def test_status_strings():
+    for s in range(8):
+        assert isinstance(px.status_string(s), str) and px.status_string(s)
+
+
+# Argument errors are returned before anything is launched, so fake addresses
+# are safe here.
+A = 0x10000
+
+
+def test_forward_argument_errors():
+    p = _plan()
+    ws = p.workspace_size(4, px.WS_FORWARD)
+    call = lambda **kw: px.LIB.poetx_forward(
+        p.handle, kw.get("T", 4), kw.get("X", A), A, A, A, A, A, kw.get("Y", A), None,
+        kw.get("ws", A), kw.get("wsb", ws), None)
+    assert call(T=0) == px.POETX_OK                      # T = 0 is a no-op
+    assert call(T=-1) == px.POETX_ERR_INVALID_ARG
+    assert call(X=None) == px.POETX_ERR_INVALID_ARG
+    assert call(Y=A + 8) == px.POETX_ERR_ALIGNMENT
+    assert call(wsb=ws - 1) == px.POETX_ERR_WORKSPACE
+    assert call(ws=None) == px.POETX_ERR_WORKSPACE
+    assert px.LIB.poetx_forward(None, 4, A, A, A, A, A, A, A, None, A, ws, None) == px.POETX_ERR_INVALID_ARG
+
+
+def test_backward_and_build_argument_errors():
+    p = _plan()
+    wsb = p.workspace_size(4, px.WS_BACKWARD)
+    args = [p.handle, 4, A, A, A, A, A, A, A, A, A, A, A, A, A, A, wsb, None]
+    assert px.LIB.poetx_backward(*args[:10], None, *args[11:]) == px.POETX_ERR_INVALID_ARG
+    bad = list(args)
+    bad[3] = A + 4
+    assert px.LIB.poetx_backward(*bad) == px.POETX_ERR_ALIGNMENT
+    bad = list(args)
+    bad[16] = 16
+    assert px.LIB.poetx_backward(*bad) == px.POETX_ERR_WORKSPACE
+    bw = p.workspace_size(0, px.WS_BUILD)
+    assert px.LIB.poetx_build_orth(p.handle, 3, A, A, None, A, bw, None) == px.POETX_ERR_INVALID_ARG
+    assert px.LIB.poetx_build_orth(p.handle, 0, A, A, None, A, bw - 1, None) == px.POETX_ERR_WORKSPACE
+    assert px.LIB.poetx_build_orth(p.handle, 0, A + 2, A, None, A, bw, None) == px.POETX_ERR_ALIGNMENT
+    assert px.LIB.poetx_permute_weight(p.handle, A, A, A, A, None) == px.POETX_ERR_INVALID_ARG
+    assert px.LIB.poetx_gather_cols(p.handle, 3, 5, A, A, A, None) == px.POETX_ERR_INVALID_ARG
+    assert px.LIB.poetx_gather_cols(p.handle, 0, 5, A, A, A + 1, None) == px.POETX_OK
+    assert px.LIB.poetx_scatter_cols(p.handle, 3, 5, A, A + 8, A + 16, None) == px.POETX_ERR_ALIGNMENT

@@ -1,0 +1,84 @@
+"""GPU parity at the five workloads' full sizes, through the same library calls
+(and therefore the same kernels and launch shapes) the benchmark times.
+
+The three single-layer workloads are compared with the full float64 oracle.
+For the 7-linear blocks at hidden 2048 and 4096 (16384 tokens) every layer is
+checked on sampled outputs the oracle computes one by one: 48 token rows of
+Y, Wa and G_X (rows are independent; the first and the last row are always
+included), all blocks of Q, and the packed parameter gradient of the first and
+the last block of each side (a full reduction over all tokens; the last block
+is the 256-wide tail where the side has one).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import blocks_concat, device_ready, log, run_layer
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not device_ready():
+        pytest.skip("no GPU")
+
+
+def _check(name, got, want, tol):
+    err = oracle.rel_fro(got, want)
+    log(f"  {name}: rel_fro={err:.3e} (tol {tol:g})")
+    assert err <= tol, (name, err)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_single_layer_workload_full(cid):
+    w = workloads.WORKLOADS[cid]
+    inp = workloads.layer_inputs(w, 0)
+    log(f"{w.name}: T={w.T} m={inp.spec.m} n={inp.spec.n}")
+    got, _ = run_layer(inp, w.k, w.dtype, backward=w.backward)
+    ref = oracle.layer_reference(inp, w.k, backward_pass=w.backward)
+    tol = TOL_F32 if w.dtype == "f32" else TOL_BF16
+    _check("Q_R", got["QR"], blocks_concat(ref["QR"]), TOL_F32)
+    _check("Q_P", got["QP"], blocks_concat(ref["QP"]), TOL_F32)
+    _check("Wa", got["Wa"], ref["Wa"], tol)
+    _check("Y", got["Y"], ref["Y"], tol)
+    if w.backward:
+        _check("G_X", got["G_X"], ref["G_X"], tol)
+        _check("g_theta_R", got["g_theta_R"], ref["g_theta_R"], tol)
+        _check("g_theta_P", got["g_theta_P"], ref["g_theta_P"], tol)
+
+
+def _sample_rows(T, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, 46, replace=False)]))
+
+
+@pytest.mark.parametrize("cid,li", [(4, i) for i in range(7)] + [(5, i) for i in range(7)])
+def test_block_workload_layer_sampled(cid, li):
+    w = workloads.WORKLOADS[cid]
+    inp = workloads.layer_inputs(w, li)
+    sp = inp.spec
+    log(f"{w.name} layer {sp.name}: T={w.T} m={sp.m} n={sp.n}")
+    got, layer = run_layer(inp, w.k, w.dtype, backward=True)
+    del layer
+    QR = oracle.build_orth(inp.theta_R, sp.bsz_R, w.k)
+    QP = oracle.build_orth(inp.theta_P, sp.bsz_P, w.k)
+    _check("Q_R", got["QR"], blocks_concat(QR), TOL_F32)
+    _check("Q_P", got["QP"], blocks_concat(QP), TOL_F32)
+    Wt = oracle.permute_weight(inp.W0, inp.pi_R, inp.pi_P)
+    rows = _sample_rows(w.T, 100 * cid + li)
+    Yr, War = oracle.forward(inp.X[rows], Wt, inp.pi_R, inp.pi_P, QR, QP, sp.bsz_R, sp.bsz_P)
+    _check("Y rows", got["Y"][rows], Yr, TOL_BF16)
+    _check("Wa rows", got["Wa"][rows], War, TOL_BF16)
+    Gr = oracle.backward_rows(inp.G_Y[rows], Wt, inp.pi_R, inp.pi_P, QR, QP, sp.bsz_R, sp.bsz_P)
+    _check("G_X rows", got["G_X"][rows], Gr, TOL_BF16)
+    for side, bsz, g in (("R", sp.bsz_R, got["g_theta_R"]), ("P", sp.bsz_P, got["g_theta_P"])):
+        offs = np.cumsum([0] + [b * (b - 1) // 2 for b in bsz])
+        for j in sorted({0, len(bsz) - 1}):
+            want = oracle.theta_grad_block(side, j, inp.X, Wt, inp.pi_R, inp.pi_P, inp.theta_R,
+                                           inp.theta_P, QR, QP, inp.G_Y, sp.bsz_R, sp.bsz_P, w.k)
+            _check(f"g_theta_{side}[block {j}]", g[offs[j]:offs[j + 1]], want, TOL_BF16)

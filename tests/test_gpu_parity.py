@@ -1,0 +1,201 @@
+"""GPU parity of libpoetx against the float64 oracle on seeded inputs, at sizes
+the oracle finishes in seconds (several tiles, ragged tails, edge cases).
+
+Tolerances (relative Frobenius error against the float64 oracle):
+  index paths (gather, scatter, weight pre-merge): bit-exact;
+  fp32 mode: 1e-5 for Q, Y, Wa, G_X and both parameter gradients;
+  bf16 inputs with fp32 accumulation: 2e-2.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import blocks_concat, device_ready, log, make_layer, run_layer, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not device_ready():
+        pytest.skip("no GPU")
+
+
+def _px():
+    from orthogonal_equivalence_cayley_amd import poetx
+    return poetx
+
+
+def _plan(dtype):
+    px = _px()
+    return px.Plan(32, 32, (16, 16), (16, 16), 1, px.POETX_BF16 if dtype == "bf16" else px.POETX_FP32)
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu()
+
+
+# ---------------------------------------------------------------- index paths
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dim", [16, 37, 2048, 5632, 11008, 40000])
+@pytest.mark.parametrize("T", [1, 9, 130])
+def test_gather_scatter_bitexact(dtype, dim, T):
+    import torch
+    log(f"gather/scatter dtype={dtype} dim={dim} T={T}")
+    rng = np.random.default_rng(dim * 7 + T)
+    x = rng.standard_normal((T, dim)).astype(np.float32)
+    idx = rng.permutation(dim).astype(np.int32)
+    X = to_dev(x, dtype)
+    I = torch.from_numpy(idx).cuda()
+    out = torch.empty_like(X)
+    back = torch.empty_like(X)
+    p = _plan(dtype)
+    p.gather_cols(T, dim, X, I, out)
+    p.scatter_cols(T, dim, out, I, back)
+    torch.cuda.synchronize()
+    Xc = X.cpu()
+    assert torch.equal(_bits(out), _bits(Xc[:, torch.from_numpy(idx).long()].contiguous()))
+    assert torch.equal(_bits(back), _bits(Xc))
+
+
+@pytest.mark.parametrize("dtype,m,n", [("bf16", 2048, 2048), ("bf16", 5632, 2048), ("f32", 37, 53)])
+def test_permute_weight_bitexact(dtype, m, n):
+    import torch
+    log(f"permute_weight {dtype} {m}x{n}")
+    rng = np.random.default_rng(m + n)
+    W0 = rng.standard_normal((m, n)).astype(np.float32)
+    piR, piP = rng.permutation(m).astype(np.int32), rng.permutation(n).astype(np.int32)
+    px = _px()
+    p = px.Plan(m, n, (m,), (n,), 0, px.POETX_BF16 if dtype == "bf16" else px.POETX_FP32)
+    Wd = to_dev(W0, dtype)
+    Wt = torch.empty_like(Wd)
+    p.permute_weight(Wd, torch.from_numpy(piR).cuda(), torch.from_numpy(piP).cuda(), Wt)
+    torch.cuda.synchronize()
+    want = Wd.cpu()[torch.from_numpy(piR).long()][:, torch.from_numpy(piP).long()].contiguous()
+    assert torch.equal(_bits(Wt), _bits(want))
+
+
+# ---------------------------------------------------------------- build
+
+@pytest.mark.parametrize("dtype,bsz,k,std", [
+    ("f32", (32,) * 8, 3, 0.01),
+    ("f32", (5, 1, 17, 64), 0, 0.05),
+    ("f32", (7, 33), 6, 0.05),
+    ("bf16", (256,) * 3, 4, 0.01),
+    ("bf16", (512, 512, 256), 5, 0.005),
+    ("bf16", (16, 48), 2, 0.05),
+])
+def test_build_orth(dtype, bsz, k, std):
+    import torch
+    log(f"build_orth {dtype} {bsz} k={k}")
+    inp = workloads.small_case(sum(bsz), 16, bsz, (16,), T=1, seed=len(bsz) + k, dtype=dtype,
+                               theta_std=std)
+    layer = make_layer(inp, k, dtype)
+    layer.build()
+    torch.cuda.synchronize()
+    want = blocks_concat(oracle.build_orth(inp.theta_R, bsz, k))
+    got = layer.Q32[0].cpu().numpy().astype(np.float64)
+    assert oracle.rel_fro(got, want) <= TOL_F32
+    if dtype == "bf16":
+        # the bf16 copy is the fp32 block rounded to nearest: within half a bf16 ulp
+        qa = layer.Qact[0].float().cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(qa - want) <= np.abs(want) * 2.0 ** -8 + 1e-6)
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _compare(got, ref, keys, tol, tag):
+    for key in keys:
+        r = ref[key]
+        if key in ("QR", "QP"):
+            r = blocks_concat(r)
+        err = oracle.rel_fro(got[key], r)
+        log(f"  {tag} {key}: rel_fro={err:.3e}")
+        assert err <= tol, (key, err)
+
+
+def test_layer_fp32_small_config():
+    w = workloads.WORKLOADS[1]
+    inp = workloads.layer_inputs(w, 0)
+    log(f"layer fp32 {w.name}")
+    got, _ = run_layer(inp, w.k, "f32")
+    ref = oracle.layer_reference(inp, w.k)
+    _compare(got, ref, ["QR", "QP", "Wa", "Y", "G_X", "g_theta_R", "g_theta_P"], TOL_F32, "cfg1")
+
+
+@pytest.mark.parametrize("case", [
+    dict(m=12, n=9, bR=(5, 7), bP=(4, 1, 4), T=7, k=0),
+    dict(m=70, n=45, bR=(30, 40), bP=(45,), T=1, k=5),
+    dict(m=96, n=130, bR=(32, 64), bP=(65, 65), T=130, k=2),
+    dict(m=64, n=64, bR=(64,), bP=(16, 16, 32), T=257, k=1),
+])
+def test_layer_fp32_ragged(case):
+    inp = workloads.small_case(case["m"], case["n"], case["bR"], case["bP"], T=case["T"],
+                               seed=case["m"] + case["T"], dtype="f32", theta_std=0.05)
+    log(f"layer fp32 ragged {case}")
+    got, _ = run_layer(inp, case["k"], "f32")
+    ref = oracle.layer_reference(inp, case["k"])
+    _compare(got, ref, ["QR", "QP", "Wa", "Y", "G_X", "g_theta_R", "g_theta_P"], TOL_F32, "ragged")
+
+
+@pytest.mark.parametrize("case", [
+    dict(m=512, n=256, bR=(256, 256), bP=(128, 128), T=300, k=4),
+    dict(m=384, n=320, bR=(128, 256), bP=(64, 256), T=77, k=3),
+    dict(m=2048, n=512, bR=(512,) * 3 + (256, 256), bP=(512,), T=1000, k=5),
+    dict(m=256, n=256, bR=(256,), bP=(256,), T=1, k=4),
+    dict(m=48, n=32, bR=(16, 32), bP=(32,), T=5, k=0),
+])
+def test_layer_bf16_small(case):
+    inp = workloads.small_case(case["m"], case["n"], case["bR"], case["bP"], T=case["T"],
+                               seed=case["n"] + case["T"], dtype="bf16", theta_std=0.01)
+    log(f"layer bf16 {case}")
+    got, _ = run_layer(inp, case["k"], "bf16")
+    ref = oracle.layer_reference(inp, case["k"])
+    _compare(got, ref, ["QR", "QP"], TOL_F32, "bf16")
+    _compare(got, ref, ["Wa", "Y", "G_X", "g_theta_R", "g_theta_P"], TOL_BF16, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_theta_zero_gives_plain_linear(dtype):
+    inp = workloads.small_case(256, 128, (128, 128), (128,), T=64, seed=3, dtype=dtype)
+    inp.theta_R[:] = 0.0
+    inp.theta_P[:] = 0.0
+    log(f"theta=0 {dtype}")
+    got, _ = run_layer(inp, 4, dtype, backward=False)
+    want = inp.X.astype(np.float64) @ inp.W0.astype(np.float64).T
+    assert oracle.rel_fro(got["Y"], want) <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+    assert np.array_equal(got["QR"], blocks_concat([np.eye(128)] * 2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_tokens(dtype):
+    import torch
+    inp = workloads.small_case(64, 32, (32, 32), (32,), T=3, seed=5, dtype=dtype)
+    layer = make_layer(inp, 2, dtype)
+    layer.build()
+    X = to_dev(inp.X[:0], dtype)
+    Y = layer.forward(X, save=True)
+    G_X, gR, gP = layer.backward(X, to_dev(inp.G_Y[:0], dtype))
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 64) and G_X.shape == (0, 32)
+    assert float(gR.abs().max()) == 0.0 and float(gP.abs().max()) == 0.0
+
+
+def test_backward_deterministic():
+    import torch
+    inp = workloads.small_case(512, 256, (256, 256), (256,), T=2000, seed=9, dtype="bf16")
+    layer = make_layer(inp, 4, "bf16")
+    layer.build()
+    X, G = to_dev(inp.X, "bf16"), to_dev(inp.G_Y, "bf16")
+    layer.forward(X)
+    a = [t.clone() for t in layer.backward(X, G)]
+    b = [t.clone() for t in layer.backward(X, G)]
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)

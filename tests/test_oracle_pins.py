@@ -270,3 +270,28 @@ def test_cnp_gradient_k0_is_identity_map():
 def test_cnp_coefficients():
     assert oracle.cnp_coefficients(0) == [1.0, 1.0]
     assert oracle.cnp_coefficients(3) == [1.0, 2.0, 2.0, 2.0, 1.0]
+
+
+# --------------------------------------------------------------------------
+# restricted forms used for sampled checks at full size agree with the full oracle
+
+def test_restricted_forms_match_full_oracle():
+    inp = workloads.small_case(24, 20, (8, 16), (4, 12, 4), T=9, seed=61, theta_std=0.1)
+    k = 3
+    ref = oracle.layer_reference(inp, k)
+    sp = inp.spec
+    rows = [0, 4, 8]
+    Yr = oracle.forward_rows(inp.X[rows], ref["Wt"], inp.pi_R, inp.pi_P, ref["QR"], ref["QP"],
+                             sp.bsz_R, sp.bsz_P)
+    assert np.max(np.abs(Yr - ref["Y"][rows])) < 1e-14
+    Gr = oracle.backward_rows(inp.G_Y[rows], ref["Wt"], inp.pi_R, inp.pi_P, ref["QR"], ref["QP"],
+                              sp.bsz_R, sp.bsz_P)
+    assert np.max(np.abs(Gr - ref["G_X"][rows])) < 1e-13
+    offs = {"R": np.cumsum([0] + [b * (b - 1) // 2 for b in sp.bsz_R]),
+            "P": np.cumsum([0] + [b * (b - 1) // 2 for b in sp.bsz_P])}
+    for side, nb, full in (("R", 2, ref["g_theta_R"]), ("P", 3, ref["g_theta_P"])):
+        for j in range(nb):
+            g = oracle.theta_grad_block(side, j, inp.X, ref["Wt"], inp.pi_R, inp.pi_P, inp.theta_R,
+                                        inp.theta_P, ref["QR"], ref["QP"], inp.G_Y, sp.bsz_R,
+                                        sp.bsz_P, k)
+            assert np.max(np.abs(g - full[offs[side][j]:offs[side][j + 1]])) < 1e-12
