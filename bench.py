@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the POET-X layer on one MI355X through libpoetx.
+
+One step = one pass of the whole path over the workload: build of every
+layer's Cayley-Neumann blocks (both sides), the input-centric forward of every
+layer (saving Wa), and the backward of every layer (gradients w.r.t. X and
+both sides' packed skew parameters). The default workload is the seven
+linears of a LLaMA-style block at hidden 2048 (q, k, v, o 2048x2048; gate, up
+5632x2048; down 2048x5632), b = 256, k = 4, bf16 activations and weights, fp32
+skew parameters, 16384 tokens, every layer independently seeded. Inputs are
+synthetic (workloads.py) and resident in HBM before the timed region.
+
+Prints one JSON line. `roofline` covers the kernel with the largest share of
+the step, timed live with HIP events on the stream it runs on; `cpu_baseline`
+times the float64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12         # MI355X HBM3E, B/s
+METRIC = "POET-X layer fwd+bwd tokens/s and % bf16 MFMA peak at hidden 2048, 1 GPU"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def stage_flops(w, T):
+    """Algorithmic flops per stage for one step of the workload."""
+    f = dict(w0_fwd=0.0, w0_bwd=0.0, block_fwd=0.0, block_bwd=0.0, dq=0.0, build=0.0, cnp_bwd=0.0)
+    for sp in w.layers:
+        sq = sum(b * b for b in sp.bsz_R) + sum(b * b for b in sp.bsz_P)
+        cube = sum(b ** 3 for b in sp.bsz_R) + sum(b ** 3 for b in sp.bsz_P)
+        f["w0_fwd"] += 2.0 * T * sp.m * sp.n
+        f["block_fwd"] += 2.0 * T * sq
+        f["build"] += 2.0 * w.k * cube
+        if w.backward:
+            f["w0_bwd"] += 2.0 * T * sp.m * sp.n
+            f["block_bwd"] += 2.0 * T * sq
+            f["dq"] += 2.0 * T * sq
+            f["cnp_bwd"] += 4.0 * w.k * cube
+    return f
+
+
+def cpu_baseline(w, tokens: int):
+    """float64 oracle on the workload's own layers: build + forward + backward at
+    0 and `tokens` tokens per layer, extrapolated linearly to the full T."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    fixed = per_tok = 0.0
+    for li in range(len(w.layers)):
+        inp = workloads.layer_inputs(w, li, T=tokens)
+        for T in (0, tokens):
+            sub = type("I", (), dict(spec=inp.spec, W0=inp.W0, theta_R=inp.theta_R,
+                                     theta_P=inp.theta_P, pi_R=inp.pi_R, pi_P=inp.pi_P,
+                                     X=inp.X[:T], G_Y=inp.G_Y[:T]))()
+            t0 = time.perf_counter()
+            oracle.layer_reference(sub, w.k, backward_pass=w.backward)
+            dt = time.perf_counter() - t0
+            if T == 0:
+                t_fixed = dt
+            else:
+                per_tok += max(dt - t_fixed, 0.0) / tokens
+        fixed += t_fixed
+    est = fixed + per_tok * w.T
+    return {
+        "value": w.T / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"float64 NumPy oracle on all {len(w.layers)} layers' own inputs: build + forward + "
+                   f"backward at 0 and {tokens} tokens per layer, extrapolated linearly to "
+                   f"{w.T} tokens (est. {est:.1f} s per step)"),
+        "seconds_per_step_est": est,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, help="workload id in workloads.WORKLOADS")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing pass")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(sharding by tokens is described in DESIGN.md).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from orthogonal_equivalence_cayley_amd import PoetxLayer, poetx
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = workloads.WORKLOADS[args.workload]
+    T = w.T
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(tdt).cuda()
+
+    log(f"bench: {w.name} T={T} layers={len(w.layers)} k={w.k}")
+    layers, bufs = [], []
+    for li in range(len(w.layers)):
+        inp = workloads.layer_inputs(w, li, draw_grad=w.backward)
+        sp = inp.spec
+        L = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, w.k, dtype=w.dtype)
+        L.set_weight(dev(inp.W0), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
+        L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
+        b = dict(X=dev(inp.X), Y=torch.empty(T, sp.m, dtype=tdt, device="cuda"),
+                 Wa=torch.empty(T, sp.m, dtype=tdt, device="cuda"))
+        if w.backward:
+            b.update(G=dev(inp.G_Y), GX=torch.empty(T, sp.n, dtype=tdt, device="cuda"),
+                     g=[torch.empty(L.nparam[s], dtype=torch.float32, device="cuda") for s in (0, 1)])
+        L.workspace(poetx.WS_BUILD)
+        L.workspace(poetx.WS_FORWARD, T)
+        if w.backward:
+            L.workspace(poetx.WS_BACKWARD, T)
+        layers.append(L)
+        bufs.append(b)
+        del inp
+    torch.cuda.synchronize()
+    log("bench: inputs resident")
+
+    def step():
+        for L in layers:
+            L.build()
+        for L, b in zip(layers, bufs):
+            L.forward(b["X"], Y=b["Y"], Wa=b["Wa"])
+        if w.backward:
+            for L, b in zip(reversed(layers), reversed(bufs)):
+                L.backward(b["X"], b["G"], G_X=b["GX"], g_theta=b["g"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("bench: warmup done")
+
+    # timed region: HIP events around the frozen-weight GEMMs only (two
+    # launches per layer), everything else untouched
+    poetx.timing_reset()
+    poetx.timing_enable(["w0_fwd", "w0_bwd"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    poetx.timing_enable([])
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    w0 = {s: poetx.timing_read(s) for s in ("w0_fwd", "w0_bwd")}
+    poetx.timing_reset()
+    log(f"bench: {ms_per_step:.3f} ms/step")
+
+    flops = stage_flops(w, T)
+    stages = {}
+    if not args.no_stages:
+        # separate diagnostic pass: every stage bracketed by events
+        poetx.timing_enable(list(poetx.STAGES))
+        n_diag = max(2, min(5, args.steps))
+        for _ in range(n_diag):
+            step()
+        torch.cuda.synchronize()
+        poetx.timing_enable([])
+        for s in poetx.STAGES:
+            ms, cnt = poetx.timing_read(s)
+            if cnt:
+                stages[s] = {"ms_per_step": ms / n_diag,
+                             "tflops": flops.get(s, 0.0) / (ms / n_diag * 1e-3) / 1e12 if ms else None}
+        poetx.timing_reset()
+
+    # dominant kernel: the frozen-weight GEMM form with the larger time share
+    dom = max(w0, key=lambda s: w0[s][0])
+    ms_tot, launches = w0[dom]
+    kernel = {"w0_fwd": "w0_gemm_nt", "w0_bwd": "w0_gemm_nn"}[dom]
+    flops_per_launch = flops[dom] / len(w.layers)
+    avg_s = ms_tot / launches * 1e-3
+    achieved = flops_per_launch / avg_s
+    gemm_keys = ("w0_fwd", "w0_bwd", "block_fwd", "block_bwd", "dq")
+    gemm_frac = None
+    if stages:
+        gt = sum(stages[s]["ms_per_step"] for s in gemm_keys if s in stages) * 1e-3
+        gemm_frac = sum(flops[s] for s in gemm_keys) / gt / PEAK_BF16 if gt else None
+    w0_total_frac = (flops["w0_fwd"] + flops["w0_bwd"]) / (
+        (w0["w0_fwd"][0] + w0["w0_bwd"][0]) / args.steps * 1e-3) / PEAK_BF16
+
+    out = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "tokens": T, "k": w.k,
+            "layers": [f"{sp.name} {sp.m}x{sp.n}" for sp in w.layers],
+            "block_size": max(max(sp.bsz_R) for sp in w.layers),
+            "passes": "build+forward+backward" if w.backward else "build+forward",
+        },
+        "roofline": {
+            "kernel": kernel, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": None,
+            "launches": launches, "avg_launch_us": avg_s * 1e6,
+            "flops_per_launch": flops_per_launch,
+        },
+        "tflops_per_step": sum(flops.values()) / (ms_per_step * 1e-3) / 1e12,
+        "w0_gemm_mfma_frac": w0_total_frac,
+        "gemm_stage_mfma_frac": gemm_frac,
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -158,6 +158,32 @@ poetx_status poetx_gather_cols(const poetx_plan* plan, int64_t T, int32_t dim, c
 poetx_status poetx_scatter_cols(const poetx_plan* plan, int64_t T, int32_t dim, const void* in,
                                 const int32_t* idx, void* out, void* stream);
 
+/* Optional stage timing for benchmarks. Stage i is timed when bit i of `mask`
+ * is set: every later call records a pair of HIP events on its own stream
+ * around that stage's kernels (event objects are created on demand; no device
+ * memory is allocated). mask = 0 (the default) records nothing. */
+typedef enum {
+  POETX_STAGE_BUILD = 0,      /* poetx_build_orth, whole call                   */
+  POETX_STAGE_GATHER = 1,     /* column gathers (forward and backward)          */
+  POETX_STAGE_BLOCK_FWD = 2,  /* block-diagonal products in the forward         */
+  POETX_STAGE_W0_FWD = 3,     /* Wa = V Wt^T                                    */
+  POETX_STAGE_SCATTER = 4,    /* column scatters (forward and backward)         */
+  POETX_STAGE_DQ = 5,         /* dL/dQ products and their fixed-order reduction  */
+  POETX_STAGE_BLOCK_BWD = 6,  /* block-diagonal products in the backward        */
+  POETX_STAGE_W0_BWD = 7,     /* G_V = G_Wa Wt                                  */
+  POETX_STAGE_CNP_BWD = 8,    /* reverse mode through the Neumann series        */
+  POETX_NUM_STAGES = 9
+} poetx_stage;
+
+poetx_status poetx_timing_enable(uint32_t mask);
+/* Waits for the recorded events of one stage and returns their total time in
+ * milliseconds and the number of recorded intervals since the last reset.
+ * POETX_ERR_INVALID_ARG for a bad stage or NULL outputs; POETX_ERR_HIP if an
+ * event query fails. */
+poetx_status poetx_timing_read(int32_t stage, double* ms, int64_t* count);
+/* Forget all recorded intervals (their events are kept for reuse). */
+void poetx_timing_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

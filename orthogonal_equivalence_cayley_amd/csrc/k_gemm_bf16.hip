@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool OUTF32>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmBf16 p) {
+__device__ __forceinline__ void gemm_body(const GemmBf16& p) {
   static_assert((BM / WM) * (BN / WN) == 4, "four waves per workgroup");
   constexpr int TM = WM / 32, TN = WN / 32;
   __shared__ __align__(16) uint16_t As[2][BM][LDK];
@@ -209,23 +209,50 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmBf16 p) {
   }
 }
 
+// One kernel symbol per role so that profiles attribute time to the stage:
+//   w0_gemm_nt:    Wa = V Wt^T                  (both operands K-contiguous)
+//   w0_gemm_nn:    G_V = G_Wa Wt                (Wt row-contiguous along N)
+//   block_gemm_nt: out[:, blk] = in[:, blk] Q^T
+//   block_gemm_nn: out[:, blk] = in[:, blk] Q
+//   dq_gemm_tn:    dQ partials = G[:, blk]^T A[:, blk], reduced over tokens
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kThreads) void w0_gemm_nt(GemmBf16 p) {
+  gemm_body<BM, BN, WM, WN, true, true, false>(p);
+}
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kThreads) void w0_gemm_nn(GemmBf16 p) {
+  gemm_body<BM, BN, WM, WN, true, false, false>(p);
+}
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kThreads) void block_gemm_nt(GemmBf16 p) {
+  gemm_body<BM, BN, WM, WN, true, true, false>(p);
+}
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kThreads) void block_gemm_nn(GemmBf16 p) {
+  gemm_body<BM, BN, WM, WN, true, false, false>(p);
+}
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kThreads) void dq_gemm_tn(GemmBf16 p) {
+  gemm_body<BM, BN, WM, WN, false, false, true>(p);
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t dispatch(const GemmBf16& p, hipStream_t s) {
   dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, p.groups * p.splits);
-#define POETX_GEMM_CASE(AK, BKM, OF)                                                          \
-  if (p.a_kmajor == AK && p.b_kmajor == BKM && p.out_f32 == OF) {                            \
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, AK, BKM, OF>), grid, dim3(kThreads), \
-                       0, s, p);                                                              \
-    return hipGetLastError();                                                                 \
-  }
-  POETX_GEMM_CASE(1, 1, 0)
-  POETX_GEMM_CASE(1, 0, 0)
-  POETX_GEMM_CASE(0, 0, 1)
-  POETX_GEMM_CASE(1, 1, 1)
-  POETX_GEMM_CASE(1, 0, 1)
-  POETX_GEMM_CASE(0, 0, 0)
-#undef POETX_GEMM_CASE
-  return hipErrorInvalidValue;
+  const int a = p.a_kmajor, b = p.b_kmajor, f = p.out_f32;
+  if (p.role == GEMM_W0 && a && b && !f)
+    hipLaunchKernelGGL((w0_gemm_nt<BM, BN, WM, WN>), grid, dim3(kThreads), 0, s, p);
+  else if (p.role == GEMM_W0 && a && !b && !f)
+    hipLaunchKernelGGL((w0_gemm_nn<BM, BN, WM, WN>), grid, dim3(kThreads), 0, s, p);
+  else if (p.role == GEMM_BLOCK && a && b && !f)
+    hipLaunchKernelGGL((block_gemm_nt<BM, BN, WM, WN>), grid, dim3(kThreads), 0, s, p);
+  else if (p.role == GEMM_BLOCK && a && !b && !f)
+    hipLaunchKernelGGL((block_gemm_nn<BM, BN, WM, WN>), grid, dim3(kThreads), 0, s, p);
+  else if (p.role == GEMM_DQ && !a && !b && f)
+    hipLaunchKernelGGL((dq_gemm_tn<BM, BN, WM, WN>), grid, dim3(kThreads), 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -28,6 +30,55 @@ struct poetx_plan {
 namespace {
 
 constexpr size_t kAlign = 256;
+
+// ------------------------------------------------------------------ stage timing
+std::atomic<uint32_t> g_tmask{0};
+std::mutex g_tmu;
+struct TimingRec {
+  int stage;
+  hipEvent_t a, b;
+};
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pooled_event() {
+  hipEvent_t e = nullptr;
+  if (!g_pool.empty()) {
+    e = g_pool.back();
+    g_pool.pop_back();
+  } else if (hipEventCreate(&e) != hipSuccess) {
+    e = nullptr;
+  }
+  return e;
+}
+
+// Records HIP events around the kernels of one stage when its timing bit is set.
+struct StageScope {
+  int stage;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  StageScope(int st, hipStream_t str) : stage(st), s(str) {
+    if (g_tmask.load(std::memory_order_relaxed) & (1u << st)) {
+      std::lock_guard<std::mutex> lk(g_tmu);
+      a = pooled_event();
+      if (a && hipEventRecord(a, s) != hipSuccess) {
+        g_pool.push_back(a);
+        a = nullptr;
+      }
+    }
+  }
+  ~StageScope() {
+    if (!a) return;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    hipEvent_t b = pooled_event();
+    if (b && hipEventRecord(b, s) == hipSuccess) {
+      g_recs.push_back(TimingRec{stage, a, b});
+    } else {
+      g_pool.push_back(a);
+      if (b) g_pool.push_back(b);
+    }
+  }
+};
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -132,12 +183,13 @@ struct Op {
 };
 
 // C(m, n) = sum_k A(m, k) B(n, k) in the plan's dtype (fp32 output when out_f32).
-poetx_status gemm(const poetx_plan* pl, Op A, Op B, void* C, long long ldc, int M, int N, int K,
-                  int groups, long long a_gs, long long b_gs, long long c_gs, int splits,
+poetx_status gemm(const poetx_plan* pl, int role, Op A, Op B, void* C, long long ldc, int M, int N,
+                  int K, int groups, long long a_gs, long long b_gs, long long c_gs, int splits,
                   long long c_ss, bool out_f32, hipStream_t s) {
   if (pl->dtype == POETX_BF16) {
     poetx::GemmBf16 g;
     g.A = A.p; g.B = B.p; g.C = C;
+    g.role = role;
     g.M = M; g.N = N; g.K = K;
     g.a_kmajor = A.cs == 1;
     g.b_kmajor = B.cs == 1;
@@ -192,7 +244,7 @@ poetx_status apply_blocks(const poetx_plan* pl, int side, long long T, const voi
     char* c = static_cast<char*>(out) + es * g.dim_off;
     // transpose_q: B(n, k) = Q[n][k]; otherwise B(n, k) = Q[k][n]
     Op B = transpose_q ? Op{q, g.b, 1} : Op{q, 1, g.b};
-    poetx_status st = gemm(pl, Op{a, dim, 1}, B, c, dim, (int)T, g.b, g.b, g.count, g.b,
+    poetx_status st = gemm(pl, poetx::GEMM_BLOCK, Op{a, dim, 1}, B, c, dim, (int)T, g.b, g.b, g.count, g.b,
                            (long long)g.b * g.b, g.b, 1, 0, false, s);
     if (st != POETX_OK) return st;
   }
@@ -210,7 +262,7 @@ poetx_status block_grads(const poetx_plan* pl, int side, long long T, const void
     const char* a = static_cast<const char*>(G) + es * g.dim_off;
     const char* b = static_cast<const char*>(A) + es * g.dim_off;
     // rows of the product index features, k indexes tokens
-    poetx_status st = gemm(pl, Op{a, 1, dim}, Op{b, 1, dim}, part + g.q_off, g.b, g.b, g.b,
+    poetx_status st = gemm(pl, poetx::GEMM_DQ, Op{a, 1, dim}, Op{b, 1, dim}, part + g.q_off, g.b, g.b, g.b,
                            (int)T, g.count, g.b, g.b, (long long)g.b * g.b, splits, ne, true, s);
     if (st != POETX_OK) return st;
   }
@@ -357,6 +409,7 @@ poetx_status poetx_build_orth(const poetx_plan* pl, int32_t side, const float* t
     return POETX_ERR_ALIGNMENT;
   if (!ws || ws_bytes < poetx_workspace_size(pl, 0, POETX_WS_BUILD)) return POETX_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  StageScope sc(POETX_STAGE_BUILD, s);
   float *S, *P0, *P1;
   layout_build(pl, ws, &S, &P0, &P1);
   const int k = pl->k;
@@ -395,17 +448,32 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
   const int es = elsize(pl);
   poetx_status st;
   // 1. gather: U = X Pi_P^T
-  HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
+  {
+    StageScope sc(POETX_STAGE_GATHER, s);
+    HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
+  }
   // 2. blocks of P: V = U D_P^T
-  if ((st = apply_blocks(pl, POETX_SIDE_P, T, w.U, Q_P, w.V, true, s)) != POETX_OK) return st;
+  {
+    StageScope sc(POETX_STAGE_BLOCK_FWD, s);
+    if ((st = apply_blocks(pl, POETX_SIDE_P, T, w.U, Q_P, w.V, true, s)) != POETX_OK) return st;
+  }
   // 3. frozen weight: Wa = V Wt^T
-  if ((st = gemm(pl, Op{w.V, pl->n, 1}, Op{Wt, pl->n, 1}, Wa, pl->m, (int)T, pl->m, pl->n, 1, 0,
-                 0, 0, 1, 0, false, s)) != POETX_OK)
-    return st;
+  {
+    StageScope sc(POETX_STAGE_W0_FWD, s);
+    if ((st = gemm(pl, poetx::GEMM_W0, Op{w.V, pl->n, 1}, Op{Wt, pl->n, 1}, Wa, pl->m, (int)T, pl->m,
+                   pl->n, 1, 0, 0, 0, 1, 0, false, s)) != POETX_OK)
+      return st;
+  }
   // 4. blocks of R: Z = Wa D_R^T
-  if ((st = apply_blocks(pl, POETX_SIDE_R, T, Wa, Q_R, w.Z, true, s)) != POETX_OK) return st;
+  {
+    StageScope sc(POETX_STAGE_BLOCK_FWD, s);
+    if ((st = apply_blocks(pl, POETX_SIDE_R, T, Wa, Q_R, w.Z, true, s)) != POETX_OK) return st;
+  }
   // 5. scatter: Y = Z Pi_R
-  HIP_TRY(poetx::launch_scatter_cols(w.Z, pi_R, Y, T, pl->m, es, s));
+  {
+    StageScope sc(POETX_STAGE_SCATTER, s);
+    HIP_TRY(poetx::launch_scatter_cols(w.Z, pi_R, Y, T, pl->m, es, s));
+  }
   return POETX_OK;
 }
 
@@ -430,23 +498,49 @@ poetx_status poetx_backward(const poetx_plan* pl, int64_t T, const void* X, cons
   poetx_status st;
   if (T > 0) {
     // R side: G_Z = G_Y Pi_R^T; dQ_R = G_Z^T Wa per block; G_Wa = G_Z D_R
-    HIP_TRY(poetx::launch_gather_cols(G_Y, pl->m, nullptr, pi_R, w.GZ, T, pl->m, es, s));
-    if ((st = block_grads(pl, POETX_SIDE_R, T, w.GZ, Wa_saved, w.part, w.dQ[0], s)) != POETX_OK)
-      return st;
-    if ((st = apply_blocks(pl, POETX_SIDE_R, T, w.GZ, Q_R, w.GWa, false, s)) != POETX_OK) return st;
+    {
+      StageScope sc(POETX_STAGE_GATHER, s);
+      HIP_TRY(poetx::launch_gather_cols(G_Y, pl->m, nullptr, pi_R, w.GZ, T, pl->m, es, s));
+    }
+    {
+      StageScope sc(POETX_STAGE_DQ, s);
+      if ((st = block_grads(pl, POETX_SIDE_R, T, w.GZ, Wa_saved, w.part, w.dQ[0], s)) != POETX_OK)
+        return st;
+    }
+    {
+      StageScope sc(POETX_STAGE_BLOCK_BWD, s);
+      if ((st = apply_blocks(pl, POETX_SIDE_R, T, w.GZ, Q_R, w.GWa, false, s)) != POETX_OK) return st;
+    }
     // frozen weight: G_V = G_Wa Wt
-    if ((st = gemm(pl, Op{w.GWa, pl->m, 1}, Op{Wt, 1, pl->n}, w.GV, pl->n, (int)T, pl->n, pl->m, 1,
-                   0, 0, 0, 1, 0, false, s)) != POETX_OK)
-      return st;
+    {
+      StageScope sc(POETX_STAGE_W0_BWD, s);
+      if ((st = gemm(pl, poetx::GEMM_W0, Op{w.GWa, pl->m, 1}, Op{Wt, 1, pl->n}, w.GV, pl->n, (int)T,
+                     pl->n, pl->m, 1, 0, 0, 0, 1, 0, false, s)) != POETX_OK)
+        return st;
+    }
     // P side: U = X Pi_P^T; dQ_P = G_V^T U per block; G_U = G_V D_P; G_X = G_U Pi_P
-    HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
-    if ((st = block_grads(pl, POETX_SIDE_P, T, w.GV, w.U, w.part, w.dQ[1], s)) != POETX_OK) return st;
-    if ((st = apply_blocks(pl, POETX_SIDE_P, T, w.GV, Q_P, w.GU, false, s)) != POETX_OK) return st;
-    HIP_TRY(poetx::launch_scatter_cols(w.GU, pi_P, G_X, T, pl->n, es, s));
+    {
+      StageScope sc(POETX_STAGE_GATHER, s);
+      HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
+    }
+    {
+      StageScope sc(POETX_STAGE_DQ, s);
+      if ((st = block_grads(pl, POETX_SIDE_P, T, w.GV, w.U, w.part, w.dQ[1], s)) != POETX_OK)
+        return st;
+    }
+    {
+      StageScope sc(POETX_STAGE_BLOCK_BWD, s);
+      if ((st = apply_blocks(pl, POETX_SIDE_P, T, w.GV, Q_P, w.GU, false, s)) != POETX_OK) return st;
+    }
+    {
+      StageScope sc(POETX_STAGE_SCATTER, s);
+      HIP_TRY(poetx::launch_scatter_cols(w.GU, pi_P, G_X, T, pl->n, es, s));
+    }
   } else {
     HIP_TRY(poetx::launch_zero(w.dQ[0], pl->nelem[0], s));
     HIP_TRY(poetx::launch_zero(w.dQ[1], pl->nelem[1], s));
   }
+  StageScope sc(POETX_STAGE_CNP_BWD, s);
   if ((st = cnp_backward(pl, POETX_SIDE_R, theta_R, w.dQ[0], g_theta_R, w.S, w.A0, w.A1, w.T0,
                          w.T1, s)) != POETX_OK)
     return st;
@@ -471,6 +565,38 @@ poetx_status poetx_scatter_cols(const poetx_plan* pl, int64_t T, int32_t dim, co
   if (!aligned16(in) || !aligned16(out) || !aligned16(idx)) return POETX_ERR_ALIGNMENT;
   HIP_TRY(poetx::launch_scatter_cols(in, idx, out, T, dim, elsize(pl), (hipStream_t)stream));
   return POETX_OK;
+}
+
+poetx_status poetx_timing_enable(uint32_t mask) {
+  g_tmask.store(mask & ((1u << POETX_NUM_STAGES) - 1u));
+  return POETX_OK;
+}
+
+poetx_status poetx_timing_read(int32_t stage, double* ms, int64_t* count) {
+  if (stage < 0 || stage >= POETX_NUM_STAGES || !ms || !count) return POETX_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  double tot = 0.0;
+  int64_t n = 0;
+  for (const TimingRec& r : g_recs) {
+    if (r.stage != stage) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return POETX_ERR_HIP;
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return POETX_ERR_HIP;
+    tot += t;
+    ++n;
+  }
+  *ms = tot;
+  *count = n;
+  return POETX_OK;
+}
+
+void poetx_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (const TimingRec& r : g_recs) {
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
 }
 
 }  // extern "C"

@@ -62,8 +62,10 @@ hipError_t launch_gemm_f32(const GemmF32& p, hipStream_t s);
 // A(m,k) = A[m*lda + k] when a_kmajor, else A[k*lda + m]; same for B with ldb.
 // Output bf16 (out_f32 = 0) or fp32; C(m,n) at C[m*ldc + n]. Batched over groups
 // and split over K like GemmF32.
+enum GemmRole { GEMM_BLOCK = 0, GEMM_W0 = 1, GEMM_DQ = 2 };
 struct GemmBf16 {
   const void* A; const void* B; void* C;
+  int role;   // GemmRole: selects the kernel symbol (layouts must match the role)
   int M, N, K;
   long long lda, ldb, ldc;
   int a_kmajor, b_kmajor, out_f32;

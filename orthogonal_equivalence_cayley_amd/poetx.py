@@ -35,8 +35,11 @@ EXPORTED = (
     "poetx_plan_create", "poetx_plan_destroy", "poetx_param_count", "poetx_block_elems",
     "poetx_workspace_size", "poetx_status_string", "poetx_permute_weight",
     "poetx_build_orth", "poetx_forward", "poetx_backward", "poetx_gather_cols",
-    "poetx_scatter_cols",
+    "poetx_scatter_cols", "poetx_timing_enable", "poetx_timing_read", "poetx_timing_reset",
 )
+
+STAGES = ("build", "gather", "block_fwd", "w0_fwd", "scatter", "dq", "block_bwd", "w0_bwd",
+          "cnp_bwd")
 
 
 class PoetxError(RuntimeError):
@@ -74,6 +77,9 @@ def _load() -> ctypes.CDLL:
                                 vp, sz, vp]),
         "poetx_gather_cols": (st, [vp, i64, i32, vp, vp, vp, vp]),
         "poetx_scatter_cols": (st, [vp, i64, i32, vp, vp, vp, vp]),
+        "poetx_timing_enable": (st, [ctypes.c_uint32]),
+        "poetx_timing_read": (st, [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+        "poetx_timing_reset": (None, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -108,6 +114,26 @@ def _stream(stream) -> Optional[int]:
         return stream if isinstance(stream, int) else stream.cuda_stream
     import torch
     return torch.cuda.current_stream().cuda_stream
+
+
+def timing_enable(stages) -> None:
+    """Record HIP events around the named stages of every later call."""
+    mask = 0
+    for name in stages:
+        mask |= 1 << STAGES.index(name)
+    _check(LIB.poetx_timing_enable(mask), "poetx_timing_enable")
+
+
+def timing_read(stage: str):
+    """(total milliseconds, number of intervals) recorded for one stage."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(LIB.poetx_timing_read(STAGES.index(stage), ctypes.byref(ms), ctypes.byref(n)),
+           "poetx_timing_read")
+    return ms.value, n.value
+
+
+def timing_reset() -> None:
+    LIB.poetx_timing_reset()
 
 
 class Plan:
