@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void unpack_skew_kernel(
 
 __global__ __launch_bounds__(kThreads) void pack_antisym_kernel(
     const float* __restrict__ Sbar, int b, int count, long long q_off, long long p_off,
-    float* __restrict__ g) {
+    float sign, float* __restrict__ g) {
   const long long bb = (long long)b * b;
   const long long np = (long long)b * (b - 1) / 2;
   const long long total = bb * count;
@@ -54,7 +54,8 @@ __global__ __launch_bounds__(kThreads) void pack_antisym_kernel(
     const int c = (int)(e - blk * bb - (long long)r * b);
     if (r < c) {
       const float* M = Sbar + q_off + blk * bb;
-      g[p_off + blk * np + tri_index(r, c, b)] = M[(long long)r * b + c] - M[(long long)c * b + r];
+      g[p_off + blk * np + tri_index(r, c, b)] =
+          sign * (M[(long long)r * b + c] - M[(long long)c * b + r]);
     }
   }
 }
@@ -111,10 +112,11 @@ hipError_t launch_unpack_skew(const float* theta, const Seg& g, float* S, float*
   return hipGetLastError();
 }
 
-hipError_t launch_pack_antisym(const float* Sbar, const Seg& g, float* gtheta, hipStream_t s) {
+hipError_t launch_pack_antisym(const float* M, const Seg& g, float sign, float* gtheta,
+                               hipStream_t s) {
   const long long total = (long long)g.b * g.b * g.count;
-  hipLaunchKernelGGL(pack_antisym_kernel, dim3(grid1d(total)), dim3(kThreads), 0, s, Sbar, g.b,
-                     g.count, g.q_off, g.p_off, gtheta);
+  hipLaunchKernelGGL(pack_antisym_kernel, dim3(grid1d(total)), dim3(kThreads), 0, s, M, g.b,
+                     g.count, g.q_off, g.p_off, sign, gtheta);
   return hipGetLastError();
 }
 

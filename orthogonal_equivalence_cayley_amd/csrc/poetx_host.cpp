@@ -121,7 +121,7 @@ int dq_splits(const poetx_plan* pl, int side, long long T) {
 struct FwdWs { void *U, *V, *Wa, *Z; };
 struct BwdWs {
   void *GZ, *GWa, *GV, *U, *GU;
-  float *dQ[2], *part, *S, *A0, *A1, *T0, *T1;
+  float *dQ[2], *part, *S, *A0, *A1, *T0, *T1, *Astore;
 };
 
 size_t layout_fwd(const poetx_plan* pl, long long T, void* base, FwdWs* w) {
@@ -157,6 +157,7 @@ size_t layout_bwd(const poetx_plan* pl, long long T, void* base, BwdWs* w) {
   x.A1 = (float*)c.take(4 * ne);
   x.T0 = (float*)c.take(4 * ne);
   x.T1 = (float*)c.take(4 * ne);
+  x.Astore = (float*)c.take(4 * ne * (pl->k + 1));
   if (w) *w = x;
   return c.off;
 }
@@ -276,14 +277,32 @@ poetx_status block_grads(const poetx_plan* pl, int side, long long T, const void
 // then dL/dtheta(i,j) = dS[i][j] - dS[j][i]. Uses S^T = -S.
 poetx_status cnp_backward(const poetx_plan* pl, int side, const float* theta, const float* G,
                           float* gtheta, float* S, float* A0, float* A1, float* T0, float* T1,
-                          hipStream_t s) {
+                          float* Astore, hipStream_t s) {
   const int k = pl->k;
   const long long ne = pl->nelem[side];
   for (const Seg& g : pl->segs[side]) HIP_TRY(poetx::launch_unpack_skew(theta, g, S, nullptr, 0.0f, s));
-  HIP_TRY(poetx::launch_scale2(G, coef(k + 1, k), A0, T0, ne, s));
-  float *Acur = A0, *Anew = A1, *Tcur = T0, *Tnew = T1;
+  bool any_generic = false;
+  for (const Seg& g : pl->segs[side]) {
+    if (!poetx::chain_supported(g.b)) {
+      any_generic = true;
+      continue;
+    }
+    // row-local first chain, then the transposed second chain, then pack
+    poetx::ChainArgs c;
+    c.S = S; c.G = G; c.out_f32 = Astore; c.out_act = nullptr; c.act_bf16 = 0;
+    c.b = g.b; c.count = g.count; c.k = k; c.q_off = g.q_off; c.ne = ne;
+    HIP_TRY(poetx::launch_chain(poetx::CHAIN_ABAR, c, s));
+    c.G = Astore; c.out_f32 = T0;
+    HIP_TRY(poetx::launch_chain(poetx::CHAIN_TCHAIN, c, s));
+    HIP_TRY(poetx::launch_pack_antisym(T0, g, -1.0f, gtheta, s));
+  }
+  if (!any_generic) return POETX_OK;
+  // blocks whose size the MFMA chain does not take: batched fp32 GEMM per step
+  HIP_TRY(poetx::launch_scale2(G, coef(k + 1, k), A0, T1, ne, s));
+  float *Acur = A0, *Anew = A1, *Tcur = T1, *Tnew = T0;
   for (int j = k; j >= 1; --j) {
     for (const Seg& g : pl->segs[side]) {
+      if (poetx::chain_supported(g.b)) continue;
       // A_j = c_j G - A_{j+1} S
       poetx_status st = chain_gemm(g, Acur, S, Anew, G, nullptr, -1.0f, coef(j, k), s);
       if (st != POETX_OK) return st;
@@ -294,7 +313,8 @@ poetx_status cnp_backward(const poetx_plan* pl, int side, const float* theta, co
     std::swap(Acur, Anew);
     std::swap(Tcur, Tnew);
   }
-  for (const Seg& g : pl->segs[side]) HIP_TRY(poetx::launch_pack_antisym(Tcur, g, gtheta, s));
+  for (const Seg& g : pl->segs[side])
+    if (!poetx::chain_supported(g.b)) HIP_TRY(poetx::launch_pack_antisym(Tcur, g, 1.0f, gtheta, s));
   return POETX_OK;
 }
 
@@ -413,20 +433,32 @@ poetx_status poetx_build_orth(const poetx_plan* pl, int32_t side, const float* t
   float *S, *P0, *P1;
   layout_build(pl, ws, &S, &P0, &P1);
   const int k = pl->k;
-  for (const Seg& g : pl->segs[side])
+  const bool bf16 = pl->dtype == POETX_BF16;
+  const int es = elsize(pl);
+  for (const Seg& g : pl->segs[side]) {
+    if (poetx::chain_supported(g.b)) {
+      // one fused kernel per run of blocks: S -> powers -> Q (fp32 and act copy)
+      HIP_TRY(poetx::launch_unpack_skew(theta, g, S, nullptr, 0.0f, s));
+      poetx::ChainArgs c;
+      c.S = S; c.G = nullptr; c.out_f32 = Q_f32; c.out_act = Q_act; c.act_bf16 = bf16;
+      c.b = g.b; c.count = g.count; c.k = k; c.q_off = g.q_off; c.ne = pl->nelem[side];
+      HIP_TRY(poetx::launch_chain(poetx::CHAIN_BUILD, c, s));
+      continue;
+    }
     HIP_TRY(poetx::launch_unpack_skew(theta, g, S, Q_f32, coef(1, k), s));
-  // powers S^j = S^{j-1} S for j = 2..k+1, each added into Q with weight c_j
-  const float* prev = S;
-  float* bufs[2] = {P0, P1};
-  for (int j = 2; j <= k + 1; ++j) {
-    float* next = (j < k + 1) ? bufs[j & 1] : nullptr;
-    for (const Seg& g : pl->segs[side]) {
+    // powers S^j = S^{j-1} S for j = 2..k+1, each added into Q with weight c_j
+    const float* prev = S;
+    float* bufs[2] = {P0, P1};
+    for (int j = 2; j <= k + 1; ++j) {
+      float* next = (j < k + 1) ? bufs[j & 1] : nullptr;
       poetx_status st = chain_gemm(g, prev, S, Q_f32, Q_f32, next, coef(j, k), 1.0f, s);
       if (st != POETX_OK) return st;
+      prev = next;
     }
-    prev = next;
+    if (Q_act)
+      HIP_TRY(poetx::launch_cast(Q_f32 + g.q_off, static_cast<char*>(Q_act) + es * g.q_off,
+                                 (long long)g.b * g.b * g.count, bf16, s));
   }
-  if (Q_act) HIP_TRY(poetx::launch_cast(Q_f32, Q_act, pl->nelem[side], pl->dtype == POETX_BF16, s));
   return POETX_OK;
 }
 
@@ -542,9 +574,10 @@ poetx_status poetx_backward(const poetx_plan* pl, int64_t T, const void* X, cons
   }
   StageScope sc(POETX_STAGE_CNP_BWD, s);
   if ((st = cnp_backward(pl, POETX_SIDE_R, theta_R, w.dQ[0], g_theta_R, w.S, w.A0, w.A1, w.T0,
-                         w.T1, s)) != POETX_OK)
+                         w.T1, w.Astore, s)) != POETX_OK)
     return st;
-  return cnp_backward(pl, POETX_SIDE_P, theta_P, w.dQ[1], g_theta_P, w.S, w.A0, w.A1, w.T0, w.T1, s);
+  return cnp_backward(pl, POETX_SIDE_P, theta_P, w.dQ[1], g_theta_P, w.S, w.A0, w.A1, w.T0, w.T1,
+                      w.Astore, s);
 }
 
 poetx_status poetx_gather_cols(const poetx_plan* pl, int64_t T, int32_t dim, const void* in,

@@ -29,8 +29,9 @@ hipError_t launch_scatter_cols(const void* in, const int32_t* idx, void* out, lo
 // S = skew(theta) for every block of the run; if Q != nullptr also Q = I + c1 * S.
 hipError_t launch_unpack_skew(const float* theta, const Seg& g, float* S, float* Q, float c1,
                               hipStream_t s);
-// g[(i,j)] = Sbar[i][j] - Sbar[j][i] for i < j, packed like theta.
-hipError_t launch_pack_antisym(const float* Sbar, const Seg& g, float* gtheta, hipStream_t s);
+// g[(i,j)] = sign * (M[i][j] - M[j][i]) for i < j, packed like theta.
+hipError_t launch_pack_antisym(const float* M, const Seg& g, float sign, float* gtheta,
+                               hipStream_t s);
 // out = (to_bf16 ? bf16 : fp32) copy of n floats.
 hipError_t launch_cast(const float* in, void* out, long long n, int to_bf16, hipStream_t s);
 // out1 = c * in; out2 = c * in (out2 may be null)
@@ -74,5 +75,21 @@ struct GemmBf16 {
   long long c_ss;
 };
 hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
+
+// ---------------------------------------------------------------- fp32 MFMA chains
+// Row-panel power chains over one run of equal blocks (see k_chain.hip).
+enum ChainMode { CHAIN_BUILD = 0, CHAIN_ABAR = 1, CHAIN_TCHAIN = 2 };
+struct ChainArgs {
+  const float* S;     // side's skew generators, fp32 [ne]
+  const float* G;     // ABAR: dL/dQ [ne]; TCHAIN: stored A_j, [(k+1) * ne]
+  float* out_f32;     // BUILD: Q [ne]; ABAR: A_j store [(k+1) * ne]; TCHAIN: T_1^T [ne]
+  void* out_act;      // BUILD: Q copy in the activation dtype, or null
+  int act_bf16;
+  int b, count, k;
+  long long q_off;    // run offset inside the side arrays
+  long long ne;       // side elements (stride of the A_j store)
+};
+bool chain_supported(int b);
+hipError_t launch_chain(int mode, const ChainArgs& p, hipStream_t s);
 
 }  // namespace poetx
