@@ -188,7 +188,7 @@ def main() -> int:
     # dominant kernel: the frozen-weight GEMM form with the larger time share
     dom = max(w0, key=lambda s: w0[s][0])
     ms_tot, launches = w0[dom]
-    kernel = {"w0_fwd": "w0_gemm_nt", "w0_bwd": "w0_gemm_nn"}[dom]
+    kernel = {"w0_fwd": "w0_gemm_nt_lds", "w0_bwd": "w0_gemm_nn_lds"}[dom]
     flops_per_launch = flops[dom] / len(w.layers)
     avg_s = ms_tot / launches * 1e-3
     achieved = flops_per_launch / avg_s

@@ -260,7 +260,11 @@ hipError_t dispatch(const GemmBf16& p, hipStream_t s) {
 hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || p.groups <= 0) return hipSuccess;
   const long long big_tiles = (long long)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.groups * p.splits;
-  if (big_tiles >= 256) return dispatch<256, 256, 128, 128>(p, s);
+  const bool big = big_tiles >= 256;
+  // whole-tile shapes take the pipelined direct-to-LDS kernels; the rest (K not a
+  // multiple of 64, partial tiles of row-contiguous operands) the kernels here
+  if (gemm_lds_supported(p, big ? 256 : 128, big ? 256 : 128)) return launch_gemm_lds(p, big, s);
+  if (big) return dispatch<256, 256, 128, 128>(p, s);
   return dispatch<128, 128, 64, 64>(p, s);
 }
 

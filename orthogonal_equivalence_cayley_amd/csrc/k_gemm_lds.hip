@@ -1,0 +1,340 @@
+// Pipelined bf16 GEMM for gfx950 (v_mfma_f32_32x32x16_bf16, fp32 accumulate)
+// used for the frozen-weight products and the batched block-diagonal products
+// when the shapes are whole tiles ([PX] = page "POET-X: Memory-efficient LLM
+// Training by Scaling Orthogonal Transformation", Résumé technique §2.A, §2.C).
+//
+// C(m,n) = sum_k A(m,k) B(n,k); each operand is K-contiguous ([rows, K]) or
+// row-contiguous ([K, rows]).
+//
+//  * Tiles move HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4):
+//    no staging registers, two LDS stages, the next K tile in flight while the
+//    current one is multiplied.
+//  * A K-contiguous tile is stored as rows of LBK elements; a row-contiguous tile
+//    as LBK rows of R elements. Each is XOR-swizzled in 16-byte units (the lane ->
+//    address mapping of the loads picks the destination) so that fragment reads
+//    hit distinct banks.
+//  * Fragments: K-contiguous tiles are read with ds_read_b128; row-contiguous
+//    tiles with two ds_read_b64_tr_b16 (the gfx950 transposing LDS read: within
+//    16 lanes, lane p receives column p of a 4 x 16 block) per 8-element operand.
+//  * 8 waves (two per SIMD), each owning a 128 x 64 (or 64 x 64) piece of the
+//    tile. Workgroups are dealt to the 8 XCDs round-robin; each XCD gets a
+//    contiguous range of tiles walked in groups of 4 tile-rows, so its resident
+//    workgroups share A and B slices in that XCD's L2.
+//
+// Requirements (checked by the dispatcher): K % 64 == 0; M % BM == 0 when A is
+// row-contiguous and N % BN == 0 when B is; 16-byte aligned rows. Rows past M or
+// N of a K-contiguous operand are clamped (their results are not stored).
+#include "poetx_internal.h"
+
+namespace poetx {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int LBK = 64;
+constexpr int GM = 4;   // tile-rows per group in the XCD-aware order
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Barrier that waits for this wave's LDS traffic only: the direct-to-LDS loads
+// of later stages stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
+}
+
+// ---- K-contiguous operand: R rows x 64 elements, 8 chunks of 16 B per row.
+// Chunk c of row r sits at 16-byte slot r * 8 + (c ^ ((r >> 1) & 7)): the 16 rows
+// read by one quarter-wave then cover all 64 banks.
+template <int R, int NT>
+struct KTile {
+  static constexpr int SLOTS = R * 8;
+  static constexpr int L = SLOTS / NT;   // loads per thread per stage
+  const uint16_t* src[L];
+  __device__ __forceinline__ void init(const uint16_t* base, long long ld, int row0, int rows) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int s = i * NT + threadIdx.x;
+      const int r = s >> 3, pos = s & 7;
+      const int c = pos ^ ((r >> 1) & 7);
+      const int gr = min(row0 + r, rows - 1);
+      src[i] = base + (long long)gr * ld + c * 8;
+    }
+  }
+  __device__ __forceinline__ void issue(unsigned char* st, int k0, int wave) const {
+#pragma unroll
+    for (int i = 0; i < L; ++i) dma16(src[i] + k0, st + (i * NT + wave * 64) * 16);
+  }
+  // 8 K-consecutive elements of row r at k = 16 * kk + 8 * half
+  __device__ __forceinline__ static bf16x8 frag(const unsigned char* st, int r, int kk, int half) {
+    const int c = 2 * kk + half;
+    return *reinterpret_cast<const bf16x8*>(st + (r * 8 + (c ^ ((r >> 1) & 7))) * 16);
+  }
+};
+
+// ---- row-contiguous operand: 64 K-rows x R elements (R / 8 chunks per K-row).
+// Chunk c of K-row k sits at slot k * (R / 8) + (c ^ (4 * (k & 3))): the 4 K-rows x
+// 4 chunks touched by 32 lanes of a transposing read fall in distinct banks.
+template <int R, int NT>
+struct MTile {
+  static constexpr int CPR = R / 8;
+  static constexpr int SLOTS = LBK * CPR;
+  static constexpr int L = SLOTS / NT;
+  const uint16_t* src[L];
+  __device__ __forceinline__ void init(const uint16_t* base, long long ld, int col0) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int s = i * NT + threadIdx.x;
+      const int k = s / CPR, pos = s % CPR;
+      const int c = pos ^ (4 * (k & 3));
+      src[i] = base + (long long)k * ld + col0 + c * 8;
+    }
+  }
+  __device__ __forceinline__ void issue(unsigned char* st, int k0, long long ld, int wave) const {
+#pragma unroll
+    for (int i = 0; i < L; ++i) dma16(src[i] + (long long)k0 * ld, st + (i * NT + wave * 64) * 16);
+  }
+  // operand for MFMA rows r0 .. r0 + 31 (lane & 31), k = 16 * kk + 8 * (lane >> 5) + 0..7
+  __device__ __forceinline__ static bf16x8 frag(const unsigned char* st, int r0, int kk, int lane) {
+    const int g = lane >> 4;                // 16-lane group
+    const int s = lane & 15;                // source lane inside the group
+    const int col = r0 + (g & 1) * 16 + 4 * (s & 3);
+    const int kb = 16 * kk + 8 * (g >> 1) + (s >> 2);
+    i16x4 lo, hi;
+    {
+      const int k = kb;
+      const int c = (col >> 3) ^ (4 * (k & 3));
+      lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(st + (k * CPR + c) * 16 + (col & 7) * 2));
+    }
+    {
+      const int k = kb + 4;
+      const int c = (col >> 3) ^ (4 * (k & 3));
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(st + (k * CPR + c) * 16 + (col & 7) * 2));
+    }
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+template <int R, int NT, bool KMAJ>
+struct Tile;
+template <int R, int NT>
+struct Tile<R, NT, true> {
+  KTile<R, NT> t;
+  static constexpr int BYTES = KTile<R, NT>::SLOTS * 16;
+  static constexpr int L = KTile<R, NT>::L;
+  __device__ __forceinline__ void init(const uint16_t* base, long long ld, int row0, int rows) {
+    t.init(base, ld, row0, rows);
+  }
+  __device__ __forceinline__ void issue(unsigned char* st, int k0, long long, int wave) const {
+    t.issue(st, k0, wave);
+  }
+  __device__ __forceinline__ static bf16x8 frag(const unsigned char* st, int r0, int kk, int lane) {
+    return KTile<R, NT>::frag(st, r0 + (lane & 31), kk, lane >> 5);
+  }
+};
+template <int R, int NT>
+struct Tile<R, NT, false> {
+  MTile<R, NT> t;
+  static constexpr int BYTES = MTile<R, NT>::SLOTS * 16;
+  static constexpr int L = MTile<R, NT>::L;
+  __device__ __forceinline__ void init(const uint16_t* base, long long ld, int row0, int) {
+    t.init(base, ld, row0);
+  }
+  __device__ __forceinline__ void issue(unsigned char* st, int k0, long long ld, int wave) const {
+    t.issue(st, k0, ld, wave);
+  }
+  __device__ __forceinline__ static bf16x8 frag(const unsigned char* st, int r0, int kk, int lane) {
+    return MTile<R, NT>::frag(st, r0, kk, lane);
+  }
+};
+
+__device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
+  const __bf16 a = static_cast<__bf16>(lo);
+  const __bf16 b = static_cast<__bf16>(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool OUTF32>
+__device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
+  constexpr int NW = (BM / WM) * (BN / WN);
+  constexpr int NT = NW * 64;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  using TA = Tile<BM, NT, AK>;
+  using TB = Tile<BN, NT, BKM>;
+  constexpr int STAGE = TA::BYTES + TB::BYTES;
+  constexpr int LOADS = TA::L + TB::L;   // direct-to-LDS loads per thread per stage
+  extern __shared__ __align__(16) unsigned char lds[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm0 = (wave / (BN / WN)) * WM;
+  const int wn0 = (wave % (BN / WN)) * WN;
+
+  // XCD-aware tile order inside one group of the batch (blockIdx.z)
+  const int tn = gridDim.x, tm = gridDim.y, ntile = tn * tm;
+  int lin = blockIdx.y * tn + blockIdx.x;
+  if (ntile % 8 == 0) lin = (lin % 8) * (ntile / 8) + lin / 8;
+  const int grp = lin / (GM * tn);
+  const int first = grp * GM;
+  const int gsz = min(GM, tm - first);
+  const int in = lin - grp * GM * tn;
+  const int m0 = (first + in % gsz) * BM;
+  const int n0 = (in / gsz) * BN;
+
+  const int g = blockIdx.z / p.splits, sp = blockIdx.z - g * p.splits;
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + g * p.a_gs;
+  const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + g * p.b_gs;
+  int kchunk = (p.K + p.splits - 1) / p.splits;
+  kchunk = (kchunk + LBK - 1) / LBK * LBK;
+  const int kbeg = sp * kchunk;
+  const int kend = min(p.K, kbeg + kchunk);
+  const int nk = kend > kbeg ? (kend - kbeg) / LBK : 0;
+
+  TA ta;
+  TB tb;
+  ta.init(A, p.lda, m0, p.M);
+  tb.init(B, p.ldb, n0, p.N);
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  if (nk > 0) {
+    ta.issue(lds, kbeg, p.lda, wave);
+    tb.issue(lds + TA::BYTES, kbeg, p.ldb, wave);
+  }
+  for (int t = 0; t < nk; ++t) {
+    wait_vmcnt<0>();
+    lds_barrier();   // stage t visible to all waves; stage t-1 no longer read
+    if (t + 1 < nk) {
+      unsigned char* nx = lds + ((t + 1) & 1) * STAGE;
+      ta.issue(nx, kbeg + (t + 1) * LBK, p.lda, wave);
+      tb.issue(nx + TA::BYTES, kbeg + (t + 1) * LBK, p.ldb, wave);
+    }
+    const unsigned char* sa = lds + (t & 1) * STAGE;
+    const unsigned char* sb = sa + TA::BYTES;
+    bf16x8 af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = TA::frag(sa, wm0 + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[0][j] = TB::frag(sb, wn0 + j * 32, 0, lane);
+#pragma unroll
+    for (int kk = 0; kk < LBK / 16; ++kk) {
+      const int cb = kk & 1, nb = cb ^ 1;
+      if (kk + 1 < LBK / 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[nb][i] = TA::frag(sa, wm0 + i * 32, kk + 1, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bfr[nb][j] = TB::frag(sb, wn0 + j * 32, kk + 1, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          // B first: the result tile is C^T, so each lane holds four consecutive
+          // output columns of one output row
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  (void)LOADS;
+
+  const int cm = lane & 31;
+  const int cn = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm0 + i * 32 + cm;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn0 + j * 32 + q * 8 + cn;
+        if (n >= p.N) continue;
+        const long long o = g * p.c_gs + sp * p.c_ss + (long long)m * p.ldc + n;
+        if (OUTF32) {
+          float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                 acc[i][j][4 * q + 3]);
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) = v;
+        } else {
+          uint2 v;
+          v.x = pack_bf16_pair(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+          v.y = pack_bf16_pair(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = v;
+        }
+      }
+    }
+  }
+}
+
+// One symbol per role (as in the register-staged kernels) so profiles attribute
+// time to the stage.
+#define POETX_LDS_KERNEL(NAME, AK, BKM, OF)                                        \
+  template <int BM, int BN, int WM, int WN>                                       \
+  __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)                        \
+  __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME(GemmBf16 p) {             \
+    gemm_lds_body<BM, BN, WM, WN, AK, BKM, OF>(p);                                \
+  }
+POETX_LDS_KERNEL(w0_gemm_nt_lds, true, true, false)
+POETX_LDS_KERNEL(w0_gemm_nn_lds, true, false, false)
+POETX_LDS_KERNEL(block_gemm_nt_lds, true, true, false)
+POETX_LDS_KERNEL(block_gemm_nn_lds, true, false, false)
+POETX_LDS_KERNEL(dq_gemm_tn_lds, false, false, true)
+#undef POETX_LDS_KERNEL
+
+template <int BM, int BN, int WM, int WN>
+hipError_t dispatch_lds(const GemmBf16& p, hipStream_t s) {
+  constexpr int NW = (BM / WM) * (BN / WN);
+  dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, p.groups * p.splits);
+  // two LDS stages of (BM + BN) x 64 bf16
+  const size_t lds = 2 * (size_t)(BM + BN) * LBK * 2;
+  const int a = p.a_kmajor, b = p.b_kmajor, f = p.out_f32;
+  if (p.role == GEMM_W0 && a && b && !f)
+    hipLaunchKernelGGL((w0_gemm_nt_lds<BM, BN, WM, WN>), grid, dim3(NW * 64), lds, s, p);
+  else if (p.role == GEMM_W0 && a && !b && !f)
+    hipLaunchKernelGGL((w0_gemm_nn_lds<BM, BN, WM, WN>), grid, dim3(NW * 64), lds, s, p);
+  else if (p.role == GEMM_BLOCK && a && b && !f)
+    hipLaunchKernelGGL((block_gemm_nt_lds<BM, BN, WM, WN>), grid, dim3(NW * 64), lds, s, p);
+  else if (p.role == GEMM_BLOCK && a && !b && !f)
+    hipLaunchKernelGGL((block_gemm_nn_lds<BM, BN, WM, WN>), grid, dim3(NW * 64), lds, s, p);
+  else if (p.role == GEMM_DQ && !a && !b && f)
+    hipLaunchKernelGGL((dq_gemm_tn_lds<BM, BN, WM, WN>), grid, dim3(NW * 64), lds, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_lds_supported(const GemmBf16& p, int bm, int bn) {
+  if (p.K % LBK != 0) return false;
+  if (p.lda % 8 || p.ldb % 8 || p.ldc % 4) return false;
+  if (!p.a_kmajor && p.M % bm) return false;
+  if (!p.b_kmajor && p.N % bn) return false;
+  if (((uintptr_t)p.A | (uintptr_t)p.B) & 15) return false;
+  return true;
+}
+
+hipError_t launch_gemm_lds(const GemmBf16& p, int big, hipStream_t s) {
+  if (big) return dispatch_lds<256, 256, 128, 64>(p, s);
+  return dispatch_lds<128, 128, 64, 64>(p, s);
+}
+
+}  // namespace poetx

@@ -75,6 +75,10 @@ struct GemmBf16 {
   long long c_ss;
 };
 hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
+// Pipelined variant (direct-to-LDS loads, see k_gemm_lds.hip) for whole-tile shapes:
+// big = 256 x 256 tiles, else 128 x 128.
+bool gemm_lds_supported(const GemmBf16& p, int bm, int bn);
+hipError_t launch_gemm_lds(const GemmBf16& p, int big, hipStream_t s);
 
 // ---------------------------------------------------------------- fp32 MFMA chains
 // Row-panel power chains over one run of equal blocks (see k_chain.hip).
