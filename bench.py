@@ -107,7 +107,7 @@ def main() -> int:
     import torch
 
     import workloads
-    from orthogonal_equivalence_cayley_amd import PoetxLayer, poetx
+    from orthogonal_equivalence_cayley_amd import PoetxLayer, build_many, poetx
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = workloads.WORKLOADS[args.workload]
@@ -139,8 +139,7 @@ def main() -> int:
     log("bench: inputs resident")
 
     def step():
-        for L in layers:
-            L.build()
+        build_many(layers)
         for L, b in zip(layers, bufs):
             L.forward(b["X"], Y=b["Y"], Wa=b["Wa"])
         if w.backward:

@@ -115,6 +115,20 @@ poetx_status poetx_build_orth(const poetx_plan* plan, int32_t side, const float*
                               float* Q_f32, void* Q_act, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Batched build: count independent (plan, side) items in as few launches as
+ * possible (one per block-size class), e.g. every side of every layer of a
+ * model once per optimizer step. The blocks of one side form a batch
+ * computed block by block ([PX] §2.C); batching sides and layers only widens
+ * the grid. Item i takes the arguments of poetx_build_orth: plans[i],
+ * sides[i], thetas[i], Q_f32[i], Q_act ? Q_act[i] : NULL, ws[i] with
+ * ws_bytes[i] >= poetx_workspace_size(plans[i], 0, POETX_WS_BUILD). Host arrays
+ * of pointers; items must not share Q or workspace buffers. Every item is
+ * checked before anything is launched; the first failing check is returned. */
+poetx_status poetx_build_orth_batch(int32_t count, const poetx_plan* const* plans,
+                                    const int32_t* sides, const float* const* thetas,
+                                    float* const* Q_f32, void* const* Q_act, void* const* ws,
+                                    const size_t* ws_bytes, void* stream);
+
 /* Input-centric forward ([PX] §2.A): Y = R W0 P applied to the rows of X without
  * forming R W0 P. Stages: gather X by pi_P, blocks of P, product with Wt,
  * blocks of R, scatter by pi_R.

@@ -34,9 +34,20 @@ __device__ __forceinline__ float coef(int j, int k) { return (j == 0 || j == k +
 // A-operand read fall in distinct banks) and two staged chunks of CR rows of S
 // (pitch b + 16: the 4 rows x 16 columns of a B-operand read fall in distinct
 // banks). Chunks are fetched with coalesced 16-byte loads one chunk ahead.
+// The run this workgroup belongs to. Constant indices only (fully unrolled), so
+// the table stays in kernel-argument memory and scalar registers.
+__device__ __forceinline__ ChainEntry select_entry(const ChainBatch& cb) {
+  ChainEntry e = cb.e[0];
+#pragma unroll
+  for (int i = 1; i < kChainMaxEntries; ++i)
+    if (i < cb.n && (int)blockIdx.x >= cb.e[i].wg0) e = cb.e[i];
+  return e;
+}
+
 template <int MODE, int NT, int CR>
-__global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs p) {
+__global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
   extern __shared__ __align__(16) float lds[];
+  const ChainEntry p = select_entry(cb);
   const int b = p.b;
   const int pitch = b + 4;
   const int spitch = b + 16;
@@ -45,12 +56,14 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs p) {
   const int panels = b / RP;
   // all panels of one block on one XCD (workgroups are dealt to the 8 XCDs
   // round-robin), so that block's S is fetched into a single L2
-  const int nwg = gridDim.x;
-  const int lid = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int nwg = panels * p.count;
+  const int loc = blockIdx.x - p.wg0;
+  if (loc >= nwg) return;   // padding of the run to a multiple of 8 workgroups
+  const int lid = (nwg % 8 == 0 && p.wg0 % 8 == 0) ? (loc % 8) * (nwg / 8) + loc / 8 : loc;
   const int blk = lid / panels;
   const int r0 = (lid - blk * panels) * RP;
   const long long bb = (long long)b * b;
-  const long long moff = p.q_off + blk * bb;       // this block inside the side arrays
+  const long long moff = blk * bb;                 // this block inside the run
   const float* S = p.S + moff;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -61,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs p) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) bcol[t] = min(wave + 4 * t, ntiles - 1) * 16;
   const int li = lane & 15, lk = lane >> 4;        // operand lane coordinates
-  const int k = p.k;
+  const int k = cb.k;
   const int q4 = b / 4;                             // float4 per row of S
   constexpr int kLoads = 8;                         // float4 per thread per chunk (max)
   const int nvec = CR * q4;                         // float4 per chunk, <= kLoads * kThreads
@@ -87,10 +100,10 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs p) {
         const float g = p.G[moff + o];
         keep[t][v] = g;
         x = coef(k + 1, k) * g;
-        p.out_f32[(long long)k * p.ne + moff + o] = x;
+        p.out[(long long)k * p.stride + moff + o] = x;
       } else {
         // A_{k+1}^T panel: element (row, col) = A_{k+1}[col][r0 + row]
-        x = p.G[(long long)k * p.ne + moff + (long long)col * b + r0 + row];
+        x = p.G[(long long)k * p.stride + moff + (long long)col * b + r0 + row];
       }
       panel[row * pitch + col] = x;
     }
@@ -155,9 +168,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs p) {
           keep[t][v] += coef(j, k) * x;
         } else if (MODE == 1) {
           x = coef(j, k) * keep[t][v] - x;
-          p.out_f32[(long long)(j - 1) * p.ne + moff + (long long)(r0 + row) * b + col] = x;
+          p.out[(long long)(j - 1) * p.stride + moff + (long long)(r0 + row) * b + col] = x;
         } else {
-          x += p.G[(long long)(j - 1) * p.ne + moff + (long long)col * b + r0 + row];
+          x += p.G[(long long)(j - 1) * p.stride + moff + (long long)col * b + r0 + row];
         }
         panel[row * pitch + col] = x;
       }
@@ -176,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs p) {
         const int row = 4 * lk + v;
         const long long o = moff + (long long)(r0 + row) * b + col;
         const float x = (MODE == 0) ? keep[t][v] : panel[row * pitch + col];
-        p.out_f32[o] = x;
+        p.out[o] = x;
         if (MODE == 0 && p.out_act) {
           if (p.act_bf16)
             reinterpret_cast<__bf16*>(p.out_act)[o] = static_cast<__bf16>(x);
@@ -191,25 +204,44 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs p) {
 #undef POETX_FETCH
 #undef POETX_STASH
 
-template <int MODE, int CR>
-hipError_t launch_cr(const ChainArgs& p, hipStream_t s) {
-  const int panels = p.b / RP;
-  dim3 grid(panels * p.count);
-  const size_t lds = ((size_t)RP * (p.b + 4) + 2 * (size_t)CR * (p.b + 16)) * sizeof(float);
-  const int nt = (p.b / 16 + 3) / 4;
-  if (nt <= 1) hipLaunchKernelGGL((chain_kernel<MODE, 1, CR>), grid, dim3(kThreads), lds, s, p);
-  else if (nt <= 2) hipLaunchKernelGGL((chain_kernel<MODE, 2, CR>), grid, dim3(kThreads), lds, s, p);
-  else if (nt <= 4) hipLaunchKernelGGL((chain_kernel<MODE, 4, CR>), grid, dim3(kThreads), lds, s, p);
-  else if (nt <= 8) hipLaunchKernelGGL((chain_kernel<MODE, 8, CR>), grid, dim3(kThreads), lds, s, p);
-  else return hipErrorInvalidValue;
+constexpr int kCR = 16;   // rows of S per staged chunk
+
+template <int MODE, int NT>
+hipError_t launch_class(ChainBatch cb, hipStream_t s) {
+  int wg = 0, bmax = 0;
+  for (int i = 0; i < cb.n; ++i) {
+    cb.e[i].wg0 = wg;
+    // runs start on a multiple of 8 workgroups so the XCD-aware order applies
+    wg += (cb.e[i].b / RP * cb.e[i].count + 7) / 8 * 8;
+    bmax = max(bmax, cb.e[i].b);
+  }
+  if (wg == 0) return hipSuccess;
+  const size_t lds = ((size_t)RP * (bmax + 4) + 2 * (size_t)kCR * (bmax + 16)) * sizeof(float);
+  hipLaunchKernelGGL((chain_kernel<MODE, NT, kCR>), dim3(wg), dim3(kThreads), lds, s, cb);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t launch_mode(const ChainArgs& p, hipStream_t s) {
-  // chunk rows: each thread moves at most 8 float4 per chunk (CR * b / 4 <= 2048)
-  if (p.b % 32 == 0 && p.b <= 256) return launch_cr<MODE, 32>(p, s);
-  return launch_cr<MODE, 16>(p, s);
+hipError_t launch_mode(const ChainBatch& all, hipStream_t s) {
+  // one launch per size class (tiles per wave)
+  for (int nt = 1; nt <= 8; nt *= 2) {
+    ChainBatch cb;
+    cb.n = 0;
+    cb.k = all.k;
+    for (int i = 0; i < all.n; ++i) {
+      const int need = (all.e[i].b / 16 + 3) / 4;
+      const int cls = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+      if (cls == nt) cb.e[cb.n++] = all.e[i];
+    }
+    if (cb.n == 0) continue;
+    hipError_t e;
+    if (nt == 1) e = launch_class<MODE, 1>(cb, s);
+    else if (nt == 2) e = launch_class<MODE, 2>(cb, s);
+    else if (nt == 4) e = launch_class<MODE, 4>(cb, s);
+    else e = launch_class<MODE, 8>(cb, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -218,14 +250,105 @@ hipError_t launch_mode(const ChainArgs& p, hipStream_t s) {
 // chunk a whole number of per-thread loads (b = 16 .. 512).
 bool chain_supported(int b) { return b % 16 == 0 && b >= 16 && b <= 512; }
 
-hipError_t launch_chain(int mode, const ChainArgs& p, hipStream_t s) {
-  if (!chain_supported(p.b) || p.count <= 0) return hipErrorInvalidValue;
+hipError_t launch_chain_batch(int mode, const ChainBatch& cb, hipStream_t s) {
+  if (cb.n < 0 || cb.n > kChainMaxEntries) return hipErrorInvalidValue;
+  for (int i = 0; i < cb.n; ++i)
+    if (!chain_supported(cb.e[i].b) || cb.e[i].count <= 0) return hipErrorInvalidValue;
   switch (mode) {
-    case CHAIN_BUILD: return launch_mode<0>(p, s);
-    case CHAIN_ABAR: return launch_mode<1>(p, s);
-    case CHAIN_TCHAIN: return launch_mode<2>(p, s);
+    case CHAIN_BUILD: return launch_mode<0>(cb, s);
+    case CHAIN_ABAR: return launch_mode<1>(cb, s);
+    case CHAIN_TCHAIN: return launch_mode<2>(cb, s);
   }
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- batched unpack / pack
+
+namespace {
+
+__device__ __forceinline__ TriEntry select_tri(const TriBatch& tb, long long e) {
+  TriEntry r = tb.e[0];
+#pragma unroll
+  for (int i = 1; i < kChainMaxEntries; ++i)
+    if (i < tb.n && e >= tb.e[i].e0) r = tb.e[i];
+  return r;
+}
+
+__device__ __forceinline__ long long tri_off(int i, int j, int b) {
+  return (long long)i * b - ((long long)i * (i + 1)) / 2 + (j - i - 1);
+}
+
+// S[r][c] = theta(r, c) above the diagonal, -theta(c, r) below, 0 on it.
+__global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb, long long total) {
+  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total;
+       e += (long long)gridDim.x * kThreads) {
+    const TriEntry t = select_tri(tb, e);
+    const long long bb = (long long)t.b * t.b;
+    const long long np = (long long)t.b * (t.b - 1) / 2;
+    const long long loc = e - t.e0;
+    const long long g = loc / bb;
+    const int r = (int)((loc - g * bb) / t.b);
+    const int c = (int)(loc - g * bb - (long long)r * t.b);
+    const float* th = t.src + g * np;
+    float v = 0.0f;
+    if (r < c) v = th[tri_off(r, c, t.b)];
+    else if (r > c) v = -th[tri_off(c, r, t.b)];
+    t.dst[loc] = v;
+  }
+}
+
+// g(r, c) = sign * (M[r][c] - M[c][r]) for r < c.
+__global__ __launch_bounds__(kThreads) void pack_batch_kernel(TriBatch tb, long long total) {
+  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total;
+       e += (long long)gridDim.x * kThreads) {
+    const TriEntry t = select_tri(tb, e);
+    const long long bb = (long long)t.b * t.b;
+    const long long np = (long long)t.b * (t.b - 1) / 2;
+    const long long loc = e - t.e0;
+    const long long g = loc / bb;
+    const int r = (int)((loc - g * bb) / t.b);
+    const int c = (int)(loc - g * bb - (long long)r * t.b);
+    if (r < c) {
+      const float* M = t.src + g * bb;
+      t.dst[g * np + tri_off(r, c, t.b)] =
+          tb.sign * (M[(long long)r * t.b + c] - M[(long long)c * t.b + r]);
+    }
+  }
+}
+
+long long fill_offsets(TriBatch& tb) {
+  long long tot = 0;
+  for (int i = 0; i < tb.n; ++i) {
+    tb.e[i].e0 = tot;
+    tot += (long long)tb.e[i].b * tb.e[i].b * tb.e[i].count;
+  }
+  return tot;
+}
+
+int tri_grid(long long total) {
+  long long g = (total + kThreads - 1) / kThreads;
+  const long long cap = 256LL * 32;
+  return (int)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+}  // namespace
+
+hipError_t launch_unpack_batch(const TriBatch& in, hipStream_t s) {
+  if (in.n <= 0) return hipSuccess;
+  if (in.n > kChainMaxEntries) return hipErrorInvalidValue;
+  TriBatch tb = in;
+  const long long total = fill_offsets(tb);
+  hipLaunchKernelGGL(unpack_batch_kernel, dim3(tri_grid(total)), dim3(kThreads), 0, s, tb, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_batch(const TriBatch& in, hipStream_t s) {
+  if (in.n <= 0) return hipSuccess;
+  if (in.n > kChainMaxEntries) return hipErrorInvalidValue;
+  TriBatch tb = in;
+  const long long total = fill_offsets(tb);
+  hipLaunchKernelGGL(pack_batch_kernel, dim3(tri_grid(total)), dim3(kThreads), 0, s, tb, total);
+  return hipGetLastError();
 }
 
 }  // namespace poetx

@@ -82,6 +82,7 @@ struct StageScope {
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool side_ok_fn(int32_t side) { return side == POETX_SIDE_R || side == POETX_SIDE_P; }
 int elsize(const poetx_plan* pl) { return pl->dtype == POETX_BF16 ? 2 : 4; }
 
 // Coefficients of Q = sum_{j=0..k+1} c_j S^j for Q = (I+S) sum_{j<=k} S^j.
@@ -121,7 +122,9 @@ int dq_splits(const poetx_plan* pl, int side, long long T) {
 struct FwdWs { void *U, *V, *Wa, *Z; };
 struct BwdWs {
   void *GZ, *GWa, *GV, *U, *GU;
-  float *dQ[2], *part, *S, *A0, *A1, *T0, *T1, *Astore;
+  float *dQ[2], *part;
+  float *Sside[2], *Tside[2], *Aside[2];      // fused chains, per side
+  float *A0, *A1, *T0, *T1;                   // generic chain path
 };
 
 size_t layout_fwd(const poetx_plan* pl, long long T, void* base, FwdWs* w) {
@@ -151,13 +154,16 @@ size_t layout_bwd(const poetx_plan* pl, long long T, void* base, BwdWs* w) {
   for (int side = 0; side < 2; ++side)
     part = std::max(part, (long long)dq_splits(pl, side, T) * pl->nelem[side]);
   x.part = (float*)c.take(4 * part);
+  for (int side = 0; side < 2; ++side) {
+    x.Sside[side] = (float*)c.take(4 * pl->nelem[side]);
+    x.Tside[side] = (float*)c.take(4 * pl->nelem[side]);
+    x.Aside[side] = (float*)c.take(4 * pl->nelem[side] * (pl->k + 1));
+  }
   const long long ne = std::max(pl->nelem[0], pl->nelem[1]);
-  x.S = (float*)c.take(4 * ne);
   x.A0 = (float*)c.take(4 * ne);
   x.A1 = (float*)c.take(4 * ne);
   x.T0 = (float*)c.take(4 * ne);
   x.T1 = (float*)c.take(4 * ne);
-  x.Astore = (float*)c.take(4 * ne * (pl->k + 1));
   if (w) *w = x;
   return c.off;
 }
@@ -271,54 +277,157 @@ poetx_status block_grads(const poetx_plan* pl, int side, long long T, const void
   return POETX_OK;
 }
 
-// Reverse mode through Q = sum_j c_j S^j for every block of one side:
+// Reverse mode through Q = sum_j c_j S^j for every block of both sides:
 //   A_{k+1} = c_{k+1} G,  A_j = c_j G + A_{j+1} S^T,
 //   T_{k+1} = A_{k+1},    T_j = A_j + S^T T_{j+1},   dL/dS = T_1,
-// then dL/dtheta(i,j) = dS[i][j] - dS[j][i]. Uses S^T = -S.
-poetx_status cnp_backward(const poetx_plan* pl, int side, const float* theta, const float* G,
-                          float* gtheta, float* S, float* A0, float* A1, float* T0, float* T1,
-                          float* Astore, hipStream_t s) {
+// then dL/dtheta(i,j) = dS[i][j] - dS[j][i]. Uses S^T = -S. Runs of supported
+// block sizes go through the fused row-panel chains, both sides in one launch
+// per chain; other sizes step through batched fp32 GEMMs.
+poetx_status cnp_backward(const poetx_plan* pl, const float* const theta[2], float* const gtheta[2],
+                          const BwdWs& w, hipStream_t s) {
   const int k = pl->k;
-  const long long ne = pl->nelem[side];
-  for (const Seg& g : pl->segs[side]) HIP_TRY(poetx::launch_unpack_skew(theta, g, S, nullptr, 0.0f, s));
-  bool any_generic = false;
-  for (const Seg& g : pl->segs[side]) {
-    if (!poetx::chain_supported(g.b)) {
-      any_generic = true;
-      continue;
-    }
-    // row-local first chain, then the transposed second chain, then pack
-    poetx::ChainArgs c;
-    c.S = S; c.G = G; c.out_f32 = Astore; c.out_act = nullptr; c.act_bf16 = 0;
-    c.b = g.b; c.count = g.count; c.k = k; c.q_off = g.q_off; c.ne = ne;
-    HIP_TRY(poetx::launch_chain(poetx::CHAIN_ABAR, c, s));
-    c.G = Astore; c.out_f32 = T0;
-    HIP_TRY(poetx::launch_chain(poetx::CHAIN_TCHAIN, c, s));
-    HIP_TRY(poetx::launch_pack_antisym(T0, g, -1.0f, gtheta, s));
-  }
-  if (!any_generic) return POETX_OK;
-  // blocks whose size the MFMA chain does not take: batched fp32 GEMM per step
-  HIP_TRY(poetx::launch_scale2(G, coef(k + 1, k), A0, T1, ne, s));
-  float *Acur = A0, *Anew = A1, *Tcur = T1, *Tnew = T0;
-  for (int j = k; j >= 1; --j) {
+  poetx::TriBatch ub{}, pb{};
+  poetx::ChainBatch ab{}, tb{};
+  ab.k = tb.k = k;
+  pb.sign = -1.0f;   // T_1^T is stored: g(i,j) = T^T[j][i] - T^T[i][j]
+  auto flush = [&]() -> poetx_status {
+    HIP_TRY(poetx::launch_unpack_batch(ub, s));
+    HIP_TRY(poetx::launch_chain_batch(poetx::CHAIN_ABAR, ab, s));
+    HIP_TRY(poetx::launch_chain_batch(poetx::CHAIN_TCHAIN, tb, s));
+    HIP_TRY(poetx::launch_pack_batch(pb, s));
+    ub.n = pb.n = ab.n = tb.n = 0;
+    return POETX_OK;
+  };
+  for (int side = 0; side < 2; ++side) {
     for (const Seg& g : pl->segs[side]) {
-      if (poetx::chain_supported(g.b)) continue;
-      // A_j = c_j G - A_{j+1} S
-      poetx_status st = chain_gemm(g, Acur, S, Anew, G, nullptr, -1.0f, coef(j, k), s);
-      if (st != POETX_OK) return st;
-      // T_j = A_j - S T_{j+1}
-      st = chain_gemm(g, S, Tcur, Tnew, Anew, nullptr, -1.0f, 1.0f, s);
-      if (st != POETX_OK) return st;
+      if (!poetx::chain_supported(g.b)) continue;
+      if (ab.n == poetx::kChainMaxEntries) {
+        poetx_status st = flush();
+        if (st != POETX_OK) return st;
+      }
+      float* S = w.Sside[side] + g.q_off;
+      ub.e[ub.n++] = poetx::TriEntry{theta[side] + g.p_off, S, g.b, g.count, 0};
+      poetx::ChainEntry e{};
+      e.S = S; e.b = g.b; e.count = g.count; e.stride = pl->nelem[side];
+      e.G = w.dQ[side] + g.q_off;
+      e.out = w.Aside[side] + g.q_off;
+      ab.e[ab.n++] = e;
+      e.G = w.Aside[side] + g.q_off;
+      e.out = w.Tside[side] + g.q_off;
+      tb.e[tb.n++] = e;
+      pb.e[pb.n++] = poetx::TriEntry{w.Tside[side] + g.q_off, gtheta[side] + g.p_off, g.b, g.count, 0};
     }
-    std::swap(Acur, Anew);
-    std::swap(Tcur, Tnew);
   }
-  for (const Seg& g : pl->segs[side])
-    if (!poetx::chain_supported(g.b)) HIP_TRY(poetx::launch_pack_antisym(Tcur, g, 1.0f, gtheta, s));
+  poetx_status st = flush();
+  if (st != POETX_OK) return st;
+  for (int side = 0; side < 2; ++side) {
+    bool any = false;
+    for (const Seg& g : pl->segs[side]) any |= !poetx::chain_supported(g.b);
+    if (!any) continue;
+    const long long ne = pl->nelem[side];
+    float* S = w.Sside[side];
+    const float* G = w.dQ[side];
+    for (const Seg& g : pl->segs[side])
+      if (!poetx::chain_supported(g.b))
+        HIP_TRY(poetx::launch_unpack_skew(theta[side], g, S, nullptr, 0.0f, s));
+    HIP_TRY(poetx::launch_scale2(G, coef(k + 1, k), w.A0, w.T1, ne, s));
+    float *Acur = w.A0, *Anew = w.A1, *Tcur = w.T1, *Tnew = w.T0;
+    for (int j = k; j >= 1; --j) {
+      for (const Seg& g : pl->segs[side]) {
+        if (poetx::chain_supported(g.b)) continue;
+        // A_j = c_j G - A_{j+1} S
+        st = chain_gemm(g, Acur, S, Anew, G, nullptr, -1.0f, coef(j, k), s);
+        if (st != POETX_OK) return st;
+        // T_j = A_j - S T_{j+1}
+        st = chain_gemm(g, S, Tcur, Tnew, Anew, nullptr, -1.0f, 1.0f, s);
+        if (st != POETX_OK) return st;
+      }
+      std::swap(Acur, Anew);
+      std::swap(Tcur, Tnew);
+    }
+    for (const Seg& g : pl->segs[side])
+      if (!poetx::chain_supported(g.b))
+        HIP_TRY(poetx::launch_pack_antisym(Tcur, g, 1.0f, gtheta[side], s));
+  }
   return POETX_OK;
 }
 
-bool side_ok(int32_t side) { return side == POETX_SIDE_R || side == POETX_SIDE_P; }
+// One build item: Q (and its activation-dtype copy) of one side of one plan.
+struct BuildItem {
+  const poetx_plan* pl;
+  int side;
+  const float* theta;
+  float* Q;
+  void* Qact;
+  void* ws;
+};
+
+poetx_status check_build_item(const BuildItem& it, size_t ws_bytes) {
+  if (!it.pl || !side_ok_fn(it.side) || !it.theta || !it.Q) return POETX_ERR_INVALID_ARG;
+  if (!aligned16(it.theta) || !aligned16(it.Q) || !aligned16(it.Qact) || !aligned16(it.ws))
+    return POETX_ERR_ALIGNMENT;
+  if (!it.ws || ws_bytes < poetx_workspace_size(it.pl, 0, POETX_WS_BUILD)) return POETX_ERR_WORKSPACE;
+  return POETX_OK;
+}
+
+// Builds every item: all runs of supported block sizes in one unpack launch and
+// one fused chain launch per size class; other sizes through batched GEMMs.
+poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
+  poetx::TriBatch ub{};
+  poetx::ChainBatch cb{};
+  int kk = -1;
+  auto flush = [&]() -> poetx_status {
+    HIP_TRY(poetx::launch_unpack_batch(ub, s));
+    HIP_TRY(poetx::launch_chain_batch(poetx::CHAIN_BUILD, cb, s));
+    ub.n = cb.n = 0;
+    return POETX_OK;
+  };
+  for (int i = 0; i < count; ++i) {
+    const BuildItem& it = items[i];
+    const poetx_plan* pl = it.pl;
+    if (kk != -1 && kk != pl->k) {   // one Neumann order per chain launch
+      poetx_status st = flush();
+      if (st != POETX_OK) return st;
+    }
+    kk = pl->k;
+    cb.k = kk;
+    float *S, *P0, *P1;
+    layout_build(pl, it.ws, &S, &P0, &P1);
+    const bool bf16 = pl->dtype == POETX_BF16;
+    const int es = elsize(pl);
+    for (const Seg& g : pl->segs[it.side]) {
+      if (poetx::chain_supported(g.b)) {
+        if (cb.n == poetx::kChainMaxEntries) {
+          poetx_status st = flush();
+          if (st != POETX_OK) return st;
+        }
+        ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, S + g.q_off, g.b, g.count, 0};
+        poetx::ChainEntry e{};
+        e.S = S + g.q_off; e.G = nullptr; e.out = it.Q + g.q_off;
+        e.out_act = it.Qact ? static_cast<char*>(it.Qact) + (size_t)es * g.q_off : nullptr;
+        e.act_bf16 = bf16; e.b = g.b; e.count = g.count; e.stride = 0;
+        cb.e[cb.n++] = e;
+        continue;
+      }
+      HIP_TRY(poetx::launch_unpack_skew(it.theta, g, S, it.Q, coef(1, pl->k), s));
+      // powers S^j = S^{j-1} S for j = 2..k+1, each added into Q with weight c_j
+      const float* prev = S;
+      float* bufs[2] = {P0, P1};
+      for (int j = 2; j <= pl->k + 1; ++j) {
+        float* next = (j < pl->k + 1) ? bufs[j & 1] : nullptr;
+        poetx_status st = chain_gemm(g, prev, S, it.Q, it.Q, next, coef(j, pl->k), 1.0f, s);
+        if (st != POETX_OK) return st;
+        prev = next;
+      }
+      if (it.Qact)
+        HIP_TRY(poetx::launch_cast(it.Q + g.q_off, static_cast<char*>(it.Qact) + es * g.q_off,
+                                   (long long)g.b * g.b * g.count, bf16, s));
+    }
+  }
+  return flush();
+}
+
+bool side_ok(int32_t side) { return side_ok_fn(side); }
 
 }  // namespace
 
@@ -424,42 +533,30 @@ poetx_status poetx_permute_weight(const poetx_plan* pl, const void* W0, const in
 
 poetx_status poetx_build_orth(const poetx_plan* pl, int32_t side, const float* theta, float* Q_f32,
                               void* Q_act, void* ws, size_t ws_bytes, void* stream) {
-  if (!pl || !side_ok(side) || !theta || !Q_f32) return POETX_ERR_INVALID_ARG;
-  if (!aligned16(theta) || !aligned16(Q_f32) || !aligned16(Q_act) || !aligned16(ws))
-    return POETX_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < poetx_workspace_size(pl, 0, POETX_WS_BUILD)) return POETX_ERR_WORKSPACE;
+  BuildItem it{pl, side, theta, Q_f32, Q_act, ws};
+  poetx_status st = check_build_item(it, ws_bytes);
+  if (st != POETX_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   StageScope sc(POETX_STAGE_BUILD, s);
-  float *S, *P0, *P1;
-  layout_build(pl, ws, &S, &P0, &P1);
-  const int k = pl->k;
-  const bool bf16 = pl->dtype == POETX_BF16;
-  const int es = elsize(pl);
-  for (const Seg& g : pl->segs[side]) {
-    if (poetx::chain_supported(g.b)) {
-      // one fused kernel per run of blocks: S -> powers -> Q (fp32 and act copy)
-      HIP_TRY(poetx::launch_unpack_skew(theta, g, S, nullptr, 0.0f, s));
-      poetx::ChainArgs c;
-      c.S = S; c.G = nullptr; c.out_f32 = Q_f32; c.out_act = Q_act; c.act_bf16 = bf16;
-      c.b = g.b; c.count = g.count; c.k = k; c.q_off = g.q_off; c.ne = pl->nelem[side];
-      HIP_TRY(poetx::launch_chain(poetx::CHAIN_BUILD, c, s));
-      continue;
-    }
-    HIP_TRY(poetx::launch_unpack_skew(theta, g, S, Q_f32, coef(1, k), s));
-    // powers S^j = S^{j-1} S for j = 2..k+1, each added into Q with weight c_j
-    const float* prev = S;
-    float* bufs[2] = {P0, P1};
-    for (int j = 2; j <= k + 1; ++j) {
-      float* next = (j < k + 1) ? bufs[j & 1] : nullptr;
-      poetx_status st = chain_gemm(g, prev, S, Q_f32, Q_f32, next, coef(j, k), 1.0f, s);
-      if (st != POETX_OK) return st;
-      prev = next;
-    }
-    if (Q_act)
-      HIP_TRY(poetx::launch_cast(Q_f32 + g.q_off, static_cast<char*>(Q_act) + es * g.q_off,
-                                 (long long)g.b * g.b * g.count, bf16, s));
+  return build_items(&it, 1, s);
+}
+
+poetx_status poetx_build_orth_batch(int32_t count, const poetx_plan* const* plans,
+                                    const int32_t* sides, const float* const* thetas,
+                                    float* const* Q_f32, void* const* Q_act, void* const* ws,
+                                    const size_t* ws_bytes, void* stream) {
+  if (count < 0) return POETX_ERR_INVALID_ARG;
+  if (count == 0) return POETX_OK;
+  if (!plans || !sides || !thetas || !Q_f32 || !ws || !ws_bytes) return POETX_ERR_INVALID_ARG;
+  std::vector<BuildItem> items((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    items[i] = BuildItem{plans[i], sides[i], thetas[i], Q_f32[i], Q_act ? Q_act[i] : nullptr, ws[i]};
+    poetx_status st = check_build_item(items[i], ws_bytes[i]);
+    if (st != POETX_OK) return st;
   }
-  return POETX_OK;
+  hipStream_t s = (hipStream_t)stream;
+  StageScope sc(POETX_STAGE_BUILD, s);
+  return build_items(items.data(), count, s);
 }
 
 poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const void* Wt,
@@ -573,11 +670,9 @@ poetx_status poetx_backward(const poetx_plan* pl, int64_t T, const void* X, cons
     HIP_TRY(poetx::launch_zero(w.dQ[1], pl->nelem[1], s));
   }
   StageScope sc(POETX_STAGE_CNP_BWD, s);
-  if ((st = cnp_backward(pl, POETX_SIDE_R, theta_R, w.dQ[0], g_theta_R, w.S, w.A0, w.A1, w.T0,
-                         w.T1, w.Astore, s)) != POETX_OK)
-    return st;
-  return cnp_backward(pl, POETX_SIDE_P, theta_P, w.dQ[1], g_theta_P, w.S, w.A0, w.A1, w.T0, w.T1,
-                      w.Astore, s);
+  const float* const th[2] = {theta_R, theta_P};
+  float* const gt[2] = {g_theta_R, g_theta_P};
+  return cnp_backward(pl, th, gt, w, s);
 }
 
 poetx_status poetx_gather_cols(const poetx_plan* pl, int64_t T, int32_t dim, const void* in,

@@ -81,19 +81,41 @@ bool gemm_lds_supported(const GemmBf16& p, int bm, int bn);
 hipError_t launch_gemm_lds(const GemmBf16& p, int big, hipStream_t s);
 
 // ---------------------------------------------------------------- fp32 MFMA chains
-// Row-panel power chains over one run of equal blocks (see k_chain.hip).
+// Row-panel power chains (see k_chain.hip), batched over runs of equal blocks
+// from any number of sides and layers so that one launch fills the chip.
 enum ChainMode { CHAIN_BUILD = 0, CHAIN_ABAR = 1, CHAIN_TCHAIN = 2 };
-struct ChainArgs {
-  const float* S;     // side's skew generators, fp32 [ne]
-  const float* G;     // ABAR: dL/dQ [ne]; TCHAIN: stored A_j, [(k+1) * ne]
-  float* out_f32;     // BUILD: Q [ne]; ABAR: A_j store [(k+1) * ne]; TCHAIN: T_1^T [ne]
-  void* out_act;      // BUILD: Q copy in the activation dtype, or null
+constexpr int kChainMaxEntries = 32;
+struct ChainEntry {
+  const float* S;     // skew generators of the run's first block, fp32
+  const float* G;     // ABAR: dL/dQ of the run; TCHAIN: stored A_j of the run
+  float* out;         // BUILD: Q; ABAR: A_j store; TCHAIN: T_1^T
+  void* out_act;      // BUILD: copy of Q in the activation dtype, or null
+  long long stride;   // elements between consecutive stored A_j (ABAR, TCHAIN)
+  int b, count;       // block size and number of blocks of the run
+  int wg0;            // first workgroup of the run (filled by the launcher)
   int act_bf16;
-  int b, count, k;
-  long long q_off;    // run offset inside the side arrays
-  long long ne;       // side elements (stride of the A_j store)
+};
+struct ChainBatch {
+  int n, k;
+  ChainEntry e[kChainMaxEntries];
 };
 bool chain_supported(int b);
-hipError_t launch_chain(int mode, const ChainArgs& p, hipStream_t s);
+// Launches the entries of `cb` (all chain_supported), one kernel per size class.
+hipError_t launch_chain_batch(int mode, const ChainBatch& cb, hipStream_t s);
+
+// Batched unpack (theta -> S) and pack (sign * (M - M^T) -> packed gradient).
+struct TriEntry {
+  const float* src;   // unpack: packed theta of the run; pack: b x b matrices of the run
+  float* dst;         // unpack: b x b matrices; pack: packed gradient of the run
+  int b, count;
+  long long e0;       // first element of the run in the flattened batch (launcher)
+};
+struct TriBatch {
+  int n;
+  float sign;
+  TriEntry e[kChainMaxEntries];
+};
+hipError_t launch_unpack_batch(const TriBatch& tb, hipStream_t s);
+hipError_t launch_pack_batch(const TriBatch& tb, hipStream_t s);
 
 }  // namespace poetx

@@ -17,6 +17,15 @@ _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 _PX_DTYPE = {"bf16": _px.POETX_BF16, "f32": _px.POETX_FP32}
 
 
+def build_many(layers) -> None:
+    """Build both sides of every layer in one batched call (one launch per
+    block-size class instead of one per side and layer)."""
+    items = []
+    for L in layers:
+        items.extend(L.build_items())
+    _px.build_orth_batch(items)
+
+
 class PoetxLayer:
     def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
                  dtype: str = "bf16", device: str = "cuda"):
@@ -63,10 +72,32 @@ class PoetxLayer:
 
     # ------------------------------------------------------------------ calls
     def build(self) -> None:
+        """Build both sides' blocks (one batched call)."""
+        build_many([self])
+
+    def build_side(self, side: int) -> None:
+        """Build one side through the single-side entry point."""
         ws = self.workspace(_px.WS_BUILD)
+        qa = self.Qact[side] if self.dtype == "bf16" else None
+        self.plan.build_orth(side, self.theta[side], self.Q32[side], qa, ws, ws.numel())
+
+    def build_items(self):
+        """(plan, side, theta, Q_f32, Q_act, ws) for both sides, for build_many()."""
+        out = []
         for side in (_px.SIDE_R, _px.SIDE_P):
             qa = self.Qact[side] if self.dtype == "bf16" else None
-            self.plan.build_orth(side, self.theta[side], self.Q32[side], qa, ws, ws.numel())
+            ws = self.workspace(_px.WS_BUILD) if side == _px.SIDE_R else self._ws_build_p()
+            out.append((self.plan, side, self.theta[side], self.Q32[side], qa, ws))
+        return out
+
+    def _ws_build_p(self) -> torch.Tensor:
+        # a second build workspace so both sides of one layer can share a batch
+        need = self.plan.workspace_size(0, _px.WS_BUILD)
+        cur = self._ws.get("build_p")
+        if cur is None or cur.numel() < need:
+            cur = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            self._ws["build_p"] = cur
+        return cur
 
     def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
                 Wa: Optional[torch.Tensor] = None, save: bool = True) -> torch.Tensor:

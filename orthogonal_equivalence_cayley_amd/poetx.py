@@ -34,7 +34,7 @@ WS_BACKWARD = 2
 EXPORTED = (
     "poetx_plan_create", "poetx_plan_destroy", "poetx_param_count", "poetx_block_elems",
     "poetx_workspace_size", "poetx_status_string", "poetx_permute_weight",
-    "poetx_build_orth", "poetx_forward", "poetx_backward", "poetx_gather_cols",
+    "poetx_build_orth", "poetx_build_orth_batch", "poetx_forward", "poetx_backward", "poetx_gather_cols",
     "poetx_scatter_cols", "poetx_timing_enable", "poetx_timing_read", "poetx_timing_reset",
 )
 
@@ -72,6 +72,7 @@ def _load() -> ctypes.CDLL:
         "poetx_status_string": (ctypes.c_char_p, [st]),
         "poetx_permute_weight": (st, [vp, vp, vp, vp, vp, vp]),
         "poetx_build_orth": (st, [vp, i32, vp, vp, vp, vp, sz, vp]),
+        "poetx_build_orth_batch": (st, [i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "poetx_forward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "poetx_backward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]),
@@ -134,6 +135,23 @@ def timing_read(stage: str):
 
 def timing_reset() -> None:
     LIB.poetx_timing_reset()
+
+
+def build_orth_batch(items, stream=None) -> None:
+    """Build many (plan, side, theta, Q_f32, Q_act, ws) items in one call."""
+    n = len(items)
+    if n == 0:
+        return
+    VP = ctypes.c_void_p * n
+    plans = VP(*[it[0].handle for it in items])
+    sides = (ctypes.c_int32 * n)(*[it[1] for it in items])
+    thetas = VP(*[_ptr(it[2]) for it in items])
+    q32 = VP(*[_ptr(it[3]) for it in items])
+    qact = VP(*[_ptr(it[4]) for it in items])
+    ws = VP(*[_ptr(it[5]) for it in items])
+    wsb = (ctypes.c_size_t * n)(*[it[5].numel() for it in items])
+    _check(LIB.poetx_build_orth_batch(n, plans, sides, thetas, q32, qact, ws, wsb, _stream(stream)),
+           "poetx_build_orth_batch")
 
 
 class Plan:

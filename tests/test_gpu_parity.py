@@ -199,3 +199,29 @@ def test_backward_deterministic():
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+def test_build_batch_matches_single_side_builds():
+    """One batched build over several layers (supported and generic block sizes,
+    bf16 and fp32 plans) gives the same blocks as the single-side entry point,
+    and both match the oracle."""
+    import torch
+    from orthogonal_equivalence_cayley_amd import build_many
+    specs = [
+        ("bf16", workloads.small_case(512, 256, (256, 256), (128, 128), T=1, seed=1, dtype="bf16", theta_std=0.01), 4),
+        ("bf16", workloads.small_case(1024, 512, (512, 256, 256), (512,), T=1, seed=2, dtype="bf16", theta_std=0.005), 4),
+        ("f32", workloads.small_case(70, 64, (30, 40), (64,), T=1, seed=3, dtype="f32", theta_std=0.05), 4),
+    ]
+    layers = [make_layer(inp, k, dt) for dt, inp, k in specs]
+    build_many(layers)
+    torch.cuda.synchronize()
+    batch = [[L.Q32[s].clone() for s in (0, 1)] for L in layers]
+    for L in layers:
+        L.build_side(0)
+        L.build_side(1)
+    torch.cuda.synchronize()
+    for (dt, inp, k), L, qb in zip(specs, layers, batch):
+        for s, bsz, th in ((0, inp.spec.bsz_R, inp.theta_R), (1, inp.spec.bsz_P, inp.theta_P)):
+            assert torch.equal(qb[s], L.Q32[s])
+            want = blocks_concat(oracle.build_orth(th, bsz, k))
+            assert oracle.rel_fro(qb[s].cpu().numpy().astype(np.float64), want) <= TOL_F32
