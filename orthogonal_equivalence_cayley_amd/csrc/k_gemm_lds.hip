@@ -182,16 +182,25 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   const int wm0 = (wave / (BN / WN)) * WM;
   const int wn0 = (wave % (BN / WN)) * WN;
 
-  // XCD-aware tile order inside one group of the batch (blockIdx.z)
-  const int tn = gridDim.x, tm = gridDim.y, ntile = tn * tm;
-  int lin = blockIdx.y * tn + blockIdx.x;
-  if (ntile % 8 == 0) lin = (lin % 8) * (ntile / 8) + lin / 8;
-  const int grp = lin / (GM * tn);
-  const int first = grp * GM;
-  const int gsz = min(GM, tm - first);
-  const int in = lin - grp * GM * tn;
-  const int m0 = (first + in % gsz) * BM;
-  const int n0 = (in / gsz) * BN;
+  // Tiles of one group (blockIdx.z) in XCD-aware order: the 8 XCDs receive
+  // workgroups round-robin, so each XCD gets a contiguous range of the tile
+  // sequence, walked in groups of GM tile-rows (co-resident workgroups share A
+  // and B slices in their XCD's L2). Each workgroup runs `tpw` consecutive tiles
+  // of that sequence with one uninterrupted load pipeline.
+  const int tn = (p.N + BN - 1) / BN, tm = (p.M + BM - 1) / BM, ntile = tn * tm;
+  const int nwg = gridDim.x;
+  const int wlin = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int tpw = p.tpw;
+  const int t_first = wlin * tpw;
+  const int t_count = max(0, min(tpw, ntile - t_first));
+  auto tile_origin = [&](int lin, int& m0, int& n0) {
+    const int grp = lin / (GM * tn);
+    const int first = grp * GM;
+    const int gsz = min(GM, tm - first);
+    const int in = lin - grp * GM * tn;
+    m0 = (first + in % gsz) * BM;
+    n0 = (in / gsz) * BN;
+  };
 
   const int g = blockIdx.z / p.splits, sp = blockIdx.z - g * p.splits;
   const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + g * p.a_gs;
@@ -202,11 +211,6 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   const int kend = min(p.K, kbeg + kchunk);
   const int nk = kend > kbeg ? (kend - kbeg) / LBK : 0;
 
-  TA ta;
-  TB tb;
-  ta.init(A, p.lda, m0, p.M);
-  tb.init(B, p.ldb, n0, p.N);
-
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -215,19 +219,73 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  if (nk > 0) {
+  const int cm = lane & 31;
+  const int cn = (lane >> 5) * 4;
+  auto store_tile = [&](int m0, int n0) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm0 + i * 32 + cm;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn0 + j * 32 + q * 8 + cn;
+          if (n >= p.N) continue;
+          const long long o = g * p.c_gs + sp * p.c_ss + (long long)m * p.ldc + n;
+          if (OUTF32) {
+            float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                   acc[i][j][4 * q + 3]);
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) = v;
+          } else {
+            uint2 v;
+            v.x = pack_bf16_pair(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            v.y = pack_bf16_pair(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = v;
+          }
+        }
+      }
+    }
+  };
+
+  if (nk == 0) {   // empty K range of a split: its partial sums are zero
+    for (int i = 0; i < t_count; ++i) {
+      int m0, n0;
+      tile_origin(t_first + i, m0, n0);
+      store_tile(m0, n0);
+    }
+    return;
+  }
+
+  TA ta;
+  TB tb;
+  int cm0, cn0;   // origin of the tile being accumulated
+  tile_origin(t_first, cm0, cn0);
+  ta.init(A, p.lda, cm0, p.M);
+  tb.init(B, p.ldb, cn0, p.N);
+  const int total = t_count * nk;
+  if (total > 0) {
     ta.issue(lds, kbeg, p.lda, wave);
     tb.issue(lds + TA::BYTES, kbeg, p.ldb, wave);
   }
-  for (int t = 0; t < nk; ++t) {
+  int kt = 0, ti = 0;
+  for (int it = 0; it < total; ++it) {
     wait_vmcnt<0>();
-    lds_barrier();   // stage t visible to all waves; stage t-1 no longer read
-    if (t + 1 < nk) {
-      unsigned char* nx = lds + ((t + 1) & 1) * STAGE;
-      ta.issue(nx, kbeg + (t + 1) * LBK, p.lda, wave);
-      tb.issue(nx + TA::BYTES, kbeg + (t + 1) * LBK, p.ldb, wave);
+    lds_barrier();   // stage `it` visible to all waves; stage it-1 no longer read
+    if (it + 1 < total) {
+      int nkt = kt + 1;
+      if (nkt == nk) {   // next load starts the next tile
+        nkt = 0;
+        int nm0, nn0;
+        tile_origin(t_first + ti + 1, nm0, nn0);
+        ta.init(A, p.lda, nm0, p.M);
+        tb.init(B, p.ldb, nn0, p.N);
+      }
+      unsigned char* nx = lds + ((it + 1) & 1) * STAGE;
+      ta.issue(nx, kbeg + nkt * LBK, p.lda, wave);
+      tb.issue(nx + TA::BYTES, kbeg + nkt * LBK, p.ldb, wave);
     }
-    const unsigned char* sa = lds + (t & 1) * STAGE;
+    const unsigned char* sa = lds + (it & 1) * STAGE;
     const unsigned char* sb = sa + TA::BYTES;
     bf16x8 af[2][TM], bfr[2][TN];
 #pragma unroll
@@ -253,35 +311,20 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  (void)LOADS;
-
-  const int cm = lane & 31;
-  const int cn = (lane >> 5) * 4;
+    if (++kt == nk) {   // tile complete: write it out and start the next one
+      store_tile(cm0, cn0);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm0 + i * 32 + cm;
-    if (m >= p.M) continue;
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn0 + j * 32 + q * 8 + cn;
-        if (n >= p.N) continue;
-        const long long o = g * p.c_gs + sp * p.c_ss + (long long)m * p.ldc + n;
-        if (OUTF32) {
-          float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                 acc[i][j][4 * q + 3]);
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) = v;
-        } else {
-          uint2 v;
-          v.x = pack_bf16_pair(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-          v.y = pack_bf16_pair(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = v;
-        }
-      }
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      kt = 0;
+      ++ti;
+      if (ti < t_count) tile_origin(t_first + ti, cm0, cn0);
     }
   }
+  (void)LOADS;
 }
 
 // One symbol per role (as in the register-staged kernels) so profiles attribute
@@ -302,7 +345,8 @@ POETX_LDS_KERNEL(dq_gemm_tn_lds, false, false, true)
 template <int BM, int BN, int WM, int WN>
 hipError_t dispatch_lds(const GemmBf16& p, hipStream_t s) {
   constexpr int NW = (BM / WM) * (BN / WN);
-  dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, p.groups * p.splits);
+  const int ntile = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
+  dim3 grid((ntile + p.tpw - 1) / p.tpw, 1, p.groups * p.splits);
   // two LDS stages of (BM + BN) x 64 bf16
   const size_t lds = 2 * (size_t)(BM + BN) * LBK * 2;
   const int a = p.a_kmajor, b = p.b_kmajor, f = p.out_f32;
@@ -332,7 +376,18 @@ bool gemm_lds_supported(const GemmBf16& p, int bm, int bn) {
   return true;
 }
 
-hipError_t launch_gemm_lds(const GemmBf16& p, int big, hipStream_t s) {
+hipError_t launch_gemm_lds(const GemmBf16& p_in, int big, hipStream_t s) {
+  // tiles per workgroup: enough workgroups for one per CU (two for the small
+  // tile), the rest of the work streamed through each workgroup's pipeline
+  GemmBf16 p = p_in;
+  const int bm = big ? 256 : 128, bn = bm;
+  const long long ntile = (long long)((p.N + bn - 1) / bn) * ((p.M + bm - 1) / bm);
+  const long long total = ntile * p.groups * p.splits;
+  const long long slots = big ? 256 : 512;
+  long long tpw = (total + slots - 1) / slots;
+  tpw = tpw < 1 ? 1 : (tpw > 16 ? 16 : tpw);
+  if (tpw > ntile) tpw = ntile;
+  p.tpw = (int)tpw;
   if (big) return dispatch_lds<256, 256, 128, 64>(p, s);
   return dispatch_lds<128, 128, 64, 64>(p, s);
 }

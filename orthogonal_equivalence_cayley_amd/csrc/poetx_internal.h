@@ -73,6 +73,7 @@ struct GemmBf16 {
   long long a_gs, b_gs, c_gs;
   int groups, splits;
   long long c_ss;
+  int tpw;    // output tiles per workgroup (set by the launcher)
 };
 hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
 // Pipelined variant (direct-to-LDS loads, see k_gemm_lds.hip) for whole-tile shapes:
