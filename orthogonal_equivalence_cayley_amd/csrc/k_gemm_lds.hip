@@ -33,7 +33,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int LBK = 64;
 constexpr int GM = 4;   // tile-rows per group in the XCD-aware order
 
 template <int N>
@@ -51,20 +50,23 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
                                    (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
 }
 
-// ---- K-contiguous operand: R rows x 64 elements, 8 chunks of 16 B per row.
-// Chunk c of row r sits at 16-byte slot r * 8 + (c ^ ((r >> 1) & 7)): the 16 rows
-// read by one quarter-wave then cover all 64 banks.
-template <int R, int NT>
+// ---- K-contiguous operand: R rows x KB elements, KB / 8 chunks of 16 B per row.
+// Chunk c of row r sits at 16-byte slot r * CPR + (c ^ ((r / RPB) % CPR)), RPB rows
+// per 256-byte bank line: the 16 rows read by one quarter-wave then cover all 64
+// banks.
+template <int R, int NT, int KB>
 struct KTile {
-  static constexpr int SLOTS = R * 8;
+  static constexpr int CPR = KB / 8;
+  static constexpr int RPB = 256 / (KB * 2);
+  static constexpr int SLOTS = R * CPR;
   static constexpr int L = SLOTS / NT;   // loads per thread per stage
   const uint16_t* src[L];
   __device__ __forceinline__ void init(const uint16_t* base, long long ld, int row0, int rows) {
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int s = i * NT + threadIdx.x;
-      const int r = s >> 3, pos = s & 7;
-      const int c = pos ^ ((r >> 1) & 7);
+      const int r = s / CPR, pos = s % CPR;
+      const int c = pos ^ ((r / RPB) % CPR);
       const int gr = min(row0 + r, rows - 1);
       src[i] = base + (long long)gr * ld + c * 8;
     }
@@ -76,17 +78,17 @@ struct KTile {
   // 8 K-consecutive elements of row r at k = 16 * kk + 8 * half
   __device__ __forceinline__ static bf16x8 frag(const unsigned char* st, int r, int kk, int half) {
     const int c = 2 * kk + half;
-    return *reinterpret_cast<const bf16x8*>(st + (r * 8 + (c ^ ((r >> 1) & 7))) * 16);
+    return *reinterpret_cast<const bf16x8*>(st + (r * CPR + (c ^ ((r / RPB) % CPR))) * 16);
   }
 };
 
-// ---- row-contiguous operand: 64 K-rows x R elements (R / 8 chunks per K-row).
+// ---- row-contiguous operand: KB K-rows x R elements (R / 8 chunks per K-row).
 // Chunk c of K-row k sits at slot k * (R / 8) + (c ^ (4 * (k & 3))): the 4 K-rows x
 // 4 chunks touched by 32 lanes of a transposing read fall in distinct banks.
-template <int R, int NT>
+template <int R, int NT, int KB>
 struct MTile {
   static constexpr int CPR = R / 8;
-  static constexpr int SLOTS = LBK * CPR;
+  static constexpr int SLOTS = KB * CPR;
   static constexpr int L = SLOTS / NT;
   const uint16_t* src[L];
   __device__ __forceinline__ void init(const uint16_t* base, long long ld, int col0) {
@@ -127,13 +129,13 @@ struct MTile {
   }
 };
 
-template <int R, int NT, bool KMAJ>
+template <int R, int NT, int KB, bool KMAJ>
 struct Tile;
-template <int R, int NT>
-struct Tile<R, NT, true> {
-  KTile<R, NT> t;
-  static constexpr int BYTES = KTile<R, NT>::SLOTS * 16;
-  static constexpr int L = KTile<R, NT>::L;
+template <int R, int NT, int KB>
+struct Tile<R, NT, KB, true> {
+  KTile<R, NT, KB> t;
+  static constexpr int BYTES = KTile<R, NT, KB>::SLOTS * 16;
+  static constexpr int L = KTile<R, NT, KB>::L;
   __device__ __forceinline__ void init(const uint16_t* base, long long ld, int row0, int rows) {
     t.init(base, ld, row0, rows);
   }
@@ -141,14 +143,14 @@ struct Tile<R, NT, true> {
     t.issue(st, k0, wave);
   }
   __device__ __forceinline__ static bf16x8 frag(const unsigned char* st, int r0, int kk, int lane) {
-    return KTile<R, NT>::frag(st, r0 + (lane & 31), kk, lane >> 5);
+    return KTile<R, NT, KB>::frag(st, r0 + (lane & 31), kk, lane >> 5);
   }
 };
-template <int R, int NT>
-struct Tile<R, NT, false> {
-  MTile<R, NT> t;
-  static constexpr int BYTES = MTile<R, NT>::SLOTS * 16;
-  static constexpr int L = MTile<R, NT>::L;
+template <int R, int NT, int KB>
+struct Tile<R, NT, KB, false> {
+  MTile<R, NT, KB> t;
+  static constexpr int BYTES = MTile<R, NT, KB>::SLOTS * 16;
+  static constexpr int L = MTile<R, NT, KB>::L;
   __device__ __forceinline__ void init(const uint16_t* base, long long ld, int row0, int) {
     t.init(base, ld, row0);
   }
@@ -156,7 +158,7 @@ struct Tile<R, NT, false> {
     t.issue(st, k0, ld, wave);
   }
   __device__ __forceinline__ static bf16x8 frag(const unsigned char* st, int r0, int kk, int lane) {
-    return MTile<R, NT>::frag(st, r0, kk, lane);
+    return MTile<R, NT, KB>::frag(st, r0, kk, lane);
   }
 };
 
@@ -166,13 +168,25 @@ __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool OUTF32>
+// Outstanding direct-to-LDS loads allowed while waiting for the oldest stage:
+// the loads of the `pending` younger stages. Epilogue stores issued in between
+// are not counted, so the wait also covers them (never too short).
+template <int LOADS, int MAXP>
+__device__ __forceinline__ void wait_stage(int pending) {
+  if (MAXP >= 2 && pending >= 2) wait_vmcnt<LOADS * 2>();
+  else if (MAXP >= 1 && pending >= 1) wait_vmcnt<LOADS>();
+  else wait_vmcnt<0>();
+}
+
+template <int BM, int BN, int WM, int WN, int KB, int STAGES, bool AK, bool BKM, bool OUTF32>
 __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
+  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int NT = NW * 64;
   constexpr int TM = WM / 32, TN = WN / 32;
-  using TA = Tile<BM, NT, AK>;
-  using TB = Tile<BN, NT, BKM>;
+  constexpr int LBK = KB;
+  using TA = Tile<BM, NT, KB, AK>;
+  using TB = Tile<BN, NT, KB, BKM>;
   constexpr int STAGE = TA::BYTES + TB::BYTES;
   constexpr int LOADS = TA::L + TB::L;   // direct-to-LDS loads per thread per stage
   extern __shared__ __align__(16) unsigned char lds[];
@@ -221,27 +235,58 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
 
   const int cm = lane & 31;
   const int cn = (lane >> 5) * 4;
+  // Epilogue. Lane l holds C[row l & 31][cols 8q + 4(l >> 5) .. +3] of each 32x32
+  // tile (q = 0..3). bf16 output: lanes l and l ^ 32 swap half of their column
+  // groups so that each lane owns 8 consecutive columns (16-byte stores: the
+  // lower lane takes q = 0, 2, the upper q = 1, 3).
+  const bool upper = (lane >> 5) != 0;
   auto store_tile = [&](int m0, int n0) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = m0 + wm0 + i * 32 + cm;
-      if (m >= p.M) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
+        if (OUTF32) {
+          if (m >= p.M) continue;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn0 + j * 32 + q * 8 + cn;
-          if (n >= p.N) continue;
-          const long long o = g * p.c_gs + sp * p.c_ss + (long long)m * p.ldc + n;
-          if (OUTF32) {
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn0 + j * 32 + q * 8 + cn;
+            if (n >= p.N) continue;
+            const long long o = g * p.c_gs + sp * p.c_ss + (long long)m * p.ldc + n;
             float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                    acc[i][j][4 * q + 3]);
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) = v;
-          } else {
-            uint2 v;
-            v.x = pack_bf16_pair(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-            v.y = pack_bf16_pair(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) = v;
+          }
+        } else {
+          uint32_t w[4][2];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            w[q][0] = pack_bf16_pair(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            w[q][1] = pack_bf16_pair(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          }
+          // send the groups the partner lane completes: lower sends q = 1, 3
+          uint32_t snd[2][2], rcv[2][2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              snd[h][d] = upper ? w[2 * h][d] : w[2 * h + 1][d];
+              rcv[h][d] = (uint32_t)__shfl_xor((int)snd[h][d], 32);
+            }
+          if (m >= p.M) continue;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int q = 2 * h + (upper ? 1 : 0);
+            const int n = n0 + wn0 + j * 32 + q * 8;
+            if (n >= p.N) continue;
+            uint4 v;
+            if (upper) {   // cols 8q .. 8q+3 come from the partner, 8q+4 .. from here
+              v.x = rcv[h][0]; v.y = rcv[h][1]; v.z = w[q][0]; v.w = w[q][1];
+            } else {
+              v.x = w[q][0]; v.y = w[q][1]; v.z = rcv[h][0]; v.w = rcv[h][1];
+            }
+            const long long o = g * p.c_gs + sp * p.c_ss + (long long)m * p.ldc + n;
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + o) = v;
           }
         }
       }
@@ -264,28 +309,32 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   ta.init(A, p.lda, cm0, p.M);
   tb.init(B, p.ldb, cn0, p.N);
   const int total = t_count * nk;
-  if (total > 0) {
-    ta.issue(lds, kbeg, p.lda, wave);
-    tb.issue(lds + TA::BYTES, kbeg, p.ldb, wave);
-  }
+  // loads run STAGES - 1 stages ahead of the multiplies
+  int iss = 0, iss_kt = 0, iss_ti = 0;
+  auto issue_next = [&]() {
+    if (iss_kt == nk) {   // the next stage starts the next tile
+      iss_kt = 0;
+      ++iss_ti;
+      int nm0, nn0;
+      tile_origin(t_first + iss_ti, nm0, nn0);
+      ta.init(A, p.lda, nm0, p.M);
+      tb.init(B, p.ldb, nn0, p.N);
+    }
+    unsigned char* st = lds + (iss % STAGES) * STAGE;
+    ta.issue(st, kbeg + iss_kt * LBK, p.lda, wave);
+    tb.issue(st + TA::BYTES, kbeg + iss_kt * LBK, p.ldb, wave);
+    ++iss;
+    ++iss_kt;
+  };
+#pragma unroll
+  for (int i = 0; i < STAGES - 1; ++i)
+    if (iss < total) issue_next();
   int kt = 0, ti = 0;
   for (int it = 0; it < total; ++it) {
-    wait_vmcnt<0>();
+    wait_stage<LOADS, STAGES - 2>(iss - it - 1);
     lds_barrier();   // stage `it` visible to all waves; stage it-1 no longer read
-    if (it + 1 < total) {
-      int nkt = kt + 1;
-      if (nkt == nk) {   // next load starts the next tile
-        nkt = 0;
-        int nm0, nn0;
-        tile_origin(t_first + ti + 1, nm0, nn0);
-        ta.init(A, p.lda, nm0, p.M);
-        tb.init(B, p.ldb, nn0, p.N);
-      }
-      unsigned char* nx = lds + ((it + 1) & 1) * STAGE;
-      ta.issue(nx, kbeg + nkt * LBK, p.lda, wave);
-      tb.issue(nx + TA::BYTES, kbeg + nkt * LBK, p.ldb, wave);
-    }
-    const unsigned char* sa = lds + (it & 1) * STAGE;
+    if (iss < total) issue_next();
+    const unsigned char* sa = lds + (it % STAGES) * STAGE;
     const unsigned char* sb = sa + TA::BYTES;
     bf16x8 af[2][TM], bfr[2][TN];
 #pragma unroll
@@ -330,10 +379,10 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
 // One symbol per role (as in the register-staged kernels) so profiles attribute
 // time to the stage.
 #define POETX_LDS_KERNEL(NAME, AK, BKM, OF)                                        \
-  template <int BM, int BN, int WM, int WN>                                       \
+  template <int BM, int BN, int WM, int WN, int KB, int ST>                       \
   __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)                        \
   __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME(GemmBf16 p) {             \
-    gemm_lds_body<BM, BN, WM, WN, AK, BKM, OF>(p);                                \
+    gemm_lds_body<BM, BN, WM, WN, KB, ST, AK, BKM, OF>(p);                        \
   }
 POETX_LDS_KERNEL(w0_gemm_nt_lds, true, true, false)
 POETX_LDS_KERNEL(w0_gemm_nn_lds, true, false, false)
@@ -342,24 +391,24 @@ POETX_LDS_KERNEL(block_gemm_nn_lds, true, false, false)
 POETX_LDS_KERNEL(dq_gemm_tn_lds, false, false, true)
 #undef POETX_LDS_KERNEL
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int KB, int ST>
 hipError_t dispatch_lds(const GemmBf16& p, hipStream_t s) {
   constexpr int NW = (BM / WM) * (BN / WN);
   const int ntile = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
   dim3 grid((ntile + p.tpw - 1) / p.tpw, 1, p.groups * p.splits);
-  // two LDS stages of (BM + BN) x 64 bf16
-  const size_t lds = 2 * (size_t)(BM + BN) * LBK * 2;
+  // ST LDS stages of (BM + BN) x KB bf16
+  const size_t lds = ST * (size_t)(BM + BN) * KB * 2;
   const int a = p.a_kmajor, b = p.b_kmajor, f = p.out_f32;
   if (p.role == GEMM_W0 && a && b && !f)
-    hipLaunchKernelGGL((w0_gemm_nt_lds<BM, BN, WM, WN>), grid, dim3(NW * 64), lds, s, p);
+    hipLaunchKernelGGL((w0_gemm_nt_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
   else if (p.role == GEMM_W0 && a && !b && !f)
-    hipLaunchKernelGGL((w0_gemm_nn_lds<BM, BN, WM, WN>), grid, dim3(NW * 64), lds, s, p);
+    hipLaunchKernelGGL((w0_gemm_nn_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
   else if (p.role == GEMM_BLOCK && a && b && !f)
-    hipLaunchKernelGGL((block_gemm_nt_lds<BM, BN, WM, WN>), grid, dim3(NW * 64), lds, s, p);
+    hipLaunchKernelGGL((block_gemm_nt_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
   else if (p.role == GEMM_BLOCK && a && !b && !f)
-    hipLaunchKernelGGL((block_gemm_nn_lds<BM, BN, WM, WN>), grid, dim3(NW * 64), lds, s, p);
+    hipLaunchKernelGGL((block_gemm_nn_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
   else if (p.role == GEMM_DQ && !a && !b && f)
-    hipLaunchKernelGGL((dq_gemm_tn_lds<BM, BN, WM, WN>), grid, dim3(NW * 64), lds, s, p);
+    hipLaunchKernelGGL((dq_gemm_tn_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -368,10 +417,11 @@ hipError_t dispatch_lds(const GemmBf16& p, hipStream_t s) {
 }  // namespace
 
 bool gemm_lds_supported(const GemmBf16& p, int bm, int bn) {
-  if (p.K % LBK != 0) return false;
+  if (p.K % 64 != 0) return false;
   if (p.lda % 8 || p.ldb % 8 || p.ldc % 4) return false;
   if (!p.a_kmajor && p.M % bm) return false;
   if (!p.b_kmajor && p.N % bn) return false;
+  if (!p.out_f32 && p.N % 8) return false;   // 16-byte epilogue stores
   if (((uintptr_t)p.A | (uintptr_t)p.B) & 15) return false;
   return true;
 }
@@ -388,8 +438,8 @@ hipError_t launch_gemm_lds(const GemmBf16& p_in, int big, hipStream_t s) {
   tpw = tpw < 1 ? 1 : (tpw > 16 ? 16 : tpw);
   if (tpw > ntile) tpw = ntile;
   p.tpw = (int)tpw;
-  if (big) return dispatch_lds<256, 256, 128, 64>(p, s);
-  return dispatch_lds<128, 128, 64, 64>(p, s);
+  if (big) return dispatch_lds<256, 256, 128, 64, 64, 2>(p, s);
+  return dispatch_lds<128, 128, 64, 64, 64, 2>(p, s);
 }
 
 }  // namespace poetx
