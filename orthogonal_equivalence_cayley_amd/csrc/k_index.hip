@@ -107,6 +107,135 @@ __global__ __launch_bounds__(kThreads) void scatter_cols_kernel(
   }
 }
 
+// Interleaved variants: G = 8 / sizeof(E) rows share one 8-byte LDS word per
+// column (word c of row group g holds element c of rows 4g..4g+3 for bf16), so
+// one random LDS access moves the element of G rows. Rows are read and written
+// with coalesced 16-byte accesses; the interleave happens in registers.
+template <typename E>
+struct Inter {
+  static constexpr int G = 8 / sizeof(E);    // rows per word
+  static constexpr int VEC = 16 / sizeof(E); // elements per 16-byte chunk
+  static constexpr int BITS = 8 * sizeof(E);
+  __device__ __forceinline__ static uint64_t elem(const uint4& v, int e) {
+    const uint32_t w = (e * BITS / 32) == 0 ? v.x : (e * BITS / 32) == 1 ? v.y : (e * BITS / 32) == 2 ? v.z : v.w;
+    if (BITS == 32) return w;
+    return (e & 1) ? (w >> 16) : (w & 0xffffu);
+  }
+};
+
+// out[t][i] = in[row(t)][idx[i]] for R rows per iteration (R a multiple of G).
+template <typename E>
+__global__ __launch_bounds__(kThreads) void gather_cols_inter(
+    const E* __restrict__ in, long long in_ld, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ idx, E* __restrict__ out, long long T, int dim, int R) {
+  using I = Inter<E>;
+  constexpr int G = I::G, VEC = I::VEC, BITS = I::BITS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint64_t* lds = reinterpret_cast<uint64_t*>(smem);   // [R / G][dim]
+  const int cpr = dim / VEC;
+  const int ngrp = R / G;
+  for (long long t0 = (long long)blockIdx.x * R; t0 < T; t0 += (long long)gridDim.x * R) {
+    const int nr = (int)((T - t0) < R ? (T - t0) : R);
+    // load G rows x VEC elements per item, interleave, write VEC words
+    for (int c = threadIdx.x; c < ngrp * cpr; c += kThreads) {
+      const int g = c / cpr, q = c - g * cpr;
+      uint4 v[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        const int rr = min(g * G + r, nr - 1);
+        const long long src_row = rows ? (long long)rows[t0 + rr] : (t0 + rr);
+        v[r] = reinterpret_cast<const uint4*>(in + src_row * in_ld)[q];
+      }
+      uint64_t* dst = lds + (long long)g * dim + q * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        uint64_t wv = 0;
+#pragma unroll
+        for (int r = 0; r < G; ++r) wv |= I::elem(v[r], e) << (BITS * r);
+        dst[e] = wv;
+      }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < ngrp * cpr; c += kThreads) {
+      const int g = c / cpr, q = c - g * cpr;
+      const uint64_t* src = lds + (long long)g * dim;
+      uint64_t wv[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) wv[e] = src[idx[q * VEC + e]];
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        const int row = g * G + r;
+        if (row >= nr) break;
+        uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const uint32_t x = (uint32_t)((wv[e] >> (BITS * r)) & (BITS == 32 ? 0xffffffffull : 0xffffull));
+          if (BITS == 32) o[e] = x;
+          else o[e >> 1] |= x << (16 * (e & 1));
+        }
+        reinterpret_cast<uint4*>(out + (t0 + row) * dim)[q] = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// out[t][idx[i]] = in[t][i]: rows interleaved into LDS at their destination
+// columns, then written out row by row.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void scatter_cols_inter(
+    const E* __restrict__ in, const int32_t* __restrict__ idx, E* __restrict__ out, long long T,
+    int dim, int R) {
+  using I = Inter<E>;
+  constexpr int G = I::G, VEC = I::VEC, BITS = I::BITS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint64_t* lds = reinterpret_cast<uint64_t*>(smem);
+  const int cpr = dim / VEC;
+  const int ngrp = R / G;
+  for (long long t0 = (long long)blockIdx.x * R; t0 < T; t0 += (long long)gridDim.x * R) {
+    const int nr = (int)((T - t0) < R ? (T - t0) : R);
+    for (int c = threadIdx.x; c < ngrp * cpr; c += kThreads) {
+      const int g = c / cpr, q = c - g * cpr;
+      uint4 v[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        const int rr = min(g * G + r, nr - 1);
+        v[r] = reinterpret_cast<const uint4*>(in + (t0 + rr) * dim)[q];
+      }
+      uint64_t* dst = lds + (long long)g * dim;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        uint64_t wv = 0;
+#pragma unroll
+        for (int r = 0; r < G; ++r) wv |= I::elem(v[r], e) << (BITS * r);
+        dst[idx[q * VEC + e]] = wv;
+      }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < ngrp * cpr; c += kThreads) {
+      const int g = c / cpr, q = c - g * cpr;
+      const uint64_t* src = lds + (long long)g * dim + q * VEC;
+      uint64_t wv[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) wv[e] = src[e];
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        const int row = g * G + r;
+        if (row >= nr) break;
+        uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const uint32_t x = (uint32_t)((wv[e] >> (BITS * r)) & (BITS == 32 ? 0xffffffffull : 0xffffull));
+          if (BITS == 32) o[e] = x;
+          else o[e >> 1] |= x << (16 * (e & 1));
+        }
+        reinterpret_cast<uint4*>(out + (t0 + row) * dim)[q] = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Rows of `dim` elements too wide for LDS: plain per-element global access.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void gather_cols_direct(
@@ -144,9 +273,17 @@ hipError_t gather_typed(const void* in, long long in_ld, const int32_t* rows, co
   }
   int R = (int)(kLdsBudget / row_bytes);
   if (R > 8) R = 8;
-  const size_t lds = (size_t)R * row_bytes;
   const bool vec = (dim % VEC == 0) && (in_ld % VEC == 0) &&
                    ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
+  constexpr int G = 8 / sizeof(E);
+  if (vec && R >= G) {
+    R = R / G * G;
+    const size_t lds = (size_t)R * row_bytes;
+    hipLaunchKernelGGL((gather_cols_inter<E>), dim3(grid_for((T + R - 1) / R)), dim3(kThreads),
+                       lds, s, (const E*)in, in_ld, rows, idx, (E*)out, T, dim, R);
+    return hipGetLastError();
+  }
+  const size_t lds = (size_t)R * row_bytes;
   const int grid = grid_for((T + R - 1) / R);
   if (vec)
     hipLaunchKernelGGL((gather_cols_kernel<E, true>), dim3(grid), dim3(kThreads), lds, s,
@@ -170,8 +307,16 @@ hipError_t scatter_typed(const void* in, const int32_t* idx, void* out, long lon
   }
   int R = (int)(kLdsBudget / row_bytes);
   if (R > 8) R = 8;
-  const size_t lds = (size_t)R * row_bytes;
   const bool vec = (dim % VEC == 0) && ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
+  constexpr int G = 8 / sizeof(E);
+  if (vec && R >= G) {
+    R = R / G * G;
+    const size_t lds = (size_t)R * row_bytes;
+    hipLaunchKernelGGL((scatter_cols_inter<E>), dim3(grid_for((T + R - 1) / R)), dim3(kThreads),
+                       lds, s, (const E*)in, idx, (E*)out, T, dim, R);
+    return hipGetLastError();
+  }
+  const size_t lds = (size_t)R * row_bytes;
   const int grid = grid_for((T + R - 1) / R);
   if (vec)
     hipLaunchKernelGGL((scatter_cols_kernel<E, true>), dim3(grid), dim3(kThreads), lds, s,
