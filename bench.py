@@ -107,7 +107,7 @@ def main() -> int:
     import torch
 
     import workloads
-    from orthogonal_equivalence_cayley_amd import PoetxLayer, build_many, poetx
+    from orthogonal_equivalence_cayley_amd import PoetxLayer, build_many, param_grad_many, poetx
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = workloads.WORKLOADS[args.workload]
@@ -132,6 +132,8 @@ def main() -> int:
         L.workspace(poetx.WS_FORWARD, T)
         if w.backward:
             L.workspace(poetx.WS_BACKWARD, T)
+            L._ws_grad(0)
+            L._ws_grad(1)
         layers.append(L)
         bufs.append(b)
         del inp
@@ -143,8 +145,11 @@ def main() -> int:
         for L, b in zip(layers, bufs):
             L.forward(b["X"], Y=b["Y"], Wa=b["Wa"])
         if w.backward:
+            # activation path layer by layer, then the chain rule through the
+            # parameterisation of all layers in one batched call
             for L, b in zip(reversed(layers), reversed(bufs)):
-                L.backward(b["X"], b["G"], G_X=b["GX"], g_theta=b["g"])
+                L.backward_dq(b["X"], b["G"], G_X=b["GX"])
+            param_grad_many(layers, [b["g"] for b in bufs])
 
     for _ in range(args.warmup):
         step()

@@ -58,7 +58,12 @@ typedef enum {
 
 typedef enum { POETX_FP32 = 0, POETX_BF16 = 1 } poetx_dtype;
 typedef enum { POETX_SIDE_R = 0, POETX_SIDE_P = 1 } poetx_side;
-typedef enum { POETX_WS_BUILD = 0, POETX_WS_FORWARD = 1, POETX_WS_BACKWARD = 2 } poetx_ws_kind;
+typedef enum {
+  POETX_WS_BUILD = 0,       /* poetx_build_orth, one item of poetx_build_orth_batch */
+  POETX_WS_FORWARD = 1,     /* poetx_forward                                        */
+  POETX_WS_BACKWARD = 2,    /* poetx_backward and poetx_backward_dq                  */
+  POETX_WS_PARAM_GRAD = 3   /* one item of poetx_param_grad_batch (T is ignored)     */
+} poetx_ws_kind;
 
 typedef struct poetx_plan poetx_plan;   /* opaque, immutable after create */
 
@@ -160,6 +165,31 @@ poetx_status poetx_backward(const poetx_plan* plan, int64_t T, const void* X, co
                             const void* Q_R, const void* Q_P, const void* Wa_saved,
                             const void* G_Y, void* G_X, float* g_theta_R, float* g_theta_P,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* The backward split in two, so that the chain rule through the parameterisation
+ * of many layers can share launches:
+ *   poetx_backward_dq: the activation path of poetx_backward. Writes G_X and
+ *     dL/dQ of both sides (fp32, block layout of poetx_build_orth: dQ_R has
+ *     poetx_block_elems(R) floats, dQ_P poetx_block_elems(P)), where Q is the
+ *     block array the forward used. Same arguments and workspace as
+ *     poetx_backward otherwise. T = 0 writes zero dQ.
+ *   poetx_param_grad_batch: dL/dQ -> packed parameter gradient for count
+ *     independent (plan, side) items: item i reads thetas[i] and dQs[i] (device
+ *     fp32) and overwrites g_thetas[i] (device fp32, poetx_param_count floats),
+ *     with its own workspace ws[i] of ws_bytes[i] >= poetx_workspace_size(
+ *     plans[i], 0, POETX_WS_PARAM_GRAD). Host arrays of pointers. All items are
+ *     checked before anything is launched.
+ * poetx_backward(...) equals poetx_backward_dq(...) followed by
+ * poetx_param_grad_batch over its two sides. */
+poetx_status poetx_backward_dq(const poetx_plan* plan, int64_t T, const void* X, const void* Wt,
+                               const int32_t* pi_R, const int32_t* pi_P,
+                               const void* Q_R, const void* Q_P, const void* Wa_saved,
+                               const void* G_Y, void* G_X, float* dQ_R, float* dQ_P,
+                               void* ws, size_t ws_bytes, void* stream);
+poetx_status poetx_param_grad_batch(int32_t count, const poetx_plan* const* plans,
+                                    const int32_t* sides, const float* const* thetas,
+                                    const float* const* dQs, float* const* g_thetas,
+                                    void* const* ws, const size_t* ws_bytes, void* stream);
 
 /* Single index operations, exposed for testing and for callers that apply the
  * permutations themselves ([PX] §2.B: index mapping, no permutation matrix).

@@ -5,6 +5,6 @@ by build_lib.build()); `PoetxLayer` wraps one layer's device buffers. Importing
 the package fails if the library has not been built.
 """
 from . import poetx  # noqa: F401  (loads libpoetx.so, raises if missing)
-from .layer import PoetxLayer, build_many  # noqa: F401
+from .layer import PoetxLayer, build_many, param_grad_many  # noqa: F401
 
-__all__ = ["poetx", "PoetxLayer", "build_many"]
+__all__ = ["poetx", "PoetxLayer", "build_many", "param_grad_many"]

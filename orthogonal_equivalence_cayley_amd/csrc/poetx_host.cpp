@@ -123,9 +123,28 @@ struct FwdWs { void *U, *V, *Wa, *Z; };
 struct BwdWs {
   void *GZ, *GWa, *GV, *U, *GU;
   float *dQ[2], *part;
-  float *Sside[2], *Tside[2], *Aside[2];      // fused chains, per side
-  float *A0, *A1, *T0, *T1;                   // generic chain path
 };
+
+// Buffers of the chain rule through the parameterisation, for one side.
+struct ChainWs {
+  float *S, *T, *A;            // fused chains: generators, T_1^T, stored A_j
+  float *A0, *A1, *T0, *T1;    // generic path (block sizes the fused chain skips)
+};
+
+size_t layout_chain(const poetx_plan* pl, int side, Carver& c, ChainWs* w) {
+  const size_t start = c.off;
+  const long long ne = pl->nelem[side];
+  ChainWs x;
+  x.S = (float*)c.take(4 * ne);
+  x.T = (float*)c.take(4 * ne);
+  x.A = (float*)c.take(4 * ne * (pl->k + 1));
+  x.A0 = (float*)c.take(4 * ne);
+  x.A1 = (float*)c.take(4 * ne);
+  x.T0 = (float*)c.take(4 * ne);
+  x.T1 = (float*)c.take(4 * ne);
+  if (w) *w = x;
+  return c.off - start;
+}
 
 size_t layout_fwd(const poetx_plan* pl, long long T, void* base, FwdWs* w) {
   Carver c(base);
@@ -139,7 +158,8 @@ size_t layout_fwd(const poetx_plan* pl, long long T, void* base, FwdWs* w) {
   return c.off;
 }
 
-size_t layout_bwd(const poetx_plan* pl, long long T, void* base, BwdWs* w) {
+// backward workspace: activation path, then (for poetx_backward) both sides' chains
+size_t layout_bwd(const poetx_plan* pl, long long T, void* base, BwdWs* w, ChainWs* cw) {
   Carver c(base);
   const size_t es = elsize(pl);
   BwdWs x;
@@ -154,17 +174,14 @@ size_t layout_bwd(const poetx_plan* pl, long long T, void* base, BwdWs* w) {
   for (int side = 0; side < 2; ++side)
     part = std::max(part, (long long)dq_splits(pl, side, T) * pl->nelem[side]);
   x.part = (float*)c.take(4 * part);
-  for (int side = 0; side < 2; ++side) {
-    x.Sside[side] = (float*)c.take(4 * pl->nelem[side]);
-    x.Tside[side] = (float*)c.take(4 * pl->nelem[side]);
-    x.Aside[side] = (float*)c.take(4 * pl->nelem[side] * (pl->k + 1));
-  }
-  const long long ne = std::max(pl->nelem[0], pl->nelem[1]);
-  x.A0 = (float*)c.take(4 * ne);
-  x.A1 = (float*)c.take(4 * ne);
-  x.T0 = (float*)c.take(4 * ne);
-  x.T1 = (float*)c.take(4 * ne);
   if (w) *w = x;
+  for (int side = 0; side < 2; ++side) layout_chain(pl, side, c, cw ? &cw[side] : nullptr);
+  return c.off;
+}
+
+size_t layout_param_grad(const poetx_plan* pl, int side, void* base, ChainWs* cw) {
+  Carver c(base);
+  layout_chain(pl, side, c, cw);
   return c.off;
 }
 
@@ -277,19 +294,27 @@ poetx_status block_grads(const poetx_plan* pl, int side, long long T, const void
   return POETX_OK;
 }
 
-// Reverse mode through Q = sum_j c_j S^j for every block of both sides:
+// One chain-rule item: dL/dQ of one side of one plan -> packed parameter gradient.
+struct GradItem {
+  const poetx_plan* pl;
+  int side;
+  const float* theta;
+  const float* dQ;
+  float* g;
+  ChainWs w;
+};
+
+// Reverse mode through Q = sum_j c_j S^j for every block of every item:
 //   A_{k+1} = c_{k+1} G,  A_j = c_j G + A_{j+1} S^T,
 //   T_{k+1} = A_{k+1},    T_j = A_j + S^T T_{j+1},   dL/dS = T_1,
 // then dL/dtheta(i,j) = dS[i][j] - dS[j][i]. Uses S^T = -S. Runs of supported
-// block sizes go through the fused row-panel chains, both sides in one launch
-// per chain; other sizes step through batched fp32 GEMMs.
-poetx_status cnp_backward(const poetx_plan* pl, const float* const theta[2], float* const gtheta[2],
-                          const BwdWs& w, hipStream_t s) {
-  const int k = pl->k;
+// block sizes of all items share one launch per chain (items with one Neumann
+// order per launch); other sizes step through batched fp32 GEMMs.
+poetx_status grad_items(const GradItem* items, int count, hipStream_t s) {
   poetx::TriBatch ub{}, pb{};
   poetx::ChainBatch ab{}, tb{};
-  ab.k = tb.k = k;
   pb.sign = -1.0f;   // T_1^T is stored: g(i,j) = T^T[j][i] - T^T[i][j]
+  int kk = -1;
   auto flush = [&]() -> poetx_status {
     HIP_TRY(poetx::launch_unpack_batch(ub, s));
     HIP_TRY(poetx::launch_chain_batch(poetx::CHAIN_ABAR, ab, s));
@@ -298,57 +323,129 @@ poetx_status cnp_backward(const poetx_plan* pl, const float* const theta[2], flo
     ub.n = pb.n = ab.n = tb.n = 0;
     return POETX_OK;
   };
-  for (int side = 0; side < 2; ++side) {
-    for (const Seg& g : pl->segs[side]) {
+  poetx_status st;
+  for (int i = 0; i < count; ++i) {
+    const GradItem& it = items[i];
+    const poetx_plan* pl = it.pl;
+    if (kk != -1 && kk != pl->k && (st = flush()) != POETX_OK) return st;
+    kk = pl->k;
+    ab.k = tb.k = kk;
+    for (const Seg& g : pl->segs[it.side]) {
       if (!poetx::chain_supported(g.b)) continue;
-      if (ab.n == poetx::kChainMaxEntries) {
-        poetx_status st = flush();
-        if (st != POETX_OK) return st;
-      }
-      float* S = w.Sside[side] + g.q_off;
-      ub.e[ub.n++] = poetx::TriEntry{theta[side] + g.p_off, S, g.b, g.count, 0};
+      if (ab.n == poetx::kChainMaxEntries && (st = flush()) != POETX_OK) return st;
+      float* S = it.w.S + g.q_off;
+      ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, S, g.b, g.count, 0};
       poetx::ChainEntry e{};
-      e.S = S; e.b = g.b; e.count = g.count; e.stride = pl->nelem[side];
-      e.G = w.dQ[side] + g.q_off;
-      e.out = w.Aside[side] + g.q_off;
+      e.S = S; e.b = g.b; e.count = g.count; e.stride = pl->nelem[it.side];
+      e.G = it.dQ + g.q_off;
+      e.out = it.w.A + g.q_off;
       ab.e[ab.n++] = e;
-      e.G = w.Aside[side] + g.q_off;
-      e.out = w.Tside[side] + g.q_off;
+      e.G = it.w.A + g.q_off;
+      e.out = it.w.T + g.q_off;
       tb.e[tb.n++] = e;
-      pb.e[pb.n++] = poetx::TriEntry{w.Tside[side] + g.q_off, gtheta[side] + g.p_off, g.b, g.count, 0};
+      pb.e[pb.n++] = poetx::TriEntry{it.w.T + g.q_off, it.g + g.p_off, g.b, g.count, 0};
     }
   }
-  poetx_status st = flush();
-  if (st != POETX_OK) return st;
-  for (int side = 0; side < 2; ++side) {
+  if ((st = flush()) != POETX_OK) return st;
+  for (int i = 0; i < count; ++i) {
+    const GradItem& it = items[i];
+    const poetx_plan* pl = it.pl;
+    const int side = it.side, k = pl->k;
     bool any = false;
     for (const Seg& g : pl->segs[side]) any |= !poetx::chain_supported(g.b);
     if (!any) continue;
     const long long ne = pl->nelem[side];
-    float* S = w.Sside[side];
-    const float* G = w.dQ[side];
+    const ChainWs& w = it.w;
+    const float* G = it.dQ;
     for (const Seg& g : pl->segs[side])
       if (!poetx::chain_supported(g.b))
-        HIP_TRY(poetx::launch_unpack_skew(theta[side], g, S, nullptr, 0.0f, s));
+        HIP_TRY(poetx::launch_unpack_skew(it.theta, g, w.S, nullptr, 0.0f, s));
     HIP_TRY(poetx::launch_scale2(G, coef(k + 1, k), w.A0, w.T1, ne, s));
     float *Acur = w.A0, *Anew = w.A1, *Tcur = w.T1, *Tnew = w.T0;
     for (int j = k; j >= 1; --j) {
       for (const Seg& g : pl->segs[side]) {
         if (poetx::chain_supported(g.b)) continue;
         // A_j = c_j G - A_{j+1} S
-        st = chain_gemm(g, Acur, S, Anew, G, nullptr, -1.0f, coef(j, k), s);
-        if (st != POETX_OK) return st;
+        if ((st = chain_gemm(g, Acur, w.S, Anew, G, nullptr, -1.0f, coef(j, k), s)) != POETX_OK)
+          return st;
         // T_j = A_j - S T_{j+1}
-        st = chain_gemm(g, S, Tcur, Tnew, Anew, nullptr, -1.0f, 1.0f, s);
-        if (st != POETX_OK) return st;
+        if ((st = chain_gemm(g, w.S, Tcur, Tnew, Anew, nullptr, -1.0f, 1.0f, s)) != POETX_OK)
+          return st;
       }
       std::swap(Acur, Anew);
       std::swap(Tcur, Tnew);
     }
     for (const Seg& g : pl->segs[side])
       if (!poetx::chain_supported(g.b))
-        HIP_TRY(poetx::launch_pack_antisym(Tcur, g, 1.0f, gtheta[side], s));
+        HIP_TRY(poetx::launch_pack_antisym(Tcur, g, 1.0f, it.g, s));
   }
+  return POETX_OK;
+}
+
+// Activation path of the backward (everything but the chain rule through the
+// parameterisation): G_X and dL/dQ of both sides (fp32).
+poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const void* Wt,
+                         const int32_t* pi_R, const int32_t* pi_P, const void* Q_R, const void* Q_P,
+                         const void* Wa_saved, const void* G_Y, void* G_X, float* const dQ[2],
+                         const BwdWs& w, hipStream_t s) {
+  const int es = elsize(pl);
+  poetx_status st;
+  if (T == 0) {
+    HIP_TRY(poetx::launch_zero(dQ[0], pl->nelem[0], s));
+    HIP_TRY(poetx::launch_zero(dQ[1], pl->nelem[1], s));
+    return POETX_OK;
+  }
+  // R side: G_Z = G_Y Pi_R^T; dQ_R = G_Z^T Wa per block; G_Wa = G_Z D_R
+  {
+    StageScope sc(POETX_STAGE_GATHER, s);
+    HIP_TRY(poetx::launch_gather_cols(G_Y, pl->m, nullptr, pi_R, w.GZ, T, pl->m, es, s));
+  }
+  {
+    StageScope sc(POETX_STAGE_DQ, s);
+    if ((st = block_grads(pl, POETX_SIDE_R, T, w.GZ, Wa_saved, w.part, dQ[0], s)) != POETX_OK)
+      return st;
+  }
+  {
+    StageScope sc(POETX_STAGE_BLOCK_BWD, s);
+    if ((st = apply_blocks(pl, POETX_SIDE_R, T, w.GZ, Q_R, w.GWa, false, s)) != POETX_OK) return st;
+  }
+  // frozen weight: G_V = G_Wa Wt
+  {
+    StageScope sc(POETX_STAGE_W0_BWD, s);
+    if ((st = gemm(pl, poetx::GEMM_W0, Op{w.GWa, pl->m, 1}, Op{Wt, 1, pl->n}, w.GV, pl->n, (int)T,
+                   pl->n, pl->m, 1, 0, 0, 0, 1, 0, false, s)) != POETX_OK)
+      return st;
+  }
+  // P side: U = X Pi_P^T; dQ_P = G_V^T U per block; G_U = G_V D_P; G_X = G_U Pi_P
+  {
+    StageScope sc(POETX_STAGE_GATHER, s);
+    HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
+  }
+  {
+    StageScope sc(POETX_STAGE_DQ, s);
+    if ((st = block_grads(pl, POETX_SIDE_P, T, w.GV, w.U, w.part, dQ[1], s)) != POETX_OK) return st;
+  }
+  {
+    StageScope sc(POETX_STAGE_BLOCK_BWD, s);
+    if ((st = apply_blocks(pl, POETX_SIDE_P, T, w.GV, Q_P, w.GU, false, s)) != POETX_OK) return st;
+  }
+  {
+    StageScope sc(POETX_STAGE_SCATTER, s);
+    HIP_TRY(poetx::launch_scatter_cols(w.GU, pi_P, G_X, T, pl->n, es, s));
+  }
+  return POETX_OK;
+}
+
+poetx_status check_backward_args(const poetx_plan* pl, long long T, const void* X, const void* Wt,
+                                 const int32_t* pi_R, const int32_t* pi_P, const void* Q_R,
+                                 const void* Q_P, const void* Wa_saved, const void* G_Y,
+                                 const void* G_X, const void* ws, size_t ws_bytes) {
+  if (!pl || T < 0) return POETX_ERR_INVALID_ARG;
+  if (T > 0 && (!X || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !Wa_saved || !G_Y || !G_X))
+    return POETX_ERR_INVALID_ARG;
+  for (const void* p : {X, Wt, (const void*)pi_R, (const void*)pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X, ws})
+    if (!aligned16(p)) return POETX_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < poetx_workspace_size(pl, T, POETX_WS_BACKWARD)) return POETX_ERR_WORKSPACE;
   return POETX_OK;
 }
 
@@ -515,7 +612,13 @@ size_t poetx_workspace_size(const poetx_plan* pl, int64_t T, int32_t kind) {
   switch (kind) {
     case POETX_WS_BUILD: return layout_build(pl, nullptr, nullptr, nullptr, nullptr);
     case POETX_WS_FORWARD: return layout_fwd(pl, T, nullptr, nullptr);
-    case POETX_WS_BACKWARD: return layout_bwd(pl, T, nullptr, nullptr);
+    case POETX_WS_BACKWARD: return layout_bwd(pl, T, nullptr, nullptr, nullptr);
+    case POETX_WS_PARAM_GRAD: {
+      size_t mx = 0;
+      for (int side = 0; side < 2; ++side)
+        mx = std::max(mx, layout_param_grad(pl, side, nullptr, nullptr));
+      return mx;
+    }
   }
   return 0;
 }
@@ -611,68 +714,68 @@ poetx_status poetx_backward(const poetx_plan* pl, int64_t T, const void* X, cons
                             const float* theta_P, const void* Q_R, const void* Q_P,
                             const void* Wa_saved, const void* G_Y, void* G_X, float* g_theta_R,
                             float* g_theta_P, void* ws, size_t ws_bytes, void* stream) {
-  if (!pl || T < 0) return POETX_ERR_INVALID_ARG;
+  poetx_status st = check_backward_args(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X,
+                                        ws, ws_bytes);
+  if (st != POETX_OK) return st;
   if (!theta_R || !theta_P || !g_theta_R || !g_theta_P) return POETX_ERR_INVALID_ARG;
-  if (T > 0 && (!X || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !Wa_saved || !G_Y || !G_X))
-    return POETX_ERR_INVALID_ARG;
-  for (const void* p : {X, Wt, (const void*)pi_R, (const void*)pi_P, (const void*)theta_R,
-                        (const void*)theta_P, Q_R, Q_P, Wa_saved, G_Y, (const void*)G_X,
-                        (const void*)g_theta_R, (const void*)g_theta_P, (const void*)ws})
+  for (const void* p : {(const void*)theta_R, (const void*)theta_P, (const void*)g_theta_R,
+                        (const void*)g_theta_P})
     if (!aligned16(p)) return POETX_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < poetx_workspace_size(pl, T, POETX_WS_BACKWARD)) return POETX_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   BwdWs w;
-  layout_bwd(pl, T, ws, &w);
-  const int es = elsize(pl);
-  poetx_status st;
-  if (T > 0) {
-    // R side: G_Z = G_Y Pi_R^T; dQ_R = G_Z^T Wa per block; G_Wa = G_Z D_R
-    {
-      StageScope sc(POETX_STAGE_GATHER, s);
-      HIP_TRY(poetx::launch_gather_cols(G_Y, pl->m, nullptr, pi_R, w.GZ, T, pl->m, es, s));
-    }
-    {
-      StageScope sc(POETX_STAGE_DQ, s);
-      if ((st = block_grads(pl, POETX_SIDE_R, T, w.GZ, Wa_saved, w.part, w.dQ[0], s)) != POETX_OK)
-        return st;
-    }
-    {
-      StageScope sc(POETX_STAGE_BLOCK_BWD, s);
-      if ((st = apply_blocks(pl, POETX_SIDE_R, T, w.GZ, Q_R, w.GWa, false, s)) != POETX_OK) return st;
-    }
-    // frozen weight: G_V = G_Wa Wt
-    {
-      StageScope sc(POETX_STAGE_W0_BWD, s);
-      if ((st = gemm(pl, poetx::GEMM_W0, Op{w.GWa, pl->m, 1}, Op{Wt, 1, pl->n}, w.GV, pl->n, (int)T,
-                     pl->n, pl->m, 1, 0, 0, 0, 1, 0, false, s)) != POETX_OK)
-        return st;
-    }
-    // P side: U = X Pi_P^T; dQ_P = G_V^T U per block; G_U = G_V D_P; G_X = G_U Pi_P
-    {
-      StageScope sc(POETX_STAGE_GATHER, s);
-      HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
-    }
-    {
-      StageScope sc(POETX_STAGE_DQ, s);
-      if ((st = block_grads(pl, POETX_SIDE_P, T, w.GV, w.U, w.part, w.dQ[1], s)) != POETX_OK)
-        return st;
-    }
-    {
-      StageScope sc(POETX_STAGE_BLOCK_BWD, s);
-      if ((st = apply_blocks(pl, POETX_SIDE_P, T, w.GV, Q_P, w.GU, false, s)) != POETX_OK) return st;
-    }
-    {
-      StageScope sc(POETX_STAGE_SCATTER, s);
-      HIP_TRY(poetx::launch_scatter_cols(w.GU, pi_P, G_X, T, pl->n, es, s));
-    }
-  } else {
-    HIP_TRY(poetx::launch_zero(w.dQ[0], pl->nelem[0], s));
-    HIP_TRY(poetx::launch_zero(w.dQ[1], pl->nelem[1], s));
-  }
+  ChainWs cw[2];
+  layout_bwd(pl, T, ws, &w, cw);
+  if ((st = backward_dq(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X, w.dQ, w, s)) !=
+      POETX_OK)
+    return st;
   StageScope sc(POETX_STAGE_CNP_BWD, s);
-  const float* const th[2] = {theta_R, theta_P};
-  float* const gt[2] = {g_theta_R, g_theta_P};
-  return cnp_backward(pl, th, gt, w, s);
+  const GradItem items[2] = {{pl, POETX_SIDE_R, theta_R, w.dQ[0], g_theta_R, cw[0]},
+                             {pl, POETX_SIDE_P, theta_P, w.dQ[1], g_theta_P, cw[1]}};
+  return grad_items(items, 2, s);
+}
+
+poetx_status poetx_backward_dq(const poetx_plan* pl, int64_t T, const void* X, const void* Wt,
+                               const int32_t* pi_R, const int32_t* pi_P, const void* Q_R,
+                               const void* Q_P, const void* Wa_saved, const void* G_Y, void* G_X,
+                               float* dQ_R, float* dQ_P, void* ws, size_t ws_bytes, void* stream) {
+  poetx_status st = check_backward_args(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X,
+                                        ws, ws_bytes);
+  if (st != POETX_OK) return st;
+  if (!dQ_R || !dQ_P) return POETX_ERR_INVALID_ARG;
+  if (!aligned16(dQ_R) || !aligned16(dQ_P)) return POETX_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  BwdWs w;
+  layout_bwd(pl, T, ws, &w, nullptr);
+  float* const dQ[2] = {dQ_R, dQ_P};
+  return backward_dq(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X, dQ, w, s);
+}
+
+poetx_status poetx_param_grad_batch(int32_t count, const poetx_plan* const* plans,
+                                    const int32_t* sides, const float* const* thetas,
+                                    const float* const* dQs, float* const* g_thetas,
+                                    void* const* ws, const size_t* ws_bytes, void* stream) {
+  if (count < 0) return POETX_ERR_INVALID_ARG;
+  if (count == 0) return POETX_OK;
+  if (!plans || !sides || !thetas || !dQs || !g_thetas || !ws || !ws_bytes)
+    return POETX_ERR_INVALID_ARG;
+  std::vector<GradItem> items((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    const poetx_plan* pl = plans[i];
+    if (!pl || !side_ok_fn(sides[i]) || !thetas[i] || !dQs[i] || !g_thetas[i] || !ws[i])
+      return POETX_ERR_INVALID_ARG;
+    if (!aligned16(thetas[i]) || !aligned16(dQs[i]) || !aligned16(g_thetas[i]) || !aligned16(ws[i]))
+      return POETX_ERR_ALIGNMENT;
+    if (ws_bytes[i] < poetx_workspace_size(pl, 0, POETX_WS_PARAM_GRAD)) return POETX_ERR_WORKSPACE;
+    items[i].pl = pl;
+    items[i].side = sides[i];
+    items[i].theta = thetas[i];
+    items[i].dQ = dQs[i];
+    items[i].g = g_thetas[i];
+    layout_param_grad(pl, sides[i], ws[i], &items[i].w);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  StageScope sc(POETX_STAGE_CNP_BWD, s);
+  return grad_items(items.data(), count, s);
 }
 
 poetx_status poetx_gather_cols(const poetx_plan* pl, int64_t T, int32_t dim, const void* in,

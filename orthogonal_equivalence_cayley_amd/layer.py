@@ -26,6 +26,21 @@ def build_many(layers) -> None:
     _px.build_orth_batch(items)
 
 
+def param_grad_many(layers, g_thetas=None):
+    """Chain rule through the parameterisation for every layer after
+    backward_dq(): both sides of all layers in one batched call. Returns the
+    packed gradients [(g_theta_R, g_theta_P), ...]."""
+    items, out = [], []
+    for i, L in enumerate(layers):
+        g = g_thetas[i] if g_thetas is not None else [
+            torch.empty(L.nparam[s], dtype=torch.float32, device=L.device) for s in (0, 1)]
+        out.append((g[0], g[1]))
+        for side in (_px.SIDE_R, _px.SIDE_P):
+            items.append((L.plan, side, L.theta[side], L.dQ[side], g[side], L._ws_grad(side)))
+    _px.param_grad_batch(items)
+    return out
+
+
 class PoetxLayer:
     def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
                  dtype: str = "bf16", device: str = "cuda"):
@@ -47,6 +62,7 @@ class PoetxLayer:
         else:
             self.Qact = self.Q32
         self.Wa = None
+        self.dQ = [torch.empty(self.nelem[s], dtype=torch.float32, device=self.device) for s in (0, 1)]
 
     # ------------------------------------------------------------------ setup
     def workspace(self, kind: int, T: int = 0) -> torch.Tensor:
@@ -99,6 +115,15 @@ class PoetxLayer:
             self._ws["build_p"] = cur
         return cur
 
+    def _ws_grad(self, side: int) -> torch.Tensor:
+        need = self.plan.workspace_size(0, _px.WS_PARAM_GRAD)
+        key = ("grad", side)
+        cur = self._ws.get(key)
+        if cur is None or cur.numel() < need:
+            cur = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            self._ws[key] = cur
+        return cur
+
     def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
                 Wa: Optional[torch.Tensor] = None, save: bool = True) -> torch.Tensor:
         T = X.shape[0]
@@ -127,3 +152,16 @@ class PoetxLayer:
                            self.Qact[0], self.Qact[1], self.Wa, G_Y, G_X, g_theta[0], g_theta[1],
                            ws, ws.numel())
         return G_X, g_theta[0], g_theta[1]
+
+    def backward_dq(self, X: torch.Tensor, G_Y: torch.Tensor, G_X: Optional[torch.Tensor] = None):
+        """Activation path of the backward: returns G_X and leaves dL/dQ of both
+        sides in self.dQ for param_grad_many()."""
+        T = X.shape[0]
+        assert self.Wa is not None and self.Wa.shape[0] == T, "forward(save=True) first"
+        assert G_Y.shape == (T, self.m) and G_Y.dtype == self.tdtype and G_Y.is_contiguous()
+        if G_X is None:
+            G_X = torch.empty(T, self.n, dtype=self.tdtype, device=self.device)
+        ws = self.workspace(_px.WS_BACKWARD, T)
+        self.plan.backward_dq(T, X, self.Wt, self.pi_R, self.pi_P, self.Qact[0], self.Qact[1],
+                              self.Wa, G_Y, G_X, self.dQ[0], self.dQ[1], ws, ws.numel())
+        return G_X

@@ -30,11 +30,13 @@ SIDE_P = 1
 WS_BUILD = 0
 WS_FORWARD = 1
 WS_BACKWARD = 2
+WS_PARAM_GRAD = 3
 
 EXPORTED = (
     "poetx_plan_create", "poetx_plan_destroy", "poetx_param_count", "poetx_block_elems",
     "poetx_workspace_size", "poetx_status_string", "poetx_permute_weight",
-    "poetx_build_orth", "poetx_build_orth_batch", "poetx_forward", "poetx_backward", "poetx_gather_cols",
+    "poetx_build_orth", "poetx_build_orth_batch", "poetx_forward", "poetx_backward",
+    "poetx_backward_dq", "poetx_param_grad_batch", "poetx_gather_cols",
     "poetx_scatter_cols", "poetx_timing_enable", "poetx_timing_read", "poetx_timing_reset",
 )
 
@@ -76,6 +78,8 @@ def _load() -> ctypes.CDLL:
         "poetx_forward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "poetx_backward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]),
+        "poetx_backward_dq": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "poetx_param_grad_batch": (st, [i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "poetx_gather_cols": (st, [vp, i64, i32, vp, vp, vp, vp]),
         "poetx_scatter_cols": (st, [vp, i64, i32, vp, vp, vp, vp]),
         "poetx_timing_enable": (st, [ctypes.c_uint32]),
@@ -154,6 +158,23 @@ def build_orth_batch(items, stream=None) -> None:
            "poetx_build_orth_batch")
 
 
+def param_grad_batch(items, stream=None) -> None:
+    """dL/dQ -> packed parameter gradients for many (plan, side, theta, dQ, g, ws) items."""
+    n = len(items)
+    if n == 0:
+        return
+    VP = ctypes.c_void_p * n
+    plans = VP(*[it[0].handle for it in items])
+    sides = (ctypes.c_int32 * n)(*[it[1] for it in items])
+    thetas = VP(*[_ptr(it[2]) for it in items])
+    dqs = VP(*[_ptr(it[3]) for it in items])
+    gs = VP(*[_ptr(it[4]) for it in items])
+    ws = VP(*[_ptr(it[5]) for it in items])
+    wsb = (ctypes.c_size_t * n)(*[it[5].numel() for it in items])
+    _check(LIB.poetx_param_grad_batch(n, plans, sides, thetas, dqs, gs, ws, wsb, _stream(stream)),
+           "poetx_param_grad_batch")
+
+
 class Plan:
     """Owns a poetx_plan (host-only object; creating one needs no GPU)."""
 
@@ -215,6 +236,13 @@ class Plan:
                                   _ptr(Wa_saved), _ptr(G_Y), _ptr(G_X), _ptr(g_theta_R),
                                   _ptr(g_theta_P), _ptr(ws), ws_bytes, _stream(stream)),
                "poetx_backward")
+
+    def backward_dq(self, T: int, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X, dQ_R, dQ_P,
+                    ws, ws_bytes: int, stream=None) -> None:
+        _check(LIB.poetx_backward_dq(self._h, T, _ptr(X), _ptr(Wt), _ptr(pi_R), _ptr(pi_P),
+                                     _ptr(Q_R), _ptr(Q_P), _ptr(Wa_saved), _ptr(G_Y), _ptr(G_X),
+                                     _ptr(dQ_R), _ptr(dQ_P), _ptr(ws), ws_bytes, _stream(stream)),
+               "poetx_backward_dq")
 
     def gather_cols(self, T: int, dim: int, inp, idx, out, stream=None) -> None:
         _check(LIB.poetx_gather_cols(self._h, T, dim, _ptr(inp), _ptr(idx), _ptr(out),

@@ -225,3 +225,29 @@ def test_build_batch_matches_single_side_builds():
             assert torch.equal(qb[s], L.Q32[s])
             want = blocks_concat(oracle.build_orth(th, bsz, k))
             assert oracle.rel_fro(qb[s].cpu().numpy().astype(np.float64), want) <= TOL_F32
+
+
+def test_backward_split_matches_backward():
+    """backward_dq per layer + one param_grad_batch over all layers gives the
+    same results as poetx_backward per layer (same kernels, bit for bit)."""
+    import torch
+    from orthogonal_equivalence_cayley_amd import param_grad_many
+    cases = [
+        (workloads.small_case(512, 256, (256, 256), (128, 128), T=300, seed=21, dtype="bf16", theta_std=0.01), 4, "bf16"),
+        (workloads.small_case(256, 512, (256,), (256, 128, 128), T=130, seed=22, dtype="bf16", theta_std=0.01), 3, "bf16"),
+        (workloads.small_case(70, 45, (30, 40), (45,), T=9, seed=23, dtype="f32", theta_std=0.05), 4, "f32"),
+    ]
+    layers, ref = [], []
+    for inp, k, dt in cases:
+        L = make_layer(inp, k, dt)
+        L.build()
+        X, G = to_dev(inp.X, dt), to_dev(inp.G_Y, dt)
+        L.forward(X)
+        gx, gr, gp = L.backward(X, G)
+        ref.append((gx.clone(), gr.clone(), gp.clone()))
+        L.backward_dq(X, G)
+        layers.append(L)
+    grads = param_grad_many(layers)
+    torch.cuda.synchronize()
+    for (gx, gr, gp), (g2r, g2p) in zip(ref, grads):
+        assert torch.equal(gr, g2r) and torch.equal(gp, g2p)
