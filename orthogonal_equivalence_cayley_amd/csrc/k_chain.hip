@@ -44,7 +44,7 @@ __device__ __forceinline__ ChainEntry select_entry(const ChainBatch& cb) {
   return e;
 }
 
-template <int MODE, int NT, int CR>
+template <int MODE, int NT, int CR, bool DIRECT, int U>
 __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
   extern __shared__ __align__(16) float lds[];
   const ChainEntry p = select_entry(cb);
@@ -133,27 +133,58 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    POETX_FETCH(0)
-    __syncthreads();          // panel written; previous step's chunk reads done
-    POETX_STASH(0)
-    if (nchunks > 1) { POETX_FETCH(1) }
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-      const float* sc = sbuf + (c & 1) * CR * spitch;
+    __syncthreads();          // panel of the previous step written
+    if (DIRECT) {
+      // B operand straight from L2 into registers, U K-steps ahead; many
+      // workgroups per CU hide the latency
+      const float* Sl = S + (long long)lk * b + li;
+      float bn[U][NT];
 #pragma unroll
-      for (int kk = 0; kk < CR; kk += 4) {
-        const float a = panel[li * pitch + c * CR + kk + lk];
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sc[(kk + lk) * spitch + bcol[t] + li],
-                                                        acc[t], 0, 0, 0);
+        for (int t = 0; t < NT; ++t) bn[u][t] = Sl[(long long)(4 * u) * b + bcol[t]];
+      for (int kc = 0; kc < b; kc += 4 * U) {
+        float bc[U][NT];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) bc[u][t] = bn[u][t];
+        const int kn = min(kc + 4 * U, b - 4 * U);   // clamped: the last prefetch is unused
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) bn[u][t] = Sl[(long long)(kn + 4 * u) * b + bcol[t]];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float a = panel[li * pitch + kc + 4 * u + lk];
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bc[u][t], acc[t], 0, 0, 0);
+        }
       }
-      if (c + 1 < nchunks) {
-        POETX_STASH((c + 1) & 1)   // the other buffer was last read in chunk c - 1
-        if (c + 2 < nchunks) { POETX_FETCH(c + 2) }
-      }
+    } else {
+      POETX_FETCH(0)
+      POETX_STASH(0)
+      if (nchunks > 1) { POETX_FETCH(1) }
       __syncthreads();
+      for (int c = 0; c < nchunks; ++c) {
+        const float* sc = sbuf + (c & 1) * CR * spitch;
+#pragma unroll
+        for (int kk = 0; kk < CR; kk += 4) {
+          const float a = panel[li * pitch + c * CR + kk + lk];
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sc[(kk + lk) * spitch + bcol[t] + li],
+                                                          acc[t], 0, 0, 0);
+        }
+        if (c + 1 < nchunks) {
+          POETX_STASH((c + 1) & 1)   // the other buffer was last read in chunk c - 1
+          if (c + 2 < nchunks) { POETX_FETCH(c + 2) }
+        }
+        __syncthreads();
+      }
     }
+    __syncthreads();          // every wave has finished reading the panel
     const int j = (MODE == 0) ? st + 2 : k - st;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -216,8 +247,9 @@ hipError_t launch_class(ChainBatch cb, hipStream_t s) {
     bmax = max(bmax, cb.e[i].b);
   }
   if (wg == 0) return hipSuccess;
-  const size_t lds = ((size_t)RP * (bmax + 4) + 2 * (size_t)kCR * (bmax + 16)) * sizeof(float);
-  hipLaunchKernelGGL((chain_kernel<MODE, NT, kCR>), dim3(wg), dim3(kThreads), lds, s, cb);
+  // b % 16 == 0: the direct path prefetches U = 4 K-steps of 4 rows
+  const size_t lds = (size_t)RP * (bmax + 4) * sizeof(float);
+  hipLaunchKernelGGL((chain_kernel<MODE, NT, kCR, true, 4>), dim3(wg), dim3(kThreads), lds, s, cb);
   return hipGetLastError();
 }
 
