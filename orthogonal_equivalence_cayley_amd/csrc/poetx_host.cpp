@@ -107,12 +107,15 @@ struct Carver {
 // the chip. Partial sums are reduced afterwards in a fixed order.
 int dq_splits(const poetx_plan* pl, int side, long long T) {
   long long tiles = 0;
-  const int tile = pl->dtype == POETX_BF16 ? 128 : 64;
+  // bf16: one 256 x 256 tile per 256-wide block (each operand read once per
+  // split); fp32: 64 x 64 tiles of the generic kernel
+  const int tile = pl->dtype == POETX_BF16 ? 256 : 64;
   for (const Seg& g : pl->segs[side]) {
     const long long t = (g.b + tile - 1) / tile;
     tiles += t * t * g.count;
   }
-  long long s = (512 + tiles - 1) / std::max<long long>(tiles, 1);
+  const long long target = pl->dtype == POETX_BF16 ? 256 : 512;
+  long long s = (target + tiles - 1) / std::max<long long>(tiles, 1);
   const long long maxs = std::max<long long>(1, (T + 255) / 256);
   s = std::min(s, maxs);
   s = std::max<long long>(1, std::min<long long>(s, 64));
