@@ -34,8 +34,9 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def stage_flops(w, T):
-    """Algorithmic flops per stage for one step of the workload."""
+def stage_flops(w, T, xmem=False):
+    """Algorithmic flops per stage for one step of the workload (with xmem, the
+    backward's recomputation of the P blocks and the Wt product counts too)."""
     f = dict(w0_fwd=0.0, w0_bwd=0.0, block_fwd=0.0, block_bwd=0.0, dq=0.0, build=0.0, cnp_bwd=0.0)
     for sp in w.layers:
         sq = sum(b * b for b in sp.bsz_R) + sum(b * b for b in sp.bsz_P)
@@ -48,6 +49,9 @@ def stage_flops(w, T):
             f["block_bwd"] += 2.0 * T * sq
             f["dq"] += 2.0 * T * sq
             f["cnp_bwd"] += 4.0 * w.k * cube
+            if xmem:
+                f["w0_fwd"] += 2.0 * T * sp.m * sp.n
+                f["block_fwd"] += 2.0 * T * sum(b * b for b in sp.bsz_P)
     return f
 
 
@@ -97,6 +101,8 @@ def main() -> int:
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing pass")
+    ap.add_argument("--xmem", action="store_true",
+                    help="POET-Xmem: keep no Wa; the backward recomputes it from X")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -124,7 +130,7 @@ def main() -> int:
         L.set_weight(dev(inp.W0), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
         L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
         b = dict(X=dev(inp.X), Y=torch.empty(T, sp.m, dtype=tdt, device="cuda"),
-                 Wa=torch.empty(T, sp.m, dtype=tdt, device="cuda"))
+                 Wa=None if args.xmem else torch.empty(T, sp.m, dtype=tdt, device="cuda"))
         if w.backward:
             b.update(G=dev(inp.G_Y), GX=torch.empty(T, sp.n, dtype=tdt, device="cuda"),
                      g=[torch.empty(L.nparam[s], dtype=torch.float32, device="cuda") for s in (0, 1)])
@@ -143,7 +149,7 @@ def main() -> int:
     def step():
         build_many(layers)
         for L, b in zip(layers, bufs):
-            L.forward(b["X"], Y=b["Y"], Wa=b["Wa"])
+            L.forward(b["X"], Y=b["Y"], Wa=b["Wa"], save=not args.xmem)
         if w.backward:
             # activation path layer by layer, then the chain rule through the
             # parameterisation of all layers in one batched call
@@ -172,7 +178,8 @@ def main() -> int:
     poetx.timing_reset()
     log(f"bench: {ms_per_step:.3f} ms/step")
 
-    flops = stage_flops(w, T)
+    xmem = bool(args.xmem and w.backward)
+    flops = stage_flops(w, T, xmem)
     stages = {}
     if not args.no_stages:
         # separate diagnostic pass: every stage bracketed by events
@@ -193,7 +200,7 @@ def main() -> int:
     dom = max(w0, key=lambda s: w0[s][0])
     ms_tot, launches = w0[dom]
     kernel = {"w0_fwd": "w0_gemm_nt_lds", "w0_bwd": "w0_gemm_nn_lds"}[dom]
-    flops_per_launch = flops[dom] / len(w.layers)
+    flops_per_launch = flops[dom] * args.steps / launches
     avg_s = ms_tot / launches * 1e-3
     achieved = flops_per_launch / avg_s
     gemm_keys = ("w0_fwd", "w0_bwd", "block_fwd", "block_bwd", "dq")
@@ -222,6 +229,7 @@ def main() -> int:
             "layers": [f"{sp.name} {sp.m}x{sp.n}" for sp in w.layers],
             "block_size": max(max(sp.bsz_R) for sp in w.layers),
             "passes": "build+forward+backward" if w.backward else "build+forward",
+            "saved_activation": "none (POET-Xmem: recomputed)" if xmem else "Wa (POET-Xfast)",
         },
         "roofline": {
             "kernel": kernel, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,

@@ -153,7 +153,10 @@ poetx_status poetx_forward(const poetx_plan* plan, int64_t T, const void* X, con
  * truncated Q the forward used. W0 is frozen and gets no gradient.
  *   X, Wt, pi_R, pi_P, Q_R, Q_P as in poetx_forward
  *   theta_R, theta_P device fp32 packed parameters (rebuild S for the chain rule)
- *   Wa_saved device [T, m] from poetx_forward (must not be NULL)
+ *   Wa_saved device [T, m] from poetx_forward, or NULL: then the backward
+ *            recomputes it from X (gather, blocks of P, Wt product: POET-Xmem,
+ *            [PX] §2.E), trading one more forward's worth of the first three
+ *            stages for T x m activations; results are identical either way
  *   G_Y      device [T, m] (dtype)      G_X device [T, n] (dtype)
  *   g_theta_R, g_theta_P device fp32 [param_count] (overwritten)
  *   ws       device, poetx_workspace_size(plan, T, POETX_WS_BACKWARD) bytes.

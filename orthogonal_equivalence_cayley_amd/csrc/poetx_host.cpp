@@ -398,6 +398,29 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
     HIP_TRY(poetx::launch_zero(dQ[1], pl->nelem[1], s));
     return POETX_OK;
   }
+  // Without a saved Wa (POET-Xmem) the forward's first three stages run again,
+  // with the forward's kernels and launch shapes, so Wa is bit-identical to the
+  // one poetx_forward would have saved. U stays for dQ_P; V borrows the G_U
+  // buffer and Wa the G_Wa buffer, both dead until the products that overwrite
+  // them, which run after their last reads on the same stream.
+  const void* Wa = Wa_saved;
+  if (!Wa_saved) {
+    {
+      StageScope sc(POETX_STAGE_GATHER, s);
+      HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
+    }
+    {
+      StageScope sc(POETX_STAGE_BLOCK_FWD, s);
+      if ((st = apply_blocks(pl, POETX_SIDE_P, T, w.U, Q_P, w.GU, true, s)) != POETX_OK) return st;
+    }
+    {
+      StageScope sc(POETX_STAGE_W0_FWD, s);
+      if ((st = gemm(pl, poetx::GEMM_W0, Op{w.GU, pl->n, 1}, Op{Wt, pl->n, 1}, w.GWa, pl->m, (int)T,
+                     pl->m, pl->n, 1, 0, 0, 0, 1, 0, false, s)) != POETX_OK)
+        return st;
+    }
+    Wa = w.GWa;
+  }
   // R side: G_Z = G_Y Pi_R^T; dQ_R = G_Z^T Wa per block; G_Wa = G_Z D_R
   {
     StageScope sc(POETX_STAGE_GATHER, s);
@@ -405,7 +428,7 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
   }
   {
     StageScope sc(POETX_STAGE_DQ, s);
-    if ((st = block_grads(pl, POETX_SIDE_R, T, w.GZ, Wa_saved, w.part, dQ[0], s)) != POETX_OK)
+    if ((st = block_grads(pl, POETX_SIDE_R, T, w.GZ, Wa, w.part, dQ[0], s)) != POETX_OK)
       return st;
   }
   {
@@ -420,7 +443,7 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
       return st;
   }
   // P side: U = X Pi_P^T; dQ_P = G_V^T U per block; G_U = G_V D_P; G_X = G_U Pi_P
-  {
+  if (Wa_saved) {
     StageScope sc(POETX_STAGE_GATHER, s);
     HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
   }
@@ -444,7 +467,7 @@ poetx_status check_backward_args(const poetx_plan* pl, long long T, const void* 
                                  const void* Q_P, const void* Wa_saved, const void* G_Y,
                                  const void* G_X, const void* ws, size_t ws_bytes) {
   if (!pl || T < 0) return POETX_ERR_INVALID_ARG;
-  if (T > 0 && (!X || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !Wa_saved || !G_Y || !G_X))
+  if (T > 0 && (!X || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !G_Y || !G_X))
     return POETX_ERR_INVALID_ARG;
   for (const void* p : {X, Wt, (const void*)pi_R, (const void*)pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X, ws})
     if (!aligned16(p)) return POETX_ERR_ALIGNMENT;

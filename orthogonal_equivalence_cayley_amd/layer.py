@@ -138,10 +138,14 @@ class PoetxLayer:
         self.Wa = Wa if save else None
         return Y
 
+    def _check_saved(self, T: int) -> None:
+        # no saved Wa (forward(save=False)): the backward recomputes it (POET-Xmem)
+        assert self.Wa is None or self.Wa.shape[0] == T, "saved Wa is from another batch"
+
     def backward(self, X: torch.Tensor, G_Y: torch.Tensor, G_X: Optional[torch.Tensor] = None,
                  g_theta: Optional[Sequence[torch.Tensor]] = None):
         T = X.shape[0]
-        assert self.Wa is not None and self.Wa.shape[0] == T, "forward(save=True) first"
+        self._check_saved(T)
         assert G_Y.shape == (T, self.m) and G_Y.dtype == self.tdtype and G_Y.is_contiguous()
         if G_X is None:
             G_X = torch.empty(T, self.n, dtype=self.tdtype, device=self.device)
@@ -157,7 +161,7 @@ class PoetxLayer:
         """Activation path of the backward: returns G_X and leaves dL/dQ of both
         sides in self.dQ for param_grad_many()."""
         T = X.shape[0]
-        assert self.Wa is not None and self.Wa.shape[0] == T, "forward(save=True) first"
+        self._check_saved(T)
         assert G_Y.shape == (T, self.m) and G_Y.dtype == self.tdtype and G_Y.is_contiguous()
         if G_X is None:
             G_X = torch.empty(T, self.n, dtype=self.tdtype, device=self.device)

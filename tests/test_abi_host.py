@@ -106,7 +106,10 @@ def test_backward_and_build_argument_errors():
     p = _plan()
     wsb = p.workspace_size(4, px.WS_BACKWARD)
     args = [p.handle, 4, A, A, A, A, A, A, A, A, A, A, A, A, A, A, wsb, None]
-    assert px.LIB.poetx_backward(*args[:10], None, *args[11:]) == px.POETX_ERR_INVALID_ARG
+    # G_Y missing is an error; Wa_saved missing is not (the backward recomputes it)
+    assert px.LIB.poetx_backward(*args[:11], None, *args[12:]) == px.POETX_ERR_INVALID_ARG
+    assert px.LIB.poetx_backward(*args[:10], None, *args[11:12], None, *args[13:]) == \
+        px.POETX_ERR_INVALID_ARG
     bad = list(args)
     bad[3] = A + 4
     assert px.LIB.poetx_backward(*bad) == px.POETX_ERR_ALIGNMENT

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import blocks_concat, device_ready, log, make_layer, run_layer, to_dev
+from gpu_util import blocks_concat, device_ready, log, make_layer, run_layer, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -251,3 +251,33 @@ def test_backward_split_matches_backward():
     torch.cuda.synchronize()
     for (gx, gr, gp), (g2r, g2p) in zip(ref, grads):
         assert torch.equal(gr, g2r) and torch.equal(gp, g2p)
+
+
+@pytest.mark.parametrize("case", [
+    ("bf16", dict(m=512, n=256, bR=(256, 256), bP=(128, 128), T=300, k=4)),
+    ("bf16", dict(m=256, n=768, bR=(256,), bP=(512, 256), T=1000, k=3)),
+    ("f32", dict(m=96, n=130, bR=(32, 64), bP=(65, 65), T=130, k=2)),
+])
+def test_xmem_recompute_matches_saved(case):
+    """Backward without a saved Wa (recomputed from X) gives the saved path's
+    results bit for bit, and both match the oracle."""
+    import torch
+    dt, c = case
+    inp = workloads.small_case(c["m"], c["n"], c["bR"], c["bP"], T=c["T"], seed=c["m"] + 7,
+                               dtype=dt, theta_std=0.01 if dt == "bf16" else 0.05)
+    log(f"xmem {dt} {c}")
+    L = make_layer(inp, c["k"], dt)
+    L.build()
+    X, G = to_dev(inp.X, dt), to_dev(inp.G_Y, dt)
+    L.forward(X, save=True)
+    saved = [t.clone() for t in L.backward(X, G)]
+    Y = L.forward(X, save=False)
+    assert L.Wa is None
+    mem = [t.clone() for t in L.backward(X, G)]
+    torch.cuda.synchronize()
+    for u, v in zip(saved, mem):
+        assert torch.equal(u, v)
+    ref = oracle.layer_reference(inp, c["k"])
+    tol = TOL_BF16 if dt == "bf16" else TOL_F32
+    got = dict(Y=to_np(Y), G_X=to_np(mem[0]), g_theta_R=to_np(mem[1]), g_theta_P=to_np(mem[2]))
+    _compare(got, ref, ["Y", "G_X", "g_theta_R", "g_theta_P"], tol, "xmem")
