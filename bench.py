@@ -17,8 +17,10 @@ times the float64 oracle on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,6 +55,47 @@ def stage_flops(w, T, xmem=False):
                 f["w0_fwd"] += 2.0 * T * sp.m * sp.n
                 f["block_fwd"] += 2.0 * T * sum(b * b for b in sp.bsz_P)
     return f
+
+
+def kernel_source_digest(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+# HBM traffic of the dominant kernel comes from two rocprofv3 counter runs
+# (FETCH_SIZE, then WRITE_SIZE) of this script with --copy-calibration, kept as
+# a JSON block in a text summary under profiles/. The counters are scaled by
+# what they read for a plain copy of known size. The figure is used only while
+# the kernel's source is the one the counters were taken on.
+TRAFFIC_SOURCES = {"w0_gemm_nn_lds": "orthogonal_equivalence_cayley_amd/csrc/k_gemm_lds.hip",
+                   "w0_gemm_nt_lds": "orthogonal_equivalence_cayley_amd/csrc/k_gemm_lds.hip"}
+
+
+def load_traffic(kernel: str, workload: str):
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    try:
+        with open(path) as f:
+            m = re.search(r"```json\n(.*?)\n```", f.read(), re.S)
+        rec = json.loads(m.group(1))
+        if rec.get("source_sha256") != kernel_source_digest(TRAFFIC_SOURCES[kernel]):
+            return None, "kernel source changed since the counters were taken"
+        return rec, None
+    except (OSError, AttributeError, ValueError, KeyError) as e:
+        return None, f"no traffic record ({type(e).__name__})"
+
+
+def copy_calibration(mib: int, reps: int = 3) -> None:
+    """A plain device copy of known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters: each launch reads and writes exactly `mib` MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(w, tokens: int):
@@ -101,6 +144,8 @@ def main() -> int:
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing pass")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB three times (for counter runs)")
     ap.add_argument("--xmem", action="store_true",
                     help="POET-Xmem: keep no Wa; the backward recomputes it from X")
     args = ap.parse_args()
@@ -157,6 +202,8 @@ def main() -> int:
                 L.backward_dq(b["X"], b["G"], G_X=b["GX"])
             param_grad_many(layers, [b["g"] for b in bufs])
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -203,6 +250,14 @@ def main() -> int:
     flops_per_launch = flops[dom] * args.steps / launches
     avg_s = ms_tot / launches * 1e-3
     achieved = flops_per_launch / avg_s
+    traffic, traffic_note = None, None
+    rec, why = load_traffic(kernel, w.name) if not xmem else (None, "counters taken without xmem")
+    if rec is not None:
+        traffic = rec["traffic_bytes_per_launch"]
+        traffic_note = (f"HBM bytes per launch, rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by a plain "
+                        f"copy; algorithmic {rec['algorithmic_bytes_per_launch']:.4g}")
+    else:
+        traffic_note = why
     gemm_keys = ("w0_fwd", "w0_bwd", "block_fwd", "block_bwd", "dq")
     gemm_frac = None
     if stages:
@@ -233,9 +288,9 @@ def main() -> int:
         },
         "roofline": {
             "kernel": kernel, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
-            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": None,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": traffic,
             "launches": launches, "avg_launch_us": avg_s * 1e6,
-            "flops_per_launch": flops_per_launch,
+            "flops_per_launch": flops_per_launch, "traffic_note": traffic_note,
         },
         "tflops_per_step": sum(flops.values()) / (ms_per_step * 1e-3) / 1e12,
         "w0_gemm_mfma_frac": w0_total_frac,

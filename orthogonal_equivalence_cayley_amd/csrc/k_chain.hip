@@ -298,11 +298,12 @@ hipError_t launch_chain_batch(int mode, const ChainBatch& cb, hipStream_t s) {
 
 namespace {
 
-__device__ __forceinline__ TriEntry select_tri(const TriBatch& tb, long long e) {
+// Workgroup w belongs to the last entry whose first workgroup is <= w.
+__device__ __forceinline__ TriEntry select_tri(const TriBatch& tb, int w) {
   TriEntry r = tb.e[0];
 #pragma unroll
   for (int i = 1; i < kChainMaxEntries; ++i)
-    if (i < tb.n && e >= tb.e[i].e0) r = tb.e[i];
+    if (i < tb.n && w >= tb.e[i].e0) r = tb.e[i];
   return r;
 }
 
@@ -310,76 +311,119 @@ __device__ __forceinline__ long long tri_off(int i, int j, int b) {
   return (long long)i * b - ((long long)i * (i + 1)) / 2 + (j - i - 1);
 }
 
-// S[r][c] = theta(r, c) above the diagonal, -theta(c, r) below, 0 on it.
-__global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb, long long total) {
-  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total;
-       e += (long long)gridDim.x * kThreads) {
-    const TriEntry t = select_tri(tb, e);
-    const long long bb = (long long)t.b * t.b;
-    const long long np = (long long)t.b * (t.b - 1) / 2;
-    const long long loc = e - t.e0;
-    const long long g = loc / bb;
-    const int r = (int)((loc - g * bb) / t.b);
-    const int c = (int)(loc - g * bb - (long long)r * t.b);
-    const float* th = t.src + g * np;
-    float v = 0.0f;
-    if (r < c) v = th[tri_off(r, c, t.b)];
-    else if (r > c) v = -th[tri_off(c, r, t.b)];
-    t.dst[loc] = v;
-  }
+// Rows of one block handled by one workgroup of the unpack / pack kernels; the
+// mirrored half of those rows is a strip of kTriRows columns, staged in LDS
+// with a padded pitch so that the transposed reads are conflict-free.
+constexpr int kTriRows = 16;
+constexpr int kTriPitch = kTriRows + 1;
+
+struct TriWork {
+  TriEntry t;
+  int g, r0;
+};
+__device__ __forceinline__ TriWork tri_work(const TriBatch& tb) {
+  TriWork w;
+  w.t = select_tri(tb, blockIdx.x);
+  const int tiles = w.t.b / kTriRows;
+  const int loc = blockIdx.x - (int)w.t.e0;
+  w.g = loc / tiles;
+  w.r0 = (loc - w.g * tiles) * kTriRows;
+  return w;
 }
 
-// g(r, c) = sign * (M[r][c] - M[c][r]) for r < c.
-__global__ __launch_bounds__(kThreads) void pack_batch_kernel(TriBatch tb, long long total) {
-  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total;
-       e += (long long)gridDim.x * kThreads) {
-    const TriEntry t = select_tri(tb, e);
-    const long long bb = (long long)t.b * t.b;
-    const long long np = (long long)t.b * (t.b - 1) / 2;
-    const long long loc = e - t.e0;
-    const long long g = loc / bb;
-    const int r = (int)((loc - g * bb) / t.b);
-    const int c = (int)(loc - g * bb - (long long)r * t.b);
-    if (r < c) {
-      const float* M = t.src + g * bb;
-      t.dst[g * np + tri_off(r, c, t.b)] =
-          tb.sign * (M[(long long)r * t.b + c] - M[(long long)c * t.b + r]);
+// S[r][c] = theta(r, c) above the diagonal, -theta(c, r) below, 0 on it, for
+// rows r0 .. r0 + 15 of one block. Above the diagonal each row is a contiguous
+// run of packed parameters; below it the values come from the 16 packed columns
+// r0 .. r0 + 15 (rows 0 .. r0 + 15), read row-wise into LDS and used transposed.
+__global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
+  __shared__ float strip[512 * kTriPitch];
+  const TriWork w = tri_work(tb);
+  const int b = w.t.b, r0 = w.r0;
+  const float* th = w.t.src + (long long)w.g * ((long long)b * (b - 1) / 2);
+  float* S = w.t.dst + (long long)w.g * b * b;
+  const int nrow = r0 + kTriRows;
+  for (int idx = threadIdx.x; idx < nrow * kTriRows; idx += kThreads) {
+    const int c = idx / kTriRows, j = idx % kTriRows;
+    const int col = r0 + j;
+    strip[c * kTriPitch + j] = c < col ? th[tri_off(c, col, b)] : 0.0f;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int j = wave; j < kTriRows; j += kThreads / 64) {
+    const int r = r0 + j;
+    float* row = S + (long long)r * b;
+    const float* up = th + (tri_off(r, r + 1, b) - (r + 1));   // theta(r, c) = up[c], c > r
+    for (int c = lane; c < b; c += 64) {
+      float v = 0.0f;
+      if (c > r) v = up[c];
+      else if (c < r) v = -strip[c * kTriPitch + j];
+      row[c] = v;
     }
   }
 }
 
+// g(r, c) = sign * (M[r][c] - M[c][r]) for r < c, packed rows r0 .. r0 + 15 of
+// one block. M[c][r] (c > r) comes from columns r0 .. r0 + 15 of rows
+// r0 .. b - 1, read row-wise into LDS and used transposed.
+__global__ __launch_bounds__(kThreads) void pack_batch_kernel(TriBatch tb) {
+  __shared__ float strip[512 * kTriPitch];
+  const TriWork w = tri_work(tb);
+  const int b = w.t.b, r0 = w.r0;
+  const float* M = w.t.src + (long long)w.g * b * b;
+  float* out = w.t.dst + (long long)w.g * ((long long)b * (b - 1) / 2);
+  const int nrow = b - r0;
+  for (int idx = threadIdx.x; idx < nrow * kTriRows; idx += kThreads) {
+    const int cl = idx / kTriRows, j = idx % kTriRows;
+    strip[cl * kTriPitch + j] = M[(long long)(r0 + cl) * b + r0 + j];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float sign = tb.sign;
+  for (int j = wave; j < kTriRows; j += kThreads / 64) {
+    const int r = r0 + j;
+    const float* row = M + (long long)r * b;
+    float* dst = out + (tri_off(r, r + 1, b) - (r + 1));   // g(r, c) = dst[c], c > r
+    for (int c = r + 1 + lane; c < b; c += 64)
+      dst[c] = sign * (row[c] - strip[(c - r0) * kTriPitch + j]);
+  }
+}
+
+// First workgroup of every entry; returns the total (blocks x row strips).
 long long fill_offsets(TriBatch& tb) {
   long long tot = 0;
   for (int i = 0; i < tb.n; ++i) {
     tb.e[i].e0 = tot;
-    tot += (long long)tb.e[i].b * tb.e[i].b * tb.e[i].count;
+    tot += (long long)tb.e[i].count * (tb.e[i].b / kTriRows);
   }
   return tot;
 }
 
-int tri_grid(long long total) {
-  long long g = (total + kThreads - 1) / kThreads;
-  const long long cap = 256LL * 32;
-  return (int)(g < 1 ? 1 : (g > cap ? cap : g));
+bool tri_batch_ok(const TriBatch& tb) {
+  if (tb.n > kChainMaxEntries) return false;
+  for (int i = 0; i < tb.n; ++i)
+    if (!chain_supported(tb.e[i].b) || tb.e[i].count < 1) return false;
+  return true;
 }
 
 }  // namespace
 
 hipError_t launch_unpack_batch(const TriBatch& in, hipStream_t s) {
   if (in.n <= 0) return hipSuccess;
-  if (in.n > kChainMaxEntries) return hipErrorInvalidValue;
+  if (!tri_batch_ok(in)) return hipErrorInvalidValue;
   TriBatch tb = in;
-  const long long total = fill_offsets(tb);
-  hipLaunchKernelGGL(unpack_batch_kernel, dim3(tri_grid(total)), dim3(kThreads), 0, s, tb, total);
+  const long long wgs = fill_offsets(tb);
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(unpack_batch_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, tb);
   return hipGetLastError();
 }
 
 hipError_t launch_pack_batch(const TriBatch& in, hipStream_t s) {
   if (in.n <= 0) return hipSuccess;
-  if (in.n > kChainMaxEntries) return hipErrorInvalidValue;
+  if (!tri_batch_ok(in)) return hipErrorInvalidValue;
   TriBatch tb = in;
-  const long long total = fill_offsets(tb);
-  hipLaunchKernelGGL(pack_batch_kernel, dim3(tri_grid(total)), dim3(kThreads), 0, s, tb, total);
+  const long long wgs = fill_offsets(tb);
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_batch_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, tb);
   return hipGetLastError();
 }
 

@@ -104,12 +104,13 @@ bool chain_supported(int b);
 // Launches the entries of `cb` (all chain_supported), one kernel per size class.
 hipError_t launch_chain_batch(int mode, const ChainBatch& cb, hipStream_t s);
 
-// Batched unpack (theta -> S) and pack (sign * (M - M^T) -> packed gradient).
+// Batched unpack (theta -> S) and pack (sign * (M - M^T) -> packed gradient)
+// over runs of chain_supported block sizes.
 struct TriEntry {
   const float* src;   // unpack: packed theta of the run; pack: b x b matrices of the run
   float* dst;         // unpack: b x b matrices; pack: packed gradient of the run
   int b, count;
-  long long e0;       // first element of the run in the flattened batch (launcher)
+  long long e0;       // first workgroup of the run (set by the launcher)
 };
 struct TriBatch {
   int n;
