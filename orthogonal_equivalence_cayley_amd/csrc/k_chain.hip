@@ -6,9 +6,10 @@
 //
 // A row panel of a product X S only needs the same row panel of X and all of S,
 // so every chain that multiplies by S from the right is row-local: one
-// workgroup owns rows [r0, r0 + 16) of one block, keeps its current panel in
+// workgroup owns rows [r0, r0 + RP) of one block, keeps its current panel in
 // LDS and runs every step of the chain without synchronising with other
-// workgroups. S (b x b, fp32) streams from L2 as the MFMA B operand.
+// workgroups. S (b x b, fp32) streams from L2 straight into registers as the
+// MFMA B operand; each B value feeds the RP / 16 row tiles of the panel.
 //
 // Modes
 //   BUILD : P_1 = S; P_j = P_{j-1} S; Q = I + sum_j c_j P_j. Writes Q (fp32)
@@ -17,7 +18,8 @@
 //           Stores every A_j (j = 1..k+1).
 //   TCHAIN: backward, transposed second chain T_j^T = A_j^T + T_{j+1}^T S with
 //           T_{k+1} = A_{k+1}; writes T_1^T = (dL/dS)^T.
-// Each workgroup has 4 waves; wave w owns the 16-column tiles w, w+4, ...
+// Each workgroup has 4 waves; wave w owns the 16-column tiles w, w+4, ... of
+// all RP rows.
 #include "poetx_internal.h"
 
 namespace poetx {
@@ -26,14 +28,9 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int RP = 16;   // rows per panel
 
 __device__ __forceinline__ float coef(int j, int k) { return (j == 0 || j == k + 1) ? 1.0f : 2.0f; }
 
-// LDS layout: the current 16-row panel (pitch b + 4 floats: the 16 rows of an
-// A-operand read fall in distinct banks) and two staged chunks of CR rows of S
-// (pitch b + 16: the 4 rows x 16 columns of a B-operand read fall in distinct
-// banks). Chunks are fetched with coalesced 16-byte loads one chunk ahead.
 // The run this workgroup belongs to. Constant indices only (fully unrolled), so
 // the table stays in kernel-argument memory and scalar registers.
 __device__ __forceinline__ ChainEntry select_entry(const ChainBatch& cb) {
@@ -44,15 +41,17 @@ __device__ __forceinline__ ChainEntry select_entry(const ChainBatch& cb) {
   return e;
 }
 
-template <int MODE, int NT, int CR, bool DIRECT, int U>
+// MT row tiles of 16 (RP = 16 MT rows per panel), NT column tiles per wave,
+// B operand prefetched U K-steps (of 4) ahead. The panel sits in LDS with pitch
+// b + 4 floats: the 16 rows of an A-operand read fall in distinct banks.
+template <int MODE, int NT, int MT, int U>
 __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
+  constexpr int RP = 16 * MT;
   extern __shared__ __align__(16) float lds[];
   const ChainEntry p = select_entry(cb);
   const int b = p.b;
   const int pitch = b + 4;
-  const int spitch = b + 16;
   float* panel = lds;
-  float* sbuf = lds + RP * pitch;                   // 2 x CR x spitch
   const int panels = b / RP;
   // all panels of one block on one XCD (workgroups are dealt to the 8 XCDs
   // round-robin), so that block's S is fetched into a single L2
@@ -75,67 +74,49 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
   for (int t = 0; t < NT; ++t) bcol[t] = min(wave + 4 * t, ntiles - 1) * 16;
   const int li = lane & 15, lk = lane >> 4;        // operand lane coordinates
   const int k = cb.k;
-  const int q4 = b / 4;                             // float4 per row of S
-  constexpr int kLoads = 8;                         // float4 per thread per chunk (max)
-  const int nvec = CR * q4;                         // float4 per chunk, <= kLoads * kThreads
 
   // initial panel
-  float keep[NT][4];   // G (ABAR) or the running Q (BUILD) in accumulator layout
+  float keep[MT][NT][4];   // G (ABAR) or the running Q (BUILD) in accumulator layout
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int tile = wave + 4 * t;
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) keep[t][v] = 0.0f;
-    if (tile >= ntiles) continue;
-    const int col = tile * 16 + li;
+    for (int t = 0; t < NT; ++t) {
+      const int tile = wave + 4 * t;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = 4 * lk + v;
-      const long long o = (long long)(r0 + row) * b + col;
-      float x;
-      if (MODE == 0) {
-        x = S[o];
-        keep[t][v] = (r0 + row == col ? 1.0f : 0.0f) + coef(1, k) * x;
-      } else if (MODE == 1) {
-        const float g = p.G[moff + o];
-        keep[t][v] = g;
-        x = coef(k + 1, k) * g;
-        p.out[(long long)k * p.stride + moff + o] = x;
-      } else {
-        // A_{k+1}^T panel: element (row, col) = A_{k+1}[col][r0 + row]
-        x = p.G[(long long)k * p.stride + moff + (long long)col * b + r0 + row];
+      for (int v = 0; v < 4; ++v) keep[mt][t][v] = 0.0f;
+      if (tile >= ntiles) continue;
+      const int col = tile * 16 + li;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * mt + 4 * lk + v;
+        const long long o = (long long)(r0 + row) * b + col;
+        float x;
+        if (MODE == 0) {
+          x = S[o];
+          keep[mt][t][v] = (r0 + row == col ? 1.0f : 0.0f) + coef(1, k) * x;
+        } else if (MODE == 1) {
+          const float g = p.G[moff + o];
+          keep[mt][t][v] = g;
+          x = coef(k + 1, k) * g;
+          p.out[(long long)k * p.stride + moff + o] = x;
+        } else {
+          // A_{k+1}^T panel: element (row, col) = A_{k+1}[col][r0 + row]
+          x = p.G[(long long)k * p.stride + moff + (long long)col * b + r0 + row];
+        }
+        panel[row * pitch + col] = x;
       }
-      panel[row * pitch + col] = x;
     }
-  }
-
-  const int nchunks = b / CR;
-  f32x4 pre[kLoads];    // the next chunk of S, in registers
-// Loads are unconditional (an index past the chunk is clamped onto its last
-// float4), so the prefetch registers never need a memory-backed default.
-#define POETX_FETCH(c)                                                              \
-  _Pragma("unroll") for (int i = 0; i < kLoads; ++i) {                              \
-    const int e = min(i * kThreads + (int)threadIdx.x, nvec - 1);                   \
-    const int r = e / q4, q = e - r * q4;                                           \
-    pre[i] = reinterpret_cast<const f32x4*>(S + (long long)((c) * CR + r) * b)[q]; \
-  }
-#define POETX_STASH(buf)                                                            \
-  _Pragma("unroll") for (int i = 0; i < kLoads; ++i) {                              \
-    const int e = i * kThreads + threadIdx.x;                                       \
-    if (e < nvec) {                                                                 \
-      const int r = e / q4, q = e - r * q4;                                         \
-      *reinterpret_cast<f32x4*>(sbuf + (buf) * CR * spitch + r * spitch + 4 * q) = pre[i]; \
-    }                                                                               \
-  }
 
   const int nsteps = k;   // BUILD: j = 2..k+1; ABAR, TCHAIN: j = k..1
   for (int st = 0; st < nsteps; ++st) {
-    f32x4 acc[NT];
+    f32x4 acc[MT][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     __syncthreads();          // panel of the previous step written
-    if (DIRECT) {
-      // B operand straight from L2 into registers, U K-steps ahead; many
+    {
+      // B operand straight from L2 into registers, U K-steps ahead; several
       // workgroups per CU hide the latency
       const float* Sl = S + (long long)lk * b + li;
       float bn[U][NT];
@@ -156,89 +137,72 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
           for (int t = 0; t < NT; ++t) bn[u][t] = Sl[(long long)(kn + 4 * u) * b + bcol[t]];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const float a = panel[li * pitch + kc + 4 * u + lk];
+          float a[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) a[mt] = panel[(16 * mt + li) * pitch + kc + 4 * u + lk];
 #pragma unroll
           for (int t = 0; t < NT; ++t)
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bc[u][t], acc[t], 0, 0, 0);
-        }
-      }
-    } else {
-      POETX_FETCH(0)
-      POETX_STASH(0)
-      if (nchunks > 1) { POETX_FETCH(1) }
-      __syncthreads();
-      for (int c = 0; c < nchunks; ++c) {
-        const float* sc = sbuf + (c & 1) * CR * spitch;
 #pragma unroll
-        for (int kk = 0; kk < CR; kk += 4) {
-          const float a = panel[li * pitch + c * CR + kk + lk];
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sc[(kk + lk) * spitch + bcol[t] + li],
-                                                          acc[t], 0, 0, 0);
+            for (int mt = 0; mt < MT; ++mt)
+              acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt], bc[u][t], acc[mt][t], 0, 0, 0);
         }
-        if (c + 1 < nchunks) {
-          POETX_STASH((c + 1) & 1)   // the other buffer was last read in chunk c - 1
-          if (c + 2 < nchunks) { POETX_FETCH(c + 2) }
-        }
-        __syncthreads();
       }
     }
     __syncthreads();          // every wave has finished reading the panel
     const int j = (MODE == 0) ? st + 2 : k - st;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int tile = wave + 4 * t;
-      if (tile >= ntiles) continue;
-      const int col = tile * 16 + li;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 4 * lk + v;
-        float x = acc[t][v];
-        if (MODE == 0) {
-          keep[t][v] += coef(j, k) * x;
-        } else if (MODE == 1) {
-          x = coef(j, k) * keep[t][v] - x;
-          p.out[(long long)(j - 1) * p.stride + moff + (long long)(r0 + row) * b + col] = x;
-        } else {
-          x += p.G[(long long)(j - 1) * p.stride + moff + (long long)col * b + r0 + row];
+      for (int t = 0; t < NT; ++t) {
+        const int tile = wave + 4 * t;
+        if (tile >= ntiles) continue;
+        const int col = tile * 16 + li;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * mt + 4 * lk + v;
+          float x = acc[mt][t][v];
+          if (MODE == 0) {
+            keep[mt][t][v] += coef(j, k) * x;
+          } else if (MODE == 1) {
+            x = coef(j, k) * keep[mt][t][v] - x;
+            p.out[(long long)(j - 1) * p.stride + moff + (long long)(r0 + row) * b + col] = x;
+          } else {
+            x += p.G[(long long)(j - 1) * p.stride + moff + (long long)col * b + r0 + row];
+          }
+          panel[row * pitch + col] = x;
         }
-        panel[row * pitch + col] = x;
       }
-    }
   }
   __syncthreads();
 
   if (MODE == 0 || MODE == 2) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int tile = wave + 4 * t;
-      if (tile >= ntiles) continue;
-      const int col = tile * 16 + li;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 4 * lk + v;
-        const long long o = moff + (long long)(r0 + row) * b + col;
-        const float x = (MODE == 0) ? keep[t][v] : panel[row * pitch + col];
-        p.out[o] = x;
-        if (MODE == 0 && p.out_act) {
-          if (p.act_bf16)
-            reinterpret_cast<__bf16*>(p.out_act)[o] = static_cast<__bf16>(x);
-          else
-            reinterpret_cast<float*>(p.out_act)[o] = x;
+      for (int t = 0; t < NT; ++t) {
+        const int tile = wave + 4 * t;
+        if (tile >= ntiles) continue;
+        const int col = tile * 16 + li;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * mt + 4 * lk + v;
+          const long long o = moff + (long long)(r0 + row) * b + col;
+          const float x = (MODE == 0) ? keep[mt][t][v] : panel[row * pitch + col];
+          p.out[o] = x;
+          if (MODE == 0 && p.out_act) {
+            if (p.act_bf16)
+              reinterpret_cast<__bf16*>(p.out_act)[o] = static_cast<__bf16>(x);
+            else
+              reinterpret_cast<float*>(p.out_act)[o] = x;
+          }
         }
       }
-    }
   }
 }
 
-#undef POETX_FETCH
-#undef POETX_STASH
-
-constexpr int kCR = 16;   // rows of S per staged chunk
-
-template <int MODE, int NT>
+template <int MODE, int NT, int MT>
 hipError_t launch_class(ChainBatch cb, hipStream_t s) {
+  constexpr int RP = 16 * MT;
   int wg = 0, bmax = 0;
   for (int i = 0; i < cb.n; ++i) {
     cb.e[i].wg0 = wg;
@@ -247,32 +211,43 @@ hipError_t launch_class(ChainBatch cb, hipStream_t s) {
     bmax = max(bmax, cb.e[i].b);
   }
   if (wg == 0) return hipSuccess;
-  // b % 16 == 0: the direct path prefetches U = 4 K-steps of 4 rows
+  // b % 16 == 0: the prefetch of U = 4 K-steps of 4 rows stays inside S
   const size_t lds = (size_t)RP * (bmax + 4) * sizeof(float);
-  hipLaunchKernelGGL((chain_kernel<MODE, NT, kCR, true, 4>), dim3(wg), dim3(kThreads), lds, s, cb);
+  hipLaunchKernelGGL((chain_kernel<MODE, NT, MT, 4>), dim3(wg), dim3(kThreads), lds, s, cb);
   return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_mode(const ChainBatch& all, hipStream_t s) {
-  // one launch per size class (tiles per wave)
-  for (int nt = 1; nt <= 8; nt *= 2) {
-    ChainBatch cb;
-    cb.n = 0;
-    cb.k = all.k;
-    for (int i = 0; i < all.n; ++i) {
-      const int need = (all.e[i].b / 16 + 3) / 4;
-      const int cls = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-      if (cls == nt) cb.e[cb.n++] = all.e[i];
+  // one launch per size class (column tiles per wave, and panels of 32 rows
+  // where b allows them: each B value then feeds two row tiles)
+  for (int nt = 1; nt <= 8; nt *= 2)
+    for (int mt = 1; mt <= 2; ++mt) {
+      ChainBatch cb;
+      cb.n = 0;
+      cb.k = all.k;
+      for (int i = 0; i < all.n; ++i) {
+        const int need = (all.e[i].b / 16 + 3) / 4;
+        const int cls = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+        // 32-row panels for the build only: the backward chains keep more state
+        // per tile and lose more to the lower occupancy than they gain
+        const int m = (MODE == 0 && all.e[i].b % 32 == 0 && cls <= 4) ? 2 : 1;
+        if (cls == nt && m == mt) cb.e[cb.n++] = all.e[i];
+      }
+      if (cb.n == 0) continue;
+      hipError_t e;
+      if (mt == 1) {
+        if (nt == 1) e = launch_class<MODE, 1, 1>(cb, s);
+        else if (nt == 2) e = launch_class<MODE, 2, 1>(cb, s);
+        else if (nt == 4) e = launch_class<MODE, 4, 1>(cb, s);
+        else e = launch_class<MODE, 8, 1>(cb, s);
+      } else {
+        if (nt == 1) e = launch_class<MODE, 1, 2>(cb, s);
+        else if (nt == 2) e = launch_class<MODE, 2, 2>(cb, s);
+        else e = launch_class<MODE, 4, 2>(cb, s);
+      }
+      if (e != hipSuccess) return e;
     }
-    if (cb.n == 0) continue;
-    hipError_t e;
-    if (nt == 1) e = launch_class<MODE, 1>(cb, s);
-    else if (nt == 2) e = launch_class<MODE, 2>(cb, s);
-    else if (nt == 4) e = launch_class<MODE, 4>(cb, s);
-    else e = launch_class<MODE, 8>(cb, s);
-    if (e != hipSuccess) return e;
-  }
   return hipSuccess;
 }
 

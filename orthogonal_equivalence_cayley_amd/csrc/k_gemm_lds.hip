@@ -173,14 +173,17 @@ __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
 // are not counted, so the wait also covers them (never too short).
 template <int LOADS, int MAXP>
 __device__ __forceinline__ void wait_stage(int pending) {
-  if (MAXP >= 2 && pending >= 2) wait_vmcnt<LOADS * 2>();
+  if (MAXP >= 3 && pending >= 3) wait_vmcnt<LOADS * 3>();
+  else if (MAXP >= 2 && pending >= 2) wait_vmcnt<LOADS * 2>();
   else if (MAXP >= 1 && pending >= 1) wait_vmcnt<LOADS>();
   else wait_vmcnt<0>();
 }
 
 template <int BM, int BN, int WM, int WN, int KB, int STAGES, bool AK, bool BKM, bool OUTF32>
 __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
-  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
+  static_assert(STAGES >= 2 && STAGES <= 5, "2 to 5 LDS stages");
+  static_assert((STAGES - 2) * (KB / 8) * (BM + BN) / (BM / WM) / (BN / WN) / 64 <= 63,
+                "direct-to-LDS loads of the pending stages exceed the vmcnt range");
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int NT = NW * 64;
   constexpr int TM = WM / 32, TN = WN / 32;

@@ -114,8 +114,10 @@ int dq_splits(const poetx_plan* pl, int side, long long T) {
     const long long t = (g.b + tile - 1) / tile;
     tiles += t * t * g.count;
   }
-  const long long target = pl->dtype == POETX_BF16 ? 256 : 512;
-  long long s = (target + tiles - 1) / std::max<long long>(tiles, 1);
+  // bf16: at most one workgroup per CU (a second round of a few workgroups
+  // would double the time); fp32: about two per CU
+  long long s = pl->dtype == POETX_BF16 ? 256 / std::max<long long>(tiles, 1)
+                                        : (512 + tiles - 1) / std::max<long long>(tiles, 1);
   const long long maxs = std::max<long long>(1, (T + 255) / 256);
   s = std::min(s, maxs);
   s = std::max<long long>(1, std::min<long long>(s, 64));
