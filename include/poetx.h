@@ -98,6 +98,10 @@ size_t poetx_workspace_size(const poetx_plan* plan, int64_t T, int32_t kind);
 /* Short static description of a status code. */
 const char* poetx_status_string(poetx_status status);
 
+/* Description of the HIP error behind the calling thread's most recent
+ * POETX_ERR_HIP (static string; "no HIP error" if there was none). */
+const char* poetx_last_hip_error(void);
+
 /* Pre-merge of the permutations into the frozen weight, once per inner loop
  * ([PX] §2.B "Réduction": permutations folded into W ahead of time, leaving
  * two index operations per step): Wt[i][j] = W0[pi_R[i]][pi_P[j]].

@@ -336,7 +336,6 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   for (int it = 0; it < total; ++it) {
     wait_stage<LOADS, STAGES - 2>(iss - it - 1);
     lds_barrier();   // stage `it` visible to all waves; stage it-1 no longer read
-    if (iss < total) issue_next();
     const unsigned char* sa = lds + (it % STAGES) * STAGE;
     const unsigned char* sb = sa + TA::BYTES;
     bf16x8 af[2][TM], bfr[2][TN];
@@ -344,6 +343,10 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
     for (int i = 0; i < TM; ++i) af[0][i] = TA::frag(sa, wm0 + i * 32, 0, lane);
 #pragma unroll
     for (int j = 0; j < TN; ++j) bfr[0][j] = TB::frag(sb, wn0 + j * 32, 0, lane);
+    // the next stage's loads go out while the first fragments are in flight
+    __builtin_amdgcn_sched_barrier(0);
+    if (iss < total) issue_next();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < LBK / 16; ++kk) {
       const int cb = kk & 1, nb = cb ^ 1;
@@ -353,7 +356,6 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) bfr[nb][j] = TB::frag(sb, wn0 + j * 32, kk + 1, lane);
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -361,6 +363,18 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
           // B first: the result tile is C^T, so each lane holds four consecutive
           // output columns of one output row
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+      if (kk + 1 < LBK / 16) {
+        // the reads of step kk + 1 go out two at a time between the first
+        // multiplies of step kk, so they have the rest of the step to land
+        constexpr int NRD = TM * (AK ? 1 : 2) + TN * (BKM ? 1 : 2);   // ds_read per step
+        constexpr int NG = (NRD + 1) / 2 < TM * TN ? (NRD + 1) / 2 : TM * TN;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+        }
+        if constexpr (TM * TN > NG) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - NG, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (++kt == nk) {   // tile complete: write it out and start the next one

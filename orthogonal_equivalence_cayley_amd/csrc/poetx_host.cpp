@@ -200,9 +200,16 @@ size_t layout_build(const poetx_plan* pl, void* base, float** S, float** P0, flo
   return c.off;
 }
 
+// HIP error behind the calling thread's last POETX_ERR_HIP
+thread_local hipError_t g_last_hip = hipSuccess;
+
 #define HIP_TRY(expr)                                   \
   do {                                                  \
-    if ((expr) != hipSuccess) return POETX_ERR_HIP;     \
+    const hipError_t e_ = (expr);                       \
+    if (e_ != hipSuccess) {                             \
+      g_last_hip = e_;                                  \
+      return POETX_ERR_HIP;                             \
+    }                                                   \
   } while (0)
 
 // Operand view: element (row, k) at p[row * rs + k * cs].
@@ -558,6 +565,10 @@ bool side_ok(int32_t side) { return side_ok_fn(side); }
 
 extern "C" {
 
+const char* poetx_last_hip_error(void) {
+  return g_last_hip == hipSuccess ? "no HIP error" : hipGetErrorString(g_last_hip);
+}
+
 const char* poetx_status_string(poetx_status st) {
   switch (st) {
     case POETX_OK: return "ok";
@@ -838,9 +849,9 @@ poetx_status poetx_timing_read(int32_t stage, double* ms, int64_t* count) {
   int64_t n = 0;
   for (const TimingRec& r : g_recs) {
     if (r.stage != stage) continue;
-    if (hipEventSynchronize(r.b) != hipSuccess) return POETX_ERR_HIP;
+    HIP_TRY(hipEventSynchronize(r.b));
     float t = 0.0f;
-    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return POETX_ERR_HIP;
+    HIP_TRY(hipEventElapsedTime(&t, r.a, r.b));
     tot += t;
     ++n;
   }

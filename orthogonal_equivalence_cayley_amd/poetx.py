@@ -34,7 +34,7 @@ WS_PARAM_GRAD = 3
 
 EXPORTED = (
     "poetx_plan_create", "poetx_plan_destroy", "poetx_param_count", "poetx_block_elems",
-    "poetx_workspace_size", "poetx_status_string", "poetx_permute_weight",
+    "poetx_workspace_size", "poetx_status_string", "poetx_last_hip_error", "poetx_permute_weight",
     "poetx_build_orth", "poetx_build_orth_batch", "poetx_forward", "poetx_backward",
     "poetx_backward_dq", "poetx_param_grad_batch", "poetx_gather_cols",
     "poetx_scatter_cols", "poetx_timing_enable", "poetx_timing_read", "poetx_timing_reset",
@@ -46,7 +46,10 @@ STAGES = ("build", "gather", "block_fwd", "w0_fwd", "scatter", "dq", "block_bwd"
 
 class PoetxError(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: status {status} ({status_string(status)})")
+        msg = f"{where}: status {status} ({status_string(status)})"
+        if status == POETX_ERR_HIP:
+            msg += f": {LIB.poetx_last_hip_error().decode()}"
+        super().__init__(msg)
         self.status = status
 
 
@@ -62,6 +65,14 @@ class Desc(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libpoetx.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+    # torch ships its own HIP runtime under an unversioned file name. Loaded
+    # first, it satisfies this library's libamdhip64.so.7 dependency by soname,
+    # so the process holds one HIP runtime; loaded after us, it would bring a
+    # second runtime, and this library's calls would then find no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     st = ctypes.c_int
@@ -72,6 +83,7 @@ def _load() -> ctypes.CDLL:
         "poetx_block_elems": (i64, [vp, i32]),
         "poetx_workspace_size": (sz, [vp, i64, i32]),
         "poetx_status_string": (ctypes.c_char_p, [st]),
+        "poetx_last_hip_error": (ctypes.c_char_p, []),
         "poetx_permute_weight": (st, [vp, vp, vp, vp, vp, vp]),
         "poetx_build_orth": (st, [vp, i32, vp, vp, vp, vp, sz, vp]),
         "poetx_build_orth_batch": (st, [i32, vp, vp, vp, vp, vp, vp, vp, vp]),
