@@ -57,6 +57,14 @@ def stage_flops(w, T, xmem=False):
     return f
 
 
+def w0_bytes_per_step(w, T):
+    """Algorithmic HBM bytes of the frozen-weight products of one pass over all
+    layers: each reads its activation operand and Wt once and writes its output
+    once (same for the forward and the backward form)."""
+    el = 2 if w.dtype == "bf16" else 4
+    return sum(el * (T * sp.n + sp.m * sp.n + T * sp.m) for sp in w.layers)
+
+
 def kernel_source_digest(path: str) -> str:
     with open(os.path.join(ROOT, path), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -290,7 +298,10 @@ def main() -> int:
             "kernel": kernel, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": traffic,
             "launches": launches, "avg_launch_us": avg_s * 1e6,
-            "flops_per_launch": flops_per_launch, "traffic_note": traffic_note,
+            "flops_per_launch": flops_per_launch,
+            "algorithmic_bytes_per_launch": w0_bytes_per_step(w, T) * args.steps / launches
+            * (2 if (xmem and dom == "w0_fwd") else 1),
+            "traffic_note": traffic_note,
         },
         "tflops_per_step": sum(flops.values()) / (ms_per_step * 1e-3) / 1e12,
         "w0_gemm_mfma_frac": w0_total_frac,

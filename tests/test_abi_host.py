@@ -124,3 +124,22 @@ def test_backward_and_build_argument_errors():
     assert px.LIB.poetx_gather_cols(p.handle, 3, 5, A, A, A, None) == px.POETX_ERR_INVALID_ARG
     assert px.LIB.poetx_gather_cols(p.handle, 0, 5, A, A, A + 1, None) == px.POETX_OK
     assert px.LIB.poetx_scatter_cols(p.handle, 3, 5, A, A + 8, A + 16, None) == px.POETX_ERR_ALIGNMENT
+
+
+def test_bench_traffic_record_is_valid_or_marked_stale():
+    """bench.py reports the dominant kernel's HBM traffic from a committed
+    counter record only while the kernel source matches it."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    rec, why = bench.load_traffic("w0_gemm_nn_lds", "poetx-llama-block-h2048-7-linears-bf16")
+    if rec is None:
+        assert why
+        return
+    for key in ("traffic_bytes_per_launch", "algorithmic_bytes_per_launch", "copy_fetch_factor",
+                "copy_write_factor", "source_sha256"):
+        assert key in rec
+    assert rec["traffic_bytes_per_launch"] >= rec["write_bytes_per_launch"] > 0
+    rec2, why2 = bench.load_traffic("w0_gemm_nn_lds", "no-such-workload")
+    assert rec2 is None and why2
