@@ -43,7 +43,8 @@ __all__ = [
     "skew_from_packed", "packed_upper", "neumann_cayley", "build_orth",
     "block_offsets", "apply_blocks_T", "apply_blocks", "permute_weight",
     "forward", "forward_rows", "cnp_backward", "backward", "cnp_coefficients",
-    "rel_fro", "layer_reference", "backward_rows", "theta_grad_block",
+    "rel_fro", "layer_reference", "backward_rows", "theta_grad_block", "side_matrix",
+    "merge_weight",
 ]
 
 
@@ -270,3 +271,26 @@ def theta_grad_block(side, j, X, Wt, pi_R, pi_P, theta_R, theta_P, QR, QP, G_Y, 
     S = skew_from_packed(np.asarray(theta, dtype=np.float64)[poff:poff + b * (b - 1) // 2], b)
     Sbar = cnp_backward(dQ, S, k)
     return packed_upper(Sbar - Sbar.T)
+
+
+def side_matrix(Qs: Sequence[np.ndarray], bsz: Sequence[int], pi) -> np.ndarray:
+    """Dense side matrix Pi^T D Pi: D = blockdiag(Qs) ([PX] §2.C) and Pi the
+    permutation matrix with (Pi v)_i = v[pi[i]] ([PX] §2.B), i.e. the rows of
+    the identity taken in the order pi."""
+    dim = sum(bsz)
+    D = np.zeros((dim, dim), dtype=np.float64)
+    for off, b, Q in zip(block_offsets(bsz), bsz, Qs):
+        D[off:off + b, off:off + b] = Q
+    Pi = np.eye(dim)[np.asarray(pi)]
+    return Pi.T @ D @ Pi
+
+
+def merge_weight(W0, theta_R, theta_P, pi_R, pi_P, bsz_R, bsz_P, k: int) -> np.ndarray:
+    """End of an inner loop: the orthogonal factors the loop trained are folded
+    into the weight, W_new = R W0 P (the two-sided orthogonal update of
+    [Pion] §数学原理; the inner loop of [PX] §2.B keeps W fixed while R and P
+    change). Dense materialised matrices, float64; the next loop starts from
+    W_new with theta = 0 and new permutations."""
+    R = side_matrix(build_orth(theta_R, bsz_R, k), bsz_R, pi_R)
+    P = side_matrix(build_orth(theta_P, bsz_P, k), bsz_P, pi_P)
+    return R @ np.asarray(W0, dtype=np.float64) @ P

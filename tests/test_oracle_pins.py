@@ -295,3 +295,61 @@ def test_restricted_forms_match_full_oracle():
                                         inp.theta_P, ref["QR"], ref["QP"], inp.G_Y, sp.bsz_R,
                                         sp.bsz_P, k)
             assert np.max(np.abs(g - full[offs[side][j]:offs[side][j + 1]])) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# merge at the end of an inner loop
+
+def test_merge_two_by_two_by_hand():
+    # one 2x2 block per side, identity permutations, k = 0: Q = I + S, so
+    # R = [[1, a], [-a, 1]] and P = [[1, c], [-c, 1]]
+    a, c = 0.3, -0.7
+    W0 = np.array([[2.0, -1.0], [0.5, 3.0]])
+    got = oracle.merge_weight(W0, [a], [c], [0, 1], [0, 1], (2,), (2,), 0)
+    w11, w12, w21, w22 = 2.0, -1.0, 0.5, 3.0
+    RW = np.array([[w11 + a * w21, w12 + a * w22], [w21 - a * w11, w22 - a * w12]])
+    want = np.array([[RW[0, 0] - c * RW[0, 1], c * RW[0, 0] + RW[0, 1]],
+                     [RW[1, 0] - c * RW[1, 1], c * RW[1, 0] + RW[1, 1]]])
+    assert np.max(np.abs(got - want)) < 1e-15
+    # swapping both coordinates of a side (pi = [1, 0]) swaps the roles of the
+    # two rows (columns): R' = Pi^T R Pi with R' = [[1, -a], [a, 1]]
+    got2 = oracle.merge_weight(W0, [a], [0.0], [1, 0], [0, 1], (2,), (2,), 0)
+    R2 = np.array([[1.0, -a], [a, 1.0]])
+    assert np.max(np.abs(got2 - R2 @ W0)) < 1e-15
+
+
+@pytest.mark.parametrize("case", [
+    dict(m=12, n=8, bR=(4, 4, 4), bP=(4, 4), k=3),
+    dict(m=10, n=9, bR=(3, 7), bP=(2, 7), k=1),
+])
+def test_merge_is_the_layer_map_and_survives_resampling(case):
+    inp = workloads.small_case(case["m"], case["n"], case["bR"], case["bP"], T=7, seed=31, theta_std=0.2)
+    k, bR, bP = case["k"], case["bR"], case["bP"]
+    QR = oracle.build_orth(inp.theta_R, bR, k)
+    QP = oracle.build_orth(inp.theta_P, bP, k)
+    Wt = oracle.permute_weight(inp.W0, inp.pi_R, inp.pi_P)
+    Y, _ = oracle.forward(inp.X, Wt, inp.pi_R, inp.pi_P, QR, QP, bR, bP)
+    Wn = oracle.merge_weight(inp.W0, inp.theta_R, inp.theta_P, inp.pi_R, inp.pi_P, bR, bP, k)
+    # the input-centric forward computes x -> W_new x
+    assert oracle.rel_fro(inp.X.astype(np.float64) @ Wn.T, Y) < 1e-14
+    # next inner loop: theta = 0 and fresh permutations give the same layer
+    rng = np.random.default_rng(5)
+    pR, pP = rng.permutation(case["m"]), rng.permutation(case["n"])
+    I_R = oracle.build_orth(np.zeros(workloads.n_params(bR)), bR, k)
+    I_P = oracle.build_orth(np.zeros(workloads.n_params(bP)), bP, k)
+    Y2, _ = oracle.forward(inp.X, oracle.permute_weight(Wn, pR, pP), pR, pP, I_R, I_P, bR, bP)
+    assert oracle.rel_fro(Y2, Y) < 1e-14
+    # theta = 0 merges to W0 itself
+    W00 = oracle.merge_weight(inp.W0, np.zeros(workloads.n_params(bR)), np.zeros(workloads.n_params(bP)),
+                              inp.pi_R, inp.pi_P, bR, bP, k)
+    assert np.array_equal(W00, inp.W0.astype(np.float64))
+
+
+def test_merge_preserves_the_spectrum_in_the_cayley_limit():
+    inp = workloads.small_case(16, 12, (4, 4, 8), (6, 6), T=2, seed=8, theta_std=0.05)
+    W0 = inp.W0.astype(np.float64)
+    Wn = oracle.merge_weight(W0, inp.theta_R, inp.theta_P, inp.pi_R, inp.pi_P, (4, 4, 8), (6, 6), 80)
+    s0 = np.linalg.svd(W0, compute_uv=False)
+    s = np.linalg.svd(Wn, compute_uv=False)
+    assert np.max(np.abs(s - s0)) / s0[0] < 1e-12
+    assert oracle.rel_fro(Wn, W0) > 1e-3      # and the weight did change
