@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12         # MI355X HBM3E, B/s
+PEAK_F32 = 157.3e12       # MI355X fp32 (vector or matrix), FLOP/s
 METRIC = "POET-X layer fwd+bwd tokens/s and % bf16 MFMA peak at hidden 2048, 1 GPU"
 
 
@@ -154,6 +155,8 @@ def main() -> int:
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB three times (for counter runs)")
+    ap.add_argument("--merge", action="store_true",
+                    help="also time the end-of-inner-loop merge W <- R W0 P of every layer")
     ap.add_argument("--xmem", action="store_true",
                     help="POET-Xmem: keep no Wa; the backward recomputes it from X")
     args = ap.parse_args()
@@ -235,6 +238,31 @@ def main() -> int:
 
     xmem = bool(args.xmem and w.backward)
     flops = stage_flops(w, T, xmem)
+    merge = None
+    if args.merge:
+        # outer loop: fold the trained factors of every layer into its weight
+        # (once per inner loop; fp32 block products on both sides)
+        outs = [torch.empty(L.m, L.n, dtype=tdt, device="cuda") for L in layers]
+        for L in layers:
+            L.workspace(poetx.WS_MERGE)
+        build_many(layers)
+        for L, o in zip(layers, outs):
+            L.merge(o)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            for L, o in zip(layers, outs):
+                L.merge(o)
+        e1.record()
+        torch.cuda.synchronize()
+        mms = e0.elapsed_time(e1) / reps
+        mfl = sum(2.0 * sp.n * sum(b * b for b in sp.bsz_R) + 2.0 * sp.m * sum(b * b for b in sp.bsz_P)
+                  for sp in w.layers)
+        merge = {"ms_all_layers": mms, "tflops": mfl / (mms * 1e-3) / 1e12,
+                 "fp32_frac": mfl / (mms * 1e-3) / PEAK_F32, "flops": mfl}
+        del outs
     stages = {}
     if not args.no_stages:
         # separate diagnostic pass: every stage bracketed by events
@@ -308,6 +336,8 @@ def main() -> int:
         "gemm_stage_mfma_frac": gemm_frac,
         "stages": stages,
     }
+    if merge is not None:
+        out["merge"] = merge
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)

@@ -62,7 +62,8 @@ typedef enum {
   POETX_WS_BUILD = 0,       /* poetx_build_orth, one item of poetx_build_orth_batch */
   POETX_WS_FORWARD = 1,     /* poetx_forward                                        */
   POETX_WS_BACKWARD = 2,    /* poetx_backward and poetx_backward_dq                  */
-  POETX_WS_PARAM_GRAD = 3   /* one item of poetx_param_grad_batch (T is ignored)     */
+  POETX_WS_PARAM_GRAD = 3,  /* one item of poetx_param_grad_batch (T is ignored)     */
+  POETX_WS_MERGE = 4        /* poetx_merge_weight (T is ignored)                     */
 } poetx_ws_kind;
 
 typedef struct poetx_plan poetx_plan;   /* opaque, immutable after create */
@@ -111,6 +112,22 @@ const char* poetx_last_hip_error(void);
 poetx_status poetx_permute_weight(const poetx_plan* plan, const void* W0,
                                   const int32_t* pi_R, const int32_t* pi_P,
                                   void* Wt, void* stream);
+
+/* End of an inner loop: the orthogonal factors are folded into the weight,
+ * W_out = R W0 P in the original coordinates (the two-sided orthogonal update
+ * W_new = Q_left W Q_right of [Pion] "数学原理"; [PX] §2.B keeps W fixed for the
+ * inner loop). The caller then starts the next inner loop from W_out with
+ * theta = 0 and new permutations (poetx_permute_weight).
+ *   Wt         device [m, n] (dtype): poetx_permute_weight(W0, pi_R, pi_P)
+ *   pi_R, pi_P device int32, the permutations Wt was built with
+ *   Q_R, Q_P   device fp32 blocks (the Q_f32 output of poetx_build_orth)
+ *   W_out      device [m, n] (dtype), not aliasing Wt
+ *   ws         device, poetx_workspace_size(plan, 0, POETX_WS_MERGE) bytes.
+ * The products run in fp32 from the fp32 blocks (Wt widened exactly); W_out is
+ * rounded once to the dtype (bf16: round to nearest even). Deterministic. */
+poetx_status poetx_merge_weight(const poetx_plan* plan, const void* Wt, const int32_t* pi_R,
+                                const int32_t* pi_P, const float* Q_R, const float* Q_P,
+                                void* W_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Cayley-Neumann blocks from packed skew parameters ([PX] §2.D).
  *   theta  device fp32 [poetx_param_count(side)]

@@ -67,6 +67,20 @@ __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const float* __rest
     out[i] = static_cast<__bf16>(in[i]);   // round to nearest even
 }
 
+__global__ __launch_bounds__(kThreads) void widen_bf16_kernel(const __bf16* __restrict__ in,
+                                                              float* __restrict__ out, long long n) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (long long)gridDim.x * kThreads)
+    out[i] = static_cast<float>(in[i]);   // exact
+}
+
+// inv[pi[i]] = i
+__global__ __launch_bounds__(kThreads) void invert_perm_kernel(const int32_t* __restrict__ pi,
+                                                               int32_t* __restrict__ inv, int n) {
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads)
+    inv[pi[i]] = i;
+}
+
 __global__ __launch_bounds__(kThreads) void copy_f32_kernel(const float* __restrict__ in,
                                                             float* __restrict__ out, long long n) {
   for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n;
@@ -126,6 +140,19 @@ hipError_t launch_cast(const float* in, void* out, long long n, int to_bf16, hip
     hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid1d(n)), dim3(kThreads), 0, s, in, (__bf16*)out, n);
   else
     hipLaunchKernelGGL(copy_f32_kernel, dim3(grid1d(n)), dim3(kThreads), 0, s, in, (float*)out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_widen(const void* in, float* out, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(widen_bf16_kernel, dim3(grid1d(n)), dim3(kThreads), 0, s, (const __bf16*)in, out,
+                     n);
+  return hipGetLastError();
+}
+
+hipError_t launch_invert_perm(const int32_t* pi, int32_t* inv, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(invert_perm_kernel, dim3(grid1d(n)), dim3(kThreads), 0, s, pi, inv, n);
   return hipGetLastError();
 }
 

@@ -190,6 +190,28 @@ size_t layout_param_grad(const poetx_plan* pl, int side, void* base, ChainWs* cw
   return c.off;
 }
 
+// merge workspace: Wt in fp32 (bf16 plans), the two fp32 products, the bf16
+// rounding of the result (bf16 plans), and both inverse permutations
+struct MergeWs {
+  float *F, *M1, *M2;
+  void* C;
+  int32_t *invR, *invP;
+};
+size_t layout_merge(const poetx_plan* pl, void* base, MergeWs* w) {
+  Carver c(base);
+  const long long mn = (long long)pl->m * pl->n;
+  const bool bf16 = pl->dtype == POETX_BF16;
+  MergeWs x;
+  x.F = bf16 ? (float*)c.take(4 * mn) : nullptr;
+  x.M1 = (float*)c.take(4 * mn);
+  x.M2 = (float*)c.take(4 * mn);
+  x.C = bf16 ? c.take(2 * mn) : nullptr;
+  x.invR = (int32_t*)c.take(4 * (size_t)pl->m);
+  x.invP = (int32_t*)c.take(4 * (size_t)pl->n);
+  if (w) *w = x;
+  return c.off;
+}
+
 size_t layout_build(const poetx_plan* pl, void* base, float** S, float** P0, float** P1) {
   Carver c(base);
   const long long ne = std::max(pl->nelem[0], pl->nelem[1]);
@@ -652,6 +674,7 @@ size_t poetx_workspace_size(const poetx_plan* pl, int64_t T, int32_t kind) {
     case POETX_WS_BUILD: return layout_build(pl, nullptr, nullptr, nullptr, nullptr);
     case POETX_WS_FORWARD: return layout_fwd(pl, T, nullptr, nullptr);
     case POETX_WS_BACKWARD: return layout_bwd(pl, T, nullptr, nullptr, nullptr);
+    case POETX_WS_MERGE: return layout_merge(pl, nullptr, nullptr);
     case POETX_WS_PARAM_GRAD: {
       size_t mx = 0;
       for (int side = 0; side < 2; ++side)
@@ -670,6 +693,57 @@ poetx_status poetx_permute_weight(const poetx_plan* pl, const void* W0, const in
   if (W0 == Wt) return POETX_ERR_INVALID_ARG;
   HIP_TRY(poetx::launch_gather_cols(W0, pl->n, pi_R, pi_P, Wt, pl->m, pl->n, elsize(pl),
                                     (hipStream_t)stream));
+  return POETX_OK;
+}
+
+poetx_status poetx_merge_weight(const poetx_plan* pl, const void* Wt, const int32_t* pi_R,
+                                const int32_t* pi_P, const float* Q_R, const float* Q_P,
+                                void* W_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!pl || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !W_out) return POETX_ERR_INVALID_ARG;
+  for (const void* p : {Wt, (const void*)pi_R, (const void*)pi_P, (const void*)Q_R,
+                        (const void*)Q_P, (const void*)W_out, (const void*)ws})
+    if (!aligned16(p)) return POETX_ERR_ALIGNMENT;
+  if (Wt == W_out) return POETX_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < poetx_workspace_size(pl, 0, POETX_WS_MERGE)) return POETX_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  MergeWs w;
+  layout_merge(pl, ws, &w);
+  const long long m = pl->m, n = pl->n;
+  const float* src = static_cast<const float*>(Wt);
+  if (pl->dtype == POETX_BF16) {
+    HIP_TRY(poetx::launch_widen(Wt, w.F, m * n, s));
+    src = w.F;
+  }
+  // M1 = D_R Wt: rows of each R block times its Q (M1[blk] = Q Wt[blk])
+  for (const Seg& g : pl->segs[POETX_SIDE_R]) {
+    poetx::GemmF32 p{};
+    p.A = Q_R + g.q_off; p.a_rs = g.b; p.a_cs = 1; p.a_gs = (long long)g.b * g.b;
+    p.B = src + g.dim_off * n; p.b_rs = 1; p.b_cs = n; p.b_gs = (long long)g.b * n;
+    p.C = w.M1 + g.dim_off * n; p.c_rs = n; p.c_gs = (long long)g.b * n;
+    p.M = g.b; p.N = (int)n; p.K = g.b; p.groups = g.count; p.splits = 1;
+    p.alpha = 1.0f;
+    HIP_TRY(poetx::launch_gemm_f32(p, s));
+  }
+  // M2 = M1 D_P: columns of each P block times its Q (M2[:, blk] = M1[:, blk] Q)
+  for (const Seg& g : pl->segs[POETX_SIDE_P]) {
+    poetx::GemmF32 p{};
+    p.A = w.M1 + g.dim_off; p.a_rs = n; p.a_cs = 1; p.a_gs = g.b;
+    p.B = Q_P + g.q_off; p.b_rs = 1; p.b_cs = g.b; p.b_gs = (long long)g.b * g.b;
+    p.C = w.M2 + g.dim_off; p.c_rs = n; p.c_gs = g.b;
+    p.M = (int)m; p.N = g.b; p.K = g.b; p.groups = g.count; p.splits = 1;
+    p.alpha = 1.0f;
+    HIP_TRY(poetx::launch_gemm_f32(p, s));
+  }
+  // back to the original coordinates: W_out = Pi_R^T M2 Pi_P, i.e.
+  // W_out[a][c] = M2[invR[a]][invP[c]], one rounding to the dtype first
+  HIP_TRY(poetx::launch_invert_perm(pi_R, w.invR, (int)m, s));
+  HIP_TRY(poetx::launch_invert_perm(pi_P, w.invP, (int)n, s));
+  const void* gsrc = w.M2;
+  if (pl->dtype == POETX_BF16) {
+    HIP_TRY(poetx::launch_cast(w.M2, w.C, m * n, 1, s));
+    gsrc = w.C;
+  }
+  HIP_TRY(poetx::launch_gather_cols(gsrc, n, w.invR, w.invP, W_out, m, (int)n, elsize(pl), s));
   return POETX_OK;
 }
 

@@ -34,6 +34,10 @@ hipError_t launch_pack_antisym(const float* M, const Seg& g, float sign, float* 
                                hipStream_t s);
 // out = (to_bf16 ? bf16 : fp32) copy of n floats.
 hipError_t launch_cast(const float* in, void* out, long long n, int to_bf16, hipStream_t s);
+// out = float(in) for n bf16 values (exact)
+hipError_t launch_widen(const void* in, float* out, long long n, hipStream_t s);
+// inv[pi[i]] = i for a permutation pi of 0..n-1
+hipError_t launch_invert_perm(const int32_t* pi, int32_t* inv, int n, hipStream_t s);
 // out1 = c * in; out2 = c * in (out2 may be null)
 hipError_t launch_scale2(const float* in, float c, float* out1, float* out2, long long n,
                          hipStream_t s);

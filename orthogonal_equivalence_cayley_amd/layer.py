@@ -81,6 +81,17 @@ class PoetxLayer:
         self.Wt = torch.empty_like(W0)
         self.plan.permute_weight(W0, self.pi_R, self.pi_P, self.Wt)
 
+    def merge(self, W_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """End of an inner loop: R W0 P in the original coordinates, from the
+        blocks of the last build(). Start the next loop with
+        set_weight(W_new, new permutations) and set_theta(zeros)."""
+        if W_out is None:
+            W_out = torch.empty(self.m, self.n, dtype=self.tdtype, device=self.device)
+        ws = self.workspace(_px.WS_MERGE)
+        self.plan.merge_weight(self.Wt, self.pi_R, self.pi_P, self.Q32[0], self.Q32[1], W_out,
+                               ws, ws.numel())
+        return W_out
+
     def set_theta(self, theta_R: torch.Tensor, theta_P: torch.Tensor) -> None:
         self.theta = [theta_R.to(device=self.device, dtype=torch.float32).contiguous(),
                       theta_P.to(device=self.device, dtype=torch.float32).contiguous()]

@@ -31,10 +31,12 @@ WS_BUILD = 0
 WS_FORWARD = 1
 WS_BACKWARD = 2
 WS_PARAM_GRAD = 3
+WS_MERGE = 4
 
 EXPORTED = (
     "poetx_plan_create", "poetx_plan_destroy", "poetx_param_count", "poetx_block_elems",
     "poetx_workspace_size", "poetx_status_string", "poetx_last_hip_error", "poetx_permute_weight",
+    "poetx_merge_weight",
     "poetx_build_orth", "poetx_build_orth_batch", "poetx_forward", "poetx_backward",
     "poetx_backward_dq", "poetx_param_grad_batch", "poetx_gather_cols",
     "poetx_scatter_cols", "poetx_timing_enable", "poetx_timing_read", "poetx_timing_reset",
@@ -85,6 +87,7 @@ def _load() -> ctypes.CDLL:
         "poetx_status_string": (ctypes.c_char_p, [st]),
         "poetx_last_hip_error": (ctypes.c_char_p, []),
         "poetx_permute_weight": (st, [vp, vp, vp, vp, vp, vp]),
+        "poetx_merge_weight": (st, [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "poetx_build_orth": (st, [vp, i32, vp, vp, vp, vp, sz, vp]),
         "poetx_build_orth_batch": (st, [i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "poetx_forward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -230,6 +233,11 @@ class Plan:
     def permute_weight(self, W0, pi_R, pi_P, Wt, stream=None) -> None:
         _check(LIB.poetx_permute_weight(self._h, _ptr(W0), _ptr(pi_R), _ptr(pi_P), _ptr(Wt),
                                         _stream(stream)), "poetx_permute_weight")
+
+    def merge_weight(self, Wt, pi_R, pi_P, Q_R, Q_P, W_out, ws, ws_bytes: int, stream=None) -> None:
+        _check(LIB.poetx_merge_weight(self._h, _ptr(Wt), _ptr(pi_R), _ptr(pi_P), _ptr(Q_R),
+                                      _ptr(Q_P), _ptr(W_out), _ptr(ws), ws_bytes, _stream(stream)),
+               "poetx_merge_weight")
 
     def build_orth(self, side: int, theta, Q_f32, Q_act, ws, ws_bytes: int, stream=None) -> None:
         _check(LIB.poetx_build_orth(self._h, side, _ptr(theta), _ptr(Q_f32), _ptr(Q_act),

@@ -143,3 +143,23 @@ def test_bench_traffic_record_is_valid_or_marked_stale():
     assert rec["traffic_bytes_per_launch"] >= rec["write_bytes_per_launch"] > 0
     rec2, why2 = bench.load_traffic("w0_gemm_nn_lds", "no-such-workload")
     assert rec2 is None and why2
+
+
+def test_merge_argument_errors():
+    p = _plan()
+    wsb = p.workspace_size(0, px.WS_MERGE)
+    assert wsb >= 2 * 64 * 48 * 4 + (64 + 48) * 4      # fp32: two fp32 products, inverse perms
+    args = [p.handle, A, A + 16, A + 32, A + 48, A + 64, A + 80, A + 96, wsb, None]
+    bad = list(args)
+    bad[6] = None
+    assert px.LIB.poetx_merge_weight(*bad) == px.POETX_ERR_INVALID_ARG
+    bad = list(args)
+    bad[6] = args[1]                      # W_out aliasing Wt
+    assert px.LIB.poetx_merge_weight(*bad) == px.POETX_ERR_INVALID_ARG
+    bad = list(args)
+    bad[4] = A + 4
+    assert px.LIB.poetx_merge_weight(*bad) == px.POETX_ERR_ALIGNMENT
+    bad = list(args)
+    bad[8] = wsb - 1
+    assert px.LIB.poetx_merge_weight(*bad) == px.POETX_ERR_WORKSPACE
+    assert px.LIB.poetx_merge_weight(None, *args[1:]) == px.POETX_ERR_INVALID_ARG

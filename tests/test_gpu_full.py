@@ -82,3 +82,20 @@ def test_block_workload_layer_sampled(cid, li):
             want = oracle.theta_grad_block(side, j, inp.X, Wt, inp.pi_R, inp.pi_P, inp.theta_R,
                                            inp.theta_P, QR, QP, inp.G_Y, sp.bsz_R, sp.bsz_P, w.k)
             _check(f"g_theta_{side}[block {j}]", g[offs[j]:offs[j + 1]], want, TOL_BF16)
+
+
+def test_merge_full_size():
+    """Merge of the 5632 x 2048 layer (b = 256 on both sides) at its real shape
+    against the dense float64 merge."""
+    import torch
+    w = workloads.WORKLOADS[3]
+    inp = workloads.layer_inputs(w, 0, T=1)
+    from gpu_util import make_layer, to_np
+    L = make_layer(inp, w.k, w.dtype)
+    L.build()
+    W = L.merge()
+    torch.cuda.synchronize()
+    sp = inp.spec
+    want = oracle.merge_weight(inp.W0, inp.theta_R, inp.theta_P, inp.pi_R, inp.pi_P, sp.bsz_R,
+                               sp.bsz_P, w.k)
+    _check("W_new", to_np(W), want, 4e-3)

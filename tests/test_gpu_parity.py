@@ -281,3 +281,56 @@ def test_xmem_recompute_matches_saved(case):
     tol = TOL_BF16 if dt == "bf16" else TOL_F32
     got = dict(Y=to_np(Y), G_X=to_np(mem[0]), g_theta_R=to_np(mem[1]), g_theta_P=to_np(mem[2]))
     _compare(got, ref, ["Y", "G_X", "g_theta_R", "g_theta_P"], tol, "xmem")
+
+
+# ---------------------------------------------------------------- outer loop
+
+@pytest.mark.parametrize("dt, c", [
+    ("f32", dict(m=96, n=130, bR=(32, 64), bP=(65, 65), k=2)),
+    ("f32", dict(m=12, n=9, bR=(5, 7), bP=(4, 1, 4), k=0)),
+    ("bf16", dict(m=512, n=256, bR=(256, 256), bP=(128, 128), k=4)),
+    ("bf16", dict(m=768, n=1024, bR=(512, 256), bP=(256,) * 4, k=3)),
+])
+def test_merge_weight(dt, c):
+    """R W0 P from the built blocks, in the original coordinates."""
+    import torch
+    inp = workloads.small_case(c["m"], c["n"], c["bR"], c["bP"], T=1, seed=c["n"] + 3, dtype=dt,
+                               theta_std=0.05 if dt == "f32" else 0.01)
+    log(f"merge {dt} {c}")
+    L = make_layer(inp, c["k"], dt)
+    L.build()
+    W = L.merge()
+    torch.cuda.synchronize()
+    want = oracle.merge_weight(inp.W0, inp.theta_R, inp.theta_P, inp.pi_R, inp.pi_P, c["bR"], c["bP"],
+                               c["k"])
+    err = oracle.rel_fro(to_np(W), want)
+    log(f"  rel_fro={err:.3e}")
+    # fp32: accumulation only; bf16: one rounding of the result (<= 2^-9 per element)
+    assert err <= (TOL_F32 if dt == "f32" else 4e-3)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_outer_loop_keeps_the_layer(dt):
+    """merge, then theta = 0 and new permutations: the layer computes the same
+    map (up to the rounding of the merged weight)."""
+    import torch
+    inp = workloads.small_case(512, 256, (256, 256), (128, 128), T=300, seed=17, dtype=dt,
+                               theta_std=0.05 if dt == "f32" else 0.01)
+    L = make_layer(inp, 4, dt)
+    L.build()
+    X = to_dev(inp.X, dt)
+    Y1 = L.forward(X, save=False).clone()
+    W = L.merge()
+    rng = np.random.default_rng(99)
+    pR = rng.permutation(512).astype(np.int32)
+    pP = rng.permutation(256).astype(np.int32)
+    L.set_weight(W, torch.from_numpy(pR), torch.from_numpy(pP))
+    L.set_theta(torch.zeros(L.nparam[0]), torch.zeros(L.nparam[1]))
+    L.build()
+    Y2 = L.forward(X, save=False)
+    torch.cuda.synchronize()
+    ref = oracle.layer_reference(inp, 4, backward_pass=False)["Y"]
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert oracle.rel_fro(to_np(Y1), ref) <= tol
+    assert oracle.rel_fro(to_np(Y2), ref) <= tol
+    assert oracle.rel_fro(to_np(Y2), to_np(Y1)) <= tol
