@@ -44,7 +44,7 @@ __all__ = [
     "block_offsets", "apply_blocks_T", "apply_blocks", "permute_weight",
     "forward", "forward_rows", "cnp_backward", "backward", "cnp_coefficients",
     "rel_fro", "layer_reference", "backward_rows", "theta_grad_block", "side_matrix",
-    "merge_weight",
+    "merge_weight", "quantize_rows", "dequantize_rows",
 ]
 
 
@@ -294,3 +294,28 @@ def merge_weight(W0, theta_R, theta_P, pi_R, pi_P, bsz_R, bsz_P, k: int) -> np.n
     R = side_matrix(build_orth(theta_R, bsz_R, k), bsz_R, pi_R)
     P = side_matrix(build_orth(theta_P, bsz_P, k), bsz_P, pi_P)
     return R @ np.asarray(W0, dtype=np.float64) @ P
+
+
+def quantize_rows(W) -> Tuple[np.ndarray, np.ndarray]:
+    """INT8 storage of the frozen weight (POET-XQ, [PX] §2.E "Quantification":
+    the base weights are kept in INT8 and dequantised on the fly). The pages do
+    not give the scheme; the one used here is symmetric, one scale per output
+    row, every step in float32 with round-to-nearest-even, as written:
+      amax = max_j |W[i, j]|,  inv = 127 / amax,  q = clamp(rint(W * inv), -127, 127),
+      s = amax / 127   (amax = 0 gives s = 0 and q = 0).
+    Returns (q int8 [m, n], s float32 [m])."""
+    W = np.asarray(W, dtype=np.float32)
+    amax = np.max(np.abs(W), axis=1)
+    nz = amax > 0
+    inv = np.zeros_like(amax)
+    inv[nz] = np.float32(127.0) / amax[nz]
+    q = np.clip(np.rint(W * inv[:, None]), -127, 127).astype(np.int8)
+    s = np.zeros_like(amax)
+    s[nz] = amax[nz] / np.float32(127.0)
+    return q, s.astype(np.float32)
+
+
+def dequantize_rows(q, s) -> np.ndarray:
+    """The weight the quantised layer computes with: W[i, j] = s[i] * q[i, j]
+    (float64; the product of an int8 and a float32 is exact in float64)."""
+    return np.asarray(s, dtype=np.float64)[:, None] * np.asarray(q, dtype=np.float64)

@@ -353,3 +353,42 @@ def test_merge_preserves_the_spectrum_in_the_cayley_limit():
     s = np.linalg.svd(Wn, compute_uv=False)
     assert np.max(np.abs(s - s0)) / s0[0] < 1e-12
     assert oracle.rel_fro(Wn, W0) > 1e-3      # and the weight did change
+
+
+# --------------------------------------------------------------------------
+# INT8 frozen weight
+
+def test_quantize_rows_bounds_and_grid():
+    rng = np.random.default_rng(12)
+    W = (rng.standard_normal((40, 70)) * rng.uniform(0.01, 3.0, size=(40, 1))).astype(np.float32)
+    W[3] = 0.0                                          # an all-zero row
+    q, s = oracle.quantize_rows(W)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert np.all(np.abs(q.astype(np.int32)) <= 127)
+    amax = np.abs(W).max(axis=1)
+    # the largest entry of every non-zero row maps to +-127 and the scale is amax / 127
+    for i in range(40):
+        if amax[i] == 0:
+            assert s[i] == 0 and np.all(q[i] == 0)
+            continue
+        assert np.abs(q[i]).max() == 127
+        assert abs(float(s[i]) * 127 - float(amax[i])) <= 1e-6 * float(amax[i])
+    # every entry within half a step of its grid point (plus float32 rounding)
+    err = np.abs(oracle.dequantize_rows(q, s) - W.astype(np.float64))
+    assert np.all(err <= 0.5 * s[:, None].astype(np.float64) * (1 + 1e-5) + 1e-12)
+    # values already on the grid come back exactly
+    W2 = (np.arange(-127, 128, dtype=np.float32) * np.float32(0.25))[None, :].repeat(2, 0)
+    q2, s2 = oracle.quantize_rows(W2)
+    assert np.array_equal(q2[0], np.arange(-127, 128).astype(np.int8))
+    assert np.array_equal(oracle.dequantize_rows(q2, s2), W2.astype(np.float64))
+
+
+def test_quantize_rows_commutes_with_row_and_column_permutations():
+    # one scale per row: permuting rows permutes (q, s); permuting columns only
+    # permutes q, so quantising W0 and then pre-merging equals quantising Wt
+    rng = np.random.default_rng(4)
+    W = rng.standard_normal((16, 24)).astype(np.float32)
+    pr, pc = rng.permutation(16), rng.permutation(24)
+    q, s = oracle.quantize_rows(W)
+    q2, s2 = oracle.quantize_rows(W[pr][:, pc])
+    assert np.array_equal(q2, q[pr][:, pc]) and np.array_equal(s2, s[pr])
