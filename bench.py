@@ -58,12 +58,14 @@ def stage_flops(w, T, xmem=False):
     return f
 
 
-def w0_bytes_per_step(w, T):
+def w0_bytes_per_step(w, T, int8=False):
     """Algorithmic HBM bytes of the frozen-weight products of one pass over all
     layers: each reads its activation operand and Wt once and writes its output
-    once (same for the forward and the backward form)."""
+    once (same for the forward and the backward form; an INT8 Wt is one byte per
+    element plus one fp32 scale per row)."""
     el = 2 if w.dtype == "bf16" else 4
-    return sum(el * (T * sp.n + sp.m * sp.n + T * sp.m) for sp in w.layers)
+    wb = (lambda sp: sp.m * sp.n + 4 * sp.m) if int8 else (lambda sp: el * sp.m * sp.n)
+    return sum(el * (T * sp.n + T * sp.m) + wb(sp) for sp in w.layers)
 
 
 def kernel_source_digest(path: str) -> str:
@@ -157,6 +159,8 @@ def main() -> int:
                     help="first run a plain device copy of MIB MiB three times (for counter runs)")
     ap.add_argument("--merge", action="store_true",
                     help="also time the end-of-inner-loop merge W <- R W0 P of every layer")
+    ap.add_argument("--xq", action="store_true",
+                    help="POET-XQ: frozen weight stored as INT8 (one scale per row)")
     ap.add_argument("--xmem", action="store_true",
                     help="POET-Xmem: keep no Wa; the backward recomputes it from X")
     args = ap.parse_args()
@@ -182,7 +186,8 @@ def main() -> int:
     for li in range(len(w.layers)):
         inp = workloads.layer_inputs(w, li, draw_grad=w.backward)
         sp = inp.spec
-        L = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, w.k, dtype=w.dtype)
+        L = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, w.k, dtype=w.dtype,
+                       weight="int8" if args.xq else "dense")
         L.set_weight(dev(inp.W0), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
         L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
         b = dict(X=dev(inp.X), Y=torch.empty(T, sp.m, dtype=tdt, device="cuda"),
@@ -283,11 +288,14 @@ def main() -> int:
     dom = max(w0, key=lambda s: w0[s][0])
     ms_tot, launches = w0[dom]
     kernel = {"w0_fwd": "w0_gemm_nt_lds", "w0_bwd": "w0_gemm_nn_lds"}[dom]
+    if args.xq:
+        kernel = kernel.replace("w0_", "w0q_")
     flops_per_launch = flops[dom] * args.steps / launches
     avg_s = ms_tot / launches * 1e-3
     achieved = flops_per_launch / avg_s
     traffic, traffic_note = None, None
-    rec, why = load_traffic(kernel, w.name) if not xmem else (None, "counters taken without xmem")
+    rec, why = load_traffic(kernel, w.name) if not (xmem or args.xq) else \
+        (None, "counters taken on the dense Xfast step only")
     if rec is not None:
         traffic = rec["traffic_bytes_per_launch"]
         traffic_note = (f"HBM bytes per launch, rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by a plain "
@@ -321,13 +329,14 @@ def main() -> int:
             "block_size": max(max(sp.bsz_R) for sp in w.layers),
             "passes": "build+forward+backward" if w.backward else "build+forward",
             "saved_activation": "none (POET-Xmem: recomputed)" if xmem else "Wa (POET-Xfast)",
+            "frozen_weight": "int8, one fp32 scale per row (POET-XQ)" if args.xq else w.dtype,
         },
         "roofline": {
             "kernel": kernel, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": traffic,
             "launches": launches, "avg_launch_us": avg_s * 1e6,
             "flops_per_launch": flops_per_launch,
-            "algorithmic_bytes_per_launch": w0_bytes_per_step(w, T) * args.steps / launches
+            "algorithmic_bytes_per_launch": w0_bytes_per_step(w, T, args.xq) * args.steps / launches
             * (2 if (xmem and dom == "w0_fwd") else 1),
             "traffic_note": traffic_note,
         },

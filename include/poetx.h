@@ -57,6 +57,16 @@ typedef enum {
 } poetx_status;
 
 typedef enum { POETX_FP32 = 0, POETX_BF16 = 1 } poetx_dtype;
+
+/* Storage of the pre-merged frozen weight Wt that forward, backward and merge read.
+ *   POETX_WEIGHT_DENSE:     [m, n] in the plan dtype (poetx_permute_weight).
+ *   POETX_WEIGHT_INT8_ROWS: POET-XQ ([PX] §2.E "Quantification": base weights
+ *     kept in INT8, dequantised on the fly); the pages give no scheme, this one
+ *     is symmetric with one fp32 scale per row of Wt. Layout: int8 q [m, n]
+ *     row-major, then at byte offset ceil(m n / 256) * 256 the fp32 scales [m];
+ *     Wt[i][j] = s[i] * q[i][j]. Built by poetx_quantize_weight; needs bf16
+ *     and m, n multiples of 256, n <= 32768. */
+typedef enum { POETX_WEIGHT_DENSE = 0, POETX_WEIGHT_INT8_ROWS = 1 } poetx_weight;
 typedef enum { POETX_SIDE_R = 0, POETX_SIDE_P = 1 } poetx_side;
 typedef enum {
   POETX_WS_BUILD = 0,       /* poetx_build_orth, one item of poetx_build_orth_batch */
@@ -77,6 +87,7 @@ typedef struct {
   int32_t dtype;            /* poetx_dtype of X, Y, W0, Wt, Q copies and gradients
                                of X/Y. Skew parameters and their gradients are
                                always fp32; accumulation is always fp32.            */
+  int32_t weight;           /* poetx_weight: how Wt is stored                       */
 } poetx_desc;
 
 /* Create a plan. Host only: no device call is made, so it works without a GPU.
@@ -108,17 +119,34 @@ const char* poetx_last_hip_error(void);
  * two index operations per step): Wt[i][j] = W0[pi_R[i]][pi_P[j]].
  *   W0   device [m, n] (dtype)        pi_R device int32 [m]
  *   pi_P device int32 [n]             Wt   device [m, n] (dtype), not aliasing W0
- * Bit-exact copy. */
+ * Bit-exact copy. POETX_ERR_UNSUPPORTED for INT8 plans (poetx_quantize_weight). */
 poetx_status poetx_permute_weight(const poetx_plan* plan, const void* W0,
                                   const int32_t* pi_R, const int32_t* pi_P,
                                   void* Wt, void* stream);
+
+/* Bytes of Wt for this plan (m n elsize dense; the int8 layout of
+ * POETX_WEIGHT_INT8_ROWS otherwise). 0 for a NULL plan. */
+size_t poetx_weight_bytes(const poetx_plan* plan);
+
+/* POETX_WEIGHT_INT8_ROWS plans: pre-merge and quantise in one pass, the INT8
+ * counterpart of poetx_permute_weight. Row i of Wt is row pi_R[i] of W0 with its
+ * columns gathered by pi_P; in fp32, round to nearest even:
+ *   amax = max_j |Wt[i][j]|, inv = 127 / amax, q[i][j] = clamp(rint(Wt[i][j] inv), -127, 127),
+ *   s[i] = amax / 127 (amax = 0: q = 0, s = 0).
+ *   W0 device [m, n] bf16     Wq device, poetx_weight_bytes(plan) bytes, not aliasing W0
+ * POETX_ERR_UNSUPPORTED for dense plans. Bit-exact (integer decisions taken
+ * in fp32 with correctly rounded division). */
+poetx_status poetx_quantize_weight(const poetx_plan* plan, const void* W0, const int32_t* pi_R,
+                                   const int32_t* pi_P, void* Wq, void* stream);
 
 /* End of an inner loop: the orthogonal factors are folded into the weight,
  * W_out = R W0 P in the original coordinates (the two-sided orthogonal update
  * W_new = Q_left W Q_right of [Pion] "数学原理"; [PX] §2.B keeps W fixed for the
  * inner loop). The caller then starts the next inner loop from W_out with
  * theta = 0 and new permutations (poetx_permute_weight).
- *   Wt         device [m, n] (dtype): poetx_permute_weight(W0, pi_R, pi_P)
+ *   Wt         device [m, n] (dtype): poetx_permute_weight(W0, pi_R, pi_P); for
+ *              INT8 plans the poetx_quantize_weight layout (dequantised exactly
+ *              to fp32 first), the result W_out is then dense bf16
  *   pi_R, pi_P device int32, the permutations Wt was built with
  *   Q_R, Q_P   device fp32 blocks (the Q_f32 output of poetx_build_orth)
  *   W_out      device [m, n] (dtype), not aliasing Wt
@@ -158,7 +186,10 @@ poetx_status poetx_build_orth_batch(int32_t count, const poetx_plan* const* plan
 /* Input-centric forward ([PX] §2.A): Y = R W0 P applied to the rows of X without
  * forming R W0 P. Stages: gather X by pi_P, blocks of P, product with Wt,
  * blocks of R, scatter by pi_R.
- *   X        device [T, n] (dtype)       Wt  device [m, n] from poetx_permute_weight
+ *   X        device [T, n] (dtype)       Wt  device [m, n] from poetx_permute_weight,
+ *            or for INT8 plans the poetx_quantize_weight layout: the product
+ *            converts q to bf16 exactly on its way into LDS and applies s to the
+ *            fp32 accumulators of each output column
  *   pi_R, pi_P device int32              Q_R, Q_P device block arrays in the plan dtype
  *   Y        device [T, m] (dtype)
  *   Wa_saved device [T, m] (dtype) or NULL: the output of the Wt product, the
@@ -172,7 +203,9 @@ poetx_status poetx_forward(const poetx_plan* plan, int64_t T, const void* X, con
 
 /* Backward of L = <G_Y, Y> w.r.t. X and both sides' skew parameters, for the
  * truncated Q the forward used. W0 is frozen and gets no gradient.
- *   X, Wt, pi_R, pi_P, Q_R, Q_P as in poetx_forward
+ *   X, Wt, pi_R, pi_P, Q_R, Q_P as in poetx_forward (INT8 plans: the scale
+ *            of row i of Wt multiplies column i of G_Wa in the block product
+ *            that produces it, so that G_V = (G_Wa diag(s)) q)
  *   theta_R, theta_P device fp32 packed parameters (rebuild S for the chain rule)
  *   Wa_saved device [T, m] from poetx_forward, or NULL: then the backward
  *            recomputes it from X (gather, blocks of P, Wt product: POET-Xmem,

@@ -264,8 +264,13 @@ hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s) {
   // whole-tile shapes take the pipelined direct-to-LDS kernels; the rest (K not a
   // multiple of 64, partial tiles of row-contiguous operands) the kernels here
   if (gemm_lds_supported(p, big ? 256 : 128, big ? 256 : 128)) return launch_gemm_lds(p, big, s);
-  if (big) return dispatch<256, 256, 128, 128>(p, s);
-  return dispatch<128, 128, 64, 64>(p, s);
+  // an int8 operand exists only on the pipelined kernels; a column scale is
+  // applied by a separate pass here (one more rounding of the bf16 output)
+  if (p.b_i8) return hipErrorInvalidValue;
+  if (p.col_scale && (p.out_f32 || p.c_gs != p.N)) return hipErrorInvalidValue;
+  const hipError_t e = big ? dispatch<256, 256, 128, 128>(p, s) : dispatch<128, 128, 64, 64>(p, s);
+  if (e != hipSuccess || !p.col_scale) return e;
+  return launch_scale_cols(p.C, p.col_scale, p.M, p.N * p.groups, p.ldc, s);
 }
 
 }  // namespace poetx

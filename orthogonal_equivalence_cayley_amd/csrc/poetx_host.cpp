@@ -20,6 +20,7 @@ using poetx::Seg;
 
 struct poetx_plan {
   int m = 0, n = 0, k = 0, dtype = 0;
+  int weight = POETX_WEIGHT_DENSE;   // poetx_weight: how Wt is stored
   std::vector<int> bsz[2];
   std::vector<Seg> segs[2];
   long long nparam[2] = {0, 0};
@@ -30,6 +31,15 @@ struct poetx_plan {
 namespace {
 
 constexpr size_t kAlign = 256;
+
+// INT8 weight: int8 [m, n] rows of Wt, then (256-byte aligned) the fp32 row scales
+bool wq(const poetx_plan* pl) { return pl->weight == POETX_WEIGHT_INT8_ROWS; }
+size_t qscale_off(const poetx_plan* pl) {
+  return ((size_t)pl->m * pl->n + kAlign - 1) / kAlign * kAlign;
+}
+const float* qscale(const poetx_plan* pl, const void* Wt) {
+  return reinterpret_cast<const float*>(static_cast<const char*>(Wt) + qscale_off(pl));
+}
 
 // ------------------------------------------------------------------ stage timing
 std::atomic<uint32_t> g_tmask{0};
@@ -243,7 +253,8 @@ struct Op {
 // C(m, n) = sum_k A(m, k) B(n, k) in the plan's dtype (fp32 output when out_f32).
 poetx_status gemm(const poetx_plan* pl, int role, Op A, Op B, void* C, long long ldc, int M, int N,
                   int K, int groups, long long a_gs, long long b_gs, long long c_gs, int splits,
-                  long long c_ss, bool out_f32, hipStream_t s) {
+                  long long c_ss, bool out_f32, hipStream_t s, const float* col_scale = nullptr,
+                  bool b_i8 = false) {
   if (pl->dtype == POETX_BF16) {
     poetx::GemmBf16 g;
     g.A = A.p; g.B = B.p; g.C = C;
@@ -257,6 +268,8 @@ poetx_status gemm(const poetx_plan* pl, int role, Op A, Op B, void* C, long long
     g.out_f32 = out_f32 ? 1 : 0;
     g.a_gs = a_gs; g.b_gs = b_gs; g.c_gs = c_gs;
     g.groups = groups; g.splits = splits; g.c_ss = c_ss;
+    g.b_i8 = b_i8 ? 1 : 0;
+    g.col_scale = col_scale;
     HIP_TRY(poetx::launch_gemm_bf16(g, s));
   } else {
     poetx::GemmF32 g;
@@ -293,7 +306,8 @@ poetx_status chain_gemm(const Seg& g, const float* X, const float* Y, float* C, 
 // Row-form product with one side's blocks: out[:, blk] = in[:, blk] Q^T
 // (transpose_q = true) or in[:, blk] Q (false), for every block of the side.
 poetx_status apply_blocks(const poetx_plan* pl, int side, long long T, const void* in,
-                          const void* Q, void* out, bool transpose_q, hipStream_t s) {
+                          const void* Q, void* out, bool transpose_q, hipStream_t s,
+                          const float* col_scale = nullptr) {
   const size_t es = elsize(pl);
   const long long dim = pl->dim[side];
   for (const Seg& g : pl->segs[side]) {
@@ -303,7 +317,8 @@ poetx_status apply_blocks(const poetx_plan* pl, int side, long long T, const voi
     // transpose_q: B(n, k) = Q[n][k]; otherwise B(n, k) = Q[k][n]
     Op B = transpose_q ? Op{q, g.b, 1} : Op{q, 1, g.b};
     poetx_status st = gemm(pl, poetx::GEMM_BLOCK, Op{a, dim, 1}, B, c, dim, (int)T, g.b, g.b, g.count, g.b,
-                           (long long)g.b * g.b, g.b, 1, 0, false, s);
+                           (long long)g.b * g.b, g.b, 1, 0, false, s,
+                           col_scale ? col_scale + g.dim_off : nullptr);
     if (st != POETX_OK) return st;
   }
   return POETX_OK;
@@ -447,7 +462,8 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
     {
       StageScope sc(POETX_STAGE_W0_FWD, s);
       if ((st = gemm(pl, poetx::GEMM_W0, Op{w.GU, pl->n, 1}, Op{Wt, pl->n, 1}, w.GWa, pl->m, (int)T,
-                     pl->m, pl->n, 1, 0, 0, 0, 1, 0, false, s)) != POETX_OK)
+                     pl->m, pl->n, 1, 0, 0, 0, 1, 0, false, s, wq(pl) ? qscale(pl, Wt) : nullptr,
+                     wq(pl))) != POETX_OK)
         return st;
     }
     Wa = w.GWa;
@@ -464,13 +480,17 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
   }
   {
     StageScope sc(POETX_STAGE_BLOCK_BWD, s);
-    if ((st = apply_blocks(pl, POETX_SIDE_R, T, w.GZ, Q_R, w.GWa, false, s)) != POETX_OK) return st;
+    // INT8 weight: G_Wa leaves scaled by the row scales of Wt, since
+    // G_Wa Wt = (G_Wa diag(s)) q
+    if ((st = apply_blocks(pl, POETX_SIDE_R, T, w.GZ, Q_R, w.GWa, false, s,
+                           wq(pl) ? qscale(pl, Wt) : nullptr)) != POETX_OK)
+      return st;
   }
   // frozen weight: G_V = G_Wa Wt
   {
     StageScope sc(POETX_STAGE_W0_BWD, s);
     if ((st = gemm(pl, poetx::GEMM_W0, Op{w.GWa, pl->m, 1}, Op{Wt, 1, pl->n}, w.GV, pl->n, (int)T,
-                   pl->n, pl->m, 1, 0, 0, 0, 1, 0, false, s)) != POETX_OK)
+                   pl->n, pl->m, 1, 0, 0, 0, 1, 0, false, s, nullptr, wq(pl))) != POETX_OK)
       return st;
   }
   // P side: U = X Pi_P^T; dQ_P = G_V^T U per block; G_U = G_V D_P; G_X = G_U Pi_P
@@ -612,6 +632,8 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
   if (d->m < 1 || d->n < 1 || d->nb_R < 1 || d->nb_P < 1) return POETX_ERR_SHAPE;
   if (!d->bsz_R || !d->bsz_P) return POETX_ERR_INVALID_ARG;
   if (d->k < 0 || d->k > 32) return POETX_ERR_SHAPE;
+  if (d->weight != POETX_WEIGHT_DENSE && d->weight != POETX_WEIGHT_INT8_ROWS)
+    return POETX_ERR_INVALID_ARG;
   const int32_t* bs[2] = {d->bsz_R, d->bsz_P};
   const int nb[2] = {d->nb_R, d->nb_P};
   const int dims[2] = {d->m, d->n};
@@ -629,9 +651,15 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
       for (int i = 0; i < nb[side]; ++i)
         if (bs[side][i] % 16) return POETX_ERR_UNSUPPORTED;
   }
+  // INT8 weight: bf16 activations and whole 256 x 256 tiles of the weight
+  // (the quantiser also stages one bf16 row of W0 in 64 KiB of LDS)
+  if (d->weight == POETX_WEIGHT_INT8_ROWS &&
+      (d->dtype != POETX_BF16 || d->m % 256 || d->n % 256 || d->n > 32768))
+    return POETX_ERR_UNSUPPORTED;
   poetx_plan* pl = new (std::nothrow) poetx_plan;
   if (!pl) return POETX_ERR_INVALID_ARG;
   pl->m = d->m; pl->n = d->n; pl->k = d->k; pl->dtype = d->dtype;
+  pl->weight = d->weight;
   for (int side = 0; side < 2; ++side) {
     pl->dim[side] = dims[side];
     long long q = 0, p = 0;
@@ -691,8 +719,28 @@ poetx_status poetx_permute_weight(const poetx_plan* pl, const void* W0, const in
   if (!aligned16(W0) || !aligned16(Wt) || !aligned16(pi_R) || !aligned16(pi_P))
     return POETX_ERR_ALIGNMENT;
   if (W0 == Wt) return POETX_ERR_INVALID_ARG;
+  if (wq(pl)) return POETX_ERR_UNSUPPORTED;   // poetx_quantize_weight builds that Wt
   HIP_TRY(poetx::launch_gather_cols(W0, pl->n, pi_R, pi_P, Wt, pl->m, pl->n, elsize(pl),
                                     (hipStream_t)stream));
+  return POETX_OK;
+}
+
+size_t poetx_weight_bytes(const poetx_plan* pl) {
+  if (!pl) return 0;
+  if (wq(pl)) return qscale_off(pl) + 4 * (size_t)pl->m;
+  return (size_t)pl->m * pl->n * elsize(pl);
+}
+
+poetx_status poetx_quantize_weight(const poetx_plan* pl, const void* W0, const int32_t* pi_R,
+                                   const int32_t* pi_P, void* Wq, void* stream) {
+  if (!pl || !W0 || !pi_R || !pi_P || !Wq) return POETX_ERR_INVALID_ARG;
+  if (!wq(pl)) return POETX_ERR_UNSUPPORTED;
+  if (!aligned16(W0) || !aligned16(Wq) || !aligned16(pi_R) || !aligned16(pi_P))
+    return POETX_ERR_ALIGNMENT;
+  if (W0 == Wq) return POETX_ERR_INVALID_ARG;
+  HIP_TRY(poetx::launch_quantize_rows(W0, pi_R, pi_P, static_cast<int8_t*>(Wq),
+                                      const_cast<float*>(qscale(pl, Wq)), pl->m, pl->n,
+                                      (hipStream_t)stream));
   return POETX_OK;
 }
 
@@ -710,7 +758,11 @@ poetx_status poetx_merge_weight(const poetx_plan* pl, const void* Wt, const int3
   layout_merge(pl, ws, &w);
   const long long m = pl->m, n = pl->n;
   const float* src = static_cast<const float*>(Wt);
-  if (pl->dtype == POETX_BF16) {
+  if (wq(pl)) {
+    HIP_TRY(poetx::launch_dequantize_rows(static_cast<const int8_t*>(Wt), qscale(pl, Wt), w.F,
+                                          (int)m, (int)n, s));
+    src = w.F;
+  } else if (pl->dtype == POETX_BF16) {
     HIP_TRY(poetx::launch_widen(Wt, w.F, m * n, s));
     src = w.F;
   }
@@ -806,7 +858,8 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
   {
     StageScope sc(POETX_STAGE_W0_FWD, s);
     if ((st = gemm(pl, poetx::GEMM_W0, Op{w.V, pl->n, 1}, Op{Wt, pl->n, 1}, Wa, pl->m, (int)T, pl->m,
-                   pl->n, 1, 0, 0, 0, 1, 0, false, s)) != POETX_OK)
+                   pl->n, 1, 0, 0, 0, 1, 0, false, s, wq(pl) ? qscale(pl, Wt) : nullptr,
+                   wq(pl))) != POETX_OK)
       return st;
   }
   // 4. blocks of R: Z = Wa D_R^T

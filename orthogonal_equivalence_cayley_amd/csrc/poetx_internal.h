@@ -36,6 +36,16 @@ hipError_t launch_pack_antisym(const float* M, const Seg& g, float sign, float* 
 hipError_t launch_cast(const float* in, void* out, long long n, int to_bf16, hipStream_t s);
 // out = float(in) for n bf16 values (exact)
 hipError_t launch_widen(const void* in, float* out, long long n, hipStream_t s);
+// INT8 rows of the pre-merged weight: q[i][j] = rint(W0[pi_R[i]][pi_P[j]] * 127 /
+// amax_i) and scale[i] = amax_i / 127 (bf16 W0, n % 8 == 0, 2n <= 64 KiB)
+hipError_t launch_quantize_rows(const void* W0, const int32_t* pi_R, const int32_t* pi_P,
+                                int8_t* q, float* scale, int m, int n, hipStream_t s);
+// bf16 C[t][c] *= scale[c] for t < rows, c < cols, row stride ld (one rounding)
+hipError_t launch_scale_cols(void* C, const float* scale, long long rows, int cols, long long ld,
+                             hipStream_t s);
+// out[i][j] = scale[i] * q[i][j] (fp32)
+hipError_t launch_dequantize_rows(const int8_t* q, const float* scale, float* out, int m, int n,
+                                  hipStream_t s);
 // inv[pi[i]] = i for a permutation pi of 0..n-1
 hipError_t launch_invert_perm(const int32_t* pi, int32_t* inv, int n, hipStream_t s);
 // out1 = c * in; out2 = c * in (out2 may be null)
@@ -78,6 +88,12 @@ struct GemmBf16 {
   int groups, splits;
   long long c_ss;
   int tpw;    // output tiles per workgroup (set by the launcher)
+  // B holds int8 values (converted exactly to bf16 on the way into LDS); only
+  // for GEMM_W0 on whole 256 x 256 (or 128 x 128) tiles
+  int b_i8 = 0;
+  // bf16 output only: column n of group g is multiplied by col_scale[g * c_gs + n]
+  // (fp32, before the rounding) when non-null
+  const float* col_scale = nullptr;
 };
 hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
 // Pipelined variant (direct-to-LDS loads, see k_gemm_lds.hip) for whole-tile shapes:

@@ -43,13 +43,17 @@ def param_grad_many(layers, g_thetas=None):
 
 class PoetxLayer:
     def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
-                 dtype: str = "bf16", device: str = "cuda"):
+                 dtype: str = "bf16", device: str = "cuda", weight: str = "dense"):
         if dtype not in _TORCH_DTYPE:
             raise ValueError(f"dtype must be one of {sorted(_TORCH_DTYPE)}")
+        if weight not in ("dense", "int8"):
+            raise ValueError("weight must be 'dense' or 'int8' (POET-XQ)")
         self.m, self.n, self.k, self.dtype = m, n, k, dtype
+        self.weight = weight
         self.device = torch.device(device)
         self.tdtype = _TORCH_DTYPE[dtype]
-        self.plan = _px.Plan(m, n, bsz_R, bsz_P, k, _PX_DTYPE[dtype])
+        self.plan = _px.Plan(m, n, bsz_R, bsz_P, k, _PX_DTYPE[dtype],
+                             _px.WEIGHT_INT8_ROWS if weight == "int8" else _px.WEIGHT_DENSE)
         self.nparam = (self.plan.param_count(_px.SIDE_R), self.plan.param_count(_px.SIDE_P))
         self.nelem = (self.plan.block_elems(_px.SIDE_R), self.plan.block_elems(_px.SIDE_P))
         self._ws = {}
@@ -74,12 +78,26 @@ class PoetxLayer:
         return cur
 
     def set_weight(self, W0: torch.Tensor, pi_R: torch.Tensor, pi_P: torch.Tensor) -> None:
-        """Pre-merge the permutations into W0 (once per inner loop)."""
+        """Pre-merge the permutations into W0 (once per inner loop); with an INT8
+        weight, quantise in the same pass."""
         assert W0.shape == (self.m, self.n) and W0.dtype == self.tdtype and W0.is_contiguous()
         self.pi_R = pi_R.to(device=self.device, dtype=torch.int32).contiguous()
         self.pi_P = pi_P.to(device=self.device, dtype=torch.int32).contiguous()
-        self.Wt = torch.empty_like(W0)
-        self.plan.permute_weight(W0, self.pi_R, self.pi_P, self.Wt)
+        if self.weight == "int8":
+            self.Wt = torch.empty(self.plan.weight_bytes(), dtype=torch.uint8, device=self.device)
+            self.plan.quantize_weight(W0, self.pi_R, self.pi_P, self.Wt)
+        else:
+            self.Wt = torch.empty_like(W0)
+            self.plan.permute_weight(W0, self.pi_R, self.pi_P, self.Wt)
+
+    def int8_weight(self):
+        """(q [m, n] int8, s [m] fp32) views of an INT8 Wt (rows in permuted order)."""
+        assert self.weight == "int8"
+        mn = self.m * self.n
+        off = (mn + 255) // 256 * 256
+        q = self.Wt[:mn].view(torch.int8).view(self.m, self.n)
+        s = self.Wt[off:off + 4 * self.m].view(torch.float32)
+        return q, s
 
     def merge(self, W_out: Optional[torch.Tensor] = None) -> torch.Tensor:
         """End of an inner loop: R W0 P in the original coordinates, from the

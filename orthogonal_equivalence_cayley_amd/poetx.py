@@ -33,10 +33,13 @@ WS_BACKWARD = 2
 WS_PARAM_GRAD = 3
 WS_MERGE = 4
 
+WEIGHT_DENSE = 0
+WEIGHT_INT8_ROWS = 1
+
 EXPORTED = (
     "poetx_plan_create", "poetx_plan_destroy", "poetx_param_count", "poetx_block_elems",
     "poetx_workspace_size", "poetx_status_string", "poetx_last_hip_error", "poetx_permute_weight",
-    "poetx_merge_weight",
+    "poetx_merge_weight", "poetx_weight_bytes", "poetx_quantize_weight",
     "poetx_build_orth", "poetx_build_orth_batch", "poetx_forward", "poetx_backward",
     "poetx_backward_dq", "poetx_param_grad_batch", "poetx_gather_cols",
     "poetx_scatter_cols", "poetx_timing_enable", "poetx_timing_read", "poetx_timing_reset",
@@ -60,7 +63,7 @@ class Desc(ctypes.Structure):
         ("m", ctypes.c_int32), ("n", ctypes.c_int32),
         ("nb_R", ctypes.c_int32), ("nb_P", ctypes.c_int32),
         ("bsz_R", ctypes.POINTER(ctypes.c_int32)), ("bsz_P", ctypes.POINTER(ctypes.c_int32)),
-        ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("weight", ctypes.c_int32),
     ]
 
 
@@ -88,6 +91,8 @@ def _load() -> ctypes.CDLL:
         "poetx_last_hip_error": (ctypes.c_char_p, []),
         "poetx_permute_weight": (st, [vp, vp, vp, vp, vp, vp]),
         "poetx_merge_weight": (st, [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "poetx_weight_bytes": (sz, [vp]),
+        "poetx_quantize_weight": (st, [vp, vp, vp, vp, vp, vp]),
         "poetx_build_orth": (st, [vp, i32, vp, vp, vp, vp, sz, vp]),
         "poetx_build_orth_batch": (st, [i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "poetx_forward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -194,12 +199,14 @@ class Plan:
     """Owns a poetx_plan (host-only object; creating one needs no GPU)."""
 
     def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
-                 dtype: int):
+                 dtype: int, weight: int = WEIGHT_DENSE):
         self.m, self.n, self.k, self.dtype = int(m), int(n), int(k), int(dtype)
+        self.weight = int(weight)
         self.bsz_R, self.bsz_P = tuple(int(b) for b in bsz_R), tuple(int(b) for b in bsz_P)
         aR = (ctypes.c_int32 * max(1, len(self.bsz_R)))(*self.bsz_R)
         aP = (ctypes.c_int32 * max(1, len(self.bsz_P)))(*self.bsz_P)
-        d = Desc(self.m, self.n, len(self.bsz_R), len(self.bsz_P), aR, aP, self.k, self.dtype)
+        d = Desc(self.m, self.n, len(self.bsz_R), len(self.bsz_P), aR, aP, self.k, self.dtype,
+                 self.weight)
         h = ctypes.c_void_p()
         self._h = None
         _check(LIB.poetx_plan_create(ctypes.byref(d), ctypes.byref(h)), "poetx_plan_create")
@@ -233,6 +240,13 @@ class Plan:
     def permute_weight(self, W0, pi_R, pi_P, Wt, stream=None) -> None:
         _check(LIB.poetx_permute_weight(self._h, _ptr(W0), _ptr(pi_R), _ptr(pi_P), _ptr(Wt),
                                         _stream(stream)), "poetx_permute_weight")
+
+    def weight_bytes(self) -> int:
+        return int(LIB.poetx_weight_bytes(self._h))
+
+    def quantize_weight(self, W0, pi_R, pi_P, Wq, stream=None) -> None:
+        _check(LIB.poetx_quantize_weight(self._h, _ptr(W0), _ptr(pi_R), _ptr(pi_P), _ptr(Wq),
+                                         _stream(stream)), "poetx_quantize_weight")
 
     def merge_weight(self, Wt, pi_R, pi_P, Q_R, Q_P, W_out, ws, ws_bytes: int, stream=None) -> None:
         _check(LIB.poetx_merge_weight(self._h, _ptr(Wt), _ptr(pi_R), _ptr(pi_P), _ptr(Q_R),

@@ -163,3 +163,27 @@ def test_merge_argument_errors():
     bad[8] = wsb - 1
     assert px.LIB.poetx_merge_weight(*bad) == px.POETX_ERR_WORKSPACE
     assert px.LIB.poetx_merge_weight(None, *args[1:]) == px.POETX_ERR_INVALID_ARG
+
+
+def test_int8_weight_plans():
+    bf, f32 = px.POETX_BF16, px.POETX_FP32
+    p = px.Plan(512, 256, (256, 256), (256,), 4, bf, px.WEIGHT_INT8_ROWS)
+    assert p.weight_bytes() == 512 * 256 + 4 * 512          # 131072 is a multiple of 256
+    p2 = px.Plan(256, 512, (256,), (256, 256), 4, bf, px.WEIGHT_INT8_ROWS)
+    assert p2.weight_bytes() == 256 * 512 + 4 * 256
+    assert px.Plan(512, 256, (256, 256), (256,), 4, bf).weight_bytes() == 512 * 256 * 2
+    for args, status in [((512, 256, (256, 256), (256,), 4, f32, 1), px.POETX_ERR_UNSUPPORTED),
+                         ((384, 256, (256, 128), (256,), 4, bf, 1), px.POETX_ERR_UNSUPPORTED),
+                         ((512, 256, (256, 256), (256,), 4, bf, 7), px.POETX_ERR_INVALID_ARG)]:
+        with pytest.raises(px.PoetxError) as e:
+            px.Plan(*args)
+        assert e.value.status == status
+    dense = px.Plan(512, 256, (256, 256), (256,), 4, bf)
+    assert px.LIB.poetx_quantize_weight(dense.handle, A, A + 16, A + 32, A + 48, None) == \
+        px.POETX_ERR_UNSUPPORTED
+    assert px.LIB.poetx_permute_weight(p.handle, A, A + 16, A + 32, A + 48, None) == \
+        px.POETX_ERR_UNSUPPORTED
+    assert px.LIB.poetx_quantize_weight(p.handle, A, A + 16, A + 32, A, None) == \
+        px.POETX_ERR_INVALID_ARG
+    assert px.LIB.poetx_quantize_weight(p.handle, A, A + 16, A + 36, A + 48, None) == \
+        px.POETX_ERR_ALIGNMENT

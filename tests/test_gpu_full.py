@@ -99,3 +99,25 @@ def test_merge_full_size():
     want = oracle.merge_weight(inp.W0, inp.theta_R, inp.theta_P, inp.pi_R, inp.pi_P, sp.bsz_R,
                                sp.bsz_P, w.k)
     _check("W_new", to_np(W), want, 4e-3)
+
+
+def test_int8_weight_full_size():
+    """POET-XQ on the 5632 x 2048 layer at 8192 tokens (build, forward,
+    backward) against the full oracle on the dequantised weight."""
+    import dataclasses
+    import torch
+    from gpu_util import make_layer, to_dev, to_np
+    w = workloads.WORKLOADS[3]
+    inp = workloads.layer_inputs(w, 0)
+    L = make_layer(inp, w.k, "bf16", weight="int8")
+    L.build()
+    X, G = to_dev(inp.X, "bf16"), to_dev(inp.G_Y, "bf16")
+    Y = L.forward(X)
+    G_X, gR, gP = L.backward(X, G)
+    torch.cuda.synchronize()
+    q, s = oracle.quantize_rows(inp.W0)
+    ref = oracle.layer_reference(dataclasses.replace(inp, W0=oracle.dequantize_rows(q, s)), w.k)
+    _check("Y", to_np(Y), ref["Y"], TOL_BF16)
+    _check("G_X", to_np(G_X), ref["G_X"], TOL_BF16)
+    _check("g_theta_R", to_np(gR), ref["g_theta_R"], TOL_BF16)
+    _check("g_theta_P", to_np(gP), ref["g_theta_P"], TOL_BF16)

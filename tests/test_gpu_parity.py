@@ -334,3 +334,69 @@ def test_outer_loop_keeps_the_layer(dt):
     assert oracle.rel_fro(to_np(Y1), ref) <= tol
     assert oracle.rel_fro(to_np(Y2), ref) <= tol
     assert oracle.rel_fro(to_np(Y2), to_np(Y1)) <= tol
+
+
+# ---------------------------------------------------------------- INT8 frozen weight
+
+def _int8_inputs(m, n, bR, bP, T, seed):
+    inp = workloads.small_case(m, n, bR, bP, T=T, seed=seed, dtype="bf16", theta_std=0.01)
+    inp.W0[5] = 0.0                       # a zero row: scale 0
+    inp.W0[7, 3] = 40.0                   # a row with one large entry (bf16-exact)
+    return inp
+
+
+def _dequantized(inp):
+    import dataclasses
+    q, s = oracle.quantize_rows(inp.W0)
+    return dataclasses.replace(inp, W0=oracle.dequantize_rows(q, s)), q, s
+
+
+@pytest.mark.parametrize("m, n", [(512, 768), (256, 256), (1024, 512)])
+def test_quantize_weight_bitexact(m, n):
+    import torch
+    inp = _int8_inputs(m, n, (256,) * (m // 256), (256,) * (n // 256), T=1, seed=m + n)
+    log(f"quantize {m}x{n}")
+    L = make_layer(inp, 2, "bf16", weight="int8")
+    q, s = L.int8_weight()
+    torch.cuda.synchronize()
+    q0, s0 = oracle.quantize_rows(inp.W0)
+    assert np.array_equal(q.cpu().numpy(), q0[inp.pi_R][:, inp.pi_P])
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s0[inp.pi_R].view(np.uint32))
+
+
+@pytest.mark.parametrize("case", [
+    dict(m=512, n=256, bR=(256, 256), bP=(256,), T=300, k=4),
+    dict(m=256, n=768, bR=(256,), bP=(512, 256), T=1000, k=3),
+    dict(m=512, n=512, bR=(128, 128, 256), bP=(256, 256), T=77, k=2),
+])
+@pytest.mark.parametrize("save", [True, False])
+def test_layer_int8_weight(case, save):
+    """POET-XQ: forward and backward with the INT8 weight against the oracle on
+    the dequantised weight (saved Wa and recomputed Wa)."""
+    import torch
+    c = case
+    inp = _int8_inputs(c["m"], c["n"], c["bR"], c["bP"], T=c["T"], seed=c["T"])
+    log(f"int8 layer {c} save={save}")
+    L = make_layer(inp, c["k"], "bf16", weight="int8")
+    L.build()
+    X, G = to_dev(inp.X, "bf16"), to_dev(inp.G_Y, "bf16")
+    Y = L.forward(X, save=save)
+    G_X, gR, gP = L.backward(X, G)
+    torch.cuda.synchronize()
+    deq, _, _ = _dequantized(inp)
+    ref = oracle.layer_reference(deq, c["k"])
+    got = dict(Y=to_np(Y), G_X=to_np(G_X), g_theta_R=to_np(gR), g_theta_P=to_np(gP))
+    _compare(got, ref, ["Y", "G_X", "g_theta_R", "g_theta_P"], TOL_BF16, "int8")
+
+
+def test_merge_int8_weight():
+    import torch
+    inp = _int8_inputs(512, 256, (256, 256), (256,), T=1, seed=3)
+    L = make_layer(inp, 4, "bf16", weight="int8")
+    L.build()
+    W = L.merge()
+    torch.cuda.synchronize()
+    deq, _, _ = _dequantized(inp)
+    want = oracle.merge_weight(deq.W0, inp.theta_R, inp.theta_P, inp.pi_R, inp.pi_P, (256, 256),
+                               (256,), 4)
+    assert oracle.rel_fro(to_np(W), want) <= 4e-3
