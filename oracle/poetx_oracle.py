@@ -44,7 +44,7 @@ __all__ = [
     "block_offsets", "apply_blocks_T", "apply_blocks", "permute_weight",
     "forward", "forward_rows", "cnp_backward", "backward", "cnp_coefficients",
     "rel_fro", "layer_reference", "backward_rows", "theta_grad_block", "side_matrix",
-    "merge_weight", "quantize_rows", "dequantize_rows",
+    "merge_weight", "quantize_rows", "dequantize_rows", "exact_cayley", "cayley_backward_exact",
 ]
 
 
@@ -98,13 +98,32 @@ def neumann_cayley(S: np.ndarray, k: int) -> np.ndarray:
     return (I + S) @ N
 
 
-def build_orth(theta: np.ndarray, bsz: Sequence[int], k: int) -> List[np.ndarray]:
-    """Packed parameters of all blocks of one side -> list of orthogonal blocks."""
+def exact_cayley(S: np.ndarray) -> np.ndarray:
+    """The Cayley transform itself, Q = (I+S)(I-S)^{-1}, by a linear solve: the
+    map [PX] §2.D's Neumann series approximates (exact-Cayley mode)."""
+    I = np.eye(S.shape[0])
+    return (I + S) @ np.linalg.solve(I - S, I)
+
+
+def cayley_backward_exact(G: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """Gradient w.r.t. S of <G, Q(S)> for the exact transform. With
+    N = (I-S)^{-1}: dN = N dS N, so dQ = dS N + (I+S) N dS N = (I+Q) dS N and
+    dL/dS = (I+Q)^T G N^T."""
+    I = np.eye(S.shape[0])
+    N = np.linalg.solve(I - S, I)
+    Q = (I + S) @ N
+    return (I + Q).T @ G @ N.T
+
+
+def build_orth(theta: np.ndarray, bsz: Sequence[int], k) -> List[np.ndarray]:
+    """Packed parameters of all blocks of one side -> list of orthogonal blocks
+    (k = None: the exact transform instead of the truncated series)."""
     theta = np.asarray(theta, dtype=np.float64)
     out, off = [], 0
     for b in bsz:
         cnt = b * (b - 1) // 2
-        out.append(neumann_cayley(skew_from_packed(theta[off:off + cnt], b), k))
+        S = skew_from_packed(theta[off:off + cnt], b)
+        out.append(exact_cayley(S) if k is None else neumann_cayley(S, k))
         off += cnt
     assert off == theta.shape[0]
     return out
@@ -185,7 +204,7 @@ def _theta_grad(dQs, theta, bsz, k) -> np.ndarray:
     for b, G in zip(bsz, dQs):
         cnt = b * (b - 1) // 2
         S = skew_from_packed(theta[off:off + cnt], b)
-        Sbar = cnp_backward(G, S, k)
+        Sbar = cayley_backward_exact(G, S) if k is None else cnp_backward(G, S, k)
         out.append(packed_upper(Sbar - Sbar.T))
         off += cnt
     return np.concatenate(out) if out else np.zeros(0)
@@ -215,9 +234,10 @@ def backward(X, Wt, pi_R, pi_P, theta_R, theta_P, QR, QP, Wa, G_Y, bsz_R, bsz_P,
     return G_X, g_R, g_P, dQ_R, dQ_P
 
 
-def layer_reference(inp, k: int, backward_pass: bool = True):
-    """Whole layer on one set of inputs (a workloads.LayerInputs-like object).
-    Returns a dict with Q blocks, Wt, Y, Wa and, if asked, the gradients."""
+def layer_reference(inp, k, backward_pass: bool = True):
+    """Whole layer on one set of inputs (a workloads.LayerInputs-like object;
+    k = None: exact Cayley transform). Returns a dict with Q blocks, Wt, Y, Wa
+    and, if asked, the gradients."""
     sp = inp.spec
     QR = build_orth(inp.theta_R, sp.bsz_R, k)
     QP = build_orth(inp.theta_P, sp.bsz_P, k)
@@ -269,7 +289,7 @@ def theta_grad_block(side, j, X, Wt, pi_R, pi_P, theta_R, theta_P, QR, QP, G_Y, 
         theta, bsz = theta_P, bsz_P
     poff = sum(bb * (bb - 1) // 2 for bb in bsz[:j])
     S = skew_from_packed(np.asarray(theta, dtype=np.float64)[poff:poff + b * (b - 1) // 2], b)
-    Sbar = cnp_backward(dQ, S, k)
+    Sbar = cayley_backward_exact(dQ, S) if k is None else cnp_backward(dQ, S, k)
     return packed_upper(Sbar - Sbar.T)
 
 

@@ -392,3 +392,63 @@ def test_quantize_rows_commutes_with_row_and_column_permutations():
     q, s = oracle.quantize_rows(W)
     q2, s2 = oracle.quantize_rows(W[pr][:, pc])
     assert np.array_equal(q2, q[pr][:, pc]) and np.array_equal(s2, s[pr])
+
+
+# --------------------------------------------------------------------------
+# exact Cayley transform
+
+def test_exact_cayley_two_by_two_closed_form():
+    # S = [[0, a], [-a, 0]]: (I+S)(I-S)^{-1} = [[1-a^2, 2a], [-2a, 1-a^2]] / (1+a^2)
+    for a in (0.1, -0.7, 2.5):
+        S = np.array([[0.0, a], [-a, 0.0]])
+        want = np.array([[1 - a * a, 2 * a], [-2 * a, 1 - a * a]]) / (1 + a * a)
+        assert np.max(np.abs(oracle.exact_cayley(S) - want)) < 1e-15
+
+
+def test_exact_cayley_is_orthogonal_and_the_neumann_limit():
+    b = 48
+    S = _rand_skew(b, 0.25 / np.sqrt(b), seed=5)      # ||S||_2 about 0.5
+    Q = oracle.exact_cayley(S)
+    assert np.max(np.abs(Q.T @ Q - np.eye(b))) < 1e-13
+    assert np.max(np.abs(Q - oracle.neumann_cayley(S, 120))) < 1e-13
+    # also for a generator far outside the Neumann series' radius
+    S2 = _rand_skew(b, 3.0 / np.sqrt(b), seed=6)
+    Q2 = oracle.exact_cayley(S2)
+    assert np.max(np.abs(Q2.T @ Q2 - np.eye(b))) < 1e-12
+    assert np.linalg.det(Q2) > 0
+
+
+def test_exact_cayley_gradient_finite_differences():
+    b = 7
+    S = _rand_skew(b, 0.8 / np.sqrt(b), seed=41)
+    G = np.random.default_rng(2).standard_normal((b, b))
+    got = oracle.cayley_backward_exact(G, S)
+    h = 1e-6
+    for (i, j) in [(0, 1), (2, 5), (6, 3), (4, 4)]:
+        E = np.zeros((b, b))
+        E[i, j] = 1.0
+        fd = (np.sum(G * oracle.exact_cayley(S + h * E)) - np.sum(G * oracle.exact_cayley(S - h * E))) / (2 * h)
+        assert abs(fd - got[i, j]) <= 1e-7 * max(1.0, abs(fd))
+
+
+def test_exact_layer_theta_gradient_finite_differences():
+    inp = workloads.small_case(8, 6, (3, 5), (6,), T=4, seed=13, theta_std=0.3)
+    sp = inp.spec
+    ref = oracle.layer_reference(inp, None)
+    h = 1e-6
+    for side, th in (("R", inp.theta_R), ("P", inp.theta_P)):
+        for idx in (0, len(th) - 1):
+            tp = np.array(th, dtype=np.float64)
+            tm = tp.copy()
+            tp[idx] += h
+            tm[idx] -= h
+            vals = []
+            for t in (tp, tm):
+                import dataclasses
+                mod = dataclasses.replace(inp, theta_R=t if side == "R" else inp.theta_R,
+                                          theta_P=t if side == "P" else inp.theta_P)
+                Y = oracle.layer_reference(mod, None, backward_pass=False)["Y"]
+                vals.append(float(np.sum(Y * inp.G_Y.astype(np.float64))))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            g = ref["g_theta_R" if side == "R" else "g_theta_P"][idx]
+            assert abs(fd - g) <= 1e-6 * max(1.0, abs(fd))
