@@ -37,7 +37,7 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def stage_flops(w, T, xmem=False):
+def stage_flops(w, T, xmem=False, exact=False):
     """Algorithmic flops per stage for one step of the workload (with xmem, the
     backward's recomputation of the P blocks and the Wt product counts too)."""
     f = dict(w0_fwd=0.0, w0_bwd=0.0, block_fwd=0.0, block_bwd=0.0, dq=0.0, build=0.0, cnp_bwd=0.0)
@@ -46,12 +46,12 @@ def stage_flops(w, T, xmem=False):
         cube = sum(b ** 3 for b in sp.bsz_R) + sum(b ** 3 for b in sp.bsz_P)
         f["w0_fwd"] += 2.0 * T * sp.m * sp.n
         f["block_fwd"] += 2.0 * T * sq
-        f["build"] += 2.0 * w.k * cube
+        f["build"] += 2.0 * (11 if exact else w.k) * cube
         if w.backward:
             f["w0_bwd"] += 2.0 * T * sp.m * sp.n
             f["block_bwd"] += 2.0 * T * sq
             f["dq"] += 2.0 * T * sq
-            f["cnp_bwd"] += 4.0 * w.k * cube
+            f["cnp_bwd"] += 2.0 * (13 if exact else 2 * w.k) * cube
             if xmem:
                 f["w0_fwd"] += 2.0 * T * sp.m * sp.n
                 f["block_fwd"] += 2.0 * T * sum(b * b for b in sp.bsz_P)
@@ -159,6 +159,8 @@ def main() -> int:
                     help="first run a plain device copy of MIB MiB three times (for counter runs)")
     ap.add_argument("--merge", action="store_true",
                     help="also time the end-of-inner-loop merge W <- R W0 P of every layer")
+    ap.add_argument("--exact", action="store_true",
+                    help="exact Cayley transform (reference build and gradient) instead of the series")
     ap.add_argument("--xq", action="store_true",
                     help="POET-XQ: frozen weight stored as INT8 (one scale per row)")
     ap.add_argument("--xmem", action="store_true",
@@ -187,7 +189,8 @@ def main() -> int:
         inp = workloads.layer_inputs(w, li, draw_grad=w.backward)
         sp = inp.spec
         L = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, w.k, dtype=w.dtype,
-                       weight="int8" if args.xq else "dense")
+                       weight="int8" if args.xq else "dense",
+                       cayley="exact" if args.exact else "neumann")
         L.set_weight(dev(inp.W0), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
         L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
         b = dict(X=dev(inp.X), Y=torch.empty(T, sp.m, dtype=tdt, device="cuda"),
@@ -242,7 +245,7 @@ def main() -> int:
     log(f"bench: {ms_per_step:.3f} ms/step")
 
     xmem = bool(args.xmem and w.backward)
-    flops = stage_flops(w, T, xmem)
+    flops = stage_flops(w, T, xmem, args.exact)
     merge = None
     if args.merge:
         # outer loop: fold the trained factors of every layer into its weight
@@ -330,6 +333,8 @@ def main() -> int:
             "passes": "build+forward+backward" if w.backward else "build+forward",
             "saved_activation": "none (POET-Xmem: recomputed)" if xmem else "Wa (POET-Xfast)",
             "frozen_weight": "int8, one fp32 scale per row (POET-XQ)" if args.xq else w.dtype,
+            "orthogonal_map": "exact Cayley (doubling build, closed-form gradient)" if args.exact
+            else f"Cayley-Neumann, k = {w.k}",
         },
         "roofline": {
             "kernel": kernel, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,

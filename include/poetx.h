@@ -67,6 +67,16 @@ typedef enum { POETX_FP32 = 0, POETX_BF16 = 1 } poetx_dtype;
  *     Wt[i][j] = s[i] * q[i][j]. Built by poetx_quantize_weight; needs bf16
  *     and m, n multiples of 256, n <= 32768. */
 typedef enum { POETX_WEIGHT_DENSE = 0, POETX_WEIGHT_INT8_ROWS = 1 } poetx_weight;
+
+/* Orthogonal map of each block.
+ *   POETX_CAYLEY_NEUMANN: Q = (I+S) sum_{j<=k} S^j, the truncated series of [PX]
+ *     §2.D, and the gradient of that truncated Q (the default).
+ *   POETX_CAYLEY_EXACT: the Cayley transform itself, Q = (I+S)(I-S)^{-1}, as a
+ *     reference build: (I-S)^{-1} = prod_{i<6} (I + S^(2^i)) (64 terms of the
+ *     series in 11 fp32 products per block, exact to fp32 while ||S||_2 <= 0.75),
+ *     and the exact gradient dL/dS = (I+Q)^T G (I-S)^{-T}. k is ignored. Runs on
+ *     the generic fp32 batched GEMM, block run by block run. */
+typedef enum { POETX_CAYLEY_NEUMANN = 0, POETX_CAYLEY_EXACT = 1 } poetx_cayley;
 typedef enum { POETX_SIDE_R = 0, POETX_SIDE_P = 1 } poetx_side;
 typedef enum {
   POETX_WS_BUILD = 0,       /* poetx_build_orth, one item of poetx_build_orth_batch */
@@ -88,6 +98,7 @@ typedef struct {
                                of X/Y. Skew parameters and their gradients are
                                always fp32; accumulation is always fp32.            */
   int32_t weight;           /* poetx_weight: how Wt is stored                       */
+  int32_t cayley;           /* poetx_cayley: truncated series or exact transform    */
 } poetx_desc;
 
 /* Create a plan. Host only: no device call is made, so it works without a GPU.

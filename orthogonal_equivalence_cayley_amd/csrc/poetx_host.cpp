@@ -21,6 +21,7 @@ using poetx::Seg;
 struct poetx_plan {
   int m = 0, n = 0, k = 0, dtype = 0;
   int weight = POETX_WEIGHT_DENSE;   // poetx_weight: how Wt is stored
+  int cayley = POETX_CAYLEY_NEUMANN; // poetx_cayley: truncated series or exact transform
   std::vector<int> bsz[2];
   std::vector<Seg> segs[2];
   long long nparam[2] = {0, 0};
@@ -222,13 +223,19 @@ size_t layout_merge(const poetx_plan* pl, void* base, MergeWs* w) {
   return c.off;
 }
 
-size_t layout_build(const poetx_plan* pl, void* base, float** S, float** P0, float** P1) {
+size_t layout_build(const poetx_plan* pl, void* base, float** S, float** P0, float** P1,
+                    float** X0 = nullptr, float** X1 = nullptr) {
   Carver c(base);
   const long long ne = std::max(pl->nelem[0], pl->nelem[1]);
   float* s = (float*)c.take(4 * ne);
   float* p0 = (float*)c.take(4 * ne);
   float* p1 = (float*)c.take(4 * ne);
   if (S) { *S = s; *P0 = p0; *P1 = p1; }
+  if (pl->cayley == POETX_CAYLEY_EXACT) {   // running products of the doubling build
+    float* x0 = (float*)c.take(4 * ne);
+    float* x1 = (float*)c.take(4 * ne);
+    if (X0) { *X0 = x0; *X1 = x1; }
+  }
   return c.off;
 }
 
@@ -300,6 +307,51 @@ poetx_status chain_gemm(const Seg& g, const float* X, const float* Y, float* C, 
   p.groups = g.count; p.splits = 1; p.c_ss = 0;
   p.alpha = alpha; p.beta = beta; p.gamma = 0.0f;
   HIP_TRY(poetx::launch_gemm_f32(p, s));
+  return POETX_OK;
+}
+
+// fp32 batched b x b product over a run of blocks with explicit strides:
+// C(m, n) = sum_k A[m * a_rs + k * a_cs] B[n * b_rs + k * b_cs] + beta * Cin(m, n).
+poetx_status run_gemm_f32(const Seg& g, const float* A, long long a_rs, long long a_cs, const float* B,
+                          long long b_rs, long long b_cs, float* C, const float* Cin, float beta,
+                          hipStream_t s) {
+  poetx::GemmF32 p{};
+  p.A = A + g.q_off; p.B = B + g.q_off; p.C = C + g.q_off;
+  p.Cin = Cin ? Cin + g.q_off : nullptr;
+  p.M = p.N = p.K = g.b;
+  p.a_rs = a_rs; p.a_cs = a_cs; p.b_rs = b_rs; p.b_cs = b_cs; p.c_rs = g.b;
+  p.a_gs = p.b_gs = p.c_gs = (long long)g.b * g.b;
+  p.groups = g.count; p.splits = 1;
+  p.alpha = 1.0f; p.beta = beta;
+  HIP_TRY(poetx::launch_gemm_f32(p, s));
+  return POETX_OK;
+}
+
+// Exact Cayley transform of every block of one run, without a solve:
+// (I - S)^{-1} = prod_{i < F} (I + S^(2^i)) up to S^(2^F) (F = 6: 64 terms of the
+// series, 11 products instead of 63), then Q = (I + S) N. Exact to fp32 while
+// ||S||_2 <= 0.75. N is left in *N_out (one of X0 / X1).
+constexpr int kExactFactors = 6;
+poetx_status exact_cayley_run(const Seg& g, const float* theta, float* S, float* P0, float* P1,
+                              float* X0, float* X1, float* Q, float** N_out, hipStream_t s) {
+  HIP_TRY(poetx::launch_unpack_skew(theta, g, S, X0, 1.0f, s));   // X = I + S
+  const long long b = g.b;
+  const float* P = S;
+  float* pw[2] = {P0, P1};
+  float *X = X0, *Xn = X1;
+  poetx_status st;
+  for (int i = 1; i < kExactFactors; ++i) {
+    float* Pn = pw[i & 1];
+    // S^(2^i) = (S^(2^(i-1)))^2
+    if ((st = run_gemm_f32(g, P, b, 1, P, 1, b, Pn, nullptr, 0.0f, s)) != POETX_OK) return st;
+    // X (I + S^(2^i)) = X + X S^(2^i)
+    if ((st = run_gemm_f32(g, X, b, 1, Pn, 1, b, Xn, X, 1.0f, s)) != POETX_OK) return st;
+    P = Pn;
+    std::swap(X, Xn);
+  }
+  // Q = (I + S) N = N + S N
+  if ((st = run_gemm_f32(g, S, b, 1, X, 1, b, Q, X, 1.0f, s)) != POETX_OK) return st;
+  *N_out = X;
   return POETX_OK;
 }
 
@@ -376,6 +428,7 @@ poetx_status grad_items(const GradItem* items, int count, hipStream_t s) {
   for (int i = 0; i < count; ++i) {
     const GradItem& it = items[i];
     const poetx_plan* pl = it.pl;
+    if (pl->cayley == POETX_CAYLEY_EXACT) continue;   // below
     if (kk != -1 && kk != pl->k && (st = flush()) != POETX_OK) return st;
     kk = pl->k;
     ab.k = tb.k = kk;
@@ -400,6 +453,23 @@ poetx_status grad_items(const GradItem* items, int count, hipStream_t s) {
     const GradItem& it = items[i];
     const poetx_plan* pl = it.pl;
     const int side = it.side, k = pl->k;
+    if (pl->cayley == POETX_CAYLEY_EXACT) {
+      // exact transform: rebuild N = (I - S)^{-1} and Q, then
+      // dL/dS = (I + Q)^T G N^T and g(i, j) = dS[i][j] - dS[j][i]
+      const ChainWs& w = it.w;
+      for (const Seg& g : pl->segs[side]) {
+        const long long b = g.b;
+        float* N;
+        if ((st = exact_cayley_run(g, it.theta, w.S, w.A0, w.A1, w.T0, w.T1, w.T, &N, s)) != POETX_OK)
+          return st;
+        // A = Q^T G + G   (A(m, k) = Q[k][m])
+        if ((st = run_gemm_f32(g, w.T, 1, b, it.dQ, 1, b, w.A, it.dQ, 1.0f, s)) != POETX_OK) return st;
+        // D = A N^T       (B(n, k) = N[n][k]); into the Q buffer, free now
+        if ((st = run_gemm_f32(g, w.A, b, 1, N, b, 1, w.T, nullptr, 0.0f, s)) != POETX_OK) return st;
+        HIP_TRY(poetx::launch_pack_antisym(w.T, g, 1.0f, it.g, s));
+      }
+      continue;
+    }
     bool any = false;
     for (const Seg& g : pl->segs[side]) any |= !poetx::chain_supported(g.b);
     if (!any) continue;
@@ -559,6 +629,20 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
   for (int i = 0; i < count; ++i) {
     const BuildItem& it = items[i];
     const poetx_plan* pl = it.pl;
+    if (pl->cayley == POETX_CAYLEY_EXACT) {
+      float *S, *P0, *P1, *X0, *X1, *N;
+      layout_build(pl, it.ws, &S, &P0, &P1, &X0, &X1);
+      const bool bf16 = pl->dtype == POETX_BF16;
+      const int es = elsize(pl);
+      for (const Seg& g : pl->segs[it.side]) {
+        poetx_status st = exact_cayley_run(g, it.theta, S, P0, P1, X0, X1, it.Q, &N, s);
+        if (st != POETX_OK) return st;
+        if (it.Qact)
+          HIP_TRY(poetx::launch_cast(it.Q + g.q_off, static_cast<char*>(it.Qact) + es * g.q_off,
+                                     (long long)g.b * g.b * g.count, bf16, s));
+      }
+      continue;
+    }
     if (kk != -1 && kk != pl->k) {   // one Neumann order per chain launch
       poetx_status st = flush();
       if (st != POETX_OK) return st;
@@ -634,6 +718,8 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
   if (d->k < 0 || d->k > 32) return POETX_ERR_SHAPE;
   if (d->weight != POETX_WEIGHT_DENSE && d->weight != POETX_WEIGHT_INT8_ROWS)
     return POETX_ERR_INVALID_ARG;
+  if (d->cayley != POETX_CAYLEY_NEUMANN && d->cayley != POETX_CAYLEY_EXACT)
+    return POETX_ERR_INVALID_ARG;
   const int32_t* bs[2] = {d->bsz_R, d->bsz_P};
   const int nb[2] = {d->nb_R, d->nb_P};
   const int dims[2] = {d->m, d->n};
@@ -660,6 +746,7 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
   if (!pl) return POETX_ERR_INVALID_ARG;
   pl->m = d->m; pl->n = d->n; pl->k = d->k; pl->dtype = d->dtype;
   pl->weight = d->weight;
+  pl->cayley = d->cayley;
   for (int side = 0; side < 2; ++side) {
     pl->dim[side] = dims[side];
     long long q = 0, p = 0;

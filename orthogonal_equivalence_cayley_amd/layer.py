@@ -43,17 +43,21 @@ def param_grad_many(layers, g_thetas=None):
 
 class PoetxLayer:
     def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
-                 dtype: str = "bf16", device: str = "cuda", weight: str = "dense"):
+                 dtype: str = "bf16", device: str = "cuda", weight: str = "dense",
+                 cayley: str = "neumann"):
         if dtype not in _TORCH_DTYPE:
             raise ValueError(f"dtype must be one of {sorted(_TORCH_DTYPE)}")
         if weight not in ("dense", "int8"):
             raise ValueError("weight must be 'dense' or 'int8' (POET-XQ)")
+        if cayley not in ("neumann", "exact"):
+            raise ValueError("cayley must be 'neumann' (truncated series) or 'exact'")
         self.m, self.n, self.k, self.dtype = m, n, k, dtype
         self.weight = weight
         self.device = torch.device(device)
         self.tdtype = _TORCH_DTYPE[dtype]
         self.plan = _px.Plan(m, n, bsz_R, bsz_P, k, _PX_DTYPE[dtype],
-                             _px.WEIGHT_INT8_ROWS if weight == "int8" else _px.WEIGHT_DENSE)
+                             _px.WEIGHT_INT8_ROWS if weight == "int8" else _px.WEIGHT_DENSE,
+                             _px.CAYLEY_EXACT if cayley == "exact" else _px.CAYLEY_NEUMANN)
         self.nparam = (self.plan.param_count(_px.SIDE_R), self.plan.param_count(_px.SIDE_P))
         self.nelem = (self.plan.block_elems(_px.SIDE_R), self.plan.block_elems(_px.SIDE_P))
         self._ws = {}

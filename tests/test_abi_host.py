@@ -187,3 +187,14 @@ def test_int8_weight_plans():
         px.POETX_ERR_INVALID_ARG
     assert px.LIB.poetx_quantize_weight(p.handle, A, A + 16, A + 36, A + 48, None) == \
         px.POETX_ERR_ALIGNMENT
+
+
+def test_cayley_mode_validation():
+    px.Plan(64, 48, (32, 32), (16, 32), 3, px.POETX_FP32, px.WEIGHT_DENSE, px.CAYLEY_EXACT)
+    with pytest.raises(px.PoetxError) as e:
+        px.Plan(64, 48, (32, 32), (16, 32), 3, px.POETX_FP32, px.WEIGHT_DENSE, 9)
+    assert e.value.status == px.POETX_ERR_INVALID_ARG
+    ex = px.Plan(64, 48, (32, 32), (16, 32), 3, px.POETX_FP32, px.WEIGHT_DENSE, px.CAYLEY_EXACT)
+    nm = px.Plan(64, 48, (32, 32), (16, 32), 3, px.POETX_FP32)
+    # the doubling build keeps two more block arrays
+    assert ex.workspace_size(0, px.WS_BUILD) > nm.workspace_size(0, px.WS_BUILD)

@@ -400,3 +400,29 @@ def test_merge_int8_weight():
     want = oracle.merge_weight(deq.W0, inp.theta_R, inp.theta_P, inp.pi_R, inp.pi_P, (256, 256),
                                (256,), 4)
     assert oracle.rel_fro(to_np(W), want) <= 4e-3
+
+
+# ---------------------------------------------------------------- exact Cayley transform
+
+@pytest.mark.parametrize("dt, c", [
+    ("f32", dict(m=96, n=130, bR=(32, 64), bP=(65, 65), T=130, std=0.03)),
+    ("f32", dict(m=70, n=45, bR=(30, 40), bP=(45,), T=9, std=0.05)),
+    ("bf16", dict(m=512, n=256, bR=(256, 256), bP=(128, 128), T=300, std=0.01)),
+])
+def test_exact_cayley_layer(dt, c):
+    """Exact-Cayley mode: blocks, forward and backward against the oracle's
+    solve-based transform and its closed-form gradient."""
+    import torch
+    from orthogonal_equivalence_cayley_amd import PoetxLayer
+    inp = workloads.small_case(c["m"], c["n"], c["bR"], c["bP"], T=c["T"], seed=c["T"] + 1, dtype=dt,
+                               theta_std=c["std"])
+    log(f"exact cayley {dt} {c}")
+    sp = inp.spec
+    L = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, 4, dtype=dt, cayley="exact")
+    L.set_weight(to_dev(inp.W0, dt), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
+    L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
+    got, _ = run_layer(inp, 4, dt, layer=L)
+    ref = oracle.layer_reference(inp, None)
+    _compare(got, ref, ["QR", "QP"], TOL_F32, "exact")
+    keys = ["Wa", "Y", "G_X", "g_theta_R", "g_theta_P"]
+    _compare(got, ref, keys, TOL_F32 if dt == "f32" else TOL_BF16, "exact")
