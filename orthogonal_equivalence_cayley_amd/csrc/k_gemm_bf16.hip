@@ -260,7 +260,8 @@ hipError_t dispatch(const GemmBf16& p, hipStream_t s) {
 hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || p.groups <= 0) return hipSuccess;
   const long long big_tiles = (long long)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.groups * p.splits;
-  const bool big = big_tiles >= 256;
+  // the token reduction (dQ) keeps 128 x 128 tiles: its split count is sized for them
+  const bool big = big_tiles >= 256 && p.role != GEMM_DQ;
   // whole-tile shapes take the pipelined direct-to-LDS kernels; the rest (K not a
   // multiple of 64, partial tiles of row-contiguous operands) the kernels here
   if (gemm_lds_supported(p, big ? 256 : 128, big ? 256 : 128)) return launch_gemm_lds(p, big, s);

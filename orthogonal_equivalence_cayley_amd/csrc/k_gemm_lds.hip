@@ -279,7 +279,16 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   // of that sequence with one uninterrupted load pipeline.
   const int tn = (p.N + BN - 1) / BN, tm = (p.M + BM - 1) / BM, ntile = tn * tm;
   const int nwg = gridDim.x;
-  const int wlin = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+  int bx = blockIdx.x, bz = blockIdx.z;
+  if (p.xcd_cluster) {
+    // dispatch order w (x fastest) goes to XCD w % 8; give the gridDim.x tiles of
+    // one (group, split) the same w % 8: w -> tile (w / 8) % X, slot w % 8 + 8 (w / 8X)
+    const int X = gridDim.x;
+    const int w = blockIdx.x + X * blockIdx.z;
+    bx = (w / 8) % X;
+    bz = (w % 8) + 8 * (w / (8 * X));
+  }
+  const int wlin = (!p.xcd_cluster && nwg % 8 == 0) ? (bx % 8) * (nwg / 8) + bx / 8 : bx;
   const int tpw = p.tpw;
   const int t_first = wlin * tpw;
   const int t_count = max(0, min(tpw, ntile - t_first));
@@ -292,7 +301,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
     n0 = (in / gsz) * BN;
   };
 
-  const int g = blockIdx.z / p.splits, sp = blockIdx.z - g * p.splits;
+  const int g = bz / p.splits, sp = bz - g * p.splits;
   const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + g * p.a_gs;
   using BElem = std::conditional_t<BQ, int8_t, uint16_t>;
   const BElem* B = reinterpret_cast<const BElem*>(p.B) + g * p.b_gs;
@@ -527,12 +536,16 @@ hipError_t dispatch_lds(const GemmBf16& p, hipStream_t s) {
   const size_t lds = ST * (size_t)(BM + BN) * KB * 2;
   const int a = p.a_kmajor, b = p.b_kmajor, f = p.out_f32;
   if (p.b_i8) {
-    if (p.role == GEMM_W0 && a && b && !f)
-      hipLaunchKernelGGL((w0q_gemm_nt_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
-    else if (p.role == GEMM_W0 && a && !b && !f)
-      hipLaunchKernelGGL((w0q_gemm_nn_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
-    else
+    if constexpr (ST != 2) {   // the int8 path is two-stage
       return hipErrorInvalidValue;
+    } else {
+      if (p.role == GEMM_W0 && a && b && !f)
+        hipLaunchKernelGGL((w0q_gemm_nt_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
+      else if (p.role == GEMM_W0 && a && !b && !f)
+        hipLaunchKernelGGL((w0q_gemm_nn_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
+      else
+        return hipErrorInvalidValue;
+    }
   } else if (p.role == GEMM_W0 && a && b && !f)
     hipLaunchKernelGGL((w0_gemm_nt_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
   else if (p.role == GEMM_W0 && a && !b && !f)
@@ -574,6 +587,8 @@ hipError_t launch_gemm_lds(const GemmBf16& p_in, int big, hipStream_t s) {
   tpw = tpw < 1 ? 1 : (tpw > 16 ? 16 : tpw);
   if (tpw > ntile) tpw = ntile;
   p.tpw = (int)tpw;
+  p.xcd_cluster = (tpw == 1 && ntile <= 16 && (p.groups * p.splits) % 8 == 0 &&
+                   p.role == GEMM_DQ) ? 1 : 0;
   if (big) return dispatch_lds<256, 256, 128, 64, 64, 2>(p, s);
   return dispatch_lds<128, 128, 64, 64, 64, 2>(p, s);
 }

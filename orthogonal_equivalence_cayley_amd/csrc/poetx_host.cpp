@@ -117,18 +117,22 @@ struct Carver {
 // dQ products reduce over tokens; split the token range so that the grid fills
 // the chip. Partial sums are reduced afterwards in a fixed order.
 int dq_splits(const poetx_plan* pl, int side, long long T) {
-  long long tiles = 0;
-  // bf16: one 256 x 256 tile per 256-wide block (each operand read once per
-  // split); fp32: 64 x 64 tiles of the generic kernel
-  const int tile = pl->dtype == POETX_BF16 ? 256 : 64;
+  long long tiles = 0, blocks = 0;
+  // bf16: 128 x 128 tiles (two workgroups per CU); fp32: 64 x 64 tiles of the
+  // generic kernel
+  const int tile = pl->dtype == POETX_BF16 ? 128 : 64;
   for (const Seg& g : pl->segs[side]) {
     const long long t = (g.b + tile - 1) / tile;
     tiles += t * t * g.count;
+    blocks += g.count;
   }
-  // bf16: at most one workgroup per CU (a second round of a few workgroups
-  // would double the time); fp32: about two per CU
-  long long s = pl->dtype == POETX_BF16 ? 256 / std::max<long long>(tiles, 1)
-                                        : (512 + tiles - 1) / std::max<long long>(tiles, 1);
+  long long s = (512 + tiles - 1) / std::max<long long>(tiles, 1);
+  if (pl->dtype == POETX_BF16) {
+    s = std::max<long long>(1, 512 / std::max<long long>(tiles, 1));   // one round of workgroups
+    // a multiple of 8 (blocks x splits) lets the tiles of one split share an XCD
+    while (s > 1 && (blocks * s) % 8) --s;
+    if ((blocks * s) % 8) s = std::max<long long>(1, 512 / std::max<long long>(tiles, 1));
+  }
   const long long maxs = std::max<long long>(1, (T + 255) / 256);
   s = std::min(s, maxs);
   s = std::max<long long>(1, std::min<long long>(s, 64));

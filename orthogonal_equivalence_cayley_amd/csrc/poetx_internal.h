@@ -94,6 +94,9 @@ struct GemmBf16 {
   // bf16 output only: column n of group g is multiplied by col_scale[g * c_gs + n]
   // (fp32, before the rounding) when non-null
   const float* col_scale = nullptr;
+  // the tiles of one (group, split) run on one XCD (they share A and B rows in
+  // its L2): set by the launcher when tpw == 1 and groups * splits % 8 == 0
+  int xcd_cluster = 0;
 };
 hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
 // Pipelined variant (direct-to-LDS loads, see k_gemm_lds.hip) for whole-tile shapes:
