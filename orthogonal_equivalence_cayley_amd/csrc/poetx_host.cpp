@@ -139,11 +139,20 @@ int dq_splits(const poetx_plan* pl, int side, long long T) {
   return (int)s;
 }
 
-struct FwdWs { void *U, *V, *Wa, *Z; };
+struct FwdWs { void *U, *V, *Wa, *Z, *Wf; };
 struct BwdWs {
-  void *GZ, *GWa, *GV, *U, *GU;
+  void *GZ, *GWa, *GV, *U, *GU, *Wf;
   float *dQ[2], *part;
 };
+
+// Folding one side's blocks into the frozen weight instead of applying them to
+// the activations: Wa = (U D_P^T) Wt^T = U (Wt D_P)^T in the forward and
+// G_V = (G_Z D_R) Wt = G_Z (D_R Wt) in the backward, whose G_Wa nothing else
+// reads. The weight-side product costs 2 m n b flops against 2 T n b (2 T m b)
+// on the activations plus a T x n (T x m) round trip through HBM, so it is taken
+// when T >= m (T >= n). INT8 weights keep the activation-side products.
+bool fold_fwd(const poetx_plan* pl, long long T) { return !wq(pl) && T > 0 && T >= pl->m; }
+bool fold_bwd(const poetx_plan* pl, long long T) { return !wq(pl) && T > 0 && T >= pl->n; }
 
 // Buffers of the chain rule through the parameterisation, for one side.
 struct ChainWs {
@@ -170,10 +179,12 @@ size_t layout_fwd(const poetx_plan* pl, long long T, void* base, FwdWs* w) {
   Carver c(base);
   const size_t es = elsize(pl);
   FwdWs x;
+  const bool fold = fold_fwd(pl, T);
   x.U = c.take(es * T * pl->n);
-  x.V = c.take(es * T * pl->n);
+  x.V = fold ? nullptr : c.take(es * T * pl->n);
   x.Wa = c.take(es * T * pl->m);
   x.Z = c.take(es * T * pl->m);
+  x.Wf = fold ? c.take(es * (size_t)pl->m * pl->n) : nullptr;
   if (w) *w = x;
   return c.off;
 }
@@ -188,6 +199,7 @@ size_t layout_bwd(const poetx_plan* pl, long long T, void* base, BwdWs* w, Chain
   x.GV = c.take(es * T * pl->n);
   x.U = c.take(es * T * pl->n);
   x.GU = c.take(es * T * pl->n);
+  x.Wf = (fold_fwd(pl, T) || fold_bwd(pl, T)) ? c.take(es * (size_t)pl->m * pl->n) : nullptr;
   x.dQ[0] = (float*)c.take(4 * pl->nelem[0]);
   x.dQ[1] = (float*)c.take(4 * pl->nelem[1]);
   long long part = 0;
@@ -380,6 +392,29 @@ poetx_status apply_blocks(const poetx_plan* pl, int side, long long T, const voi
   return POETX_OK;
 }
 
+// Wf = Wt D_P: every row of Wt times the P blocks, out[:, blk] = Wt[:, blk] Q.
+poetx_status fold_p(const poetx_plan* pl, const void* Wt, const void* Q_P, void* Wf, hipStream_t s) {
+  return apply_blocks(pl, POETX_SIDE_P, pl->m, Wt, Q_P, Wf, false, s);
+}
+
+// Wf = D_R Wt: the rows of each R block of Wt multiplied from the left by its Q,
+// Wf[blk] = Q Wt[blk] (b x b times b x n per block).
+poetx_status fold_r(const poetx_plan* pl, const void* Wt, const void* Q_R, void* Wf, hipStream_t s) {
+  const size_t es = elsize(pl);
+  const long long n = pl->n;
+  for (const Seg& g : pl->segs[POETX_SIDE_R]) {
+    const char* q = static_cast<const char*>(Q_R) + es * g.q_off;
+    const char* w = static_cast<const char*>(Wt) + es * g.dim_off * n;
+    char* c = static_cast<char*>(Wf) + es * g.dim_off * n;
+    // A(m, k) = Q[m][k]; B(j, k) = Wt[off + k][j]
+    poetx_status st = gemm(pl, poetx::GEMM_BLOCK, Op{q, g.b, 1}, Op{w, 1, n}, c, n, g.b, (int)n, g.b,
+                           g.count, (long long)g.b * g.b, (long long)g.b * n, (long long)g.b * n, 1, 0,
+                           false, s);
+    if (st != POETX_OK) return st;
+  }
+  return POETX_OK;
+}
+
 // dQ[blk] = G[:, blk]^T A[:, blk] (reduction over tokens), fp32.
 poetx_status block_grads(const poetx_plan* pl, int side, long long T, const void* G, const void* A,
                          float* part, float* dQ, hipStream_t s) {
@@ -529,15 +564,19 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
       StageScope sc(POETX_STAGE_GATHER, s);
       HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
     }
+    const bool fold = fold_fwd(pl, T);
     {
       StageScope sc(POETX_STAGE_BLOCK_FWD, s);
-      if ((st = apply_blocks(pl, POETX_SIDE_P, T, w.U, Q_P, w.GU, true, s)) != POETX_OK) return st;
+      st = fold ? fold_p(pl, Wt, Q_P, w.Wf, s)
+                : apply_blocks(pl, POETX_SIDE_P, T, w.U, Q_P, w.GU, true, s);
+      if (st != POETX_OK) return st;
     }
     {
       StageScope sc(POETX_STAGE_W0_FWD, s);
-      if ((st = gemm(pl, poetx::GEMM_W0, Op{w.GU, pl->n, 1}, Op{Wt, pl->n, 1}, w.GWa, pl->m, (int)T,
-                     pl->m, pl->n, 1, 0, 0, 0, 1, 0, false, s, wq(pl) ? qscale(pl, Wt) : nullptr,
-                     wq(pl))) != POETX_OK)
+      const Op a = fold ? Op{w.U, pl->n, 1} : Op{w.GU, pl->n, 1};
+      const Op b = fold ? Op{w.Wf, pl->n, 1} : Op{Wt, pl->n, 1};
+      if ((st = gemm(pl, poetx::GEMM_W0, a, b, w.GWa, pl->m, (int)T, pl->m, pl->n, 1, 0, 0, 0, 1, 0,
+                     false, s, wq(pl) ? qscale(pl, Wt) : nullptr, wq(pl))) != POETX_OK)
         return st;
     }
     Wa = w.GWa;
@@ -552,19 +591,23 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
     if ((st = block_grads(pl, POETX_SIDE_R, T, w.GZ, Wa, w.part, dQ[0], s)) != POETX_OK)
       return st;
   }
+  const bool foldb = fold_bwd(pl, T);
   {
     StageScope sc(POETX_STAGE_BLOCK_BWD, s);
-    // INT8 weight: G_Wa leaves scaled by the row scales of Wt, since
-    // G_Wa Wt = (G_Wa diag(s)) q
-    if ((st = apply_blocks(pl, POETX_SIDE_R, T, w.GZ, Q_R, w.GWa, false, s,
-                           wq(pl) ? qscale(pl, Wt) : nullptr)) != POETX_OK)
-      return st;
+    // folded: Wf = D_R Wt replaces G_Wa = G_Z D_R. INT8 weight: G_Wa leaves
+    // scaled by the row scales of Wt, since G_Wa Wt = (G_Wa diag(s)) q
+    st = foldb ? fold_r(pl, Wt, Q_R, w.Wf, s)
+               : apply_blocks(pl, POETX_SIDE_R, T, w.GZ, Q_R, w.GWa, false, s,
+                              wq(pl) ? qscale(pl, Wt) : nullptr);
+    if (st != POETX_OK) return st;
   }
-  // frozen weight: G_V = G_Wa Wt
+  // frozen weight: G_V = G_Wa Wt (folded: G_V = G_Z (D_R Wt))
   {
     StageScope sc(POETX_STAGE_W0_BWD, s);
-    if ((st = gemm(pl, poetx::GEMM_W0, Op{w.GWa, pl->m, 1}, Op{Wt, 1, pl->n}, w.GV, pl->n, (int)T,
-                   pl->n, pl->m, 1, 0, 0, 0, 1, 0, false, s, nullptr, wq(pl))) != POETX_OK)
+    const Op a = foldb ? Op{w.GZ, pl->m, 1} : Op{w.GWa, pl->m, 1};
+    const Op b = foldb ? Op{w.Wf, 1, pl->n} : Op{Wt, 1, pl->n};
+    if ((st = gemm(pl, poetx::GEMM_W0, a, b, w.GV, pl->n, (int)T, pl->n, pl->m, 1, 0, 0, 0, 1, 0, false,
+                   s, nullptr, wq(pl))) != POETX_OK)
       return st;
   }
   // P side: U = X Pi_P^T; dQ_P = G_V^T U per block; G_U = G_V D_P; G_X = G_U Pi_P
@@ -940,17 +983,21 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
     StageScope sc(POETX_STAGE_GATHER, s);
     HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
   }
-  // 2. blocks of P: V = U D_P^T
+  // 2. blocks of P: V = U D_P^T, or folded into the weight, Wf = Wt D_P
+  const bool fold = fold_fwd(pl, T);
   {
     StageScope sc(POETX_STAGE_BLOCK_FWD, s);
-    if ((st = apply_blocks(pl, POETX_SIDE_P, T, w.U, Q_P, w.V, true, s)) != POETX_OK) return st;
+    st = fold ? fold_p(pl, Wt, Q_P, w.Wf, s)
+              : apply_blocks(pl, POETX_SIDE_P, T, w.U, Q_P, w.V, true, s);
+    if (st != POETX_OK) return st;
   }
-  // 3. frozen weight: Wa = V Wt^T
+  // 3. frozen weight: Wa = V Wt^T (folded: Wa = U Wf^T)
   {
     StageScope sc(POETX_STAGE_W0_FWD, s);
-    if ((st = gemm(pl, poetx::GEMM_W0, Op{w.V, pl->n, 1}, Op{Wt, pl->n, 1}, Wa, pl->m, (int)T, pl->m,
-                   pl->n, 1, 0, 0, 0, 1, 0, false, s, wq(pl) ? qscale(pl, Wt) : nullptr,
-                   wq(pl))) != POETX_OK)
+    const Op a = fold ? Op{w.U, pl->n, 1} : Op{w.V, pl->n, 1};
+    const Op b = fold ? Op{w.Wf, pl->n, 1} : Op{Wt, pl->n, 1};
+    if ((st = gemm(pl, poetx::GEMM_W0, a, b, Wa, pl->m, (int)T, pl->m, pl->n, 1, 0, 0, 0, 1, 0, false,
+                   s, wq(pl) ? qscale(pl, Wt) : nullptr, wq(pl))) != POETX_OK)
       return st;
   }
   // 4. blocks of R: Z = Wa D_R^T

@@ -426,3 +426,34 @@ def test_exact_cayley_layer(dt, c):
     _compare(got, ref, ["QR", "QP"], TOL_F32, "exact")
     keys = ["Wa", "Y", "G_X", "g_theta_R", "g_theta_P"]
     _compare(got, ref, keys, TOL_F32 if dt == "f32" else TOL_BF16, "exact")
+
+
+# ---------------------------------------------------------------- blocks folded into the weight
+
+@pytest.mark.parametrize("dt, c", [
+    ("bf16", dict(m=256, n=512, bR=(256,), bP=(256, 128, 128), T=600, k=4)),   # T >= m, n: both folds
+    ("bf16", dict(m=512, n=256, bR=(256, 256), bP=(256,), T=384, k=3)),        # T < m: backward fold only
+    ("f32", dict(m=64, n=45, bR=(30, 34), bP=(45,), T=100, k=2)),              # generic fp32 products
+])
+@pytest.mark.parametrize("save", [True, False])
+def test_layer_with_folded_blocks(dt, c, save):
+    """With T >= m (T >= n) the P (R) blocks are folded into the frozen weight
+    instead of being applied to T rows; results against the oracle."""
+    import torch
+    inp = workloads.small_case(c["m"], c["n"], c["bR"], c["bP"], T=c["T"], seed=c["T"] + c["m"], dtype=dt,
+                               theta_std=0.01 if dt == "bf16" else 0.05)
+    log(f"folded {dt} {c} save={save}")
+    L = make_layer(inp, c["k"], dt)
+    L.build()
+    X, G = to_dev(inp.X, dt), to_dev(inp.G_Y, dt)
+    Y = L.forward(X, save=save)
+    Wa = L.Wa
+    G_X, gR, gP = L.backward(X, G)
+    torch.cuda.synchronize()
+    ref = oracle.layer_reference(inp, c["k"])
+    got = dict(Y=to_np(Y), G_X=to_np(G_X), g_theta_R=to_np(gR), g_theta_P=to_np(gP))
+    keys = ["Y", "G_X", "g_theta_R", "g_theta_P"]
+    if save:
+        got["Wa"] = to_np(Wa)
+        keys.append("Wa")
+    _compare(got, ref, keys, TOL_F32 if dt == "f32" else TOL_BF16, "folded")
