@@ -983,6 +983,25 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
     StageScope sc(POETX_STAGE_GATHER, s);
     HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
   }
+  // Without a saved Wa (POET-Xmem) both sides fold when T >= m and T >= n:
+  // Y = (U (D_R Wt D_P)^T) Pi_R, one product with the doubly folded weight
+  // (built in the free Wa buffer, T x m >= m x n).
+  if (!Wa_saved && fold_fwd(pl, T) && fold_bwd(pl, T)) {
+    {
+      StageScope sc(POETX_STAGE_BLOCK_FWD, s);
+      if ((st = fold_p(pl, Wt, Q_P, w.Wf, s)) != POETX_OK) return st;
+      if ((st = fold_r(pl, w.Wf, Q_R, w.Wa, s)) != POETX_OK) return st;
+    }
+    {
+      StageScope sc(POETX_STAGE_W0_FWD, s);
+      if ((st = gemm(pl, poetx::GEMM_W0, Op{w.U, pl->n, 1}, Op{w.Wa, pl->n, 1}, w.Z, pl->m, (int)T,
+                     pl->m, pl->n, 1, 0, 0, 0, 1, 0, false, s)) != POETX_OK)
+        return st;
+    }
+    StageScope sc(POETX_STAGE_SCATTER, s);
+    HIP_TRY(poetx::launch_scatter_cols(w.Z, pi_R, Y, T, pl->m, es, s));
+    return POETX_OK;
+  }
   // 2. blocks of P: V = U D_P^T, or folded into the weight, Wf = Wt D_P
   const bool fold = fold_fwd(pl, T);
   {
