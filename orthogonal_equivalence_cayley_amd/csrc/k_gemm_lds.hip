@@ -525,6 +525,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void w0q_gemm_nn_lds(GemmBf16 p) {
 POETX_LDS_KERNEL(block_gemm_nt_lds, true, true, false)
 POETX_LDS_KERNEL(block_gemm_nn_lds, true, false, false)
 POETX_LDS_KERNEL(dq_gemm_tn_lds, false, false, true)
+POETX_LDS_KERNEL(block_gemm_tn_lds, false, true, false)
 #undef POETX_LDS_KERNEL
 
 template <int BM, int BN, int WM, int WN, int KB, int ST>
@@ -554,6 +555,8 @@ hipError_t dispatch_lds(const GemmBf16& p, hipStream_t s) {
     hipLaunchKernelGGL((block_gemm_nt_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
   else if (p.role == GEMM_BLOCK && a && !b && !f)
     hipLaunchKernelGGL((block_gemm_nn_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
+  else if (p.role == GEMM_BLOCK && !a && b && !f)
+    hipLaunchKernelGGL((block_gemm_tn_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
   else if (p.role == GEMM_DQ && !a && !b && f)
     hipLaunchKernelGGL((dq_gemm_tn_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
   else

@@ -415,6 +415,32 @@ poetx_status fold_r(const poetx_plan* pl, const void* Wt, const void* Q_R, void*
   return POETX_OK;
 }
 
+// Transposed form of fold_r, WfT = (D_R Wt)^T [n, m]: the backward product then
+// reads it K-contiguous (the faster NT form). Per block: WfT[:, blk] =
+// Wt[blk]^T Q^T. bf16 plans need whole 256-row tiles of n and b % 64 == 0 (the
+// pipelined kernel is the only one with this operand layout).
+bool fold_rt_ok(const poetx_plan* pl) {
+  if (pl->dtype != POETX_BF16) return true;
+  if (pl->n % 256) return false;
+  for (const Seg& g : pl->segs[POETX_SIDE_R])
+    if (g.b % 64) return false;
+  return true;
+}
+poetx_status fold_rt(const poetx_plan* pl, const void* Wt, const void* Q_R, void* WfT, hipStream_t s) {
+  const size_t es = elsize(pl);
+  const long long n = pl->n, m = pl->m;
+  for (const Seg& g : pl->segs[POETX_SIDE_R]) {
+    const char* q = static_cast<const char*>(Q_R) + es * g.q_off;
+    const char* w = static_cast<const char*>(Wt) + es * g.dim_off * n;
+    char* c = static_cast<char*>(WfT) + es * g.dim_off;
+    // A(j, k) = Wt[off + k][j]; B(i, k) = Q[i][k]; C(j, i) at WfT[j][off + i]
+    poetx_status st = gemm(pl, poetx::GEMM_BLOCK, Op{w, 1, n}, Op{q, g.b, 1}, c, m, (int)n, g.b, g.b,
+                           g.count, (long long)g.b * n, (long long)g.b * g.b, g.b, 1, 0, false, s);
+    if (st != POETX_OK) return st;
+  }
+  return POETX_OK;
+}
+
 // dQ[blk] = G[:, blk]^T A[:, blk] (reduction over tokens), fp32.
 poetx_status block_grads(const poetx_plan* pl, int side, long long T, const void* G, const void* A,
                          float* part, float* dQ, hipStream_t s) {
@@ -592,20 +618,24 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
       return st;
   }
   const bool foldb = fold_bwd(pl, T);
+  const bool foldt = foldb && fold_rt_ok(pl);
   {
     StageScope sc(POETX_STAGE_BLOCK_BWD, s);
-    // folded: Wf = D_R Wt replaces G_Wa = G_Z D_R. INT8 weight: G_Wa leaves
-    // scaled by the row scales of Wt, since G_Wa Wt = (G_Wa diag(s)) q
-    st = foldb ? fold_r(pl, Wt, Q_R, w.Wf, s)
-               : apply_blocks(pl, POETX_SIDE_R, T, w.GZ, Q_R, w.GWa, false, s,
-                              wq(pl) ? qscale(pl, Wt) : nullptr);
+    // folded: Wf = D_R Wt (stored transposed where possible) replaces
+    // G_Wa = G_Z D_R. INT8 weight: G_Wa leaves scaled by the row scales of Wt,
+    // since G_Wa Wt = (G_Wa diag(s)) q
+    st = foldt ? fold_rt(pl, Wt, Q_R, w.Wf, s)
+         : foldb ? fold_r(pl, Wt, Q_R, w.Wf, s)
+                 : apply_blocks(pl, POETX_SIDE_R, T, w.GZ, Q_R, w.GWa, false, s,
+                                wq(pl) ? qscale(pl, Wt) : nullptr);
     if (st != POETX_OK) return st;
   }
   // frozen weight: G_V = G_Wa Wt (folded: G_V = G_Z (D_R Wt))
   {
     StageScope sc(POETX_STAGE_W0_BWD, s);
     const Op a = foldb ? Op{w.GZ, pl->m, 1} : Op{w.GWa, pl->m, 1};
-    const Op b = foldb ? Op{w.Wf, 1, pl->n} : Op{Wt, 1, pl->n};
+    // B(j, i) = (D_R Wt)[i][j]: WfT[j][i] (K-contiguous) or Wf[i][j]
+    const Op b = foldt ? Op{w.Wf, pl->m, 1} : foldb ? Op{w.Wf, 1, pl->n} : Op{Wt, 1, pl->n};
     if ((st = gemm(pl, poetx::GEMM_W0, a, b, w.GV, pl->n, (int)T, pl->n, pl->m, 1, 0, 0, 0, 1, 0, false,
                    s, nullptr, wq(pl))) != POETX_OK)
       return st;
