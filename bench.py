@@ -287,13 +287,29 @@ def main() -> int:
                              "tflops": flops.get(s, 0.0) / (ms / n_diag * 1e-3) / 1e12 if ms else None}
         poetx.timing_reset()
 
-    # dominant kernel: the frozen-weight GEMM form with the larger time share
-    dom = max(w0, key=lambda s: w0[s][0])
-    ms_tot, launches = w0[dom]
-    kernel = {"w0_fwd": "w0_gemm_nt_lds", "w0_bwd": "w0_gemm_nn_lds"}[dom]
+    # dominant kernel: the frozen-weight product with the largest time share.
+    # The forward is always the K-contiguous (NT) kernel; the backward is too
+    # when the library folds D_R into a transposed weight (T >= n, whole
+    # 256-wide tiles of n, R blocks multiples of 64; not for INT8 weights).
+    folded_t = (not args.xq and all(T >= sp.n and sp.n % 256 == 0 and all(b % 64 == 0 for b in sp.bsz_R)
+                                    for sp in w.layers) and w.dtype == "bf16")
+    stage_kernel = {"w0_fwd": "w0_gemm_nt_lds", "w0_bwd": "w0_gemm_nt_lds" if folded_t else "w0_gemm_nn_lds"}
     if args.xq:
-        kernel = kernel.replace("w0_", "w0q_")
-    flops_per_launch = flops[dom] * args.steps / launches
+        stage_kernel = {k: v.replace("w0_", "w0q_") for k, v in stage_kernel.items()}
+    per_kernel = {}
+    for st, kname in stage_kernel.items():
+        ms_s, n_s = w0[st]
+        if n_s == 0:
+            continue
+        tot = per_kernel.setdefault(kname, [0.0, 0, 0.0, []])
+        tot[0] += ms_s
+        tot[1] += n_s
+        tot[2] += flops[st] * args.steps
+        tot[3].append(st)
+    kernel = max(per_kernel, key=lambda k: per_kernel[k][0])
+    ms_tot, launches, kflops, kstages = per_kernel[kernel]
+    dom = kstages[0]
+    flops_per_launch = kflops / launches
     avg_s = ms_tot / launches * 1e-3
     achieved = flops_per_launch / avg_s
     traffic, traffic_note = None, None
@@ -341,8 +357,9 @@ def main() -> int:
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": traffic,
             "launches": launches, "avg_launch_us": avg_s * 1e6,
             "flops_per_launch": flops_per_launch,
-            "algorithmic_bytes_per_launch": w0_bytes_per_step(w, T, args.xq) * args.steps / launches
-            * (2 if (xmem and dom == "w0_fwd") else 1),
+            "algorithmic_bytes_per_launch": w0_bytes_per_step(w, T, args.xq) * args.steps
+            * sum(2 if (xmem and st == "w0_fwd") else 1 for st in kstages) / launches,
+            "stages": kstages,
             "traffic_note": traffic_note,
         },
         "tflops_per_step": sum(flops.values()) / (ms_per_step * 1e-3) / 1e12,

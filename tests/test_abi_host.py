@@ -133,15 +133,21 @@ def test_bench_traffic_record_is_valid_or_marked_stale():
     spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
     bench = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(bench)
-    rec, why = bench.load_traffic("w0_gemm_nn_lds", "poetx-llama-block-h2048-7-linears-bf16")
-    if rec is None:
-        assert why
-        return
-    for key in ("traffic_bytes_per_launch", "algorithmic_bytes_per_launch", "copy_fetch_factor",
-                "copy_write_factor", "source_sha256"):
-        assert key in rec
-    assert rec["traffic_bytes_per_launch"] >= rec["write_bytes_per_launch"] > 0
-    rec2, why2 = bench.load_traffic("w0_gemm_nn_lds", "no-such-workload")
+    import glob
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md")):
+        name = os.path.basename(path)[:-len("_traffic.md")]
+        kernel = next(k for k in bench.TRAFFIC_SOURCES if name.startswith(k + "_"))
+        workload = name[len(kernel) + 1:]
+        rec, why = bench.load_traffic(kernel, workload)
+        if rec is None:
+            assert why
+            continue
+        for key in ("traffic_bytes_per_launch", "algorithmic_bytes_per_launch", "copy_fetch_factor",
+                    "copy_write_factor", "source_sha256"):
+            assert key in rec
+        assert rec["kernel"] == kernel and rec["workload"] == workload
+        assert rec["traffic_bytes_per_launch"] >= rec["write_bytes_per_launch"] > 0
+    rec2, why2 = bench.load_traffic("w0_gemm_nt_lds", "no-such-workload")
     assert rec2 is None and why2
 
 
