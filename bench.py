@@ -194,7 +194,8 @@ def main() -> int:
         L.set_weight(dev(inp.W0), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
         L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
         b = dict(X=dev(inp.X), Y=torch.empty(T, sp.m, dtype=tdt, device="cuda"),
-                 Wa=None if args.xmem else torch.empty(T, sp.m, dtype=tdt, device="cuda"))
+                 Wa=None if args.xmem else torch.empty(T, sp.m, dtype=tdt, device="cuda"),
+                 U=torch.empty(T, sp.n, dtype=tdt, device="cuda"))
         if w.backward:
             b.update(G=dev(inp.G_Y), GX=torch.empty(T, sp.n, dtype=tdt, device="cuda"),
                      g=[torch.empty(L.nparam[s], dtype=torch.float32, device="cuda") for s in (0, 1)])
@@ -213,7 +214,8 @@ def main() -> int:
     def step():
         build_many(layers)
         for L, b in zip(layers, bufs):
-            L.forward(b["X"], Y=b["Y"], Wa=b["Wa"], save=not args.xmem)
+            # the input is kept in the permuted order the backward reads it in
+            L.forward(b["X"], Y=b["Y"], Wa=b["Wa"], save=not args.xmem, keep_u=True, U=b["U"])
         if w.backward:
             # activation path layer by layer, then the chain rule through the
             # parameterisation of all layers in one batched call
@@ -347,7 +349,8 @@ def main() -> int:
             "layers": [f"{sp.name} {sp.m}x{sp.n}" for sp in w.layers],
             "block_size": max(max(sp.bsz_R) for sp in w.layers),
             "passes": "build+forward+backward" if w.backward else "build+forward",
-            "saved_activation": "none (POET-Xmem: recomputed)" if xmem else "Wa (POET-Xfast)",
+            "saved_activation": ("none (POET-Xmem: recomputed)" if xmem else "Wa (POET-Xfast)")
+            + "; layer input kept as U = X Pi_P^T",
             "frozen_weight": "int8, one fp32 scale per row (POET-XQ)" if args.xq else w.dtype,
             "orthogonal_map": "exact Cayley (doubling build, closed-form gradient)" if args.exact
             else f"Cayley-Neumann, k = {w.k}",

@@ -205,12 +205,17 @@ poetx_status poetx_build_orth_batch(int32_t count, const poetx_plan* const* plan
  *   Y        device [T, m] (dtype)
  *   Wa_saved device [T, m] (dtype) or NULL: the output of the Wt product, the
  *            one extra activation kept for the backward (POET-Xfast, [PX] §2.E)
+ *   U_saved  device [T, n] (dtype) or NULL: receives U = X Pi_P^T, the input in
+ *            the permuted order the backward reads it in. A caller that keeps
+ *            U_saved instead of X for the backward spares it a gather at no
+ *            extra memory.
  *   ws       device, poetx_workspace_size(plan, T, POETX_WS_FORWARD) bytes.
  * T = 0 is a no-op. */
 poetx_status poetx_forward(const poetx_plan* plan, int64_t T, const void* X, const void* Wt,
                            const int32_t* pi_R, const int32_t* pi_P,
                            const void* Q_R, const void* Q_P,
-                           void* Y, void* Wa_saved, void* ws, size_t ws_bytes, void* stream);
+                           void* Y, void* Wa_saved, void* U_saved, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* Backward of L = <G_Y, Y> w.r.t. X and both sides' skew parameters, for the
  * truncated Q the forward used. W0 is frozen and gets no gradient.
@@ -222,6 +227,8 @@ poetx_status poetx_forward(const poetx_plan* plan, int64_t T, const void* X, con
  *            recomputes it from X (gather, blocks of P, Wt product: POET-Xmem,
  *            [PX] §2.E), trading one more forward's worth of the first three
  *            stages for T x m activations; results are identical either way
+ *   U_saved  device [T, n] from poetx_forward's U_saved, or NULL: with it X is
+ *            not read (may be NULL) and the backward skips its gather of X
  *   G_Y      device [T, m] (dtype)      G_X device [T, n] (dtype)
  *   g_theta_R, g_theta_P device fp32 [param_count] (overwritten)
  *   ws       device, poetx_workspace_size(plan, T, POETX_WS_BACKWARD) bytes.
@@ -231,8 +238,8 @@ poetx_status poetx_backward(const poetx_plan* plan, int64_t T, const void* X, co
                             const int32_t* pi_R, const int32_t* pi_P,
                             const float* theta_R, const float* theta_P,
                             const void* Q_R, const void* Q_P, const void* Wa_saved,
-                            const void* G_Y, void* G_X, float* g_theta_R, float* g_theta_P,
-                            void* ws, size_t ws_bytes, void* stream);
+                            const void* U_saved, const void* G_Y, void* G_X, float* g_theta_R,
+                            float* g_theta_P, void* ws, size_t ws_bytes, void* stream);
 
 /* The backward split in two, so that the chain rule through the parameterisation
  * of many layers can share launches:
@@ -252,8 +259,8 @@ poetx_status poetx_backward(const poetx_plan* plan, int64_t T, const void* X, co
 poetx_status poetx_backward_dq(const poetx_plan* plan, int64_t T, const void* X, const void* Wt,
                                const int32_t* pi_R, const int32_t* pi_P,
                                const void* Q_R, const void* Q_P, const void* Wa_saved,
-                               const void* G_Y, void* G_X, float* dQ_R, float* dQ_P,
-                               void* ws, size_t ws_bytes, void* stream);
+                               const void* U_saved, const void* G_Y, void* G_X, float* dQ_R,
+                               float* dQ_P, void* ws, size_t ws_bytes, void* stream);
 poetx_status poetx_param_grad_batch(int32_t count, const poetx_plan* const* plans,
                                     const int32_t* sides, const float* const* thetas,
                                     const float* const* dQs, float* const* g_thetas,

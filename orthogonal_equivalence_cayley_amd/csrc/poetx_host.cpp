@@ -570,8 +570,8 @@ poetx_status grad_items(const GradItem* items, int count, hipStream_t s) {
 // parameterisation): G_X and dL/dQ of both sides (fp32).
 poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const void* Wt,
                          const int32_t* pi_R, const int32_t* pi_P, const void* Q_R, const void* Q_P,
-                         const void* Wa_saved, const void* G_Y, void* G_X, float* const dQ[2],
-                         const BwdWs& w, hipStream_t s) {
+                         const void* Wa_saved, const void* U_saved, const void* G_Y, void* G_X,
+                         float* const dQ[2], const BwdWs& w, hipStream_t s) {
   const int es = elsize(pl);
   poetx_status st;
   if (T == 0) {
@@ -585,8 +585,10 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
   // buffer and Wa the G_Wa buffer, both dead until the products that overwrite
   // them, which run after their last reads on the same stream.
   const void* Wa = Wa_saved;
+  // U = X Pi_P^T: kept by the caller, or gathered here (once)
+  const void* U = U_saved ? U_saved : w.U;
   if (!Wa_saved) {
-    {
+    if (!U_saved) {
       StageScope sc(POETX_STAGE_GATHER, s);
       HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
     }
@@ -594,12 +596,12 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
     {
       StageScope sc(POETX_STAGE_BLOCK_FWD, s);
       st = fold ? fold_p(pl, Wt, Q_P, w.Wf, s)
-                : apply_blocks(pl, POETX_SIDE_P, T, w.U, Q_P, w.GU, true, s);
+                : apply_blocks(pl, POETX_SIDE_P, T, U, Q_P, w.GU, true, s);
       if (st != POETX_OK) return st;
     }
     {
       StageScope sc(POETX_STAGE_W0_FWD, s);
-      const Op a = fold ? Op{w.U, pl->n, 1} : Op{w.GU, pl->n, 1};
+      const Op a = fold ? Op{U, pl->n, 1} : Op{w.GU, pl->n, 1};
       const Op b = fold ? Op{w.Wf, pl->n, 1} : Op{Wt, pl->n, 1};
       if ((st = gemm(pl, poetx::GEMM_W0, a, b, w.GWa, pl->m, (int)T, pl->m, pl->n, 1, 0, 0, 0, 1, 0,
                      false, s, wq(pl) ? qscale(pl, Wt) : nullptr, wq(pl))) != POETX_OK)
@@ -641,13 +643,13 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
       return st;
   }
   // P side: U = X Pi_P^T; dQ_P = G_V^T U per block; G_U = G_V D_P; G_X = G_U Pi_P
-  if (Wa_saved) {
+  if (Wa_saved && !U_saved) {
     StageScope sc(POETX_STAGE_GATHER, s);
     HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
   }
   {
     StageScope sc(POETX_STAGE_DQ, s);
-    if ((st = block_grads(pl, POETX_SIDE_P, T, w.GV, w.U, w.part, dQ[1], s)) != POETX_OK) return st;
+    if ((st = block_grads(pl, POETX_SIDE_P, T, w.GV, U, w.part, dQ[1], s)) != POETX_OK) return st;
   }
   {
     StageScope sc(POETX_STAGE_BLOCK_BWD, s);
@@ -662,12 +664,13 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
 
 poetx_status check_backward_args(const poetx_plan* pl, long long T, const void* X, const void* Wt,
                                  const int32_t* pi_R, const int32_t* pi_P, const void* Q_R,
-                                 const void* Q_P, const void* Wa_saved, const void* G_Y,
-                                 const void* G_X, const void* ws, size_t ws_bytes) {
+                                 const void* Q_P, const void* Wa_saved, const void* U_saved,
+                                 const void* G_Y, const void* G_X, const void* ws, size_t ws_bytes) {
   if (!pl || T < 0) return POETX_ERR_INVALID_ARG;
-  if (T > 0 && (!X || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !G_Y || !G_X))
+  if (T > 0 && ((!X && !U_saved) || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !G_Y || !G_X))
     return POETX_ERR_INVALID_ARG;
-  for (const void* p : {X, Wt, (const void*)pi_R, (const void*)pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X, ws})
+  for (const void* p : {X, Wt, (const void*)pi_R, (const void*)pi_P, Q_R, Q_P, Wa_saved, U_saved, G_Y,
+                        G_X, ws})
     if (!aligned16(p)) return POETX_ERR_ALIGNMENT;
   if (!ws || ws_bytes < poetx_workspace_size(pl, T, POETX_WS_BACKWARD)) return POETX_ERR_WORKSPACE;
   return POETX_OK;
@@ -993,19 +996,20 @@ poetx_status poetx_build_orth_batch(int32_t count, const poetx_plan* const* plan
 
 poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const void* Wt,
                            const int32_t* pi_R, const int32_t* pi_P, const void* Q_R,
-                           const void* Q_P, void* Y, void* Wa_saved, void* ws, size_t ws_bytes,
-                           void* stream) {
+                           const void* Q_P, void* Y, void* Wa_saved, void* U_saved, void* ws,
+                           size_t ws_bytes, void* stream) {
   if (!pl || T < 0) return POETX_ERR_INVALID_ARG;
   if (T == 0) return POETX_OK;
   if (!X || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !Y) return POETX_ERR_INVALID_ARG;
   for (const void* p : {X, Wt, (const void*)pi_R, (const void*)pi_P, Q_R, Q_P, (const void*)Y,
-                        (const void*)Wa_saved, (const void*)ws})
+                        (const void*)Wa_saved, (const void*)U_saved, (const void*)ws})
     if (!aligned16(p)) return POETX_ERR_ALIGNMENT;
   if (!ws || ws_bytes < poetx_workspace_size(pl, T, POETX_WS_FORWARD)) return POETX_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   FwdWs w;
   layout_fwd(pl, T, ws, &w);
   void* Wa = Wa_saved ? Wa_saved : w.Wa;
+  if (U_saved) w.U = U_saved;   // the gather writes the caller's buffer
   const int es = elsize(pl);
   poetx_status st;
   // 1. gather: U = X Pi_P^T
@@ -1065,10 +1069,11 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
 poetx_status poetx_backward(const poetx_plan* pl, int64_t T, const void* X, const void* Wt,
                             const int32_t* pi_R, const int32_t* pi_P, const float* theta_R,
                             const float* theta_P, const void* Q_R, const void* Q_P,
-                            const void* Wa_saved, const void* G_Y, void* G_X, float* g_theta_R,
-                            float* g_theta_P, void* ws, size_t ws_bytes, void* stream) {
-  poetx_status st = check_backward_args(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X,
-                                        ws, ws_bytes);
+                            const void* Wa_saved, const void* U_saved, const void* G_Y, void* G_X,
+                            float* g_theta_R, float* g_theta_P, void* ws, size_t ws_bytes,
+                            void* stream) {
+  poetx_status st = check_backward_args(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, U_saved, G_Y,
+                                        G_X, ws, ws_bytes);
   if (st != POETX_OK) return st;
   if (!theta_R || !theta_P || !g_theta_R || !g_theta_P) return POETX_ERR_INVALID_ARG;
   for (const void* p : {(const void*)theta_R, (const void*)theta_P, (const void*)g_theta_R,
@@ -1078,8 +1083,8 @@ poetx_status poetx_backward(const poetx_plan* pl, int64_t T, const void* X, cons
   BwdWs w;
   ChainWs cw[2];
   layout_bwd(pl, T, ws, &w, cw);
-  if ((st = backward_dq(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X, w.dQ, w, s)) !=
-      POETX_OK)
+  if ((st = backward_dq(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, U_saved, G_Y, G_X, w.dQ, w,
+                        s)) != POETX_OK)
     return st;
   StageScope sc(POETX_STAGE_CNP_BWD, s);
   const GradItem items[2] = {{pl, POETX_SIDE_R, theta_R, w.dQ[0], g_theta_R, cw[0]},
@@ -1089,10 +1094,11 @@ poetx_status poetx_backward(const poetx_plan* pl, int64_t T, const void* X, cons
 
 poetx_status poetx_backward_dq(const poetx_plan* pl, int64_t T, const void* X, const void* Wt,
                                const int32_t* pi_R, const int32_t* pi_P, const void* Q_R,
-                               const void* Q_P, const void* Wa_saved, const void* G_Y, void* G_X,
-                               float* dQ_R, float* dQ_P, void* ws, size_t ws_bytes, void* stream) {
-  poetx_status st = check_backward_args(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X,
-                                        ws, ws_bytes);
+                               const void* Q_P, const void* Wa_saved, const void* U_saved,
+                               const void* G_Y, void* G_X, float* dQ_R, float* dQ_P, void* ws,
+                               size_t ws_bytes, void* stream) {
+  poetx_status st = check_backward_args(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, U_saved, G_Y,
+                                        G_X, ws, ws_bytes);
   if (st != POETX_OK) return st;
   if (!dQ_R || !dQ_P) return POETX_ERR_INVALID_ARG;
   if (!aligned16(dQ_R) || !aligned16(dQ_P)) return POETX_ERR_ALIGNMENT;
@@ -1100,7 +1106,7 @@ poetx_status poetx_backward_dq(const poetx_plan* pl, int64_t T, const void* X, c
   BwdWs w;
   layout_bwd(pl, T, ws, &w, nullptr);
   float* const dQ[2] = {dQ_R, dQ_P};
-  return backward_dq(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X, dQ, w, s);
+  return backward_dq(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, U_saved, G_Y, G_X, dQ, w, s);
 }
 
 poetx_status poetx_param_grad_batch(int32_t count, const poetx_plan* const* plans,

@@ -70,6 +70,7 @@ class PoetxLayer:
         else:
             self.Qact = self.Q32
         self.Wa = None
+        self.U = None
         self.dQ = [torch.empty(self.nelem[s], dtype=torch.float32, device=self.device) for s in (0, 1)]
 
     # ------------------------------------------------------------------ setup
@@ -158,26 +159,35 @@ class PoetxLayer:
         return cur
 
     def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
-                Wa: Optional[torch.Tensor] = None, save: bool = True) -> torch.Tensor:
+                Wa: Optional[torch.Tensor] = None, save: bool = True, keep_u: bool = False,
+                U: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """save: keep Wa for the backward (POET-Xfast); else it is recomputed.
+        keep_u: keep the input in permuted order, U = X Pi_P^T (in U if given),
+        which the backward then reads instead of gathering X again."""
         T = X.shape[0]
         assert X.shape == (T, self.n) and X.dtype == self.tdtype and X.is_contiguous()
         if Y is None:
             Y = torch.empty(T, self.m, dtype=self.tdtype, device=self.device)
         if save and Wa is None:
             Wa = torch.empty(T, self.m, dtype=self.tdtype, device=self.device)
+        if keep_u and U is None:
+            U = torch.empty(T, self.n, dtype=self.tdtype, device=self.device)
         ws = self.workspace(_px.WS_FORWARD, T)
         self.plan.forward(T, X, self.Wt, self.pi_R, self.pi_P, self.Qact[0], self.Qact[1], Y,
-                          Wa if save else None, ws, ws.numel())
+                          Wa if save else None, ws, ws.numel(), U_saved=U if keep_u else None)
         self.Wa = Wa if save else None
+        self.U = U if keep_u else None
         return Y
 
     def _check_saved(self, T: int) -> None:
         # no saved Wa (forward(save=False)): the backward recomputes it (POET-Xmem)
         assert self.Wa is None or self.Wa.shape[0] == T, "saved Wa is from another batch"
+        assert self.U is None or self.U.shape[0] == T, "kept U is from another batch"
 
-    def backward(self, X: torch.Tensor, G_Y: torch.Tensor, G_X: Optional[torch.Tensor] = None,
+    def backward(self, X: Optional[torch.Tensor], G_Y: torch.Tensor, G_X: Optional[torch.Tensor] = None,
                  g_theta: Optional[Sequence[torch.Tensor]] = None):
-        T = X.shape[0]
+        """X may be None when the forward kept U."""
+        T = G_Y.shape[0]
         self._check_saved(T)
         assert G_Y.shape == (T, self.m) and G_Y.dtype == self.tdtype and G_Y.is_contiguous()
         if G_X is None:
@@ -187,18 +197,21 @@ class PoetxLayer:
         ws = self.workspace(_px.WS_BACKWARD, T)
         self.plan.backward(T, X, self.Wt, self.pi_R, self.pi_P, self.theta[0], self.theta[1],
                            self.Qact[0], self.Qact[1], self.Wa, G_Y, G_X, g_theta[0], g_theta[1],
-                           ws, ws.numel())
+                           ws, ws.numel(), U_saved=self.U)
         return G_X, g_theta[0], g_theta[1]
 
-    def backward_dq(self, X: torch.Tensor, G_Y: torch.Tensor, G_X: Optional[torch.Tensor] = None):
+    def backward_dq(self, X: Optional[torch.Tensor], G_Y: torch.Tensor,
+                    G_X: Optional[torch.Tensor] = None):
         """Activation path of the backward: returns G_X and leaves dL/dQ of both
-        sides in self.dQ for param_grad_many()."""
-        T = X.shape[0]
+        sides in self.dQ for param_grad_many(). X may be None when the forward
+        kept U."""
+        T = G_Y.shape[0]
         self._check_saved(T)
         assert G_Y.shape == (T, self.m) and G_Y.dtype == self.tdtype and G_Y.is_contiguous()
         if G_X is None:
             G_X = torch.empty(T, self.n, dtype=self.tdtype, device=self.device)
         ws = self.workspace(_px.WS_BACKWARD, T)
         self.plan.backward_dq(T, X, self.Wt, self.pi_R, self.pi_P, self.Qact[0], self.Qact[1],
-                              self.Wa, G_Y, G_X, self.dQ[0], self.dQ[1], ws, ws.numel())
+                              self.Wa, G_Y, G_X, self.dQ[0], self.dQ[1], ws, ws.numel(),
+                              U_saved=self.U)
         return G_X

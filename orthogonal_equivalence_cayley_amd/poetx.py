@@ -99,10 +99,11 @@ def _load() -> ctypes.CDLL:
         "poetx_quantize_weight": (st, [vp, vp, vp, vp, vp, vp]),
         "poetx_build_orth": (st, [vp, i32, vp, vp, vp, vp, sz, vp]),
         "poetx_build_orth_batch": (st, [i32, vp, vp, vp, vp, vp, vp, vp, vp]),
-        "poetx_forward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
-        "poetx_backward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+        "poetx_forward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "poetx_backward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]),
-        "poetx_backward_dq": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "poetx_backward_dq": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                   vp]),
         "poetx_param_grad_batch": (st, [i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "poetx_gather_cols": (st, [vp, i64, i32, vp, vp, vp, vp]),
         "poetx_scatter_cols": (st, [vp, i64, i32, vp, vp, vp, vp]),
@@ -262,25 +263,25 @@ class Plan:
                                     _ptr(ws), ws_bytes, _stream(stream)), "poetx_build_orth")
 
     def forward(self, T: int, X, Wt, pi_R, pi_P, Q_R, Q_P, Y, Wa_saved, ws, ws_bytes: int,
-                stream=None) -> None:
+                stream=None, U_saved=None) -> None:
         _check(LIB.poetx_forward(self._h, T, _ptr(X), _ptr(Wt), _ptr(pi_R), _ptr(pi_P),
-                                 _ptr(Q_R), _ptr(Q_P), _ptr(Y), _ptr(Wa_saved), _ptr(ws),
-                                 ws_bytes, _stream(stream)), "poetx_forward")
+                                 _ptr(Q_R), _ptr(Q_P), _ptr(Y), _ptr(Wa_saved), _ptr(U_saved),
+                                 _ptr(ws), ws_bytes, _stream(stream)), "poetx_forward")
 
     def backward(self, T: int, X, Wt, pi_R, pi_P, theta_R, theta_P, Q_R, Q_P, Wa_saved, G_Y,
-                 G_X, g_theta_R, g_theta_P, ws, ws_bytes: int, stream=None) -> None:
+                 G_X, g_theta_R, g_theta_P, ws, ws_bytes: int, stream=None, U_saved=None) -> None:
         _check(LIB.poetx_backward(self._h, T, _ptr(X), _ptr(Wt), _ptr(pi_R), _ptr(pi_P),
                                   _ptr(theta_R), _ptr(theta_P), _ptr(Q_R), _ptr(Q_P),
-                                  _ptr(Wa_saved), _ptr(G_Y), _ptr(G_X), _ptr(g_theta_R),
-                                  _ptr(g_theta_P), _ptr(ws), ws_bytes, _stream(stream)),
-               "poetx_backward")
+                                  _ptr(Wa_saved), _ptr(U_saved), _ptr(G_Y), _ptr(G_X),
+                                  _ptr(g_theta_R), _ptr(g_theta_P), _ptr(ws), ws_bytes,
+                                  _stream(stream)), "poetx_backward")
 
     def backward_dq(self, T: int, X, Wt, pi_R, pi_P, Q_R, Q_P, Wa_saved, G_Y, G_X, dQ_R, dQ_P,
-                    ws, ws_bytes: int, stream=None) -> None:
+                    ws, ws_bytes: int, stream=None, U_saved=None) -> None:
         _check(LIB.poetx_backward_dq(self._h, T, _ptr(X), _ptr(Wt), _ptr(pi_R), _ptr(pi_P),
-                                     _ptr(Q_R), _ptr(Q_P), _ptr(Wa_saved), _ptr(G_Y), _ptr(G_X),
-                                     _ptr(dQ_R), _ptr(dQ_P), _ptr(ws), ws_bytes, _stream(stream)),
-               "poetx_backward_dq")
+                                     _ptr(Q_R), _ptr(Q_P), _ptr(Wa_saved), _ptr(U_saved),
+                                     _ptr(G_Y), _ptr(G_X), _ptr(dQ_R), _ptr(dQ_P), _ptr(ws),
+                                     ws_bytes, _stream(stream)), "poetx_backward_dq")
 
     def gather_cols(self, T: int, dim: int, inp, idx, out, stream=None) -> None:
         _check(LIB.poetx_gather_cols(self._h, T, dim, _ptr(inp), _ptr(idx), _ptr(out),

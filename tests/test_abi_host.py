@@ -92,29 +92,39 @@ def test_forward_argument_errors():
     ws = p.workspace_size(4, px.WS_FORWARD)
     call = lambda **kw: px.LIB.poetx_forward(
         p.handle, kw.get("T", 4), kw.get("X", A), A, A, A, A, A, kw.get("Y", A), None,
-        kw.get("ws", A), kw.get("wsb", ws), None)
+        kw.get("U", None), kw.get("ws", A), kw.get("wsb", ws), None)
     assert call(T=0) == px.POETX_OK                      # T = 0 is a no-op
     assert call(T=-1) == px.POETX_ERR_INVALID_ARG
     assert call(X=None) == px.POETX_ERR_INVALID_ARG
     assert call(Y=A + 8) == px.POETX_ERR_ALIGNMENT
     assert call(wsb=ws - 1) == px.POETX_ERR_WORKSPACE
     assert call(ws=None) == px.POETX_ERR_WORKSPACE
-    assert px.LIB.poetx_forward(None, 4, A, A, A, A, A, A, A, None, A, ws, None) == px.POETX_ERR_INVALID_ARG
+    assert call(U=A + 4) == px.POETX_ERR_ALIGNMENT
+    assert px.LIB.poetx_forward(None, 4, A, A, A, A, A, A, A, None, None, A, ws, None) == \
+        px.POETX_ERR_INVALID_ARG
 
 
 def test_backward_and_build_argument_errors():
     p = _plan()
     wsb = p.workspace_size(4, px.WS_BACKWARD)
-    args = [p.handle, 4, A, A, A, A, A, A, A, A, A, A, A, A, A, A, wsb, None]
-    # G_Y missing is an error; Wa_saved missing is not (the backward recomputes it)
-    assert px.LIB.poetx_backward(*args[:11], None, *args[12:]) == px.POETX_ERR_INVALID_ARG
-    assert px.LIB.poetx_backward(*args[:10], None, *args[11:12], None, *args[13:]) == \
-        px.POETX_ERR_INVALID_ARG
+    #       h, T, X, Wt, piR, piP, thR, thP, QR, QP, Wa, U, GY, GX, gR, gP, ws, wsb, stream
+    args = [p.handle, 4, A, A, A, A, A, A, A, A, A, None, A, A, A, A, A, wsb, None]
+    # Wa_saved and U_saved may be missing (recomputed / gathered); G_Y may not,
+    # nor both X and U_saved
+    for idx, val in ((12, None), (2, None), (10, None)):
+        bad = list(args)
+        bad[idx] = val
+        if idx == 10:
+            bad[12] = None
+        assert px.LIB.poetx_backward(*bad) == px.POETX_ERR_INVALID_ARG, idx
     bad = list(args)
     bad[3] = A + 4
     assert px.LIB.poetx_backward(*bad) == px.POETX_ERR_ALIGNMENT
     bad = list(args)
-    bad[16] = 16
+    bad[11] = A + 4
+    assert px.LIB.poetx_backward(*bad) == px.POETX_ERR_ALIGNMENT
+    bad = list(args)
+    bad[17] = 16
     assert px.LIB.poetx_backward(*bad) == px.POETX_ERR_WORKSPACE
     bw = p.workspace_size(0, px.WS_BUILD)
     assert px.LIB.poetx_build_orth(p.handle, 3, A, A, None, A, bw, None) == px.POETX_ERR_INVALID_ARG

@@ -457,3 +457,22 @@ def test_layer_with_folded_blocks(dt, c, save):
         got["Wa"] = to_np(Wa)
         keys.append("Wa")
     _compare(got, ref, keys, TOL_F32 if dt == "f32" else TOL_BF16, "folded")
+
+
+@pytest.mark.parametrize("save", [True, False])
+def test_kept_input_permutation_matches_gathering(save):
+    """A backward that reads the U = X Pi_P^T the forward kept (X not passed)
+    gives the same results, bit for bit, as one that gathers X again."""
+    import torch
+    inp = workloads.small_case(256, 512, (256,), (256, 256), T=700, seed=44, dtype="bf16",
+                               theta_std=0.01)
+    L = make_layer(inp, 4, "bf16")
+    L.build()
+    X, G = to_dev(inp.X, "bf16"), to_dev(inp.G_Y, "bf16")
+    L.forward(X, save=save)
+    a = [t.clone() for t in L.backward(X, G)]
+    L.forward(X, save=save, keep_u=True)
+    b = [t.clone() for t in L.backward(None, G)]
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
