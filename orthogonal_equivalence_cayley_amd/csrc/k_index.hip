@@ -14,6 +14,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kLdsBudget = 64 * 1024;   // bytes of LDS for staged rows per workgroup
+constexpr int kMaxRows = 4;             // rows per workgroup: small tiles keep the grid full
 
 template <typename E, int VEC>
 struct Vec { E v[VEC]; };
@@ -272,7 +273,7 @@ hipError_t gather_typed(const void* in, long long in_ld, const int32_t* rows, co
     return hipGetLastError();
   }
   int R = (int)(kLdsBudget / row_bytes);
-  if (R > 8) R = 8;
+  if (R > kMaxRows) R = kMaxRows;
   const bool vec = (dim % VEC == 0) && (in_ld % VEC == 0) &&
                    ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
   constexpr int G = 8 / sizeof(E);
@@ -306,7 +307,7 @@ hipError_t scatter_typed(const void* in, const int32_t* idx, void* out, long lon
     return hipGetLastError();
   }
   int R = (int)(kLdsBudget / row_bytes);
-  if (R > 8) R = 8;
+  if (R > kMaxRows) R = kMaxRows;
   const bool vec = (dim % VEC == 0) && ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
   constexpr int G = 8 / sizeof(E);
   if (vec && R >= G) {
