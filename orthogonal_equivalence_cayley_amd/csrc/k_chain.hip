@@ -17,7 +17,9 @@
 //   ABAR  : backward, A_{k+1} = c_{k+1} G; A_j = c_j G - A_{j+1} S  (S^T = -S).
 //           Stores every A_j (j = 1..k+1).
 //   TCHAIN: backward, transposed second chain T_j^T = A_j^T + T_{j+1}^T S with
-//           T_{k+1} = A_{k+1}; writes T_1^T = (dL/dS)^T.
+//           T_{k+1} = A_{k+1}; writes T_1^T = (dL/dS)^T. A lane's 4 accumulator
+//           rows of one column are 4 consecutive elements of one row of A_j,
+//           read with one 16-byte load.
 // Each workgroup has 4 waves; wave w owns the 16-column tiles w, w+4, ... of
 // all RP rows.
 #include "poetx_internal.h"
@@ -30,6 +32,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ float coef(int j, int k) { return (j == 0 || j == k + 1) ? 1.0f : 2.0f; }
+
+// 4 consecutive floats at a 16-byte aligned address (b % 16 == 0, panel rows in
+// groups of 4 from a multiple of 16).
+__device__ __forceinline__ float4 load_t4(const float* src) { return *reinterpret_cast<const float4*>(src); }
+__device__ __forceinline__ float f4(const float4& a, int v) {
+  return v == 0 ? a.x : v == 1 ? a.y : v == 2 ? a.z : a.w;
+}
 
 // The run this workgroup belongs to. Constant indices only (fully unrolled), so
 // the table stays in kernel-argument memory and scalar registers.
@@ -86,6 +95,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
       for (int v = 0; v < 4; ++v) keep[mt][t][v] = 0.0f;
       if (tile >= ntiles) continue;
       const int col = tile * 16 + li;
+      float4 at;   // TCHAIN: A_{k+1}^T panel rows 16 mt + 4 lk + 0..3 = A_{k+1}[col][r0 + ...]
+      if (MODE == 2)
+        at = load_t4(p.G + (long long)k * p.stride + moff + (long long)col * b + r0 + 16 * mt + 4 * lk);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = 16 * mt + 4 * lk + v;
@@ -100,8 +112,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
           x = coef(k + 1, k) * g;
           p.out[(long long)k * p.stride + moff + o] = x;
         } else {
-          // A_{k+1}^T panel: element (row, col) = A_{k+1}[col][r0 + row]
-          x = p.G[(long long)k * p.stride + moff + (long long)col * b + r0 + row];
+          x = f4(at, v);
         }
         panel[row * pitch + col] = x;
       }
@@ -157,6 +168,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
         const int tile = wave + 4 * t;
         if (tile >= ntiles) continue;
         const int col = tile * 16 + li;
+        float4 at;
+        if (MODE == 2)
+          at = load_t4(p.G + (long long)(j - 1) * p.stride + moff + (long long)col * b + r0 + 16 * mt + 4 * lk);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int row = 16 * mt + 4 * lk + v;
@@ -167,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
             x = coef(j, k) * keep[mt][t][v] - x;
             p.out[(long long)(j - 1) * p.stride + moff + (long long)(r0 + row) * b + col] = x;
           } else {
-            x += p.G[(long long)(j - 1) * p.stride + moff + (long long)col * b + r0 + row];
+            x += f4(at, v);
           }
           panel[row * pitch + col] = x;
         }
