@@ -225,9 +225,16 @@ hipError_t launch_class(ChainBatch cb, hipStream_t s) {
     bmax = max(bmax, cb.e[i].b);
   }
   if (wg == 0) return hipSuccess;
-  // b % 16 == 0: the prefetch of U = 4 K-steps of 4 rows stays inside S
+  // b % 16 == 0: the prefetch of U = 4 K-steps of 4 rows stays inside S; the
+  // backward chains prefetch 8 K-steps when every b is a multiple of 32
+  bool deep = MODE != 0;
+  for (int i = 0; i < cb.n; ++i)
+    if (cb.e[i].b % 32) deep = false;
   const size_t lds = (size_t)RP * (bmax + 4) * sizeof(float);
-  hipLaunchKernelGGL((chain_kernel<MODE, NT, MT, 4>), dim3(wg), dim3(kThreads), lds, s, cb);
+  if (deep)
+    hipLaunchKernelGGL((chain_kernel<MODE, NT, MT, 8>), dim3(wg), dim3(kThreads), lds, s, cb);
+  else
+    hipLaunchKernelGGL((chain_kernel<MODE, NT, MT, 4>), dim3(wg), dim3(kThreads), lds, s, cb);
   return hipGetLastError();
 }
 
