@@ -226,8 +226,9 @@ hipError_t launch_class(ChainBatch cb, hipStream_t s) {
   }
   if (wg == 0) return hipSuccess;
   // b % 16 == 0: the prefetch of U = 4 K-steps of 4 rows stays inside S; the
-  // backward chains prefetch 8 K-steps when every b is a multiple of 32
-  bool deep = MODE != 0;
+  // chains prefetch 8 K-steps when every b is a multiple of 32 (the loads from
+  // L2 are what the waves wait on: 16 K-steps was slower again)
+  bool deep = true;
   for (int i = 0; i < cb.n; ++i)
     if (cb.e[i].b % 32) deep = false;
   const size_t lds = (size_t)RP * (bmax + 4) * sizeof(float);
