@@ -128,13 +128,23 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
     __syncthreads();          // panel of the previous step written
     {
       // B operand straight from L2 into registers, U K-steps ahead; several
-      // workgroups per CU hide the latency
-      const float* Sl = S + (long long)lk * b + li;
+      // workgroups per CU hide the latency. Raw buffer loads over this block's S:
+      // a per-lane byte offset for each column tile plus the K-step's row offset
+      // in a scalar register (no 64-bit address per load), range-checked by the
+      // hardware against the block's b * b floats.
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(S), (short)0, (int)(bb * 4), 0x00020000);
+      int voff[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) voff[t] = (lk * b + bcol[t] + li) * 4;
+      auto ldb = [&](int t, int krow) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff[t], krow * b * 4, 0));
+      };
       float bn[U][NT];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) bn[u][t] = Sl[(long long)(4 * u) * b + bcol[t]];
+        for (int t = 0; t < NT; ++t) bn[u][t] = ldb(t, 4 * u);
       for (int kc = 0; kc < b; kc += 4 * U) {
         float bc[U][NT];
 #pragma unroll
@@ -145,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-          for (int t = 0; t < NT; ++t) bn[u][t] = Sl[(long long)(kn + 4 * u) * b + bcol[t]];
+          for (int t = 0; t < NT; ++t) bn[u][t] = ldb(t, kn + 4 * u);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float a[MT];
