@@ -261,9 +261,9 @@ hipError_t launch_mode(const ChainBatch& all, hipStream_t s) {
       for (int i = 0; i < all.n; ++i) {
         const int need = (all.e[i].b / 16 + 3) / 4;
         const int cls = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-        // 32-row panels for the build only: the backward chains keep more state
-        // per tile and lose more to the lower occupancy than they gain
-        const int m = (MODE != 1 && all.e[i].b % 32 == 0 && cls <= 4) ? 2 : 1;
+        // 32-row panels wherever b allows them (with S read through buffer loads
+        // the extra accumulators still leave 2-3 waves per SIMD)
+        const int m = (all.e[i].b % 32 == 0 && cls <= 4) ? 2 : 1;
         if (cls == nt && m == mt) cb.e[cb.n++] = all.e[i];
       }
       if (cb.n == 0) continue;
