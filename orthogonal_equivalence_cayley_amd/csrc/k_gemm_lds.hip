@@ -90,6 +90,8 @@ struct KTile {
 template <int R, int NT, int KB>
 struct MTile {
   static constexpr int CPR = R / 8;
+  // the swizzle moves a chunk by up to 12 positions inside its K-row
+  static_assert(CPR >= 16, "row-contiguous tiles need R >= 128");
   static constexpr int SLOTS = KB * CPR;
   static constexpr int L = SLOTS / NT;
   const uint16_t* src[L];
@@ -184,6 +186,7 @@ struct QTile {
   static constexpr int L = CH / NT;        // loads per thread per stage
   static constexpr int BYTES = R * KB * 2; // bf16 in LDS
   static_assert(CH % NT == 0, "whole loads per thread");
+  static_assert(KMAJ || R >= 128, "the row-contiguous layout of MTile needs R >= 128");
   const int8_t* src[L];
   uint4 reg[L];
   __device__ __forceinline__ void init(const int8_t* base, long long ld, int rc0, int rows) {
