@@ -343,7 +343,7 @@ __device__ __forceinline__ TriWork tri_work(const TriBatch& tb) {
 // run of packed parameters; below it the values come from the 16 packed columns
 // r0 .. r0 + 15 (rows 0 .. r0 + 15), read row-wise into LDS and used transposed.
 __global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
-  __shared__ float strip[512 * kTriPitch];
+  extern __shared__ float strip[];   // [largest b of the batch][kTriPitch]
   const TriWork w = tri_work(tb);
   const int b = w.t.b, r0 = w.r0;
   const float* th = w.t.src + (long long)w.g * ((long long)b * (b - 1) / 2);
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
 // one block. M[c][r] (c > r) comes from columns r0 .. r0 + 15 of rows
 // r0 .. b - 1, read row-wise into LDS and used transposed.
 __global__ __launch_bounds__(kThreads) void pack_batch_kernel(TriBatch tb) {
-  __shared__ float strip[512 * kTriPitch];
+  extern __shared__ float strip[];   // [largest b of the batch][kTriPitch]
   const TriWork w = tri_work(tb);
   const int b = w.t.b, r0 = w.r0;
   const float* M = w.t.src + (long long)w.g * b * b;
@@ -405,6 +405,15 @@ long long fill_offsets(TriBatch& tb) {
   return tot;
 }
 
+// LDS of one workgroup: a strip of kTriRows columns over at most b rows, sized
+// for the batch (a fixed 512-row strip held b = 256 batches to half the
+// workgroups per CU).
+size_t strip_bytes(const TriBatch& tb) {
+  int bmax = 0;
+  for (int i = 0; i < tb.n; ++i) bmax = max(bmax, tb.e[i].b);
+  return (size_t)bmax * kTriPitch * sizeof(float);
+}
+
 bool tri_batch_ok(const TriBatch& tb) {
   if (tb.n > kChainMaxEntries) return false;
   for (int i = 0; i < tb.n; ++i)
@@ -420,7 +429,7 @@ hipError_t launch_unpack_batch(const TriBatch& in, hipStream_t s) {
   TriBatch tb = in;
   const long long wgs = fill_offsets(tb);
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(unpack_batch_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, tb);
+  hipLaunchKernelGGL(unpack_batch_kernel, dim3((unsigned)wgs), dim3(kThreads), strip_bytes(tb), s, tb);
   return hipGetLastError();
 }
 
@@ -430,7 +439,7 @@ hipError_t launch_pack_batch(const TriBatch& in, hipStream_t s) {
   TriBatch tb = in;
   const long long wgs = fill_offsets(tb);
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(pack_batch_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, tb);
+  hipLaunchKernelGGL(pack_batch_kernel, dim3((unsigned)wgs), dim3(kThreads), strip_bytes(tb), s, tb);
   return hipGetLastError();
 }
 
