@@ -1,0 +1,215 @@
+// Batched block-diagonal products with blocks of 256 on gfx950
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulate): C[:, blk g] = A[:, blk g] B_g,
+// B_g(n, k) one 256 x 256 block of Q or of its transpose. These are the
+// products of the orthogonal factors on the activations (Z = Wa D_R^T in the
+// forward, G_U = G_V D_P in the backward) and the weight-side Wf = Wt D_P
+// ([PX] = page "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
+// Transformation", Résumé technique §2.C: the block-diagonal factors applied as
+// batched block products).
+//
+// K is only 256, so a tiled GEMM spends most of its time filling and draining
+// its pipeline. Here the block of B stays in registers instead: each of the 8
+// waves owns 32 output columns and keeps B_g(those columns, all 256 k) as its 16
+// MFMA operand fragments (64 VGPRs), loaded once per workgroup (a workgroup
+// stays on one block). Row tiles of A
+// (128 rows x the block's 256 columns, 64 KiB) stream from HBM into a two-stage
+// LDS ring with direct-to-LDS loads, so one tile is in flight while the other is
+// multiplied, and every wave reads the whole A tile from LDS.
+//
+// A tile in LDS: row r of 256 bf16 is 32 chunks of 16 bytes; chunk c sits at
+// slot r * 32 + (c ^ (r & 31)), so the 16 rows read by one pass of an operand
+// read (one chunk each) fall in distinct banks.
+#include "poetx_internal.h"
+
+namespace poetx {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kB = 256;                         // block size (N = K)
+constexpr int kRows = 128;                      // rows of A per tile
+constexpr int kWaves = 8;                       // each owns 32 of the 256 columns
+constexpr int kThreads = kWaves * 64;
+constexpr int kNKK = kB / 16;                   // 16-deep K steps
+constexpr int kCPR = kB / 8;                    // 16-byte chunks per row of A
+constexpr int kStage = kRows * kB * 2;          // bytes of one A tile in LDS
+constexpr int kLoads = kRows * kCPR / kThreads; // direct-to-LDS loads per thread per tile
+constexpr int kMT = kRows / 32;                 // 32-row MFMA tiles per wave and tile
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
+}
+// Waits for every vector memory operation of this wave (the tile's loads, the
+// previous tile's stores), then for all waves: what the loads wrote is in LDS
+// and every earlier LDS read of the workgroup is done.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
+  const __bf16 a = static_cast<__bf16>(lo);
+  const __bf16 b = static_cast<__bf16>(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// BKM: B(n, k) = B_g[n * ldb + k] (K-contiguous, the transposed Q); otherwise
+// B(n, k) = B_g[k * ldb + n]. Workgroup w works on block g = w / wpg and runs
+// row tiles [(w % wpg) * per_wg, + per_wg) of it, so it loads B_g only once.
+template <bool BKM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
+  extern __shared__ __align__(16) unsigned char lds[];   // two A tiles
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.x / wpg;
+  const int t0 = (blockIdx.x - g * wpg) * per_wg;
+  const int t1 = min(tiles_per_group, t0 + per_wg);
+  if (g >= p.groups || t0 >= t1) return;
+  const uint16_t* Ag = static_cast<const uint16_t*>(p.A) + (long long)g * p.a_gs;
+  const uint16_t* Bg = static_cast<const uint16_t*>(p.B) + (long long)g * p.b_gs;
+  uint16_t* Cg = static_cast<uint16_t*>(p.C) + (long long)g * p.c_gs + wave * 32;
+  const int nl = lane & 31, h = lane >> 5;
+  const int ncol = wave * 32 + nl;   // B column of this lane's operand fragments
+  auto stage = [&](int i) { return lds + i * kStage; };
+
+  // row tile t of A -> LDS stage st: lane `tid` of load i fills slot i * kThreads + tid
+  auto issue = [&](int t, unsigned char* st) {
+    const long long row0 = (long long)t * kRows;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int s = i * kThreads + tid;
+      const int r = s / kCPR;
+      const int c = (s % kCPR) ^ (r & 31);
+      const long long row = min(row0 + r, (long long)p.M - 1);   // rows past M: loaded, not stored
+      dma16(Ag + row * p.lda + c * 8, st + (i * kThreads + wave * 64) * 16);
+    }
+  };
+
+  // B_g(ncol, 16 kk + 8 h .. + 7) for kk = 0 .. 15
+  bf16x8 bq[kNKK];
+  issue(t0, stage(0));   // the first A tile is in flight while B is fetched
+  if (BKM) {
+#pragma unroll
+    for (int kk = 0; kk < kNKK; ++kk)
+      bq[kk] = *reinterpret_cast<const bf16x8*>(Bg + (long long)ncol * p.ldb + 16 * kk + 8 * h);
+  } else {
+    // column ncol of B_g, through the free stage: 128 rows of B_g at a time in
+    // natural layout (row k = 512 bytes); the 32 lanes of a read take 64
+    // consecutive bytes of one row
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int s = i * kThreads + tid;
+        const int k = 128 * half + s / kCPR;
+        dma16(Bg + (long long)k * p.ldb + (s % kCPR) * 8, stage(1) + (i * kThreads + wave * 64) * 16);
+      }
+      tile_barrier();
+      const uint16_t* Bl = reinterpret_cast<const uint16_t*>(stage(1));
+#pragma unroll
+      for (int kk = 0; kk < kNKK / 2; ++kk) {
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          v[e] = __builtin_bit_cast(__bf16, Bl[(16 * kk + 8 * h + e) * kB + ncol]);
+        bq[8 * half + kk] = v;
+      }
+      tile_barrier();   // every wave has read this half before the stage is reused
+    }
+  }
+
+  const bool upper = h != 0;
+  for (int t = t0; t < t1; ++t) {
+    const int it = t - t0;
+    const unsigned char* st = stage(it & 1);
+    tile_barrier();
+    if (t + 1 < t1) issue(t + 1, stage((it + 1) & 1));
+    f32x16 acc[kMT];
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < kNKK; ++kk) {
+      bf16x8 af[kMT];
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const int r = 32 * mt + nl;
+        const int c = 2 * kk + h;
+        af[mt] = *reinterpret_cast<const bf16x8*>(st + (r * kCPR + (c ^ (r & 31))) * 16);
+      }
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+        // B first: the result is C^T, each lane holds four consecutive output
+        // columns (8 q + 4 h .. + 3 of the wave's 32) of output row nl
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[kk], af[mt], acc[mt], 0, 0, 0);
+    }
+    // epilogue: lanes l and l ^ 32 swap half of their column groups so that each
+    // lane stores 8 consecutive columns (the lower lane q = 0, 2, the upper 1, 3)
+    const long long row0 = (long long)t * kRows;
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      uint32_t w[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[q][0] = pack_bf16_pair(acc[mt][4 * q], acc[mt][4 * q + 1]);
+        w[q][1] = pack_bf16_pair(acc[mt][4 * q + 2], acc[mt][4 * q + 3]);
+      }
+      const long long m = row0 + 32 * mt + nl;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        // own groups (q = 2 hh + upper) and the ones sent to the partner
+        const uint32_t o0 = upper ? w[2 * hh + 1][0] : w[2 * hh][0];
+        const uint32_t o1 = upper ? w[2 * hh + 1][1] : w[2 * hh][1];
+        const uint32_t s0 = upper ? w[2 * hh][0] : w[2 * hh + 1][0];
+        const uint32_t s1 = upper ? w[2 * hh][1] : w[2 * hh + 1][1];
+        const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32);
+        const uint32_t r1 = (uint32_t)__shfl_xor((int)s1, 32);
+        if (m >= p.M) continue;
+        uint4 v;
+        if (upper) {   // columns 8q .. 8q+3 come from the partner, 8q+4 .. from here
+          v.x = r0; v.y = r1; v.z = o0; v.w = o1;
+        } else {
+          v.x = o0; v.y = o1; v.z = r0; v.w = r1;
+        }
+        *reinterpret_cast<uint4*>(Cg + m * p.ldc + 8 * (2 * hh + (upper ? 1 : 0))) = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool block_regb_supported(const GemmBf16& p) {
+  if (p.role != GEMM_BLOCK || p.N != kB || p.K != kB || !p.a_kmajor || p.out_f32) return false;
+  if (p.splits != 1 || p.b_i8 || p.col_scale || p.M <= 0 || p.groups <= 0) return false;
+  if (p.lda % 8 || p.a_gs % 8 || p.ldc % 8 || p.c_gs % 8) return false;   // 16-byte rows
+  if (p.ldb % 8 || p.ldb < kB) return false;   // 16-byte rows of B either way
+  if (((uintptr_t)p.A | (uintptr_t)p.C | (uintptr_t)p.B) & 15) return false;
+  return true;
+}
+
+hipError_t launch_block_regb(const GemmBf16& p, hipStream_t s) {
+  if (!block_regb_supported(p)) return hipErrorInvalidValue;
+  const long long tpg = (p.M + kRows - 1) / kRows;
+  if (tpg > INT32_MAX) return hipErrorInvalidValue;
+  // one workgroup per CU (two 64 KiB stages): up to 256 / groups workgroups per
+  // block, each on consecutive row tiles of that block only
+  const long long wmax = p.groups >= 256 ? 1 : 256 / p.groups;
+  const long long per = (tpg + wmax - 1) / wmax;
+  const long long wpg = (tpg + per - 1) / per;
+  const long long wgs = wpg * p.groups;
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  const size_t lds = 2 * (size_t)kStage;
+  if (p.b_kmajor)
+    hipLaunchKernelGGL(block_regb_kernel<true>, dim3((unsigned)wgs), dim3(kThreads), lds, s, p,
+                       (int)tpg, (int)wpg, (int)per);
+  else
+    hipLaunchKernelGGL(block_regb_kernel<false>, dim3((unsigned)wgs), dim3(kThreads), lds, s, p,
+                       (int)tpg, (int)wpg, (int)per);
+  return hipGetLastError();
+}
+
+}  // namespace poetx

@@ -259,6 +259,7 @@ hipError_t dispatch(const GemmBf16& p, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || p.groups <= 0) return hipSuccess;
+  if (block_regb_supported(p)) return launch_block_regb(p, s);
   const long long big_tiles = (long long)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.groups * p.splits;
   // the token reduction (dQ) keeps 128 x 128 tiles: its split count is sized for them
   const bool big = big_tiles >= 256 && p.role != GEMM_DQ;
