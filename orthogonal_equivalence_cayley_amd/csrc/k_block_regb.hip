@@ -11,10 +11,11 @@
 // its pipeline. Here the block of B stays in registers instead: each of the 8
 // waves owns 32 output columns and keeps B_g(those columns, all 256 k) as its 16
 // MFMA operand fragments (64 VGPRs), loaded once per workgroup (a workgroup
-// stays on one block). Row tiles of A
-// (128 rows x the block's 256 columns, 64 KiB) stream from HBM into a two-stage
-// LDS ring with direct-to-LDS loads, so one tile is in flight while the other is
-// multiplied, and every wave reads the whole A tile from LDS.
+// stays on one block). Row tiles of A (ROWS rows x the block's 256 columns)
+// stream from HBM into an LDS ring of ST stages with direct-to-LDS loads, ST - 1
+// tiles in flight while one is multiplied; every wave reads the whole A tile
+// from LDS. An HBM stream needs on the order of 100 KiB in flight per CU, so
+// the ring holds several small tiles rather than two large ones.
 //
 // A tile in LDS: row r of 256 bf16 is 32 chunks of 16 bytes; chunk c sits at
 // slot r * 32 + (c ^ (r & 31)), so the 16 rows read by one pass of an operand
@@ -28,24 +29,33 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kB = 256;                         // block size (N = K)
-constexpr int kRows = 128;                      // rows of A per tile
 constexpr int kWaves = 8;                       // each owns 32 of the 256 columns
 constexpr int kThreads = kWaves * 64;
 constexpr int kNKK = kB / 16;                   // 16-deep K steps
 constexpr int kCPR = kB / 8;                    // 16-byte chunks per row of A
-constexpr int kStage = kRows * kB * 2;          // bytes of one A tile in LDS
-constexpr int kLoads = kRows * kCPR / kThreads; // direct-to-LDS loads per thread per tile
-constexpr int kMT = kRows / 32;                 // 32-row MFMA tiles per wave and tile
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                    (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
 }
-// Waits for every vector memory operation of this wave (the tile's loads, the
-// previous tile's stores), then for all waves: what the loads wrote is in LDS
-// and every earlier LDS read of the workgroup is done.
-__device__ __forceinline__ void tile_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Then for all waves: what the awaited loads wrote is in LDS and every earlier
+// LDS read of the workgroup is done.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Loads return in order among themselves, so allowing the loads of `younger`
+// later tiles to stay outstanding covers this tile's; epilogue stores in between
+// only make the count larger, i.e. the wait stricter, never shorter.
+template <int LOADS, int MAXY>
+__device__ __forceinline__ void wait_tile(int younger) {
+  if (MAXY >= 3 && younger >= 3) wait_vmcnt<3 * LOADS>();
+  else if (MAXY >= 2 && younger == 2) wait_vmcnt<2 * LOADS>();
+  else if (MAXY >= 1 && younger == 1) wait_vmcnt<LOADS>();
+  else wait_vmcnt<0>();
 }
 
 __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
@@ -57,10 +67,16 @@ __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
 // BKM: B(n, k) = B_g[n * ldb + k] (K-contiguous, the transposed Q); otherwise
 // B(n, k) = B_g[k * ldb + n]. Workgroup w works on block g = w / wpg and runs
 // row tiles [(w % wpg) * per_wg, + per_wg) of it, so it loads B_g only once.
-template <bool BKM>
+template <bool BKM, int ROWS, int ST>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
-  extern __shared__ __align__(16) unsigned char lds[];   // two A tiles
+  constexpr int STAGE = ROWS * kB * 2;             // bytes of one A tile in LDS
+  constexpr int LOADS = ROWS * kCPR / kThreads;    // direct-to-LDS loads per thread per tile
+  constexpr int MT = ROWS / 32;                    // 32-row MFMA tiles per wave and tile
+  constexpr int BROWS = STAGE / (kB * 2);          // rows of B_g one stage holds (NN fill)
+  static_assert(ST >= 2 && ST <= 5 && LOADS * kThreads == ROWS * kCPR && ROWS % 32 == 0, "tile");
+  static_assert(kB % BROWS == 0 && BROWS % 16 == 0, "B in whole K steps per stage");
+  extern __shared__ __align__(16) unsigned char lds[];   // ST A tiles
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = blockIdx.x / wpg;
@@ -72,13 +88,13 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
   uint16_t* Cg = static_cast<uint16_t*>(p.C) + (long long)g * p.c_gs + wave * 32;
   const int nl = lane & 31, h = lane >> 5;
   const int ncol = wave * 32 + nl;   // B column of this lane's operand fragments
-  auto stage = [&](int i) { return lds + i * kStage; };
+  auto stage = [&](int i) { return lds + i * STAGE; };
 
   // row tile t of A -> LDS stage st: lane `tid` of load i fills slot i * kThreads + tid
   auto issue = [&](int t, unsigned char* st) {
-    const long long row0 = (long long)t * kRows;
+    const long long row0 = (long long)t * ROWS;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
+    for (int i = 0; i < LOADS; ++i) {
       const int s = i * kThreads + tid;
       const int r = s / kCPR;
       const int c = (s % kCPR) ^ (r & 31);
@@ -87,70 +103,76 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
     }
   };
 
+  // the first ST - 1 tiles go out while B is fetched
+#pragma unroll
+  for (int i = 0; i < ST - 1; ++i)
+    if (t0 + i < t1) issue(t0 + i, stage(i));
   // B_g(ncol, 16 kk + 8 h .. + 7) for kk = 0 .. 15
   bf16x8 bq[kNKK];
-  issue(t0, stage(0));   // the first A tile is in flight while B is fetched
   if (BKM) {
 #pragma unroll
     for (int kk = 0; kk < kNKK; ++kk)
       bq[kk] = *reinterpret_cast<const bf16x8*>(Bg + (long long)ncol * p.ldb + 16 * kk + 8 * h);
   } else {
-    // column ncol of B_g, through the free stage: 128 rows of B_g at a time in
-    // natural layout (row k = 512 bytes); the 32 lanes of a read take 64
-    // consecutive bytes of one row
+    // column ncol of B_g through the still free last stage, BROWS rows of B_g at
+    // a time in natural layout (row k = 512 bytes); the 32 lanes of a read take
+    // 64 consecutive bytes of one row
+    const uint16_t* Bl = reinterpret_cast<const uint16_t*>(stage(ST - 1));
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int part = 0; part < kB / BROWS; ++part) {
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
+      for (int i = 0; i < LOADS; ++i) {
         const int s = i * kThreads + tid;
-        const int k = 128 * half + s / kCPR;
-        dma16(Bg + (long long)k * p.ldb + (s % kCPR) * 8, stage(1) + (i * kThreads + wave * 64) * 16);
+        const int k = part * BROWS + s / kCPR;
+        dma16(Bg + (long long)k * p.ldb + (s % kCPR) * 8, stage(ST - 1) + (i * kThreads + wave * 64) * 16);
       }
-      tile_barrier();
-      const uint16_t* Bl = reinterpret_cast<const uint16_t*>(stage(1));
+      wait_vmcnt<0>();
+      lds_barrier();
 #pragma unroll
-      for (int kk = 0; kk < kNKK / 2; ++kk) {
+      for (int kk = 0; kk < BROWS / 16; ++kk) {
         bf16x8 v;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           v[e] = __builtin_bit_cast(__bf16, Bl[(16 * kk + 8 * h + e) * kB + ncol]);
-        bq[8 * half + kk] = v;
+        bq[part * (BROWS / 16) + kk] = v;
       }
-      tile_barrier();   // every wave has read this half before the stage is reused
+      lds_barrier();   // every wave has read this part before the stage is reused
     }
   }
 
   const bool upper = h != 0;
   for (int t = t0; t < t1; ++t) {
     const int it = t - t0;
-    const unsigned char* st = stage(it & 1);
-    tile_barrier();
-    if (t + 1 < t1) issue(t + 1, stage((it + 1) & 1));
-    f32x16 acc[kMT];
+    // tiles issued after this one: t + 1 .. min(t + ST - 2, t1 - 1)
+    wait_tile<LOADS, ST - 2>(min(ST - 2, t1 - 1 - t));
+    lds_barrier();   // tile t in LDS; the stage of tile t - 1 no longer read
+    if (t + ST - 1 < t1) issue(t + ST - 1, stage((it + ST - 1) % ST));
+    const unsigned char* st = stage(it % ST);
+    f32x16 acc[MT];
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < kNKK; ++kk) {
-      bf16x8 af[kMT];
+      bf16x8 af[MT];
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         const int r = 32 * mt + nl;
         const int c = 2 * kk + h;
         af[mt] = *reinterpret_cast<const bf16x8*>(st + (r * kCPR + (c ^ (r & 31))) * 16);
       }
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
         // B first: the result is C^T, each lane holds four consecutive output
         // columns (8 q + 4 h .. + 3 of the wave's 32) of output row nl
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[kk], af[mt], acc[mt], 0, 0, 0);
     }
     // epilogue: lanes l and l ^ 32 swap half of their column groups so that each
     // lane stores 8 consecutive columns (the lower lane q = 0, 2, the upper 1, 3)
-    const long long row0 = (long long)t * kRows;
+    const long long row0 = (long long)t * ROWS;
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       uint32_t w[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -180,6 +202,9 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
   }
 }
 
+constexpr int kRows = 64;   // rows of A per tile
+constexpr int kST = 4;      // LDS stages: three 32 KiB tiles in flight
+
 }  // namespace
 
 bool block_regb_supported(const GemmBf16& p) {
@@ -195,20 +220,20 @@ hipError_t launch_block_regb(const GemmBf16& p, hipStream_t s) {
   if (!block_regb_supported(p)) return hipErrorInvalidValue;
   const long long tpg = (p.M + kRows - 1) / kRows;
   if (tpg > INT32_MAX) return hipErrorInvalidValue;
-  // one workgroup per CU (two 64 KiB stages): up to 256 / groups workgroups per
+  // one workgroup per CU (the LDS ring): up to 256 / groups workgroups per
   // block, each on consecutive row tiles of that block only
   const long long wmax = p.groups >= 256 ? 1 : 256 / p.groups;
   const long long per = (tpg + wmax - 1) / wmax;
   const long long wpg = (tpg + per - 1) / per;
   const long long wgs = wpg * p.groups;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  const size_t lds = 2 * (size_t)kStage;
+  const size_t lds = (size_t)kST * kRows * kB * 2;
   if (p.b_kmajor)
-    hipLaunchKernelGGL(block_regb_kernel<true>, dim3((unsigned)wgs), dim3(kThreads), lds, s, p,
+    hipLaunchKernelGGL((block_regb_kernel<true, kRows, kST>), dim3((unsigned)wgs), dim3(kThreads), lds, s, p,
                        (int)tpg, (int)wpg, (int)per);
   else
-    hipLaunchKernelGGL(block_regb_kernel<false>, dim3((unsigned)wgs), dim3(kThreads), lds, s, p,
-                       (int)tpg, (int)wpg, (int)per);
+    hipLaunchKernelGGL((block_regb_kernel<false, kRows, kST>), dim3((unsigned)wgs), dim3(kThreads), lds, s,
+                       p, (int)tpg, (int)wpg, (int)per);
   return hipGetLastError();
 }
 
