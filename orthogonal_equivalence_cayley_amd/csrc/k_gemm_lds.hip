@@ -293,8 +293,20 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   }
   const int wlin = (!p.xcd_cluster && nwg % 8 == 0) ? (bx % 8) * (nwg / 8) + bx / 8 : bx;
   const int tpw = p.tpw;
-  const int t_first = wlin * tpw;
-  const int t_count = max(0, min(tpw, ntile - t_first));
+  // this workgroup's tiles: t_first + i * t_step, i < t_count
+  int t_first, t_step, t_count;
+  if (p.xcd_stride) {
+    const int x = bx % 8, sx = bx / 8;
+    const int nx = nwg / 8 + (x < nwg % 8 ? 1 : 0);
+    const int base = (int)((long long)ntile * x / 8), end = (int)((long long)ntile * (x + 1) / 8);
+    t_first = base + sx;
+    t_step = nx;
+    t_count = t_first < end ? (end - t_first + nx - 1) / nx : 0;
+  } else {
+    t_first = wlin * tpw;
+    t_step = 1;
+    t_count = max(0, min(tpw, ntile - t_first));
+  }
   auto tile_origin = [&](int lin, int& m0, int& n0) {
     const int grp = lin / (GM * tn);
     const int first = grp * GM;
@@ -389,7 +401,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   if (nk == 0) {   // empty K range of a split: its partial sums are zero
     for (int i = 0; i < t_count; ++i) {
       int m0, n0;
-      tile_origin(t_first + i, m0, n0);
+      tile_origin(t_first + i * t_step, m0, n0);
       store_tile(m0, n0);
     }
     return;
@@ -411,7 +423,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
       iss_kt = 0;
       ++iss_ti;
       int nm0, nn0;
-      tile_origin(t_first + iss_ti, nm0, nn0);
+      tile_origin(t_first + iss_ti * t_step, nm0, nn0);
       ta.init(A, p.lda, nm0, p.M);
       tb.init(B, p.ldb, nn0, p.N);
     }
@@ -498,7 +510,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
           for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
       kt = 0;
       ++ti;
-      if (ti < t_count) tile_origin(t_first + ti, cm0, cn0);
+      if (ti < t_count) tile_origin(t_first + ti * t_step, cm0, cn0);
     }
   }
   (void)LOADS;
@@ -535,7 +547,7 @@ template <int BM, int BN, int WM, int WN, int KB, int ST>
 hipError_t dispatch_lds(const GemmBf16& p, hipStream_t s) {
   constexpr int NW = (BM / WM) * (BN / WN);
   const int ntile = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
-  dim3 grid((ntile + p.tpw - 1) / p.tpw, 1, p.groups * p.splits);
+  dim3 grid(p.xcd_stride ? std::min(ntile, 256) : (ntile + p.tpw - 1) / p.tpw, 1, p.groups * p.splits);
   // ST LDS stages of (BM + BN) x KB bf16
   const size_t lds = ST * (size_t)(BM + BN) * KB * 2;
   const int a = p.a_kmajor, b = p.b_kmajor, f = p.out_f32;
@@ -595,6 +607,7 @@ hipError_t launch_gemm_lds(const GemmBf16& p_in, int big, hipStream_t s) {
   p.tpw = (int)tpw;
   p.xcd_cluster = (tpw == 1 && ntile <= 16 && (p.groups * p.splits) % 8 == 0 &&
                    p.role == GEMM_DQ) ? 1 : 0;
+  p.xcd_stride = (big && p.role == GEMM_W0 && p.groups * p.splits == 1 && ntile >= 256) ? 1 : 0;
   if (big) return dispatch_lds<256, 256, 128, 64, 64, 2>(p, s);
   return dispatch_lds<128, 128, 64, 64, 64, 2>(p, s);
 }

@@ -97,6 +97,11 @@ struct GemmBf16 {
   // the tiles of one (group, split) run on one XCD (they share A and B rows in
   // its L2): set by the launcher when tpw == 1 and groups * splits % 8 == 0
   int xcd_cluster = 0;
+  // single-group launches with >= 256 tiles: 256 workgroups; the tiles of XCD x
+  // are the contiguous range [ntile x / 8, ntile (x + 1) / 8), walked by its
+  // workgroups with a stride of their count, so those resident together take
+  // consecutive tiles (set by the launcher)
+  int xcd_stride = 0;
 };
 hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
 // Pipelined variant (direct-to-LDS loads, see k_gemm_lds.hip) for whole-tile shapes:
