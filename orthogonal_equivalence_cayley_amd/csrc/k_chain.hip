@@ -54,7 +54,7 @@ __device__ __forceinline__ ChainEntry select_entry(const ChainBatch& cb) {
 // B operand prefetched U K-steps (of 4) ahead. The panel sits in LDS with pitch
 // b + 4 floats: the 16 rows of an A-operand read fall in distinct banks.
 template <int MODE, int NT, int MT, int U>
-__global__ __launch_bounds__(kThreads) void chain_kernel(ChainBatch cb) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chain_kernel(ChainBatch cb) {
   constexpr int RP = 16 * MT;
   extern __shared__ __align__(16) float lds[];
   const ChainEntry p = select_entry(cb);
