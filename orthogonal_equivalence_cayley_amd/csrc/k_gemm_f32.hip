@@ -1,6 +1,7 @@
 // fp32 batched GEMM with general element strides. It serves the fp32 layer
-// mode end to end and the b x b power chains of the Cayley-Neumann build and its
-// backward, where every product must keep fp32 accuracy.
+// mode end to end, the exact Cayley transform, the merge, and the b x b power
+// chains of block sizes the fused chain kernel does not take, where every
+// product must keep fp32 accuracy.
 //
 // C(m,n) = alpha * sum_k A(m,k) B(n,k) + beta * Cin(m,n) + gamma * [m == n]
 // E(m,n) = sum_k A(m,k) B(n,k)                        (optional second output)
@@ -81,10 +82,130 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmF32 p) {
   }
 }
 
+// The same product on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32
+// inputs and accumulation) for operands with a unit stride along K or along
+// their rows: 64 x 64 tiles, 32-deep K steps staged in LDS, 4 waves of 2 x 2
+// 16 x 16 tiles. The loads run along the operand's contiguous dimension.
+constexpr int MB = 64, MK = 32, MPAD = MB + 4;
+
+template <bool AKC, bool BKC>
+__global__ __launch_bounds__(kThreads) void gemm_f32_mfma_kernel(GemmF32 p) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ float As[MK][MPAD];
+  __shared__ float Bs[MK][MPAD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int n0 = blockIdx.x * MB, m0 = blockIdx.y * MB;
+  const int g = blockIdx.z / p.splits, sp = blockIdx.z - g * p.splits;
+  const float* A = p.A + g * p.a_gs;
+  const float* B = p.B + g * p.b_gs;
+  int kchunk = (p.K + p.splits - 1) / p.splits;
+  kchunk = (kchunk + MK - 1) / MK * MK;
+  const int kbeg = sp * kchunk;
+  const int kend = min(p.K, kbeg + kchunk);
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const int li = lane & 15, lq = lane >> 4;
+  // MB x MK elements per operand and K step, PER per thread, consecutive threads
+  // along the contiguous dimension; the next step's values are loaded into
+  // registers while the current step is multiplied
+  constexpr int PER = MB * MK / kThreads;
+  float ra[PER], rb[PER];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kThreads;
+      int mm, kk;
+      if (AKC) { kk = e % MK; mm = e / MK; } else { mm = e % MB; kk = e / MB; }
+      const int gm = m0 + mm, gk = k0 + kk;
+      ra[i] = (gm < p.M && gk < kend) ? A[gm * p.a_rs + gk * p.a_cs] : 0.0f;
+      int nn, kb;
+      if (BKC) { kb = e % MK; nn = e / MK; } else { nn = e % MB; kb = e / MB; }
+      const int gn = n0 + nn, gkb = k0 + kb;
+      rb[i] = (gn < p.N && gkb < kend) ? B[gn * p.b_rs + gkb * p.b_cs] : 0.0f;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kThreads;
+      int mm, kk;
+      if (AKC) { kk = e % MK; mm = e / MK; } else { mm = e % MB; kk = e / MB; }
+      As[kk][mm] = ra[i];
+      int nn, kb;
+      if (BKC) { kb = e % MK; nn = e / MK; } else { nn = e % MB; kb = e / MB; }
+      Bs[kb][nn] = rb[i];
+    }
+  };
+  if (kbeg < kend) load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += MK) {
+    store();
+    __syncthreads();
+    if (k0 + MK < kend) load(k0 + MK);
+#pragma unroll
+    for (int kq = 0; kq < MK / 4; ++kq) {
+      const int k = 4 * kq + lq;
+      float a[2], b[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        a[t] = As[k][32 * wr + 16 * t + li];
+        b[t] = Bs[k][32 * wc + 16 * t + li];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // lane l holds rows 4 (l / 16) + r (r = 0..3) of column l % 16 of each 16 x 16 tile
+  float* C = p.C + g * p.c_gs + sp * p.c_ss;
+  const float* Cin = p.Cin ? p.Cin + g * p.c_gs : nullptr;
+  float* E = p.E ? p.E + g * p.c_gs : nullptr;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + 32 * wc + 16 * j + li;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 32 * wr + 16 * i + 4 * lq + r;
+        if (m >= p.M) continue;
+        const long long o = (long long)m * p.c_rs + n;
+        const float x = acc[i][j][r];
+        float v = p.alpha * x;
+        if (p.splits == 1) {
+          if (Cin) v += p.beta * Cin[o];
+          if (m == n) v += p.gamma;
+          if (E) E[o] = x;
+        }
+        C[o] = v;
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_f32(const GemmF32& p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || p.groups <= 0) return hipSuccess;
+  const bool akc = p.a_cs == 1, arc = p.a_rs == 1;
+  const bool bkc = p.b_cs == 1, brc = p.b_rs == 1;
+  if ((akc || arc) && (bkc || brc)) {
+    dim3 grid((p.N + MB - 1) / MB, (p.M + MB - 1) / MB, p.groups * p.splits);
+    if (akc && bkc) hipLaunchKernelGGL((gemm_f32_mfma_kernel<true, true>), grid, dim3(kThreads), 0, s, p);
+    else if (akc) hipLaunchKernelGGL((gemm_f32_mfma_kernel<true, false>), grid, dim3(kThreads), 0, s, p);
+    else if (bkc) hipLaunchKernelGGL((gemm_f32_mfma_kernel<false, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((gemm_f32_mfma_kernel<false, false>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+  }
   dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, p.groups * p.splits);
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
