@@ -84,13 +84,15 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmF32 p) {
 
 // The same product on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32
 // inputs and accumulation) for operands with a unit stride along K or along
-// their rows: 64 x 64 tiles, 32-deep K steps staged in LDS, 4 waves of 2 x 2
-// 16 x 16 tiles. The loads run along the operand's contiguous dimension.
-constexpr int MB = 64, MK = 32, MPAD = MB + 4;
+// their rows: MB x MB tiles (64, or 32 when the grid would not fill the chip),
+// 32-deep K steps staged in LDS, 4 waves each owning MB/32 x MB/32 tiles of
+// 16 x 16. The loads run along the operand's contiguous dimension.
+constexpr int MK = 32;
 
-template <bool AKC, bool BKC>
+template <bool AKC, bool BKC, int MB>
 __global__ __launch_bounds__(kThreads) void gemm_f32_mfma_kernel(GemmF32 p) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int MPAD = MB + 4, TW = MB / 32;   // 16 x 16 tiles per wave and dimension
   __shared__ float As[MK][MPAD];
   __shared__ float Bs[MK][MPAD];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -105,11 +107,11 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_mfma_kernel(GemmF32 p) {
   const int kbeg = sp * kchunk;
   const int kend = min(p.K, kbeg + kchunk);
 
-  f32x4 acc[2][2];
+  f32x4 acc[TW][TW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < TW; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int li = lane & 15, lq = lane >> 4;
   // MB x MK elements per operand and K step, PER per thread, consecutive threads
   // along the contiguous dimension; the next step's values are loaded into
@@ -150,16 +152,16 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_mfma_kernel(GemmF32 p) {
 #pragma unroll
     for (int kq = 0; kq < MK / 4; ++kq) {
       const int k = 4 * kq + lq;
-      float a[2], b[2];
+      float a[TW], b[TW];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        a[t] = As[k][32 * wr + 16 * t + li];
-        b[t] = Bs[k][32 * wc + 16 * t + li];
+      for (int t = 0; t < TW; ++t) {
+        a[t] = As[k][16 * TW * wr + 16 * t + li];
+        b[t] = Bs[k][16 * TW * wc + 16 * t + li];
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TW; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TW; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
@@ -170,14 +172,14 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_mfma_kernel(GemmF32 p) {
   const float* Cin = p.Cin ? p.Cin + g * p.c_gs : nullptr;
   float* E = p.E ? p.E + g * p.c_gs : nullptr;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + 32 * wc + 16 * j + li;
+    for (int j = 0; j < TW; ++j) {
+      const int n = n0 + 16 * TW * wc + 16 * j + li;
       if (n >= p.N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 32 * wr + 16 * i + 4 * lq + r;
+        const int m = m0 + 16 * TW * wr + 16 * i + 4 * lq + r;
         if (m >= p.M) continue;
         const long long o = (long long)m * p.c_rs + n;
         const float x = acc[i][j][r];
@@ -192,6 +194,16 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_mfma_kernel(GemmF32 p) {
     }
 }
 
+template <int MB>
+hipError_t launch_mfma(const GemmF32& p, bool akc, bool bkc, hipStream_t s) {
+  dim3 grid((p.N + MB - 1) / MB, (p.M + MB - 1) / MB, p.groups * p.splits);
+  if (akc && bkc) hipLaunchKernelGGL((gemm_f32_mfma_kernel<true, true, MB>), grid, dim3(kThreads), 0, s, p);
+  else if (akc) hipLaunchKernelGGL((gemm_f32_mfma_kernel<true, false, MB>), grid, dim3(kThreads), 0, s, p);
+  else if (bkc) hipLaunchKernelGGL((gemm_f32_mfma_kernel<false, true, MB>), grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((gemm_f32_mfma_kernel<false, false, MB>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_f32(const GemmF32& p, hipStream_t s) {
@@ -199,12 +211,9 @@ hipError_t launch_gemm_f32(const GemmF32& p, hipStream_t s) {
   const bool akc = p.a_cs == 1, arc = p.a_rs == 1;
   const bool bkc = p.b_cs == 1, brc = p.b_rs == 1;
   if ((akc || arc) && (bkc || brc)) {
-    dim3 grid((p.N + MB - 1) / MB, (p.M + MB - 1) / MB, p.groups * p.splits);
-    if (akc && bkc) hipLaunchKernelGGL((gemm_f32_mfma_kernel<true, true>), grid, dim3(kThreads), 0, s, p);
-    else if (akc) hipLaunchKernelGGL((gemm_f32_mfma_kernel<true, false>), grid, dim3(kThreads), 0, s, p);
-    else if (bkc) hipLaunchKernelGGL((gemm_f32_mfma_kernel<false, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((gemm_f32_mfma_kernel<false, false>), grid, dim3(kThreads), 0, s, p);
-    return hipGetLastError();
+    const long long g64 = (long long)((p.N + 63) / 64) * ((p.M + 63) / 64) * p.groups * p.splits;
+    if (g64 >= 512) return launch_mfma<64>(p, akc, bkc, s);
+    return launch_mfma<32>(p, akc, bkc, s);
   }
   dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, p.groups * p.splits);
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(kThreads), 0, s, p);
