@@ -67,7 +67,7 @@ __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
 // BKM: B(n, k) = B_g[n * ldb + k] (K-contiguous, the transposed Q); otherwise
 // B(n, k) = B_g[k * ldb + n]. Workgroup w works on block g = w / wpg and runs
 // row tiles [(w % wpg) * per_wg, + per_wg) of it, so it loads B_g only once.
-template <bool BKM, int ROWS, int ST>
+template <bool BKM, int ROWS, int ST, bool SCALE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
   constexpr int STAGE = ROWS * kB * 2;             // bytes of one A tile in LDS
@@ -176,8 +176,11 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
       uint32_t w[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        w[q][0] = pack_bf16_pair(acc[mt][4 * q], acc[mt][4 * q + 1]);
-        w[q][1] = pack_bf16_pair(acc[mt][4 * q + 2], acc[mt][4 * q + 3]);
+        float4 sc = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        if (SCALE)   // column n scaled by col_scale[g * c_gs + n] before the rounding
+          sc = *reinterpret_cast<const float4*>(p.col_scale + (long long)g * p.c_gs + wave * 32 + 8 * q + 4 * h);
+        w[q][0] = pack_bf16_pair(acc[mt][4 * q] * sc.x, acc[mt][4 * q + 1] * sc.y);
+        w[q][1] = pack_bf16_pair(acc[mt][4 * q + 2] * sc.z, acc[mt][4 * q + 3] * sc.w);
       }
       const long long m = row0 + 32 * mt + nl;
 #pragma unroll
@@ -209,7 +212,8 @@ constexpr int kST = 4;      // LDS stages: three 32 KiB tiles in flight
 
 bool block_regb_supported(const GemmBf16& p) {
   if (p.role != GEMM_BLOCK || p.N != kB || p.K != kB || !p.a_kmajor || p.out_f32) return false;
-  if (p.splits != 1 || p.b_i8 || p.col_scale || p.M <= 0 || p.groups <= 0) return false;
+  if (p.splits != 1 || p.b_i8 || p.M <= 0 || p.groups <= 0) return false;
+  if (p.col_scale && (((uintptr_t)p.col_scale & 15) || p.c_gs % 4)) return false;
   if (p.lda % 8 || p.a_gs % 8 || p.ldc % 8 || p.c_gs % 8) return false;   // 16-byte rows
   if (p.ldb % 8 || p.ldb < kB) return false;   // 16-byte rows of B either way
   if (((uintptr_t)p.A | (uintptr_t)p.C | (uintptr_t)p.B) & 15) return false;
@@ -228,12 +232,16 @@ hipError_t launch_block_regb(const GemmBf16& p, hipStream_t s) {
   const long long wgs = wpg * p.groups;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   const size_t lds = (size_t)kST * kRows * kB * 2;
-  if (p.b_kmajor)
-    hipLaunchKernelGGL((block_regb_kernel<true, kRows, kST>), dim3((unsigned)wgs), dim3(kThreads), lds, s, p,
-                       (int)tpg, (int)wpg, (int)per);
+  const dim3 grid((unsigned)wgs), block(kThreads);
+  const int a = (int)tpg, b = (int)wpg, c = (int)per;
+  if (p.b_kmajor && p.col_scale)
+    hipLaunchKernelGGL((block_regb_kernel<true, kRows, kST, true>), grid, block, lds, s, p, a, b, c);
+  else if (p.b_kmajor)
+    hipLaunchKernelGGL((block_regb_kernel<true, kRows, kST, false>), grid, block, lds, s, p, a, b, c);
+  else if (p.col_scale)
+    hipLaunchKernelGGL((block_regb_kernel<false, kRows, kST, true>), grid, block, lds, s, p, a, b, c);
   else
-    hipLaunchKernelGGL((block_regb_kernel<false, kRows, kST>), dim3((unsigned)wgs), dim3(kThreads), lds, s,
-                       p, (int)tpg, (int)wpg, (int)per);
+    hipLaunchKernelGGL((block_regb_kernel<false, kRows, kST, false>), grid, block, lds, s, p, a, b, c);
   return hipGetLastError();
 }
 

@@ -109,7 +109,8 @@ hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
 bool gemm_lds_supported(const GemmBf16& p, int bm, int bn);
 hipError_t launch_gemm_lds(const GemmBf16& p, int big, hipStream_t s);
 // Block products with b = 256 (N = K = 256, GEMM_BLOCK, A K-contiguous, bf16
-// output): B in registers, A tiles streamed through LDS (k_block_regb.hip).
+// output, optional column scale): B in registers, A tiles streamed through LDS
+// (k_block_regb.hip).
 bool block_regb_supported(const GemmBf16& p);
 hipError_t launch_block_regb(const GemmBf16& p, hipStream_t s);
 
