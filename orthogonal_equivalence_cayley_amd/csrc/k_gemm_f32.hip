@@ -5,6 +5,8 @@
 //
 // C(m,n) = alpha * sum_k A(m,k) B(n,k) + beta * Cin(m,n) + gamma * [m == n]
 // E(m,n) = sum_k A(m,k) B(n,k)                        (optional second output)
+#include <algorithm>
+
 #include "poetx_internal.h"
 
 namespace poetx {
@@ -89,8 +91,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmF32 p) {
 // 16 x 16. The loads run along the operand's contiguous dimension.
 constexpr int MK = 32;
 
+// gz: group and split of this workgroup (g * splits + split)
 template <bool AKC, bool BKC, int MB>
-__global__ __launch_bounds__(kThreads) void gemm_f32_mfma_kernel(GemmF32 p) {
+__device__ __forceinline__ void gemm_f32_mfma_body(const GemmF32& p, int gz) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   constexpr int MPAD = MB + 4, TW = MB / 32;   // 16 x 16 tiles per wave and dimension
   __shared__ float As[MK][MPAD];
@@ -99,7 +102,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_mfma_kernel(GemmF32 p) {
   const int wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int n0 = blockIdx.x * MB, m0 = blockIdx.y * MB;
-  const int g = blockIdx.z / p.splits, sp = blockIdx.z - g * p.splits;
+  if (n0 >= p.N || m0 >= p.M) return;
+  const int g = gz / p.splits, sp = gz - g * p.splits;
   const float* A = p.A + g * p.a_gs;
   const float* B = p.B + g * p.b_gs;
   int kchunk = (p.K + p.splits - 1) / p.splits;
@@ -194,6 +198,25 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_mfma_kernel(GemmF32 p) {
     }
 }
 
+template <bool AKC, bool BKC, int MB>
+__global__ __launch_bounds__(kThreads) void gemm_f32_mfma_kernel(GemmF32 p) {
+  gemm_f32_mfma_body<AKC, BKC, MB>(p, blockIdx.z);
+}
+
+// Several runs of the same shape and strides in one launch: blockIdx.z walks
+// the groups of run 0, then of run 1, ...
+template <bool AKC, bool BKC, int MB>
+__global__ __launch_bounds__(kThreads) void gemm_f32_mfma_runs_kernel(GemmF32Runs rr) {
+  int r = 0;
+#pragma unroll
+  for (int i = 1; i < kF32MaxRuns; ++i)
+    if (i < rr.n && (int)blockIdx.z >= rr.z0[i]) r = i;
+  GemmF32 p = rr.p;
+  p.A = rr.r[r].A; p.B = rr.r[r].B; p.C = rr.r[r].C; p.Cin = rr.r[r].Cin; p.E = nullptr;
+  p.groups = rr.r[r].groups;
+  gemm_f32_mfma_body<AKC, BKC, MB>(p, blockIdx.z - rr.z0[r]);
+}
+
 template <int MB>
 hipError_t launch_mfma(const GemmF32& p, bool akc, bool bkc, hipStream_t s) {
   dim3 grid((p.N + MB - 1) / MB, (p.M + MB - 1) / MB, p.groups * p.splits);
@@ -218,6 +241,48 @@ hipError_t launch_gemm_f32(const GemmF32& p, hipStream_t s) {
   dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, p.groups * p.splits);
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32_runs(const GemmF32& shape, const GemmF32Run* runs, int n, hipStream_t s) {
+  const bool akc = shape.a_cs == 1, arc = shape.a_rs == 1;
+  const bool bkc = shape.b_cs == 1, brc = shape.b_rs == 1;
+  if (shape.M <= 0 || shape.N <= 0 || shape.splits != 1) return hipErrorInvalidValue;
+  if (!((akc || arc) && (bkc || brc))) {   // one launch per run on the generic kernel
+    for (int i = 0; i < n; ++i) {
+      GemmF32 p = shape;
+      p.A = runs[i].A; p.B = runs[i].B; p.C = runs[i].C; p.Cin = runs[i].Cin; p.E = nullptr;
+      p.groups = runs[i].groups;
+      const hipError_t e = launch_gemm_f32(p, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  for (int i0 = 0; i0 < n; i0 += kF32MaxRuns) {
+    GemmF32Runs rr{};
+    rr.p = shape;
+    rr.n = std::min(kF32MaxRuns, n - i0);
+    int z = 0;
+    for (int i = 0; i < rr.n; ++i) {
+      rr.r[i] = runs[i0 + i];
+      rr.z0[i] = z;
+      z += runs[i0 + i].groups;
+    }
+    if (z == 0) continue;
+    const long long g64 = (long long)((shape.N + 63) / 64) * ((shape.M + 63) / 64) * z;
+    const bool big = g64 >= 512;
+    const int mb = big ? 64 : 32;
+    dim3 grid((shape.N + mb - 1) / mb, (shape.M + mb - 1) / mb, z);
+#define POETX_F32_RUNS(MBV)                                                                              \
+  if (akc && bkc) hipLaunchKernelGGL((gemm_f32_mfma_runs_kernel<true, true, MBV>), grid, dim3(kThreads), 0, s, rr); \
+  else if (akc) hipLaunchKernelGGL((gemm_f32_mfma_runs_kernel<true, false, MBV>), grid, dim3(kThreads), 0, s, rr); \
+  else if (bkc) hipLaunchKernelGGL((gemm_f32_mfma_runs_kernel<false, true, MBV>), grid, dim3(kThreads), 0, s, rr); \
+  else hipLaunchKernelGGL((gemm_f32_mfma_runs_kernel<false, false, MBV>), grid, dim3(kThreads), 0, s, rr);
+    if (big) { POETX_F32_RUNS(64) } else { POETX_F32_RUNS(32) }
+#undef POETX_F32_RUNS
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace poetx

@@ -326,48 +326,78 @@ poetx_status chain_gemm(const Seg& g, const float* X, const float* Y, float* C, 
   return POETX_OK;
 }
 
-// fp32 batched b x b product over a run of blocks with explicit strides:
-// C(m, n) = sum_k A[m * a_rs + k * a_cs] B[n * b_rs + k * b_cs] + beta * Cin(m, n).
-poetx_status run_gemm_f32(const Seg& g, const float* A, long long a_rs, long long a_cs, const float* B,
-                          long long b_rs, long long b_cs, float* C, const float* Cin, float beta,
-                          hipStream_t s) {
+// Exact Cayley transform without a solve: (I - S)^{-1} = prod_{i < F} (I + S^(2^i))
+// up to S^(2^F) (F = 6: 64 terms of the series, 11 products instead of 63), then
+// Q = (I + S) N. Exact to fp32 while ||S||_2 <= 0.75.
+constexpr int kExactFactors = 6;
+
+// One run of the exact transform: one segment of one side; every pointer is at
+// the segment's first block. N is set by exact_cayley_runs (X0 or X1).
+struct ExactRun {
+  Seg g;
+  const float* theta;   // the side's packed parameters (segment offset applied by the unpack)
+  float *S, *P0, *P1, *X0, *X1, *Q, *N;
+};
+
+// Batched product over runs of one block size b: C_r = A_r B_r (+ beta Cin_r),
+// all b x b row-major, A(m, k) = A_r[m * a_rs + k * a_cs], B(n, k) =
+// B_r[n * b_rs + k * b_cs].
+poetx_status f32_runs(int b, long long a_rs, long long a_cs, long long b_rs, long long b_cs,
+                      const std::vector<poetx::GemmF32Run>& runs, float beta, hipStream_t s) {
   poetx::GemmF32 p{};
-  p.A = A + g.q_off; p.B = B + g.q_off; p.C = C + g.q_off;
-  p.Cin = Cin ? Cin + g.q_off : nullptr;
-  p.M = p.N = p.K = g.b;
-  p.a_rs = a_rs; p.a_cs = a_cs; p.b_rs = b_rs; p.b_cs = b_cs; p.c_rs = g.b;
-  p.a_gs = p.b_gs = p.c_gs = (long long)g.b * g.b;
-  p.groups = g.count; p.splits = 1;
+  p.M = p.N = p.K = b;
+  p.a_rs = a_rs; p.a_cs = a_cs; p.b_rs = b_rs; p.b_cs = b_cs; p.c_rs = b;
+  p.a_gs = p.b_gs = p.c_gs = (long long)b * b;
+  p.splits = 1;
   p.alpha = 1.0f; p.beta = beta;
-  HIP_TRY(poetx::launch_gemm_f32(p, s));
+  HIP_TRY(poetx::launch_gemm_f32_runs(p, runs.data(), (int)runs.size(), s));
   return POETX_OK;
 }
 
-// Exact Cayley transform of every block of one run, without a solve:
-// (I - S)^{-1} = prod_{i < F} (I + S^(2^i)) up to S^(2^F) (F = 6: 64 terms of the
-// series, 11 products instead of 63), then Q = (I + S) N. Exact to fp32 while
-// ||S||_2 <= 0.75. N is left in *N_out (one of X0 / X1).
-constexpr int kExactFactors = 6;
-poetx_status exact_cayley_run(const Seg& g, const float* theta, float* S, float* P0, float* P1,
-                              float* X0, float* X1, float* Q, float** N_out, hipStream_t s) {
-  HIP_TRY(poetx::launch_unpack_skew(theta, g, S, X0, 1.0f, s));   // X = I + S
-  const long long b = g.b;
-  const float* P = S;
-  float* pw[2] = {P0, P1};
-  float *X = X0, *Xn = X1;
-  poetx_status st;
-  for (int i = 1; i < kExactFactors; ++i) {
-    float* Pn = pw[i & 1];
-    // S^(2^i) = (S^(2^(i-1)))^2
-    if ((st = run_gemm_f32(g, P, b, 1, P, 1, b, Pn, nullptr, 0.0f, s)) != POETX_OK) return st;
-    // X (I + S^(2^i)) = X + X S^(2^i)
-    if ((st = run_gemm_f32(g, X, b, 1, Pn, 1, b, Xn, X, 1.0f, s)) != POETX_OK) return st;
-    P = Pn;
-    std::swap(X, Xn);
+// The exact transform of many runs at once: each of its 11 products is one
+// launch over all runs of a block size (a single side has too few blocks to fill
+// the chip). X ends as N = (I - S)^{-1} in X0 or X1 (r.N).
+poetx_status exact_cayley_runs(std::vector<ExactRun>& runs, hipStream_t s) {
+  std::vector<int> sizes;
+  for (const ExactRun& r : runs)
+    if (std::find(sizes.begin(), sizes.end(), r.g.b) == sizes.end()) sizes.push_back(r.g.b);
+  for (int b : sizes) {
+    std::vector<ExactRun*> rs;
+    for (ExactRun& r : runs)
+      if (r.g.b == b) rs.push_back(&r);
+    const size_t n = rs.size();
+    std::vector<const float*> P(n);
+    std::vector<float*> X(n), Xn(n);
+    for (size_t i = 0; i < n; ++i) {
+      ExactRun& r = *rs[i];
+      // X = I + S; the unpack takes base pointers and applies the segment offset
+      HIP_TRY(poetx::launch_unpack_skew(r.theta, r.g, r.S - r.g.q_off, r.X0 - r.g.q_off, 1.0f, s));
+      P[i] = r.S;
+      X[i] = r.X0;
+      Xn[i] = r.X1;
+    }
+    std::vector<poetx::GemmF32Run> v(n);
+    poetx_status st;
+    for (int f = 1; f < kExactFactors; ++f) {
+      // S^(2^f) = (S^(2^(f-1)))^2
+      for (size_t i = 0; i < n; ++i) {
+        float* Pn = (f & 1) ? rs[i]->P1 : rs[i]->P0;
+        v[i] = poetx::GemmF32Run{P[i], P[i], Pn, nullptr, rs[i]->g.count};
+      }
+      if ((st = f32_runs(b, b, 1, 1, b, v, 0.0f, s)) != POETX_OK) return st;
+      // X (I + S^(2^f)) = X + X S^(2^f)
+      for (size_t i = 0; i < n; ++i) {
+        P[i] = v[i].C;
+        v[i] = poetx::GemmF32Run{X[i], P[i], Xn[i], X[i], rs[i]->g.count};
+      }
+      if ((st = f32_runs(b, b, 1, 1, b, v, 1.0f, s)) != POETX_OK) return st;
+      for (size_t i = 0; i < n; ++i) std::swap(X[i], Xn[i]);
+    }
+    // Q = (I + S) N = N + S N
+    for (size_t i = 0; i < n; ++i) v[i] = poetx::GemmF32Run{rs[i]->S, X[i], rs[i]->Q, X[i], rs[i]->g.count};
+    if ((st = f32_runs(b, b, 1, 1, b, v, 1.0f, s)) != POETX_OK) return st;
+    for (size_t i = 0; i < n; ++i) rs[i]->N = X[i];
   }
-  // Q = (I + S) N = N + S N
-  if ((st = run_gemm_f32(g, S, b, 1, X, 1, b, Q, X, 1.0f, s)) != POETX_OK) return st;
-  *N_out = X;
   return POETX_OK;
 }
 
@@ -514,24 +544,21 @@ poetx_status grad_items(const GradItem* items, int count, hipStream_t s) {
     }
   }
   if ((st = flush()) != POETX_OK) return st;
+  std::vector<ExactRun> exact;
+  std::vector<int> exact_items;
   for (int i = 0; i < count; ++i) {
     const GradItem& it = items[i];
     const poetx_plan* pl = it.pl;
     const int side = it.side, k = pl->k;
     if (pl->cayley == POETX_CAYLEY_EXACT) {
       // exact transform: rebuild N = (I - S)^{-1} and Q, then
-      // dL/dS = (I + Q)^T G N^T and g(i, j) = dS[i][j] - dS[j][i]
+      // dL/dS = (I + Q)^T G N^T and g(i, j) = dS[i][j] - dS[j][i] (batched below)
       const ChainWs& w = it.w;
       for (const Seg& g : pl->segs[side]) {
-        const long long b = g.b;
-        float* N;
-        if ((st = exact_cayley_run(g, it.theta, w.S, w.A0, w.A1, w.T0, w.T1, w.T, &N, s)) != POETX_OK)
-          return st;
-        // A = Q^T G + G   (A(m, k) = Q[k][m])
-        if ((st = run_gemm_f32(g, w.T, 1, b, it.dQ, 1, b, w.A, it.dQ, 1.0f, s)) != POETX_OK) return st;
-        // D = A N^T       (B(n, k) = N[n][k]); into the Q buffer, free now
-        if ((st = run_gemm_f32(g, w.A, b, 1, N, b, 1, w.T, nullptr, 0.0f, s)) != POETX_OK) return st;
-        HIP_TRY(poetx::launch_pack_antisym(w.T, g, 1.0f, it.g, s));
+        const long long o = g.q_off;
+        exact.push_back(ExactRun{g, it.theta, w.S + o, w.A0 + o, w.A1 + o, w.T0 + o, w.T1 + o, w.T + o,
+                                 nullptr});
+        exact_items.push_back(i);
       }
       continue;
     }
@@ -562,6 +589,30 @@ poetx_status grad_items(const GradItem* items, int count, hipStream_t s) {
     for (const Seg& g : pl->segs[side])
       if (!poetx::chain_supported(g.b))
         HIP_TRY(poetx::launch_pack_antisym(Tcur, g, 1.0f, it.g, s));
+  }
+  if (exact.empty()) return POETX_OK;
+  if ((st = exact_cayley_runs(exact, s)) != POETX_OK) return st;
+  std::vector<int> sizes;
+  for (const ExactRun& r : exact)
+    if (std::find(sizes.begin(), sizes.end(), r.g.b) == sizes.end()) sizes.push_back(r.g.b);
+  for (int b : sizes) {
+    std::vector<poetx::GemmF32Run> v1, v2;
+    for (size_t i = 0; i < exact.size(); ++i) {
+      const ExactRun& r = exact[i];
+      if (r.g.b != b) continue;
+      const GradItem& it = items[exact_items[i]];
+      const long long o = r.g.q_off;
+      // A = Q^T G + G (A(m, k) = Q[k][m]), into the stored-A buffer
+      v1.push_back(poetx::GemmF32Run{r.Q, it.dQ + o, it.w.A + o, it.dQ + o, r.g.count});
+      // D = A N^T (B(n, k) = N[n][k]), into the Q buffer, free now
+      v2.push_back(poetx::GemmF32Run{it.w.A + o, r.N, r.Q, nullptr, r.g.count});
+    }
+    if ((st = f32_runs(b, 1, b, 1, b, v1, 1.0f, s)) != POETX_OK) return st;
+    if ((st = f32_runs(b, b, 1, b, 1, v2, 0.0f, s)) != POETX_OK) return st;
+  }
+  for (size_t i = 0; i < exact.size(); ++i) {
+    const ExactRun& r = exact[i];
+    HIP_TRY(poetx::launch_pack_antisym(r.Q - r.g.q_off, r.g, 1.0f, items[exact_items[i]].g, s));
   }
   return POETX_OK;
 }
@@ -699,6 +750,8 @@ poetx_status check_build_item(const BuildItem& it, size_t ws_bytes) {
 poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
   poetx::TriBatch ub{};
   poetx::ChainBatch cb{};
+  std::vector<ExactRun> exact;
+  std::vector<int> exact_items;
   int kk = -1;
   auto flush = [&]() -> poetx_status {
     HIP_TRY(poetx::launch_unpack_batch(ub, s));
@@ -709,17 +762,13 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
   for (int i = 0; i < count; ++i) {
     const BuildItem& it = items[i];
     const poetx_plan* pl = it.pl;
-    if (pl->cayley == POETX_CAYLEY_EXACT) {
-      float *S, *P0, *P1, *X0, *X1, *N;
+    if (pl->cayley == POETX_CAYLEY_EXACT) {   // batched after the loop
+      float *S, *P0, *P1, *X0, *X1;
       layout_build(pl, it.ws, &S, &P0, &P1, &X0, &X1);
-      const bool bf16 = pl->dtype == POETX_BF16;
-      const int es = elsize(pl);
       for (const Seg& g : pl->segs[it.side]) {
-        poetx_status st = exact_cayley_run(g, it.theta, S, P0, P1, X0, X1, it.Q, &N, s);
-        if (st != POETX_OK) return st;
-        if (it.Qact)
-          HIP_TRY(poetx::launch_cast(it.Q + g.q_off, static_cast<char*>(it.Qact) + es * g.q_off,
-                                     (long long)g.b * g.b * g.count, bf16, s));
+        const long long o = g.q_off;
+        exact.push_back(ExactRun{g, it.theta, S + o, P0 + o, P1 + o, X0 + o, X1 + o, it.Q + o, nullptr});
+        exact_items.push_back(i);
       }
       continue;
     }
@@ -762,7 +811,18 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
                                    (long long)g.b * g.b * g.count, bf16, s));
     }
   }
-  return flush();
+  poetx_status st = flush();
+  if (st != POETX_OK || exact.empty()) return st;
+  if ((st = exact_cayley_runs(exact, s)) != POETX_OK) return st;
+  for (size_t i = 0; i < exact.size(); ++i) {
+    const BuildItem& it = items[exact_items[i]];
+    if (!it.Qact) continue;
+    const ExactRun& r = exact[i];
+    const int es = elsize(it.pl);
+    HIP_TRY(poetx::launch_cast(r.Q, static_cast<char*>(it.Qact) + (size_t)es * r.g.q_off,
+                               (long long)r.g.b * r.g.b * r.g.count, it.pl->dtype == POETX_BF16, s));
+  }
+  return POETX_OK;
 }
 
 bool side_ok(int32_t side) { return side_ok_fn(side); }

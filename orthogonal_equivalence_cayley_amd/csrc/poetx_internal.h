@@ -71,6 +71,20 @@ struct GemmF32 {
   float alpha, beta, gamma;
 };
 hipError_t launch_gemm_f32(const GemmF32& p, hipStream_t s);
+// Runs of the same shape and strides (splits = 1, no E output) in one launch:
+// run i has its own A, B, C, Cin and group count; group strides from `shape`.
+struct GemmF32Run {
+  const float* A; const float* B; float* C; const float* Cin;
+  int groups;
+};
+constexpr int kF32MaxRuns = 16;
+struct GemmF32Runs {
+  GemmF32 p;
+  int n;
+  GemmF32Run r[kF32MaxRuns];
+  int z0[kF32MaxRuns];
+};
+hipError_t launch_gemm_f32_runs(const GemmF32& shape, const GemmF32Run* runs, int n, hipStream_t s);
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM
 // C(m,n) = sum_k A(m,k) B(n,k), bf16 inputs, fp32 accumulation.
