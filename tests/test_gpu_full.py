@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import blocks_concat, device_ready, log, run_layer
+from gpu_util import blocks_concat, device_ready, log, run_layer, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,28 @@ def test_single_layer_workload_full(cid):
         _check("G_X", got["G_X"], ref["G_X"], tol)
         _check("g_theta_R", got["g_theta_R"], ref["g_theta_R"], tol)
         _check("g_theta_P", got["g_theta_P"], ref["g_theta_P"], tol)
+
+
+def test_exact_cayley_workload_full():
+    """Exact-Cayley mode at the full size of the 5632 x 2048 workload (8192
+    tokens, forward and backward), against the oracle's solve-based transform
+    and its closed-form gradient. The batched fp32 products of the transform
+    then run over both sides' 30 blocks in single launches."""
+    import torch
+    from orthogonal_equivalence_cayley_amd import PoetxLayer
+    w = workloads.WORKLOADS[3]
+    inp = workloads.layer_inputs(w, 0)
+    sp = inp.spec
+    log(f"{w.name} exact: T={w.T} m={sp.m} n={sp.n}")
+    L = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, w.k, dtype=w.dtype, cayley="exact")
+    L.set_weight(to_dev(inp.W0, w.dtype), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
+    L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
+    got, _ = run_layer(inp, w.k, w.dtype, backward=w.backward, layer=L)
+    ref = oracle.layer_reference(inp, None, backward_pass=w.backward)
+    _check("Q_R", got["QR"], blocks_concat(ref["QR"]), TOL_F32)
+    _check("Q_P", got["QP"], blocks_concat(ref["QP"]), TOL_F32)
+    for key in ("Wa", "Y", "G_X", "g_theta_R", "g_theta_P"):
+        _check(key, got[key], ref[key], TOL_BF16)
 
 
 def _sample_rows(T, seed):
