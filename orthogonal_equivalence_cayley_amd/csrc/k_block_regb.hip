@@ -42,8 +42,9 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// Then for all waves: what the awaited loads wrote is in LDS and every earlier
-// LDS read of the workgroup is done.
+// Waits for this wave's LDS reads, then for all waves: after a wait for the
+// tile's loads, what they wrote is in LDS, and every earlier LDS read of the
+// workgroup is done.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
