@@ -1,8 +1,9 @@
-// fp32 power chains of the Cayley-Neumann parameterisation on the gfx950
-// matrix cores (v_mfma_f32_16x16x4_f32) ([PX] = page "POET-X: Memory-efficient
-// LLM Training by Scaling Orthogonal Transformation", Résumé technique §2.D:
-// the Neumann series is evaluated in one fused kernel with its operands kept
-// on chip).
+// Power chains of the Cayley-Neumann parameterisation on the gfx950 matrix
+// cores ([PX] = page "POET-X: Memory-efficient LLM Training by Scaling
+// Orthogonal Transformation", Résumé technique §2.D: the Neumann series is
+// evaluated in one fused kernel with its operands kept on chip): fp32 plans on
+// v_mfma_f32_16x16x4_f32; bf16 plans on split bf16 products (three
+// v_mfma_f32_32x32x16_bf16 per product, see chain_split_kernel).
 //
 // A row panel of a product X S only needs the same row panel of X and all of S,
 // so every chain that multiplies by S from the right is row-local: one
@@ -224,6 +225,251 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 }
 
+// ---- split bf16 products (bf16 plans). Every product X S of a chain runs as
+// Xh Mh + Xh Ml + Xl Mh on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation), where X = Xh + Xl and M = -S = S^T = Mh + Ml are split
+// into a bf16 value and its bf16 residual (16 significant bits together); the
+// dropped Xl Ml and the two residual roundings leave about 2^-15 relative error
+// per product term, next to the bf16 rounding the activation path applies to Q.
+// One workgroup owns 32 rows of one block; the panel sits in LDS as its two bf16
+// halves (row pitch b + 8, so that the 16 rows read by one pass of a fragment
+// read fall in distinct banks); S^T streams from L2 as the MFMA A operand,
+// stored by the unpack in fragment order (one contiguous KiB per operand load).
+// Each lane holds 4 consecutive columns of one panel row per 32 x 32 output tile.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void split4(float4 x, uint2& h, uint2& l) {
+  const __bf16 h0 = static_cast<__bf16>(x.x), h1 = static_cast<__bf16>(x.y);
+  const __bf16 h2 = static_cast<__bf16>(x.z), h3 = static_cast<__bf16>(x.w);
+  const __bf16 l0 = static_cast<__bf16>(x.x - static_cast<float>(h0));
+  const __bf16 l1 = static_cast<__bf16>(x.y - static_cast<float>(h1));
+  const __bf16 l2 = static_cast<__bf16>(x.z - static_cast<float>(h2));
+  const __bf16 l3 = static_cast<__bf16>(x.w - static_cast<float>(h3));
+  auto u = [](__bf16 v) { return (uint32_t)__builtin_bit_cast(uint16_t, v); };
+  h = make_uint2(u(h0) | (u(h1) << 16), u(h2) | (u(h3) << 16));
+  l = make_uint2(u(l0) | (u(l1) << 16), u(l2) | (u(l3) << 16));
+}
+
+// NT 32-column tiles per wave (4 waves), U K-steps of 16 prefetched.
+template <int MODE, int NT, int U>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chain_split_kernel(ChainBatch cb) {
+  constexpr int RP = 32;
+  extern __shared__ __align__(16) float lds[];
+  const ChainEntry p = select_entry(cb);
+  const int b = p.b;
+  const int pitch = b + 8;                         // bf16 elements per panel row
+  uint16_t* const ph = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* const pl = ph + RP * pitch;
+  const int panels = b / RP;
+  const int nwg = panels * p.count;
+  const int loc = blockIdx.x - p.wg0;
+  if (loc >= nwg) return;   // padding of the run to a multiple of 8 workgroups
+  // all panels of one block on one XCD, so that block's S^T is fetched into one L2
+  const int lid = (nwg % 8 == 0 && p.wg0 % 8 == 0) ? (loc % 8) * (nwg / 8) + loc / 8 : loc;
+  const int blk = lid / panels;
+  const int r0 = (lid - blk * panels) * RP;
+  const long long bb = (long long)b * b;
+  const long long moff = blk * bb;
+  const float* S = p.S + moff;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntiles = b / 32;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int k = cb.k;
+  // first column of each of this wave's tiles; tiles past the last one are
+  // clamped onto it (the MFMA loop stays branch-free; their results are dropped)
+  int n0[NT];
+  bool valid[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    valid[t] = wave + 4 * t < ntiles;
+    n0[t] = min(wave + 4 * t, ntiles - 1) * 32;
+  }
+  // this lane's panel row and its 4-column groups: row l32, columns n0 + 8 q + 4 hf + 0..3
+  const int row = l32;
+  const long long rowg = (long long)(r0 + row) * b;   // element offset of the row in a block
+
+  float keep[NT][16];   // running Q (BUILD) or G (ABAR), accumulator layout
+  float last[NT][16];   // TCHAIN: the latest panel in fp32
+  auto put_panel = [&](int t, int q, float4 x) {
+    uint2 h, l;
+    split4(x, h, l);
+    const int c = n0[t] + 8 * q + 4 * hf;
+    *reinterpret_cast<uint2*>(ph + row * pitch + c) = h;
+    *reinterpret_cast<uint2*>(pl + row * pitch + c) = l;
+  };
+  // initial panel
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = n0[t] + 8 * q + 4 * hf;
+      float4 x;
+      if (MODE == 0) {
+        x = *reinterpret_cast<const float4*>(S + rowg + c);
+        const float c1 = coef(1, k);
+        keep[t][4 * q + 0] = (r0 + row == c + 0 ? 1.0f : 0.0f) + c1 * x.x;
+        keep[t][4 * q + 1] = (r0 + row == c + 1 ? 1.0f : 0.0f) + c1 * x.y;
+        keep[t][4 * q + 2] = (r0 + row == c + 2 ? 1.0f : 0.0f) + c1 * x.z;
+        keep[t][4 * q + 3] = (r0 + row == c + 3 ? 1.0f : 0.0f) + c1 * x.w;
+      } else if (MODE == 1) {
+        const float4 g = *reinterpret_cast<const float4*>(p.G + moff + rowg + c);
+        keep[t][4 * q + 0] = g.x; keep[t][4 * q + 1] = g.y;
+        keep[t][4 * q + 2] = g.z; keep[t][4 * q + 3] = g.w;
+        const float ck = coef(k + 1, k);
+        x = make_float4(ck * g.x, ck * g.y, ck * g.z, ck * g.w);
+        if (valid[t]) *reinterpret_cast<float4*>(p.out + (long long)k * p.stride + moff + rowg + c) = x;
+      } else {
+        // A_{k+1}^T: element (row, c + e) = A_{k+1}[c + e][r0 + row]
+        const float* A = p.G + (long long)k * p.stride + moff + r0 + row;
+        x = make_float4(A[(long long)(c + 0) * b], A[(long long)(c + 1) * b], A[(long long)(c + 2) * b],
+                        A[(long long)(c + 3) * b]);
+        last[t][4 * q + 0] = x.x; last[t][4 * q + 1] = x.y;
+        last[t][4 * q + 2] = x.z; last[t][4 * q + 3] = x.w;
+      }
+      if (valid[t]) put_panel(t, q, x);
+    }
+  }
+
+  // M = -S = S^T split into bf16 value and residual, in fragment order
+  const uint16_t* Mh = p.Mh + moff;
+  const uint16_t* Ml = p.Mh + (long long)p.count * bb + moff;
+  const __amdgpu_buffer_rsrc_t rh =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Mh), (short)0, (int)(bb * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rl =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Ml), (short)0, (int)(bb * 2), 0x00020000);
+  // fragment order: the 1 KiB of (tile n0 / 32, K-step kc / 16) at
+  // ((n0 / 32) (b / 16) + kc / 16) KiB, this lane's 16 bytes at 16 lane
+  int tbase[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) tbase[t] = (n0[t] >> 5) * (b >> 4) * 1024;
+  const int voff = lane * 16;
+  auto ldm = [&](const __amdgpu_buffer_rsrc_t& r, int t, int kc) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, tbase[t] + kc * 64, 0));
+  };
+
+  for (int st = 0; st < k; ++st) {
+    f32x16 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+    __syncthreads();   // panel of the previous step written
+    bf16x8 bnh[U][NT], bnl[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        bnh[u][t] = ldm(rh, t, 16 * u);
+        bnl[u][t] = ldm(rl, t, 16 * u);
+      }
+    for (int kc = 0; kc < b; kc += 16 * U) {
+      bf16x8 bch[U][NT], bcl[U][NT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          bch[u][t] = bnh[u][t];
+          bcl[u][t] = bnl[u][t];
+        }
+      const int kn = min(kc + 16 * U, b - 16 * U);   // clamped: the last prefetch is unused
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          bnh[u][t] = ldm(rh, t, kn + 16 * u);
+          bnl[u][t] = ldm(rl, t, kn + 16 * u);
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = kc + 16 * u + 8 * hf;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(ph + row * pitch + kk);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(pl + row * pitch + kk);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bcl[u][t], ah, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bch[u][t], al, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bch[u][t], ah, acc[t], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();   // every wave has finished reading the panel
+    const int j = (MODE == 0) ? st + 2 : k - st;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = n0[t] + 8 * q + 4 * hf;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[t][4 * q + e];
+        if (MODE == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) keep[t][4 * q + e] += coef(j, k) * x[e];
+        } else if (MODE == 1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = coef(j, k) * keep[t][4 * q + e] - x[e];
+          if (valid[t])
+            *reinterpret_cast<float4*>(p.out + (long long)(j - 1) * p.stride + moff + rowg + c) =
+                make_float4(x[0], x[1], x[2], x[3]);
+        } else {
+          const float* A = p.G + (long long)(j - 1) * p.stride + moff + r0 + row;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] += A[(long long)(c + e) * b];
+            last[t][4 * q + e] = x[e];
+          }
+        }
+        if (valid[t] && st + 1 < k) put_panel(t, q, make_float4(x[0], x[1], x[2], x[3]));
+      }
+    }
+  }
+
+  if (MODE == 0 || MODE == 2) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (!valid[t]) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = n0[t] + 8 * q + 4 * hf;
+        const float* src = MODE == 0 ? keep[t] : last[t];
+        const float4 x = make_float4(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
+        *reinterpret_cast<float4*>(p.out + moff + rowg + c) = x;
+        if (MODE == 0 && p.out_act) {
+          if (p.act_bf16) {
+            uint2 h, l;
+            split4(x, h, l);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out_act) + moff + rowg + c) = h;
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out_act) + moff + rowg + c) = x;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, int NT>
+hipError_t launch_split_class(ChainBatch cb, hipStream_t s) {
+  constexpr int RP = 32;
+  int wg = 0, bmax = 0, bmin = 1 << 30;
+  for (int i = 0; i < cb.n; ++i) {
+    cb.e[i].wg0 = wg;
+    wg += (cb.e[i].b / RP * cb.e[i].count + 7) / 8 * 8;
+    bmax = max(bmax, cb.e[i].b);
+    bmin = min(bmin, cb.e[i].b);
+  }
+  if (wg == 0) return hipSuccess;
+  const size_t lds = (size_t)2 * RP * (bmax + 8) * sizeof(uint16_t);
+  // the prefetch of U K-steps of 16 stays inside the block: b >= 16 U
+  if (bmin >= 64)
+    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 4>), dim3(wg), dim3(kThreads), lds, s, cb);
+  else
+    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 2>), dim3(wg), dim3(kThreads), lds, s, cb);
+  return hipGetLastError();
+}
+
 template <int MODE, int NT, int MT>
 hipError_t launch_class(ChainBatch cb, hipStream_t s) {
   constexpr int RP = 16 * MT;
@@ -251,6 +497,20 @@ hipError_t launch_class(ChainBatch cb, hipStream_t s) {
 
 template <int MODE>
 hipError_t launch_mode(const ChainBatch& all, hipStream_t s) {
+  // split bf16 products: one launch per class of 32-column tiles per wave
+  for (int nt = 1; nt <= 2; ++nt) {
+    ChainBatch cb;
+    cb.n = 0;
+    cb.k = all.k;
+    for (int i = 0; i < all.n; ++i) {
+      const ChainEntry& e = all.e[i];
+      if (!e.Mh || !chain_split_supported(e.b)) continue;
+      if ((e.b / 32 + 3) / 4 == nt) cb.e[cb.n++] = e;
+    }
+    if (cb.n == 0) continue;
+    const hipError_t e = nt == 1 ? launch_split_class<MODE, 1>(cb, s) : launch_split_class<MODE, 2>(cb, s);
+    if (e != hipSuccess) return e;
+  }
   // one launch per size class (column tiles per wave, and panels of 32 rows
   // where b allows them: each B value then feeds two row tiles)
   for (int nt = 1; nt <= 8; nt *= 2)
@@ -259,6 +519,7 @@ hipError_t launch_mode(const ChainBatch& all, hipStream_t s) {
       cb.n = 0;
       cb.k = all.k;
       for (int i = 0; i < all.n; ++i) {
+        if (all.e[i].Mh && chain_split_supported(all.e[i].b)) continue;   // launched above
         const int need = (all.e[i].b / 16 + 3) / 4;
         const int cls = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
         // 32-row panels wherever b allows them (with S read through buffer loads
@@ -288,6 +549,8 @@ hipError_t launch_mode(const ChainBatch& all, hipStream_t s) {
 // b % 16 == 0 keeps every row of S a whole number of float4 and every 16-row
 // chunk a whole number of per-thread loads (b = 16 .. 512).
 bool chain_supported(int b) { return b % 16 == 0 && b >= 16 && b <= 512; }
+// 32-row panels and 32-column tiles; at most two tiles per wave
+bool chain_split_supported(int b) { return b % 32 == 0 && b >= 32 && b <= 256; }
 
 hipError_t launch_chain_batch(int mode, const ChainBatch& cb, hipStream_t s) {
   if (cb.n < 0 || cb.n > kChainMaxEntries) return hipErrorInvalidValue;
@@ -312,6 +575,14 @@ __device__ __forceinline__ TriEntry select_tri(const TriBatch& tb, int w) {
   for (int i = 1; i < kChainMaxEntries; ++i)
     if (i < tb.n && w >= tb.e[i].e0) r = tb.e[i];
   return r;
+}
+
+// Split operand of the bf16 chains in MFMA fragment order: for 32-row tile nt of
+// M and K-step kc (16 columns), 64 lanes x 8 bf16 = 1 KiB, lane r + 32 h holding
+// M[32 nt + r][16 kc + 8 h .. + 7]; so each operand load is one contiguous read.
+__device__ __forceinline__ long long split_frag_offset(int n, int k, int b) {
+  const int nt = n >> 5, r = n & 31, kc = k >> 4, h = (k >> 3) & 1, e = k & 7;
+  return ((((long long)nt * (b >> 4) + kc) * 64) + r + 32 * h) * 8 + e;
 }
 
 __device__ __forceinline__ long long tri_off(int i, int j, int b) {
@@ -360,11 +631,20 @@ __global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
     const int r = r0 + j;
     float* row = S + (long long)r * b;
     const float* up = th + (tri_off(r, r + 1, b) - (r + 1));   // theta(r, c) = up[c], c > r
+    uint16_t* mh = w.t.split ? w.t.split + (long long)w.g * b * b : nullptr;
+    uint16_t* ml = w.t.split ? mh + (long long)w.t.count * b * b : nullptr;
     for (int c = lane; c < b; c += 64) {
       float v = 0.0f;
       if (c > r) v = up[c];
       else if (c < r) v = -strip[c * kTriPitch + j];
       row[c] = v;
+      if (mh) {   // -v = value + residual, both bf16, at M[r][c] in fragment order
+        const __bf16 h = static_cast<__bf16>(-v);
+        const __bf16 l = static_cast<__bf16>(-v - static_cast<float>(h));
+        const long long o = split_frag_offset(r, c, b);
+        mh[o] = __builtin_bit_cast(uint16_t, h);
+        ml[o] = __builtin_bit_cast(uint16_t, l);
+      }
     }
   }
 }

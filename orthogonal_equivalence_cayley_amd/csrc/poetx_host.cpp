@@ -531,9 +531,14 @@ poetx_status grad_items(const GradItem* items, int count, hipStream_t s) {
       if (!poetx::chain_supported(g.b)) continue;
       if (ab.n == poetx::kChainMaxEntries && (st = flush()) != POETX_OK) return st;
       float* S = it.w.S + g.q_off;
-      ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, S, g.b, g.count, 0};
+      // bf16 plans: the chains run on split bf16 products; the split of -S goes
+      // to this run's part of A0 (used only by the generic path of other sizes)
+      uint16_t* split = (pl->dtype == POETX_BF16 && poetx::chain_split_supported(g.b))
+                            ? reinterpret_cast<uint16_t*>(it.w.A0 + g.q_off) : nullptr;
+      ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, S, g.b, g.count, 0, split};
       poetx::ChainEntry e{};
       e.S = S; e.b = g.b; e.count = g.count; e.stride = pl->nelem[it.side];
+      e.Mh = split;
       e.G = it.dQ + g.q_off;
       e.out = it.w.A + g.q_off;
       ab.e[ab.n++] = e;
@@ -788,9 +793,14 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
           poetx_status st = flush();
           if (st != POETX_OK) return st;
         }
-        ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, S + g.q_off, g.b, g.count, 0};
+        // bf16 plans: split bf16 products, the split of -S in this run's part of
+        // P0 (used only by the generic path of other sizes)
+        uint16_t* split = (bf16 && poetx::chain_split_supported(g.b))
+                              ? reinterpret_cast<uint16_t*>(P0 + g.q_off) : nullptr;
+        ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, S + g.q_off, g.b, g.count, 0, split};
         poetx::ChainEntry e{};
         e.S = S + g.q_off; e.G = nullptr; e.out = it.Q + g.q_off;
+        e.Mh = split;
         e.out_act = it.Qact ? static_cast<char*>(it.Qact) + (size_t)es * g.q_off : nullptr;
         e.act_bf16 = bf16; e.b = g.b; e.count = g.count; e.stride = 0;
         cb.e[cb.n++] = e;

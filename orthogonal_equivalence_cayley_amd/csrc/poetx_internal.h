@@ -142,6 +142,10 @@ struct ChainEntry {
   int b, count;       // block size and number of blocks of the run
   int wg0;            // first workgroup of the run (filled by the launcher)
   int act_bf16;
+  // bf16 split of -S = S^T (the run's count blocks of b x b rounded to bf16,
+  // then the count blocks of the residuals), written by the unpack; when set
+  // (b % 32 == 0, b <= 256) the products run as three bf16 MFMAs each
+  const uint16_t* Mh = nullptr;
 };
 struct ChainBatch {
   int n, k;
@@ -158,7 +162,10 @@ struct TriEntry {
   float* dst;         // unpack: b x b matrices; pack: packed gradient of the run
   int b, count;
   long long e0;       // first workgroup of the run (set by the launcher)
+  uint16_t* split = nullptr;   // unpack: also the bf16 split of -S (ChainEntry::Mh)
 };
+// Block sizes whose chains can run on the bf16 split products.
+bool chain_split_supported(int b);
 struct TriBatch {
   int n;
   float sign;
