@@ -252,12 +252,15 @@ __device__ __forceinline__ void split4(float4 x, uint2& h, uint2& l) {
 }
 
 // NT 32-column tiles per wave (4 waves), U K-steps of 16 prefetched.
-template <int MODE, int NT, int U>
+// BF: the block size when every entry of the launch has it (0: read per entry);
+// with it fixed the K loop unrolls completely and each operand load is waited
+// for exactly (in a rolled loop the compiler waits for every load each pass).
+template <int MODE, int NT, int U, int BF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chain_split_kernel(ChainBatch cb) {
   constexpr int RP = 32;
   extern __shared__ __align__(16) float lds[];
   const ChainEntry p = select_entry(cb);
-  const int b = p.b;
+  const int b = BF ? BF : p.b;
   const int pitch = b + 8;                         // bf16 elements per panel row
   uint16_t* const ph = reinterpret_cast<uint16_t*>(lds);
   uint16_t* const pl = ph + RP * pitch;
@@ -364,6 +367,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         bnh[u][t] = ldm(rh, t, 16 * u);
         bnl[u][t] = ldm(rl, t, 16 * u);
       }
+    constexpr int kUnroll = BF > 0 ? BF / 16 : 1;
+#pragma unroll kUnroll
     for (int kc = 0; kc < b; kc += 16 * U) {
       bf16x8 bch[U][NT], bcl[U][NT];
 #pragma unroll
@@ -381,6 +386,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           bnh[u][t] = ldm(rh, t, kn + 16 * u);
           bnl[u][t] = ldm(rl, t, kn + 16 * u);
         }
+      // keep the next loads ahead of these multiplies (the scheduler would sink
+      // them to their uses)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kk = kc + 16 * u + 8 * hf;
@@ -393,6 +401,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bch[u][t], ah, acc[t], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();   // every wave has finished reading the panel
     const int j = (MODE == 0) ? st + 2 : k - st;
@@ -463,10 +472,12 @@ hipError_t launch_split_class(ChainBatch cb, hipStream_t s) {
   if (wg == 0) return hipSuccess;
   const size_t lds = (size_t)2 * RP * (bmax + 8) * sizeof(uint16_t);
   // the prefetch of U K-steps of 16 stays inside the block: b >= 16 U
-  if (bmin >= 64)
-    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 4>), dim3(wg), dim3(kThreads), lds, s, cb);
+  if (bmin == 256 && bmax == 256)
+    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 4, 256>), dim3(wg), dim3(kThreads), lds, s, cb);
+  else if (bmin >= 64)
+    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 4, 0>), dim3(wg), dim3(kThreads), lds, s, cb);
   else
-    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 2>), dim3(wg), dim3(kThreads), lds, s, cb);
+    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 2, 0>), dim3(wg), dim3(kThreads), lds, s, cb);
   return hipGetLastError();
 }
 
@@ -631,19 +642,39 @@ __global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
     const int r = r0 + j;
     float* row = S + (long long)r * b;
     const float* up = th + (tri_off(r, r + 1, b) - (r + 1));   // theta(r, c) = up[c], c > r
-    uint16_t* mh = w.t.split ? w.t.split + (long long)w.g * b * b : nullptr;
-    uint16_t* ml = w.t.split ? mh + (long long)w.t.count * b * b : nullptr;
     for (int c = lane; c < b; c += 64) {
       float v = 0.0f;
       if (c > r) v = up[c];
       else if (c < r) v = -strip[c * kTriPitch + j];
       row[c] = v;
-      if (mh) {   // -v = value + residual, both bf16, at M[r][c] in fragment order
-        const __bf16 h = static_cast<__bf16>(-v);
-        const __bf16 l = static_cast<__bf16>(-v - static_cast<float>(h));
-        const long long o = split_frag_offset(r, c, b);
-        mh[o] = __builtin_bit_cast(uint16_t, h);
-        ml[o] = __builtin_bit_cast(uint16_t, l);
+    }
+    if (w.t.split) {
+      // M[r][c] = -S[r][c] = value + residual, both bf16, in fragment order:
+      // 8 consecutive columns per lane, one 16-byte store of each
+      uint16_t* mh = w.t.split + (long long)w.g * b * b;
+      uint16_t* ml = mh + (long long)w.t.count * b * b;
+      for (int c0 = 8 * lane; c0 < b; c0 += 8 * 64) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float m[2];
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const int c = c0 + e + d;
+            float v = 0.0f;
+            if (c > r) v = up[c];
+            else if (c < r) v = -strip[c * kTriPitch + j];
+            m[d] = -v;
+          }
+          const __bf16 h0 = static_cast<__bf16>(m[0]), h1 = static_cast<__bf16>(m[1]);
+          const __bf16 l0 = static_cast<__bf16>(m[0] - static_cast<float>(h0));
+          const __bf16 l1 = static_cast<__bf16>(m[1] - static_cast<float>(h1));
+          hw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          lw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        }
+        const long long o = split_frag_offset(r, c0, b);   // c0 % 8 == 0: a whole 16-byte piece
+        *reinterpret_cast<uint4*>(mh + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(ml + o) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
     }
   }

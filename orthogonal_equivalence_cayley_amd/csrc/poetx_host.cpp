@@ -490,6 +490,15 @@ poetx_status block_grads(const poetx_plan* pl, int side, long long T, const void
   return POETX_OK;
 }
 
+// bf16 plans: where the run's split of -S goes (its part of a b x b fp32
+// buffer, 4 bytes per element for the two bf16 halves), or null for the fp32
+// chains (fp32 plans, other block sizes, a part not on a 16-byte boundary).
+uint16_t* split_buffer(const poetx_plan* pl, const Seg& g, float* buf) {
+  if (pl->dtype != POETX_BF16 || !poetx::chain_split_supported(g.b)) return nullptr;
+  float* p = buf + g.q_off;
+  return ((uintptr_t)p & 15) ? nullptr : reinterpret_cast<uint16_t*>(p);
+}
+
 // One chain-rule item: dL/dQ of one side of one plan -> packed parameter gradient.
 struct GradItem {
   const poetx_plan* pl;
@@ -533,8 +542,7 @@ poetx_status grad_items(const GradItem* items, int count, hipStream_t s) {
       float* S = it.w.S + g.q_off;
       // bf16 plans: the chains run on split bf16 products; the split of -S goes
       // to this run's part of A0 (used only by the generic path of other sizes)
-      uint16_t* split = (pl->dtype == POETX_BF16 && poetx::chain_split_supported(g.b))
-                            ? reinterpret_cast<uint16_t*>(it.w.A0 + g.q_off) : nullptr;
+      uint16_t* split = split_buffer(pl, g, it.w.A0);
       ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, S, g.b, g.count, 0, split};
       poetx::ChainEntry e{};
       e.S = S; e.b = g.b; e.count = g.count; e.stride = pl->nelem[it.side];
@@ -795,8 +803,7 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
         }
         // bf16 plans: split bf16 products, the split of -S in this run's part of
         // P0 (used only by the generic path of other sizes)
-        uint16_t* split = (bf16 && poetx::chain_split_supported(g.b))
-                              ? reinterpret_cast<uint16_t*>(P0 + g.q_off) : nullptr;
+        uint16_t* split = split_buffer(pl, g, P0);
         ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, S + g.q_off, g.b, g.count, 0, split};
         poetx::ChainEntry e{};
         e.S = S + g.q_off; e.G = nullptr; e.out = it.Q + g.q_off;
