@@ -358,6 +358,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+    const int j = (MODE == 0) ? st + 2 : k - st;
+    // TCHAIN: this step's A_j^T values (element (row, c) = A_j[c][r0 + row]),
+    // loaded before the multiplies so that their latency hides behind them
+    float at[MODE == 2 ? NT : 1][MODE == 2 ? 16 : 1];
+    if (MODE == 2) {
+      const float* A = p.G + (long long)(j - 1) * p.stride + moff + r0 + row;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            at[t][4 * q + e] = A[(long long)(n0[t] + 8 * q + 4 * hf + e) * b];
+    }
     __syncthreads();   // panel of the previous step written
     bf16x8 bnh[U][NT], bnl[U][NT];
 #pragma unroll
@@ -404,7 +418,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();   // every wave has finished reading the panel
-    const int j = (MODE == 0) ? st + 2 : k - st;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -423,10 +436,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             *reinterpret_cast<float4*>(p.out + (long long)(j - 1) * p.stride + moff + rowg + c) =
                 make_float4(x[0], x[1], x[2], x[3]);
         } else {
-          const float* A = p.G + (long long)(j - 1) * p.stride + moff + r0 + row;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x[e] += A[(long long)(c + e) * b];
+            x[e] += at[MODE == 2 ? t : 0][MODE == 2 ? 4 * q + e : 0];
             last[t][4 * q + e] = x[e];
           }
         }
@@ -472,10 +484,12 @@ hipError_t launch_split_class(ChainBatch cb, hipStream_t s) {
   if (wg == 0) return hipSuccess;
   const size_t lds = (size_t)2 * RP * (bmax + 8) * sizeof(uint16_t);
   // the prefetch of U K-steps of 16 stays inside the block: b >= 16 U
+  // (mixed sizes: the transposed chain's extra loads leave registers for two steps)
+  constexpr int UM = MODE == 2 ? 2 : 4;
   if (bmin == 256 && bmax == 256)
     hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 4, 256>), dim3(wg), dim3(kThreads), lds, s, cb);
-  else if (bmin >= 64)
-    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 4, 0>), dim3(wg), dim3(kThreads), lds, s, cb);
+  else if (bmin >= 16 * UM)
+    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, UM, 0>), dim3(wg), dim3(kThreads), lds, s, cb);
   else
     hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 2, 0>), dim3(wg), dim3(kThreads), lds, s, cb);
   return hipGetLastError();
@@ -629,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
   const TriWork w = tri_work(tb);
   const int b = w.t.b, r0 = w.r0;
   const float* th = w.t.src + (long long)w.g * ((long long)b * (b - 1) / 2);
-  float* S = w.t.dst + (long long)w.g * b * b;
+  float* S = w.t.dst ? w.t.dst + (long long)w.g * b * b : nullptr;   // null: the split only
   const int nrow = r0 + kTriRows;
   for (int idx = threadIdx.x; idx < nrow * kTriRows; idx += kThreads) {
     const int c = idx / kTriRows, j = idx % kTriRows;
@@ -640,13 +654,15 @@ __global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int j = wave; j < kTriRows; j += kThreads / 64) {
     const int r = r0 + j;
-    float* row = S + (long long)r * b;
     const float* up = th + (tri_off(r, r + 1, b) - (r + 1));   // theta(r, c) = up[c], c > r
-    for (int c = lane; c < b; c += 64) {
-      float v = 0.0f;
-      if (c > r) v = up[c];
-      else if (c < r) v = -strip[c * kTriPitch + j];
-      row[c] = v;
+    if (S) {
+      float* row = S + (long long)r * b;
+      for (int c = lane; c < b; c += 64) {
+        float v = 0.0f;
+        if (c > r) v = up[c];
+        else if (c < r) v = -strip[c * kTriPitch + j];
+        row[c] = v;
+      }
     }
     if (w.t.split) {
       // M[r][c] = -S[r][c] = value + residual, both bf16, in fragment order:

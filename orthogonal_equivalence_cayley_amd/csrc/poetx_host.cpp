@@ -543,7 +543,8 @@ poetx_status grad_items(const GradItem* items, int count, hipStream_t s) {
       // bf16 plans: the chains run on split bf16 products; the split of -S goes
       // to this run's part of A0 (used only by the generic path of other sizes)
       uint16_t* split = split_buffer(pl, g, it.w.A0);
-      ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, S, g.b, g.count, 0, split};
+      // the split chains never read S itself
+      ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, split ? nullptr : S, g.b, g.count, 0, split};
       poetx::ChainEntry e{};
       e.S = S; e.b = g.b; e.count = g.count; e.stride = pl->nelem[it.side];
       e.Mh = split;
