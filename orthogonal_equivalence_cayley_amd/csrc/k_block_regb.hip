@@ -26,6 +26,7 @@ namespace poetx {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kB = 256;                         // block size (N = K)
@@ -65,10 +66,38 @@ __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// BKM: B(n, k) = B_g[n * ldb + k] (K-contiguous, the transposed Q); otherwise
-// B(n, k) = B_g[k * ldb + n]. Workgroup w works on block g = w / wpg and runs
-// row tiles [(w % wpg) * per_wg, + per_wg) of it, so it loads B_g only once.
-template <bool BKM, int ROWS, int ST, bool SCALE>
+// A row-contiguous A tile (A(m, k) = A[k lda + m]) sits in LDS as 256 K-rows of
+// ROWS elements; chunk c of K-row k at slot k (ROWS / 8) + (c ^ 4 (k & 3)), so
+// the 4 K-rows x 4 chunks touched by 32 lanes of a transposing read
+// (ds_read_b64_tr_b16: within 16 lanes, lane p receives column p of a 4 x 16
+// block) fall in distinct banks. Operand rows r0 .. r0 + 31 at k = 16 kk +
+// 8 (lane / 32) .. + 7 take two such reads.
+template <int ROWS>
+__device__ __forceinline__ bf16x8 frag_t(const unsigned char* st, int r0, int kk, int lane) {
+  constexpr int CPR = ROWS / 8;
+  static_assert(CPR >= 16, "the swizzle moves a chunk by up to 12 positions");
+  const int g = lane >> 4, s = lane & 15;
+  const int col = r0 + (g & 1) * 16 + 4 * (s & 3);
+  const int kb = 16 * kk + 8 * (g >> 1) + (s >> 2);
+  i16x4 v[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int k = kb + 4 * i;
+    const int c = (col >> 3) ^ (4 * (k & 3));
+    v[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(st + (k * CPR + c) * 16 + (col & 7) * 2));
+  }
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 w = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// AKM: A(m, k) = A_g[m * lda + k] (K-contiguous); otherwise A_g[k * lda + m]
+// (then M % ROWS == 0). BKM: B(n, k) = B_g[n * ldb + k] (K-contiguous, the
+// transposed Q); otherwise B(n, k) = B_g[k * ldb + n]. Workgroup w works on
+// block g = w / wpg and runs row tiles [(w % wpg) * per_wg, + per_wg) of it, so
+// it loads B_g only once.
+template <bool AKM, bool BKM, int ROWS, int ST, bool SCALE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
   constexpr int STAGE = ROWS * kB * 2;             // bytes of one A tile in LDS
@@ -97,10 +126,17 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int s = i * kThreads + tid;
-      const int r = s / kCPR;
-      const int c = (s % kCPR) ^ (r & 31);
-      const long long row = min(row0 + r, (long long)p.M - 1);   // rows past M: loaded, not stored
-      dma16(Ag + row * p.lda + c * 8, st + (i * kThreads + wave * 64) * 16);
+      if constexpr (AKM) {
+        const int r = s / kCPR;
+        const int c = (s % kCPR) ^ (r & 31);
+        const long long row = min(row0 + r, (long long)p.M - 1);   // rows past M: loaded, not stored
+        dma16(Ag + row * p.lda + c * 8, st + (i * kThreads + wave * 64) * 16);
+      } else {
+        constexpr int CPR = ROWS / 8;   // chunks per K-row of the tile
+        const int k = s / CPR;
+        const int c = (s % CPR) ^ (4 * (k & 3));
+        dma16(Ag + (long long)k * p.lda + row0 + c * 8, st + (i * kThreads + wave * 64) * 16);
+      }
     }
   };
 
@@ -159,9 +195,13 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
       bf16x8 af[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int r = 32 * mt + nl;
-        const int c = 2 * kk + h;
-        af[mt] = *reinterpret_cast<const bf16x8*>(st + (r * kCPR + (c ^ (r & 31))) * 16);
+        if constexpr (AKM) {
+          const int r = 32 * mt + nl;
+          const int c = 2 * kk + h;
+          af[mt] = *reinterpret_cast<const bf16x8*>(st + (r * kCPR + (c ^ (r & 31))) * 16);
+        } else {
+          af[mt] = frag_t<ROWS>(st, 32 * mt, kk, lane);
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -208,11 +248,16 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
 
 constexpr int kRows = 64;   // rows of A per tile
 constexpr int kST = 4;      // LDS stages: three 32 KiB tiles in flight
+constexpr int kRowsT = 128; // row-contiguous A: 128-row tiles (64 KiB, the swizzle needs 16 chunks)
+constexpr int kSTT = 2;     // and two stages
 
 }  // namespace
 
 bool block_regb_supported(const GemmBf16& p) {
-  if (p.role != GEMM_BLOCK || p.N != kB || p.K != kB || !p.a_kmajor || p.out_f32) return false;
+  if (p.role != GEMM_BLOCK || p.N != kB || p.K != kB || p.out_f32) return false;
+  // row-contiguous A (the transposed weight fold): whole tiles, K-contiguous Q,
+  // no column scale
+  if (!p.a_kmajor && (p.M % kRowsT || !p.b_kmajor || p.col_scale)) return false;
   if (p.splits != 1 || p.b_i8 || p.M <= 0 || p.groups <= 0) return false;
   if (p.col_scale && (((uintptr_t)p.col_scale & 15) || p.c_gs % 4)) return false;
   if (p.lda % 8 || p.a_gs % 8 || p.ldc % 8 || p.c_gs % 8) return false;   // 16-byte rows
@@ -223,7 +268,8 @@ bool block_regb_supported(const GemmBf16& p) {
 
 hipError_t launch_block_regb(const GemmBf16& p, hipStream_t s) {
   if (!block_regb_supported(p)) return hipErrorInvalidValue;
-  const long long tpg = (p.M + kRows - 1) / kRows;
+  const int rows = p.a_kmajor ? kRows : kRowsT;
+  const long long tpg = (p.M + rows - 1) / rows;
   if (tpg > INT32_MAX) return hipErrorInvalidValue;
   // one workgroup per CU (the LDS ring): up to 256 / groups workgroups per
   // block, each on consecutive row tiles of that block only
@@ -232,17 +278,23 @@ hipError_t launch_block_regb(const GemmBf16& p, hipStream_t s) {
   const long long wpg = (tpg + per - 1) / per;
   const long long wgs = wpg * p.groups;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  const size_t lds = (size_t)kST * kRows * kB * 2;
   const dim3 grid((unsigned)wgs), block(kThreads);
   const int a = (int)tpg, b = (int)wpg, c = (int)per;
+  if (!p.a_kmajor) {   // the transposed weight fold: K-contiguous Q, no column scale
+    if (!p.b_kmajor || p.col_scale) return hipErrorInvalidValue;
+    const size_t lds = (size_t)kSTT * kRowsT * kB * 2;
+    hipLaunchKernelGGL((block_regb_kernel<false, true, kRowsT, kSTT, false>), grid, block, lds, s, p, a, b, c);
+    return hipGetLastError();
+  }
+  const size_t lds = (size_t)kST * kRows * kB * 2;
   if (p.b_kmajor && p.col_scale)
-    hipLaunchKernelGGL((block_regb_kernel<true, kRows, kST, true>), grid, block, lds, s, p, a, b, c);
+    hipLaunchKernelGGL((block_regb_kernel<true, true, kRows, kST, true>), grid, block, lds, s, p, a, b, c);
   else if (p.b_kmajor)
-    hipLaunchKernelGGL((block_regb_kernel<true, kRows, kST, false>), grid, block, lds, s, p, a, b, c);
+    hipLaunchKernelGGL((block_regb_kernel<true, true, kRows, kST, false>), grid, block, lds, s, p, a, b, c);
   else if (p.col_scale)
-    hipLaunchKernelGGL((block_regb_kernel<false, kRows, kST, true>), grid, block, lds, s, p, a, b, c);
+    hipLaunchKernelGGL((block_regb_kernel<true, false, kRows, kST, true>), grid, block, lds, s, p, a, b, c);
   else
-    hipLaunchKernelGGL((block_regb_kernel<false, kRows, kST, false>), grid, block, lds, s, p, a, b, c);
+    hipLaunchKernelGGL((block_regb_kernel<true, false, kRows, kST, false>), grid, block, lds, s, p, a, b, c);
   return hipGetLastError();
 }
 
