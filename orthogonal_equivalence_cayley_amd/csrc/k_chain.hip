@@ -513,8 +513,10 @@ hipError_t launch_class(ChainBatch cb, hipStream_t s) {
   for (int i = 0; i < cb.n; ++i)
     if (cb.e[i].b % 32) deep = false;
   const size_t lds = (size_t)RP * (bmax + 4) * sizeof(float);
+  // (eight column tiles per wave leave no registers for the deeper prefetch)
+  constexpr int UD = NT < 8 ? 8 : 4;
   if (deep)
-    hipLaunchKernelGGL((chain_kernel<MODE, NT, MT, 8>), dim3(wg), dim3(kThreads), lds, s, cb);
+    hipLaunchKernelGGL((chain_kernel<MODE, NT, MT, UD>), dim3(wg), dim3(kThreads), lds, s, cb);
   else
     hipLaunchKernelGGL((chain_kernel<MODE, NT, MT, 4>), dim3(wg), dim3(kThreads), lds, s, cb);
   return hipGetLastError();
