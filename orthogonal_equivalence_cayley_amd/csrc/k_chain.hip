@@ -381,6 +381,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         bnh[u][t] = ldm(rh, t, 16 * u);
         bnl[u][t] = ldm(rl, t, 16 * u);
       }
+    // (the launcher picks U so that 16 U divides b: no pass runs past the block)
     constexpr int kUnroll = BF > 0 ? BF / 16 : 1;
 #pragma unroll kUnroll
     for (int kc = 0; kc < b; kc += 16 * U) {
@@ -475,20 +476,23 @@ template <int MODE, int NT>
 hipError_t launch_split_class(ChainBatch cb, hipStream_t s) {
   constexpr int RP = 32;
   int wg = 0, bmax = 0, bmin = 1 << 30;
+  bool by64 = true;
   for (int i = 0; i < cb.n; ++i) {
     cb.e[i].wg0 = wg;
     wg += (cb.e[i].b / RP * cb.e[i].count + 7) / 8 * 8;
     bmax = max(bmax, cb.e[i].b);
     bmin = min(bmin, cb.e[i].b);
+    by64 = by64 && cb.e[i].b % 64 == 0;
   }
   if (wg == 0) return hipSuccess;
   const size_t lds = (size_t)2 * RP * (bmax + 8) * sizeof(uint16_t);
-  // the prefetch of U K-steps of 16 stays inside the block: b >= 16 U
-  // (mixed sizes: the transposed chain's extra loads leave registers for two steps)
+  // each pass of the K loop takes U K-steps of 16, so 16 U must divide every b
+  // (b % 32 == 0 always allows U = 2; mixed sizes: the transposed chain's extra
+  // loads leave registers for two steps only)
   constexpr int UM = MODE == 2 ? 2 : 4;
   if (bmin == 256 && bmax == 256)
     hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 4, 256>), dim3(wg), dim3(kThreads), lds, s, cb);
-  else if (bmin >= 16 * UM)
+  else if (UM == 2 || by64)
     hipLaunchKernelGGL((chain_split_kernel<MODE, NT, UM, 0>), dim3(wg), dim3(kThreads), lds, s, cb);
   else
     hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 2, 0>), dim3(wg), dim3(kThreads), lds, s, cb);

@@ -150,6 +150,10 @@ def test_layer_fp32_ragged(case):
     dict(m=2048, n=512, bR=(512,) * 3 + (256, 256), bP=(512,), T=1000, k=5),
     dict(m=256, n=256, bR=(256,), bP=(256,), T=1, k=4),
     dict(m=48, n=32, bR=(16, 32), bP=(32,), T=5, k=0),
+    # split chains over blocks that are multiples of 32 but not of 64, alone and
+    # mixed with other sizes in one launch
+    dict(m=256, n=288, bR=(96, 160), bP=(224, 64), T=200, k=4),
+    dict(m=320, n=96, bR=(192, 64, 64), bP=(96,), T=64, k=3),
 ])
 def test_layer_bf16_small(case):
     inp = workloads.small_case(case["m"], case["n"], case["bR"], case["bP"], T=case["T"],
