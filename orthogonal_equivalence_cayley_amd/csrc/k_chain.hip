@@ -274,7 +274,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int r0 = (lid - blk * panels) * RP;
   const long long bb = (long long)b * b;
   const long long moff = blk * bb;
-  const float* S = p.S + moff;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ntiles = b / 32;
@@ -293,48 +292,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int row = l32;
   const long long rowg = (long long)(r0 + row) * b;   // element offset of the row in a block
 
-  float keep[NT][16];   // running Q (BUILD) or G (ABAR), accumulator layout
-  float last[NT][16];   // TCHAIN: the latest panel in fp32
-  auto put_panel = [&](int t, int q, float4 x) {
-    uint2 h, l;
-    split4(x, h, l);
-    const int c = n0[t] + 8 * q + 4 * hf;
-    *reinterpret_cast<uint2*>(ph + row * pitch + c) = h;
-    *reinterpret_cast<uint2*>(pl + row * pitch + c) = l;
-  };
-  // initial panel
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = n0[t] + 8 * q + 4 * hf;
-      float4 x;
-      if (MODE == 0) {
-        x = *reinterpret_cast<const float4*>(S + rowg + c);
-        const float c1 = coef(1, k);
-        keep[t][4 * q + 0] = (r0 + row == c + 0 ? 1.0f : 0.0f) + c1 * x.x;
-        keep[t][4 * q + 1] = (r0 + row == c + 1 ? 1.0f : 0.0f) + c1 * x.y;
-        keep[t][4 * q + 2] = (r0 + row == c + 2 ? 1.0f : 0.0f) + c1 * x.z;
-        keep[t][4 * q + 3] = (r0 + row == c + 3 ? 1.0f : 0.0f) + c1 * x.w;
-      } else if (MODE == 1) {
-        const float4 g = *reinterpret_cast<const float4*>(p.G + moff + rowg + c);
-        keep[t][4 * q + 0] = g.x; keep[t][4 * q + 1] = g.y;
-        keep[t][4 * q + 2] = g.z; keep[t][4 * q + 3] = g.w;
-        const float ck = coef(k + 1, k);
-        x = make_float4(ck * g.x, ck * g.y, ck * g.z, ck * g.w);
-        if (valid[t]) *reinterpret_cast<float4*>(p.out + (long long)k * p.stride + moff + rowg + c) = x;
-      } else {
-        // A_{k+1}^T: element (row, c + e) = A_{k+1}[c + e][r0 + row]
-        const float* A = p.G + (long long)k * p.stride + moff + r0 + row;
-        x = make_float4(A[(long long)(c + 0) * b], A[(long long)(c + 1) * b], A[(long long)(c + 2) * b],
-                        A[(long long)(c + 3) * b]);
-        last[t][4 * q + 0] = x.x; last[t][4 * q + 1] = x.y;
-        last[t][4 * q + 2] = x.z; last[t][4 * q + 3] = x.w;
-      }
-      if (valid[t]) put_panel(t, q, x);
-    }
-  }
-
   // M = -S = S^T split into bf16 value and residual, in fragment order
   const uint16_t* Mh = p.Mh + moff;
   const uint16_t* Ml = p.Mh + (long long)p.count * bb + moff;
@@ -351,6 +308,99 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   auto ldm = [&](const __amdgpu_buffer_rsrc_t& r, int t, int kc) {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, tbase[t] + kc * 64, 0));
   };
+
+  // the first U K-steps of M for the first step; later steps get theirs from
+  // the previous step's last pass (M is the same in every step)
+  bf16x8 bnh[U][NT], bnl[U][NT];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bnh[u][t] = ldm(rh, t, 16 * u);
+      bnl[u][t] = ldm(rl, t, 16 * u);
+    }
+
+  float keep[NT][16];   // running Q (BUILD) or G (ABAR), accumulator layout
+  float last[NT][16];   // TCHAIN: the latest panel in fp32
+  auto put_panel = [&](int t, int q, float4 x) {
+    uint2 h, l;
+    split4(x, h, l);
+    const int c = n0[t] + 8 * q + 4 * hf;
+    *reinterpret_cast<uint2*>(ph + row * pitch + c) = h;
+    *reinterpret_cast<uint2*>(pl + row * pitch + c) = l;
+  };
+  // initial panel
+  if constexpr (MODE == 0) {
+    // the panel is S: its rows r0 .. r0 + 31 are the negated rows of M, which
+    // the 1 KiB fragment blocks of tile r0 / 32 hold (lane l: row l % 32, the 8
+    // columns from 16 ks + 8 (l / 32) in K-step ks); negating bf16 is exact.
+    // Each wave copies K-steps wave, wave + 4, ... (b <= 256: at most 4); loads
+    // past the block's last K-step are not stored (those past the block's end
+    // read zeros: buffer loads are range-checked)
+    const int nk = b >> 4;
+    const int rb = (r0 >> 5) * nk * 1024;
+    uint4 fh[4], fl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ks = wave + 4 * i;
+      fh[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, voff, rb + ks * 1024, 0));
+      fl[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rl, voff, rb + ks * 1024, 0));
+    }
+    constexpr uint32_t kNeg = 0x80008000u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ks = wave + 4 * i;
+      if (ks < nk) {
+        const int c = 16 * ks + 8 * hf;
+        *reinterpret_cast<uint4*>(ph + row * pitch + c) =
+            make_uint4(fh[i].x ^ kNeg, fh[i].y ^ kNeg, fh[i].z ^ kNeg, fh[i].w ^ kNeg);
+        *reinterpret_cast<uint4*>(pl + row * pitch + c) =
+            make_uint4(fl[i].x ^ kNeg, fl[i].y ^ kNeg, fl[i].z ^ kNeg, fl[i].w ^ kNeg);
+      }
+    }
+    __syncthreads();
+    // the running sum I + c_1 S, S = value + residual read back from the panel
+    const float c1 = coef(1, k);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = n0[t] + 8 * q + 4 * hf;
+        const uint2 h = *reinterpret_cast<const uint2*>(ph + row * pitch + c);
+        const uint2 l = *reinterpret_cast<const uint2*>(pl + row * pitch + c);
+        const uint32_t hv[4] = {h.x << 16, h.x & 0xffff0000u, h.y << 16, h.y & 0xffff0000u};
+        const uint32_t lv[4] = {l.x << 16, l.x & 0xffff0000u, l.y << 16, l.y & 0xffff0000u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          keep[t][4 * q + e] = (r0 + row == c + e ? 1.0f : 0.0f) +
+                               c1 * (__uint_as_float(hv[e]) + __uint_as_float(lv[e]));
+      }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = n0[t] + 8 * q + 4 * hf;
+        float4 x;
+        if constexpr (MODE == 1) {
+          const float4 g = *reinterpret_cast<const float4*>(p.G + moff + rowg + c);
+          keep[t][4 * q + 0] = g.x; keep[t][4 * q + 1] = g.y;
+          keep[t][4 * q + 2] = g.z; keep[t][4 * q + 3] = g.w;
+          const float ck = coef(k + 1, k);
+          x = make_float4(ck * g.x, ck * g.y, ck * g.z, ck * g.w);
+          if (valid[t]) *reinterpret_cast<float4*>(p.out + (long long)k * p.stride + moff + rowg + c) = x;
+        } else {
+          // A_{k+1}^T: element (row, c + e) = A_{k+1}[c + e][r0 + row]
+          const float* A = p.G + (long long)k * p.stride + moff + r0 + row;
+          x = make_float4(A[(long long)(c + 0) * b], A[(long long)(c + 1) * b], A[(long long)(c + 2) * b],
+                          A[(long long)(c + 3) * b]);
+          last[t][4 * q + 0] = x.x; last[t][4 * q + 1] = x.y;
+          last[t][4 * q + 2] = x.z; last[t][4 * q + 3] = x.w;
+        }
+        if (valid[t]) put_panel(t, q, x);
+      }
+    }
+  }
 
   for (int st = 0; st < k; ++st) {
     f32x16 acc[NT];
@@ -373,14 +423,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             at[t][4 * q + e] = A[(long long)(n0[t] + 8 * q + 4 * hf + e) * b];
     }
     __syncthreads();   // panel of the previous step written
-    bf16x8 bnh[U][NT], bnl[U][NT];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        bnh[u][t] = ldm(rh, t, 16 * u);
-        bnl[u][t] = ldm(rl, t, 16 * u);
-      }
     // (the launcher picks U so that 16 U divides b: no pass runs past the block)
     constexpr int kUnroll = BF > 0 ? BF / 16 : 1;
 #pragma unroll kUnroll
@@ -393,7 +435,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           bch[u][t] = bnh[u][t];
           bcl[u][t] = bnl[u][t];
         }
-      const int kn = min(kc + 16 * U, b - 16 * U);   // clamped: the last prefetch is unused
+      // the last pass fetches the first K-steps again, for the next step
+      const int kn = kc + 16 * U < b ? kc + 16 * U : 0;
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll

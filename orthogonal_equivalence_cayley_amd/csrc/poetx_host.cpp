@@ -805,7 +805,8 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
         // bf16 plans: split bf16 products, the split of -S in this run's part of
         // P0 (used only by the generic path of other sizes)
         uint16_t* split = split_buffer(pl, g, P0);
-        ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, S + g.q_off, g.b, g.count, 0, split};
+        // the split chains take their first panel from the split, not from S
+        ub.e[ub.n++] = poetx::TriEntry{it.theta + g.p_off, split ? nullptr : S + g.q_off, g.b, g.count, 0, split};
         poetx::ChainEntry e{};
         e.S = S + g.q_off; e.G = nullptr; e.out = it.Q + g.q_off;
         e.Mh = split;

@@ -134,7 +134,7 @@ hipError_t launch_block_regb(const GemmBf16& p, hipStream_t s);
 enum ChainMode { CHAIN_BUILD = 0, CHAIN_ABAR = 1, CHAIN_TCHAIN = 2 };
 constexpr int kChainMaxEntries = 32;
 struct ChainEntry {
-  const float* S;     // skew generators of the run's first block, fp32
+  const float* S;     // skew generators of the run's first block, fp32 (unused when Mh is set)
   const float* G;     // ABAR: dL/dQ of the run; TCHAIN: stored A_j of the run
   float* out;         // BUILD: Q; ABAR: A_j store; TCHAIN: T_1^T
   void* out_act;      // BUILD: copy of Q in the activation dtype, or null
@@ -159,7 +159,7 @@ hipError_t launch_chain_batch(int mode, const ChainBatch& cb, hipStream_t s);
 // over runs of chain_supported block sizes.
 struct TriEntry {
   const float* src;   // unpack: packed theta of the run; pack: b x b matrices of the run
-  float* dst;         // unpack: b x b matrices; pack: packed gradient of the run
+  float* dst;         // unpack: b x b matrices (or null: split only); pack: packed gradient of the run
   int b, count;
   long long e0;       // first workgroup of the run (set by the launcher)
   uint16_t* split = nullptr;   // unpack: also the bf16 split of -S (ChainEntry::Mh)
