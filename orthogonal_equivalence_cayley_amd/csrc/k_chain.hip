@@ -692,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
   const TriWork w = tri_work(tb);
   const int b = w.t.b, r0 = w.r0;
   const float* th = w.t.src + (long long)w.g * ((long long)b * (b - 1) / 2);
-  float* S = w.t.dst ? w.t.dst + (long long)w.g * b * b : nullptr;   // null: the split only
+  float* S = w.t.dst + (long long)w.g * b * b;
   const int nrow = r0 + kTriRows;
   for (int idx = threadIdx.x; idx < nrow * kTriRows; idx += kThreads) {
     const int c = idx / kTriRows, j = idx % kTriRows;
@@ -704,44 +704,104 @@ __global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
   for (int j = wave; j < kTriRows; j += kThreads / 64) {
     const int r = r0 + j;
     const float* up = th + (tri_off(r, r + 1, b) - (r + 1));   // theta(r, c) = up[c], c > r
-    if (S) {
-      float* row = S + (long long)r * b;
-      for (int c = lane; c < b; c += 64) {
-        float v = 0.0f;
-        if (c > r) v = up[c];
-        else if (c < r) v = -strip[c * kTriPitch + j];
-        row[c] = v;
-      }
+    float* row = S + (long long)r * b;
+    for (int c = lane; c < b; c += 64) {
+      float v = 0.0f;
+      if (c > r) v = up[c];
+      else if (c < r) v = -strip[c * kTriPitch + j];
+      row[c] = v;
     }
-    if (w.t.split) {
-      // M[r][c] = -S[r][c] = value + residual, both bf16, in fragment order:
-      // 8 consecutive columns per lane, one 16-byte store of each
-      uint16_t* mh = w.t.split + (long long)w.g * b * b;
-      uint16_t* ml = mh + (long long)w.t.count * b * b;
-      for (int c0 = 8 * lane; c0 < b; c0 += 8 * 64) {
-        uint32_t hw[4], lw[4];
+  }
+}
+
+// The split operand of the bf16 chains: M = -S = S^T, rows 32 nt .. 32 nt + 31
+// of one block, rounded to bf16 values and residuals in fragment order
+// (split_frag_offset). The tile of M is staged in LDS in fp32: above the
+// diagonal, M[r][c] = -theta(r, c), one contiguous run of packed parameters per
+// row; below it, M[r][c] = theta(c, r), 32 consecutive packed parameters of each
+// row c < r (a 128-byte run), stored transposed. Each wave then writes whole
+// 1 KiB fragment blocks of both halves.
+constexpr int kSplitRows = 32;
+__global__ __launch_bounds__(kThreads) void unpack_split_kernel(TriBatch tb) {
+  extern __shared__ __align__(16) float tile[];   // [kSplitRows][b + 4]
+  const TriEntry t = select_tri(tb, blockIdx.x);
+  const int b = t.b;
+  const int tiles = b / kSplitRows;
+  const int n = t.count * tiles;
+  const int loc = blockIdx.x - (int)t.e0;
+  if (loc >= n) return;   // padding of the entry to a multiple of 8 workgroups
+  // the tiles of one block on one XCD: each packed parameter is read twice (once
+  // per triangle), the second time from that XCD's L2
+  const int lid = (n % 8 == 0) ? (loc % 8) * (n / 8) + loc / 8 : loc;
+  const int g = lid / tiles, nt = lid - g * tiles, R0 = nt * kSplitRows;
+  const float* th = t.src + (long long)g * ((long long)b * (b - 1) / 2);
+  const int pitch = b + 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // every load of both triangles is issued before the first LDS write (b <=
+  // 256: at most 64 per lane), so that a workgroup waits for memory once. The
+  // loads are unconditional range-checked buffer loads of the block's packed
+  // parameters (an offset past the end reads 0) and the triangle tests select
+  // among the loaded values: a load under a branch waits for its value there.
+  const int nth = b * (b - 1) / 2;
+  const __amdgpu_buffer_rsrc_t rth =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(th), (short)0, nth * 4, 0x00020000);
+  auto ld = [&](int idx) {   // theta[idx], 0 outside the block
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rth, max(idx, 0) * 4, 0, 0));
+  };
+  // diagonal and above: rows R0 + wave + 4 jj, columns r .. b - 1 in four
+  // passes of 64 lanes; theta(r, c) at tri_off(r, c) = rs + c for c > r
+  float vu[8][4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float m[2];
+  for (int jj = 0; jj < 8; ++jj) {
+    const int r = R0 + wave + 4 * jj;
+    const int rs = (int)tri_off(r, r + 1, b) - (r + 1);
 #pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const int c = c0 + e + d;
-            float v = 0.0f;
-            if (c > r) v = up[c];
-            else if (c < r) v = -strip[c * kTriPitch + j];
-            m[d] = -v;
-          }
-          const __bf16 h0 = static_cast<__bf16>(m[0]), h1 = static_cast<__bf16>(m[1]);
-          const __bf16 l0 = static_cast<__bf16>(m[0] - static_cast<float>(h0));
-          const __bf16 l1 = static_cast<__bf16>(m[1] - static_cast<float>(h1));
-          hw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-          lw[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-        }
-        const long long o = split_frag_offset(r, c0, b);   // c0 % 8 == 0: a whole 16-byte piece
-        *reinterpret_cast<uint4*>(mh + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(ml + o) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int c = r + lane + 64 * i;
+      const float v = ld(rs + c);
+      vu[jj][i] = c > r ? -v : 0.0f;
     }
+  }
+  // below the diagonal: packed rows c < R0 + 31, two per wave instruction (half
+  // a wave each), columns R0 + j with c < R0 + j
+  const int j = lane & 31, col = R0 + j;
+  float vl[4][8];
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = 64 * pass + 8 * u + 2 * wave + (lane >> 5);
+      const float v = ld((int)tri_off(min(c, b - 1), col, b));
+      vl[pass][u] = c < col ? v : 0.0f;
+    }
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int jr = wave + 4 * jj, r = R0 + jr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = r + lane + 64 * i;
+      if (c < b) tile[jr * pitch + c] = vu[jj][i];
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = 64 * pass + 8 * u + 2 * wave + (lane >> 5);
+      if (c < col) tile[j * pitch + c] = vl[pass][u];
+    }
+  __syncthreads();
+  uint16_t* mh = t.split + (long long)g * b * b;
+  uint16_t* ml = mh + (long long)t.count * b * b;
+  const int nk = b / 16;
+  for (int ks = wave; ks < nk; ks += kThreads / 64) {
+    const float* src = tile + (lane & 31) * pitch + 16 * ks + 8 * (lane >> 5);
+    uint2 h0, l0, h1, l1;
+    split4(*reinterpret_cast<const float4*>(src), h0, l0);
+    split4(*reinterpret_cast<const float4*>(src + 4), h1, l1);
+    const long long o = ((long long)(nt * nk + ks) * 64 + lane) * 8;
+    *reinterpret_cast<uint4*>(mh + o) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+    *reinterpret_cast<uint4*>(ml + o) = make_uint4(l0.x, l0.y, l1.x, l1.y);
   }
 }
 
@@ -802,11 +862,39 @@ bool tri_batch_ok(const TriBatch& tb) {
 hipError_t launch_unpack_batch(const TriBatch& in, hipStream_t s) {
   if (in.n <= 0) return hipSuccess;
   if (!tri_batch_ok(in)) return hipErrorInvalidValue;
-  TriBatch tb = in;
-  const long long wgs = fill_offsets(tb);
-  if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(unpack_batch_kernel, dim3((unsigned)wgs), dim3(kThreads), strip_bytes(tb), s, tb);
-  return hipGetLastError();
+  // entries with an fp32 S (the strip kernel) and entries with a split (the
+  // tile kernel; an entry with both goes to both)
+  TriBatch tb = in, ts = in;
+  tb.n = ts.n = 0;
+  for (int i = 0; i < in.n; ++i) {
+    const TriEntry& e = in.e[i];
+    if (!e.dst && !e.split) return hipErrorInvalidValue;
+    if (e.split && !chain_split_supported(e.b)) return hipErrorInvalidValue;
+    if (e.dst) { tb.e[tb.n] = e; tb.e[tb.n++].split = nullptr; }
+    if (e.split) { ts.e[ts.n] = e; ts.e[ts.n++].dst = nullptr; }
+  }
+  if (tb.n > 0) {
+    const long long wgs = fill_offsets(tb);
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(unpack_batch_kernel, dim3((unsigned)wgs), dim3(kThreads), strip_bytes(tb), s, tb);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (ts.n > 0) {
+    // entries start on a multiple of 8 workgroups so the XCD-aware order applies
+    long long wgs = 0;
+    int bmax = 0;
+    for (int i = 0; i < ts.n; ++i) {
+      ts.e[i].e0 = wgs;
+      wgs += ((long long)ts.e[i].count * (ts.e[i].b / kSplitRows) + 7) / 8 * 8;
+      bmax = max(bmax, ts.e[i].b);
+    }
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    const size_t lds = (size_t)kSplitRows * (bmax + 4) * sizeof(float);
+    hipLaunchKernelGGL(unpack_split_kernel, dim3((unsigned)wgs), dim3(kThreads), lds, s, ts);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_pack_batch(const TriBatch& in, hipStream_t s) {
