@@ -807,27 +807,64 @@ __global__ __launch_bounds__(kThreads) void unpack_split_kernel(TriBatch tb) {
 
 // g(r, c) = sign * (M[r][c] - M[c][r]) for r < c, packed rows r0 .. r0 + 15 of
 // one block. M[c][r] (c > r) comes from columns r0 .. r0 + 15 of rows
-// r0 .. b - 1, read row-wise into LDS and used transposed.
+// r0 .. b - 1, read row-wise into LDS and used transposed. Loads are
+// unconditional range-checked buffer loads issued in batches (a load under a
+// branch would wait for its value there); strip rows past the block go to a
+// spare LDS row and stores past a row's end to an offset outside the buffer,
+// which the hardware drops. NI: 64-column passes per row (b <= 64 NI).
+template <int NI>
 __global__ __launch_bounds__(kThreads) void pack_batch_kernel(TriBatch tb) {
-  extern __shared__ float strip[];   // [largest b of the batch][kTriPitch]
+  extern __shared__ float strip[];   // [largest b of the batch + 1][kTriPitch]
   const TriWork w = tri_work(tb);
   const int b = w.t.b, r0 = w.r0;
   const float* M = w.t.src + (long long)w.g * b * b;
   float* out = w.t.dst + (long long)w.g * ((long long)b * (b - 1) / 2);
+  const __amdgpu_buffer_rsrc_t rm =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(M), (short)0, b * b * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(out, (short)0, b * (b - 1) / 2 * 4, 0x00020000);
+  auto ldm = [&](int idx) {   // M[idx] of the block, 0 past its end
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, idx * 4, 0, 0));
+  };
   const int nrow = b - r0;
-  for (int idx = threadIdx.x; idx < nrow * kTriRows; idx += kThreads) {
-    const int cl = idx / kTriRows, j = idx % kTriRows;
-    strip[cl * kTriPitch + j] = M[(long long)(r0 + cl) * b + r0 + j];
+  const int tid = threadIdx.x;
+  for (int base = 0; base < nrow * kTriRows; base += 8 * kThreads) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * kThreads + tid;
+      const int cl = idx / kTriRows, j = idx % kTriRows;
+      v[u] = ldm((r0 + cl) * b + r0 + j);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * kThreads + tid;
+      const int cl = idx / kTriRows, j = idx % kTriRows;
+      strip[min(cl, b) * kTriPitch + j] = v[u];   // row b: the spare row
+    }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const float sign = tb.sign;
-  for (int j = wave; j < kTriRows; j += kThreads / 64) {
-    const int r = r0 + j;
-    const float* row = M + (long long)r * b;
-    float* dst = out + (tri_off(r, r + 1, b) - (r + 1));   // g(r, c) = dst[c], c > r
-    for (int c = r + 1 + lane; c < b; c += 64)
-      dst[c] = sign * (row[c] - strip[(c - r0) * kTriPitch + j]);
+  constexpr int kRowsPerWave = kTriRows / (kThreads / 64);
+  float a[kRowsPerWave][NI];
+#pragma unroll
+  for (int jj = 0; jj < kRowsPerWave; ++jj) {
+    const int r = r0 + wave + 4 * jj;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) a[jj][i] = ldm(r * b + r + 1 + lane + 64 * i);
+  }
+#pragma unroll
+  for (int jj = 0; jj < kRowsPerWave; ++jj) {
+    const int j = wave + 4 * jj, r = r0 + j;
+    const int rs = (int)tri_off(r, r + 1, b) - (r + 1);   // g(r, c) at rs + c, c > r
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = r + 1 + lane + 64 * i;
+      const float g = sign * (a[jj][i] - strip[(min(c, b) - r0) * kTriPitch + j]);
+      const int off = c < b ? (rs + c) * 4 : 0x7ffffff0;   // past the end: dropped
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, g), ro, off, 0, 0);
+    }
   }
 }
 
@@ -847,7 +884,7 @@ long long fill_offsets(TriBatch& tb) {
 size_t strip_bytes(const TriBatch& tb) {
   int bmax = 0;
   for (int i = 0; i < tb.n; ++i) bmax = max(bmax, tb.e[i].b);
-  return (size_t)bmax * kTriPitch * sizeof(float);
+  return (size_t)(bmax + 1) * kTriPitch * sizeof(float);
 }
 
 bool tri_batch_ok(const TriBatch& tb) {
@@ -903,7 +940,12 @@ hipError_t launch_pack_batch(const TriBatch& in, hipStream_t s) {
   TriBatch tb = in;
   const long long wgs = fill_offsets(tb);
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(pack_batch_kernel, dim3((unsigned)wgs), dim3(kThreads), strip_bytes(tb), s, tb);
+  int bmax = 0;
+  for (int i = 0; i < tb.n; ++i) bmax = max(bmax, tb.e[i].b);
+  if (bmax <= 256)
+    hipLaunchKernelGGL(pack_batch_kernel<4>, dim3((unsigned)wgs), dim3(kThreads), strip_bytes(tb), s, tb);
+  else
+    hipLaunchKernelGGL(pack_batch_kernel<8>, dim3((unsigned)wgs), dim3(kThreads), strip_bytes(tb), s, tb);
   return hipGetLastError();
 }
 
