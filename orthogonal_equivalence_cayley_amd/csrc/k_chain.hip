@@ -687,29 +687,62 @@ __device__ __forceinline__ TriWork tri_work(const TriBatch& tb) {
 // rows r0 .. r0 + 15 of one block. Above the diagonal each row is a contiguous
 // run of packed parameters; below it the values come from the 16 packed columns
 // r0 .. r0 + 15 (rows 0 .. r0 + 15), read row-wise into LDS and used transposed.
+// Loads are unconditional range-checked buffer loads issued in batches (a load
+// under a branch would wait for its value there); strip rows past the block go
+// to a spare LDS row and stores past a row's end to an offset outside the
+// buffer, which the hardware drops. NI: 64-column passes per row (b <= 64 NI).
+template <int NI>
 __global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
-  extern __shared__ float strip[];   // [largest b of the batch][kTriPitch]
+  extern __shared__ float strip[];   // [largest b of the batch + 1][kTriPitch]
   const TriWork w = tri_work(tb);
   const int b = w.t.b, r0 = w.r0;
   const float* th = w.t.src + (long long)w.g * ((long long)b * (b - 1) / 2);
   float* S = w.t.dst + (long long)w.g * b * b;
+  const __amdgpu_buffer_rsrc_t rth =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(th), (short)0, b * (b - 1) / 2 * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(S, (short)0, b * b * 4, 0x00020000);
+  auto ld = [&](int idx) {   // theta[idx] of the block, 0 outside it
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rth, max(idx, 0) * 4, 0, 0));
+  };
+  const int tid = threadIdx.x;
   const int nrow = r0 + kTriRows;
-  for (int idx = threadIdx.x; idx < nrow * kTriRows; idx += kThreads) {
-    const int c = idx / kTriRows, j = idx % kTriRows;
-    const int col = r0 + j;
-    strip[c * kTriPitch + j] = c < col ? th[tri_off(c, col, b)] : 0.0f;
+  for (int base = 0; base < nrow * kTriRows; base += 8 * kThreads) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * kThreads + tid;
+      const int c = idx / kTriRows, col = r0 + idx % kTriRows;
+      v[u] = ld((int)tri_off(min(c, b - 1), col, b));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * kThreads + tid;
+      const int c = idx / kTriRows, j = idx % kTriRows;
+      strip[min(c, b) * kTriPitch + j] = c < r0 + j ? v[u] : 0.0f;   // row b: the spare row
+    }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int j = wave; j < kTriRows; j += kThreads / 64) {
-    const int r = r0 + j;
-    const float* up = th + (tri_off(r, r + 1, b) - (r + 1));   // theta(r, c) = up[c], c > r
-    float* row = S + (long long)r * b;
-    for (int c = lane; c < b; c += 64) {
-      float v = 0.0f;
-      if (c > r) v = up[c];
-      else if (c < r) v = -strip[c * kTriPitch + j];
-      row[c] = v;
+  const int lane = tid & 63, wave = tid >> 6;
+  constexpr int kRowsPerWave = kTriRows / (kThreads / 64);
+  float up[kRowsPerWave][NI];
+#pragma unroll
+  for (int jj = 0; jj < kRowsPerWave; ++jj) {
+    const int r = r0 + wave + 4 * jj;
+    const int rs0 = (int)tri_off(r, r + 1, b) - (r + 1);   // theta(r, c) at rs0 + c, c > r
+#pragma unroll
+    for (int i = 0; i < NI; ++i) up[jj][i] = ld(rs0 + lane + 64 * i);
+  }
+#pragma unroll
+  for (int jj = 0; jj < kRowsPerWave; ++jj) {
+    const int j = wave + 4 * jj, r = r0 + j;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = lane + 64 * i;
+      const float lo = -strip[min(c, b) * kTriPitch + j];
+      const float v = c > r ? up[jj][i] : (c < r ? lo : 0.0f);
+      const int off = c < b ? (r * b + c) * 4 : 0x7ffffff0;   // past the row: dropped
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, off, 0, 0);
     }
   }
 }
@@ -913,7 +946,12 @@ hipError_t launch_unpack_batch(const TriBatch& in, hipStream_t s) {
   if (tb.n > 0) {
     const long long wgs = fill_offsets(tb);
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(unpack_batch_kernel, dim3((unsigned)wgs), dim3(kThreads), strip_bytes(tb), s, tb);
+    int bmax = 0;
+    for (int i = 0; i < tb.n; ++i) bmax = max(bmax, tb.e[i].b);
+    if (bmax <= 256)
+      hipLaunchKernelGGL(unpack_batch_kernel<4>, dim3((unsigned)wgs), dim3(kThreads), strip_bytes(tb), s, tb);
+    else
+      hipLaunchKernelGGL(unpack_batch_kernel<8>, dim3((unsigned)wgs), dim3(kThreads), strip_bytes(tb), s, tb);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
