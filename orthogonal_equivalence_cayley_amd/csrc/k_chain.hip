@@ -376,6 +376,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                                c1 * (__uint_as_float(hv[e]) + __uint_as_float(lv[e]));
       }
   } else {
+    // every load first: out may alias G, so no load moves above a store
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = n0[t] + 8 * q + 4 * hf;
+        if constexpr (MODE == 1) {
+          const float4 g = *reinterpret_cast<const float4*>(p.G + moff + rowg + c);
+          keep[t][4 * q + 0] = g.x; keep[t][4 * q + 1] = g.y;
+          keep[t][4 * q + 2] = g.z; keep[t][4 * q + 3] = g.w;
+        } else {
+          // A_{k+1}^T: element (row, c + e) = A_{k+1}[c + e][r0 + row]
+          const float* A = p.G + (long long)k * p.stride + moff + r0 + row;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) last[t][4 * q + e] = A[(long long)(c + e) * b];
+        }
+      }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -383,19 +400,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int c = n0[t] + 8 * q + 4 * hf;
         float4 x;
         if constexpr (MODE == 1) {
-          const float4 g = *reinterpret_cast<const float4*>(p.G + moff + rowg + c);
-          keep[t][4 * q + 0] = g.x; keep[t][4 * q + 1] = g.y;
-          keep[t][4 * q + 2] = g.z; keep[t][4 * q + 3] = g.w;
           const float ck = coef(k + 1, k);
-          x = make_float4(ck * g.x, ck * g.y, ck * g.z, ck * g.w);
+          x = make_float4(ck * keep[t][4 * q], ck * keep[t][4 * q + 1], ck * keep[t][4 * q + 2],
+                          ck * keep[t][4 * q + 3]);
           if (valid[t]) *reinterpret_cast<float4*>(p.out + (long long)k * p.stride + moff + rowg + c) = x;
         } else {
-          // A_{k+1}^T: element (row, c + e) = A_{k+1}[c + e][r0 + row]
-          const float* A = p.G + (long long)k * p.stride + moff + r0 + row;
-          x = make_float4(A[(long long)(c + 0) * b], A[(long long)(c + 1) * b], A[(long long)(c + 2) * b],
-                          A[(long long)(c + 3) * b]);
-          last[t][4 * q + 0] = x.x; last[t][4 * q + 1] = x.y;
-          last[t][4 * q + 2] = x.z; last[t][4 * q + 3] = x.w;
+          x = make_float4(last[t][4 * q], last[t][4 * q + 1], last[t][4 * q + 2], last[t][4 * q + 3]);
         }
         if (valid[t]) put_panel(t, q, x);
       }
