@@ -99,14 +99,28 @@ __global__ __launch_bounds__(kThreads) void scale2_kernel(const float* __restric
   }
 }
 
+// out[i] = part[i] + part[stride + i] + ..., added in order of the split from
+// 0.0f. The loads of eight splits are issued together before their adds (one
+// at a time, each add would wait for its load); VEC consecutive elements per
+// thread (VEC = 4: n, stride and the pointers are multiples of 4 floats).
+template <int VEC>
 __global__ __launch_bounds__(kThreads) void sum_splits_kernel(const float* __restrict__ part,
                                                               int nsplit, long long stride,
                                                               long long n, float* __restrict__ out) {
-  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n;
-       i += (long long)gridDim.x * kThreads) {
-    float acc = 0.0f;
-    for (int s = 0; s < nsplit; ++s) acc += part[s * stride + i];
-    out[i] = acc;
+  typedef float V __attribute__((ext_vector_type(VEC)));
+  for (long long i = ((long long)blockIdx.x * kThreads + threadIdx.x) * VEC; i < n;
+       i += (long long)gridDim.x * kThreads * VEC) {
+    V acc = (V)(0.0f);
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      V v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = s0 + u < nsplit ? *reinterpret_cast<const V*>(part + (s0 + u) * stride + i) : (V)(0.0f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < nsplit) acc += v[u];
+    }
+    *reinterpret_cast<V*>(out + i) = acc;
   }
 }
 
@@ -165,8 +179,13 @@ hipError_t launch_scale2(const float* in, float c, float* o1, float* o2, long lo
 hipError_t launch_sum_splits(const float* part, int nsplit, long long stride, long long n,
                              float* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(sum_splits_kernel, dim3(grid1d(n)), dim3(kThreads), 0, s, part, nsplit,
-                     stride, n, out);
+  const bool v4 = n % 4 == 0 && stride % 4 == 0 && ((uintptr_t)part & 15) == 0 && ((uintptr_t)out & 15) == 0;
+  if (v4)
+    hipLaunchKernelGGL(sum_splits_kernel<4>, dim3(grid1d(n / 4)), dim3(kThreads), 0, s, part, nsplit,
+                       stride, n, out);
+  else
+    hipLaunchKernelGGL(sum_splits_kernel<1>, dim3(grid1d(n)), dim3(kThreads), 0, s, part, nsplit,
+                       stride, n, out);
   return hipGetLastError();
 }
 
