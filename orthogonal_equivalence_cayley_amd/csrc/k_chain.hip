@@ -85,37 +85,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int li = lane & 15, lk = lane >> 4;        // operand lane coordinates
   const int k = cb.k;
 
-  // initial panel
+  // initial panel: every load first (out may alias G, so no load moves above a
+  // store; a load under a branch waits for its value there); tiles past the
+  // last one read the clamped columns and are dropped
   float keep[MT][NT][4];   // G (ABAR) or the running Q (BUILD) in accumulator layout
+  float x0[MT][NT][4];     // the panel's values
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int tile = wave + 4 * t;
+      const int col = bcol[t] + li;
+      if constexpr (MODE == 2) {
+        // A_{k+1}^T panel rows 16 mt + 4 lk + 0..3 = A_{k+1}[col][r0 + ...]
+        const float4 at =
+            load_t4(p.G + (long long)k * p.stride + moff + (long long)col * b + r0 + 16 * mt + 4 * lk);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) keep[mt][t][v] = 0.0f;
-      if (tile >= ntiles) continue;
-      const int col = tile * 16 + li;
-      float4 at;   // TCHAIN: A_{k+1}^T panel rows 16 mt + 4 lk + 0..3 = A_{k+1}[col][r0 + ...]
-      if (MODE == 2)
-        at = load_t4(p.G + (long long)k * p.stride + moff + (long long)col * b + r0 + 16 * mt + 4 * lk);
+        for (int v = 0; v < 4; ++v) x0[mt][t][v] = f4(at, v);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const long long o = (long long)(r0 + 16 * mt + 4 * lk + v) * b + col;
+          x0[mt][t][v] = MODE == 0 ? S[o] : p.G[moff + o];
+        }
+      }
+    }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const bool valid = wave + 4 * t < ntiles;
+      const int col = bcol[t] + li;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = 16 * mt + 4 * lk + v;
         const long long o = (long long)(r0 + row) * b + col;
-        float x;
+        float x = x0[mt][t][v];
         if (MODE == 0) {
-          x = S[o];
-          keep[mt][t][v] = (r0 + row == col ? 1.0f : 0.0f) + coef(1, k) * x;
+          keep[mt][t][v] = valid ? (r0 + row == col ? 1.0f : 0.0f) + coef(1, k) * x : 0.0f;
         } else if (MODE == 1) {
-          const float g = p.G[moff + o];
-          keep[mt][t][v] = g;
-          x = coef(k + 1, k) * g;
-          p.out[(long long)k * p.stride + moff + o] = x;
+          keep[mt][t][v] = valid ? x : 0.0f;
+          x = coef(k + 1, k) * x;
+          if (valid) p.out[(long long)k * p.stride + moff + o] = x;
         } else {
-          x = f4(at, v);
+          keep[mt][t][v] = 0.0f;
         }
-        panel[row * pitch + col] = x;
+        if (valid) panel[row * pitch + col] = x;
       }
     }
 
