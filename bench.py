@@ -177,7 +177,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
-              "(sharding by tokens is described in DESIGN.md).", file=sys.stderr)
+              "(across GPUs it would shard by tokens, each GPU holding every layer's blocks).", file=sys.stderr)
         return 2
 
     import numpy as np
