@@ -209,6 +209,10 @@ poetx_status poetx_build_orth_batch(int32_t count, const poetx_plan* const* plan
  *            the permuted order the backward reads it in. A caller that keeps
  *            U_saved instead of X for the backward spares it a gather at no
  *            extra memory.
+ *   X = NULL with U_saved set: U_saved already holds U (poetx_gather_cols of
+ *            X by pi_P) and the forward skips its gather, so a caller can run
+ *            the gather apart, e.g. on another stream ahead of the rest;
+ *            X = NULL without U_saved is POETX_ERR_INVALID_ARG.
  *   ws       device, poetx_workspace_size(plan, T, POETX_WS_FORWARD) bytes.
  * T = 0 is a no-op. */
 poetx_status poetx_forward(const poetx_plan* plan, int64_t T, const void* X, const void* Wt,

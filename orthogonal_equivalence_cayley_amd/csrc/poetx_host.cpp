@@ -1079,7 +1079,8 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
                            size_t ws_bytes, void* stream) {
   if (!pl || T < 0) return POETX_ERR_INVALID_ARG;
   if (T == 0) return POETX_OK;
-  if (!X || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !Y) return POETX_ERR_INVALID_ARG;
+  // X may be NULL when U_saved already holds the gathered input
+  if ((!X && !U_saved) || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !Y) return POETX_ERR_INVALID_ARG;
   for (const void* p : {X, Wt, (const void*)pi_R, (const void*)pi_P, Q_R, Q_P, (const void*)Y,
                         (const void*)Wa_saved, (const void*)U_saved, (const void*)ws})
     if (!aligned16(p)) return POETX_ERR_ALIGNMENT;
@@ -1091,8 +1092,8 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
   if (U_saved) w.U = U_saved;   // the gather writes the caller's buffer
   const int es = elsize(pl);
   poetx_status st;
-  // 1. gather: U = X Pi_P^T
-  {
+  // 1. gather: U = X Pi_P^T (none when the caller passes U instead of X)
+  if (X) {
     StageScope sc(POETX_STAGE_GATHER, s);
     HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
   }

@@ -158,14 +158,22 @@ class PoetxLayer:
             self._ws[key] = cur
         return cur
 
-    def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
+    def forward(self, X: Optional[torch.Tensor], Y: Optional[torch.Tensor] = None,
                 Wa: Optional[torch.Tensor] = None, save: bool = True, keep_u: bool = False,
                 U: Optional[torch.Tensor] = None) -> torch.Tensor:
         """save: keep Wa for the backward (POET-Xfast); else it is recomputed.
         keep_u: keep the input in permuted order, U = X Pi_P^T (in U if given),
-        which the backward then reads instead of gathering X again."""
-        T = X.shape[0]
-        assert X.shape == (T, self.n) and X.dtype == self.tdtype and X.is_contiguous()
+        which the backward then reads instead of gathering X again.
+        X None: U already holds X Pi_P^T (gather_u) and the forward skips its
+        gather (keep_u is implied)."""
+        if X is None:
+            assert U is not None, "forward without X needs the gathered input U"
+            keep_u = True
+            T = U.shape[0]
+            assert U.shape == (T, self.n) and U.dtype == self.tdtype and U.is_contiguous()
+        else:
+            T = X.shape[0]
+            assert X.shape == (T, self.n) and X.dtype == self.tdtype and X.is_contiguous()
         if Y is None:
             Y = torch.empty(T, self.m, dtype=self.tdtype, device=self.device)
         if save and Wa is None:
@@ -178,6 +186,15 @@ class PoetxLayer:
         self.Wa = Wa if save else None
         self.U = U if keep_u else None
         return Y
+
+    def gather_u(self, X: torch.Tensor, U: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """U = X Pi_P^T, the input in the permuted order forward(None, U=U) takes."""
+        T = X.shape[0]
+        assert X.shape == (T, self.n) and X.dtype == self.tdtype and X.is_contiguous()
+        if U is None:
+            U = torch.empty(T, self.n, dtype=self.tdtype, device=self.device)
+        self.plan.gather_cols(T, self.n, X, self.pi_P, U)
+        return U
 
     def _check_saved(self, T: int) -> None:
         # no saved Wa (forward(save=False)): the backward recomputes it (POET-Xmem)

@@ -96,6 +96,10 @@ def test_forward_argument_errors():
     assert call(T=0) == px.POETX_OK                      # T = 0 is a no-op
     assert call(T=-1) == px.POETX_ERR_INVALID_ARG
     assert call(X=None) == px.POETX_ERR_INVALID_ARG
+    # X = NULL is accepted when U_saved holds the gathered input (the later
+    # checks then decide)
+    assert call(X=None, U=A + 4) == px.POETX_ERR_ALIGNMENT
+    assert call(X=None, U=A, wsb=ws - 1) == px.POETX_ERR_WORKSPACE
     assert call(Y=A + 8) == px.POETX_ERR_ALIGNMENT
     assert call(wsb=ws - 1) == px.POETX_ERR_WORKSPACE
     assert call(ws=None) == px.POETX_ERR_WORKSPACE

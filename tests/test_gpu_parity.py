@@ -287,6 +287,33 @@ def test_xmem_recompute_matches_saved(case):
     _compare(got, ref, ["Y", "G_X", "g_theta_R", "g_theta_P"], tol, "xmem")
 
 
+@pytest.mark.parametrize("dt, c", [
+    ("bf16", dict(m=512, n=256, bR=(256, 256), bP=(128, 128), T=300, k=4)),
+    ("f32", dict(m=70, n=45, bR=(30, 40), bP=(45,), T=9, k=3)),
+])
+def test_forward_from_gathered_input(dt, c):
+    """forward(None, U=gather_u(X)) skips its gather and gives forward(X)'s Y,
+    Wa, U and backward bit for bit."""
+    import torch
+    inp = workloads.small_case(c["m"], c["n"], c["bR"], c["bP"], T=c["T"], seed=c["m"] + 31,
+                               dtype=dt, theta_std=0.01 if dt == "bf16" else 0.05)
+    log(f"forward from U {dt} {c}")
+    L = make_layer(inp, c["k"], dt)
+    L.build()
+    X, G = to_dev(inp.X, dt), to_dev(inp.G_Y, dt)
+    Y1 = L.forward(X, keep_u=True).clone()
+    Wa1, U1 = L.Wa.clone(), L.U.clone()
+    g1 = [t.clone() for t in L.backward(X, G)]
+    U = L.gather_u(X)
+    Y2 = L.forward(None, U=U)
+    torch.cuda.synchronize()
+    assert torch.equal(U, U1) and torch.equal(Y2, Y1) and torch.equal(L.Wa, Wa1)
+    g2 = [t.clone() for t in L.backward(None, G)]
+    torch.cuda.synchronize()
+    for u, v in zip(g1, g2):
+        assert torch.equal(u, v)
+
+
 # ---------------------------------------------------------------- outer loop
 
 @pytest.mark.parametrize("dt, c", [
