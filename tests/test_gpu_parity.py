@@ -314,6 +314,48 @@ def test_forward_from_gathered_input(dt, c):
         assert torch.equal(u, v)
 
 
+def test_two_streams_match_one_stream():
+    """Two layers' forward and backward issued on two HIP streams at once (each
+    call with its own workspace, as the header allows) give the one-stream
+    results bit for bit: the library keeps no state shared between calls."""
+    import torch
+    from orthogonal_equivalence_cayley_amd import build_many, param_grad_many
+    specs = [workloads.small_case(512, 256, (256, 256), (128, 128), T=600, seed=41 + i, dtype="bf16",
+                                  theta_std=0.01) for i in range(2)]
+    layers = [make_layer(inp, 4, "bf16") for inp in specs]
+    X = [to_dev(inp.X, "bf16") for inp in specs]
+    G = [to_dev(inp.G_Y, "bf16") for inp in specs]
+    outs = [dict(Y=torch.empty(600, 512, dtype=torch.bfloat16, device="cuda"),
+                 GX=torch.empty(600, 256, dtype=torch.bfloat16, device="cuda"),
+                 g=[torch.empty(L.nparam[s], dtype=torch.float32, device="cuda") for s in (0, 1)])
+            for L in layers]
+
+    def run(two):
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream() if two else main
+        build_many(layers)
+        side.wait_stream(main)
+        for i, L in enumerate(layers):
+            with torch.cuda.stream(side if (two and i == 1) else main):
+                L.forward(X[i], Y=outs[i]["Y"])
+        for i, L in enumerate(layers):
+            with torch.cuda.stream(side if (two and i == 1) else main):
+                L.backward_dq(X[i], G[i], G_X=outs[i]["GX"])
+        main.wait_stream(side)
+        param_grad_many(layers, [o["g"] for o in outs])
+        torch.cuda.synchronize()
+        return [[o["Y"].clone(), o["GX"].clone(), o["g"][0].clone(), o["g"][1].clone()] for o in outs]
+
+    one = run(False)
+    for _ in range(2):
+        two = run(True)
+        for a, b in zip(one, two):
+            for u, v in zip(a, b):
+                assert torch.equal(u, v)
+    ref = oracle.layer_reference(specs[1], 4)
+    _compare(dict(Y=to_np(one[1][0]), G_X=to_np(one[1][1])), ref, ["Y", "G_X"], TOL_BF16, "streams")
+
+
 # ---------------------------------------------------------------- outer loop
 
 @pytest.mark.parametrize("dt, c", [
