@@ -4,10 +4,13 @@
 One step = one pass of the whole path over the workload: build of every
 layer's Cayley-Neumann blocks (both sides), the input-centric forward of every
 layer (saving Wa), and the backward of every layer (gradients w.r.t. X and
-both sides' packed skew parameters). The default workload is the seven
-linears of a LLaMA-style block at hidden 2048 (q, k, v, o 2048x2048; gate, up
-5632x2048; down 2048x5632), b = 256, k = 4, bf16 activations and weights, fp32
-skew parameters, 16384 tokens, every layer independently seeded. Inputs are
+both sides' packed skew parameters). Every block product runs on the
+activations, in the stage order of the input-centric method; --fold times the
+variant that folds one side's blocks into the weight where the batch is large.
+The default workload is the seven linears of a LLaMA-style block at hidden 2048
+(q, k, v, o 2048x2048; gate, up 5632x2048; down 2048x5632), b = 256, k = 4,
+bf16 activations and weights, fp32 skew parameters, 16384 tokens, every layer
+independently seeded. Inputs are
 synthetic (workloads.py) and resident in HBM before the timed region. The
 layers a LLaMA block computes independently (q, k, v; gate, up) run on two HIP
 streams by default (--streams 1: layer by layer on one stream); the per-stage
@@ -43,24 +46,31 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def stage_flops(w, T, xmem=False, exact=False):
-    """Algorithmic flops per stage for one step of the workload (with xmem, the
-    backward's recomputation of the P blocks and the Wt product counts too)."""
+def stage_flops(w, T, xmem=False, exact=False, fold=False, int8=False):
+    """Flops each stage executes in one step of the workload. Input-centric
+    (the default): 2 T sum(b^2) per side and pass for the block products. With
+    --fold, a side folded into the weight costs 2 m sum(b_P^2) (forward, T >= m)
+    or 2 n sum(b_R^2) (backward, T >= n) instead. With xmem, the backward's
+    recomputation of the P blocks and the Wt product counts too."""
     f = dict(w0_fwd=0.0, w0_bwd=0.0, block_fwd=0.0, block_bwd=0.0, dq=0.0, build=0.0, cnp_bwd=0.0)
     for sp in w.layers:
-        sq = sum(b * b for b in sp.bsz_R) + sum(b * b for b in sp.bsz_P)
+        sqR = sum(b * b for b in sp.bsz_R)
+        sqP = sum(b * b for b in sp.bsz_P)
         cube = sum(b ** 3 for b in sp.bsz_R) + sum(b ** 3 for b in sp.bsz_P)
+        fold_f = fold and not int8 and T >= sp.m
+        fold_b = fold and not int8 and T >= sp.n
+        p_fwd = 2.0 * (sp.m if fold_f else T) * sqP
         f["w0_fwd"] += 2.0 * T * sp.m * sp.n
-        f["block_fwd"] += 2.0 * T * sq
+        f["block_fwd"] += p_fwd + 2.0 * T * sqR
         f["build"] += 2.0 * (11 if exact else w.k) * cube
         if w.backward:
             f["w0_bwd"] += 2.0 * T * sp.m * sp.n
-            f["block_bwd"] += 2.0 * T * sq
-            f["dq"] += 2.0 * T * sq
+            f["block_bwd"] += 2.0 * (sp.n if fold_b else T) * sqR + 2.0 * T * sqP
+            f["dq"] += 2.0 * T * (sqR + sqP)
             f["cnp_bwd"] += 2.0 * (13 if exact else 2 * w.k) * cube
             if xmem:
                 f["w0_fwd"] += 2.0 * T * sp.m * sp.n
-                f["block_fwd"] += 2.0 * T * sum(b * b for b in sp.bsz_P)
+                f["block_fwd"] += p_fwd
     return f
 
 
@@ -88,8 +98,9 @@ TRAFFIC_SOURCES = {"w0_gemm_nn_lds": "orthogonal_equivalence_cayley_amd/csrc/k_g
                    "w0_gemm_nt_lds": "orthogonal_equivalence_cayley_amd/csrc/k_gemm_lds.hip"}
 
 
-def load_traffic(kernel: str, workload: str):
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+def load_traffic(kernel: str, workload: str, fold: bool = False):
+    suffix = "_fold" if fold else ""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}{suffix}_traffic.md")
     try:
         with open(path) as f:
             m = re.search(r"```json\n(.*?)\n```", f.read(), re.S)
@@ -115,10 +126,23 @@ def copy_calibration(mib: int, reps: int = 3) -> None:
     del src, dst
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, tokens: int):
-    """float64 oracle on the workload's own layers: build + forward + backward at
-    0 and `tokens` tokens per layer, extrapolated linearly to the full T."""
-    import numpy as np
+    """float64 oracle on the workload's own layers, every layer at `tokens`
+    tokens (build + forward + backward). At the workload's full T the figure is
+    measured; below it, the oracle also runs at 0 tokens (the build and the
+    chain rule, which do not depend on T) and the per-token part is scaled to
+    the full T, which the sample states."""
     import oracle
     import workloads
     try:
@@ -127,28 +151,37 @@ def cpu_baseline(w, tokens: int):
                        if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    fixed = per_tok = 0.0
+    tokens = min(tokens, w.T)
+    full = tokens == w.T
+    fixed = per_tok = measured = 0.0
     for li in range(len(w.layers)):
-        inp = workloads.layer_inputs(w, li, T=tokens)
-        for T in (0, tokens):
+        inp = workloads.layer_inputs(w, li, T=tokens, draw_grad=w.backward)
+        for T in ((tokens,) if full else (0, tokens)):
             sub = type("I", (), dict(spec=inp.spec, W0=inp.W0, theta_R=inp.theta_R,
                                      theta_P=inp.theta_P, pi_R=inp.pi_R, pi_P=inp.pi_P,
-                                     X=inp.X[:T], G_Y=inp.G_Y[:T]))()
+                                     X=inp.X[:T], G_Y=None if inp.G_Y is None else inp.G_Y[:T]))()
             t0 = time.perf_counter()
             oracle.layer_reference(sub, w.k, backward_pass=w.backward)
             dt = time.perf_counter() - t0
+            measured += dt
             if T == 0:
                 t_fixed = dt
-            else:
+            elif not full:
                 per_tok += max(dt - t_fixed, 0.0) / tokens
-        fixed += t_fixed
-    est = fixed + per_tok * w.T
+        if not full:
+            fixed += t_fixed
+        del inp
+    est = measured if full else fixed + per_tok * w.T
+    what = "build + forward + backward" if w.backward else "build + forward"
+    sample = (f"float64 NumPy oracle, {what} of all {len(w.layers)} layers on their own inputs at "
+              f"the full {w.T} tokens: {est:.1f} s per step, measured" if full else
+              f"float64 NumPy oracle, {what} of all {len(w.layers)} layers on their own inputs at 0 "
+              f"and {tokens} tokens; the per-token part scaled to {w.T} tokens (est. {est:.1f} s "
+              f"per step; {measured:.1f} s measured)")
     return {
         "value": w.T / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"float64 NumPy oracle on all {len(w.layers)} layers' own inputs: build + forward + "
-                   f"backward at 0 and {tokens} tokens per layer, extrapolated linearly to "
-                   f"{w.T} tokens (est. {est:.1f} s per step)"),
-        "seconds_per_step_est": est,
+        "sample": sample, "seconds_per_step": est, "measured": full,
+        "cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
     }
 
 
@@ -158,7 +191,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4, help="workload id in workloads.WORKLOADS")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens per layer of the oracle's timed sample (default: the full T "
+                         "up to 16384 tokens of hidden 2048, 4096 tokens above)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing pass")
     ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
@@ -174,97 +209,35 @@ def main() -> int:
                     help="POET-XQ: frozen weight stored as INT8 (one scale per row)")
     ap.add_argument("--xmem", action="store_true",
                     help="POET-Xmem: keep no Wa; the backward recomputes it from X")
+    ap.add_argument("--fold", action="store_true",
+                    help="variant: fold the P blocks into the weight in the forward (T >= m) and the R "
+                         "blocks in the backward (T >= n) instead of applying them to the activations")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
               "(across GPUs it would shard by tokens, each GPU holding every layer's blocks).", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import workloads
-    from orthogonal_equivalence_cayley_amd import PoetxLayer, build_many, param_grad_many, poetx
+    from orthogonal_equivalence_cayley_amd import build_many, poetx
+    from orthogonal_equivalence_cayley_amd.block_step import BlockStep
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = workloads.WORKLOADS[args.workload]
     T = w.T
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(tdt).cuda()
 
     log(f"bench: {w.name} T={T} layers={len(w.layers)} k={w.k}")
-    layers, bufs = [], []
-    for li in range(len(w.layers)):
-        inp = workloads.layer_inputs(w, li, draw_grad=w.backward)
-        sp = inp.spec
-        L = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, w.k, dtype=w.dtype,
-                       weight="int8" if args.xq else "dense",
-                       cayley="exact" if args.exact else "neumann")
-        L.set_weight(dev(inp.W0), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
-        L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
-        b = dict(X=dev(inp.X), Y=torch.empty(T, sp.m, dtype=tdt, device="cuda"),
-                 Wa=None if args.xmem else torch.empty(T, sp.m, dtype=tdt, device="cuda"),
-                 U=torch.empty(T, sp.n, dtype=tdt, device="cuda"))
-        if w.backward:
-            b.update(G=dev(inp.G_Y), GX=torch.empty(T, sp.n, dtype=tdt, device="cuda"),
-                     g=[torch.empty(L.nparam[s], dtype=torch.float32, device="cuda") for s in (0, 1)])
-        L.workspace(poetx.WS_BUILD)
-        L.workspace(poetx.WS_FORWARD, T)
-        if w.backward:
-            L.workspace(poetx.WS_BACKWARD, T)
-            L._ws_grad(0)
-            L._ws_grad(1)
-        layers.append(L)
-        bufs.append(b)
-        del inp
+    blk = BlockStep([workloads.layer_inputs(w, li, draw_grad=w.backward) for li in range(len(w.layers))],
+                    w.k, w.dtype, backward=w.backward, streams=args.streams,
+                    weight="int8" if args.xq else "dense", cayley="exact" if args.exact else "neumann",
+                    fold="weight" if args.fold else "none", xmem=args.xmem)
+    layers = blk.layers
+    step = blk.step
     torch.cuda.synchronize()
     log("bench: inputs resident")
-
-    # groups of layers with no data dependence between them in a llama block:
-    # q, k, v read the same input; gate and up too (o follows the attention,
-    # down the gated product). With --streams 2 the members of a group alternate
-    # between the main stream and a side stream, and each group waits for the one
-    # before it (the backward walks the groups in reverse).
-    indep = ({"q", "k", "v"}, {"gate", "up"})
-    groups = []
-    for li, sp in enumerate(w.layers):
-        g = next((s for s in indep if sp.name in s), None)
-        if groups and g is not None and w.layers[groups[-1][-1]].name in g:
-            groups[-1].append(li)
-        else:
-            groups.append([li])
-    side = torch.cuda.Stream() if args.streams == 2 else None
-
-    def run_groups(order, fn, two):
-        main = torch.cuda.current_stream()
-        for grp in order:
-            if not two or len(grp) == 1:
-                for li in grp:
-                    fn(li)
-                continue
-            side.wait_stream(main)
-            for j, li in enumerate(grp):
-                with torch.cuda.stream(main if j % 2 == 0 else side):
-                    fn(li)
-            main.wait_stream(side)
-
-    def fwd(li):
-        L, b = layers[li], bufs[li]
-        # the input is kept in the permuted order the backward reads it in
-        L.forward(b["X"], Y=b["Y"], Wa=b["Wa"], save=not args.xmem, keep_u=True, U=b["U"])
-
-    def bwd(li):
-        L, b = layers[li], bufs[li]
-        L.backward_dq(b["X"], b["G"], G_X=b["GX"])
-
-    def step(two=side is not None):
-        build_many(layers)
-        run_groups(groups, fwd, two)
-        if w.backward:
-            # activation path layer by layer, then the chain rule through the
-            # parameterisation of all layers in one batched call
-            run_groups([list(reversed(g)) for g in reversed(groups)], bwd, two)
-            param_grad_many(layers, [b["g"] for b in bufs])
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -290,7 +263,7 @@ def main() -> int:
     log(f"bench: {ms_per_step:.3f} ms/step")
 
     xmem = bool(args.xmem and w.backward)
-    flops = stage_flops(w, T, xmem, args.exact)
+    flops = stage_flops(w, T, xmem, args.exact, args.fold, args.xq)
     merge = None
     if args.merge:
         # outer loop: fold the trained factors of every layer into its weight
@@ -335,10 +308,11 @@ def main() -> int:
 
     # dominant kernel: the frozen-weight product with the largest time share.
     # The forward is always the K-contiguous (NT) kernel; the backward is too
-    # when the library folds D_R into a transposed weight (T >= n, whole
-    # 256-wide tiles of n, R blocks multiples of 64; not for INT8 weights).
-    folded_t = (not args.xq and all(T >= sp.n and sp.n % 256 == 0 and all(b % 64 == 0 for b in sp.bsz_R)
-                                    for sp in w.layers) and w.dtype == "bf16")
+    # only in the fold variant, which folds D_R into a transposed weight (T >= n,
+    # whole 256-wide tiles of n, R blocks multiples of 64; not for INT8 weights).
+    folded_t = (args.fold and not args.xq and w.dtype == "bf16" and
+                all(T >= sp.n and sp.n % 256 == 0 and all(b % 64 == 0 for b in sp.bsz_R)
+                    for sp in w.layers))
     stage_kernel = {"w0_fwd": "w0_gemm_nt_lds", "w0_bwd": "w0_gemm_nt_lds" if folded_t else "w0_gemm_nn_lds"}
     if args.xq:
         stage_kernel = {k: v.replace("w0_", "w0q_") for k, v in stage_kernel.items()}
@@ -359,7 +333,7 @@ def main() -> int:
     avg_s = ms_tot / launches * 1e-3
     achieved = flops_per_launch / avg_s
     traffic, traffic_note = None, None
-    rec, why = load_traffic(kernel, w.name) if not (xmem or args.xq) else \
+    rec, why = load_traffic(kernel, w.name, args.fold) if not (xmem or args.xq or args.exact) else \
         (None, "counters taken on the dense Xfast step only")
     if rec is not None:
         traffic = rec["traffic_bytes_per_launch"]
@@ -404,9 +378,15 @@ def main() -> int:
             "frozen_weight": "int8, one fp32 scale per row (POET-XQ)" if args.xq else w.dtype,
             "orthogonal_map": "exact Cayley (doubling build, closed-form gradient)" if args.exact
             else f"Cayley-Neumann, k = {w.k}",
+            "block_products": ("fold variant: P blocks folded into the weight in the forward where "
+                               "T >= m, R blocks in the backward where T >= n, the other side on the "
+                               "activations" if args.fold else
+                               "on the activations (input-centric order: gather, P blocks, Wt product, "
+                               "R blocks, scatter; the backward in reverse)"),
+            "fold": bool(args.fold),
             "streams": args.streams,
             "schedule": ("independent layers (q, k, v; gate, up) on two HIP streams, in block order; "
-                         "backward in reverse" if args.streams == 2 and any(len(g) > 1 for g in groups)
+                         "backward in reverse" if blk.two_streams
                          else "layer by layer on one stream"),
         },
         "roofline": {
@@ -429,7 +409,10 @@ def main() -> int:
         out["merge"] = merge
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+        tok = args.cpu_tokens
+        if tok is None:
+            tok = w.T if max(sp.n for sp in w.layers) <= 2048 else 4096
+        out["cpu_baseline"] = cpu_baseline(w, tok)
     print(json.dumps(out), flush=True)
     return 0
 

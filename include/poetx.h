@@ -77,6 +77,19 @@ typedef enum { POETX_WEIGHT_DENSE = 0, POETX_WEIGHT_INT8_ROWS = 1 } poetx_weight
  *     and the exact gradient dL/dS = (I+Q)^T G (I-S)^{-T}. k is ignored. Runs on
  *     the generic fp32 batched GEMM, block run by block run. */
 typedef enum { POETX_CAYLEY_NEUMANN = 0, POETX_CAYLEY_EXACT = 1 } poetx_cayley;
+
+/* Where the block-diagonal factors are applied.
+ *   POETX_FOLD_NONE (the default): on the activations at every batch size, in
+ *     the order of the input-centric method ([PX] §2.A): gather, blocks of P,
+ *     Wt product, blocks of R, scatter (backward: the reverse). No weight-sized
+ *     product with an orthogonal factor is ever formed.
+ *   POETX_FOLD_WEIGHT: a variant that reassociates one product per pass when
+ *     the batch is large: the forward forms Wt D_P (m x n, one side's blocks
+ *     applied to the weight's columns) when T >= m and then Wa = U (Wt D_P)^T;
+ *     the backward forms D_R Wt when T >= n and then G_V = G_Z (D_R Wt). Same
+ *     results up to rounding (the bf16 rounding moves from the activation to the
+ *     folded weight); not for INT8 weights. */
+typedef enum { POETX_FOLD_NONE = 0, POETX_FOLD_WEIGHT = 1 } poetx_fold;
 typedef enum { POETX_SIDE_R = 0, POETX_SIDE_P = 1 } poetx_side;
 typedef enum {
   POETX_WS_BUILD = 0,       /* poetx_build_orth, one item of poetx_build_orth_batch */
@@ -99,6 +112,7 @@ typedef struct {
                                always fp32; accumulation is always fp32.            */
   int32_t weight;           /* poetx_weight: how Wt is stored                       */
   int32_t cayley;           /* poetx_cayley: truncated series or exact transform    */
+  int32_t fold;             /* poetx_fold: activations only, or the weight-side fold */
 } poetx_desc;
 
 /* Create a plan. Host only: no device call is made, so it works without a GPU.

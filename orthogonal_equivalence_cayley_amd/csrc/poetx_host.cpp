@@ -22,6 +22,7 @@ struct poetx_plan {
   int m = 0, n = 0, k = 0, dtype = 0;
   int weight = POETX_WEIGHT_DENSE;   // poetx_weight: how Wt is stored
   int cayley = POETX_CAYLEY_NEUMANN; // poetx_cayley: truncated series or exact transform
+  int fold = POETX_FOLD_NONE;        // poetx_fold: activations only, or the weight-side fold
   std::vector<int> bsz[2];
   std::vector<Seg> segs[2];
   long long nparam[2] = {0, 0};
@@ -145,14 +146,19 @@ struct BwdWs {
   float *dQ[2], *part;
 };
 
-// Folding one side's blocks into the frozen weight instead of applying them to
-// the activations: Wa = (U D_P^T) Wt^T = U (Wt D_P)^T in the forward and
-// G_V = (G_Z D_R) Wt = G_Z (D_R Wt) in the backward, whose G_Wa nothing else
-// reads. The weight-side product costs 2 m n b flops against 2 T n b (2 T m b)
-// on the activations plus a T x n (T x m) round trip through HBM, so it is taken
-// when T >= m (T >= n). INT8 weights keep the activation-side products.
-bool fold_fwd(const poetx_plan* pl, long long T) { return !wq(pl) && T > 0 && T >= pl->m; }
-bool fold_bwd(const poetx_plan* pl, long long T) { return !wq(pl) && T > 0 && T >= pl->n; }
+// POETX_FOLD_WEIGHT plans only (the default keeps every block product on the
+// activations): one side's blocks are folded into the frozen weight instead,
+// Wa = (U D_P^T) Wt^T = U (Wt D_P)^T in the forward and G_V = (G_Z D_R) Wt =
+// G_Z (D_R Wt) in the backward, whose G_Wa nothing else reads. The weight-side
+// product costs 2 m n b flops against 2 T n b (2 T m b) on the activations plus
+// a T x n (T x m) round trip through HBM, so it is taken when T >= m (T >= n).
+// INT8 weights keep the activation-side products.
+bool fold_fwd(const poetx_plan* pl, long long T) {
+  return pl->fold == POETX_FOLD_WEIGHT && !wq(pl) && T > 0 && T >= pl->m;
+}
+bool fold_bwd(const poetx_plan* pl, long long T) {
+  return pl->fold == POETX_FOLD_WEIGHT && !wq(pl) && T > 0 && T >= pl->n;
+}
 
 // Buffers of the chain rule through the parameterisation, for one side.
 struct ChainWs {
@@ -879,6 +885,7 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
     return POETX_ERR_INVALID_ARG;
   if (d->cayley != POETX_CAYLEY_NEUMANN && d->cayley != POETX_CAYLEY_EXACT)
     return POETX_ERR_INVALID_ARG;
+  if (d->fold != POETX_FOLD_NONE && d->fold != POETX_FOLD_WEIGHT) return POETX_ERR_INVALID_ARG;
   const int32_t* bs[2] = {d->bsz_R, d->bsz_P};
   const int nb[2] = {d->nb_R, d->nb_P};
   const int dims[2] = {d->m, d->n};
@@ -906,6 +913,7 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
   pl->m = d->m; pl->n = d->n; pl->k = d->k; pl->dtype = d->dtype;
   pl->weight = d->weight;
   pl->cayley = d->cayley;
+  pl->fold = d->fold;
   for (int side = 0; side < 2; ++side) {
     pl->dim[side] = dims[side];
     long long q = 0, p = 0;
@@ -1096,25 +1104,6 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
   if (X) {
     StageScope sc(POETX_STAGE_GATHER, s);
     HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
-  }
-  // Without a saved Wa (POET-Xmem) both sides fold when T >= m and T >= n:
-  // Y = (U (D_R Wt D_P)^T) Pi_R, one product with the doubly folded weight
-  // (built in the free Wa buffer, T x m >= m x n).
-  if (!Wa_saved && fold_fwd(pl, T) && fold_bwd(pl, T)) {
-    {
-      StageScope sc(POETX_STAGE_BLOCK_FWD, s);
-      if ((st = fold_p(pl, Wt, Q_P, w.Wf, s)) != POETX_OK) return st;
-      if ((st = fold_r(pl, w.Wf, Q_R, w.Wa, s)) != POETX_OK) return st;
-    }
-    {
-      StageScope sc(POETX_STAGE_W0_FWD, s);
-      if ((st = gemm(pl, poetx::GEMM_W0, Op{w.U, pl->n, 1}, Op{w.Wa, pl->n, 1}, w.Z, pl->m, (int)T,
-                     pl->m, pl->n, 1, 0, 0, 0, 1, 0, false, s)) != POETX_OK)
-        return st;
-    }
-    StageScope sc(POETX_STAGE_SCATTER, s);
-    HIP_TRY(poetx::launch_scatter_cols(w.Z, pi_R, Y, T, pl->m, es, s));
-    return POETX_OK;
   }
   // 2. blocks of P: V = U D_P^T, or folded into the weight, Wf = Wt D_P
   const bool fold = fold_fwd(pl, T);

@@ -39,6 +39,9 @@ WEIGHT_INT8_ROWS = 1
 CAYLEY_NEUMANN = 0
 CAYLEY_EXACT = 1
 
+FOLD_NONE = 0
+FOLD_WEIGHT = 1
+
 EXPORTED = (
     "poetx_plan_create", "poetx_plan_destroy", "poetx_param_count", "poetx_block_elems",
     "poetx_workspace_size", "poetx_status_string", "poetx_last_hip_error", "poetx_permute_weight",
@@ -67,7 +70,7 @@ class Desc(ctypes.Structure):
         ("nb_R", ctypes.c_int32), ("nb_P", ctypes.c_int32),
         ("bsz_R", ctypes.POINTER(ctypes.c_int32)), ("bsz_P", ctypes.POINTER(ctypes.c_int32)),
         ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("weight", ctypes.c_int32),
-        ("cayley", ctypes.c_int32),
+        ("cayley", ctypes.c_int32), ("fold", ctypes.c_int32),
     ]
 
 
@@ -204,14 +207,15 @@ class Plan:
     """Owns a poetx_plan (host-only object; creating one needs no GPU)."""
 
     def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
-                 dtype: int, weight: int = WEIGHT_DENSE, cayley: int = CAYLEY_NEUMANN):
+                 dtype: int, weight: int = WEIGHT_DENSE, cayley: int = CAYLEY_NEUMANN,
+                 fold: int = FOLD_NONE):
         self.m, self.n, self.k, self.dtype = int(m), int(n), int(k), int(dtype)
-        self.weight, self.cayley = int(weight), int(cayley)
+        self.weight, self.cayley, self.fold = int(weight), int(cayley), int(fold)
         self.bsz_R, self.bsz_P = tuple(int(b) for b in bsz_R), tuple(int(b) for b in bsz_P)
         aR = (ctypes.c_int32 * max(1, len(self.bsz_R)))(*self.bsz_R)
         aP = (ctypes.c_int32 * max(1, len(self.bsz_P)))(*self.bsz_P)
         d = Desc(self.m, self.n, len(self.bsz_R), len(self.bsz_P), aR, aP, self.k, self.dtype,
-                 self.weight, self.cayley)
+                 self.weight, self.cayley, self.fold)
         h = ctypes.c_void_p()
         self._h = None
         _check(LIB.poetx_plan_create(ctypes.byref(d), ctypes.byref(h)), "poetx_plan_create")

@@ -218,3 +218,23 @@ def test_cayley_mode_validation():
     nm = px.Plan(64, 48, (32, 32), (16, 32), 3, px.POETX_FP32)
     # the doubling build keeps two more block arrays
     assert ex.workspace_size(0, px.WS_BUILD) > nm.workspace_size(0, px.WS_BUILD)
+
+
+def test_fold_option():
+    """The weight-side fold is a plan option, off by default: without it the
+    forward workspace holds the activation-side V at every T and no folded
+    weight; with it (T >= m) the folded m x n weight replaces V."""
+    bf = px.POETX_BF16
+    args = (256, 512, (256,), (256, 256), 4, bf, px.WEIGHT_DENSE, px.CAYLEY_NEUMANN)
+    none = px.Plan(*args)
+    fold = px.Plan(*args, px.FOLD_WEIGHT)
+    T = 600
+    U = V = T * 512 * 2
+    Wa = Z = T * 256 * 2
+    assert none.workspace_size(T, px.WS_FORWARD) >= U + V + Wa + Z
+    assert fold.workspace_size(T, px.WS_FORWARD) < none.workspace_size(T, px.WS_FORWARD)
+    # below the fold threshold both plans lay out the same workspace
+    assert fold.workspace_size(100, px.WS_FORWARD) == none.workspace_size(100, px.WS_FORWARD)
+    with pytest.raises(px.PoetxError) as e:
+        px.Plan(*args, 2)
+    assert e.value.status == px.POETX_ERR_INVALID_ARG

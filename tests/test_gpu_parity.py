@@ -510,13 +510,14 @@ def test_exact_cayley_layer(dt, c):
 ])
 @pytest.mark.parametrize("save", [True, False])
 def test_layer_with_folded_blocks(dt, c, save):
-    """With T >= m (T >= n) the P (R) blocks are folded into the frozen weight
-    instead of being applied to T rows; results against the oracle."""
+    """Plans with the weight-side fold: with T >= m (T >= n) the P (R) blocks
+    are folded into the frozen weight instead of being applied to T rows;
+    results against the oracle."""
     import torch
     inp = workloads.small_case(c["m"], c["n"], c["bR"], c["bP"], T=c["T"], seed=c["T"] + c["m"], dtype=dt,
                                theta_std=0.01 if dt == "bf16" else 0.05)
     log(f"folded {dt} {c} save={save}")
-    L = make_layer(inp, c["k"], dt)
+    L = make_layer(inp, c["k"], dt, fold="weight")
     L.build()
     X, G = to_dev(inp.X, dt), to_dev(inp.G_Y, dt)
     Y = L.forward(X, save=save)
