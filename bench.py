@@ -232,7 +232,7 @@ def main() -> int:
     log(f"bench: {w.name} T={T} layers={len(w.layers)} k={w.k}")
     blk = BlockStep([workloads.layer_inputs(w, li, draw_grad=w.backward) for li in range(len(w.layers))],
                     w.k, w.dtype, backward=w.backward, streams=args.streams,
-                    weight="int8" if args.xq else "dense", cayley="exact" if args.exact else "neumann",
+                    weight="int8" if args.xq else "dense_t", cayley="exact" if args.exact else "neumann",
                     fold="weight" if args.fold else "none", xmem=args.xmem)
     layers = blk.layers
     step = blk.step
@@ -313,7 +313,10 @@ def main() -> int:
     folded_t = (args.fold and not args.xq and w.dtype == "bf16" and
                 all(T >= sp.n and sp.n % 256 == 0 and all(b % 64 == 0 for b in sp.bsz_R)
                     for sp in w.layers))
-    stage_kernel = {"w0_fwd": "w0_gemm_nt_lds", "w0_bwd": "w0_gemm_nt_lds" if folded_t else "w0_gemm_nn_lds"}
+    # With the weight kept beside its transpose (the default for dense weights)
+    # the backward reads WtT K-contiguous: the NT kernel as well.
+    nt_bwd = folded_t or (not args.xq and not args.fold and w.dtype == "bf16")
+    stage_kernel = {"w0_fwd": "w0_gemm_nt_lds", "w0_bwd": "w0_gemm_nt_lds" if nt_bwd else "w0_gemm_nn_lds"}
     if args.xq:
         stage_kernel = {k: v.replace("w0_", "w0q_") for k, v in stage_kernel.items()}
     per_kernel = {}
@@ -375,7 +378,8 @@ def main() -> int:
             "passes": "build+forward+backward" if w.backward else "build+forward",
             "saved_activation": ("none (POET-Xmem: recomputed)" if xmem else "Wa (POET-Xfast)")
             + "; layer input kept as U = X Pi_P^T",
-            "frozen_weight": "int8, one fp32 scale per row (POET-XQ)" if args.xq else w.dtype,
+            "frozen_weight": "int8, one fp32 scale per row (POET-XQ)" if args.xq
+            else f"{w.dtype}, kept with its transpose",
             "orthogonal_map": "exact Cayley (doubling build, closed-form gradient)" if args.exact
             else f"Cayley-Neumann, k = {w.k}",
             "block_products": ("fold variant: P blocks folded into the weight in the forward where "

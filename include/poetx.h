@@ -65,8 +65,17 @@ typedef enum { POETX_FP32 = 0, POETX_BF16 = 1 } poetx_dtype;
  *     is symmetric with one fp32 scale per row of Wt. Layout: int8 q [m, n]
  *     row-major, then at byte offset ceil(m n / 256) * 256 the fp32 scales [m];
  *     Wt[i][j] = s[i] * q[i][j]. Built by poetx_quantize_weight; needs bf16
- *     and m, n multiples of 256, n <= 32768. */
-typedef enum { POETX_WEIGHT_DENSE = 0, POETX_WEIGHT_INT8_ROWS = 1 } poetx_weight;
+ *     and m, n multiples of 256, n <= 32768.
+ *   POETX_WEIGHT_DENSE_T:   POETX_WEIGHT_DENSE followed by the transpose of Wt,
+ *     WtT [n, m] in the plan dtype at byte offset ceil(m n elsize / 256) * 256
+ *     (poetx_permute_weight writes both). The frozen weight is kept twice so that
+ *     the backward's product G_V = G_Wa Wt reads it K-contiguous, like the
+ *     forward's V Wt^T; results are identical to POETX_WEIGHT_DENSE. */
+typedef enum {
+  POETX_WEIGHT_DENSE = 0,
+  POETX_WEIGHT_INT8_ROWS = 1,
+  POETX_WEIGHT_DENSE_T = 2
+} poetx_weight;
 
 /* Orthogonal map of each block.
  *   POETX_CAYLEY_NEUMANN: Q = (I+S) sum_{j<=k} S^j, the truncated series of [PX]
@@ -90,6 +99,20 @@ typedef enum { POETX_CAYLEY_NEUMANN = 0, POETX_CAYLEY_EXACT = 1 } poetx_cayley;
  *     results up to rounding (the bf16 rounding moves from the activation to the
  *     folded weight); not for INT8 weights. */
 typedef enum { POETX_FOLD_NONE = 0, POETX_FOLD_WEIGHT = 1 } poetx_fold;
+
+/* How the index mappings run ([PX] §2.B: permutations as index arrays).
+ *   POETX_INDEX_SEPARATE (the default): each gather and scatter is its own
+ *     pass over the rows (whole rows staged in LDS, coalesced 16-byte reads and
+ *     writes), next to the block products, which keep each block of Q in
+ *     registers while token tiles stream past.
+ *   POETX_INDEX_FUSED: bf16 sides of 256-wide blocks up to 2048 features run
+ *     the index mapping inside the block products: one pass stages 32 whole
+ *     token rows in LDS, permutes them there and multiplies them block by block,
+ *     so the permuted activation never goes through HBM. Each 32-row panel then
+ *     streams every Q block of the side from L2 (4x the activation bytes it
+ *     saves at 2048 features), which on MI355X makes these passes slower than
+ *     the separate ones; same results. Other sides keep the separate kernels. */
+typedef enum { POETX_INDEX_SEPARATE = 0, POETX_INDEX_FUSED = 1 } poetx_index;
 typedef enum { POETX_SIDE_R = 0, POETX_SIDE_P = 1 } poetx_side;
 typedef enum {
   POETX_WS_BUILD = 0,       /* poetx_build_orth, one item of poetx_build_orth_batch */
@@ -113,6 +136,7 @@ typedef struct {
   int32_t weight;           /* poetx_weight: how Wt is stored                       */
   int32_t cayley;           /* poetx_cayley: truncated series or exact transform    */
   int32_t fold;             /* poetx_fold: activations only, or the weight-side fold */
+  int32_t index;            /* poetx_index: separate index passes, or fused         */
 } poetx_desc;
 
 /* Create a plan. Host only: no device call is made, so it works without a GPU.
@@ -143,7 +167,9 @@ const char* poetx_last_hip_error(void);
  * ([PX] §2.B "Réduction": permutations folded into W ahead of time, leaving
  * two index operations per step): Wt[i][j] = W0[pi_R[i]][pi_P[j]].
  *   W0   device [m, n] (dtype)        pi_R device int32 [m]
- *   pi_P device int32 [n]             Wt   device [m, n] (dtype), not aliasing W0
+ *   pi_P device int32 [n]             Wt   device, poetx_weight_bytes(plan)
+ *        bytes, not aliasing W0: [m, n] (dtype), for POETX_WEIGHT_DENSE_T plans
+ *        followed by WtT[j][i] = Wt[i][j]
  * Bit-exact copy. POETX_ERR_UNSUPPORTED for INT8 plans (poetx_quantize_weight). */
 poetx_status poetx_permute_weight(const poetx_plan* plan, const void* W0,
                                   const int32_t* pi_R, const int32_t* pi_P,

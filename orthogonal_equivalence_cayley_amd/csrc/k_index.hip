@@ -256,6 +256,24 @@ __global__ __launch_bounds__(kThreads) void scatter_cols_direct(
     for (int q = threadIdx.x; q < dim; q += kThreads) out[t * dim + idx[q]] = in[t * dim + q];
 }
 
+// out[c][r] = in[r][c] for an R x C matrix (32 x 32 tiles through LDS; edges
+// of sizes that are not multiples of 32 checked)
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ in, E* __restrict__ out,
+                                                        int R, int C) {
+  __shared__ E t[32][33];
+  const int tc = (C + 31) / 32;
+  const int r0 = (blockIdx.x / tc) * 32, c0 = (blockIdx.x % tc) * 32;
+  const int x = threadIdx.x & 31, y = threadIdx.x >> 5;   // 8 rows per pass
+#pragma unroll
+  for (int i = 0; i < 32; i += 8)
+    if (r0 + y + i < R && c0 + x < C) t[y + i][x] = in[(long long)(r0 + y + i) * C + c0 + x];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 32; i += 8)
+    if (c0 + y + i < C && r0 + x < R) out[(long long)(c0 + y + i) * R + r0 + x] = t[x][y + i];
+}
+
 inline int grid_for(long long units) {
   const long long cap = 256LL * 16;   // 16 workgroups per CU on 256 CUs
   return (int)(units < cap ? (units < 1 ? 1 : units) : cap);
@@ -335,6 +353,19 @@ hipError_t launch_gather_cols(const void* in, long long in_ld, const int32_t* ro
                               hipStream_t s) {
   if (elsize == 2) return gather_typed<uint16_t>(in, in_ld, rows, idx, out, T, dim, s);
   return gather_typed<uint32_t>(in, in_ld, rows, idx, out, T, dim, s);
+}
+
+hipError_t launch_transpose(const void* in, void* out, int R, int C, int elsize, hipStream_t s) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  const long long tiles = (long long)((R + 31) / 32) * ((C + 31) / 32);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  if (elsize == 2)
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3((unsigned)tiles), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, C);
+  else
+    hipLaunchKernelGGL(transpose_kernel<uint32_t>, dim3((unsigned)tiles), dim3(256), 0, s,
+                       static_cast<const uint32_t*>(in), static_cast<uint32_t*>(out), R, C);
+  return hipGetLastError();
 }
 
 hipError_t launch_scatter_cols(const void* in, const int32_t* idx, void* out, long long T,

@@ -23,6 +23,7 @@ struct poetx_plan {
   int weight = POETX_WEIGHT_DENSE;   // poetx_weight: how Wt is stored
   int cayley = POETX_CAYLEY_NEUMANN; // poetx_cayley: truncated series or exact transform
   int fold = POETX_FOLD_NONE;        // poetx_fold: activations only, or the weight-side fold
+  int index = POETX_INDEX_SEPARATE;  // poetx_index: separate index passes, or fused
   std::vector<int> bsz[2];
   std::vector<Seg> segs[2];
   long long nparam[2] = {0, 0};
@@ -36,6 +37,13 @@ constexpr size_t kAlign = 256;
 
 // INT8 weight: int8 [m, n] rows of Wt, then (256-byte aligned) the fp32 row scales
 bool wq(const poetx_plan* pl) { return pl->weight == POETX_WEIGHT_INT8_ROWS; }
+// dense weight kept with its transpose: WtT [n, m] after Wt, 256-byte aligned
+bool wpair(const poetx_plan* pl) { return pl->weight == POETX_WEIGHT_DENSE_T; }
+size_t wtt_off(const poetx_plan* pl) {
+  const size_t es = pl->dtype == POETX_BF16 ? 2 : 4;
+  return ((size_t)pl->m * pl->n * es + kAlign - 1) / kAlign * kAlign;
+}
+const void* wtt(const poetx_plan* pl, const void* Wt) { return static_cast<const char*>(Wt) + wtt_off(pl); }
 size_t qscale_off(const poetx_plan* pl) {
   return ((size_t)pl->m * pl->n + kAlign - 1) / kAlign * kAlign;
 }
@@ -143,6 +151,7 @@ int dq_splits(const poetx_plan* pl, int side, long long T) {
 struct FwdWs { void *U, *V, *Wa, *Z, *Wf; };
 struct BwdWs {
   void *GZ, *GWa, *GV, *U, *GU, *Wf;
+  void* QT[2];   // bf16 Q^T of a side that runs the fused products (or null)
   float *dQ[2], *part;
 };
 
@@ -158,6 +167,16 @@ bool fold_fwd(const poetx_plan* pl, long long T) {
 }
 bool fold_bwd(const poetx_plan* pl, long long T) {
   return pl->fold == POETX_FOLD_WEIGHT && !wq(pl) && T > 0 && T >= pl->n;
+}
+
+// POETX_INDEX_FUSED plans: one side's index mapping and block products in one
+// pass over the rows (k_panel.hip), for bf16 sides made of 256-wide blocks, up
+// to 2048 features.
+bool panel_side(const poetx_plan* pl, int side) {
+  if (pl->index != POETX_INDEX_FUSED) return false;
+  if (pl->dtype != POETX_BF16 || pl->segs[side].size() != 1) return false;
+  const Seg& g = pl->segs[side][0];
+  return poetx::panel_supported(pl->dim[side], g.b, g.count);
 }
 
 // Buffers of the chain rule through the parameterisation, for one side.
@@ -206,6 +225,8 @@ size_t layout_bwd(const poetx_plan* pl, long long T, void* base, BwdWs* w, Chain
   x.U = c.take(es * T * pl->n);
   x.GU = c.take(es * T * pl->n);
   x.Wf = (fold_fwd(pl, T) || fold_bwd(pl, T)) ? c.take(es * (size_t)pl->m * pl->n) : nullptr;
+  for (int side = 0; side < 2; ++side)
+    x.QT[side] = panel_side(pl, side) ? c.take(2 * pl->nelem[side]) : nullptr;
   x.dQ[0] = (float*)c.take(4 * pl->nelem[0]);
   x.dQ[1] = (float*)c.take(4 * pl->nelem[1]);
   long long part = 0;
@@ -650,49 +671,63 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
     HIP_TRY(poetx::launch_zero(dQ[1], pl->nelem[1], s));
     return POETX_OK;
   }
-  // Without a saved Wa (POET-Xmem) the forward's first three stages run again,
-  // with the forward's kernels and launch shapes, so Wa is bit-identical to the
-  // one poetx_forward would have saved. U stays for dQ_P; V borrows the G_U
-  // buffer and Wa the G_Wa buffer, both dead until the products that overwrite
-  // them, which run after their last reads on the same stream.
-  const void* Wa = Wa_saved;
   // U = X Pi_P^T: kept by the caller, or gathered here (once)
   const void* U = U_saved ? U_saved : w.U;
-  if (!Wa_saved) {
-    if (!U_saved) {
+  const bool foldb = fold_bwd(pl, T);
+  const bool foldt = foldb && fold_rt_ok(pl);
+  // fused R pass: gathers G_Y, keeps G_Z and applies the R blocks (B = Q_R^T)
+  // in one pass; INT8 weights scale G_Wa's columns and keep the separate kernels
+  const bool fused_r = !foldb && !wq(pl) && w.QT[0];
+
+  // Without a saved Wa (POET-Xmem) the forward's first three stages run again,
+  // with the forward's kernels and launch shapes, so Wa is bit-identical to the
+  // one poetx_forward would have saved. V borrows the G_U buffer and Wa the G_Wa
+  // buffer, both dead until their next writer. With the fused R pass (which
+  // writes G_Wa and G_Z before dQ_R reads Wa) this runs after the Wt product has
+  // consumed G_Wa; otherwise first.
+  auto recompute_wa = [&]() -> poetx_status {
+    const bool fold = fold_fwd(pl, T);
+    // the fused pass gathers X and applies the P blocks at once, keeping U
+    const bool fused = !fold && !U_saved && panel_side(pl, POETX_SIDE_P);
+    if (!U_saved && !fused) {
       StageScope sc(POETX_STAGE_GATHER, s);
       HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
     }
-    const bool fold = fold_fwd(pl, T);
     {
       StageScope sc(POETX_STAGE_BLOCK_FWD, s);
-      st = fold ? fold_p(pl, Wt, Q_P, w.Wf, s)
-                : apply_blocks(pl, POETX_SIDE_P, T, U, Q_P, w.GU, true, s);
-      if (st != POETX_OK) return st;
+      poetx_status r;
+      if (fused) {
+        HIP_TRY(poetx::launch_panel_block(X, pi_P, Q_P, w.GU, w.U, T, pl->n, true, false, s));
+        r = POETX_OK;
+      } else {
+        r = fold ? fold_p(pl, Wt, Q_P, w.Wf, s) : apply_blocks(pl, POETX_SIDE_P, T, U, Q_P, w.GU, true, s);
+      }
+      if (r != POETX_OK) return r;
     }
-    {
-      StageScope sc(POETX_STAGE_W0_FWD, s);
-      const Op a = fold ? Op{U, pl->n, 1} : Op{w.GU, pl->n, 1};
-      const Op b = fold ? Op{w.Wf, pl->n, 1} : Op{Wt, pl->n, 1};
-      if ((st = gemm(pl, poetx::GEMM_W0, a, b, w.GWa, pl->m, (int)T, pl->m, pl->n, 1, 0, 0, 0, 1, 0,
-                     false, s, wq(pl) ? qscale(pl, Wt) : nullptr, wq(pl))) != POETX_OK)
-        return st;
-    }
-    Wa = w.GWa;
-  }
+    StageScope sc(POETX_STAGE_W0_FWD, s);
+    const Op a = fold ? Op{U, pl->n, 1} : Op{w.GU, pl->n, 1};
+    const Op b = fold ? Op{w.Wf, pl->n, 1} : Op{Wt, pl->n, 1};
+    return gemm(pl, poetx::GEMM_W0, a, b, w.GWa, pl->m, (int)T, pl->m, pl->n, 1, 0, 0, 0, 1, 0, false, s,
+                wq(pl) ? qscale(pl, Wt) : nullptr, wq(pl));
+  };
+  const void* Wa = Wa_saved ? Wa_saved : w.GWa;
+  if (!Wa_saved && !fused_r && (st = recompute_wa()) != POETX_OK) return st;
+
   // R side: G_Z = G_Y Pi_R^T; dQ_R = G_Z^T Wa per block; G_Wa = G_Z D_R
-  {
+  if (fused_r) {
+    StageScope sc(POETX_STAGE_BLOCK_BWD, s);
+    HIP_TRY(poetx::launch_transpose_blocks(Q_R, w.QT[0], (int)pl->segs[0][0].count, s));
+    HIP_TRY(poetx::launch_panel_block(G_Y, pi_R, w.QT[0], w.GWa, w.GZ, T, pl->m, true, false, s));
+  } else {
     StageScope sc(POETX_STAGE_GATHER, s);
     HIP_TRY(poetx::launch_gather_cols(G_Y, pl->m, nullptr, pi_R, w.GZ, T, pl->m, es, s));
   }
-  {
+  const bool dq_r_now = Wa_saved || !fused_r;
+  if (dq_r_now) {
     StageScope sc(POETX_STAGE_DQ, s);
-    if ((st = block_grads(pl, POETX_SIDE_R, T, w.GZ, Wa, w.part, dQ[0], s)) != POETX_OK)
-      return st;
+    if ((st = block_grads(pl, POETX_SIDE_R, T, w.GZ, Wa, w.part, dQ[0], s)) != POETX_OK) return st;
   }
-  const bool foldb = fold_bwd(pl, T);
-  const bool foldt = foldb && fold_rt_ok(pl);
-  {
+  if (!fused_r) {
     StageScope sc(POETX_STAGE_BLOCK_BWD, s);
     // folded: Wf = D_R Wt (stored transposed where possible) replaces
     // G_Wa = G_Z D_R. INT8 weight: G_Wa leaves scaled by the row scales of Wt,
@@ -707,11 +742,19 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
   {
     StageScope sc(POETX_STAGE_W0_BWD, s);
     const Op a = foldb ? Op{w.GZ, pl->m, 1} : Op{w.GWa, pl->m, 1};
-    // B(j, i) = (D_R Wt)[i][j]: WfT[j][i] (K-contiguous) or Wf[i][j]
-    const Op b = foldt ? Op{w.Wf, pl->m, 1} : foldb ? Op{w.Wf, 1, pl->n} : Op{Wt, 1, pl->n};
+    // B(j, i) = (D_R Wt)[i][j]: WfT[j][i] (K-contiguous) or Wf[i][j]; unfolded
+    // B(j, i) = Wt[i][j], read K-contiguous from the kept transpose WtT[j][i]
+    const Op b = foldt ? Op{w.Wf, pl->m, 1} : foldb ? Op{w.Wf, 1, pl->n}
+                 : wpair(pl) ? Op{wtt(pl, Wt), pl->m, 1} : Op{Wt, 1, pl->n};
     if ((st = gemm(pl, poetx::GEMM_W0, a, b, w.GV, pl->n, (int)T, pl->n, pl->m, 1, 0, 0, 0, 1, 0, false,
                    s, nullptr, wq(pl))) != POETX_OK)
       return st;
+  }
+  if (!dq_r_now) {
+    // POET-Xmem with the fused R pass: G_Wa is consumed, Wa goes into its buffer
+    if ((st = recompute_wa()) != POETX_OK) return st;
+    StageScope sc(POETX_STAGE_DQ, s);
+    if ((st = block_grads(pl, POETX_SIDE_R, T, w.GZ, Wa, w.part, dQ[0], s)) != POETX_OK) return st;
   }
   // P side: U = X Pi_P^T; dQ_P = G_V^T U per block; G_U = G_V D_P; G_X = G_U Pi_P
   if (Wa_saved && !U_saved) {
@@ -721,6 +764,13 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
   {
     StageScope sc(POETX_STAGE_DQ, s);
     if ((st = block_grads(pl, POETX_SIDE_P, T, w.GV, U, w.part, dQ[1], s)) != POETX_OK) return st;
+  }
+  if (w.QT[1]) {
+    // fused: G_U = G_V D_P (B = Q_P^T) scattered to G_X in the same pass
+    StageScope sc(POETX_STAGE_BLOCK_BWD, s);
+    HIP_TRY(poetx::launch_transpose_blocks(Q_P, w.QT[1], (int)pl->segs[1][0].count, s));
+    HIP_TRY(poetx::launch_panel_block(w.GV, pi_P, w.QT[1], G_X, nullptr, T, pl->n, false, true, s));
+    return POETX_OK;
   }
   {
     StageScope sc(POETX_STAGE_BLOCK_BWD, s);
@@ -881,11 +931,13 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
   if (d->m < 1 || d->n < 1 || d->nb_R < 1 || d->nb_P < 1) return POETX_ERR_SHAPE;
   if (!d->bsz_R || !d->bsz_P) return POETX_ERR_INVALID_ARG;
   if (d->k < 0 || d->k > 32) return POETX_ERR_SHAPE;
-  if (d->weight != POETX_WEIGHT_DENSE && d->weight != POETX_WEIGHT_INT8_ROWS)
+  if (d->weight != POETX_WEIGHT_DENSE && d->weight != POETX_WEIGHT_INT8_ROWS &&
+      d->weight != POETX_WEIGHT_DENSE_T)
     return POETX_ERR_INVALID_ARG;
   if (d->cayley != POETX_CAYLEY_NEUMANN && d->cayley != POETX_CAYLEY_EXACT)
     return POETX_ERR_INVALID_ARG;
   if (d->fold != POETX_FOLD_NONE && d->fold != POETX_FOLD_WEIGHT) return POETX_ERR_INVALID_ARG;
+  if (d->index != POETX_INDEX_SEPARATE && d->index != POETX_INDEX_FUSED) return POETX_ERR_INVALID_ARG;
   const int32_t* bs[2] = {d->bsz_R, d->bsz_P};
   const int nb[2] = {d->nb_R, d->nb_P};
   const int dims[2] = {d->m, d->n};
@@ -914,6 +966,7 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
   pl->weight = d->weight;
   pl->cayley = d->cayley;
   pl->fold = d->fold;
+  pl->index = d->index;
   for (int side = 0; side < 2; ++side) {
     pl->dim[side] = dims[side];
     long long q = 0, p = 0;
@@ -976,12 +1029,16 @@ poetx_status poetx_permute_weight(const poetx_plan* pl, const void* W0, const in
   if (wq(pl)) return POETX_ERR_UNSUPPORTED;   // poetx_quantize_weight builds that Wt
   HIP_TRY(poetx::launch_gather_cols(W0, pl->n, pi_R, pi_P, Wt, pl->m, pl->n, elsize(pl),
                                     (hipStream_t)stream));
+  if (wpair(pl))
+    HIP_TRY(poetx::launch_transpose(Wt, const_cast<void*>(wtt(pl, Wt)), pl->m, pl->n, elsize(pl),
+                                    (hipStream_t)stream));
   return POETX_OK;
 }
 
 size_t poetx_weight_bytes(const poetx_plan* pl) {
   if (!pl) return 0;
   if (wq(pl)) return qscale_off(pl) + 4 * (size_t)pl->m;
+  if (wpair(pl)) return wtt_off(pl) + (size_t)pl->m * pl->n * elsize(pl);
   return (size_t)pl->m * pl->n * elsize(pl);
 }
 
@@ -1100,17 +1157,25 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
   if (U_saved) w.U = U_saved;   // the gather writes the caller's buffer
   const int es = elsize(pl);
   poetx_status st;
+  const bool fold = fold_fwd(pl, T);
+  // 1 + 2 fused: one pass over X gathers it by pi_P and applies the P blocks
+  // (U kept in U_saved when given)
+  const bool fused_p = X && !fold && panel_side(pl, POETX_SIDE_P);
   // 1. gather: U = X Pi_P^T (none when the caller passes U instead of X)
-  if (X) {
+  if (X && !fused_p) {
     StageScope sc(POETX_STAGE_GATHER, s);
     HIP_TRY(poetx::launch_gather_cols(X, pl->n, nullptr, pi_P, w.U, T, pl->n, es, s));
   }
   // 2. blocks of P: V = U D_P^T, or folded into the weight, Wf = Wt D_P
-  const bool fold = fold_fwd(pl, T);
   {
     StageScope sc(POETX_STAGE_BLOCK_FWD, s);
-    st = fold ? fold_p(pl, Wt, Q_P, w.Wf, s)
-              : apply_blocks(pl, POETX_SIDE_P, T, w.U, Q_P, w.V, true, s);
+    if (fused_p) {
+      HIP_TRY(poetx::launch_panel_block(X, pi_P, Q_P, w.V, U_saved, T, pl->n, true, false, s));
+      st = POETX_OK;
+    } else {
+      st = fold ? fold_p(pl, Wt, Q_P, w.Wf, s)
+                : apply_blocks(pl, POETX_SIDE_P, T, w.U, Q_P, w.V, true, s);
+    }
     if (st != POETX_OK) return st;
   }
   // 3. frozen weight: Wa = V Wt^T (folded: Wa = U Wf^T)
@@ -1121,6 +1186,12 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
     if ((st = gemm(pl, poetx::GEMM_W0, a, b, Wa, pl->m, (int)T, pl->m, pl->n, 1, 0, 0, 0, 1, 0, false,
                    s, wq(pl) ? qscale(pl, Wt) : nullptr, wq(pl))) != POETX_OK)
       return st;
+  }
+  // 4 + 5 fused: Z = Wa D_R^T scattered to Y in one pass over the rows
+  if (panel_side(pl, POETX_SIDE_R)) {
+    StageScope sc(POETX_STAGE_BLOCK_FWD, s);
+    HIP_TRY(poetx::launch_panel_block(Wa, pi_R, Q_R, Y, nullptr, T, pl->m, false, true, s));
+    return POETX_OK;
   }
   // 4. blocks of R: Z = Wa D_R^T
   {

@@ -21,9 +21,23 @@ struct Seg {
 hipError_t launch_gather_cols(const void* in, long long in_ld, const int32_t* rows,
                               const int32_t* idx, void* out, long long T, int dim,
                               int elsize, hipStream_t s);
+// out[c][r] = in[r][c] for an R x C row-major matrix of 2- or 4-byte elements
+hipError_t launch_transpose(const void* in, void* out, int R, int C, int elsize, hipStream_t s);
 // out[t][idx[i]] = in[t][i]
 hipError_t launch_scatter_cols(const void* in, const int32_t* idx, void* out, long long T,
                                int dim, int elsize, hipStream_t s);
+
+// Index mapping fused with the block products (k_panel.hip), bf16, blocks of 256,
+// dim <= 2048: gather: out[:, blk] = P[:, blk] Bq_g^T with P[t][i] = in[t][idx[i]]
+// (P also written to in_copy when non-null); scatter: C[:, blk] = in[:, blk]
+// Bq_g^T and out[t][idx[i]] = C[t][i]. Bq holds the blocks K-contiguous
+// (Bq_g(n, k) = Bq[g * 65536 + n * 256 + k]). All rows [T, dim] row-major.
+bool panel_supported(int dim, int b, int nblocks);
+hipError_t launch_panel_block(const void* in, const int32_t* idx, const void* Bq, void* out,
+                              void* in_copy, long long T, int dim, bool gather, bool scatter,
+                              hipStream_t s);
+// QT[g][n][k] = Q[g][k][n] for count bf16 blocks of 256 x 256
+hipError_t launch_transpose_blocks(const void* Q, void* QT, int count, hipStream_t s);
 
 // ---------------------------------------------------------------- block helpers (fp32)
 // S = skew(theta) for every block of the run; if Q != nullptr also Q = I + c1 * S.

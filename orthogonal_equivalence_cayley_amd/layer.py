@@ -44,24 +44,29 @@ def param_grad_many(layers, g_thetas=None):
 class PoetxLayer:
     def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
                  dtype: str = "bf16", device: str = "cuda", weight: str = "dense",
-                 cayley: str = "neumann", fold: str = "none"):
+                 cayley: str = "neumann", fold: str = "none", index: str = "separate"):
         if dtype not in _TORCH_DTYPE:
             raise ValueError(f"dtype must be one of {sorted(_TORCH_DTYPE)}")
-        if weight not in ("dense", "int8"):
-            raise ValueError("weight must be 'dense' or 'int8' (POET-XQ)")
+        if weight not in ("dense", "dense_t", "int8"):
+            raise ValueError("weight must be 'dense', 'dense_t' (kept with its transpose) or "
+                             "'int8' (POET-XQ)")
         if cayley not in ("neumann", "exact"):
             raise ValueError("cayley must be 'neumann' (truncated series) or 'exact'")
         if fold not in ("none", "weight"):
             raise ValueError("fold must be 'none' (blocks on the activations) or 'weight'")
-        self.fold = fold
+        if index not in ("separate", "fused"):
+            raise ValueError("index must be 'separate' or 'fused' (index maps inside the block products)")
+        self.fold, self.index = fold, index
         self.m, self.n, self.k, self.dtype = m, n, k, dtype
         self.weight = weight
         self.device = torch.device(device)
         self.tdtype = _TORCH_DTYPE[dtype]
         self.plan = _px.Plan(m, n, bsz_R, bsz_P, k, _PX_DTYPE[dtype],
-                             _px.WEIGHT_INT8_ROWS if weight == "int8" else _px.WEIGHT_DENSE,
+                             {"dense": _px.WEIGHT_DENSE, "dense_t": _px.WEIGHT_DENSE_T,
+                              "int8": _px.WEIGHT_INT8_ROWS}[weight],
                              _px.CAYLEY_EXACT if cayley == "exact" else _px.CAYLEY_NEUMANN,
-                             _px.FOLD_WEIGHT if fold == "weight" else _px.FOLD_NONE)
+                             _px.FOLD_WEIGHT if fold == "weight" else _px.FOLD_NONE,
+                             _px.INDEX_FUSED if index == "fused" else _px.INDEX_SEPARATE)
         self.nparam = (self.plan.param_count(_px.SIDE_R), self.plan.param_count(_px.SIDE_P))
         self.nelem = (self.plan.block_elems(_px.SIDE_R), self.plan.block_elems(_px.SIDE_P))
         self._ws = {}
@@ -95,6 +100,11 @@ class PoetxLayer:
         if self.weight == "int8":
             self.Wt = torch.empty(self.plan.weight_bytes(), dtype=torch.uint8, device=self.device)
             self.plan.quantize_weight(W0, self.pi_R, self.pi_P, self.Wt)
+        elif self.weight == "dense_t":
+            # Wt [m, n] then its transpose in one buffer; self.Wt views the first part
+            self._wbuf = torch.empty(self.plan.weight_bytes(), dtype=torch.uint8, device=self.device)
+            self.Wt = self._wbuf[:W0.numel() * W0.element_size()].view(self.tdtype).view(self.m, self.n)
+            self.plan.permute_weight(W0, self.pi_R, self.pi_P, self.Wt)
         else:
             self.Wt = torch.empty_like(W0)
             self.plan.permute_weight(W0, self.pi_R, self.pi_P, self.Wt)

@@ -35,12 +35,16 @@ WS_MERGE = 4
 
 WEIGHT_DENSE = 0
 WEIGHT_INT8_ROWS = 1
+WEIGHT_DENSE_T = 2
 
 CAYLEY_NEUMANN = 0
 CAYLEY_EXACT = 1
 
 FOLD_NONE = 0
 FOLD_WEIGHT = 1
+
+INDEX_SEPARATE = 0
+INDEX_FUSED = 1
 
 EXPORTED = (
     "poetx_plan_create", "poetx_plan_destroy", "poetx_param_count", "poetx_block_elems",
@@ -70,7 +74,7 @@ class Desc(ctypes.Structure):
         ("nb_R", ctypes.c_int32), ("nb_P", ctypes.c_int32),
         ("bsz_R", ctypes.POINTER(ctypes.c_int32)), ("bsz_P", ctypes.POINTER(ctypes.c_int32)),
         ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("weight", ctypes.c_int32),
-        ("cayley", ctypes.c_int32), ("fold", ctypes.c_int32),
+        ("cayley", ctypes.c_int32), ("fold", ctypes.c_int32), ("index", ctypes.c_int32),
     ]
 
 
@@ -208,14 +212,15 @@ class Plan:
 
     def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
                  dtype: int, weight: int = WEIGHT_DENSE, cayley: int = CAYLEY_NEUMANN,
-                 fold: int = FOLD_NONE):
+                 fold: int = FOLD_NONE, index: int = INDEX_SEPARATE):
         self.m, self.n, self.k, self.dtype = int(m), int(n), int(k), int(dtype)
         self.weight, self.cayley, self.fold = int(weight), int(cayley), int(fold)
+        self.index = int(index)
         self.bsz_R, self.bsz_P = tuple(int(b) for b in bsz_R), tuple(int(b) for b in bsz_P)
         aR = (ctypes.c_int32 * max(1, len(self.bsz_R)))(*self.bsz_R)
         aP = (ctypes.c_int32 * max(1, len(self.bsz_P)))(*self.bsz_P)
         d = Desc(self.m, self.n, len(self.bsz_R), len(self.bsz_P), aR, aP, self.k, self.dtype,
-                 self.weight, self.cayley, self.fold)
+                 self.weight, self.cayley, self.fold, self.index)
         h = ctypes.c_void_p()
         self._h = None
         _check(LIB.poetx_plan_create(ctypes.byref(d), ctypes.byref(h)), "poetx_plan_create")

@@ -30,11 +30,13 @@ def to_np(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def make_layer(inp, k: int, dtype: str, weight: str = "dense", fold: str = "none"):
+def make_layer(inp, k: int, dtype: str, weight: str = "dense", fold: str = "none",
+               index: str = "separate"):
     import torch
     from orthogonal_equivalence_cayley_amd import PoetxLayer
     sp = inp.spec
-    layer = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, k, dtype=dtype, weight=weight, fold=fold)
+    layer = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, k, dtype=dtype, weight=weight, fold=fold,
+                       index=index)
     layer.set_weight(to_dev(inp.W0, dtype), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
     layer.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
     return layer

@@ -238,3 +238,28 @@ def test_fold_option():
     with pytest.raises(px.PoetxError) as e:
         px.Plan(*args, 2)
     assert e.value.status == px.POETX_ERR_INVALID_ARG
+
+
+def test_dense_weight_with_transpose_bytes():
+    """POETX_WEIGHT_DENSE_T keeps WtT [n, m] after Wt at a 256-byte boundary."""
+    bf, f32 = px.POETX_BF16, px.POETX_FP32
+    p = px.Plan(512, 256, (256, 256), (256,), 4, bf, px.WEIGHT_DENSE_T)
+    assert p.weight_bytes() == 2 * (512 * 256 * 2)
+    q = px.Plan(37, 53, (37,), (53,), 2, f32, px.WEIGHT_DENSE_T)
+    off = (37 * 53 * 4 + 255) // 256 * 256
+    assert q.weight_bytes() == off + 37 * 53 * 4
+    with pytest.raises(px.PoetxError) as e:
+        px.Plan(37, 53, (37,), (53,), 2, f32, 3)
+    assert e.value.status == px.POETX_ERR_INVALID_ARG
+
+
+def test_index_option():
+    bf = px.POETX_BF16
+    args = (256, 512, (256,), (256, 256), 4, bf, px.WEIGHT_DENSE, px.CAYLEY_NEUMANN, px.FOLD_NONE)
+    sep = px.Plan(*args)
+    fus = px.Plan(*args, px.INDEX_FUSED)
+    # the fused backward keeps bf16 transposes of both sides' blocks
+    assert fus.workspace_size(100, px.WS_BACKWARD) > sep.workspace_size(100, px.WS_BACKWARD)
+    with pytest.raises(px.PoetxError) as e:
+        px.Plan(*args, 2)
+    assert e.value.status == px.POETX_ERR_INVALID_ARG

@@ -550,3 +550,29 @@ def test_kept_input_permutation_matches_gathering(save):
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("dt, c", [
+    ("bf16", dict(m=768, n=512, bR=(256,) * 3, bP=(256, 256), T=300)),
+    ("f32", dict(m=37, n=53, bR=(37,), bP=(20, 33), T=41)),
+])
+def test_weight_kept_with_transpose(dt, c):
+    """POETX_WEIGHT_DENSE_T: permute_weight also writes WtT (bit-exact
+    transpose), and the backward that reads it gives the oracle's results."""
+    import torch
+    inp = workloads.small_case(c["m"], c["n"], c["bR"], c["bP"], T=c["T"], seed=c["m"] + 11, dtype=dt,
+                               theta_std=0.01 if dt == "bf16" else 0.05)
+    log(f"dense_t {dt} {c}")
+    L = make_layer(inp, 3, dt, weight="dense_t")
+    D = make_layer(inp, 3, dt)
+    torch.cuda.synchronize()
+    m, n = c["m"], c["n"]
+    es = 2 if dt == "bf16" else 4
+    off = (m * n * es + 255) // 256 * 256
+    WtT = L._wbuf[off:off + m * n * es].view(L.tdtype).view(n, m)
+    assert torch.equal(_bits(L.Wt), _bits(D.Wt))
+    assert torch.equal(_bits(WtT), _bits(D.Wt.t().contiguous()))
+    got, _ = run_layer(inp, 3, dt, layer=L)
+    ref = oracle.layer_reference(inp, 3)
+    _compare(got, ref, ["Wa", "Y", "G_X", "g_theta_R", "g_theta_P"], TOL_F32 if dt == "f32" else TOL_BF16,
+             "dense_t")
