@@ -261,6 +261,25 @@ poetx_status poetx_forward(const poetx_plan* plan, int64_t T, const void* X, con
                            void* Y, void* Wa_saved, void* U_saved, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* poetx_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without the workspace, which comes from a static device
+ * array inside the library instead (poetx_forward_noalloc_max_bytes() bytes,
+ * 64 MiB; each GPU holds its own copy from the library's first use on it until
+ * the process ends). The call allocates nothing and runs the same kernels as
+ * poetx_forward, with the same results.
+ *   POETX_ERR_WORKSPACE when poetx_workspace_size(plan, T, POETX_WS_FORWARD)
+ *   exceeds that size (checked before the device is touched); argument errors
+ *   as for poetx_forward.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (concurrent streams or threads) race and must be serialised by the
+ * caller. Nothing in the array needs to start at zero. */
+poetx_status poetx_forward_noalloc(const poetx_plan* plan, int64_t T, const void* X, const void* Wt,
+                                   const int32_t* pi_R, const int32_t* pi_P, const void* Q_R,
+                                   const void* Q_P, void* Y, void* Wa_saved, void* U_saved,
+                                   void* stream);
+size_t poetx_forward_noalloc_max_bytes(void);
+
 /* Backward of L = <G_Y, Y> w.r.t. X and both sides' skew parameters, for the
  * truncated Q the forward used. W0 is frozen and gets no gradient.
  *   X, Wt, pi_R, pi_P, Q_R, Q_P as in poetx_forward (INT8 plans: the scale

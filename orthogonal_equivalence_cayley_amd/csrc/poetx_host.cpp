@@ -902,6 +902,35 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
 
 bool side_ok(int32_t side) { return side_ok_fn(side); }
 
+// ------------------------------------------------------------------ allocation-free forward
+// poetx_forward_noalloc takes its workspace from this array instead of the
+// caller. Each GPU the library runs on holds its own copy until the process
+// ends; every call on a GPU shares it, so calls that overlap on one GPU race.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): it uses the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+poetx_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return POETX_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return POETX_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return POETX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1204,6 +1233,27 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
     HIP_TRY(poetx::launch_scatter_cols(w.Z, pi_R, Y, T, pl->m, es, s));
   }
   return POETX_OK;
+}
+
+size_t poetx_forward_noalloc_max_bytes(void) { return kScratchBytes; }
+
+poetx_status poetx_forward_noalloc(const poetx_plan* pl, int64_t T, const void* X, const void* Wt,
+                                   const int32_t* pi_R, const int32_t* pi_P, const void* Q_R,
+                                   const void* Q_P, void* Y, void* Wa_saved, void* U_saved,
+                                   void* stream) {
+  // the argument checks of poetx_forward, before the device is touched
+  if (!pl || T < 0) return POETX_ERR_INVALID_ARG;
+  if (T == 0) return POETX_OK;
+  if ((!X && !U_saved) || !Wt || !pi_R || !pi_P || !Q_R || !Q_P || !Y) return POETX_ERR_INVALID_ARG;
+  for (const void* p : {X, Wt, (const void*)pi_R, (const void*)pi_P, Q_R, Q_P, (const void*)Y,
+                        (const void*)Wa_saved, (const void*)U_saved})
+    if (!aligned16(p)) return POETX_ERR_ALIGNMENT;
+  if (poetx_workspace_size(pl, T, POETX_WS_FORWARD) > kScratchBytes) return POETX_ERR_WORKSPACE;
+  void* ws = nullptr;
+  poetx_status st = scratch_for_current_device(&ws);
+  if (st != POETX_OK) return st;
+  return poetx_forward(pl, T, X, Wt, pi_R, pi_P, Q_R, Q_P, Y, Wa_saved, U_saved, ws, kScratchBytes,
+                       stream);
 }
 
 poetx_status poetx_backward(const poetx_plan* pl, int64_t T, const void* X, const void* Wt,

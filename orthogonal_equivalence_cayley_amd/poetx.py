@@ -53,6 +53,7 @@ EXPORTED = (
     "poetx_build_orth", "poetx_build_orth_batch", "poetx_forward", "poetx_backward",
     "poetx_backward_dq", "poetx_param_grad_batch", "poetx_gather_cols",
     "poetx_scatter_cols", "poetx_timing_enable", "poetx_timing_read", "poetx_timing_reset",
+    "poetx_forward_noalloc", "poetx_forward_noalloc_max_bytes",
 )
 
 STAGES = ("build", "gather", "block_fwd", "w0_fwd", "scatter", "dq", "block_bwd", "w0_bwd",
@@ -107,6 +108,8 @@ def _load() -> ctypes.CDLL:
         "poetx_build_orth": (st, [vp, i32, vp, vp, vp, vp, sz, vp]),
         "poetx_build_orth_batch": (st, [i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "poetx_forward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "poetx_forward_noalloc": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "poetx_forward_noalloc_max_bytes": (sz, []),
         "poetx_backward": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]),
         "poetx_backward_dq": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -276,6 +279,12 @@ class Plan:
         _check(LIB.poetx_forward(self._h, T, _ptr(X), _ptr(Wt), _ptr(pi_R), _ptr(pi_P),
                                  _ptr(Q_R), _ptr(Q_P), _ptr(Y), _ptr(Wa_saved), _ptr(U_saved),
                                  _ptr(ws), ws_bytes, _stream(stream)), "poetx_forward")
+
+    def forward_noalloc(self, T: int, X, Wt, pi_R, pi_P, Q_R, Q_P, Y, Wa_saved, stream=None,
+                        U_saved=None) -> None:
+        _check(LIB.poetx_forward_noalloc(self._h, T, _ptr(X), _ptr(Wt), _ptr(pi_R), _ptr(pi_P),
+                                         _ptr(Q_R), _ptr(Q_P), _ptr(Y), _ptr(Wa_saved),
+                                         _ptr(U_saved), _stream(stream)), "poetx_forward_noalloc")
 
     def backward(self, T: int, X, Wt, pi_R, pi_P, theta_R, theta_P, Q_R, Q_P, Wa_saved, G_Y,
                  G_X, g_theta_R, g_theta_P, ws, ws_bytes: int, stream=None, U_saved=None) -> None:

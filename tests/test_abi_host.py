@@ -253,6 +253,23 @@ def test_dense_weight_with_transpose_bytes():
     assert e.value.status == px.POETX_ERR_INVALID_ARG
 
 
+def test_forward_noalloc_host_checks():
+    """The allocation-free forward checks its arguments and its size limit on
+    the host, before the device is touched."""
+    p = _plan()
+    A = 1 << 20
+    f = px.LIB.poetx_forward_noalloc
+    assert px.LIB.poetx_forward_noalloc_max_bytes() == 64 << 20
+    assert f(None, 4, A, A, A, A, A, A, A, None, None, None) == px.POETX_ERR_INVALID_ARG
+    assert f(p.handle, -1, A, A, A, A, A, A, A, None, None, None) == px.POETX_ERR_INVALID_ARG
+    assert f(p.handle, 0, None, None, None, None, None, None, None, None, None, None) == px.POETX_OK
+    assert f(p.handle, 4, None, A, A, A, A, A, A, None, None, None) == px.POETX_ERR_INVALID_ARG
+    assert f(p.handle, 4, A + 8, A, A, A, A, A, A, None, None, None) == px.POETX_ERR_ALIGNMENT
+    T = (64 << 20) // (4 * (64 + 48)) + 1
+    assert p.workspace_size(T, px.WS_FORWARD) > 64 << 20
+    assert f(p.handle, T, A, A, A, A, A, A, A, None, None, None) == px.POETX_ERR_WORKSPACE
+
+
 def test_index_option():
     bf = px.POETX_BF16
     args = (256, 512, (256,), (256, 256), 4, bf, px.WEIGHT_DENSE, px.CAYLEY_NEUMANN, px.FOLD_NONE)
