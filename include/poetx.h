@@ -80,11 +80,16 @@ typedef enum {
 /* Orthogonal map of each block.
  *   POETX_CAYLEY_NEUMANN: Q = (I+S) sum_{j<=k} S^j, the truncated series of [PX]
  *     §2.D, and the gradient of that truncated Q (the default).
- *   POETX_CAYLEY_EXACT: the Cayley transform itself, Q = (I+S)(I-S)^{-1}, as a
- *     reference build: (I-S)^{-1} = prod_{i<6} (I + S^(2^i)) (64 terms of the
- *     series in 11 fp32 products per block, exact to fp32 while ||S||_2 <= 0.75),
- *     and the exact gradient dL/dS = (I+Q)^T G (I-S)^{-T}. k is ignored. Runs on
- *     the generic fp32 batched GEMM, block run by block run. */
+ *   POETX_CAYLEY_EXACT: the Cayley transform itself, Q = (I+S)(I-S)^{-1} =
+ *     2 (I-S)^{-1} - I, as a reference build, and the exact gradient
+ *     dL/dS = (I+Q)^T G (I-S)^{-T}. k is ignored. (I-S)^{-1} comes from the
+ *     Newton-Schulz iteration X <- X (2I - (I-S) X) started at
+ *     X0 = (I+S) 2 / (2 + c^2), c = max row sum of |S| >= ||S||_2, which
+ *     converges for every skew S (the residual is symmetric with norm at most
+ *     c^2 / (2 + c^2) and squares each step); each block runs the steps it needs
+ *     for a residual below 2^-30 (6 at c = 2), at most 28 (c up to ~4000).
+ *     fp32 products on the batched fp32 GEMM, one launch per step over every
+ *     block of a size. */
 typedef enum { POETX_CAYLEY_NEUMANN = 0, POETX_CAYLEY_EXACT = 1 } poetx_cayley;
 
 /* Where the block-diagonal factors are applied.
@@ -113,6 +118,20 @@ typedef enum { POETX_FOLD_NONE = 0, POETX_FOLD_WEIGHT = 1 } poetx_fold;
  *     saves at 2048 features), which on MI355X makes these passes slower than
  *     the separate ones; same results. Other sides keep the separate kernels. */
 typedef enum { POETX_INDEX_SEPARATE = 0, POETX_INDEX_FUSED = 1 } poetx_index;
+
+/* How the build evaluates Q = sum_{j=0..k+1} c_j S^j (c_0 = c_{k+1} = 1,
+ * c_j = 2 otherwise; [PX] §2.D) for POETX_CAYLEY_NEUMANN plans.
+ *   POETX_SERIES_CHAIN (the default): the power chain P_j = P_{j-1} S, k
+ *     products per block, fused in one kernel per block size (row panels of a
+ *     block kept on chip).
+ *   POETX_SERIES_PS: Paterson-Stockmeyer. With s = the step that minimises the
+ *     product count, the powers S^2 .. S^s (s - 1 products), then
+ *     Q = B_0 + S^s (B_1 + S^s (B_2 + ...)) with each B_i = sum_{l<s} c_{is+l}
+ *     S^l formed from the stored powers without products (a last B_i that is a
+ *     multiple of I is folded in the same way): 3 products at k = 4 and k = 5
+ *     instead of 4 and 5, 2 sqrt(k) or so for large k. Batched fp32 products
+ *     (fp32 accuracy in every plan). The backward is the same for both. */
+typedef enum { POETX_SERIES_CHAIN = 0, POETX_SERIES_PS = 1 } poetx_series;
 typedef enum { POETX_SIDE_R = 0, POETX_SIDE_P = 1 } poetx_side;
 typedef enum {
   POETX_WS_BUILD = 0,       /* poetx_build_orth, one item of poetx_build_orth_batch */
@@ -137,6 +156,7 @@ typedef struct {
   int32_t cayley;           /* poetx_cayley: truncated series or exact transform    */
   int32_t fold;             /* poetx_fold: activations only, or the weight-side fold */
   int32_t index;            /* poetx_index: separate index passes, or fused         */
+  int32_t series;           /* poetx_series: power chain or Paterson-Stockmeyer     */
 } poetx_desc;
 
 /* Create a plan. Host only: no device call is made, so it works without a GPU.

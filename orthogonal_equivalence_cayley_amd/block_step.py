@@ -48,7 +48,8 @@ class BlockStep:
 
     def __init__(self, layer_inputs, k: int, dtype: str = "bf16", *, backward: bool = True,
                  streams: int = 2, weight: str = "dense_t", cayley: str = "neumann",
-                 fold: str = "none", index: str = "separate", xmem: bool = False):
+                 fold: str = "none", index: str = "separate", series: str = "chain",
+                 xmem: bool = False):
         if streams not in (1, 2):
             raise ValueError("streams must be 1 or 2")
         self.k, self.dtype, self.backward, self.xmem = k, dtype, backward, xmem
@@ -60,7 +61,7 @@ class BlockStep:
             sp = inp.spec
             T = inp.X.shape[0]
             L = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, k, dtype=dtype, weight=weight,
-                           cayley=cayley, fold=fold, index=index)
+                           cayley=cayley, fold=fold, index=index, series=series)
             L.set_weight(dev(inp.W0), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
             L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
             b = dict(X=dev(inp.X), Y=torch.empty(T, sp.m, dtype=tdt, device="cuda"),

@@ -41,6 +41,82 @@ __global__ __launch_bounds__(kThreads) void unpack_skew_kernel(
   }
 }
 
+// Newton-Schulz start for N = (I - S)^{-1}, one workgroup per block: with
+// c = max_i sum_j |S[i][j]| (an upper bound of ||S||_2), X0 = a (I + S) =
+// a (I - S)^T with a = 2 / (2 + c^2). The residual R = I - (I - S) X0 is
+// symmetric with eigenvalues 1 - a (1 + s^2) for the singular values s <= c of
+// S, so ||R||_2 <= r = c^2 / (2 + c^2) < 1, and after j steps X <- X (2I - (I -
+// S) X) it is R^(2^j). iters[block] = the least j with r^(2^j) <= 2^-30
+// (0 when S = 0), at most jmax.
+__global__ __launch_bounds__(kThreads) void ns_init_kernel(const float* __restrict__ S, int b,
+                                                           float* __restrict__ X0,
+                                                           int32_t* __restrict__ iters, int jmax) {
+  __shared__ float red[kThreads];
+  const long long bb = (long long)b * b;
+  const float* Sg = S + blockIdx.x * bb;
+  float* Xg = X0 + blockIdx.x * bb;
+  float mx = 0.0f;
+  for (int r = threadIdx.x; r < b; r += kThreads) {
+    float sum = 0.0f;
+    for (int c = 0; c < b; ++c) sum += fabsf(Sg[(long long)r * b + c]);
+    mx = fmaxf(mx, sum);
+  }
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  const double c = red[0];
+  const float a = (float)(2.0 / (2.0 + c * c));
+  for (long long e = threadIdx.x; e < bb; e += kThreads) {
+    const int r = (int)(e / b), col = (int)(e - (long long)r * b);
+    Xg[e] = a * ((r == col ? 1.0f : 0.0f) + Sg[e]);
+  }
+  if (threadIdx.x == 0) {
+    int j = 0;
+    if (c > 0.0) {
+      const double rho = c * c / (2.0 + c * c);
+      // rho^(2^j) <= 2^-30  <=>  2^j >= 30 ln 2 / (-ln rho)
+      const double need = 30.0 * 0.6931471805599453 / -log(rho);
+      while (j < jmax && ldexp(1.0, j) < need) ++j;
+    }
+    iters[blockIdx.x] = j;
+  }
+}
+
+// After the iterations, block g's N sits in X0 for an even iteration count and
+// in X1 for an odd one: N_out = N and Q = (I + S)(I - S)^{-1} = 2 N - I.
+__global__ __launch_bounds__(kThreads) void ns_final_kernel(const float* __restrict__ X0,
+                                                            const float* __restrict__ X1,
+                                                            const int32_t* __restrict__ iters,
+                                                            int b, float* __restrict__ N,
+                                                            float* __restrict__ Q) {
+  const long long bb = (long long)b * b;
+  const float* src = ((iters[blockIdx.x] & 1) ? X1 : X0) + blockIdx.x * bb;
+  for (long long e = threadIdx.x; e < bb; e += kThreads) {
+    const int r = (int)(e / b), col = (int)(e - (long long)r * b);
+    const float v = src[e];
+    N[blockIdx.x * bb + e] = v;
+    Q[blockIdx.x * bb + e] = 2.0f * v - (r == col ? 1.0f : 0.0f);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void lincomb_kernel(LinComb lc, float* out, int b,
+                                                           long long total) {
+  const long long bb = (long long)b * b;
+  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total;
+       e += (long long)gridDim.x * kThreads) {
+    const long long w = e % bb;
+    const int r = (int)(w / b), c = (int)(w - (long long)r * b);
+    float v = r == c ? lc.diag : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kLinCombMax; ++i)
+      if (i < lc.n) v += lc.coef[i] * lc.mats[i][e];
+    out[e] = v;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void pack_antisym_kernel(
     const float* __restrict__ Sbar, int b, int count, long long q_off, long long p_off,
     float sign, float* __restrict__ g) {
@@ -137,6 +213,27 @@ hipError_t launch_unpack_skew(const float* theta, const Seg& g, float* S, float*
   const long long total = (long long)g.b * g.b * g.count;
   hipLaunchKernelGGL(unpack_skew_kernel, dim3(grid1d(total)), dim3(kThreads), 0, s, theta, g.b,
                      g.count, g.q_off, g.p_off, S, Q, c1);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_init(const float* S, int b, int count, float* X0, int32_t* iters, int jmax,
+                          hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ns_init_kernel, dim3(count), dim3(kThreads), 0, s, S, b, X0, iters, jmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_final(const float* X0, const float* X1, const int32_t* iters, int b, int count,
+                           float* N, float* Q, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ns_final_kernel, dim3(count), dim3(kThreads), 0, s, X0, X1, iters, b, N, Q);
+  return hipGetLastError();
+}
+
+hipError_t launch_lincomb(const LinComb& lc, float* out, int b, int count, hipStream_t s) {
+  if (count <= 0 || lc.n < 0 || lc.n > kLinCombMax) return count <= 0 ? hipSuccess : hipErrorInvalidValue;
+  const long long total = (long long)b * b * count;
+  hipLaunchKernelGGL(lincomb_kernel, dim3(grid1d(total)), dim3(kThreads), 0, s, lc, out, b, total);
   return hipGetLastError();
 }
 

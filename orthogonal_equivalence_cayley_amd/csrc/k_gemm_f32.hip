@@ -21,6 +21,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmF32 p) {
   const int tx = tid & 15, ty = tid >> 4;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   const int g = blockIdx.z / p.splits, sp = blockIdx.z - g * p.splits;
+  if (p.iters && p.iters[g] <= p.it) return;
   const float* A = p.A + g * p.a_gs;
   const float* B = p.B + g * p.b_gs;
 
@@ -104,6 +105,7 @@ __device__ __forceinline__ void gemm_f32_mfma_body(const GemmF32& p, int gz) {
   const int n0 = blockIdx.x * MB, m0 = blockIdx.y * MB;
   if (n0 >= p.N || m0 >= p.M) return;
   const int g = gz / p.splits, sp = gz - g * p.splits;
+  if (p.iters && p.iters[g] <= p.it) return;
   const float* A = p.A + g * p.a_gs;
   const float* B = p.B + g * p.b_gs;
   int kchunk = (p.K + p.splits - 1) / p.splits;
@@ -214,6 +216,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_mfma_runs_kernel(GemmF32Run
   GemmF32 p = rr.p;
   p.A = rr.r[r].A; p.B = rr.r[r].B; p.C = rr.r[r].C; p.Cin = rr.r[r].Cin; p.E = nullptr;
   p.groups = rr.r[r].groups;
+  p.iters = rr.r[r].iters;
   gemm_f32_mfma_body<AKC, BKC, MB>(p, blockIdx.z - rr.z0[r]);
 }
 
@@ -252,6 +255,7 @@ hipError_t launch_gemm_f32_runs(const GemmF32& shape, const GemmF32Run* runs, in
       GemmF32 p = shape;
       p.A = runs[i].A; p.B = runs[i].B; p.C = runs[i].C; p.Cin = runs[i].Cin; p.E = nullptr;
       p.groups = runs[i].groups;
+      p.iters = runs[i].iters;
       const hipError_t e = launch_gemm_f32(p, s);
       if (e != hipSuccess) return e;
     }

@@ -24,6 +24,7 @@ struct poetx_plan {
   int cayley = POETX_CAYLEY_NEUMANN; // poetx_cayley: truncated series or exact transform
   int fold = POETX_FOLD_NONE;        // poetx_fold: activations only, or the weight-side fold
   int index = POETX_INDEX_SEPARATE;  // poetx_index: separate index passes, or fused
+  int series = POETX_SERIES_CHAIN;   // poetx_series: power chain or Paterson-Stockmeyer
   std::vector<int> bsz[2];
   std::vector<Seg> segs[2];
   long long nparam[2] = {0, 0};
@@ -183,6 +184,7 @@ bool panel_side(const poetx_plan* pl, int side) {
 struct ChainWs {
   float *S, *T, *A;            // fused chains: generators, T_1^T, stored A_j
   float *A0, *A1, *T0, *T1;    // generic path (block sizes the fused chain skips)
+  int32_t* iters;              // exact transform: Newton-Schulz steps per block
 };
 
 size_t layout_chain(const poetx_plan* pl, int side, Carver& c, ChainWs* w) {
@@ -196,6 +198,7 @@ size_t layout_chain(const poetx_plan* pl, int side, Carver& c, ChainWs* w) {
   x.A1 = (float*)c.take(4 * ne);
   x.T0 = (float*)c.take(4 * ne);
   x.T1 = (float*)c.take(4 * ne);
+  x.iters = pl->cayley == POETX_CAYLEY_EXACT ? (int32_t*)c.take(4 * pl->bsz[side].size()) : nullptr;
   if (w) *w = x;
   return c.off - start;
 }
@@ -266,18 +269,46 @@ size_t layout_merge(const poetx_plan* pl, void* base, MergeWs* w) {
   return c.off;
 }
 
+// Paterson-Stockmeyer split of Q = sum_{j<=d} c_j S^j, d = k + 1: with step s,
+// Q = sum_{i<=r} (S^s)^i B_i (r = d / s, B_i = sum_{l<s} c_{is+l} S^l), evaluated
+// as H = B_r, H <- B_i + S^s H for i = r-1 .. 0. Products: s - 1 for S^2 .. S^s
+// (d - 1 when r = 0) and r for the recurrence, one less when B_r = c_d I (then
+// B_{r-1} + c_d S^s is formed without a product). Returns the s with the fewest
+// products (the smallest on ties), s <= kLinCombMax.
+int ps_step(int d, int* products = nullptr) {
+  int best = 1, bestp = 1 << 30;
+  for (int s = 1; s <= std::min(d, poetx::kLinCombMax); ++s) {
+    const int r = d / s;
+    const int pr = r == 0 ? std::max(0, d - 1) : (s - 1) + r - (d % s == 0 ? 1 : 0);
+    if (pr < bestp) { bestp = pr; best = s; }
+  }
+  if (products) *products = bestp;
+  return best;
+}
+bool build_ps(const poetx_plan* pl) {
+  return pl->series == POETX_SERIES_PS && pl->cayley == POETX_CAYLEY_NEUMANN;
+}
+
 size_t layout_build(const poetx_plan* pl, void* base, float** S, float** P0, float** P1,
-                    float** X0 = nullptr, float** X1 = nullptr) {
+                    float** X0 = nullptr, float** X1 = nullptr, int32_t** iters = nullptr,
+                    float** pw = nullptr) {
   Carver c(base);
   const long long ne = std::max(pl->nelem[0], pl->nelem[1]);
   float* s = (float*)c.take(4 * ne);
   float* p0 = (float*)c.take(4 * ne);
   float* p1 = (float*)c.take(4 * ne);
   if (S) { *S = s; *P0 = p0; *P1 = p1; }
-  if (pl->cayley == POETX_CAYLEY_EXACT) {   // running products of the doubling build
+  if (pl->cayley == POETX_CAYLEY_EXACT) {   // Newton-Schulz iterates and step counts
     float* x0 = (float*)c.take(4 * ne);
     float* x1 = (float*)c.take(4 * ne);
+    int32_t* it = (int32_t*)c.take(4 * std::max(pl->bsz[0].size(), pl->bsz[1].size()));
     if (X0) { *X0 = x0; *X1 = x1; }
+    if (iters) *iters = it;
+  }
+  if (build_ps(pl)) {   // S^2 .. S^s and the recurrence's B (P0 and P1 hold H)
+    const int st = ps_step(pl->k + 1);
+    float* w = (float*)c.take(4 * ne * st);
+    if (pw) *pw = w;
   }
   return c.off;
 }
@@ -353,37 +384,42 @@ poetx_status chain_gemm(const Seg& g, const float* X, const float* Y, float* C, 
   return POETX_OK;
 }
 
-// Exact Cayley transform without a solve: (I - S)^{-1} = prod_{i < F} (I + S^(2^i))
-// up to S^(2^F) (F = 6: 64 terms of the series, 11 products instead of 63), then
-// Q = (I + S) N. Exact to fp32 while ||S||_2 <= 0.75.
-constexpr int kExactFactors = 6;
+// Exact Cayley transform: N = (I - S)^{-1} by Newton-Schulz, X <- X (2I - (I -
+// S) X) from X0 = a (I + S), which converges for every skew S (launch_ns_init),
+// then Q = (I + S) N = 2 N - I. Each block stops after its own step count
+// (iters, at most kNsMaxSteps: enough for max row sums of |S| up to ~4000; the
+// GEMM launches skip finished blocks).
+constexpr int kNsMaxSteps = 28;
 
 // One run of the exact transform: one segment of one side; every pointer is at
-// the segment's first block. N is set by exact_cayley_runs (X0 or X1).
+// the segment's first block. N is written to P0.
 struct ExactRun {
   Seg g;
   const float* theta;   // the side's packed parameters (segment offset applied by the unpack)
   float *S, *P0, *P1, *X0, *X1, *Q, *N;
+  int32_t* iters;       // one step count per block of the run
 };
 
-// Batched product over runs of one block size b: C_r = A_r B_r (+ beta Cin_r),
-// all b x b row-major, A(m, k) = A_r[m * a_rs + k * a_cs], B(n, k) =
-// B_r[n * b_rs + k * b_cs].
+// Batched product over runs of one block size b: C_r = alpha A_r B_r (+ beta
+// Cin_r) (+ gamma I), all b x b row-major, A(m, k) = A_r[m * a_rs + k * a_cs],
+// B(n, k) = B_r[n * b_rs + k * b_cs]; blocks whose iters <= it are skipped.
 poetx_status f32_runs(int b, long long a_rs, long long a_cs, long long b_rs, long long b_cs,
-                      const std::vector<poetx::GemmF32Run>& runs, float beta, hipStream_t s) {
+                      const std::vector<poetx::GemmF32Run>& runs, float beta, hipStream_t s,
+                      float alpha = 1.0f, float gamma = 0.0f, int it = 0) {
   poetx::GemmF32 p{};
   p.M = p.N = p.K = b;
   p.a_rs = a_rs; p.a_cs = a_cs; p.b_rs = b_rs; p.b_cs = b_cs; p.c_rs = b;
   p.a_gs = p.b_gs = p.c_gs = (long long)b * b;
   p.splits = 1;
-  p.alpha = 1.0f; p.beta = beta;
+  p.alpha = alpha; p.beta = beta; p.gamma = gamma;
+  p.it = it;
   HIP_TRY(poetx::launch_gemm_f32_runs(p, runs.data(), (int)runs.size(), s));
   return POETX_OK;
 }
 
-// The exact transform of many runs at once: each of its 11 products is one
-// launch over all runs of a block size (a single side has too few blocks to fill
-// the chip). X ends as N = (I - S)^{-1} in X0 or X1 (r.N).
+// The exact transform of many runs at once: each Newton-Schulz product is one
+// launch over all runs of a block size (a single side has too few blocks to
+// fill the chip). Sets r.N (= r.P0) and writes r.Q.
 poetx_status exact_cayley_runs(std::vector<ExactRun>& runs, hipStream_t s) {
   std::vector<int> sizes;
   for (const ExactRun& r : runs)
@@ -393,37 +429,33 @@ poetx_status exact_cayley_runs(std::vector<ExactRun>& runs, hipStream_t s) {
     for (ExactRun& r : runs)
       if (r.g.b == b) rs.push_back(&r);
     const size_t n = rs.size();
-    std::vector<const float*> P(n);
-    std::vector<float*> X(n), Xn(n);
     for (size_t i = 0; i < n; ++i) {
       ExactRun& r = *rs[i];
-      // X = I + S; the unpack takes base pointers and applies the segment offset
-      HIP_TRY(poetx::launch_unpack_skew(r.theta, r.g, r.S - r.g.q_off, r.X0 - r.g.q_off, 1.0f, s));
-      P[i] = r.S;
-      X[i] = r.X0;
-      Xn[i] = r.X1;
+      // the unpack takes base pointers and applies the segment offset
+      HIP_TRY(poetx::launch_unpack_skew(r.theta, r.g, r.S - r.g.q_off, nullptr, 0.0f, s));
+      HIP_TRY(poetx::launch_ns_init(r.S, b, r.g.count, r.X0, r.iters, kNsMaxSteps, s));
     }
     std::vector<poetx::GemmF32Run> v(n);
     poetx_status st;
-    for (int f = 1; f < kExactFactors; ++f) {
-      // S^(2^f) = (S^(2^(f-1)))^2
+    for (int it = 0; it < kNsMaxSteps; ++it) {
+      // Y = 2I - (I - S) X = S X - X + 2I (in P1), then X' = X Y
       for (size_t i = 0; i < n; ++i) {
-        float* Pn = (f & 1) ? rs[i]->P1 : rs[i]->P0;
-        v[i] = poetx::GemmF32Run{P[i], P[i], Pn, nullptr, rs[i]->g.count};
+        const float* X = (it & 1) ? rs[i]->X1 : rs[i]->X0;
+        v[i] = poetx::GemmF32Run{rs[i]->S, X, rs[i]->P1, X, rs[i]->g.count, rs[i]->iters};
       }
-      if ((st = f32_runs(b, b, 1, 1, b, v, 0.0f, s)) != POETX_OK) return st;
-      // X (I + S^(2^f)) = X + X S^(2^f)
+      if ((st = f32_runs(b, b, 1, 1, b, v, -1.0f, s, 1.0f, 2.0f, it)) != POETX_OK) return st;
       for (size_t i = 0; i < n; ++i) {
-        P[i] = v[i].C;
-        v[i] = poetx::GemmF32Run{X[i], P[i], Xn[i], X[i], rs[i]->g.count};
+        const float* X = (it & 1) ? rs[i]->X1 : rs[i]->X0;
+        float* Xn = (it & 1) ? rs[i]->X0 : rs[i]->X1;
+        v[i] = poetx::GemmF32Run{X, rs[i]->P1, Xn, nullptr, rs[i]->g.count, rs[i]->iters};
       }
-      if ((st = f32_runs(b, b, 1, 1, b, v, 1.0f, s)) != POETX_OK) return st;
-      for (size_t i = 0; i < n; ++i) std::swap(X[i], Xn[i]);
+      if ((st = f32_runs(b, b, 1, 1, b, v, 0.0f, s, 1.0f, 0.0f, it)) != POETX_OK) return st;
     }
-    // Q = (I + S) N = N + S N
-    for (size_t i = 0; i < n; ++i) v[i] = poetx::GemmF32Run{rs[i]->S, X[i], rs[i]->Q, X[i], rs[i]->g.count};
-    if ((st = f32_runs(b, b, 1, 1, b, v, 1.0f, s)) != POETX_OK) return st;
-    for (size_t i = 0; i < n; ++i) rs[i]->N = X[i];
+    for (size_t i = 0; i < n; ++i) {
+      ExactRun& r = *rs[i];
+      HIP_TRY(poetx::launch_ns_final(r.X0, r.X1, r.iters, b, r.g.count, r.P0, r.Q, s));
+      r.N = r.P0;
+    }
   }
   return POETX_OK;
 }
@@ -595,11 +627,13 @@ poetx_status grad_items(const GradItem* items, int count, hipStream_t s) {
       // exact transform: rebuild N = (I - S)^{-1} and Q, then
       // dL/dS = (I + Q)^T G N^T and g(i, j) = dS[i][j] - dS[j][i] (batched below)
       const ChainWs& w = it.w;
+      int blk = 0;
       for (const Seg& g : pl->segs[side]) {
         const long long o = g.q_off;
         exact.push_back(ExactRun{g, it.theta, w.S + o, w.A0 + o, w.A1 + o, w.T0 + o, w.T1 + o, w.T + o,
-                                 nullptr});
+                                 nullptr, w.iters + blk});
         exact_items.push_back(i);
+        blk += g.count;
       }
       continue;
     }
@@ -815,6 +849,86 @@ poetx_status check_build_item(const BuildItem& it, size_t ws_bytes) {
   return POETX_OK;
 }
 
+// Q of one build item by Paterson-Stockmeyer (ps_step): S from the packed
+// parameters, the powers S^2 .. S^s, then the recurrence H <- B_i + S^s H with
+// each B_i a linear combination of I, S .. S^(s-1); fp32 throughout, Q cast to
+// the activation dtype at the end.
+poetx_status build_ps_item(const BuildItem& it, hipStream_t s) {
+  const poetx_plan* pl = it.pl;
+  const int d = pl->k + 1;
+  const int st = ps_step(d);
+  const int r = d / st;
+  float *S, *H0, *H1, *pw;
+  layout_build(pl, it.ws, &S, &H0, &H1, nullptr, nullptr, nullptr, &pw);
+  const long long ne = std::max(pl->nelem[0], pl->nelem[1]);
+  // P[j] = S^j for j = 1 .. s (P[0] unused: I enters through the diagonal)
+  std::vector<float*> P(st + 1, nullptr);
+  P[1] = S;
+  for (int j = 2; j <= st; ++j) P[j] = pw + (j - 2) * ne;
+  float* B = pw + (st - 1) * ne;
+  auto c = [&](int j) { return j <= d ? coef(j, pl->k) : 0.0f; };
+  for (const Seg& g : pl->segs[it.side]) {
+    const int b = g.b;
+    const long long o = g.q_off;
+    HIP_TRY(poetx::launch_unpack_skew(it.theta, g, S, nullptr, 0.0f, s));
+    // powers up to S^s (up to S^d when d < s never happens: s <= d)
+    const int top = r == 0 ? d : st;
+    for (int j = 2; j <= top; ++j) {
+      poetx_status e = chain_gemm(g, P[j - 1], S, P[j], nullptr, nullptr, 1.0f, 0.0f, s);
+      if (e != POETX_OK) return e;
+    }
+    // B_i = c_{is} I + sum_{0<l<s} c_{is+l} S^l; with fold, also + c_d S^s
+    auto make_b = [&](int i, float* out, bool fold_top) -> poetx_status {
+      poetx::LinComb lc{};
+      lc.diag = c(i * st);
+      for (int l = 1; l < st; ++l) {
+        lc.mats[lc.n] = P[l] + o;
+        lc.coef[lc.n++] = c(i * st + l);
+      }
+      if (fold_top) {
+        lc.mats[lc.n] = P[st] + o;
+        lc.coef[lc.n++] = c(d);
+      }
+      HIP_TRY(poetx::launch_lincomb(lc, out + o, b, g.count, s));
+      return POETX_OK;
+    };
+    poetx_status e;
+    if (r == 0) {   // degree below s: Q = sum_j c_j S^j directly
+      poetx::LinComb lc{};
+      lc.diag = c(0);
+      for (int j = 1; j <= d; ++j) {
+        lc.mats[lc.n] = P[j] + o;
+        lc.coef[lc.n++] = c(j);
+      }
+      HIP_TRY(poetx::launch_lincomb(lc, it.Q + o, b, g.count, s));
+    } else {
+      // H = B_r, or H = B_{r-1} + c_d S^s when B_r = c_d I
+      int i = r;
+      float* H = H0;
+      float* Hn = H1;
+      if (d % st == 0) {
+        --i;
+        if ((e = make_b(i, H, true)) != POETX_OK) return e;
+      } else {
+        if ((e = make_b(i, H, false)) != POETX_OK) return e;
+      }
+      for (--i; i >= 0; --i) {
+        if ((e = make_b(i, B, false)) != POETX_OK) return e;
+        float* dst = i == 0 ? it.Q : Hn;
+        if ((e = chain_gemm(g, P[st], H, dst, B, nullptr, 1.0f, 1.0f, s)) != POETX_OK) return e;
+        std::swap(H, Hn);
+      }
+      if (d % st == 0 && r == 1) {   // no product at all: H is Q
+        HIP_TRY(poetx::launch_lincomb(poetx::LinComb{{H + o}, {1.0f}, 1, 0.0f}, it.Q + o, b, g.count, s));
+      }
+    }
+    if (it.Qact)
+      HIP_TRY(poetx::launch_cast(it.Q + o, static_cast<char*>(it.Qact) + (size_t)elsize(pl) * o,
+                                 (long long)b * b * g.count, pl->dtype == POETX_BF16, s));
+  }
+  return POETX_OK;
+}
+
 // Builds every item: all runs of supported block sizes in one unpack launch and
 // one fused chain launch per size class; other sizes through batched GEMMs.
 poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
@@ -834,12 +948,21 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
     const poetx_plan* pl = it.pl;
     if (pl->cayley == POETX_CAYLEY_EXACT) {   // batched after the loop
       float *S, *P0, *P1, *X0, *X1;
-      layout_build(pl, it.ws, &S, &P0, &P1, &X0, &X1);
+      int32_t* iters;
+      layout_build(pl, it.ws, &S, &P0, &P1, &X0, &X1, &iters);
+      int blk = 0;
       for (const Seg& g : pl->segs[it.side]) {
         const long long o = g.q_off;
-        exact.push_back(ExactRun{g, it.theta, S + o, P0 + o, P1 + o, X0 + o, X1 + o, it.Q + o, nullptr});
+        exact.push_back(ExactRun{g, it.theta, S + o, P0 + o, P1 + o, X0 + o, X1 + o, it.Q + o, nullptr,
+                                 iters + blk});
         exact_items.push_back(i);
+        blk += g.count;
       }
+      continue;
+    }
+    if (build_ps(pl)) {   // Paterson-Stockmeyer on batched fp32 products
+      poetx_status st = build_ps_item(it, s);
+      if (st != POETX_OK) return st;
       continue;
     }
     if (kk != -1 && kk != pl->k) {   // one Neumann order per chain launch
@@ -967,6 +1090,7 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
     return POETX_ERR_INVALID_ARG;
   if (d->fold != POETX_FOLD_NONE && d->fold != POETX_FOLD_WEIGHT) return POETX_ERR_INVALID_ARG;
   if (d->index != POETX_INDEX_SEPARATE && d->index != POETX_INDEX_FUSED) return POETX_ERR_INVALID_ARG;
+  if (d->series != POETX_SERIES_CHAIN && d->series != POETX_SERIES_PS) return POETX_ERR_INVALID_ARG;
   const int32_t* bs[2] = {d->bsz_R, d->bsz_P};
   const int nb[2] = {d->nb_R, d->nb_P};
   const int dims[2] = {d->m, d->n};
@@ -996,6 +1120,7 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
   pl->cayley = d->cayley;
   pl->fold = d->fold;
   pl->index = d->index;
+  pl->series = d->series;
   for (int side = 0; side < 2; ++side) {
     pl->dim[side] = dims[side];
     long long q = 0, p = 0;

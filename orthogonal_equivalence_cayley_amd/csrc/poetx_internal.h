@@ -43,6 +43,24 @@ hipError_t launch_transpose_blocks(const void* Q, void* QT, int count, hipStream
 // S = skew(theta) for every block of the run; if Q != nullptr also Q = I + c1 * S.
 hipError_t launch_unpack_skew(const float* theta, const Seg& g, float* S, float* Q, float c1,
                               hipStream_t s);
+// Newton-Schulz inverse of I - S for count b x b blocks: X0 = a (I + S) with
+// a = 2 / (2 + c^2), c = max row sum of |S| (>= ||S||_2); iters[g] = steps
+// X <- X (2I - (I - S) X) block g needs for a residual below 2^-30 (<= jmax).
+hipError_t launch_ns_init(const float* S, int b, int count, float* X0, int32_t* iters, int jmax,
+                          hipStream_t s);
+// N = the iterate of block g (X0 if iters[g] is even, else X1); Q = 2 N - I.
+hipError_t launch_ns_final(const float* X0, const float* X1, const int32_t* iters, int b, int count,
+                           float* N, float* Q, hipStream_t s);
+// out = diag * I + sum_{i < n} coef[i] * mats[i] over count b x b blocks
+// (elementwise; n <= kLinCombMax; out may be one of mats).
+constexpr int kLinCombMax = 8;
+struct LinComb {
+  const float* mats[kLinCombMax];
+  float coef[kLinCombMax];
+  int n;
+  float diag;
+};
+hipError_t launch_lincomb(const LinComb& lc, float* out, int b, int count, hipStream_t s);
 // g[(i,j)] = sign * (M[i][j] - M[j][i]) for i < j, packed like theta.
 hipError_t launch_pack_antisym(const float* M, const Seg& g, float sign, float* gtheta,
                                hipStream_t s);
@@ -83,6 +101,9 @@ struct GemmF32 {
   int groups, splits;
   long long c_ss;
   float alpha, beta, gamma;
+  // when set, group g is skipped (C untouched) unless iters[g] > it
+  const int32_t* iters = nullptr;
+  int it = 0;
 };
 hipError_t launch_gemm_f32(const GemmF32& p, hipStream_t s);
 // Runs of the same shape and strides (splits = 1, no E output) in one launch:
@@ -90,6 +111,7 @@ hipError_t launch_gemm_f32(const GemmF32& p, hipStream_t s);
 struct GemmF32Run {
   const float* A; const float* B; float* C; const float* Cin;
   int groups;
+  const int32_t* iters = nullptr;   // per-group skip (GemmF32::iters, with the shape's it)
 };
 constexpr int kF32MaxRuns = 16;
 struct GemmF32Runs {

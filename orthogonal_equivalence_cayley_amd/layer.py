@@ -44,7 +44,8 @@ def param_grad_many(layers, g_thetas=None):
 class PoetxLayer:
     def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
                  dtype: str = "bf16", device: str = "cuda", weight: str = "dense",
-                 cayley: str = "neumann", fold: str = "none", index: str = "separate"):
+                 cayley: str = "neumann", fold: str = "none", index: str = "separate",
+                 series: str = "chain"):
         if dtype not in _TORCH_DTYPE:
             raise ValueError(f"dtype must be one of {sorted(_TORCH_DTYPE)}")
         if weight not in ("dense", "dense_t", "int8"):
@@ -56,7 +57,9 @@ class PoetxLayer:
             raise ValueError("fold must be 'none' (blocks on the activations) or 'weight'")
         if index not in ("separate", "fused"):
             raise ValueError("index must be 'separate' or 'fused' (index maps inside the block products)")
-        self.fold, self.index = fold, index
+        if series not in ("chain", "ps"):
+            raise ValueError("series must be 'chain' (power chain) or 'ps' (Paterson-Stockmeyer)")
+        self.fold, self.index, self.series = fold, index, series
         self.m, self.n, self.k, self.dtype = m, n, k, dtype
         self.weight = weight
         self.device = torch.device(device)
@@ -66,7 +69,8 @@ class PoetxLayer:
                               "int8": _px.WEIGHT_INT8_ROWS}[weight],
                              _px.CAYLEY_EXACT if cayley == "exact" else _px.CAYLEY_NEUMANN,
                              _px.FOLD_WEIGHT if fold == "weight" else _px.FOLD_NONE,
-                             _px.INDEX_FUSED if index == "fused" else _px.INDEX_SEPARATE)
+                             _px.INDEX_FUSED if index == "fused" else _px.INDEX_SEPARATE,
+                             _px.SERIES_PS if series == "ps" else _px.SERIES_CHAIN)
         self.nparam = (self.plan.param_count(_px.SIDE_R), self.plan.param_count(_px.SIDE_P))
         self.nelem = (self.plan.block_elems(_px.SIDE_R), self.plan.block_elems(_px.SIDE_P))
         self._ws = {}

@@ -46,6 +46,9 @@ FOLD_WEIGHT = 1
 INDEX_SEPARATE = 0
 INDEX_FUSED = 1
 
+SERIES_CHAIN = 0
+SERIES_PS = 1
+
 EXPORTED = (
     "poetx_plan_create", "poetx_plan_destroy", "poetx_param_count", "poetx_block_elems",
     "poetx_workspace_size", "poetx_status_string", "poetx_last_hip_error", "poetx_permute_weight",
@@ -76,6 +79,7 @@ class Desc(ctypes.Structure):
         ("bsz_R", ctypes.POINTER(ctypes.c_int32)), ("bsz_P", ctypes.POINTER(ctypes.c_int32)),
         ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("weight", ctypes.c_int32),
         ("cayley", ctypes.c_int32), ("fold", ctypes.c_int32), ("index", ctypes.c_int32),
+        ("series", ctypes.c_int32),
     ]
 
 
@@ -215,15 +219,15 @@ class Plan:
 
     def __init__(self, m: int, n: int, bsz_R: Sequence[int], bsz_P: Sequence[int], k: int,
                  dtype: int, weight: int = WEIGHT_DENSE, cayley: int = CAYLEY_NEUMANN,
-                 fold: int = FOLD_NONE, index: int = INDEX_SEPARATE):
+                 fold: int = FOLD_NONE, index: int = INDEX_SEPARATE, series: int = SERIES_CHAIN):
         self.m, self.n, self.k, self.dtype = int(m), int(n), int(k), int(dtype)
         self.weight, self.cayley, self.fold = int(weight), int(cayley), int(fold)
-        self.index = int(index)
+        self.index, self.series = int(index), int(series)
         self.bsz_R, self.bsz_P = tuple(int(b) for b in bsz_R), tuple(int(b) for b in bsz_P)
         aR = (ctypes.c_int32 * max(1, len(self.bsz_R)))(*self.bsz_R)
         aP = (ctypes.c_int32 * max(1, len(self.bsz_P)))(*self.bsz_P)
         d = Desc(self.m, self.n, len(self.bsz_R), len(self.bsz_P), aR, aP, self.k, self.dtype,
-                 self.weight, self.cayley, self.fold, self.index)
+                 self.weight, self.cayley, self.fold, self.index, self.series)
         h = ctypes.c_void_p()
         self._h = None
         _check(LIB.poetx_plan_create(ctypes.byref(d), ctypes.byref(h)), "poetx_plan_create")

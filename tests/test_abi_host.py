@@ -280,3 +280,20 @@ def test_index_option():
     with pytest.raises(px.PoetxError) as e:
         px.Plan(*args, 2)
     assert e.value.status == px.POETX_ERR_INVALID_ARG
+
+
+def test_series_option():
+    """Paterson-Stockmeyer builds keep the powers S^2 .. S^s and a B buffer:
+    at k = 4 the step is s = 2 (S^2 and B), so the build workspace grows by two
+    block arrays; bad values are refused."""
+    f32 = px.POETX_FP32
+    args = (64, 48, (32, 32), (16, 32), 4, f32, px.WEIGHT_DENSE, px.CAYLEY_NEUMANN, px.FOLD_NONE,
+            px.INDEX_SEPARATE)
+    chain = px.Plan(*args)
+    ps = px.Plan(*args, px.SERIES_PS)
+    ne = max(chain.block_elems(px.SIDE_R), chain.block_elems(px.SIDE_P))
+    grow = ps.workspace_size(0, px.WS_BUILD) - chain.workspace_size(0, px.WS_BUILD)
+    assert 2 * 4 * ne <= grow <= 2 * 4 * ne + 256
+    with pytest.raises(px.PoetxError) as e:
+        px.Plan(*args, 2)
+    assert e.value.status == px.POETX_ERR_INVALID_ARG

@@ -481,6 +481,11 @@ def test_merge_int8_weight():
     ("f32", dict(m=96, n=130, bR=(32, 64), bP=(65, 65), T=130, std=0.03)),
     ("f32", dict(m=70, n=45, bR=(30, 40), bP=(45,), T=9, std=0.05)),
     ("bf16", dict(m=512, n=256, bR=(256, 256), bP=(128, 128), T=300, std=0.01)),
+    # generators near and far past ||S||_2 = 1, where no truncated series converges
+    ("f32", dict(m=128, n=96, bR=(64, 64), bP=(32, 64), T=50, std=0.06)),
+    ("f32", dict(m=96, n=130, bR=(32, 64), bP=(65, 65), T=40, std=0.25)),
+    ("f32", dict(m=64, n=32, bR=(32, 32), bP=(32,), T=20, std=2.0)),
+    ("bf16", dict(m=256, n=512, bR=(256,), bP=(256, 256), T=200, std=0.06)),
 ])
 def test_exact_cayley_layer(dt, c):
     """Exact-Cayley mode: blocks, forward and backward against the oracle's
@@ -489,8 +494,9 @@ def test_exact_cayley_layer(dt, c):
     from orthogonal_equivalence_cayley_amd import PoetxLayer
     inp = workloads.small_case(c["m"], c["n"], c["bR"], c["bP"], T=c["T"], seed=c["T"] + 1, dtype=dt,
                                theta_std=c["std"])
-    log(f"exact cayley {dt} {c}")
     sp = inp.spec
+    S = oracle.skew_from_packed(inp.theta_R[:sp.bsz_R[0] * (sp.bsz_R[0] - 1) // 2], sp.bsz_R[0])
+    log(f"exact cayley {dt} {c}: ||S||_2 of the first R block {np.linalg.norm(S, 2):.3f}")
     L = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, 4, dtype=dt, cayley="exact")
     L.set_weight(to_dev(inp.W0, dt), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
     L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
@@ -576,3 +582,51 @@ def test_weight_kept_with_transpose(dt, c):
     ref = oracle.layer_reference(inp, 3)
     _compare(got, ref, ["Wa", "Y", "G_X", "g_theta_R", "g_theta_P"], TOL_F32 if dt == "f32" else TOL_BF16,
              "dense_t")
+
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 4, 5, 6, 7, 8, 12, 32])
+def test_paterson_stockmeyer_build(dt, k):
+    """POETX_SERIES_PS builds the same Q = sum_j c_j S^j as the power chain:
+    against the oracle's build at 1e-5 for every k the plans take a few of
+    (including k = 0, where Q = I + S, and the largest, 32), blocks of 32, 96,
+    256 and 512."""
+    import torch
+    from orthogonal_equivalence_cayley_amd import PoetxLayer
+    bsz = (32, 96, 256, 512) if dt == "f32" else (256, 512, 32, 96)
+    n = sum(bsz)
+    rng = np.random.default_rng(100 + k)
+    npar = sum(b * (b - 1) // 2 for b in bsz)
+    theta = (rng.standard_normal(npar) * 0.005).astype(np.float32)
+    log(f"PS build {dt} k={k}")
+    L = PoetxLayer(n, n, bsz, bsz, k, dtype=dt, series="ps")
+    L.set_theta(torch.from_numpy(theta), torch.from_numpy(theta))
+    L.build()
+    torch.cuda.synchronize()
+    want = blocks_concat(oracle.build_orth(theta, bsz, k))
+    for side in (0, 1):
+        err = oracle.rel_fro(to_np(L.Q32[side]), want)
+        log(f"  side {side}: rel_fro={err:.3e}")
+        assert err <= TOL_F32, (side, err)
+    if dt == "bf16":
+        # the activation copy is the round-to-nearest-even bf16 of the fp32 Q
+        assert torch.equal(L.Qact[0].view(torch.int16).cpu(),
+                           L.Q32[0].to(torch.bfloat16).view(torch.int16).cpu())
+
+
+def test_paterson_stockmeyer_layer():
+    """A whole layer (build, forward, backward) with the Paterson-Stockmeyer
+    build against the oracle."""
+    inp = workloads.small_case(512, 768, (256, 256), (256,) * 3, T=150, seed=77, dtype="bf16",
+                               theta_std=0.01)
+    import torch
+    from orthogonal_equivalence_cayley_amd import PoetxLayer
+    sp = inp.spec
+    L = PoetxLayer(sp.m, sp.n, sp.bsz_R, sp.bsz_P, 4, dtype="bf16", series="ps")
+    L.set_weight(to_dev(inp.W0, "bf16"), torch.from_numpy(inp.pi_R), torch.from_numpy(inp.pi_P))
+    L.set_theta(torch.from_numpy(inp.theta_R), torch.from_numpy(inp.theta_P))
+    got, _ = run_layer(inp, 4, "bf16", layer=L)
+    ref = oracle.layer_reference(inp, 4)
+    _compare(got, ref, ["QR", "QP"], TOL_F32, "ps")
+    _compare(got, ref, ["Wa", "Y", "G_X", "g_theta_R", "g_theta_P"], TOL_BF16, "ps")
