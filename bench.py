@@ -46,7 +46,42 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def stage_flops(w, T, xmem=False, exact=False, fold=False, int8=False):
+def ps_products(d: int) -> int:
+    """Products of the Paterson-Stockmeyer evaluation of a degree-d polynomial
+    (the step with the fewest: s - 1 powers and d // s recurrence products, one
+    less when d % s == 0)."""
+    return min((s - 1) + d // s - (1 if d % s == 0 else 0) for s in range(1, min(d, 8) + 1))
+
+
+def ns_steps(w) -> float:
+    """Mean Newton-Schulz step count of the exact transform over the workload's
+    blocks, by the library's rule: c = max row sum of |S|, rho = c^2 / (2 + c^2),
+    the least j with rho^(2^j) <= 2^-30 (at most 28)."""
+    import numpy as np
+    import workloads
+    steps = []
+    for li in range(len(w.layers)):
+        inp = workloads.layer_inputs(w, li, T=0, draw_grad=False)
+        for theta, bsz in ((inp.theta_R, inp.spec.bsz_R), (inp.theta_P, inp.spec.bsz_P)):
+            off = 0
+            for b in bsz:
+                npar = b * (b - 1) // 2
+                S = np.zeros((b, b))
+                S[np.triu_indices(b, 1)] = theta[off:off + npar]
+                S = S - S.T
+                off += npar
+                c = np.abs(S).sum(1).max()
+                j = 0
+                if c > 0:
+                    rho = c * c / (2 + c * c)
+                    need = 30 * np.log(2) / -np.log(rho)
+                    while j < 28 and 2.0 ** j < need:
+                        j += 1
+                steps.append(j)
+    return float(np.mean(steps))
+
+
+def stage_flops(w, T, xmem=False, exact=False, fold=False, int8=False, series="chain", nsj=0.0):
     """Flops each stage executes in one step of the workload. Input-centric
     (the default): 2 T sum(b^2) per side and pass for the block products. With
     --fold, a side folded into the weight costs 2 m sum(b_P^2) (forward, T >= m)
@@ -62,12 +97,13 @@ def stage_flops(w, T, xmem=False, exact=False, fold=False, int8=False):
         p_fwd = 2.0 * (sp.m if fold_f else T) * sqP
         f["w0_fwd"] += 2.0 * T * sp.m * sp.n
         f["block_fwd"] += p_fwd + 2.0 * T * sqR
-        f["build"] += 2.0 * (11 if exact else w.k) * cube
+        nprod = 2 * nsj if exact else (ps_products(w.k + 1) if series == "ps" else w.k)
+        f["build"] += 2.0 * nprod * cube
         if w.backward:
             f["w0_bwd"] += 2.0 * T * sp.m * sp.n
             f["block_bwd"] += 2.0 * (sp.n if fold_b else T) * sqR + 2.0 * T * sqP
             f["dq"] += 2.0 * T * (sqR + sqP)
-            f["cnp_bwd"] += 2.0 * (13 if exact else 2 * w.k) * cube
+            f["cnp_bwd"] += 2.0 * (2 * nsj + 2 if exact else 2 * w.k) * cube
             if xmem:
                 f["w0_fwd"] += 2.0 * T * sp.m * sp.n
                 f["block_fwd"] += p_fwd
@@ -209,6 +245,8 @@ def main() -> int:
                     help="POET-XQ: frozen weight stored as INT8 (one scale per row)")
     ap.add_argument("--xmem", action="store_true",
                     help="POET-Xmem: keep no Wa; the backward recomputes it from X")
+    ap.add_argument("--series", choices=("chain", "ps"), default="chain",
+                    help="build: power chain (default) or Paterson-Stockmeyer")
     ap.add_argument("--fold", action="store_true",
                     help="variant: fold the P blocks into the weight in the forward (T >= m) and the R "
                          "blocks in the backward (T >= n) instead of applying them to the activations")
@@ -233,7 +271,7 @@ def main() -> int:
     blk = BlockStep([workloads.layer_inputs(w, li, draw_grad=w.backward) for li in range(len(w.layers))],
                     w.k, w.dtype, backward=w.backward, streams=args.streams,
                     weight="int8" if args.xq else "dense_t", cayley="exact" if args.exact else "neumann",
-                    fold="weight" if args.fold else "none", xmem=args.xmem)
+                    fold="weight" if args.fold else "none", series=args.series, xmem=args.xmem)
     layers = blk.layers
     step = blk.step
     torch.cuda.synchronize()
@@ -263,7 +301,8 @@ def main() -> int:
     log(f"bench: {ms_per_step:.3f} ms/step")
 
     xmem = bool(args.xmem and w.backward)
-    flops = stage_flops(w, T, xmem, args.exact, args.fold, args.xq)
+    flops = stage_flops(w, T, xmem, args.exact, args.fold, args.xq, args.series,
+                        ns_steps(w) if args.exact else 0.0)
     merge = None
     if args.merge:
         # outer loop: fold the trained factors of every layer into its weight
@@ -380,8 +419,9 @@ def main() -> int:
             + "; layer input kept as U = X Pi_P^T",
             "frozen_weight": "int8, one fp32 scale per row (POET-XQ)" if args.xq
             else f"{w.dtype}, kept with its transpose",
-            "orthogonal_map": "exact Cayley (doubling build, closed-form gradient)" if args.exact
-            else f"Cayley-Neumann, k = {w.k}",
+            "orthogonal_map": "exact Cayley (Newton-Schulz inverse, closed-form gradient)" if args.exact
+            else f"Cayley-Neumann, k = {w.k}" + (", Paterson-Stockmeyer build" if args.series == "ps"
+                                                   else ", power-chain build"),
             "block_products": ("fold variant: P blocks folded into the weight in the forward where "
                                "T >= m, R blocks in the backward where T >= n, the other side on the "
                                "activations" if args.fold else
