@@ -338,11 +338,17 @@ def main() -> int:
             step(False)
         torch.cuda.synchronize()
         poetx.timing_enable([])
+        recorded = {s: poetx.timing_read(s) for s in poetx.STAGES}
+        # where the backward's block products and dL/dQ reductions run as one
+        # pass (sides of 256-wide blocks), their time is recorded under block_bwd
+        sflops = dict(flops)
+        if recorded["dq"][1] == 0:
+            sflops["block_bwd"] = sflops.get("block_bwd", 0.0) + sflops.get("dq", 0.0)
         for s in poetx.STAGES:
-            ms, cnt = poetx.timing_read(s)
+            ms, cnt = recorded[s]
             if cnt:
                 stages[s] = {"ms_per_step": ms / n_diag,
-                             "tflops": flops.get(s, 0.0) / (ms / n_diag * 1e-3) / 1e12 if ms else None}
+                             "tflops": sflops.get(s, 0.0) / (ms / n_diag * 1e-3) / 1e12 if ms else None}
         poetx.timing_reset()
 
     # dominant kernel: the frozen-weight product with the largest time share.

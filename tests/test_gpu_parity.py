@@ -630,3 +630,24 @@ def test_paterson_stockmeyer_layer():
     ref = oracle.layer_reference(inp, 4)
     _compare(got, ref, ["QR", "QP"], TOL_F32, "ps")
     _compare(got, ref, ["Wa", "Y", "G_X", "g_theta_R", "g_theta_P"], TOL_BF16, "ps")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 1000, 4097])
+@pytest.mark.parametrize("save", [True, False])
+def test_backward_token_tiles(T, save):
+    """Backward of sides of 256-wide blocks at token counts around the 64-token
+    tile of the dL/dQ reduction and its splits, and with a ragged tail, against
+    the oracle (save=False: POET-Xmem recomputation)."""
+    inp = workloads.small_case(512, 768, (256, 256), (256,) * 3, T=T, seed=T + 3, dtype="bf16",
+                               theta_std=0.01)
+    log(f"backward T={T} save={save}")
+    L = make_layer(inp, 4, "bf16")
+    L.build()
+    import torch
+    X, G = to_dev(inp.X, "bf16"), to_dev(inp.G_Y, "bf16")
+    L.forward(X, save=save)
+    G_X, gR, gP = L.backward(X, G)
+    torch.cuda.synchronize()
+    ref = oracle.layer_reference(inp, 4)
+    got = dict(G_X=to_np(G_X), g_theta_R=to_np(gR), g_theta_P=to_np(gP))
+    _compare(got, ref, ["G_X", "g_theta_R", "g_theta_P"], TOL_BF16, "backward")
