@@ -228,8 +228,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4, help="workload id in workloads.WORKLOADS")
     ap.add_argument("--cpu-tokens", type=int, default=None,
-                    help="tokens per layer of the oracle's timed sample (default: the full T "
-                         "up to 16384 tokens of hidden 2048, 4096 tokens above)")
+                    help="tokens per layer of the oracle's timed sample (default: the full batch "
+                         "at hidden 2048 and below, a quarter of it at hidden 4096)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing pass")
     ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
@@ -461,7 +461,9 @@ def main() -> int:
         log("bench: cpu baseline (oracle)")
         tok = args.cpu_tokens
         if tok is None:
-            tok = w.T if max(sp.n for sp in w.layers) <= 2048 else 4096
+            # the full batch up to hidden 2048 (about 20 s of float64 work on 16
+            # cores); a quarter of it at hidden 4096
+            tok = w.T if min(min(sp.m, sp.n) for sp in w.layers) <= 2048 else w.T // 4
         out["cpu_baseline"] = cpu_baseline(w, tok)
     print(json.dumps(out), flush=True)
     return 0
