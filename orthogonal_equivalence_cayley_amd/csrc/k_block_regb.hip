@@ -1,6 +1,6 @@
-// Batched block-diagonal products with blocks of 256 on gfx950
+// Batched block-diagonal products with blocks of 256 or 512 on gfx950
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulate): C[:, blk g] = A[:, blk g] B_g,
-// B_g(n, k) one 256 x 256 block of Q or of its transpose. These are the
+// B_g(n, k) one b x b block of Q or of its transpose. These are the
 // products of the orthogonal factors on the activations (Z = Wa D_R^T in the
 // forward, G_U = G_V D_P in the backward) and the weight-side Wf = Wt D_P
 // ([PX] = page "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
@@ -11,15 +11,17 @@
 // its pipeline. Here the block of B stays in registers instead: each of the 8
 // waves owns 32 output columns and keeps B_g(those columns, all 256 k) as its 16
 // MFMA operand fragments (64 VGPRs), loaded once per workgroup (a workgroup
-// stays on one block). Row tiles of A (ROWS rows x the block's 256 columns)
+// stays on one block). A block of 512 takes two workgroups, each with 256 of
+// its output columns and all 512 k (128 VGPRs of B per lane); its A tiles are
+// 64 rows x 512 (64 KiB) in two stages. Row tiles of A (ROWS rows x the block's columns)
 // stream from HBM into an LDS ring of ST stages with direct-to-LDS loads, ST - 1
 // tiles in flight while one is multiplied; every wave reads the whole A tile
 // from LDS. An HBM stream needs on the order of 100 KiB in flight per CU, so
 // the ring holds several small tiles rather than two large ones.
 //
-// A tile in LDS: row r of 256 bf16 is 32 chunks of 16 bytes; chunk c sits at
-// slot r * 32 + (c ^ (r & 31)), so the 16 rows read by one pass of an operand
-// read (one chunk each) fall in distinct banks.
+// A tile in LDS: row r of b bf16 is b / 8 chunks of 16 bytes; chunk c sits at
+// slot r * b / 8 + (c ^ (r & 31)), so the 16 rows read by one pass of an
+// operand read (one chunk each) fall in distinct banks.
 #include "poetx_internal.h"
 
 namespace poetx {
@@ -29,11 +31,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kB = 256;                         // block size (N = K)
+constexpr int kB = 256;                         // output columns per workgroup
 constexpr int kWaves = 8;                       // each owns 32 of the 256 columns
 constexpr int kThreads = kWaves * 64;
-constexpr int kNKK = kB / 16;                   // 16-deep K steps
-constexpr int kCPR = kB / 8;                    // 16-byte chunks per row of A
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
@@ -94,28 +94,37 @@ __device__ __forceinline__ bf16x8 frag_t(const unsigned char* st, int r0, int kk
 
 // AKM: A(m, k) = A_g[m * lda + k] (K-contiguous); otherwise A_g[k * lda + m]
 // (then M % ROWS == 0). BKM: B(n, k) = B_g[n * ldb + k] (K-contiguous, the
-// transposed Q); otherwise B(n, k) = B_g[k * ldb + n]. Workgroup w works on
-// block g = w / wpg and runs row tiles [(w % wpg) * per_wg, + per_wg) of it, so
-// it loads B_g only once.
-template <bool AKM, bool BKM, int ROWS, int ST, bool SCALE>
+// transposed Q); otherwise B(n, k) = B_g[k * ldb + n]. KD: the block size, which
+// is K; a block of 512 has its 512 output columns split over two workgroups of
+// 256 each (NH = KD / 256 column slices). Workgroup w works on slice w / wpg
+// (block g = slice / NH) and runs row tiles [(w % wpg) * per_wg, + per_wg) of
+// it, so it loads its part of B_g only once.
+template <bool AKM, bool BKM, int ROWS, int ST, bool SCALE, int KD = 256>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
-  constexpr int STAGE = ROWS * kB * 2;             // bytes of one A tile in LDS
+  constexpr int NH = KD / kB;                      // column slices per block
+  constexpr int kNKK = KD / 16;                    // 16-deep K steps
+  constexpr int kCPR = KD / 8;                     // 16-byte chunks per row of A
+  constexpr int STAGE = ROWS * KD * 2;             // bytes of one A tile in LDS
   constexpr int LOADS = ROWS * kCPR / kThreads;    // direct-to-LDS loads per thread per tile
   constexpr int MT = ROWS / 32;                    // 32-row MFMA tiles per wave and tile
-  constexpr int BROWS = STAGE / (kB * 2);          // rows of B_g one stage holds (NN fill)
+  constexpr int BROWS = STAGE / (kB * 2);          // rows of the slice of B_g one stage holds (NN fill)
+  constexpr int BLOADS = BROWS * (kB / 8) / kThreads;
   static_assert(ST >= 2 && ST <= 5 && LOADS * kThreads == ROWS * kCPR && ROWS % 32 == 0, "tile");
-  static_assert(kB % BROWS == 0 && BROWS % 16 == 0, "B in whole K steps per stage");
+  static_assert(KD % BROWS == 0 && BROWS % 16 == 0, "B in whole K steps per stage");
+  static_assert(AKM || KD == 256, "row-contiguous A only for blocks of 256");
   extern __shared__ __align__(16) unsigned char lds[];   // ST A tiles
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = blockIdx.x / wpg;
-  const int t0 = (blockIdx.x - g * wpg) * per_wg;
+  const int gs = blockIdx.x / wpg;                 // column slice
+  const int g = gs / NH, hs = gs - g * NH;
+  const int t0 = (blockIdx.x - gs * wpg) * per_wg;
   const int t1 = min(tiles_per_group, t0 + per_wg);
   if (g >= p.groups || t0 >= t1) return;
   const uint16_t* Ag = static_cast<const uint16_t*>(p.A) + (long long)g * p.a_gs;
-  const uint16_t* Bg = static_cast<const uint16_t*>(p.B) + (long long)g * p.b_gs;
-  uint16_t* Cg = static_cast<uint16_t*>(p.C) + (long long)g * p.c_gs + wave * 32;
+  const uint16_t* Bg = static_cast<const uint16_t*>(p.B) + (long long)g * p.b_gs +
+                       (long long)hs * kB * (BKM ? p.ldb : 1);
+  uint16_t* Cg = static_cast<uint16_t*>(p.C) + (long long)g * p.c_gs + hs * kB + wave * 32;
   const int nl = lane & 31, h = lane >> 5;
   const int ncol = wave * 32 + nl;   // B column of this lane's operand fragments
   auto stage = [&](int i) { return lds + i * STAGE; };
@@ -151,17 +160,17 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
     for (int kk = 0; kk < kNKK; ++kk)
       bq[kk] = *reinterpret_cast<const bf16x8*>(Bg + (long long)ncol * p.ldb + 16 * kk + 8 * h);
   } else {
-    // column ncol of B_g through the still free last stage, BROWS rows of B_g at
-    // a time in natural layout (row k = 512 bytes); the 32 lanes of a read take
-    // 64 consecutive bytes of one row
+    // column ncol of the slice of B_g through the still free last stage,
+    // BROWS rows of it at a time in natural layout (row k = 512 bytes); the 32
+    // lanes of a read take 64 consecutive bytes of one row
     const uint16_t* Bl = reinterpret_cast<const uint16_t*>(stage(ST - 1));
 #pragma unroll
-    for (int part = 0; part < kB / BROWS; ++part) {
+    for (int part = 0; part < KD / BROWS; ++part) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
+      for (int i = 0; i < BLOADS; ++i) {
         const int s = i * kThreads + tid;
-        const int k = part * BROWS + s / kCPR;
-        dma16(Bg + (long long)k * p.ldb + (s % kCPR) * 8, stage(ST - 1) + (i * kThreads + wave * 64) * 16);
+        const int k = part * BROWS + s / (kB / 8);
+        dma16(Bg + (long long)k * p.ldb + (s % (kB / 8)) * 8, stage(ST - 1) + (i * kThreads + wave * 64) * 16);
       }
       wait_vmcnt<0>();
       lds_barrier();
@@ -219,7 +228,8 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
       for (int q = 0; q < 4; ++q) {
         float4 sc = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
         if (SCALE)   // column n scaled by col_scale[g * c_gs + n] before the rounding
-          sc = *reinterpret_cast<const float4*>(p.col_scale + (long long)g * p.c_gs + wave * 32 + 8 * q + 4 * h);
+          sc = *reinterpret_cast<const float4*>(p.col_scale + (long long)g * p.c_gs + hs * kB + wave * 32 +
+                                                8 * q + 4 * h);
         w[q][0] = pack_bf16_pair(acc[mt][4 * q] * sc.x, acc[mt][4 * q + 1] * sc.y);
         w[q][1] = pack_bf16_pair(acc[mt][4 * q + 2] * sc.z, acc[mt][4 * q + 3] * sc.w);
       }
@@ -248,20 +258,22 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
 
 constexpr int kRows = 64;   // rows of A per tile
 constexpr int kST = 4;      // LDS stages: three 32 KiB tiles in flight
+constexpr int kST512 = 2;   // blocks of 512: 64 KiB tiles, two stages
 constexpr int kRowsT = 128; // row-contiguous A: 128-row tiles (64 KiB, the swizzle needs 16 chunks)
 constexpr int kSTT = 2;     // and two stages
 
 }  // namespace
 
 bool block_regb_supported(const GemmBf16& p) {
-  if (p.role != GEMM_BLOCK || p.N != kB || p.K != kB || p.out_f32) return false;
+  if (p.role != GEMM_BLOCK || p.out_f32) return false;
+  if (!((p.N == kB && p.K == kB) || (p.N == 2 * kB && p.K == 2 * kB && p.a_kmajor))) return false;
   // row-contiguous A (the transposed weight fold): whole tiles, K-contiguous Q,
   // no column scale
   if (!p.a_kmajor && (p.M % kRowsT || !p.b_kmajor || p.col_scale)) return false;
   if (p.splits != 1 || p.b_i8 || p.M <= 0 || p.groups <= 0) return false;
   if (p.col_scale && (((uintptr_t)p.col_scale & 15) || p.c_gs % 4)) return false;
   if (p.lda % 8 || p.a_gs % 8 || p.ldc % 8 || p.c_gs % 8) return false;   // 16-byte rows
-  if (p.ldb % 8 || p.ldb < kB) return false;   // 16-byte rows of B either way
+  if (p.ldb % 8 || p.ldb < p.N) return false;   // 16-byte rows of B either way (N = K)
   if (((uintptr_t)p.A | (uintptr_t)p.C | (uintptr_t)p.B) & 15) return false;
   return true;
 }
@@ -271,15 +283,28 @@ hipError_t launch_block_regb(const GemmBf16& p, hipStream_t s) {
   const int rows = p.a_kmajor ? kRows : kRowsT;
   const long long tpg = (p.M + rows - 1) / rows;
   if (tpg > INT32_MAX) return hipErrorInvalidValue;
-  // one workgroup per CU (the LDS ring): up to 256 / groups workgroups per
-  // block, each on consecutive row tiles of that block only
-  const long long wmax = p.groups >= 256 ? 1 : 256 / p.groups;
+  // one workgroup per CU (the LDS ring): up to 256 / slices workgroups per
+  // column slice (blocks of 512 have two), each on consecutive row tiles of it
+  const long long slices = (long long)p.groups * (p.N / kB);
+  const long long wmax = slices >= 256 ? 1 : 256 / slices;
   const long long per = (tpg + wmax - 1) / wmax;
   const long long wpg = (tpg + per - 1) / per;
-  const long long wgs = wpg * p.groups;
+  const long long wgs = wpg * slices;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs), block(kThreads);
   const int a = (int)tpg, b = (int)wpg, c = (int)per;
+  if (p.N == 2 * kB) {   // blocks of 512 (K-contiguous A)
+    const size_t lds = (size_t)kST512 * kRows * 2 * kB * 2;
+    if (p.b_kmajor && p.col_scale)
+      hipLaunchKernelGGL((block_regb_kernel<true, true, kRows, kST512, true, 512>), grid, block, lds, s, p, a, b, c);
+    else if (p.b_kmajor)
+      hipLaunchKernelGGL((block_regb_kernel<true, true, kRows, kST512, false, 512>), grid, block, lds, s, p, a, b, c);
+    else if (p.col_scale)
+      hipLaunchKernelGGL((block_regb_kernel<true, false, kRows, kST512, true, 512>), grid, block, lds, s, p, a, b, c);
+    else
+      hipLaunchKernelGGL((block_regb_kernel<true, false, kRows, kST512, false, 512>), grid, block, lds, s, p, a, b, c);
+    return hipGetLastError();
+  }
   if (!p.a_kmajor) {   // the transposed weight fold: K-contiguous Q, no column scale
     if (!p.b_kmajor || p.col_scale) return hipErrorInvalidValue;
     const size_t lds = (size_t)kSTT * kRowsT * kB * 2;

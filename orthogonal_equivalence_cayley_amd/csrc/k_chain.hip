@@ -265,12 +265,13 @@ __device__ __forceinline__ void split4(float4 x, uint2& h, uint2& l) {
   l = make_uint2(u(l0) | (u(l1) << 16), u(l2) | (u(l3) << 16));
 }
 
-// NT 32-column tiles per wave (4 waves), U K-steps of 16 prefetched.
+// NT 32-column tiles per wave (NW waves: 4 up to b = 256, 8 for b = 512, so
+// that a wave's registers do not grow with b), U K-steps of 16 prefetched.
 // BF: the block size when every entry of the launch has it (0: read per entry);
 // with it fixed the K loop unrolls completely and each operand load is waited
 // for exactly (in a rolled loop the compiler waits for every load each pass).
-template <int MODE, int NT, int U, int BF>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chain_split_kernel(ChainBatch cb) {
+template <int MODE, int NT, int U, int BF, int NW = 4>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void chain_split_kernel(ChainBatch cb) {
   constexpr int RP = 32;
   extern __shared__ __align__(16) float lds[];
   const ChainEntry p = select_entry(cb);
@@ -299,8 +300,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   bool valid[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    valid[t] = wave + 4 * t < ntiles;
-    n0[t] = min(wave + 4 * t, ntiles - 1) * 32;
+    valid[t] = wave + NW * t < ntiles;
+    n0[t] = min(wave + NW * t, ntiles - 1) * 32;
   }
   // this lane's panel row and its 4-column groups: row l32, columns n0 + 8 q + 4 hf + 0..3
   const int row = l32;
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // the panel is S: its rows r0 .. r0 + 31 are the negated rows of M, which
     // the 1 KiB fragment blocks of tile r0 / 32 hold (lane l: row l % 32, the 8
     // columns from 16 ks + 8 (l / 32) in K-step ks); negating bf16 is exact.
-    // Each wave copies K-steps wave, wave + 4, ... (b <= 256: at most 4); loads
+    // Each wave copies K-steps wave, wave + NW, ... (b <= 64 NW: at most 4); loads
     // past the block's last K-step are not stored (those past the block's end
     // read zeros: buffer loads are range-checked)
     const int nk = b >> 4;
@@ -356,14 +357,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     uint4 fh[4], fl[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ks = wave + 4 * i;
+      const int ks = wave + NW * i;
       fh[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, voff, rb + ks * 1024, 0));
       fl[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rl, voff, rb + ks * 1024, 0));
     }
     constexpr uint32_t kNeg = 0x80008000u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ks = wave + 4 * i;
+      const int ks = wave + NW * i;
       if (ks < nk) {
         const int c = 16 * ks + 8 * hf;
         *reinterpret_cast<uint4*>(ph + row * pitch + c) =
@@ -539,7 +540,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-template <int MODE, int NT>
+template <int MODE, int NT, int NW = 4>
 hipError_t launch_split_class(ChainBatch cb, hipStream_t s) {
   constexpr int RP = 32;
   int wg = 0, bmax = 0, bmin = 1 << 30;
@@ -557,12 +558,15 @@ hipError_t launch_split_class(ChainBatch cb, hipStream_t s) {
   // (b % 32 == 0 always allows U = 2; mixed sizes: the transposed chain's extra
   // loads leave registers for two steps only)
   constexpr int UM = MODE == 2 ? 2 : 4;
-  if (bmin == 256 && bmax == 256)
-    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 4, 256>), dim3(wg), dim3(kThreads), lds, s, cb);
+  const dim3 blk(NW * 64);
+  if (NW == 8 && bmin == 512 && bmax == 512)
+    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 4, 512, NW>), dim3(wg), blk, lds, s, cb);
+  else if (NW == 4 && bmin == 256 && bmax == 256)
+    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 4, 256, NW>), dim3(wg), blk, lds, s, cb);
   else if (UM == 2 || by64)
-    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, UM, 0>), dim3(wg), dim3(kThreads), lds, s, cb);
+    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, UM, 0, NW>), dim3(wg), blk, lds, s, cb);
   else
-    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 2, 0>), dim3(wg), dim3(kThreads), lds, s, cb);
+    hipLaunchKernelGGL((chain_split_kernel<MODE, NT, 2, 0, NW>), dim3(wg), blk, lds, s, cb);
   return hipGetLastError();
 }
 
@@ -602,12 +606,24 @@ hipError_t launch_mode(const ChainBatch& all, hipStream_t s) {
     cb.k = all.k;
     for (int i = 0; i < all.n; ++i) {
       const ChainEntry& e = all.e[i];
-      if (!e.Mh || !chain_split_supported(e.b)) continue;
+      if (!e.Mh || !chain_split_supported(e.b) || e.b > 256) continue;
       if ((e.b / 32 + 3) / 4 == nt) cb.e[cb.n++] = e;
     }
     if (cb.n == 0) continue;
     const hipError_t e = nt == 1 ? launch_split_class<MODE, 1>(cb, s) : launch_split_class<MODE, 2>(cb, s);
     if (e != hipSuccess) return e;
+  }
+  {
+    // blocks of 288 .. 512: 8 waves of up to two 32-column tiles each
+    ChainBatch cb;
+    cb.n = 0;
+    cb.k = all.k;
+    for (int i = 0; i < all.n; ++i)
+      if (all.e[i].Mh && chain_split_supported(all.e[i].b) && all.e[i].b > 256) cb.e[cb.n++] = all.e[i];
+    if (cb.n > 0) {
+      const hipError_t e = launch_split_class<MODE, 2, 8>(cb, s);
+      if (e != hipSuccess) return e;
+    }
   }
   // one launch per size class (column tiles per wave, and panels of 32 rows
   // where b allows them: each B value then feeds two row tiles)
@@ -647,8 +663,8 @@ hipError_t launch_mode(const ChainBatch& all, hipStream_t s) {
 // b % 16 == 0 keeps every row of S a whole number of float4 and every 16-row
 // chunk a whole number of per-thread loads (b = 16 .. 512).
 bool chain_supported(int b) { return b % 16 == 0 && b >= 16 && b <= 512; }
-// 32-row panels and 32-column tiles; at most two tiles per wave
-bool chain_split_supported(int b) { return b % 32 == 0 && b >= 32 && b <= 256; }
+// 32-row panels and 32-column tiles; at most two tiles per wave (8 waves above 256)
+bool chain_split_supported(int b) { return b % 32 == 0 && b >= 32 && b <= 512; }
 
 hipError_t launch_chain_batch(int mode, const ChainBatch& cb, hipStream_t s) {
   if (cb.n < 0 || cb.n > kChainMaxEntries) return hipErrorInvalidValue;
@@ -678,7 +694,7 @@ __device__ __forceinline__ TriEntry select_tri(const TriBatch& tb, int w) {
 // Split operand of the bf16 chains in MFMA fragment order: for 32-row tile nt of
 // M and K-step kc (16 columns), 64 lanes x 8 bf16 = 1 KiB, lane r + 32 h holding
 // M[32 nt + r][16 kc + 8 h .. + 7]; so each operand load is one contiguous read.
-__device__ __forceinline__ long long split_frag_offset(int n, int k, int b) {
+[[maybe_unused]] __device__ __forceinline__ long long split_frag_offset(int n, int k, int b) {
   const int nt = n >> 5, r = n & 31, kc = k >> 4, h = (k >> 3) & 1, e = k & 7;
   return ((((long long)nt * (b >> 4) + kc) * 64) + r + 32 * h) * 8 + e;
 }
@@ -779,6 +795,8 @@ __global__ __launch_bounds__(kThreads) void unpack_batch_kernel(TriBatch tb) {
 // row c < r (a 128-byte run), stored transposed. Each wave then writes whole
 // 1 KiB fragment blocks of both halves.
 constexpr int kSplitRows = 32;
+// NP: 64-column passes per row (b <= 64 NP)
+template <int NP>
 __global__ __launch_bounds__(kThreads) void unpack_split_kernel(TriBatch tb) {
   extern __shared__ __align__(16) float tile[];   // [kSplitRows][b + 4]
   const TriEntry t = select_tri(tb, blockIdx.x);
@@ -794,8 +812,8 @@ __global__ __launch_bounds__(kThreads) void unpack_split_kernel(TriBatch tb) {
   const float* th = t.src + (long long)g * ((long long)b * (b - 1) / 2);
   const int pitch = b + 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // every load of both triangles is issued before the first LDS write (b <=
-  // 256: at most 64 per lane), so that a workgroup waits for memory once. The
+  // every load of both triangles is issued before the first LDS write (at most
+  // 16 NP per lane), so that a workgroup waits for memory once. The
   // loads are unconditional range-checked buffer loads of the block's packed
   // parameters (an offset past the end reads 0) and the triangle tests select
   // among the loaded values: a load under a branch waits for its value there.
@@ -805,15 +823,15 @@ __global__ __launch_bounds__(kThreads) void unpack_split_kernel(TriBatch tb) {
   auto ld = [&](int idx) {   // theta[idx], 0 outside the block
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rth, max(idx, 0) * 4, 0, 0));
   };
-  // diagonal and above: rows R0 + wave + 4 jj, columns r .. b - 1 in four
+  // diagonal and above: rows R0 + wave + 4 jj, columns r .. b - 1 in NP
   // passes of 64 lanes; theta(r, c) at tri_off(r, c) = rs + c for c > r
-  float vu[8][4];
+  float vu[8][NP];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     const int r = R0 + wave + 4 * jj;
     const int rs = (int)tri_off(r, r + 1, b) - (r + 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NP; ++i) {
       const int c = r + lane + 64 * i;
       const float v = ld(rs + c);
       vu[jj][i] = c > r ? -v : 0.0f;
@@ -822,9 +840,9 @@ __global__ __launch_bounds__(kThreads) void unpack_split_kernel(TriBatch tb) {
   // below the diagonal: packed rows c < R0 + 31, two per wave instruction (half
   // a wave each), columns R0 + j with c < R0 + j
   const int j = lane & 31, col = R0 + j;
-  float vl[4][8];
+  float vl[NP][8];
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass)
+  for (int pass = 0; pass < NP; ++pass)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int c = 64 * pass + 8 * u + 2 * wave + (lane >> 5);
@@ -835,13 +853,13 @@ __global__ __launch_bounds__(kThreads) void unpack_split_kernel(TriBatch tb) {
   for (int jj = 0; jj < 8; ++jj) {
     const int jr = wave + 4 * jj, r = R0 + jr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NP; ++i) {
       const int c = r + lane + 64 * i;
       if (c < b) tile[jr * pitch + c] = vu[jj][i];
     }
   }
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass)
+  for (int pass = 0; pass < NP; ++pass)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int c = 64 * pass + 8 * u + 2 * wave + (lane >> 5);
@@ -990,7 +1008,10 @@ hipError_t launch_unpack_batch(const TriBatch& in, hipStream_t s) {
     }
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
     const size_t lds = (size_t)kSplitRows * (bmax + 4) * sizeof(float);
-    hipLaunchKernelGGL(unpack_split_kernel, dim3((unsigned)wgs), dim3(kThreads), lds, s, ts);
+    if (bmax <= 256)
+      hipLaunchKernelGGL(unpack_split_kernel<4>, dim3((unsigned)wgs), dim3(kThreads), lds, s, ts);
+    else
+      hipLaunchKernelGGL(unpack_split_kernel<8>, dim3((unsigned)wgs), dim3(kThreads), lds, s, ts);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -158,8 +158,8 @@ hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
 // big = 256 x 256 tiles, else 128 x 128.
 bool gemm_lds_supported(const GemmBf16& p, int bm, int bn);
 hipError_t launch_gemm_lds(const GemmBf16& p, int big, hipStream_t s);
-// Block products with b = 256 (N = K = 256, GEMM_BLOCK, A K-contiguous, bf16
-// output, optional column scale): B in registers, A tiles streamed through LDS
+// Block products with b = 256 or 512 (N = K, GEMM_BLOCK, bf16 output, optional
+// column scale): B in registers, A tiles streamed through LDS
 // (k_block_regb.hip).
 bool block_regb_supported(const GemmBf16& p);
 hipError_t launch_block_regb(const GemmBf16& p, hipStream_t s);

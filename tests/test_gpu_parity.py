@@ -148,6 +148,10 @@ def test_layer_fp32_ragged(case):
     dict(m=512, n=256, bR=(256, 256), bP=(128, 128), T=300, k=4),
     dict(m=384, n=320, bR=(128, 256), bP=(64, 256), T=77, k=3),
     dict(m=2048, n=512, bR=(512,) * 3 + (256, 256), bP=(512,), T=1000, k=5),
+    # blocks of 512 only: the block products with two workgroups per block and
+    # the split chains with eight waves (ragged and whole row tiles)
+    dict(m=1024, n=1024, bR=(512, 512), bP=(512, 512), T=130, k=4),
+    dict(m=512, n=1536, bR=(512,), bP=(512,) * 3, T=64, k=5),
     dict(m=256, n=256, bR=(256,), bP=(256,), T=1, k=4),
     dict(m=48, n=32, bR=(16, 32), bP=(32,), T=5, k=0),
     # split chains over blocks that are multiples of 32 but not of 64, alone and
@@ -260,6 +264,7 @@ def test_backward_split_matches_backward():
 @pytest.mark.parametrize("case", [
     ("bf16", dict(m=512, n=256, bR=(256, 256), bP=(128, 128), T=300, k=4)),
     ("bf16", dict(m=256, n=768, bR=(256,), bP=(512, 256), T=1000, k=3)),
+    ("bf16", dict(m=1024, n=512, bR=(512, 512), bP=(512,), T=200, k=4)),
     ("f32", dict(m=96, n=130, bR=(32, 64), bP=(65, 65), T=130, k=2)),
 ])
 def test_xmem_recompute_matches_saved(case):
