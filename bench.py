@@ -344,11 +344,19 @@ def main() -> int:
         sflops = dict(flops)
         if recorded["dq"][1] == 0:
             sflops["block_bwd"] = sflops.get("block_bwd", 0.0) + sflops.get("dq", 0.0)
+        # bf16 plans run every product of the build and chain-rule chains as
+        # three bf16 MFMAs on split operands (blocks that are multiples of 32 up
+        # to 512): the matrix cores then run 3x the products' flops
+        split = (w.dtype == "bf16" and not args.exact and args.series == "chain" and
+                 all(b % 32 == 0 and b <= 512 for sp in w.layers for b in sp.bsz_R + sp.bsz_P))
         for s in poetx.STAGES:
             ms, cnt = recorded[s]
             if cnt:
                 stages[s] = {"ms_per_step": ms / n_diag,
                              "tflops": sflops.get(s, 0.0) / (ms / n_diag * 1e-3) / 1e12 if ms else None}
+                if split and s in ("build", "cnp_bwd") and ms:
+                    stages[s]["mfma_tflops_bf16"] = 3.0 * stages[s]["tflops"]
+                    stages[s]["frac_of_bf16_peak"] = 3.0 * stages[s]["tflops"] * 1e12 / PEAK_BF16
         poetx.timing_reset()
 
     # dominant kernel: the frozen-weight product with the largest time share.
