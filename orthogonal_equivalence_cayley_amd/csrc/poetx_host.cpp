@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstring>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -1063,7 +1064,12 @@ const char* poetx_last_hip_error(void) {
 }
 
 const char* poetx_status_string(poetx_status st) {
-  switch (st) {
+  // callers may pass any integer: read it as one (a value outside the
+  // enumerators is not a valid value of the enum type in C++)
+  static_assert(sizeof(poetx_status) == sizeof(int), "status passed as an int");
+  int v;
+  std::memcpy(&v, &st, sizeof v);
+  switch (v) {
     case POETX_OK: return "ok";
     case POETX_ERR_INVALID_ARG: return "invalid argument";
     case POETX_ERR_SHAPE: return "inconsistent shape";

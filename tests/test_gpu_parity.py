@@ -108,6 +108,22 @@ def test_build_orth(dtype, bsz, k, std):
         assert np.all(np.abs(qa - want) <= np.abs(want) * 2.0 ** -8 + 1e-6)
 
 
+@pytest.mark.parametrize("k", list(range(9)))
+@pytest.mark.parametrize("dtype,bsz", [("f32", (64, 33)), ("bf16", (256, 96))])
+def test_build_orth_every_k(dtype, bsz, k):
+    """The power-chain build for every k from 0 to 8 (fp32 chains; split bf16
+    chains for the bf16 plan) against the oracle's series."""
+    import torch
+    log(f"build_orth chain {dtype} {bsz} k={k}")
+    inp = workloads.small_case(sum(bsz), 16, bsz, (16,), T=1, seed=100 + k, dtype=dtype, theta_std=0.02)
+    layer = make_layer(inp, k, dtype)
+    layer.build()
+    torch.cuda.synchronize()
+    want = blocks_concat(oracle.build_orth(inp.theta_R, bsz, k))
+    got = layer.Q32[0].cpu().numpy().astype(np.float64)
+    assert oracle.rel_fro(got, want) <= TOL_F32
+
+
 # ---------------------------------------------------------------- whole layer
 
 def _compare(got, ref, keys, tol, tag):
@@ -167,6 +183,29 @@ def test_layer_bf16_small(case):
     ref = oracle.layer_reference(inp, case["k"])
     _compare(got, ref, ["QR", "QP"], TOL_F32, "bf16")
     _compare(got, ref, ["Wa", "Y", "G_X", "g_theta_R", "g_theta_P"], TOL_BF16, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_identity_permutations(dtype):
+    """pi_R and pi_P the identity: the gather and the scatter copy rows
+    unchanged (U = X bit for bit) and the layer matches the oracle."""
+    import torch
+    inp = workloads.small_case(512, 256, (256, 256), (128, 128), T=200, seed=31, dtype=dtype,
+                               theta_std=0.01 if dtype == "bf16" else 0.05)
+    inp.pi_R = np.arange(512, dtype=inp.pi_R.dtype)
+    inp.pi_P = np.arange(256, dtype=inp.pi_P.dtype)
+    log(f"identity permutations {dtype}")
+    L = make_layer(inp, 4, dtype)
+    L.build()
+    X = to_dev(inp.X, dtype)
+    U = L.gather_u(X)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(U), _bits(X))
+    got, _ = run_layer(inp, 4, dtype)
+    ref = oracle.layer_reference(inp, 4)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    _compare(got, ref, ["QR", "QP"], TOL_F32, "identity")
+    _compare(got, ref, ["Wa", "Y", "G_X", "g_theta_R", "g_theta_P"], tol, "identity")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
