@@ -15,6 +15,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLdsBudget = 64 * 1024;   // bytes of LDS for staged rows per workgroup
 constexpr int kMaxRows = 4;             // rows per workgroup: small tiles keep the grid full
+// Second-phase items of the interleaved gather: (R / G) (dim / VEC) =
+// R dim sizeof(E)^2 / 128 <= kLdsBudget sizeof(E) / 128 <= kLdsBudget / 32
+// (G = 8 / sizeof(E), VEC = 16 / sizeof(E), sizeof(E) <= 4).
+static_assert(kLdsBudget / 32 <= 8 * 256, "gather index prefetch covers every item");
 
 template <typename E, int VEC>
 struct Vec { E v[VEC]; };
@@ -125,7 +129,10 @@ struct Inter {
 };
 
 // out[t][i] = in[row(t)][idx[i]] for R rows per iteration (R a multiple of G).
-template <typename E>
+// A thread's items of the second phase are the same in every iteration, so
+// their indices are loaded once, before the first rows: the random LDS reads
+// after the barrier then wait on nothing but LDS (ngrp * cpr <= NI * kThreads).
+template <typename E, int NI>
 __global__ __launch_bounds__(kThreads) void gather_cols_inter(
     const E* __restrict__ in, long long in_ld, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ idx, E* __restrict__ out, long long T, int dim, int R) {
@@ -135,6 +142,14 @@ __global__ __launch_bounds__(kThreads) void gather_cols_inter(
   uint64_t* lds = reinterpret_cast<uint64_t*>(smem);   // [R / G][dim]
   const int cpr = dim / VEC;
   const int ngrp = R / G;
+  int ixs[NI][VEC];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int c = threadIdx.x + j * kThreads;
+    const int q = c < ngrp * cpr ? c % cpr : 0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ixs[j][e] = idx[q * VEC + e];
+  }
   for (long long t0 = (long long)blockIdx.x * R; t0 < T; t0 += (long long)gridDim.x * R) {
     const int nr = (int)((T - t0) < R ? (T - t0) : R);
     // load G rows x VEC elements per item, interleave, write VEC words
@@ -157,12 +172,15 @@ __global__ __launch_bounds__(kThreads) void gather_cols_inter(
       }
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < ngrp * cpr; c += kThreads) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int c = threadIdx.x + j * kThreads;
+      if (c >= ngrp * cpr) break;
       const int g = c / cpr, q = c - g * cpr;
       const uint64_t* src = lds + (long long)g * dim;
       uint64_t wv[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) wv[e] = src[idx[q * VEC + e]];
+      for (int e = 0; e < VEC; ++e) wv[e] = src[ixs[j][e]];
 #pragma unroll
       for (int r = 0; r < G; ++r) {
         const int row = g * G + r;
@@ -298,8 +316,20 @@ hipError_t gather_typed(const void* in, long long in_ld, const int32_t* rows, co
   if (vec && R >= G) {
     R = R / G * G;
     const size_t lds = (size_t)R * row_bytes;
-    hipLaunchKernelGGL((gather_cols_inter<E>), dim3(grid_for((T + R - 1) / R)), dim3(kThreads),
-                       lds, s, (const E*)in, in_ld, rows, idx, (E*)out, T, dim, R);
+    const long long items = (long long)(R / G) * (dim / VEC);   // second-phase items per workgroup
+    const dim3 grid(grid_for((T + R - 1) / R)), block(kThreads);
+    if (items <= kThreads)
+      hipLaunchKernelGGL((gather_cols_inter<E, 1>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
+                         (E*)out, T, dim, R);
+    else if (items <= 2 * kThreads)
+      hipLaunchKernelGGL((gather_cols_inter<E, 2>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
+                         (E*)out, T, dim, R);
+    else if (items <= 4 * kThreads)
+      hipLaunchKernelGGL((gather_cols_inter<E, 4>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
+                         (E*)out, T, dim, R);
+    else   // R <= kMaxRows and R dim sizeof(E) <= kLdsBudget bound items by 8 kThreads
+      hipLaunchKernelGGL((gather_cols_inter<E, 8>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
+                         (E*)out, T, dim, R);
     return hipGetLastError();
   }
   const size_t lds = (size_t)R * row_bytes;
