@@ -270,7 +270,7 @@ def main() -> int:
     log(f"bench: {w.name} T={T} layers={len(w.layers)} k={w.k}")
     blk = BlockStep([workloads.layer_inputs(w, li, draw_grad=w.backward) for li in range(len(w.layers))],
                     w.k, w.dtype, backward=w.backward, streams=args.streams,
-                    weight="int8" if args.xq else "dense_t", cayley="exact" if args.exact else "neumann",
+                    weight="int8_t" if args.xq else "dense_t", cayley="exact" if args.exact else "neumann",
                     fold="weight" if args.fold else "none", series=args.series, xmem=args.xmem)
     layers = blk.layers
     step = blk.step
@@ -366,9 +366,9 @@ def main() -> int:
     folded_t = (args.fold and not args.xq and w.dtype == "bf16" and
                 all(T >= sp.n and sp.n % 256 == 0 and all(b % 64 == 0 for b in sp.bsz_R)
                     for sp in w.layers))
-    # With the weight kept beside its transpose (the default for dense weights)
-    # the backward reads WtT K-contiguous: the NT kernel as well.
-    nt_bwd = folded_t or (not args.xq and not args.fold and w.dtype == "bf16")
+    # With the weight kept beside its transpose (dense or INT8; the default
+    # here) the backward reads it K-contiguous: the NT kernel as well.
+    nt_bwd = folded_t or (not args.fold and w.dtype == "bf16")
     stage_kernel = {"w0_fwd": "w0_gemm_nt_lds", "w0_bwd": "w0_gemm_nt_lds" if nt_bwd else "w0_gemm_nn_lds"}
     if args.xq:
         stage_kernel = {k: v.replace("w0_", "w0q_") for k, v in stage_kernel.items()}
@@ -431,7 +431,7 @@ def main() -> int:
             "passes": "build+forward+backward" if w.backward else "build+forward",
             "saved_activation": ("none (POET-Xmem: recomputed)" if xmem else "Wa (POET-Xfast)")
             + "; layer input kept as U = X Pi_P^T",
-            "frozen_weight": "int8, one fp32 scale per row (POET-XQ)" if args.xq
+            "frozen_weight": "int8, one fp32 scale per row (POET-XQ), kept with its transpose" if args.xq
             else f"{w.dtype}, kept with its transpose",
             "orthogonal_map": "exact Cayley (Newton-Schulz inverse, closed-form gradient)" if args.exact
             else f"Cayley-Neumann, k = {w.k}" + (", Paterson-Stockmeyer build" if args.series == "ps"

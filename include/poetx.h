@@ -70,11 +70,16 @@ typedef enum { POETX_FP32 = 0, POETX_BF16 = 1 } poetx_dtype;
  *     WtT [n, m] in the plan dtype at byte offset ceil(m n elsize / 256) * 256
  *     (poetx_permute_weight writes both). The frozen weight is kept twice so that
  *     the backward's product G_V = G_Wa Wt reads it K-contiguous, like the
- *     forward's V Wt^T; results are identical to POETX_WEIGHT_DENSE. */
+ *     forward's V Wt^T; results are identical to POETX_WEIGHT_DENSE.
+ *   POETX_WEIGHT_INT8_ROWS_T: POETX_WEIGHT_INT8_ROWS followed by the transpose
+ *     of q, qT [n, m] int8, at byte offset ceil((ceil(m n / 256) * 256 + 4 m) /
+ *     256) * 256 (poetx_quantize_weight writes all three), for the same reason;
+ *     results are identical to POETX_WEIGHT_INT8_ROWS. */
 typedef enum {
   POETX_WEIGHT_DENSE = 0,
   POETX_WEIGHT_INT8_ROWS = 1,
-  POETX_WEIGHT_DENSE_T = 2
+  POETX_WEIGHT_DENSE_T = 2,
+  POETX_WEIGHT_INT8_ROWS_T = 3
 } poetx_weight;
 
 /* Orthogonal map of each block.

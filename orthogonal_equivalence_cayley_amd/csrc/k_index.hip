@@ -389,7 +389,10 @@ hipError_t launch_transpose(const void* in, void* out, int R, int C, int elsize,
   if (R <= 0 || C <= 0) return hipSuccess;
   const long long tiles = (long long)((R + 31) / 32) * ((C + 31) / 32);
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
-  if (elsize == 2)
+  if (elsize == 1)
+    hipLaunchKernelGGL(transpose_kernel<uint8_t>, dim3((unsigned)tiles), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(in), static_cast<uint8_t*>(out), R, C);
+  else if (elsize == 2)
     hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3((unsigned)tiles), dim3(256), 0, s,
                        static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, C);
   else

@@ -37,8 +37,12 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
-// INT8 weight: int8 [m, n] rows of Wt, then (256-byte aligned) the fp32 row scales
-bool wq(const poetx_plan* pl) { return pl->weight == POETX_WEIGHT_INT8_ROWS; }
+// INT8 weight: int8 [m, n] rows of Wt, then (256-byte aligned) the fp32 row
+// scales, then for POETX_WEIGHT_INT8_ROWS_T (256-byte aligned) qT [n, m]
+bool wq(const poetx_plan* pl) {
+  return pl->weight == POETX_WEIGHT_INT8_ROWS || pl->weight == POETX_WEIGHT_INT8_ROWS_T;
+}
+bool wqpair(const poetx_plan* pl) { return pl->weight == POETX_WEIGHT_INT8_ROWS_T; }
 // dense weight kept with its transpose: WtT [n, m] after Wt, 256-byte aligned
 bool wpair(const poetx_plan* pl) { return pl->weight == POETX_WEIGHT_DENSE_T; }
 size_t wtt_off(const poetx_plan* pl) {
@@ -49,6 +53,10 @@ const void* wtt(const poetx_plan* pl, const void* Wt) { return static_cast<const
 size_t qscale_off(const poetx_plan* pl) {
   return ((size_t)pl->m * pl->n + kAlign - 1) / kAlign * kAlign;
 }
+size_t qt_off(const poetx_plan* pl) {
+  return (qscale_off(pl) + 4 * (size_t)pl->m + kAlign - 1) / kAlign * kAlign;
+}
+const void* qt(const poetx_plan* pl, const void* Wt) { return static_cast<const char*>(Wt) + qt_off(pl); }
 const float* qscale(const poetx_plan* pl, const void* Wt) {
   return reinterpret_cast<const float*>(static_cast<const char*>(Wt) + qscale_off(pl));
 }
@@ -779,8 +787,10 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
     const Op a = foldb ? Op{w.GZ, pl->m, 1} : Op{w.GWa, pl->m, 1};
     // B(j, i) = (D_R Wt)[i][j]: WfT[j][i] (K-contiguous) or Wf[i][j]; unfolded
     // B(j, i) = Wt[i][j], read K-contiguous from the kept transpose WtT[j][i]
+    // (qT[j][i] for an INT8 weight)
     const Op b = foldt ? Op{w.Wf, pl->m, 1} : foldb ? Op{w.Wf, 1, pl->n}
-                 : wpair(pl) ? Op{wtt(pl, Wt), pl->m, 1} : Op{Wt, 1, pl->n};
+                 : wpair(pl) ? Op{wtt(pl, Wt), pl->m, 1}
+                 : wqpair(pl) ? Op{qt(pl, Wt), pl->m, 1} : Op{Wt, 1, pl->n};
     if ((st = gemm(pl, poetx::GEMM_W0, a, b, w.GV, pl->n, (int)T, pl->n, pl->m, 1, 0, 0, 0, 1, 0, false,
                    s, nullptr, wq(pl))) != POETX_OK)
       return st;
@@ -1090,7 +1100,7 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
   if (!d->bsz_R || !d->bsz_P) return POETX_ERR_INVALID_ARG;
   if (d->k < 0 || d->k > 32) return POETX_ERR_SHAPE;
   if (d->weight != POETX_WEIGHT_DENSE && d->weight != POETX_WEIGHT_INT8_ROWS &&
-      d->weight != POETX_WEIGHT_DENSE_T)
+      d->weight != POETX_WEIGHT_DENSE_T && d->weight != POETX_WEIGHT_INT8_ROWS_T)
     return POETX_ERR_INVALID_ARG;
   if (d->cayley != POETX_CAYLEY_NEUMANN && d->cayley != POETX_CAYLEY_EXACT)
     return POETX_ERR_INVALID_ARG;
@@ -1116,7 +1126,7 @@ poetx_status poetx_plan_create(const poetx_desc* d, poetx_plan** out) {
   }
   // INT8 weight: bf16 activations and whole 256 x 256 tiles of the weight
   // (the quantiser also stages one bf16 row of W0 in 64 KiB of LDS)
-  if (d->weight == POETX_WEIGHT_INT8_ROWS &&
+  if ((d->weight == POETX_WEIGHT_INT8_ROWS || d->weight == POETX_WEIGHT_INT8_ROWS_T) &&
       (d->dtype != POETX_BF16 || d->m % 256 || d->n % 256 || d->n > 32768))
     return POETX_ERR_UNSUPPORTED;
   poetx_plan* pl = new (std::nothrow) poetx_plan;
@@ -1197,6 +1207,7 @@ poetx_status poetx_permute_weight(const poetx_plan* pl, const void* W0, const in
 
 size_t poetx_weight_bytes(const poetx_plan* pl) {
   if (!pl) return 0;
+  if (wqpair(pl)) return qt_off(pl) + (size_t)pl->m * pl->n;
   if (wq(pl)) return qscale_off(pl) + 4 * (size_t)pl->m;
   if (wpair(pl)) return wtt_off(pl) + (size_t)pl->m * pl->n * elsize(pl);
   return (size_t)pl->m * pl->n * elsize(pl);
@@ -1212,6 +1223,9 @@ poetx_status poetx_quantize_weight(const poetx_plan* pl, const void* W0, const i
   HIP_TRY(poetx::launch_quantize_rows(W0, pi_R, pi_P, static_cast<int8_t*>(Wq),
                                       const_cast<float*>(qscale(pl, Wq)), pl->m, pl->n,
                                       (hipStream_t)stream));
+  if (wqpair(pl))
+    HIP_TRY(poetx::launch_transpose(Wq, const_cast<void*>(qt(pl, Wq)), pl->m, pl->n, 1,
+                                    (hipStream_t)stream));
   return POETX_OK;
 }
 

@@ -48,9 +48,9 @@ class PoetxLayer:
                  series: str = "chain"):
         if dtype not in _TORCH_DTYPE:
             raise ValueError(f"dtype must be one of {sorted(_TORCH_DTYPE)}")
-        if weight not in ("dense", "dense_t", "int8"):
-            raise ValueError("weight must be 'dense', 'dense_t' (kept with its transpose) or "
-                             "'int8' (POET-XQ)")
+        if weight not in ("dense", "dense_t", "int8", "int8_t"):
+            raise ValueError("weight must be 'dense', 'dense_t' (kept with its transpose), "
+                             "'int8' (POET-XQ) or 'int8_t' (INT8 kept with its transpose)")
         if cayley not in ("neumann", "exact"):
             raise ValueError("cayley must be 'neumann' (truncated series) or 'exact'")
         if fold not in ("none", "weight"):
@@ -66,7 +66,7 @@ class PoetxLayer:
         self.tdtype = _TORCH_DTYPE[dtype]
         self.plan = _px.Plan(m, n, bsz_R, bsz_P, k, _PX_DTYPE[dtype],
                              {"dense": _px.WEIGHT_DENSE, "dense_t": _px.WEIGHT_DENSE_T,
-                              "int8": _px.WEIGHT_INT8_ROWS}[weight],
+                              "int8": _px.WEIGHT_INT8_ROWS, "int8_t": _px.WEIGHT_INT8_ROWS_T}[weight],
                              _px.CAYLEY_EXACT if cayley == "exact" else _px.CAYLEY_NEUMANN,
                              _px.FOLD_WEIGHT if fold == "weight" else _px.FOLD_NONE,
                              _px.INDEX_FUSED if index == "fused" else _px.INDEX_SEPARATE,
@@ -101,7 +101,7 @@ class PoetxLayer:
         assert W0.shape == (self.m, self.n) and W0.dtype == self.tdtype and W0.is_contiguous()
         self.pi_R = pi_R.to(device=self.device, dtype=torch.int32).contiguous()
         self.pi_P = pi_P.to(device=self.device, dtype=torch.int32).contiguous()
-        if self.weight == "int8":
+        if self.weight in ("int8", "int8_t"):
             self.Wt = torch.empty(self.plan.weight_bytes(), dtype=torch.uint8, device=self.device)
             self.plan.quantize_weight(W0, self.pi_R, self.pi_P, self.Wt)
         elif self.weight == "dense_t":
@@ -115,7 +115,7 @@ class PoetxLayer:
 
     def int8_weight(self):
         """(q [m, n] int8, s [m] fp32) views of an INT8 Wt (rows in permuted order)."""
-        assert self.weight == "int8"
+        assert self.weight in ("int8", "int8_t")
         mn = self.m * self.n
         off = (mn + 255) // 256 * 256
         q = self.Wt[:mn].view(torch.int8).view(self.m, self.n)

@@ -36,6 +36,7 @@ WS_MERGE = 4
 WEIGHT_DENSE = 0
 WEIGHT_INT8_ROWS = 1
 WEIGHT_DENSE_T = 2
+WEIGHT_INT8_ROWS_T = 3
 
 CAYLEY_NEUMANN = 0
 CAYLEY_EXACT = 1

@@ -47,7 +47,7 @@ void* mis(uintptr_t i) { return reinterpret_cast<void*>(0x7f0000000000ull + 0x10
 void plan_options() {
   // every combination of options on a bf16 plan of 256-wide blocks, plus an
   // fp32 plan with ragged blocks
-  for (int weight = 0; weight < 3; ++weight)
+  for (int weight = 0; weight < 4; ++weight)
     for (int cayley = 0; cayley < 2; ++cayley)
       for (int fold = 0; fold < 2; ++fold)
         for (int index = 0; index < 2; ++index)

@@ -249,8 +249,26 @@ def test_dense_weight_with_transpose_bytes():
     off = (37 * 53 * 4 + 255) // 256 * 256
     assert q.weight_bytes() == off + 37 * 53 * 4
     with pytest.raises(px.PoetxError) as e:
-        px.Plan(37, 53, (37,), (53,), 2, f32, 3)
+        px.Plan(37, 53, (37,), (53,), 2, f32, 4)
     assert e.value.status == px.POETX_ERR_INVALID_ARG
+
+
+def test_int8_weight_with_transpose_bytes():
+    """POETX_WEIGHT_INT8_ROWS_T: q [m, n], the row scales, then qT [n, m], each
+    at a 256-byte boundary; the same shape rules as POETX_WEIGHT_INT8_ROWS."""
+    bf = px.POETX_BF16
+    p = px.Plan(512, 768, (256, 256), (256,) * 3, 4, bf, px.WEIGHT_INT8_ROWS_T)
+    mn = 512 * 768
+    off = ((mn + 255) // 256 * 256 + 4 * 512 + 255) // 256 * 256
+    assert p.weight_bytes() == off + mn
+    for args in [(512, 256, (256, 256), (256,), 4, px.POETX_FP32),     # fp32 activations
+                 (256, 320, (256,), (320,), 4, bf)]:                    # n not a multiple of 256
+        with pytest.raises(px.PoetxError) as e:
+            px.Plan(*args, px.WEIGHT_INT8_ROWS_T)
+        assert e.value.status == px.POETX_ERR_UNSUPPORTED
+    A = 1 << 20
+    assert px.LIB.poetx_permute_weight(p.handle, A, A + 16, A + 32, A + 48, None) == \
+        px.POETX_ERR_UNSUPPORTED
 
 
 def test_forward_noalloc_host_checks():

@@ -506,6 +506,33 @@ def test_layer_int8_weight(case, save):
     _compare(got, ref, ["Y", "G_X", "g_theta_R", "g_theta_P"], TOL_BF16, "int8")
 
 
+@pytest.mark.parametrize("save", [True, False])
+def test_int8_weight_kept_with_transpose(save):
+    """POETX_WEIGHT_INT8_ROWS_T: quantize_weight also writes qT (the exact
+    transpose of q), and every output equals the INT8_ROWS plan's bit for bit
+    (the backward's weight product reads qT K-contiguous, same MFMA order)."""
+    import torch
+    inp = _int8_inputs(512, 768, (256, 256), (256,) * 3, T=333, seed=12)
+    outs = []
+    for weight in ("int8", "int8_t"):
+        L = make_layer(inp, 4, "bf16", weight=weight)
+        L.build()
+        X, G = to_dev(inp.X, "bf16"), to_dev(inp.G_Y, "bf16")
+        Y = L.forward(X, save=save)
+        G_X, gR, gP = L.backward(X, G)
+        torch.cuda.synchronize()
+        outs.append([Y, G_X, gR, gP])
+        if weight == "int8_t":
+            q, _ = L.int8_weight()
+            mn = 512 * 768
+            off = ((mn + 255) // 256 * 256 + 4 * 512 + 255) // 256 * 256
+            assert L.plan.weight_bytes() == off + mn
+            qT = L.Wt[off:off + mn].view(torch.int8).view(768, 512)
+            assert torch.equal(qT.cpu(), q.cpu().t().contiguous())
+    for a, b in zip(*outs):
+        assert torch.equal(_bits(a), _bits(b))
+
+
 def test_merge_int8_weight():
     import torch
     inp = _int8_inputs(512, 256, (256, 256), (256,), T=1, seed=3)
