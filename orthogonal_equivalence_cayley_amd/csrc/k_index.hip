@@ -16,8 +16,9 @@ constexpr int kThreads = 256;
 constexpr int kLdsBudget = 64 * 1024;   // bytes of LDS for staged rows per workgroup
 constexpr int kMaxRows = 4;             // rows per workgroup: small tiles keep the grid full
 // Second-phase items of the interleaved gather: (R / G) (dim / VEC) =
-// R dim sizeof(E)^2 / 128 <= kLdsBudget sizeof(E) / 128 <= kLdsBudget / 32
-// (G = 8 / sizeof(E), VEC = 16 / sizeof(E), sizeof(E) <= 4).
+// R dim sizeof(E)^2 / (16 sizeof(W)) <= kLdsBudget sizeof(E) / (16 sizeof(W))
+// <= kLdsBudget / 32 (G = sizeof(W) / sizeof(E), VEC = 16 / sizeof(E),
+// sizeof(E) <= 4 with 8-byte words, sizeof(E) = 2 with 4-byte words).
 static_assert(kLdsBudget / 32 <= 8 * 256, "gather index prefetch covers every item");
 
 template <typename E, int VEC>
@@ -112,16 +113,19 @@ __global__ __launch_bounds__(kThreads) void scatter_cols_kernel(
   }
 }
 
-// Interleaved variants: G = 8 / sizeof(E) rows share one 8-byte LDS word per
-// column (word c of row group g holds element c of rows 4g..4g+3 for bf16), so
-// one random LDS access moves the element of G rows. Rows are read and written
-// with coalesced 16-byte accesses; the interleave happens in registers.
-template <typename E>
+// Interleaved variants: G = sizeof(W) / sizeof(E) rows share one LDS word W per
+// column (with 8-byte words, word c of row group g holds element c of rows
+// 4g..4g+3 for bf16), so one random LDS access moves the element of G rows.
+// Rows too wide for 4 staged rows take 4-byte words (2 bf16 rows per word).
+// Rows are read and written with coalesced 16-byte accesses; the interleave
+// happens in registers.
+template <typename E, typename W = uint64_t>
 struct Inter {
-  static constexpr int G = 8 / sizeof(E);    // rows per word
-  static constexpr int VEC = 16 / sizeof(E); // elements per 16-byte chunk
+  static constexpr int G = sizeof(W) / sizeof(E);   // rows per word
+  static constexpr int VEC = 16 / sizeof(E);        // elements per 16-byte chunk
   static constexpr int BITS = 8 * sizeof(E);
-  __device__ __forceinline__ static uint64_t elem(const uint4& v, int e) {
+  static_assert(G >= 2, "at least two rows per word");
+  __device__ __forceinline__ static W elem(const uint4& v, int e) {
     const uint32_t w = (e * BITS / 32) == 0 ? v.x : (e * BITS / 32) == 1 ? v.y : (e * BITS / 32) == 2 ? v.z : v.w;
     if (BITS == 32) return w;
     return (e & 1) ? (w >> 16) : (w & 0xffffu);
@@ -132,14 +136,14 @@ struct Inter {
 // A thread's items of the second phase are the same in every iteration, so
 // their indices are loaded once, before the first rows: the random LDS reads
 // after the barrier then wait on nothing but LDS (ngrp * cpr <= NI * kThreads).
-template <typename E, int NI>
+template <typename E, typename W, int NI>
 __global__ __launch_bounds__(kThreads) void gather_cols_inter(
     const E* __restrict__ in, long long in_ld, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ idx, E* __restrict__ out, long long T, int dim, int R) {
-  using I = Inter<E>;
+  using I = Inter<E, W>;
   constexpr int G = I::G, VEC = I::VEC, BITS = I::BITS;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint64_t* lds = reinterpret_cast<uint64_t*>(smem);   // [R / G][dim]
+  W* lds = reinterpret_cast<W*>(smem);   // [R / G][dim]
   const int cpr = dim / VEC;
   const int ngrp = R / G;
   int ixs[NI][VEC];
@@ -162,10 +166,10 @@ __global__ __launch_bounds__(kThreads) void gather_cols_inter(
         const long long src_row = rows ? (long long)rows[t0 + rr] : (t0 + rr);
         v[r] = reinterpret_cast<const uint4*>(in + src_row * in_ld)[q];
       }
-      uint64_t* dst = lds + (long long)g * dim + q * VEC;
+      W* dst = lds + (long long)g * dim + q * VEC;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        uint64_t wv = 0;
+        W wv = 0;
 #pragma unroll
         for (int r = 0; r < G; ++r) wv |= I::elem(v[r], e) << (BITS * r);
         dst[e] = wv;
@@ -177,8 +181,8 @@ __global__ __launch_bounds__(kThreads) void gather_cols_inter(
       const int c = threadIdx.x + j * kThreads;
       if (c >= ngrp * cpr) break;
       const int g = c / cpr, q = c - g * cpr;
-      const uint64_t* src = lds + (long long)g * dim;
-      uint64_t wv[VEC];
+      const W* src = lds + (long long)g * dim;
+      W wv[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) wv[e] = src[ixs[j][e]];
 #pragma unroll
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void gather_cols_inter(
         uint32_t o[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const uint32_t x = (uint32_t)((wv[e] >> (BITS * r)) & (BITS == 32 ? 0xffffffffull : 0xffffull));
+          const uint32_t x = (uint32_t)((wv[e] >> (BITS * r)) & (BITS == 32 ? 0xffffffffu : 0xffffu));
           if (BITS == 32) o[e] = x;
           else o[e >> 1] |= x << (16 * (e & 1));
         }
@@ -201,14 +205,14 @@ __global__ __launch_bounds__(kThreads) void gather_cols_inter(
 
 // out[t][idx[i]] = in[t][i]: rows interleaved into LDS at their destination
 // columns, then written out row by row.
-template <typename E>
+template <typename E, typename W>
 __global__ __launch_bounds__(kThreads) void scatter_cols_inter(
     const E* __restrict__ in, const int32_t* __restrict__ idx, E* __restrict__ out, long long T,
     int dim, int R) {
-  using I = Inter<E>;
+  using I = Inter<E, W>;
   constexpr int G = I::G, VEC = I::VEC, BITS = I::BITS;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint64_t* lds = reinterpret_cast<uint64_t*>(smem);
+  W* lds = reinterpret_cast<W*>(smem);
   const int cpr = dim / VEC;
   const int ngrp = R / G;
   for (long long t0 = (long long)blockIdx.x * R; t0 < T; t0 += (long long)gridDim.x * R) {
@@ -221,10 +225,10 @@ __global__ __launch_bounds__(kThreads) void scatter_cols_inter(
         const int rr = min(g * G + r, nr - 1);
         v[r] = reinterpret_cast<const uint4*>(in + (t0 + rr) * dim)[q];
       }
-      uint64_t* dst = lds + (long long)g * dim;
+      W* dst = lds + (long long)g * dim;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        uint64_t wv = 0;
+        W wv = 0;
 #pragma unroll
         for (int r = 0; r < G; ++r) wv |= I::elem(v[r], e) << (BITS * r);
         dst[idx[q * VEC + e]] = wv;
@@ -233,8 +237,8 @@ __global__ __launch_bounds__(kThreads) void scatter_cols_inter(
     __syncthreads();
     for (int c = threadIdx.x; c < ngrp * cpr; c += kThreads) {
       const int g = c / cpr, q = c - g * cpr;
-      const uint64_t* src = lds + (long long)g * dim + q * VEC;
-      uint64_t wv[VEC];
+      const W* src = lds + (long long)g * dim + q * VEC;
+      W wv[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) wv[e] = src[e];
 #pragma unroll
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void scatter_cols_inter(
         uint32_t o[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const uint32_t x = (uint32_t)((wv[e] >> (BITS * r)) & (BITS == 32 ? 0xffffffffull : 0xffffull));
+          const uint32_t x = (uint32_t)((wv[e] >> (BITS * r)) & (BITS == 32 ? 0xffffffffu : 0xffffu));
           if (BITS == 32) o[e] = x;
           else o[e >> 1] |= x << (16 * (e & 1));
         }
@@ -297,6 +301,39 @@ inline int grid_for(long long units) {
   return (int)(units < cap ? (units < 1 ? 1 : units) : cap);
 }
 
+template <typename E, typename W>
+hipError_t gather_inter(const void* in, long long in_ld, const int32_t* rows, const int32_t* idx,
+                        void* out, long long T, int dim, int R, hipStream_t s) {
+  using I = Inter<E, W>;
+  const size_t lds = (size_t)R * dim * sizeof(E);
+  const long long items = (long long)(R / I::G) * (dim / I::VEC);   // second-phase items per workgroup
+  const dim3 grid(grid_for((T + R - 1) / R)), block(kThreads);
+  if (items <= kThreads)
+    hipLaunchKernelGGL((gather_cols_inter<E, W, 1>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
+                       (E*)out, T, dim, R);
+  else if (items <= 2 * kThreads)
+    hipLaunchKernelGGL((gather_cols_inter<E, W, 2>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
+                       (E*)out, T, dim, R);
+  else if (items <= 4 * kThreads)
+    hipLaunchKernelGGL((gather_cols_inter<E, W, 4>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
+                       (E*)out, T, dim, R);
+  else if (items <= 8 * kThreads)
+    hipLaunchKernelGGL((gather_cols_inter<E, W, 8>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
+                       (E*)out, T, dim, R);
+  else
+    return hipErrorInvalidValue;   // not reached: R dim sizeof(E) <= kLdsBudget bounds the items
+  return hipGetLastError();
+}
+
+template <typename E, typename W>
+hipError_t scatter_inter(const void* in, const int32_t* idx, void* out, long long T, int dim, int R,
+                         hipStream_t s) {
+  const size_t lds = (size_t)R * dim * sizeof(E);
+  hipLaunchKernelGGL((scatter_cols_inter<E, W>), dim3(grid_for((T + R - 1) / R)), dim3(kThreads), lds, s,
+                     (const E*)in, idx, (E*)out, T, dim, R);
+  return hipGetLastError();
+}
+
 template <typename E>
 hipError_t gather_typed(const void* in, long long in_ld, const int32_t* rows, const int32_t* idx,
                         void* out, long long T, int dim, hipStream_t s) {
@@ -313,25 +350,10 @@ hipError_t gather_typed(const void* in, long long in_ld, const int32_t* rows, co
   const bool vec = (dim % VEC == 0) && (in_ld % VEC == 0) &&
                    ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
   constexpr int G = 8 / sizeof(E);
-  if (vec && R >= G) {
-    R = R / G * G;
-    const size_t lds = (size_t)R * row_bytes;
-    const long long items = (long long)(R / G) * (dim / VEC);   // second-phase items per workgroup
-    const dim3 grid(grid_for((T + R - 1) / R)), block(kThreads);
-    if (items <= kThreads)
-      hipLaunchKernelGGL((gather_cols_inter<E, 1>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
-                         (E*)out, T, dim, R);
-    else if (items <= 2 * kThreads)
-      hipLaunchKernelGGL((gather_cols_inter<E, 2>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
-                         (E*)out, T, dim, R);
-    else if (items <= 4 * kThreads)
-      hipLaunchKernelGGL((gather_cols_inter<E, 4>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
-                         (E*)out, T, dim, R);
-    else   // R <= kMaxRows and R dim sizeof(E) <= kLdsBudget bound items by 8 kThreads
-      hipLaunchKernelGGL((gather_cols_inter<E, 8>), grid, block, lds, s, (const E*)in, in_ld, rows, idx,
-                         (E*)out, T, dim, R);
-    return hipGetLastError();
-  }
+  if (vec && R >= G)
+    return gather_inter<E, uint64_t>(in, in_ld, rows, idx, out, T, dim, R / G * G, s);
+  if constexpr (sizeof(E) == 2)   // rows too wide for 4 staged rows: 2 rows per 4-byte word
+    if (vec && R >= 2) return gather_inter<E, uint32_t>(in, in_ld, rows, idx, out, T, dim, R / 2 * 2, s);
   const size_t lds = (size_t)R * row_bytes;
   const int grid = grid_for((T + R - 1) / R);
   if (vec)
@@ -358,13 +380,9 @@ hipError_t scatter_typed(const void* in, const int32_t* idx, void* out, long lon
   if (R > kMaxRows) R = kMaxRows;
   const bool vec = (dim % VEC == 0) && ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
   constexpr int G = 8 / sizeof(E);
-  if (vec && R >= G) {
-    R = R / G * G;
-    const size_t lds = (size_t)R * row_bytes;
-    hipLaunchKernelGGL((scatter_cols_inter<E>), dim3(grid_for((T + R - 1) / R)), dim3(kThreads),
-                       lds, s, (const E*)in, idx, (E*)out, T, dim, R);
-    return hipGetLastError();
-  }
+  if (vec && R >= G) return scatter_inter<E, uint64_t>(in, idx, out, T, dim, R / G * G, s);
+  if constexpr (sizeof(E) == 2)   // rows too wide for 4 staged rows: 2 rows per 4-byte word
+    if (vec && R >= 2) return scatter_inter<E, uint32_t>(in, idx, out, T, dim, R / 2 * 2, s);
   const size_t lds = (size_t)R * row_bytes;
   const int grid = grid_for((T + R - 1) / R);
   if (vec)

@@ -43,7 +43,7 @@ def _bits(t):
 # ---------------------------------------------------------------- index paths
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("dim", [16, 37, 2048, 5632, 11008, 40000])
+@pytest.mark.parametrize("dim", [16, 37, 2048, 5632, 9000, 11008, 16384, 40000])
 @pytest.mark.parametrize("T", [1, 9, 130])
 def test_gather_scatter_bitexact(dtype, dim, T):
     import torch
@@ -64,7 +64,8 @@ def test_gather_scatter_bitexact(dtype, dim, T):
     assert torch.equal(_bits(back), _bits(Xc))
 
 
-@pytest.mark.parametrize("dtype,m,n", [("bf16", 2048, 2048), ("bf16", 5632, 2048), ("f32", 37, 53)])
+@pytest.mark.parametrize("dtype,m,n", [("bf16", 2048, 2048), ("bf16", 5632, 2048), ("bf16", 80, 11008),
+                                        ("f32", 37, 53)])
 def test_permute_weight_bitexact(dtype, m, n):
     import torch
     log(f"permute_weight {dtype} {m}x{n}")
