@@ -131,7 +131,8 @@ def kernel_source_digest(path: str) -> str:
 # what they read for a plain copy of known size. The figure is used only while
 # the kernel's source is the one the counters were taken on.
 TRAFFIC_SOURCES = {"w0_gemm_nn_lds": "orthogonal_equivalence_cayley_amd/csrc/k_gemm_lds.hip",
-                   "w0_gemm_nt_lds": "orthogonal_equivalence_cayley_amd/csrc/k_gemm_lds.hip"}
+                   "w0_gemm_nt_lds": "orthogonal_equivalence_cayley_amd/csrc/k_gemm_lds.hip",
+                   "w0_gemm_nt_pipe": "orthogonal_equivalence_cayley_amd/csrc/k_gemm_w0.hip"}
 
 
 def load_traffic(kernel: str, workload: str, fold: bool = False):
@@ -369,7 +370,13 @@ def main() -> int:
     # With the weight kept beside its transpose (dense or INT8; the default
     # here) the backward reads it K-contiguous: the NT kernel as well.
     nt_bwd = folded_t or (not args.fold and w.dtype == "bf16")
-    stage_kernel = {"w0_fwd": "w0_gemm_nt_lds", "w0_bwd": "w0_gemm_nt_lds" if nt_bwd else "w0_gemm_nn_lds"}
+    # dense NT products on whole 256 x 256 tiles with at least one tile per CU
+    # run the dedicated frozen-weight kernel (k_gemm_w0.hip)
+    pipe = (w.dtype == "bf16" and not args.xq and T % 256 == 0 and
+            all(sp.m % 256 == 0 and sp.n % 256 == 0 and (T // 256) * (min(sp.m, sp.n) // 256) >= 256
+                for sp in w.layers))
+    nt_name = "w0_gemm_nt_pipe" if pipe else "w0_gemm_nt_lds"
+    stage_kernel = {"w0_fwd": nt_name, "w0_bwd": nt_name if nt_bwd else "w0_gemm_nn_lds"}
     if args.xq:
         stage_kernel = {k: v.replace("w0_", "w0q_") for k, v in stage_kernel.items()}
     per_kernel = {}

@@ -265,6 +265,7 @@ hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s) {
   const bool big = big_tiles >= 256 && p.role != GEMM_DQ;
   // whole-tile shapes take the pipelined direct-to-LDS kernels; the rest (K not a
   // multiple of 64, partial tiles of row-contiguous operands) the kernels here
+  if (big && w0_pipe_supported(p)) return launch_w0_pipe(p, s);
   if (gemm_lds_supported(p, big ? 256 : 128, big ? 256 : 128)) return launch_gemm_lds(p, big, s);
   // an int8 operand exists only on the pipelined kernels; a column scale is
   // applied by a separate pass here (one more rounding of the bf16 output)

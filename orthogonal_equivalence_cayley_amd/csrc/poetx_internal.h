@@ -158,6 +158,9 @@ hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
 // big = 256 x 256 tiles, else 128 x 128.
 bool gemm_lds_supported(const GemmBf16& p, int bm, int bn);
 hipError_t launch_gemm_lds(const GemmBf16& p, int big, hipStream_t s);
+// Frozen-weight NT product on whole 256 x 256 tiles (k_gemm_w0.hip).
+bool w0_pipe_supported(const GemmBf16& p);
+hipError_t launch_w0_pipe(const GemmBf16& p, hipStream_t s);
 // Block products with b = 256 or 512 (N = K, GEMM_BLOCK, bf16 output, optional
 // column scale): B in registers, A tiles streamed through LDS
 // (k_block_regb.hip).
