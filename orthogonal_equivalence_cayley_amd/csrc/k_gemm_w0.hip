@@ -18,9 +18,11 @@
 //    permutes the chunk bits below a row's base, so each read is one XOR plus
 //    an immediate offset;
 //  * the schedule: each 16-deep step issues the next step's six fragment reads
-//    one per MFMA; the barrier of a stage sits after half of its last step's
-//    MFMAs, so the matrix cores have work while waves wait there, and the next
-//    stage's loads and first fragment reads are issued between the other half.
+//    one per MFMA; the barrier of a stage sits after the first two MFMAs of its
+//    last step, so the matrix cores have work while waves wait there, and the
+//    next stage's loads and first fragment reads are spread over the other six
+//    (two, zero or four MFMAs before the barrier measured within 3 % of each
+//    other; two the fastest on the step's shapes).
 //
 // Requirements (w0_pipe_supported): M, N multiples of 256, K of 64, 16-byte
 // rows, each operand below 2 GiB (32-bit offsets), one group, no split.
@@ -35,6 +37,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kTile = 256;       // output tile rows and columns
 constexpr int kThr = 512;        // 8 waves
 constexpr int kGroupRows = 4;    // tile-rows per group of the XCD-aware order
+constexpr int kPre = 2;          // MFMAs of a stage's last step issued before its barrier
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -242,13 +245,12 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           __builtin_amdgcn_sched_barrier(0);
         } else {
-          // half of the last step's MFMAs are issued before the barrier, so the
-          // matrix core has work while the wave waits there
+          // the first kPre of the last step's MFMAs are issued before the
+          // barrier, so the matrix core has work while the wave waits there
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+          for (int q = 0; q < kPre; ++q)
+            acc[q / 2][q % 2] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cb][q % 2], af[cb][q / 2], acc[q / 2][q % 2], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           wait_for(ST - 2);
           lds_sync();
@@ -261,15 +263,15 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) bf[nb][j] = Op::frag(na, fb, j, 0);
 #pragma unroll
-          for (int i = 2; i < 4; ++i)
+          for (int q = kPre; q < 8; ++q)
+            acc[q / 2][q % 2] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cb][q % 2], af[cb][q / 2], acc[q / 2][q % 2], 0, 0, 0);
+          // the stage's loads and the next fragments spread over those MFMAs
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
+          for (int g = 0; g < 8 - kPre; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, LOADS / 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, (LOADS + 7 - kPre) / (8 - kPre), 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, (6 + 7 - kPre) / (8 - kPre), 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
