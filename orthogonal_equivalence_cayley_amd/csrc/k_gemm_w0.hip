@@ -281,6 +281,9 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
     }
     store_tile(acc, cm0, cn0);
   }
+  // the last iterations loaded the final stage again into buffers nobody reads:
+  // let those direct-to-LDS writes land before the workgroup's LDS is released
+  vm_wait<0>();
 }
 
 constexpr int kKB = 64;   // stage depth
