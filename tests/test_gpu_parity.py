@@ -170,6 +170,9 @@ def test_layer_fp32_ragged(case):
     dict(m=1024, n=1024, bR=(512, 512), bP=(512, 512), T=130, k=4),
     dict(m=512, n=1536, bR=(512,), bP=(512,) * 3, T=64, k=5),
     dict(m=256, n=256, bR=(256,), bP=(256,), T=1, k=4),
+    # frozen-weight product on whole 256 x 256 tiles with one 64-deep stage
+    # (K = n = 64) and 1088 tiles on 256 workgroups
+    dict(m=4352, n=64, bR=(256,) * 17, bP=(64,), T=16384, k=2),
     dict(m=48, n=32, bR=(16, 32), bP=(32,), T=5, k=0),
     # split chains over blocks that are multiples of 32 but not of 64, alone and
     # mixed with other sizes in one launch
