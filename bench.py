@@ -248,6 +248,8 @@ def main() -> int:
                     help="POET-Xmem: keep no Wa; the backward recomputes it from X")
     ap.add_argument("--series", choices=("chain", "ps"), default="chain",
                     help="build: power chain (default) or Paterson-Stockmeyer")
+    ap.add_argument("--index", choices=("separate", "fused"), default="separate",
+                    help="fused: index maps inside the block products (sides of 256-wide blocks up to 2048)")
     ap.add_argument("--fold", action="store_true",
                     help="variant: fold the P blocks into the weight in the forward (T >= m) and the R "
                          "blocks in the backward (T >= n) instead of applying them to the activations")
@@ -272,7 +274,8 @@ def main() -> int:
     blk = BlockStep([workloads.layer_inputs(w, li, draw_grad=w.backward) for li in range(len(w.layers))],
                     w.k, w.dtype, backward=w.backward, streams=args.streams,
                     weight="int8_t" if args.xq else "dense_t", cayley="exact" if args.exact else "neumann",
-                    fold="weight" if args.fold else "none", series=args.series, xmem=args.xmem)
+                    fold="weight" if args.fold else "none", series=args.series, xmem=args.xmem,
+                    index=args.index)
     layers = blk.layers
     step = blk.step
     torch.cuda.synchronize()
@@ -449,6 +452,8 @@ def main() -> int:
                                "on the activations (input-centric order: gather, P blocks, Wt product, "
                                "R blocks, scatter; the backward in reverse)"),
             "fold": bool(args.fold),
+            "index_maps": ("fused into the block products (sides up to 2048 features)" if args.index == "fused"
+                           else "separate gather and scatter passes"),
             "streams": args.streams,
             "schedule": ("independent layers (q, k, v; gate, up) on two HIP streams, in block order; "
                          "backward in reverse" if blk.two_streams
