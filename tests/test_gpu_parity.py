@@ -90,6 +90,9 @@ def test_permute_weight_bitexact(dtype, m, n):
     ("f32", (7, 33), 6, 0.05),
     ("bf16", (256,) * 3, 4, 0.01),
     ("bf16", (512, 512, 256), 5, 0.005),
+    # split chains with eight waves for blocks between 256 and 512 that are not
+    # 512 (the generic K loop), mixed in one launch
+    ("bf16", (384, 288, 320, 448), 4, 0.01),
     ("bf16", (16, 48), 2, 0.05),
 ])
 def test_build_orth(dtype, bsz, k, std):
@@ -168,6 +171,7 @@ def test_layer_fp32_ragged(case):
     # blocks of 512 only: the block products with two workgroups per block and
     # the split chains with eight waves (ragged and whole row tiles)
     dict(m=1024, n=1024, bR=(512, 512), bP=(512, 512), T=130, k=4),
+    dict(m=768, n=736, bR=(384, 384), bP=(448, 288), T=100, k=3),
     dict(m=512, n=1536, bR=(512,), bP=(512,) * 3, T=64, k=5),
     dict(m=256, n=256, bR=(256,), bP=(256,), T=1, k=4),
     # frozen-weight product on whole 256 x 256 tiles with one 64-deep stage
