@@ -18,14 +18,21 @@
 //    permutes the chunk bits below a row's base, so each read is one XOR plus
 //    an immediate offset;
 //  * the schedule: each 16-deep step issues the next step's six fragment reads
-//    one per MFMA; the barrier of a stage sits after the first two MFMAs of its
-//    last step, so the matrix cores have work while waves wait there, and the
-//    next stage's loads and first fragment reads are spread over the other six
-//    (two, zero or four MFMAs before the barrier measured within 3 % of each
-//    other; two the fastest on the step's shapes).
+//    one per MFMA, and only waves 0-3 load. A CU accepts the 64-lane
+//    direct-to-LDS loads one every 10-16 cycles, so when all eight waves issue
+//    theirs right after a barrier they stall together and the matrix cores
+//    idle (in-kernel timestamps showed the last step of a stage taking about
+//    three times its MFMA time). Here waves 0-3 issue the A tile of stage
+//    s + 2 right after the barrier that frees its buffer (interleaved with
+//    that step's MFMAs) and its B tile during the first step of stage s + 1;
+//    waves 4-7 only read fragments and multiply, and keep the matrix cores
+//    busy while the loads queue: 5-11 % faster on the 16384 x {2048, 5632} x
+//    {2048, 5632} shapes than all waves loading, with the same bits.
 //
 // Requirements (w0_pipe_supported): M, N multiples of 256, K of 64, 16-byte
 // rows, each operand below 2 GiB (32-bit offsets), one group, no split.
+#include <type_traits>
+
 #include "poetx_internal.h"
 
 namespace poetx {
@@ -37,7 +44,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kTile = 256;       // output tile rows and columns
 constexpr int kThr = 512;        // 8 waves
 constexpr int kGroupRows = 4;    // tile-rows per group of the XCD-aware order
-constexpr int kPre = 2;          // MFMAs of a stage's last step issued before its barrier
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -76,21 +82,39 @@ struct OpTile {
   }
 };
 
+// The same tile loaded by the 256 threads of waves 0-3: load i of thread g
+// fills slot i * 256 + g (OpTile's slot -> row, chunk map), so one 32-bit row
+// offset per lane serves every load of an operand.
+template <int KB>
+struct LoadTile {
+  static constexpr int CPR = KB / 8;
+  static constexpr int RPB = 256 / (KB * 2);
+  static constexpr int RPL = 256 / CPR;     // rows per load
+  static constexpr int L = kTile / RPL;     // loads per lane and operand
+  static_assert(RPL % RPB == 0 && (RPL / RPB) % CPR == 0, "chunk index independent of the load");
+  static __device__ __forceinline__ uint32_t lane_offset(int g, long long ld) {
+    const int r = g / CPR, pos = g % CPR;
+    const int c = pos ^ ((r / RPB) % CPR);
+    return (uint32_t)(((long long)r * ld + c * 8) * 2);
+  }
+};
+
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   const __bf16 a = static_cast<__bf16>(lo);
   const __bf16 b = static_cast<__bf16>(hi);
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-template <int KB, int ST>
+template <int KB>
 __global__ __launch_bounds__(kThr) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void w0_gemm_nt_pipe(GemmBf16 p) {
   using Op = OpTile<KB>;
+  using Ld = LoadTile<KB>;
+  constexpr int ST = 2;                        // LDS stages
   constexpr int NK = KB / 16;                  // 16-deep steps per stage
-  constexpr int LOADS = 2 * Op::L;             // loads per thread per stage
   constexpr int STAGE = 2 * Op::BYTES;         // A tile, then B tile
-  static_assert(NK >= 2, "the barrier sits before the last step");
-  static_assert((ST - 1) * LOADS <= 63, "vmcnt range");
+  static_assert(NK >= 2 && NK % 2 == 0, "a first and a last step; fragment buffer parity across stages");
+  static_assert(2 * Ld::L <= 63, "vmcnt range");
   extern __shared__ __align__(16) unsigned char lds[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -122,41 +146,37 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
       const_cast<void*>(p.A), (short)0, (int)((long long)p.M * p.lda * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(p.B), (short)0, (int)((long long)p.N * p.ldb * 2), 0x00020000);
-  const uint32_t va = Op::lane_offset(tid, p.lda), vb = Op::lane_offset(tid, p.ldb);
+  const int g = tid & 255;   // thread index within waves 0-3 (loaders)
+  const uint32_t va = Ld::lane_offset(g, p.lda), vb = Ld::lane_offset(g, p.ldb);
   const int nk = p.K / KB;
   const int total = t_count * nk;
 
-  // the operands of global stage s into LDS buffer `buf` (A at +0, B at
-  // +Op::BYTES); stage s lives in buffer s % ST
-  auto issue = [&](int s, int buf) {
+  // operand `op` (0: A, 1: B) of global stage s (past the end: the last stage
+  // again, into a buffer nobody reads) into LDS buffer s % ST, by waves 0-3; the
+  // wave-uniform part of each offset goes in soffset (whole tiles: every access
+  // is inside the operand)
+  auto issue = [&](int s, int op) {
+    const int buf = s % ST;
+    s = min(s, total - 1);
     const int ti = s / nk, kt = s - ti * nk;
     int m0, n0;
     origin(ti, m0, n0);
-    unsigned char* st = lds + buf * STAGE;
-    const uint32_t ka = (uint32_t)(((long long)m0 * p.lda + (long long)kt * KB) * 2);
-    const uint32_t kb = (uint32_t)(((long long)n0 * p.ldb + (long long)kt * KB) * 2);
-    // the wave-uniform part of each offset goes in soffset (whole tiles: every
-    // access is inside the operand)
+    unsigned char* st = lds + buf * STAGE + op * Op::BYTES + (wave & 3) * 64 * 16;
+    if (op == 0) {
+      const uint32_t ka = (uint32_t)(((long long)m0 * p.lda + (long long)kt * KB) * 2);
 #pragma unroll
-    for (int i = 0; i < Op::L; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(st + (i * kThr + wave * 64) * 16), 16,
-          va, (int)(ka + (uint32_t)(i * Op::RPL * p.lda * 2)), 0, 0);
+      for (int i = 0; i < Ld::L; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(st + i * 256 * 16), 16, va,
+            (int)(ka + (uint32_t)(i * Ld::RPL * p.lda * 2)), 0, 0);
+    } else {
+      const uint32_t kb = (uint32_t)(((long long)n0 * p.ldb + (long long)kt * KB) * 2);
 #pragma unroll
-    for (int i = 0; i < Op::L; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (__attribute__((address_space(3))) void*)(st + Op::BYTES + (i * kThr + wave * 64) * 16), 16,
-          vb, (int)(kb + (uint32_t)(i * Op::RPL * p.ldb * 2)), 0, 0);
-  };
-  // wait until the loads of a stage are done: the loads of the `younger`
-  // stages issued after it may stay in flight (loads complete in order); stores
-  // issued in between only make the wait stricter
-  auto wait_for = [&](int younger) {
-    if (ST >= 5 && younger >= 4) vm_wait<(ST >= 5 ? 4 : 0) * LOADS>();
-    else if (ST >= 4 && younger == 3) vm_wait<(ST >= 4 ? 3 : 0) * LOADS>();
-    else if (ST >= 3 && younger == 2) vm_wait<(ST >= 3 ? 2 : 0) * LOADS>();
-    else if (younger == 1) vm_wait<LOADS>();
-    else vm_wait<0>();
+      for (int i = 0; i < Ld::L; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(st + i * 256 * 16), 16, vb,
+            (int)(kb + (uint32_t)(i * Ld::RPL * p.ldb * 2)), 0, 0);
+    }
   };
 
   const int cm = lane & 31, half = lane >> 5;
@@ -199,95 +219,103 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
     }
   };
 
-  // prologue: ST stages in flight, then the first fragments
+  // The two wave groups run separate copies of the loop (LD: waves 0-3), each
+  // with its own instruction schedule. Stage s + 2 lands in the buffer stage s
+  // leaves: its A tile is issued right after the barrier of stage s's last
+  // step, its B tile during the first step of stage s + 1, and the loaders wait
+  // for both before the barrier of stage s + 1's last step.
+  auto run = [&](auto ld_tag) {
+    constexpr bool LD = decltype(ld_tag)::value;
+    if constexpr (LD) {
+      issue(0, 0);
+      issue(0, 1);
+      issue(1, 0);          // stage 1's A tile; its B tile goes out in stage 0's first step
+      vm_wait<Ld::L>();     // stage 0 landed
+    }
+    lds_sync();
+    bf16x8 af[2][4], bf[2][2];
 #pragma unroll
-  for (int s = 0; s < ST; ++s) issue(min(s, total - 1), s);   // past the end: the last stage again, never read
-  wait_for(ST - 1);
-  lds_sync();
-  bf16x8 af[2][4], bf[2][2];
+    for (int i = 0; i < 4; ++i) af[0][i] = Op::frag(lds, fa, i, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) af[0][i] = Op::frag(lds, fa, i, 0);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) bf[0][j] = Op::frag(lds, fb, j, 0);
+    for (int j = 0; j < 2; ++j) bf[0][j] = Op::frag(lds, fb, j, 0);
 
-  for (int ti = 0; ti < t_count; ++ti) {
-    int cm0, cn0;
-    origin(ti, cm0, cn0);
-    f32x16 acc[4][2];
+    for (int ti = 0; ti < t_count; ++ti) {
+      int cm0, cn0;
+      origin(ti, cm0, cn0);
+      f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    for (int kt = 0; kt < nk; ++kt) {
-      const int it = ti * nk + kt;
-      const unsigned char* sa = lds + (it % ST) * STAGE;
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      for (int kt = 0; kt < nk; ++kt) {
+        const int it = ti * nk + kt;
+        const unsigned char* sa = lds + (it % ST) * STAGE;
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        const int cb = kk & 1, nb = cb ^ 1;
-        if (kk + 1 < NK) {
+        for (int kk = 0; kk < NK; ++kk) {
+          const int cb = kk & 1, nb = cb ^ 1;
+          if (kk + 1 < NK) {
+            if (LD && kk == 0) issue(it + 1, 1);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) af[nb][i] = Op::frag(sa, fa, i, kk + 1);
+            for (int i = 0; i < 4; ++i) af[nb][i] = Op::frag(sa, fa, i, kk + 1);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) bf[nb][j] = Op::frag(sa, fb, j, kk + 1);
+            for (int j = 0; j < 2; ++j) bf[nb][j] = Op::frag(sa, fb, j, kk + 1);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
-          // the next step's 6 reads go out one per MFMA at the start of this step
+              for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+            // the next step's 6 reads (and the loaders' B tile) go out between
+            // the first six MFMAs
 #pragma unroll
-          for (int g = 0; g < 6; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int q = 0; q < 6; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              if (LD && kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, (Ld::L + 5) / 6, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          } else {
+            // last step: stage it + 1 landed and stage it no longer read by
+            // anyone once every wave is past this barrier
+            if constexpr (LD) vm_wait<0>();
+            lds_sync();
+            if constexpr (LD) issue(it + ST, 0);
+            const unsigned char* na = lds + ((it + 1) % ST) * STAGE;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[nb][i] = Op::frag(na, fa, i, 0);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bf[nb][j] = Op::frag(na, fb, j, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+            // the loaders' A tile and the next stage's first fragment reads go
+            // out between the MFMAs
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              if (LD) __builtin_amdgcn_sched_group_barrier(0x020, (Ld::L + 7) / 8, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        } else {
-          // the first kPre of the last step's MFMAs are issued before the
-          // barrier, so the matrix core has work while the wave waits there
-#pragma unroll
-          for (int q = 0; q < kPre; ++q)
-            acc[q / 2][q % 2] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cb][q % 2], af[cb][q / 2], acc[q / 2][q % 2], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          wait_for(ST - 2);
-          lds_sync();
-          // into the buffer stage it leaves; past the end the last stage
-          // again, so every iteration issues the same number of loads
-          issue(min(it + ST, total - 1), it % ST);
-          const unsigned char* na = lds + ((it + 1) % ST) * STAGE;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) af[nb][i] = Op::frag(na, fa, i, 0);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) bf[nb][j] = Op::frag(na, fb, j, 0);
-#pragma unroll
-          for (int q = kPre; q < 8; ++q)
-            acc[q / 2][q % 2] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cb][q % 2], af[cb][q / 2], acc[q / 2][q % 2], 0, 0, 0);
-          // the stage's loads and the next fragments spread over those MFMAs
-#pragma unroll
-          for (int g = 0; g < 8 - kPre; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, (LOADS + 7 - kPre) / (8 - kPre), 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, (6 + 7 - kPre) / (8 - kPre), 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // NK even: the next stage's first fragments are in buffer 0 again
-      static_assert(NK % 2 == 0, "fragment buffer parity across stages");
+      store_tile(acc, cm0, cn0);
     }
-    store_tile(acc, cm0, cn0);
-  }
+  };
+  if (wave < 4) run(std::true_type{});
+  else run(std::false_type{});
   // the last iterations loaded the final stage again into buffers nobody reads:
   // let those direct-to-LDS writes land before the workgroup's LDS is released
   vm_wait<0>();
 }
 
 constexpr int kKB = 64;   // stage depth
-constexpr int kST = 2;    // LDS stages (2 x 64 KiB)
+constexpr int kST = 2;    // LDS stages (2 x 64 KiB), fixed in the kernel
 
 }  // namespace
 
@@ -305,7 +333,7 @@ hipError_t launch_w0_pipe(const GemmBf16& p, hipStream_t s) {
   if (!w0_pipe_supported(p)) return hipErrorInvalidValue;
   const long long ntile = (long long)(p.M / kTile) * (p.N / kTile);
   const size_t lds = (size_t)kST * 2 * kTile * kKB * 2;
-  hipLaunchKernelGGL((w0_gemm_nt_pipe<kKB, kST>), dim3((unsigned)std::min<long long>(ntile, 256)), dim3(kThr),
+  hipLaunchKernelGGL((w0_gemm_nt_pipe<kKB>), dim3((unsigned)std::min<long long>(ntile, 256)), dim3(kThr),
                      lds, s, p);
   return hipGetLastError();
 }
