@@ -24,10 +24,10 @@
 //    idle (in-kernel timestamps showed the last step of a stage taking about
 //    three times its MFMA time). Here waves 0-3 issue the A tile of stage
 //    s + 2 right after the barrier that frees its buffer (interleaved with
-//    that step's MFMAs) and its B tile during the first step of stage s + 1;
-//    waves 4-7 only read fragments and multiply, and keep the matrix cores
-//    busy while the loads queue: 5-11 % faster on the 16384 x {2048, 5632} x
-//    {2048, 5632} shapes than all waves loading, with the same bits.
+//    that step's MFMAs) and its B tile in halves during the first two steps of
+//    stage s + 1; waves 4-7 only read fragments and multiply, and keep the
+//    matrix cores busy while the loads queue: 5-12 % faster on the 16384 x
+//    {2048, 5632} x {2048, 5632} shapes than all waves loading, same bits.
 //
 // Requirements (w0_pipe_supported): M, N multiples of 256, K of 64, 16-byte
 // rows, each operand below 2 GiB (32-bit offsets), one group, no split.
@@ -113,7 +113,7 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
   constexpr int ST = 2;                        // LDS stages
   constexpr int NK = KB / 16;                  // 16-deep steps per stage
   constexpr int STAGE = 2 * Op::BYTES;         // A tile, then B tile
-  static_assert(NK >= 2 && NK % 2 == 0, "a first and a last step; fragment buffer parity across stages");
+  static_assert(NK >= 3 && NK % 2 == 0, "two B steps and a last step; fragment buffer parity across stages");
   static_assert(2 * Ld::L <= 63, "vmcnt range");
   extern __shared__ __align__(16) unsigned char lds[];
 
@@ -151,11 +151,11 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
   const int nk = p.K / KB;
   const int total = t_count * nk;
 
-  // operand `op` (0: A, 1: B) of global stage s (past the end: the last stage
-  // again, into a buffer nobody reads) into LDS buffer s % ST, by waves 0-3; the
-  // wave-uniform part of each offset goes in soffset (whole tiles: every access
-  // is inside the operand)
-  auto issue = [&](int s, int op) {
+  // loads [i0, i1) of operand `op` (0: A, 1: B) of global stage s (past the
+  // end: the last stage again, into a buffer nobody reads) into LDS buffer
+  // s % ST, by waves 0-3; the wave-uniform part of each offset goes in soffset
+  // (whole tiles: every access is inside the operand)
+  auto issue = [&](int s, int op, int i0 = 0, int i1 = Ld::L) {
     const int buf = s % ST;
     s = min(s, total - 1);
     const int ti = s / nk, kt = s - ti * nk;
@@ -165,14 +165,14 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
     if (op == 0) {
       const uint32_t ka = (uint32_t)(((long long)m0 * p.lda + (long long)kt * KB) * 2);
 #pragma unroll
-      for (int i = 0; i < Ld::L; ++i)
+      for (int i = i0; i < i1; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, (__attribute__((address_space(3))) void*)(st + i * 256 * 16), 16, va,
             (int)(ka + (uint32_t)(i * Ld::RPL * p.lda * 2)), 0, 0);
     } else {
       const uint32_t kb = (uint32_t)(((long long)n0 * p.ldb + (long long)kt * KB) * 2);
 #pragma unroll
-      for (int i = 0; i < Ld::L; ++i)
+      for (int i = i0; i < i1; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rb, (__attribute__((address_space(3))) void*)(st + i * 256 * 16), 16, vb,
             (int)(kb + (uint32_t)(i * Ld::RPL * p.ldb * 2)), 0, 0);
@@ -222,14 +222,14 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
   // The two wave groups run separate copies of the loop (LD: waves 0-3), each
   // with its own instruction schedule. Stage s + 2 lands in the buffer stage s
   // leaves: its A tile is issued right after the barrier of stage s's last
-  // step, its B tile during the first step of stage s + 1, and the loaders wait
-  // for both before the barrier of stage s + 1's last step.
+  // step, its B tile in halves during the first two steps of stage s + 1, and
+  // the loaders wait for both before the barrier of stage s + 1's last step.
   auto run = [&](auto ld_tag) {
     constexpr bool LD = decltype(ld_tag)::value;
     if constexpr (LD) {
       issue(0, 0);
       issue(0, 1);
-      issue(1, 0);          // stage 1's A tile; its B tile goes out in stage 0's first step
+      issue(1, 0);          // stage 1's A tile; its B tile goes out in stage 0's first steps
       vm_wait<Ld::L>();     // stage 0 landed
     }
     lds_sync();
@@ -256,7 +256,7 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
         for (int kk = 0; kk < NK; ++kk) {
           const int cb = kk & 1, nb = cb ^ 1;
           if (kk + 1 < NK) {
-            if (LD && kk == 0) issue(it + 1, 1);
+            if (LD && kk < 2) issue(it + 1, 1, kk * (Ld::L / 2), (kk + 1) * (Ld::L / 2));
 #pragma unroll
             for (int i = 0; i < 4; ++i) af[nb][i] = Op::frag(sa, fa, i, kk + 1);
 #pragma unroll
@@ -271,7 +271,7 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
 #pragma unroll
             for (int q = 0; q < 6; ++q) {
               __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              if (LD && kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, (Ld::L + 5) / 6, 0);
+              if (LD && kk < 2) __builtin_amdgcn_sched_group_barrier(0x020, (Ld::L / 2 + 5) / 6, 0);
               __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
