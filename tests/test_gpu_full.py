@@ -84,15 +84,18 @@ def test_merge_full_size():
     _check("W_new", to_np(W), want, 4e-3)
 
 
-def test_int8_weight_full_size():
+@pytest.mark.parametrize("weight", ["int8", "int8_t"])
+def test_int8_weight_full_size(weight):
     """POET-XQ on the 5632 x 2048 layer at 8192 tokens (build, forward,
-    backward) against the full oracle on the dequantised weight."""
+    backward) against the full oracle on the dequantised weight, with the int8
+    weight alone ("int8": the backward's product reads it N-contiguous) and
+    kept beside its transpose ("int8_t": K-contiguous, the NT kernel)."""
     import dataclasses
     import torch
     from gpu_util import make_layer, to_dev, to_np
     w = workloads.WORKLOADS[3]
     inp = workloads.layer_inputs(w, 0)
-    L = make_layer(inp, w.k, "bf16", weight="int8")
+    L = make_layer(inp, w.k, "bf16", weight=weight)
     L.build()
     X, G = to_dev(inp.X, "bf16"), to_dev(inp.G_Y, "bf16")
     Y = L.forward(X)

@@ -514,13 +514,22 @@ def test_layer_int8_weight(case, save):
     _compare(got, ref, ["Y", "G_X", "g_theta_R", "g_theta_P"], TOL_BF16, "int8")
 
 
+@pytest.mark.parametrize("size", ["small", "whole_tiles"])
 @pytest.mark.parametrize("save", [True, False])
-def test_int8_weight_kept_with_transpose(save):
+def test_int8_weight_kept_with_transpose(save, size):
     """POETX_WEIGHT_INT8_ROWS_T: quantize_weight also writes qT (the exact
     transpose of q), and every output equals the INT8_ROWS plan's bit for bit
-    (the backward's weight product reads qT K-contiguous, same MFMA order)."""
+    (the backward's weight product reads qT K-contiguous, same MFMA order).
+    whole_tiles: 1024 x 1024 at 16384 tokens, on whole 256 x 256 tiles with at
+    least one tile per CU (the int8_t plan's backward on the NT kernel, the int8
+    plan's on the NN kernel)."""
     import torch
-    inp = _int8_inputs(512, 768, (256, 256), (256,) * 3, T=333, seed=12)
+    if size == "small":
+        m, n, T = 512, 768, 333
+        inp = _int8_inputs(m, n, (256, 256), (256,) * 3, T=T, seed=12)
+    else:
+        m, n, T = 1024, 1024, 16384
+        inp = _int8_inputs(m, n, (256,) * 4, (256,) * 4, T=T, seed=13)
     outs = []
     for weight in ("int8", "int8_t"):
         L = make_layer(inp, 4, "bf16", weight=weight)
@@ -532,10 +541,10 @@ def test_int8_weight_kept_with_transpose(save):
         outs.append([Y, G_X, gR, gP])
         if weight == "int8_t":
             q, _ = L.int8_weight()
-            mn = 512 * 768
-            off = ((mn + 255) // 256 * 256 + 4 * 512 + 255) // 256 * 256
+            mn = m * n
+            off = ((mn + 255) // 256 * 256 + 4 * m + 255) // 256 * 256
             assert L.plan.weight_bytes() == off + mn
-            qT = L.Wt[off:off + mn].view(torch.int8).view(768, 512)
+            qT = L.Wt[off:off + mn].view(torch.int8).view(n, m)
             assert torch.equal(qT.cpu(), q.cpu().t().contiguous())
     for a, b in zip(*outs):
         assert torch.equal(_bits(a), _bits(b))
