@@ -174,51 +174,70 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, tokens: int):
-    """float64 oracle on the workload's own layers, every layer at `tokens`
-    tokens (build + forward + backward). At the workload's full T the figure is
-    measured; below it, the oracle also runs at 0 tokens (the build and the
-    chain rule, which do not depend on T) and the per-token part is scaled to
-    the full T, which the sample states."""
+def _oracle_seconds(w, tokens: int, dtype):
+    """Seconds per step of the oracle on the workload's own layers, every layer
+    at `tokens` tokens (build + forward + backward) in float type `dtype`. At
+    the workload's full T the figure is measured; below it the oracle also runs
+    at 0 tokens (the build and the chain rule, which do not depend on T) and
+    the per-token part is scaled to the full T. Returns (seconds, measured
+    seconds, full)."""
     import oracle
     import workloads
+    tokens = min(tokens, w.T)
+    full = tokens == w.T
+    fixed = per_tok = measured = 0.0
+    with oracle.precision(dtype):
+        for li in range(len(w.layers)):
+            inp = workloads.layer_inputs(w, li, T=tokens, draw_grad=w.backward)
+            for T in ((tokens,) if full else (0, tokens)):
+                sub = type("I", (), dict(spec=inp.spec, W0=inp.W0, theta_R=inp.theta_R,
+                                         theta_P=inp.theta_P, pi_R=inp.pi_R, pi_P=inp.pi_P,
+                                         X=inp.X[:T], G_Y=None if inp.G_Y is None else inp.G_Y[:T]))()
+                t0 = time.perf_counter()
+                oracle.layer_reference(sub, w.k, backward_pass=w.backward)
+                dt = time.perf_counter() - t0
+                measured += dt
+                if T == 0:
+                    t_fixed = dt
+                elif not full:
+                    per_tok += max(dt - t_fixed, 0.0) / tokens
+            if not full:
+                fixed += t_fixed
+            del inp
+    return (measured if full else fixed + per_tok * w.T), measured, full
+
+
+def cpu_baseline(w, tokens: int):
+    """The float64 oracle on the workload's own layers, every layer at `tokens`
+    tokens (build + forward + backward), measured at the workload's full T or
+    scaled from a sample (which the sample states); beside it the same steps in
+    float32 on a quarter of those tokens, as a CPU throughput figure."""
+    import numpy as np
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()
                        if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    tokens = min(tokens, w.T)
-    full = tokens == w.T
-    fixed = per_tok = measured = 0.0
-    for li in range(len(w.layers)):
-        inp = workloads.layer_inputs(w, li, T=tokens, draw_grad=w.backward)
-        for T in ((tokens,) if full else (0, tokens)):
-            sub = type("I", (), dict(spec=inp.spec, W0=inp.W0, theta_R=inp.theta_R,
-                                     theta_P=inp.theta_P, pi_R=inp.pi_R, pi_P=inp.pi_P,
-                                     X=inp.X[:T], G_Y=None if inp.G_Y is None else inp.G_Y[:T]))()
-            t0 = time.perf_counter()
-            oracle.layer_reference(sub, w.k, backward_pass=w.backward)
-            dt = time.perf_counter() - t0
-            measured += dt
-            if T == 0:
-                t_fixed = dt
-            elif not full:
-                per_tok += max(dt - t_fixed, 0.0) / tokens
-        if not full:
-            fixed += t_fixed
-        del inp
-    est = measured if full else fixed + per_tok * w.T
+    est, measured, full = _oracle_seconds(w, tokens, np.float64)
     what = "build + forward + backward" if w.backward else "build + forward"
+    tokens = min(tokens, w.T)
     sample = (f"float64 NumPy oracle, {what} of all {len(w.layers)} layers on their own inputs at "
               f"the full {w.T} tokens: {est:.1f} s per step, measured" if full else
               f"float64 NumPy oracle, {what} of all {len(w.layers)} layers on their own inputs at 0 "
               f"and {tokens} tokens; the per-token part scaled to {w.T} tokens (est. {est:.1f} s "
               f"per step; {measured:.1f} s measured)")
+    t32 = max(1, tokens // 4)
+    est32, meas32, full32 = _oracle_seconds(w, t32, np.float32)
     return {
         "value": w.T / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
         "sample": sample, "seconds_per_step": est, "measured": full,
         "cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+        "fp32": {"value": w.T / est32, "unit": "tokens/s", "seconds_per_step": est32,
+                 "sample": (f"the same oracle steps in float32, at 0 and {t32} tokens per layer, the "
+                            f"per-token part scaled to {w.T} tokens ({meas32:.1f} s measured)"
+                            if not full32 else f"the same oracle steps in float32 at the full {w.T} "
+                            f"tokens, measured")},
     }
 
 

@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE. This module is the checker, not the product: only
 tests/, the smoke check and the benchmark's cpu_baseline leg may import it.
 It shares no code with the HIP library (no kernels, tables or helpers), and
 nothing here is tuned: every step is written as the definition reads, one
-library primitive (matmul, indexing) per step, in float64.
+library primitive (matmul, indexing) per step, in float64. (`precision`
+switches the float type, for timing the same steps in float32 as a CPU
+throughput figure; every check uses float64.)
 
 Citations
   [PX]   page "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
@@ -37,6 +39,8 @@ from __future__ import annotations
 
 from typing import List, Sequence, Tuple
 
+import contextlib
+
 import numpy as np
 
 __all__ = [
@@ -45,7 +49,24 @@ __all__ = [
     "forward", "forward_rows", "cnp_backward", "backward", "cnp_coefficients",
     "rel_fro", "layer_reference", "backward_rows", "theta_grad_block", "side_matrix",
     "merge_weight", "quantize_rows", "dequantize_rows", "exact_cayley", "cayley_backward_exact",
+    "precision",
 ]
+
+
+
+_DT = np.float64   # the float type of every step (float64 unless `precision` says otherwise)
+
+
+@contextlib.contextmanager
+def precision(dtype):
+    """Run the oracle's steps in another float type while the context lasts
+    (float32 for a CPU throughput figure); checks use the float64 default."""
+    global _DT
+    old, _DT = _DT, np.dtype(dtype).type
+    try:
+        yield
+    finally:
+        _DT = old
 
 
 def rel_fro(a, ref) -> float:
@@ -70,9 +91,9 @@ def block_offsets(bsz: Sequence[int]) -> List[int]:
 
 def skew_from_packed(theta_blk: np.ndarray, b: int) -> np.ndarray:
     """[PX] §2.D: the skew generator from its stored strict upper triangle."""
-    theta_blk = np.asarray(theta_blk, dtype=np.float64)
+    theta_blk = np.asarray(theta_blk, dtype=_DT)
     assert theta_blk.shape == (b * (b - 1) // 2,)
-    S = np.zeros((b, b), dtype=np.float64)
+    S = np.zeros((b, b), dtype=_DT)
     iu = np.triu_indices(b, 1)
     S[iu] = theta_blk
     S[(iu[1], iu[0])] = -theta_blk
@@ -82,14 +103,14 @@ def skew_from_packed(theta_blk: np.ndarray, b: int) -> np.ndarray:
 def packed_upper(M: np.ndarray) -> np.ndarray:
     """Strict upper triangle of a square matrix, row-major."""
     b = M.shape[0]
-    return np.asarray(M, dtype=np.float64)[np.triu_indices(b, 1)]
+    return np.asarray(M, dtype=_DT)[np.triu_indices(b, 1)]
 
 
 def neumann_cayley(S: np.ndarray, k: int) -> np.ndarray:
     """[PX] §2.D: Cayley transform (I+S)(I-S)^{-1} with the inverse replaced by
     the Neumann series I + S + ... + S^k; powers by repeated multiplication."""
     b = S.shape[0]
-    I = np.eye(b)
+    I = np.eye(b, dtype=_DT)
     N = I.copy()
     Pj = I.copy()
     for _ in range(k):
@@ -101,7 +122,7 @@ def neumann_cayley(S: np.ndarray, k: int) -> np.ndarray:
 def exact_cayley(S: np.ndarray) -> np.ndarray:
     """The Cayley transform itself, Q = (I+S)(I-S)^{-1}, by a linear solve: the
     map [PX] §2.D's Neumann series approximates (exact-Cayley mode)."""
-    I = np.eye(S.shape[0])
+    I = np.eye(S.shape[0], dtype=_DT)
     return (I + S) @ np.linalg.solve(I - S, I)
 
 
@@ -109,7 +130,7 @@ def cayley_backward_exact(G: np.ndarray, S: np.ndarray) -> np.ndarray:
     """Gradient w.r.t. S of <G, Q(S)> for the exact transform. With
     N = (I-S)^{-1}: dN = N dS N, so dQ = dS N + (I+S) N dS N = (I+Q) dS N and
     dL/dS = (I+Q)^T G N^T."""
-    I = np.eye(S.shape[0])
+    I = np.eye(S.shape[0], dtype=_DT)
     N = np.linalg.solve(I - S, I)
     Q = (I + S) @ N
     return (I + Q).T @ G @ N.T
@@ -118,7 +139,7 @@ def cayley_backward_exact(G: np.ndarray, S: np.ndarray) -> np.ndarray:
 def build_orth(theta: np.ndarray, bsz: Sequence[int], k) -> List[np.ndarray]:
     """Packed parameters of all blocks of one side -> list of orthogonal blocks
     (k = None: the exact transform instead of the truncated series)."""
-    theta = np.asarray(theta, dtype=np.float64)
+    theta = np.asarray(theta, dtype=_DT)
     out, off = [], 0
     for b in bsz:
         cnt = b * (b - 1) // 2
@@ -131,7 +152,7 @@ def build_orth(theta: np.ndarray, bsz: Sequence[int], k) -> List[np.ndarray]:
 
 def apply_blocks_T(A: np.ndarray, Qs: Sequence[np.ndarray], bsz: Sequence[int]) -> np.ndarray:
     """[PX] §2.C, row form of D x: each block separately, out[:, blk] = A[:, blk] Q^T."""
-    out = np.empty((A.shape[0], sum(bsz)), dtype=np.float64)
+    out = np.empty((A.shape[0], sum(bsz)), dtype=_DT)
     for off, b, Q in zip(block_offsets(bsz), bsz, Qs):
         out[:, off:off + b] = A[:, off:off + b] @ Q.T
     return out
@@ -139,7 +160,7 @@ def apply_blocks_T(A: np.ndarray, Qs: Sequence[np.ndarray], bsz: Sequence[int]) 
 
 def apply_blocks(A: np.ndarray, Qs: Sequence[np.ndarray], bsz: Sequence[int]) -> np.ndarray:
     """Row form of D^T g: out[:, blk] = A[:, blk] Q (used by the backward)."""
-    out = np.empty((A.shape[0], sum(bsz)), dtype=np.float64)
+    out = np.empty((A.shape[0], sum(bsz)), dtype=_DT)
     for off, b, Q in zip(block_offsets(bsz), bsz, Qs):
         out[:, off:off + b] = A[:, off:off + b] @ Q
     return out
@@ -147,15 +168,15 @@ def apply_blocks(A: np.ndarray, Qs: Sequence[np.ndarray], bsz: Sequence[int]) ->
 
 def permute_weight(W0: np.ndarray, pi_R: np.ndarray, pi_P: np.ndarray) -> np.ndarray:
     """[PX] §2.B: fold both permutations into W once: Wt[i, j] = W0[pi_R[i], pi_P[j]]."""
-    W0 = np.asarray(W0, dtype=np.float64)
+    W0 = np.asarray(W0, dtype=_DT)
     return W0[np.asarray(pi_R)][:, np.asarray(pi_P)]
 
 
 def forward(X, Wt, pi_R, pi_P, QR, QP, bsz_R, bsz_P) -> Tuple[np.ndarray, np.ndarray]:
     """[PX] §2.A input-centric layer: the orthogonal factors act on activations,
     R W0 P is never formed. Returns (Y, Wa) with Wa the saved activation."""
-    X = np.asarray(X, dtype=np.float64)
-    Wt = np.asarray(Wt, dtype=np.float64)
+    X = np.asarray(X, dtype=_DT)
+    Wt = np.asarray(Wt, dtype=_DT)
     U = X[:, np.asarray(pi_P)]                 # gather: U = X Pi_P^T
     V = apply_blocks_T(U, QP, bsz_P)           # V = U D_P^T
     Wa = V @ Wt.T                              # Wa = V Wt^T
@@ -186,10 +207,10 @@ def cnp_backward(G: np.ndarray, S: np.ndarray, k: int) -> np.ndarray:
     c = cnp_coefficients(k)
     b = S.shape[0]
     St = S.T
-    pw = [np.eye(b)]
+    pw = [np.eye(b, dtype=_DT)]
     for _ in range(k + 1):
         pw.append(pw[-1] @ St)
-    Sbar = np.zeros((b, b))
+    Sbar = np.zeros((b, b), dtype=_DT)
     for j in range(1, k + 2):
         for a in range(j):
             Sbar += c[j] * (pw[a] @ G @ pw[j - 1 - a])
@@ -199,7 +220,7 @@ def cnp_backward(G: np.ndarray, S: np.ndarray, k: int) -> np.ndarray:
 def _theta_grad(dQs, theta, bsz, k) -> np.ndarray:
     """Map each block's dL/dQ to the packed parameters: dL/dtheta_(i,j) =
     Sbar[i, j] - Sbar[j, i] since S[i, j] = theta and S[j, i] = -theta."""
-    theta = np.asarray(theta, dtype=np.float64)
+    theta = np.asarray(theta, dtype=_DT)
     out, off = [], 0
     for b, G in zip(bsz, dQs):
         cnt = b * (b - 1) // 2
@@ -214,10 +235,10 @@ def backward(X, Wt, pi_R, pi_P, theta_R, theta_P, QR, QP, Wa, G_Y, bsz_R, bsz_P,
     """Gradients of L = <G_Y, Y> w.r.t. X, theta_R and theta_P, following the
     forward's steps in reverse (W0 is frozen, so it gets no gradient).
     Returns (G_X, g_theta_R, g_theta_P, dQ_R, dQ_P)."""
-    X = np.asarray(X, dtype=np.float64)
-    Wt = np.asarray(Wt, dtype=np.float64)
-    Wa = np.asarray(Wa, dtype=np.float64)
-    G_Y = np.asarray(G_Y, dtype=np.float64)
+    X = np.asarray(X, dtype=_DT)
+    Wt = np.asarray(Wt, dtype=_DT)
+    Wa = np.asarray(Wa, dtype=_DT)
+    G_Y = np.asarray(G_Y, dtype=_DT)
     pi_R = np.asarray(pi_R)
     pi_P = np.asarray(pi_P)
     G_Z = G_Y[:, pi_R]                                   # undo the scatter
@@ -254,10 +275,10 @@ def layer_reference(inp, k, backward_pass: bool = True):
 def backward_rows(G_Y_rows, Wt, pi_R, pi_P, QR, QP, bsz_R, bsz_P) -> np.ndarray:
     """G_X for a subset of token rows: each row of G_X depends only on the same
     row of G_Y (the backward steps of the activation path, restricted to rows)."""
-    G_Y_rows = np.asarray(G_Y_rows, dtype=np.float64)
+    G_Y_rows = np.asarray(G_Y_rows, dtype=_DT)
     G_Z = G_Y_rows[:, np.asarray(pi_R)]
     G_Wa = apply_blocks(G_Z, QR, bsz_R)
-    G_V = G_Wa @ np.asarray(Wt, dtype=np.float64)
+    G_V = G_Wa @ np.asarray(Wt, dtype=_DT)
     G_U = apply_blocks(G_V, QP, bsz_P)
     G_X = np.empty_like(G_U)
     G_X[:, np.asarray(pi_P)] = G_U
@@ -267,9 +288,9 @@ def backward_rows(G_Y_rows, Wt, pi_R, pi_P, QR, QP, bsz_R, bsz_P) -> np.ndarray:
 def theta_grad_block(side, j, X, Wt, pi_R, pi_P, theta_R, theta_P, QR, QP, G_Y, bsz_R, bsz_P, k):
     """Packed gradient of one block (side "R" or "P", block index j) over all
     tokens, computing only the columns that block's dL/dQ needs."""
-    X = np.asarray(X, dtype=np.float64)
-    Wt = np.asarray(Wt, dtype=np.float64)
-    G_Y = np.asarray(G_Y, dtype=np.float64)
+    X = np.asarray(X, dtype=_DT)
+    Wt = np.asarray(Wt, dtype=_DT)
+    G_Y = np.asarray(G_Y, dtype=_DT)
     pi_R = np.asarray(pi_R)
     pi_P = np.asarray(pi_P)
     if side == "R":
@@ -288,7 +309,7 @@ def theta_grad_block(side, j, X, Wt, pi_R, pi_P, theta_R, theta_P, QR, QP, G_Y, 
         dQ = G_V_blk.T @ U_blk
         theta, bsz = theta_P, bsz_P
     poff = sum(bb * (bb - 1) // 2 for bb in bsz[:j])
-    S = skew_from_packed(np.asarray(theta, dtype=np.float64)[poff:poff + b * (b - 1) // 2], b)
+    S = skew_from_packed(np.asarray(theta, dtype=_DT)[poff:poff + b * (b - 1) // 2], b)
     Sbar = cayley_backward_exact(dQ, S) if k is None else cnp_backward(dQ, S, k)
     return packed_upper(Sbar - Sbar.T)
 
@@ -298,10 +319,10 @@ def side_matrix(Qs: Sequence[np.ndarray], bsz: Sequence[int], pi) -> np.ndarray:
     permutation matrix with (Pi v)_i = v[pi[i]] ([PX] §2.B), i.e. the rows of
     the identity taken in the order pi."""
     dim = sum(bsz)
-    D = np.zeros((dim, dim), dtype=np.float64)
+    D = np.zeros((dim, dim), dtype=_DT)
     for off, b, Q in zip(block_offsets(bsz), bsz, Qs):
         D[off:off + b, off:off + b] = Q
-    Pi = np.eye(dim)[np.asarray(pi)]
+    Pi = np.eye(dim, dtype=_DT)[np.asarray(pi)]
     return Pi.T @ D @ Pi
 
 
@@ -313,7 +334,7 @@ def merge_weight(W0, theta_R, theta_P, pi_R, pi_P, bsz_R, bsz_P, k: int) -> np.n
     W_new with theta = 0 and new permutations."""
     R = side_matrix(build_orth(theta_R, bsz_R, k), bsz_R, pi_R)
     P = side_matrix(build_orth(theta_P, bsz_P, k), bsz_P, pi_P)
-    return R @ np.asarray(W0, dtype=np.float64) @ P
+    return R @ np.asarray(W0, dtype=_DT) @ P
 
 
 def quantize_rows(W) -> Tuple[np.ndarray, np.ndarray]:
