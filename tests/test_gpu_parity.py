@@ -177,6 +177,10 @@ def test_layer_fp32_ragged(case):
     # frozen-weight product on whole 256 x 256 tiles with one 64-deep stage
     # (K = n = 64) and 1088 tiles on 256 workgroups
     dict(m=4352, n=64, bR=(256,) * 17, bP=(64,), T=16384, k=2),
+    # the same kernel with three 64-deep stages per tile and 320 tiles (some
+    # workgroups take a second tile), and with two stages on exactly 256 tiles
+    dict(m=1280, n=192, bR=(256,) * 5, bP=(64, 128), T=16384, k=3),
+    dict(m=1024, n=128, bR=(256,) * 4, bP=(128,), T=16384, k=2),
     dict(m=48, n=32, bR=(16, 32), bP=(32,), T=5, k=0),
     # split chains over blocks that are multiples of 32 but not of 64, alone and
     # mixed with other sizes in one launch
