@@ -13,7 +13,10 @@
 // MFMA operand fragments (64 VGPRs), loaded once per workgroup (a workgroup
 // stays on one block). A block of 512 takes two workgroups, each with 256 of
 // its output columns and all 512 k (128 VGPRs of B per lane); its A tiles are
-// 64 rows x 512 (64 KiB) in two stages. Row tiles of A (ROWS rows x the block's columns)
+// 64 rows x 512 (64 KiB) in two stages. B is fetched before the first A tiles
+// (a block of 256 in natural layout through the whole, still empty LDS ring):
+// behind them it would wait for all of them, which doubled the start-up of a
+// workgroup that runs only 8 tiles. Row tiles of A (ROWS rows x the block's columns)
 // stream from HBM into an LDS ring of ST stages with direct-to-LDS loads, ST - 1
 // tiles in flight while one is multiplied; every wave reads the whole A tile
 // from LDS. An HBM stream needs on the order of 100 KiB in flight per CU, so
@@ -149,17 +152,41 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
     }
   };
 
-  // the first ST - 1 tiles go out while B is fetched
-#pragma unroll
-  for (int i = 0; i < ST - 1; ++i)
-    if (t0 + i < t1) issue(t0 + i, stage(i));
-  // B_g(ncol, 16 kk + 8 h .. + 7) for kk = 0 .. 15
+  // B_g(ncol, 16 kk + 8 h .. + 7) for kk = 0 .. 15. B goes out before the first
+  // A tiles: loads return in order, so B queued behind ST - 1 tiles of A would
+  // wait for all of them before the first multiply could start.
   bf16x8 bq[kNKK];
-  if (BKM) {
+  // natural-layout B of a 256 block: the whole block (256 K-rows of 512 bytes)
+  // fits the empty LDS ring, so it arrives in one round trip
+  constexpr bool kRingB = !BKM && KD == kB && ST * STAGE >= KD * kB * 2;
+  if constexpr (BKM) {
 #pragma unroll
     for (int kk = 0; kk < kNKK; ++kk)
       bq[kk] = *reinterpret_cast<const bf16x8*>(Bg + (long long)ncol * p.ldb + 16 * kk + 8 * h);
-  } else {
+  } else if constexpr (kRingB) {
+    // K-row k of the block in the layout of a row-contiguous A tile (chunk c at
+    // slot k (kB / 8) + (c ^ 4 (k & 3))), read back column-wise with the
+    // transposing reads of frag_t
+    constexpr int CPRB = kB / 8;
+    constexpr int RLOADS = KD * CPRB / kThreads;
+#pragma unroll
+    for (int i = 0; i < RLOADS; ++i) {
+      const int s = i * kThreads + tid;
+      const int k = s / CPRB;
+      const int c = (s % CPRB) ^ (4 * (k & 3));
+      dma16(Bg + (long long)k * p.ldb + c * 8, lds + (i * kThreads + wave * 64) * 16);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+#pragma unroll
+    for (int kk = 0; kk < kNKK; ++kk) bq[kk] = frag_t<kB>(lds, wave * 32, kk, lane);
+    lds_barrier();   // every wave has its B before the ring takes A tiles
+  }
+  // the first ST - 1 tiles of A
+#pragma unroll
+  for (int i = 0; i < ST - 1; ++i)
+    if (t0 + i < t1) issue(t0 + i, stage(i));
+  if constexpr (!BKM && !kRingB) {
     // column ncol of the slice of B_g through the still free last stage,
     // BROWS rows of it at a time in natural layout (row k = 512 bytes); the 32
     // lanes of a read take 64 consecutive bytes of one row
