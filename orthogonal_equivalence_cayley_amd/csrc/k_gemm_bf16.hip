@@ -261,8 +261,11 @@ hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || p.groups <= 0) return hipSuccess;
   if (block_regb_supported(p)) return launch_block_regb(p, s);
   const long long big_tiles = (long long)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.groups * p.splits;
-  // the token reduction (dQ) keeps 128 x 128 tiles: its split count is sized for them
-  const bool big = big_tiles >= 256 && p.role != GEMM_DQ;
+  // the token reduction (dQ) takes its tile size from dq_big_tiles, which its
+  // split count was sized for
+  const bool big = p.role == GEMM_DQ
+                       ? (p.M == p.N && dq_big_tiles(p.M, p.groups, p.K) && gemm_lds_supported(p, 256, 256))
+                       : big_tiles >= 256;
   // whole-tile shapes take the pipelined direct-to-LDS kernels; the rest (K not a
   // multiple of 64, partial tiles of row-contiguous operands) the kernels here
   if (big && w0_pipe_supported(p)) return launch_w0_pipe(p, s);

@@ -133,29 +133,38 @@ struct Carver {
   }
 };
 
-// dQ products reduce over tokens; split the token range so that the grid fills
-// the chip. Partial sums are reduced afterwards in a fixed order.
-int dq_splits(const poetx_plan* pl, int side, long long T) {
-  long long tiles = 0, blocks = 0;
-  // bf16: 128 x 128 tiles (two workgroups per CU); fp32: 64 x 64 tiles of the
-  // generic kernel
-  const int tile = pl->dtype == POETX_BF16 ? 128 : 64;
-  for (const Seg& g : pl->segs[side]) {
-    const long long t = (g.b + tile - 1) / tile;
-    tiles += t * t * g.count;
-    blocks += g.count;
-  }
-  long long s = (512 + tiles - 1) / std::max<long long>(tiles, 1);
+// Split count over the tokens of dQ = G^T A for one run of equal blocks (each
+// run is its own launch with its own partial sums): about one round of
+// workgroups on the chip. bf16: 128 x 128 tiles at two workgroups per CU, or
+// the 256 x 256 tiles of dq_big_tiles at one; fp32: 64 x 64 tiles of the
+// generic kernel. A multiple of 8 (blocks x splits) where possible, so the
+// tiles of one split share an XCD; at most one split per 256 tokens and 64.
+int dq_splits(const poetx_plan* pl, const Seg& g, long long T) {
+  long long s;
   if (pl->dtype == POETX_BF16) {
-    s = std::max<long long>(1, 512 / std::max<long long>(tiles, 1));   // one round of workgroups
-    // a multiple of 8 (blocks x splits) lets the tiles of one split share an XCD
-    while (s > 1 && (blocks * s) % 8) --s;
-    if ((blocks * s) % 8) s = std::max<long long>(1, 512 / std::max<long long>(tiles, 1));
+    const bool big = poetx::dq_big_tiles(g.b, g.count, T);
+    const int tile = big ? 256 : 128;
+    const long long slots = big ? 256 : 512;
+    const long long per = (g.b + tile - 1) / tile;
+    const long long tiles = std::max<long long>(1, per * per * g.count);
+    s = std::max<long long>(1, slots / tiles);
+    while (s > 1 && (g.count * s) % 8) --s;
+    if ((g.count * s) % 8) s = std::max<long long>(1, slots / tiles);
+  } else {
+    const long long per = (g.b + 63) / 64;
+    const long long tiles = std::max<long long>(1, per * per * g.count);
+    s = (512 + tiles - 1) / tiles;
   }
   const long long maxs = std::max<long long>(1, (T + 255) / 256);
   s = std::min(s, maxs);
   s = std::max<long long>(1, std::min<long long>(s, 64));
   return (int)s;
+}
+// fp32 partial sums one side's dQ needs: splits x elements of each run
+long long dq_part_elems(const poetx_plan* pl, int side, long long T) {
+  long long n = 0;
+  for (const Seg& g : pl->segs[side]) n += (long long)dq_splits(pl, g, T) * g.count * g.b * g.b;
+  return n;
 }
 
 struct FwdWs { void *U, *V, *Wa, *Z, *Wf; };
@@ -242,8 +251,7 @@ size_t layout_bwd(const poetx_plan* pl, long long T, void* base, BwdWs* w, Chain
   x.dQ[0] = (float*)c.take(4 * pl->nelem[0]);
   x.dQ[1] = (float*)c.take(4 * pl->nelem[1]);
   long long part = 0;
-  for (int side = 0; side < 2; ++side)
-    part = std::max(part, (long long)dq_splits(pl, side, T) * pl->nelem[side]);
+  for (int side = 0; side < 2; ++side) part = std::max(part, dq_part_elems(pl, side, T));
   x.part = (float*)c.take(4 * part);
   if (w) *w = x;
   for (int side = 0; side < 2; ++side) layout_chain(pl, side, c, cw ? &cw[side] : nullptr);
@@ -539,22 +547,25 @@ poetx_status fold_rt(const poetx_plan* pl, const void* Wt, const void* Q_R, void
   return POETX_OK;
 }
 
-// dQ[blk] = G[:, blk]^T A[:, blk] (reduction over tokens), fp32.
+// dQ[blk] = G[:, blk]^T A[:, blk] (reduction over tokens), fp32: each run of
+// equal blocks splits the tokens its own way (dq_splits) into its own part of
+// the partial sums, then sums them into its blocks of dQ.
 poetx_status block_grads(const poetx_plan* pl, int side, long long T, const void* G, const void* A,
                          float* part, float* dQ, hipStream_t s) {
   const size_t es = elsize(pl);
   const long long dim = pl->dim[side];
-  const int splits = dq_splits(pl, side, T);
-  const long long ne = pl->nelem[side];
   for (const Seg& g : pl->segs[side]) {
+    const int splits = dq_splits(pl, g, T);
+    const long long ne = (long long)g.count * g.b * g.b;
     const char* a = static_cast<const char*>(G) + es * g.dim_off;
     const char* b = static_cast<const char*>(A) + es * g.dim_off;
     // rows of the product index features, k indexes tokens
-    poetx_status st = gemm(pl, poetx::GEMM_DQ, Op{a, 1, dim}, Op{b, 1, dim}, part + g.q_off, g.b, g.b, g.b,
+    poetx_status st = gemm(pl, poetx::GEMM_DQ, Op{a, 1, dim}, Op{b, 1, dim}, part, g.b, g.b, g.b,
                            (int)T, g.count, g.b, g.b, (long long)g.b * g.b, splits, ne, true, s);
     if (st != POETX_OK) return st;
+    HIP_TRY(poetx::launch_sum_splits(part, splits, ne, ne, dQ + g.q_off, s));
+    part += (long long)splits * ne;
   }
-  HIP_TRY(poetx::launch_sum_splits(part, splits, ne, ne, dQ, s));
   return POETX_OK;
 }
 

@@ -154,6 +154,25 @@ struct GemmBf16 {
   int xcd_stride = 0;
 };
 hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s);
+// The token reduction dQ = G^T A over `count` blocks of b (K = the tokens):
+// 128 x 128 output tiles at two workgroups per CU, or, for blocks of 512 and up
+// (whole-tile pipelined kernels only, so K a multiple of 64), 256 x 256 tiles at
+// one per CU when a round of them fills the chip clearly better: 21 blocks of 512
+// give 336 small tiles (a third of the chip idle at one split, two rounds at
+// two) but 84 large ones (three splits, 252 workgroups). Where both fill it the
+// small tiles win: same time per launch at half the partial sums. The host
+// sizes the split count with the same rule.
+inline double dq_round_fill(long long tiles, long long slots) {
+  const long long s = tiles >= slots ? 1 : slots / tiles;
+  const long long wgs = tiles * s;
+  return (double)wgs / (double)(((wgs + slots - 1) / slots) * slots);
+}
+inline bool dq_big_tiles(int b, int count, long long K) {
+  if (b < 512 || b % 256 || K % 64 || count <= 0) return false;
+  const long long small = (long long)(b / 128) * (b / 128) * count;
+  const long long big = (long long)(b / 256) * (b / 256) * count;
+  return dq_round_fill(big, 256) > dq_round_fill(small, 512) + 0.1;
+}
 // Pipelined variant (direct-to-LDS loads, see k_gemm_lds.hip) for whole-tile shapes:
 // big = 256 x 256 tiles, else 128 x 128.
 bool gemm_lds_supported(const GemmBf16& p, int bm, int bn);

@@ -186,6 +186,11 @@ def test_layer_fp32_ragged(case):
     # mixed with other sizes in one launch
     dict(m=256, n=288, bR=(96, 160), bP=(224, 64), T=200, k=4),
     dict(m=320, n=96, bR=(192, 64, 64), bP=(96,), T=64, k=3),
+    # the token reduction dQ per run of equal blocks: 21 blocks of 512 on
+    # 256 x 256 tiles (three splits) beside one block of 256 with its own split
+    # count, as on an 11008-wide side; four blocks of 768 on the large tiles too
+    dict(m=11008, n=512, bR=(512,) * 21 + (256,), bP=(512,), T=1024, k=4),
+    dict(m=3072, n=256, bR=(768,) * 4, bP=(256,), T=640, k=3),
 ])
 def test_layer_bf16_small(case):
     inp = workloads.small_case(case["m"], case["n"], case["bR"], case["bP"], T=case["T"],
