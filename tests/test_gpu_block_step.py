@@ -7,8 +7,11 @@ chain rule through the parameterisation; independent layers on two HIP
 streams) runs at the real sizes of the hidden-2048 and hidden-4096 blocks
 (16384 tokens). Every element of Y, Wa and G_X, every block of Q and every
 packed parameter gradient of every layer is compared with the full float64
-oracle of that layer. At hidden 2048 the fold variant runs beside the default
-input-centric order and is checked against the same oracle results.
+oracle of that layer. At hidden 2048 the variants the benchmark also times run
+beside the default input-centric order and are checked against the same
+oracle results: the fold of the blocks into the weight, POET-Xmem (Wa not
+kept: the backward recomputes it), the Paterson-Stockmeyer build and the
+index maps fused into the block products.
 
 The step runs twice before the comparison, so the checked outputs are those
 of a step that reuses every workspace of the one before.
@@ -32,13 +35,21 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _run(cid, fold):
+# variants of the step at hidden 2048, as BlockStep options
+_VARIANTS = {
+    "fold": dict(fold="weight"),
+    "xmem": dict(xmem=True),
+    "ps": dict(series="ps"),
+    "fused": dict(index="fused"),
+}
+
+
+def _run(cid, **opts):
     import torch
     from orthogonal_equivalence_cayley_amd.block_step import BlockStep
     w = workloads.WORKLOADS[cid]
-    log(f"{w.name}: step with fold={fold}, T={w.T}, two streams")
-    blk = BlockStep(workloads.workload_layers(w), w.k, w.dtype, backward=w.backward, streams=2,
-                    fold=fold)
+    log(f"{w.name}: step with {opts or 'the default options'}, T={w.T}, two streams")
+    blk = BlockStep(workloads.workload_layers(w), w.k, w.dtype, backward=w.backward, streams=2, **opts)
     for _ in range(2):
         blk.step()
     torch.cuda.synchronize()
@@ -49,9 +60,10 @@ def _run(cid, fold):
 def steps(request):
     import torch
     cid = request.param
-    out = {"none": _run(cid, "none")}
+    out = {"default": _run(cid)}
     if cid == 4:
-        out["weight"] = _run(cid, "weight")
+        for name, opts in _VARIANTS.items():
+            out[name] = _run(cid, **opts)
     yield cid, out
     del out
     torch.cuda.empty_cache()
@@ -72,12 +84,14 @@ def test_block_step_layer_full(steps, li):
     sp = inp.spec
     log(f"{w.name} layer {sp.name} {sp.m}x{sp.n}: float64 oracle at T={w.T}")
     ref = oracle.layer_reference(inp, w.k, backward_pass=True)
-    for fold, blk in runs.items():
-        got = {k: to_np(v) for k, v in blk.outputs(li).items()}
-        log(f" fold={fold}")
+    for variant, blk in runs.items():
+        got = {k: to_np(v) for k, v in blk.outputs(li).items() if v is not None}
+        log(f" {variant}")
         _check("Q_R", got["QR"], blocks_concat(ref["QR"]), TOL_F32)
         _check("Q_P", got["QP"], blocks_concat(ref["QP"]), TOL_F32)
         for key in ("Wa", "Y", "G_X", "g_theta_R", "g_theta_P"):
+            if key == "Wa" and key not in got:   # POET-Xmem keeps no Wa
+                continue
             _check(key, got[key], ref[key], TOL_BF16)
         # every block's gradient on its own, so that no block can hide in the
         # norm of the whole side
