@@ -14,13 +14,15 @@
 // stays on one block). A block of 512 takes two workgroups, each with 256 of
 // its output columns and all 512 k (128 VGPRs of B per lane); its A tiles are
 // 64 rows x 512 (64 KiB) in two stages. B is fetched before the first A tiles
-// (a block of 256 in natural layout through the whole, still empty LDS ring):
-// behind them it would wait for all of them, which doubled the start-up of a
-// workgroup that runs only 8 tiles. Row tiles of A (ROWS rows x the block's columns)
-// stream from HBM into an LDS ring of ST stages with direct-to-LDS loads, ST - 1
-// tiles in flight while one is multiplied; every wave reads the whole A tile
-// from LDS. An HBM stream needs on the order of 100 KiB in flight per CU, so
-// the ring holds several small tiles rather than two large ones.
+// (natural-layout B through the still empty LDS ring: one part for a block of
+// 256, two for a block of 512): behind them it would wait for all of them,
+// which doubled the start-up of a workgroup that runs only 8 tiles. Row tiles
+// of A (ROWS rows x the block's columns) stream from HBM into an LDS ring of ST
+// stages with direct-to-LDS buffer loads, ST - 1 tiles in flight while one is
+// multiplied; every wave reads the whole A tile from LDS, the fragments of the
+// next 16-deep step before the MFMAs of the current one. An HBM stream needs on
+// the order of 100 KiB in flight per CU, so the ring holds several small tiles
+// rather than two large ones.
 //
 // A tile in LDS: row r of b bf16 is b / 8 chunks of 16 bytes; chunk c sits at
 // slot r * b / 8 + (c ^ (r & 31)), so the 16 rows read by one pass of an
@@ -111,10 +113,7 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
   constexpr int STAGE = ROWS * KD * 2;             // bytes of one A tile in LDS
   constexpr int LOADS = ROWS * kCPR / kThreads;    // direct-to-LDS loads per thread per tile
   constexpr int MT = ROWS / 32;                    // 32-row MFMA tiles per wave and tile
-  constexpr int BROWS = STAGE / (kB * 2);          // rows of the slice of B_g one stage holds (NN fill)
-  constexpr int BLOADS = BROWS * (kB / 8) / kThreads;
   static_assert(ST >= 2 && ST <= 5 && LOADS * kThreads == ROWS * kCPR && ROWS % 32 == 0, "tile");
-  static_assert(KD % BROWS == 0 && BROWS % 16 == 0, "B in whole K steps per stage");
   static_assert(AKM || KD == 256, "row-contiguous A only for blocks of 256");
   extern __shared__ __align__(16) unsigned char lds[];   // ST A tiles
   const int tid = threadIdx.x, lane = tid & 63;
@@ -132,23 +131,35 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
   const int ncol = wave * 32 + nl;   // B column of this lane's operand fragments
   auto stage = [&](int i) { return lds + i * STAGE; };
 
-  // row tile t of A -> LDS stage st: lane `tid` of load i fills slot i * kThreads + tid
+  // row tile t of A -> LDS stage st: lane `tid` of load i fills slot i * kThreads + tid.
+  // Buffer loads (counted by vmcnt only, so the LDS reads of the K loop get
+  // exact lgkmcnt waits while tiles are in flight): the tile's first row goes
+  // in soffset, the lane's row and chunk in voffset; rows past M fall outside
+  // the buffer and load zeros (their results are not stored).
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Ag), (short)0,
+      (int)(AKM ? (long long)p.M * p.lda * 2 : (long long)KD * p.lda * 2), 0x00020000);
   auto issue = [&](int t, unsigned char* st) {
     const long long row0 = (long long)t * ROWS;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int s = i * kThreads + tid;
+      uint32_t vo, so;
       if constexpr (AKM) {
         const int r = s / kCPR;
         const int c = (s % kCPR) ^ (r & 31);
-        const long long row = min(row0 + r, (long long)p.M - 1);   // rows past M: loaded, not stored
-        dma16(Ag + row * p.lda + c * 8, st + (i * kThreads + wave * 64) * 16);
+        vo = (uint32_t)(((long long)r * p.lda + c * 8) * 2);
+        so = (uint32_t)(row0 * p.lda * 2);
       } else {
         constexpr int CPR = ROWS / 8;   // chunks per K-row of the tile
         const int k = s / CPR;
         const int c = (s % CPR) ^ (4 * (k & 3));
-        dma16(Ag + (long long)k * p.lda + row0 + c * 8, st + (i * kThreads + wave * 64) * 16);
+        vo = (uint32_t)(((long long)k * p.lda + c * 8) * 2);
+        so = (uint32_t)(row0 * 2);
       }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsa, (__attribute__((address_space(3))) void*)(st + (i * kThreads + wave * 64) * 16), 16, vo,
+          (int)so, 0, 0);
     }
   };
 
@@ -156,62 +167,45 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
   // A tiles: loads return in order, so B queued behind ST - 1 tiles of A would
   // wait for all of them before the first multiply could start.
   bf16x8 bq[kNKK];
-  // natural-layout B of a 256 block: the whole block (256 K-rows of 512 bytes)
-  // fits the empty LDS ring, so it arrives in one round trip
-  constexpr bool kRingB = !BKM && KD == kB && ST * STAGE >= KD * kB * 2;
+  // natural-layout B: the slice's K-rows (512 bytes each) go through the still
+  // empty LDS ring in as few parts as fit (one for a block of 256, two of 256
+  // K-rows for a block of 512), each part in one round trip
+  constexpr int kRingParts = (KD * kB * 2 + ST * STAGE - 1) / (ST * STAGE);
+  constexpr int kRingRows = KD / kRingParts;   // K-rows of B per part
+  static_assert(BKM || (KD % kRingParts == 0 && kRingRows % 16 == 0 && kRingRows * kB * 2 <= ST * STAGE),
+                "natural-layout B in whole 16-deep steps per part of the ring");
   if constexpr (BKM) {
 #pragma unroll
     for (int kk = 0; kk < kNKK; ++kk)
       bq[kk] = *reinterpret_cast<const bf16x8*>(Bg + (long long)ncol * p.ldb + 16 * kk + 8 * h);
-  } else if constexpr (kRingB) {
-    // K-row k of the block in the layout of a row-contiguous A tile (chunk c at
+  } else {
+    // K-row k of a part in the layout of a row-contiguous A tile (chunk c at
     // slot k (kB / 8) + (c ^ 4 (k & 3))), read back column-wise with the
     // transposing reads of frag_t
     constexpr int CPRB = kB / 8;
-    constexpr int RLOADS = KD * CPRB / kThreads;
+    constexpr int RLOADS = kRingRows * CPRB / kThreads;
+    static_assert(RLOADS * kThreads == kRingRows * CPRB, "whole loads per part");
 #pragma unroll
-    for (int i = 0; i < RLOADS; ++i) {
-      const int s = i * kThreads + tid;
-      const int k = s / CPRB;
-      const int c = (s % CPRB) ^ (4 * (k & 3));
-      dma16(Bg + (long long)k * p.ldb + c * 8, lds + (i * kThreads + wave * 64) * 16);
+    for (int part = 0; part < kRingParts; ++part) {
+#pragma unroll
+      for (int i = 0; i < RLOADS; ++i) {
+        const int s = i * kThreads + tid;
+        const int k = s / CPRB;
+        const int c = (s % CPRB) ^ (4 * (k & 3));
+        dma16(Bg + (long long)(part * kRingRows + k) * p.ldb + c * 8, lds + (i * kThreads + wave * 64) * 16);
+      }
+      wait_vmcnt<0>();
+      lds_barrier();
+#pragma unroll
+      for (int kk = 0; kk < kRingRows / 16; ++kk)
+        bq[part * (kRingRows / 16) + kk] = frag_t<kB>(lds, wave * 32, kk, lane);
+      lds_barrier();   // every wave has this part before the ring is reused
     }
-    wait_vmcnt<0>();
-    lds_barrier();
-#pragma unroll
-    for (int kk = 0; kk < kNKK; ++kk) bq[kk] = frag_t<kB>(lds, wave * 32, kk, lane);
-    lds_barrier();   // every wave has its B before the ring takes A tiles
   }
   // the first ST - 1 tiles of A
 #pragma unroll
   for (int i = 0; i < ST - 1; ++i)
     if (t0 + i < t1) issue(t0 + i, stage(i));
-  if constexpr (!BKM && !kRingB) {
-    // column ncol of the slice of B_g through the still free last stage,
-    // BROWS rows of it at a time in natural layout (row k = 512 bytes); the 32
-    // lanes of a read take 64 consecutive bytes of one row
-    const uint16_t* Bl = reinterpret_cast<const uint16_t*>(stage(ST - 1));
-#pragma unroll
-    for (int part = 0; part < KD / BROWS; ++part) {
-#pragma unroll
-      for (int i = 0; i < BLOADS; ++i) {
-        const int s = i * kThreads + tid;
-        const int k = part * BROWS + s / (kB / 8);
-        dma16(Bg + (long long)k * p.ldb + (s % (kB / 8)) * 8, stage(ST - 1) + (i * kThreads + wave * 64) * 16);
-      }
-      wait_vmcnt<0>();
-      lds_barrier();
-#pragma unroll
-      for (int kk = 0; kk < BROWS / 16; ++kk) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v[e] = __builtin_bit_cast(__bf16, Bl[(16 * kk + 8 * h + e) * kB + ncol]);
-        bq[part * (BROWS / 16) + kk] = v;
-      }
-      lds_barrier();   // every wave has read this part before the stage is reused
-    }
-  }
 
   const bool upper = h != 0;
   for (int t = t0; t < t1; ++t) {
@@ -226,24 +220,47 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < kNKK; ++kk) {
-      bf16x8 af[MT];
+    // A fragments of step kk + 1 are read before the MFMAs of step kk (two
+    // register sets), so the LDS latency of a step hides behind the multiplies
+    // of the one before instead of adding to them
+    // K-contiguous A: chunk 2 kk + h of row r = 32 mt + nl sits at byte
+    // r kCPR 16 + (((2 kk + h) ^ nl) << 4) = (nl kCPR 16 + ((h ^ nl) << 4)) ^
+    // (kk << 5) + mt 32 kCPR 16 (the XOR only permutes chunk bits below the
+    // row's base): one XOR per step. The base passes through an empty asm so
+    // that the per-step addresses are formed in the step, not hoisted out of
+    // the tile loop and held live.
+    uint32_t abase = (uint32_t)(nl * kCPR * 16 + ((h ^ nl) << 4));
+    asm volatile("" : "+v"(abase));
+    auto read_a = [&](bf16x8 (&af)[MT], int kk) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if constexpr (AKM) {
-          const int r = 32 * mt + nl;
-          const int c = 2 * kk + h;
-          af[mt] = *reinterpret_cast<const bf16x8*>(st + (r * kCPR + (c ^ (r & 31))) * 16);
+          af[mt] = *reinterpret_cast<const bf16x8*>(st + ((abase ^ (uint32_t)(kk << 5)) + mt * 32 * kCPR * 16));
         } else {
           af[mt] = frag_t<ROWS>(st, 32 * mt, kk, lane);
         }
       }
+    };
+    // the A fragments of step kk + 1 are read before the MFMAs of step kk (two
+    // register sets), so a step's LDS latency hides behind the multiplies of
+    // the step before instead of adding to them
+    bf16x8 af[2][MT];
+    read_a(af[0], 0);
+#pragma unroll
+    for (int kk = 0; kk < kNKK; ++kk) {
+      const int cb = kk & 1;
+      if (kk + 1 < kNKK) read_a(af[cb ^ 1], kk + 1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         // B first: the result is C^T, each lane holds four consecutive output
         // columns (8 q + 4 h .. + 3 of the wave's 32) of output row nl
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[kk], af[mt], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[kk], af[cb][mt], acc[mt], 0, 0, 0);
+      if (kk + 1 < kNKK) {
+        // the next step's reads go out first, then this step's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, AKM ? MT : 2 * MT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // epilogue: lanes l and l ^ 32 swap half of their column groups so that each
     // lane stores 8 consecutive columns (the lower lane q = 0, 2, the upper 1, 3)
@@ -300,6 +317,8 @@ bool block_regb_supported(const GemmBf16& p) {
   if (p.splits != 1 || p.b_i8 || p.M <= 0 || p.groups <= 0) return false;
   if (p.col_scale && (((uintptr_t)p.col_scale & 15) || p.c_gs % 4)) return false;
   if (p.lda % 8 || p.a_gs % 8 || p.ldc % 8 || p.c_gs % 8) return false;   // 16-byte rows
+  // A tiles come through a buffer resource per group: byte offsets below 2^31
+  if ((long long)(p.a_kmajor ? p.M : p.K) * p.lda * 2 >= (1LL << 31)) return false;
   if (p.ldb % 8 || p.ldb < p.N) return false;   // 16-byte rows of B either way (N = K)
   if (((uintptr_t)p.A | (uintptr_t)p.C | (uintptr_t)p.B) & 15) return false;
   return true;
