@@ -41,24 +41,42 @@ __global__ __launch_bounds__(kThreads) void unpack_skew_kernel(
   }
 }
 
-// Newton-Schulz start for N = (I - S)^{-1}, one workgroup per block: with
-// c = max_i sum_j |S[i][j]| (an upper bound of ||S||_2), X0 = a (I + S) =
-// a (I - S)^T with a = 2 / (2 + c^2). The residual R = I - (I - S) X0 is
-// symmetric with eigenvalues 1 - a (1 + s^2) for the singular values s <= c of
-// S, so ||R||_2 <= r = c^2 / (2 + c^2) < 1, and after j steps X <- X (2I - (I -
-// S) X) it is R^(2^j). iters[block] = the least j with r^(2^j) <= 2^-30
-// (0 when S = 0), at most jmax.
+// Newton-Schulz start for N = (I - S)^{-1}: with c = max_i sum_j |S[i][j]| (an
+// upper bound of ||S||_2), X0 = a (I + S) = a (I - S)^T with a = 2 / (2 + c^2).
+// The residual R = I - (I - S) X0 is symmetric with eigenvalues 1 - a (1 + s^2)
+// for the singular values s <= c of S, so ||R||_2 <= r = c^2 / (2 + c^2) < 1,
+// and after j steps X <- X (2I - (I - S) X) it is R^(2^j). iters[block] = the
+// least j with r^(2^j) <= 2^-30 (0 when S = 0), at most jmax.
+//
+// kNsParts workgroups per block: each finds c for the whole block (one thread
+// per row, each row summed in column order, 16-byte loads where the rows allow
+// them; the block is read from L2 by all but the first), then writes its share
+// of the rows of X0; the first also writes iters.
+constexpr int kNsParts = 8;
 __global__ __launch_bounds__(kThreads) void ns_init_kernel(const float* __restrict__ S, int b,
                                                            float* __restrict__ X0,
                                                            int32_t* __restrict__ iters, int jmax) {
   __shared__ float red[kThreads];
+  const int blk = blockIdx.x / kNsParts, part = blockIdx.x - blk * kNsParts;
   const long long bb = (long long)b * b;
-  const float* Sg = S + blockIdx.x * bb;
-  float* Xg = X0 + blockIdx.x * bb;
+  const float* Sg = S + blk * bb;
+  float* Xg = X0 + blk * bb;
+  const bool vec = (b % 4) == 0;   // then every row starts on a 16-byte boundary
   float mx = 0.0f;
   for (int r = threadIdx.x; r < b; r += kThreads) {
+    const float* row = Sg + (long long)r * b;
     float sum = 0.0f;
-    for (int c = 0; c < b; ++c) sum += fabsf(Sg[(long long)r * b + c]);
+    if (vec) {
+      for (int c = 0; c < b; c += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(row + c);
+        sum += fabsf(v.x);
+        sum += fabsf(v.y);
+        sum += fabsf(v.z);
+        sum += fabsf(v.w);
+      }
+    } else {
+      for (int c = 0; c < b; ++c) sum += fabsf(row[c]);
+    }
     mx = fmaxf(mx, sum);
   }
   red[threadIdx.x] = mx;
@@ -69,11 +87,12 @@ __global__ __launch_bounds__(kThreads) void ns_init_kernel(const float* __restri
   }
   const double c = red[0];
   const float a = (float)(2.0 / (2.0 + c * c));
-  for (long long e = threadIdx.x; e < bb; e += kThreads) {
+  const int r0 = (int)((long long)b * part / kNsParts), r1 = (int)((long long)b * (part + 1) / kNsParts);
+  for (long long e = (long long)r0 * b + threadIdx.x; e < (long long)r1 * b; e += kThreads) {
     const int r = (int)(e / b), col = (int)(e - (long long)r * b);
     Xg[e] = a * ((r == col ? 1.0f : 0.0f) + Sg[e]);
   }
-  if (threadIdx.x == 0) {
+  if (part == 0 && threadIdx.x == 0) {
     int j = 0;
     if (c > 0.0) {
       const double rho = c * c / (2.0 + c * c);
@@ -81,24 +100,28 @@ __global__ __launch_bounds__(kThreads) void ns_init_kernel(const float* __restri
       const double need = 30.0 * 0.6931471805599453 / -log(rho);
       while (j < jmax && ldexp(1.0, j) < need) ++j;
     }
-    iters[blockIdx.x] = j;
+    iters[blk] = j;
   }
 }
 
 // After the iterations, block g's N sits in X0 for an even iteration count and
 // in X1 for an odd one: N_out = N and Q = (I + S)(I - S)^{-1} = 2 N - I.
+// Elementwise over all blocks of the run.
 __global__ __launch_bounds__(kThreads) void ns_final_kernel(const float* __restrict__ X0,
                                                             const float* __restrict__ X1,
                                                             const int32_t* __restrict__ iters,
-                                                            int b, float* __restrict__ N,
+                                                            int b, long long total,
+                                                            float* __restrict__ N,
                                                             float* __restrict__ Q) {
   const long long bb = (long long)b * b;
-  const float* src = ((iters[blockIdx.x] & 1) ? X1 : X0) + blockIdx.x * bb;
-  for (long long e = threadIdx.x; e < bb; e += kThreads) {
-    const int r = (int)(e / b), col = (int)(e - (long long)r * b);
-    const float v = src[e];
-    N[blockIdx.x * bb + e] = v;
-    Q[blockIdx.x * bb + e] = 2.0f * v - (r == col ? 1.0f : 0.0f);
+  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total;
+       e += (long long)gridDim.x * kThreads) {
+    const long long g = e / bb;
+    const long long w = e - g * bb;
+    const int r = (int)(w / b), col = (int)(w - (long long)r * b);
+    const float v = ((iters[g] & 1) ? X1 : X0)[e];
+    N[e] = v;
+    Q[e] = 2.0f * v - (r == col ? 1.0f : 0.0f);
   }
 }
 
@@ -219,14 +242,16 @@ hipError_t launch_unpack_skew(const float* theta, const Seg& g, float* S, float*
 hipError_t launch_ns_init(const float* S, int b, int count, float* X0, int32_t* iters, int jmax,
                           hipStream_t s) {
   if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ns_init_kernel, dim3(count), dim3(kThreads), 0, s, S, b, X0, iters, jmax);
+  hipLaunchKernelGGL(ns_init_kernel, dim3(count * kNsParts), dim3(kThreads), 0, s, S, b, X0, iters, jmax);
   return hipGetLastError();
 }
 
 hipError_t launch_ns_final(const float* X0, const float* X1, const int32_t* iters, int b, int count,
                            float* N, float* Q, hipStream_t s) {
   if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ns_final_kernel, dim3(count), dim3(kThreads), 0, s, X0, X1, iters, b, N, Q);
+  const long long total = (long long)b * b * count;
+  hipLaunchKernelGGL(ns_final_kernel, dim3(grid1d(total)), dim3(kThreads), 0, s, X0, X1, iters, b, total, N,
+                     Q);
   return hipGetLastError();
 }
 
