@@ -871,83 +871,122 @@ poetx_status check_build_item(const BuildItem& it, size_t ws_bytes) {
   return POETX_OK;
 }
 
-// Q of one build item by Paterson-Stockmeyer (ps_step): S from the packed
-// parameters, the powers S^2 .. S^s, then the recurrence H <- B_i + S^s H with
-// each B_i a linear combination of I, S .. S^(s-1); fp32 throughout, Q cast to
-// the activation dtype at the end.
-poetx_status build_ps_item(const BuildItem& it, hipStream_t s) {
-  const poetx_plan* pl = it.pl;
-  const int d = pl->k + 1;
+// Q by Paterson-Stockmeyer (ps_step) for build items that share one Neumann
+// order: S from the packed parameters, the powers S^2 .. S^s, then the
+// recurrence H <- B_i + S^s H with each B_i a linear combination of I, S ..
+// S^(s-1); fp32 throughout, Q cast to the activation dtype at the end. Every
+// product is one launch over all runs of a block size across the items (one
+// side of one layer has too few blocks to fill the chip); the unpacks, linear
+// combinations and casts stay per run.
+struct PsRun {
+  const BuildItem* it;
+  Seg g;
+  std::vector<float*> P;   // P[j] = S^j, j = 1 .. s (at the run's first block)
+  float *B, *H0, *H1, *Q;
+};
+poetx_status build_ps_group(const BuildItem* items, const std::vector<int>& idx, hipStream_t s) {
+  if (idx.empty()) return POETX_OK;
+  const poetx_plan* pl0 = items[idx[0]].pl;
+  const int k = pl0->k, d = k + 1;
   const int st = ps_step(d);
   const int r = d / st;
-  float *S, *H0, *H1, *pw;
-  layout_build(pl, it.ws, &S, &H0, &H1, nullptr, nullptr, nullptr, &pw);
-  const long long ne = std::max(pl->nelem[0], pl->nelem[1]);
-  // P[j] = S^j for j = 1 .. s (P[0] unused: I enters through the diagonal)
-  std::vector<float*> P(st + 1, nullptr);
-  P[1] = S;
-  for (int j = 2; j <= st; ++j) P[j] = pw + (j - 2) * ne;
-  float* B = pw + (st - 1) * ne;
-  auto c = [&](int j) { return j <= d ? coef(j, pl->k) : 0.0f; };
-  for (const Seg& g : pl->segs[it.side]) {
-    const int b = g.b;
-    const long long o = g.q_off;
-    HIP_TRY(poetx::launch_unpack_skew(it.theta, g, S, nullptr, 0.0f, s));
-    // powers up to S^s (up to S^d when d < s never happens: s <= d)
-    const int top = r == 0 ? d : st;
-    for (int j = 2; j <= top; ++j) {
-      poetx_status e = chain_gemm(g, P[j - 1], S, P[j], nullptr, nullptr, 1.0f, 0.0f, s);
+  auto c = [&](int j) { return j <= d ? coef(j, k) : 0.0f; };
+  std::vector<PsRun> runs;
+  for (int i : idx) {
+    const BuildItem& it = items[i];
+    float *S, *H0, *H1, *pw;
+    layout_build(it.pl, it.ws, &S, &H0, &H1, nullptr, nullptr, nullptr, &pw);
+    const long long ne = std::max(it.pl->nelem[0], it.pl->nelem[1]);
+    for (const Seg& g : it.pl->segs[it.side]) {
+      const long long o = g.q_off;
+      PsRun pr{&it, g, std::vector<float*>(st + 1, nullptr), pw + (st - 1) * ne + o, H0 + o, H1 + o,
+               it.Q + o};
+      pr.P[1] = S + o;
+      for (int j = 2; j <= st; ++j) pr.P[j] = pw + (j - 2) * ne + o;
+      runs.push_back(std::move(pr));
+      // the unpack takes the side's base pointers and applies the run's offsets
+      HIP_TRY(poetx::launch_unpack_skew(it.theta, g, S, nullptr, 0.0f, s));
+    }
+  }
+  std::vector<int> sizes;
+  for (const PsRun& pr : runs)
+    if (std::find(sizes.begin(), sizes.end(), pr.g.b) == sizes.end()) sizes.push_back(pr.g.b);
+  // C = A B (+ Cin) for every run of each block size: one launch per size
+  auto products = [&](auto pick) -> poetx_status {
+    for (int b : sizes) {
+      std::vector<poetx::GemmF32Run> v;
+      for (PsRun& pr : runs)
+        if (pr.g.b == b) {
+          const float *A, *Bm, *Cin;
+          float* C;
+          pick(pr, A, Bm, C, Cin);
+          v.push_back(poetx::GemmF32Run{A, Bm, C, Cin, pr.g.count, nullptr});
+        }
+      const bool acc = v[0].Cin != nullptr;
+      poetx_status e = f32_runs(b, b, 1, 1, b, v, acc ? 1.0f : 0.0f, s);
       if (e != POETX_OK) return e;
     }
-    // B_i = c_{is} I + sum_{0<l<s} c_{is+l} S^l; with fold, also + c_d S^s
-    auto make_b = [&](int i, float* out, bool fold_top) -> poetx_status {
-      poetx::LinComb lc{};
-      lc.diag = c(i * st);
-      for (int l = 1; l < st; ++l) {
-        lc.mats[lc.n] = P[l] + o;
-        lc.coef[lc.n++] = c(i * st + l);
-      }
-      if (fold_top) {
-        lc.mats[lc.n] = P[st] + o;
-        lc.coef[lc.n++] = c(d);
-      }
-      HIP_TRY(poetx::launch_lincomb(lc, out + o, b, g.count, s));
-      return POETX_OK;
-    };
-    poetx_status e;
-    if (r == 0) {   // degree below s: Q = sum_j c_j S^j directly
+    return POETX_OK;
+  };
+  // B_i = c_{is} I + sum_{0<l<s} c_{is+l} S^l; with fold, also + c_d S^s
+  auto make_b = [&](const PsRun& pr, int i, float* out, bool fold_top) -> poetx_status {
+    poetx::LinComb lc{};
+    lc.diag = c(i * st);
+    for (int l = 1; l < st; ++l) {
+      lc.mats[lc.n] = pr.P[l];
+      lc.coef[lc.n++] = c(i * st + l);
+    }
+    if (fold_top) {
+      lc.mats[lc.n] = pr.P[st];
+      lc.coef[lc.n++] = c(d);
+    }
+    HIP_TRY(poetx::launch_lincomb(lc, out, pr.g.b, pr.g.count, s));
+    return POETX_OK;
+  };
+  poetx_status e;
+  // powers up to S^s (up to S^d when r = 0, which needs d < s: never, s <= d)
+  const int top = r == 0 ? d : st;
+  for (int j = 2; j <= top; ++j)
+    if ((e = products([&](PsRun& pr, const float*& A, const float*& Bm, float*& C, const float*& Cin) {
+           A = pr.P[j - 1]; Bm = pr.P[1]; C = pr.P[j]; Cin = nullptr;
+         })) != POETX_OK)
+      return e;
+  if (r == 0) {   // degree below s: Q = sum_j c_j S^j directly
+    for (const PsRun& pr : runs) {
       poetx::LinComb lc{};
       lc.diag = c(0);
       for (int j = 1; j <= d; ++j) {
-        lc.mats[lc.n] = P[j] + o;
+        lc.mats[lc.n] = pr.P[j];
         lc.coef[lc.n++] = c(j);
       }
-      HIP_TRY(poetx::launch_lincomb(lc, it.Q + o, b, g.count, s));
-    } else {
-      // H = B_r, or H = B_{r-1} + c_d S^s when B_r = c_d I
-      int i = r;
-      float* H = H0;
-      float* Hn = H1;
-      if (d % st == 0) {
-        --i;
-        if ((e = make_b(i, H, true)) != POETX_OK) return e;
-      } else {
-        if ((e = make_b(i, H, false)) != POETX_OK) return e;
-      }
-      for (--i; i >= 0; --i) {
-        if ((e = make_b(i, B, false)) != POETX_OK) return e;
-        float* dst = i == 0 ? it.Q : Hn;
-        if ((e = chain_gemm(g, P[st], H, dst, B, nullptr, 1.0f, 1.0f, s)) != POETX_OK) return e;
-        std::swap(H, Hn);
-      }
-      if (d % st == 0 && r == 1) {   // no product at all: H is Q
-        HIP_TRY(poetx::launch_lincomb(poetx::LinComb{{H + o}, {1.0f}, 1, 0.0f}, it.Q + o, b, g.count, s));
-      }
+      HIP_TRY(poetx::launch_lincomb(lc, pr.Q, pr.g.b, pr.g.count, s));
     }
-    if (it.Qact)
-      HIP_TRY(poetx::launch_cast(it.Q + o, static_cast<char*>(it.Qact) + (size_t)elsize(pl) * o,
-                                 (long long)b * b * g.count, pl->dtype == POETX_BF16, s));
+  } else {
+    // H = B_r, or H = B_{r-1} + c_d S^s when B_r = c_d I
+    int i = r;
+    bool h0 = true;   // H in H0 (else in H1)
+    if (d % st == 0) --i;
+    for (const PsRun& pr : runs)
+      if ((e = make_b(pr, i, pr.H0, d % st == 0)) != POETX_OK) return e;
+    for (--i; i >= 0; --i) {
+      for (const PsRun& pr : runs)
+        if ((e = make_b(pr, i, pr.B, false)) != POETX_OK) return e;
+      const bool last = i == 0;
+      if ((e = products([&](PsRun& pr, const float*& A, const float*& Bm, float*& C, const float*& Cin) {
+             A = pr.P[st]; Bm = h0 ? pr.H0 : pr.H1; C = last ? pr.Q : (h0 ? pr.H1 : pr.H0); Cin = pr.B;
+           })) != POETX_OK)
+        return e;
+      h0 = !h0;
+    }
+    if (d % st == 0 && r == 1)   // no product at all: H is Q
+      for (const PsRun& pr : runs)
+        HIP_TRY(poetx::launch_lincomb(poetx::LinComb{{h0 ? pr.H0 : pr.H1}, {1.0f}, 1, 0.0f}, pr.Q, pr.g.b,
+                                      pr.g.count, s));
   }
+  for (const PsRun& pr : runs)
+    if (pr.it->Qact)
+      HIP_TRY(poetx::launch_cast(pr.Q, static_cast<char*>(pr.it->Qact) + (size_t)elsize(pr.it->pl) * pr.g.q_off,
+                                 (long long)pr.g.b * pr.g.b * pr.g.count, pr.it->pl->dtype == POETX_BF16, s));
   return POETX_OK;
 }
 
@@ -957,7 +996,7 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
   poetx::TriBatch ub{};
   poetx::ChainBatch cb{};
   std::vector<ExactRun> exact;
-  std::vector<int> exact_items;
+  std::vector<int> exact_items, ps_items;
   int kk = -1;
   auto flush = [&]() -> poetx_status {
     HIP_TRY(poetx::launch_unpack_batch(ub, s));
@@ -982,9 +1021,8 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
       }
       continue;
     }
-    if (build_ps(pl)) {   // Paterson-Stockmeyer on batched fp32 products
-      poetx_status st = build_ps_item(it, s);
-      if (st != POETX_OK) return st;
+    if (build_ps(pl)) {   // Paterson-Stockmeyer: batched after the loop
+      ps_items.push_back(i);
       continue;
     }
     if (kk != -1 && kk != pl->k) {   // one Neumann order per chain launch
@@ -1032,7 +1070,16 @@ poetx_status build_items(const BuildItem* items, int count, hipStream_t s) {
     }
   }
   poetx_status st = flush();
-  if (st != POETX_OK || exact.empty()) return st;
+  if (st != POETX_OK) return st;
+  // Paterson-Stockmeyer items, one batch per Neumann order
+  while (!ps_items.empty()) {
+    const int k = items[ps_items[0]].pl->k;
+    std::vector<int> grp, rest;
+    for (int i : ps_items) (items[i].pl->k == k ? grp : rest).push_back(i);
+    if ((st = build_ps_group(items, grp, s)) != POETX_OK) return st;
+    ps_items.swap(rest);
+  }
+  if (exact.empty()) return POETX_OK;
   if ((st = exact_cayley_runs(exact, s)) != POETX_OK) return st;
   for (size_t i = 0; i < exact.size(); ++i) {
     const BuildItem& it = items[exact_items[i]];
