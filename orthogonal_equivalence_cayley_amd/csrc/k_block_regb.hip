@@ -133,33 +133,33 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
 
   // row tile t of A -> LDS stage st: lane `tid` of load i fills slot i * kThreads + tid.
   // Buffer loads (counted by vmcnt only, so the LDS reads of the K loop get
-  // exact lgkmcnt waits while tiles are in flight): the tile's first row goes
-  // in soffset, the lane's row and chunk in voffset; rows past M fall outside
-  // the buffer and load zeros (their results are not stored).
-  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Ag), (short)0,
-      (int)(AKM ? (long long)p.M * p.lda * 2 : (long long)KD * p.lda * 2), 0x00020000);
+  // exact lgkmcnt waits while tiles are in flight) through a resource that
+  // starts at the tile (its base and size in scalar registers, so offsets stay
+  // small at any M); rows past M fall outside it and load zeros (their
+  // results are not stored).
   auto issue = [&](int t, unsigned char* st) {
     const long long row0 = (long long)t * ROWS;
+    const uint16_t* base = AKM ? Ag + row0 * p.lda : Ag + row0;
+    const long long nrec = AKM ? (long long)min((long long)ROWS, p.M - row0) * p.lda * 2
+                               : (long long)KD * p.lda * 2 - row0 * 2;
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base), (short)0, (int)min(nrec, (long long)INT32_MAX), 0x00020000);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int s = i * kThreads + tid;
-      uint32_t vo, so;
+      uint32_t vo;
       if constexpr (AKM) {
         const int r = s / kCPR;
         const int c = (s % kCPR) ^ (r & 31);
         vo = (uint32_t)(((long long)r * p.lda + c * 8) * 2);
-        so = (uint32_t)(row0 * p.lda * 2);
       } else {
         constexpr int CPR = ROWS / 8;   // chunks per K-row of the tile
         const int k = s / CPR;
         const int c = (s % CPR) ^ (4 * (k & 3));
         vo = (uint32_t)(((long long)k * p.lda + c * 8) * 2);
-        so = (uint32_t)(row0 * 2);
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsa, (__attribute__((address_space(3))) void*)(st + (i * kThreads + wave * 64) * 16), 16, vo,
-          (int)so, 0, 0);
+          rsa, (__attribute__((address_space(3))) void*)(st + (i * kThreads + wave * 64) * 16), 16, vo, 0, 0, 0);
     }
   };
 
@@ -317,8 +317,8 @@ bool block_regb_supported(const GemmBf16& p) {
   if (p.splits != 1 || p.b_i8 || p.M <= 0 || p.groups <= 0) return false;
   if (p.col_scale && (((uintptr_t)p.col_scale & 15) || p.c_gs % 4)) return false;
   if (p.lda % 8 || p.a_gs % 8 || p.ldc % 8 || p.c_gs % 8) return false;   // 16-byte rows
-  // A tiles come through a buffer resource per group: byte offsets below 2^31
-  if ((long long)(p.a_kmajor ? p.M : p.K) * p.lda * 2 >= (1LL << 31)) return false;
+  // a buffer resource per A tile: one tile's byte offsets below 2^31
+  if ((long long)(p.a_kmajor ? kRows : p.K) * p.lda * 2 >= (1LL << 31)) return false;
   if (p.ldb % 8 || p.ldb < p.N) return false;   // 16-byte rows of B either way (N = K)
   if (((uintptr_t)p.A | (uintptr_t)p.C | (uintptr_t)p.B) & 15) return false;
   return true;

@@ -107,3 +107,40 @@ def test_int8_weight_full_size(weight):
     _check("G_X", to_np(G_X), ref["G_X"], TOL_BF16)
     _check("g_theta_R", to_np(gR), ref["g_theta_R"], TOL_BF16)
     _check("g_theta_P", to_np(gP), ref["g_theta_P"], TOL_BF16)
+
+
+def test_activations_past_2gib_rows_sampled():
+    """A layer at 2.2 M tokens, so that every [T, 512] bf16 activation is larger
+    than 2 GiB (row 2^21 starts at byte 2^31): the block products address
+    their A tiles through one buffer resource per tile, the frozen-weight
+    product leaves its 32-bit-offset kernel for the general one. Every output
+    row depends only on its own input row (and Q), so rows on both sides of
+    the 2 GiB line and at both ends are checked against the float64 oracle run
+    on those rows alone; the parameter gradients (sums over all tokens) are
+    not compared here."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from gpu_util import make_layer, to_np
+    T, k = 2_200_000, 4
+    small = workloads.small_case(512, 512, (256, 256), (256, 256), T=1, seed=77, dtype="bf16",
+                                 theta_std=0.01)
+    layer = make_layer(small, k, "bf16", weight="dense_t")
+    layer.build()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2024)
+    X = torch.randn((T, 512), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    G = torch.randn((T, 512), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    log(f"T={T}: X {X.numel() * 2 / 2**30:.2f} GiB")
+    Y = layer.forward(X, save=True)
+    G_X, _, _ = layer.backward(X, G)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 777, 2**21 - 2, 2**21 - 1, 2**21, 2**21 + 1, 2**21 + 12345, T - 2, T - 1])
+    idx = torch.from_numpy(rows).cuda()
+    sub = dataclasses.replace(small, X=to_np(X[idx]).astype(np.float32), G_Y=to_np(G[idx]).astype(np.float32))
+    ref = oracle.layer_reference(sub, k, backward_pass=True)
+    _check("Wa rows", to_np(layer.Wa[idx]), ref["Wa"], TOL_BF16)
+    _check("Y rows", to_np(Y[idx]), ref["Y"], TOL_BF16)
+    _check("G_X rows", to_np(G_X[idx]), ref["G_X"], TOL_BF16)
