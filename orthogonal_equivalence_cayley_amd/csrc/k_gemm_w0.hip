@@ -30,7 +30,8 @@
 //    {2048, 5632} x {2048, 5632} shapes than all waves loading, same bits.
 //
 // Requirements (w0_pipe_supported): M, N multiples of 256, K of 64, 16-byte
-// rows, each operand below 2 GiB (32-bit offsets), one group, no split.
+// rows, 256 rows of each operand below 2 GiB (32-bit offsets within a tile's
+// buffer resource), one group, no split.
 #include <type_traits>
 
 #include "poetx_internal.h"
@@ -142,10 +143,12 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
     n0 = (in / gsz) * kTile;
   };
 
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(p.A), (short)0, (int)((long long)p.M * p.lda * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(p.B), (short)0, (int)((long long)p.N * p.ldb * 2), 0x00020000);
+  // each load goes through a buffer resource that starts at its tile's first
+  // row (base and size in scalar registers), so offsets stay below one tile's
+  // 256 rows at any M and N
+  const uint16_t* const pa = static_cast<const uint16_t*>(p.A);
+  const uint16_t* const pb = static_cast<const uint16_t*>(p.B);
+  const int tra = (int)(256LL * p.lda * 2), trb = (int)(256LL * p.ldb * 2);
   const int g = tid & 255;   // thread index within waves 0-3 (loaders)
   const uint32_t va = Ld::lane_offset(g, p.lda), vb = Ld::lane_offset(g, p.ldb);
   const int nk = p.K / KB;
@@ -163,14 +166,18 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
     origin(ti, m0, n0);
     unsigned char* st = lds + buf * STAGE + op * Op::BYTES + (wave & 3) * 64 * 16;
     if (op == 0) {
-      const uint32_t ka = (uint32_t)(((long long)m0 * p.lda + (long long)kt * KB) * 2);
+      const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(pa + (long long)m0 * p.lda), (short)0, tra, 0x00020000);
+      const uint32_t ka = (uint32_t)(kt * KB * 2);
 #pragma unroll
       for (int i = i0; i < i1; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, (__attribute__((address_space(3))) void*)(st + i * 256 * 16), 16, va,
             (int)(ka + (uint32_t)(i * Ld::RPL * p.lda * 2)), 0, 0);
     } else {
-      const uint32_t kb = (uint32_t)(((long long)n0 * p.ldb + (long long)kt * KB) * 2);
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(pb + (long long)n0 * p.ldb), (short)0, trb, 0x00020000);
+      const uint32_t kb = (uint32_t)(kt * KB * 2);
 #pragma unroll
       for (int i = i0; i < i1; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -324,7 +331,8 @@ bool w0_pipe_supported(const GemmBf16& p) {
   if (p.groups != 1 || p.splits != 1) return false;
   if (p.M <= 0 || p.N <= 0 || p.M % kTile || p.N % kTile || p.K <= 0 || p.K % kKB) return false;
   if (p.lda % 8 || p.ldb % 8 || p.ldc % 8 || p.lda < p.K || p.ldb < p.K || p.ldc < p.N) return false;
-  if ((long long)p.M * p.lda * 2 >= (1LL << 31) || (long long)p.N * p.ldb * 2 >= (1LL << 31)) return false;
+  // one tile's 256 rows of either operand within 32-bit buffer offsets
+  if (256LL * p.lda * 2 >= (1LL << 31) || 256LL * p.ldb * 2 >= (1LL << 31)) return false;
   if (((uintptr_t)p.A | (uintptr_t)p.B | (uintptr_t)p.C) & 15) return false;
   return true;
 }

@@ -110,10 +110,10 @@ def test_int8_weight_full_size(weight):
 
 
 def test_activations_past_2gib_rows_sampled():
-    """A layer at 2.2 M tokens, so that every [T, 512] bf16 activation is larger
-    than 2 GiB (row 2^21 starts at byte 2^31): the block products address
-    their A tiles through one buffer resource per tile, the frozen-weight
-    product leaves its 32-bit-offset kernel for the general one. Every output
+    """A layer at 2.2 M tokens (8593 tiles of 256), so that every [T, 512] bf16
+    activation is larger than 2 GiB (row 2^21 starts at byte 2^31): the block
+    products and the frozen-weight products address their tiles through one
+    buffer resource per tile. Every output
     row depends only on its own input row (and Q), so rows on both sides of
     the 2 GiB line and at both ends are checked against the float64 oracle run
     on those rows alone; the parameter gradients (sums over all tokens) are
@@ -124,7 +124,7 @@ def test_activations_past_2gib_rows_sampled():
     import torch
 
     from gpu_util import make_layer, to_np
-    T, k = 2_200_000, 4
+    T, k = 8593 * 256, 4
     small = workloads.small_case(512, 512, (256, 256), (256, 256), T=1, seed=77, dtype="bf16",
                                  theta_std=0.01)
     layer = make_layer(small, k, "bf16", weight="dense_t")
