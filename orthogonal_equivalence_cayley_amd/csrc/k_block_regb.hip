@@ -220,9 +220,6 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
-    // A fragments of step kk + 1 are read before the MFMAs of step kk (two
-    // register sets), so the LDS latency of a step hides behind the multiplies
-    // of the one before instead of adding to them
     // K-contiguous A: chunk 2 kk + h of row r = 32 mt + nl sits at byte
     // r kCPR 16 + (((2 kk + h) ^ nl) << 4) = (nl kCPR 16 + ((h ^ nl) << 4)) ^
     // (kk << 5) + mt 32 kCPR 16 (the XOR only permutes chunk bits below the
@@ -256,7 +253,9 @@ void block_regb_kernel(GemmBf16 p, int tiles_per_group, int wpg, int per_wg) {
         // columns (8 q + 4 h .. + 3 of the wave's 32) of output row nl
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[kk], af[cb][mt], acc[mt], 0, 0, 0);
       if (kk + 1 < kNKK) {
-        // the next step's reads go out first, then this step's MFMAs
+        // one scheduling region per step: the next step's reads and this
+        // step's MFMAs (the reads are not hoisted further ahead, where their
+        // registers would have to stay live)
         __builtin_amdgcn_sched_group_barrier(0x100, AKM ? MT : 2 * MT, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
         __builtin_amdgcn_sched_barrier(0);
