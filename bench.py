@@ -392,15 +392,15 @@ def main() -> int:
     # With the weight kept beside its transpose (dense or INT8; the default
     # here) the backward reads it K-contiguous: the NT kernel as well.
     nt_bwd = folded_t or (not args.fold and w.dtype == "bf16")
-    # dense NT products on whole 256 x 256 tiles with at least one tile per CU
-    # run the dedicated frozen-weight kernel (k_gemm_w0.hip)
-    pipe = (w.dtype == "bf16" and not args.xq and T % 256 == 0 and
+    # NT products on whole 256 x 256 tiles with at least one tile per CU run the
+    # dedicated frozen-weight kernel (k_gemm_w0.hip); an INT8 weight (--xq) is
+    # widened exactly to bf16 first (a pass inside the same stage) and takes
+    # the same kernels, its row scales applied in the forward's epilogue
+    pipe = (w.dtype == "bf16" and T % 256 == 0 and
             all(sp.m % 256 == 0 and sp.n % 256 == 0 and (T // 256) * (min(sp.m, sp.n) // 256) >= 256
                 for sp in w.layers))
     nt_name = "w0_gemm_nt_pipe" if pipe else "w0_gemm_nt_lds"
     stage_kernel = {"w0_fwd": nt_name, "w0_bwd": nt_name if nt_bwd else "w0_gemm_nn_lds"}
-    if args.xq:
-        stage_kernel = {k: v.replace("w0_", "w0q_") for k, v in stage_kernel.items()}
     per_kernel = {}
     for st, kname in stage_kernel.items():
         ms_s, n_s = w0[st]

@@ -263,9 +263,10 @@ poetx_status poetx_build_orth_batch(int32_t count, const poetx_plan* const* plan
  * forming R W0 P. Stages: gather X by pi_P, blocks of P, product with Wt,
  * blocks of R, scatter by pi_R.
  *   X        device [T, n] (dtype)       Wt  device [m, n] from poetx_permute_weight,
- *            or for INT8 plans the poetx_quantize_weight layout: the product
- *            converts q to bf16 exactly on its way into LDS and applies s to the
- *            fp32 accumulators of each output column
+ *            or for INT8 plans the poetx_quantize_weight layout: each call
+ *            widens q exactly to bf16 in its workspace (m n 2 bytes of it) and
+ *            the product applies s to the fp32 accumulators of each output
+ *            column
  *   pi_R, pi_P device int32              Q_R, Q_P device block arrays in the plan dtype
  *   Y        device [T, m] (dtype)
  *   Wa_saved device [T, m] (dtype) or NULL: the output of the Wt product, the

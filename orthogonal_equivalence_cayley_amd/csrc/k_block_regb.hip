@@ -313,7 +313,7 @@ bool block_regb_supported(const GemmBf16& p) {
   // row-contiguous A (the transposed weight fold): whole tiles, K-contiguous Q,
   // no column scale
   if (!p.a_kmajor && (p.M % kRowsT || !p.b_kmajor || p.col_scale)) return false;
-  if (p.splits != 1 || p.b_i8 || p.M <= 0 || p.groups <= 0) return false;
+  if (p.splits != 1 || p.M <= 0 || p.groups <= 0) return false;
   if (p.col_scale && (((uintptr_t)p.col_scale & 15) || p.c_gs % 4)) return false;
   if (p.lda % 8 || p.a_gs % 8 || p.ldc % 8 || p.c_gs % 8) return false;   // 16-byte rows
   // a buffer resource per A tile: one tile's byte offsets below 2^31

@@ -270,9 +270,8 @@ hipError_t launch_gemm_bf16(const GemmBf16& p, hipStream_t s) {
   // multiple of 64, partial tiles of row-contiguous operands) the kernels here
   if (big && w0_pipe_supported(p)) return launch_w0_pipe(p, s);
   if (gemm_lds_supported(p, big ? 256 : 128, big ? 256 : 128)) return launch_gemm_lds(p, big, s);
-  // an int8 operand exists only on the pipelined kernels; a column scale is
-  // applied by a separate pass here (one more rounding of the bf16 output)
-  if (p.b_i8) return hipErrorInvalidValue;
+  // a column scale is applied by a separate pass here (one more rounding of
+  // the bf16 output)
   if (p.col_scale && (p.out_f32 || p.c_gs != p.N)) return hipErrorInvalidValue;
   const hipError_t e = big ? dispatch<256, 256, 128, 128>(p, s) : dispatch<128, 128, 64, 64>(p, s);
   if (e != hipSuccess || !p.col_scale) return e;

@@ -166,76 +166,6 @@ struct Tile<R, NT, KB, false> {
   }
 };
 
-// ---- int8 operand (a frozen weight stored as INT8): loaded through registers,
-// 16 values per 16-byte load, converted exactly to bf16 and written to LDS in
-// the layout of KTile (K-contiguous, KMAJ) or MTile (row-contiguous), so the
-// fragment reads and MFMAs are those of the bf16 operand.
-__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>((lo >> (8 * e)) & 0xff)));
-    r[4 + e] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>((hi >> (8 * e)) & 0xff)));
-  }
-  return r;
-}
-
-template <int R, int NT, int KB, bool KMAJ>
-struct QTile {
-  static constexpr int CH = R * KB / 16;   // 16-byte int8 chunks per stage
-  static constexpr int L = CH / NT;        // loads per thread per stage
-  static constexpr int BYTES = R * KB * 2; // bf16 in LDS
-  static_assert(CH % NT == 0, "whole loads per thread");
-  static_assert(KMAJ || R >= 128, "the row-contiguous layout of MTile needs R >= 128");
-  const int8_t* src[L];
-  uint4 reg[L];
-  __device__ __forceinline__ void init(const int8_t* base, long long ld, int rc0, int rows) {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int s = i * NT + threadIdx.x;
-      if (KMAJ) {
-        const int r = s / (KB / 16), q = s % (KB / 16);
-        src[i] = base + (long long)min(rc0 + r, rows - 1) * ld + q * 16;
-      } else {
-        const int k = s / (R / 16), q = s % (R / 16);
-        src[i] = base + (long long)k * ld + rc0 + q * 16;
-      }
-    }
-  }
-  __device__ __forceinline__ void load(int k0, long long ld) {
-#pragma unroll
-    for (int i = 0; i < L; ++i)
-      reg[i] = *reinterpret_cast<const uint4*>(KMAJ ? src[i] + k0 : src[i] + (long long)k0 * ld);
-  }
-  __device__ __forceinline__ void commit(unsigned char* st) const {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int s = i * NT + threadIdx.x;
-      const bf16x8 c0 = i8x8_to_bf16(reg[i].x, reg[i].y);
-      const bf16x8 c1 = i8x8_to_bf16(reg[i].z, reg[i].w);
-      int slot0, slot1;
-      if (KMAJ) {
-        constexpr int CPR = KB / 8, RPB = 256 / (KB * 2);
-        const int r = s / (KB / 16), q = s % (KB / 16);
-        const int sw = (r / RPB) % CPR;
-        slot0 = r * CPR + ((2 * q) ^ sw);
-        slot1 = r * CPR + ((2 * q + 1) ^ sw);
-      } else {
-        constexpr int CPR = R / 8;
-        const int k = s / (R / 16), q = s % (R / 16);
-        slot0 = k * CPR + ((2 * q) ^ (4 * (k & 3)));
-        slot1 = k * CPR + ((2 * q + 1) ^ (4 * (k & 3)));
-      }
-      *reinterpret_cast<bf16x8*>(st + slot0 * 16) = c0;
-      *reinterpret_cast<bf16x8*>(st + slot1 * 16) = c1;
-    }
-  }
-  __device__ __forceinline__ static bf16x8 frag(const unsigned char* st, int r0, int kk, int lane) {
-    if (KMAJ) return KTile<R, NT, KB>::frag(st, r0 + (lane & 31), kk, lane >> 5);
-    return MTile<R, NT, KB>::frag(st, r0, kk, lane);
-  }
-};
-
 __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
   const __bf16 a = static_cast<__bf16>(lo);
   const __bf16 b = static_cast<__bf16>(hi);
@@ -253,8 +183,7 @@ __device__ __forceinline__ void wait_stage(int pending) {
   else wait_vmcnt<0>();
 }
 
-template <int BM, int BN, int WM, int WN, int KB, int STAGES, bool AK, bool BKM, bool OUTF32,
-          bool BQ = false>
+template <int BM, int BN, int WM, int WN, int KB, int STAGES, bool AK, bool BKM, bool OUTF32>
 __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   static_assert(STAGES >= 2 && STAGES <= 5, "2 to 5 LDS stages");
   static_assert((STAGES - 2) * (KB / 8) * (BM + BN) / (BM / WM) / (BN / WN) / 64 <= 63,
@@ -264,8 +193,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int LBK = KB;
   using TA = Tile<BM, NT, KB, AK>;
-  using TB = std::conditional_t<BQ, QTile<BN, NT, KB, BKM>, Tile<BN, NT, KB, BKM>>;
-  static_assert(!BQ || STAGES == 2, "the int8 operand is committed one stage ahead");
+  using TB = Tile<BN, NT, KB, BKM>;
   constexpr int STAGE = TA::BYTES + TB::BYTES;
   constexpr int LOADS = TA::L + TB::L;   // direct-to-LDS loads per thread per stage
   extern __shared__ __align__(16) unsigned char lds[];
@@ -318,8 +246,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
 
   const int g = bz / p.splits, sp = bz - g * p.splits;
   const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + g * p.a_gs;
-  using BElem = std::conditional_t<BQ, int8_t, uint16_t>;
-  const BElem* B = reinterpret_cast<const BElem*>(p.B) + g * p.b_gs;
+  const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + g * p.b_gs;
   int kchunk = (p.K + p.splits - 1) / p.splits;
   kchunk = (kchunk + LBK - 1) / LBK * LBK;
   const int kbeg = sp * kchunk;
@@ -416,8 +343,6 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   const int total = t_count * nk;
   // loads run STAGES - 1 stages ahead of the multiplies
   int iss = 0, iss_kt = 0, iss_ti = 0;
-  unsigned char* qstage = nullptr;   // LDS stage the int8 operand in registers belongs to
-  (void)qstage;
   auto issue_next = [&]() {
     if (iss_kt == nk) {   // the next stage starts the next tile
       iss_kt = 0;
@@ -429,24 +354,13 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
     }
     unsigned char* st = lds + (iss % STAGES) * STAGE;
     ta.issue(st, kbeg + iss_kt * LBK, p.lda, wave);
-    if constexpr (BQ) {
-      tb.load(kbeg + iss_kt * LBK, p.ldb);   // into registers; committed to LDS later
-      qstage = st + TA::BYTES;
-    } else {
-      tb.issue(st + TA::BYTES, kbeg + iss_kt * LBK, p.ldb, wave);
-    }
+    tb.issue(st + TA::BYTES, kbeg + iss_kt * LBK, p.ldb, wave);
     ++iss;
     ++iss_kt;
   };
 #pragma unroll
   for (int i = 0; i < STAGES - 1; ++i)
     if (iss < total) issue_next();
-  if constexpr (BQ) {
-    // int8 operand of the first stage: wait for it and write it out as bf16;
-    // the barrier at the top of the loop publishes it
-    wait_vmcnt<0>();
-    tb.commit(qstage);
-  }
   int kt = 0, ti = 0;
   for (int it = 0; it < total; ++it) {
     wait_stage<LOADS, STAGES - 2>(iss - it - 1);
@@ -492,14 +406,6 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (BQ) {
-      // the next stage's int8 operand: its buffer was last read in iteration
-      // it - 1, which every wave finished before the barrier above
-      if (it + 1 < total) {
-        wait_vmcnt<0>();
-        tb.commit(qstage);
-      }
-    }
     if (++kt == nk) {   // tile complete: write it out and start the next one
       store_tile(cm0, cn0);
 #pragma unroll
@@ -526,17 +432,6 @@ __device__ __forceinline__ void gemm_lds_body(const GemmBf16& p) {
   }
 POETX_LDS_KERNEL(w0_gemm_nt_lds, true, true, false)
 POETX_LDS_KERNEL(w0_gemm_nn_lds, true, false, false)
-// frozen weight stored as int8 (B operand)
-template <int BM, int BN, int WM, int WN, int KB, int ST>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(2, 2))) void w0q_gemm_nt_lds(GemmBf16 p) {
-  gemm_lds_body<BM, BN, WM, WN, KB, ST, true, true, false, true>(p);
-}
-template <int BM, int BN, int WM, int WN, int KB, int ST>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(2, 2))) void w0q_gemm_nn_lds(GemmBf16 p) {
-  gemm_lds_body<BM, BN, WM, WN, KB, ST, true, false, false, true>(p);
-}
 POETX_LDS_KERNEL(block_gemm_nt_lds, true, true, false)
 POETX_LDS_KERNEL(block_gemm_nn_lds, true, false, false)
 POETX_LDS_KERNEL(dq_gemm_tn_lds, false, false, true)
@@ -551,18 +446,7 @@ hipError_t dispatch_lds(const GemmBf16& p, hipStream_t s) {
   // ST LDS stages of (BM + BN) x KB bf16
   const size_t lds = ST * (size_t)(BM + BN) * KB * 2;
   const int a = p.a_kmajor, b = p.b_kmajor, f = p.out_f32;
-  if (p.b_i8) {
-    if constexpr (ST != 2) {   // the int8 path is two-stage
-      return hipErrorInvalidValue;
-    } else {
-      if (p.role == GEMM_W0 && a && b && !f)
-        hipLaunchKernelGGL((w0q_gemm_nt_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
-      else if (p.role == GEMM_W0 && a && !b && !f)
-        hipLaunchKernelGGL((w0q_gemm_nn_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
-      else
-        return hipErrorInvalidValue;
-    }
-  } else if (p.role == GEMM_W0 && a && b && !f)
+  if (p.role == GEMM_W0 && a && b && !f)
     hipLaunchKernelGGL((w0_gemm_nt_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
   else if (p.role == GEMM_W0 && a && !b && !f)
     hipLaunchKernelGGL((w0_gemm_nn_lds<BM, BN, WM, WN, KB, ST>), grid, dim3(NW * 64), lds, s, p);
@@ -588,7 +472,6 @@ bool gemm_lds_supported(const GemmBf16& p, int bm, int bn) {
   if (!p.b_kmajor && p.N % bn) return false;
   if (!p.out_f32 && p.N % 8) return false;   // 16-byte epilogue stores
   if (((uintptr_t)p.A | (uintptr_t)p.B) & 15) return false;
-  if (p.b_i8 && (p.ldb % 16 || p.role != GEMM_W0 || p.out_f32)) return false;   // 16 int8 per load
   if (p.col_scale && (((uintptr_t)p.col_scale & 15) || p.c_gs % 4 || p.out_f32)) return false;
   return true;
 }

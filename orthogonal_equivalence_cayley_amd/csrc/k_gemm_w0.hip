@@ -106,7 +106,10 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-template <int KB>
+// SCALE: output column n multiplied by col_scale[n] (fp32, before the rounding
+// to bf16), for an INT8 weight's row scales when the weight comes in as its
+// exact bf16 widening
+template <int KB, bool SCALE>
 __global__ __launch_bounds__(kThr) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void w0_gemm_nt_pipe(GemmBf16 p) {
   using Op = OpTile<KB>;
@@ -204,8 +207,16 @@ void w0_gemm_nt_pipe(GemmBf16 p) {
         uint32_t w[4][2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          w[q][0] = pack2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-          w[q][1] = pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          if constexpr (SCALE) {
+            // this lane's columns n0 + wn0 + 32 j + 8 q + 4 (lane >> 5) .. + 3
+            const float4 sc = *reinterpret_cast<const float4*>(p.col_scale + n0 + wn0 + j * 32 + 8 * q +
+                                                               (upper ? 4 : 0));
+            w[q][0] = pack2(acc[i][j][4 * q] * sc.x, acc[i][j][4 * q + 1] * sc.y);
+            w[q][1] = pack2(acc[i][j][4 * q + 2] * sc.z, acc[i][j][4 * q + 3] * sc.w);
+          } else {
+            w[q][0] = pack2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            w[q][1] = pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          }
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -327,7 +338,8 @@ constexpr int kST = 2;    // LDS stages (2 x 64 KiB), fixed in the kernel
 }  // namespace
 
 bool w0_pipe_supported(const GemmBf16& p) {
-  if (p.role != GEMM_W0 || !p.a_kmajor || !p.b_kmajor || p.out_f32 || p.b_i8 || p.col_scale) return false;
+  if (p.role != GEMM_W0 || !p.a_kmajor || !p.b_kmajor || p.out_f32) return false;
+  if (((uintptr_t)p.col_scale & 15) != 0) return false;   // 16-byte scale loads
   if (p.groups != 1 || p.splits != 1) return false;
   if (p.M <= 0 || p.N <= 0 || p.M % kTile || p.N % kTile || p.K <= 0 || p.K % kKB) return false;
   if (p.lda % 8 || p.ldb % 8 || p.ldc % 8 || p.lda < p.K || p.ldb < p.K || p.ldc < p.N) return false;
@@ -341,8 +353,11 @@ hipError_t launch_w0_pipe(const GemmBf16& p, hipStream_t s) {
   if (!w0_pipe_supported(p)) return hipErrorInvalidValue;
   const long long ntile = (long long)(p.M / kTile) * (p.N / kTile);
   const size_t lds = (size_t)kST * 2 * kTile * kKB * 2;
-  hipLaunchKernelGGL((w0_gemm_nt_pipe<kKB>), dim3((unsigned)std::min<long long>(ntile, 256)), dim3(kThr),
-                     lds, s, p);
+  const dim3 grid((unsigned)std::min<long long>(ntile, 256));
+  if (p.col_scale)
+    hipLaunchKernelGGL((w0_gemm_nt_pipe<kKB, true>), grid, dim3(kThr), lds, s, p);
+  else
+    hipLaunchKernelGGL((w0_gemm_nt_pipe<kKB, false>), grid, dim3(kThr), lds, s, p);
   return hipGetLastError();
 }
 

@@ -72,6 +72,32 @@ __global__ __launch_bounds__(kThreads) void dequantize_rows_kernel(const int8_t*
     out[(long long)i * n + c] = s * static_cast<float>(q[(long long)i * n + c]);
 }
 
+// out[e] = bf16(q[e]) for n elements (exact: every int8 is a bf16), 16 per
+// thread and step with 16-byte loads where n allows it
+__global__ __launch_bounds__(kThreads) void widen_i8_kernel(const int8_t* __restrict__ q,
+                                                            uint16_t* __restrict__ out, long long n) {
+  const long long n16 = n / 16;
+  for (long long v = (long long)blockIdx.x * kThreads + threadIdx.x; v < n16;
+       v += (long long)gridDim.x * kThreads) {
+    const uint4 x = reinterpret_cast<const uint4*>(q)[v];
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t word = w[i / 2] >> (16 * (i & 1));
+      const __bf16 lo = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(word & 0xff)));
+      const __bf16 hi = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>((word >> 8) & 0xff)));
+      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(out) + 2 * v;
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+  for (long long e = n16 * 16 + (long long)blockIdx.x * kThreads + threadIdx.x; e < n;
+       e += (long long)gridDim.x * kThreads)
+    out[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(static_cast<float>(q[e])));
+}
+
 // C[t][c] = bf16(float(C[t][c]) * scale[c]) for t < rows, c < cols (row stride ld)
 __global__ __launch_bounds__(kThreads) void scale_cols_kernel(uint16_t* __restrict__ C,
                                                               const float* __restrict__ scale,
@@ -105,6 +131,17 @@ hipError_t launch_quantize_rows(const void* W0, const int32_t* pi_R, const int32
   if (n % 8 || (size_t)n * 2 > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quantize_rows_kernel, dim3(m), dim3(kThreads), (size_t)n * 2, s,
                      static_cast<const uint16_t*>(W0), pi_R, pi_P, q, scale, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_widen_i8(const void* q, void* out, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (((uintptr_t)q & 15) || ((uintptr_t)out & 15)) return hipErrorInvalidValue;
+  long long blocks = (n / 16 + kThreads - 1) / kThreads;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 256LL * 16) blocks = 256LL * 16;
+  hipLaunchKernelGGL(widen_i8_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                     static_cast<const int8_t*>(q), static_cast<uint16_t*>(out), n);
   return hipGetLastError();
 }
 

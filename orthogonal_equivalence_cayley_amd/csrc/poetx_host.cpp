@@ -167,9 +167,9 @@ long long dq_part_elems(const poetx_plan* pl, int side, long long T) {
   return n;
 }
 
-struct FwdWs { void *U, *V, *Wa, *Z, *Wf; };
+struct FwdWs { void *U, *V, *Wa, *Z, *Wf, *Wq; };
 struct BwdWs {
-  void *GZ, *GWa, *GV, *U, *GU, *Wf;
+  void *GZ, *GWa, *GV, *U, *GU, *Wf, *Wq;
   void* QT[2];   // bf16 Q^T of a side that runs the fused products (or null)
   float *dQ[2], *part;
 };
@@ -231,6 +231,7 @@ size_t layout_fwd(const poetx_plan* pl, long long T, void* base, FwdWs* w) {
   x.Wa = c.take(es * T * pl->m);
   x.Z = c.take(es * T * pl->m);
   x.Wf = fold ? c.take(es * (size_t)pl->m * pl->n) : nullptr;
+  x.Wq = wq(pl) ? c.take(2 * (size_t)pl->m * pl->n) : nullptr;
   if (w) *w = x;
   return c.off;
 }
@@ -246,6 +247,7 @@ size_t layout_bwd(const poetx_plan* pl, long long T, void* base, BwdWs* w, Chain
   x.U = c.take(es * T * pl->n);
   x.GU = c.take(es * T * pl->n);
   x.Wf = (fold_fwd(pl, T) || fold_bwd(pl, T)) ? c.take(es * (size_t)pl->m * pl->n) : nullptr;
+  x.Wq = wq(pl) ? c.take(2 * (size_t)pl->m * pl->n) : nullptr;
   for (int side = 0; side < 2; ++side)
     x.QT[side] = panel_side(pl, side) ? c.take(2 * pl->nelem[side]) : nullptr;
   x.dQ[0] = (float*)c.take(4 * pl->nelem[0]);
@@ -351,8 +353,7 @@ struct Op {
 // C(m, n) = sum_k A(m, k) B(n, k) in the plan's dtype (fp32 output when out_f32).
 poetx_status gemm(const poetx_plan* pl, int role, Op A, Op B, void* C, long long ldc, int M, int N,
                   int K, int groups, long long a_gs, long long b_gs, long long c_gs, int splits,
-                  long long c_ss, bool out_f32, hipStream_t s, const float* col_scale = nullptr,
-                  bool b_i8 = false) {
+                  long long c_ss, bool out_f32, hipStream_t s, const float* col_scale = nullptr) {
   if (pl->dtype == POETX_BF16) {
     poetx::GemmBf16 g;
     g.A = A.p; g.B = B.p; g.C = C;
@@ -366,7 +367,6 @@ poetx_status gemm(const poetx_plan* pl, int role, Op A, Op B, void* C, long long
     g.out_f32 = out_f32 ? 1 : 0;
     g.a_gs = a_gs; g.b_gs = b_gs; g.c_gs = c_gs;
     g.groups = groups; g.splits = splits; g.c_ss = c_ss;
-    g.b_i8 = b_i8 ? 1 : 0;
     g.col_scale = col_scale;
     HIP_TRY(poetx::launch_gemm_bf16(g, s));
   } else {
@@ -475,6 +475,21 @@ poetx_status exact_cayley_runs(std::vector<ExactRun>& runs, hipStream_t s) {
     }
   }
   return POETX_OK;
+}
+
+// Wa = A Wt^T for the forward form of the frozen-weight product. An INT8 weight
+// (POET-XQ) is first widened exactly to bf16 into Wq (one pass over m n bytes),
+// so the product runs on the bf16 kernels with the row scales of Wt applied to
+// Wa's columns in its epilogue: Wa = (A q^T) diag(s), exact int8 values and an
+// fp32 scale of each column's accumulator before the rounding to bf16.
+poetx_status w0_forward_product(const poetx_plan* pl, Op A, const void* Wt, void* Wq, void* Wa,
+                                long long T, hipStream_t s) {
+  if (!wq(pl))
+    return gemm(pl, poetx::GEMM_W0, A, Op{Wt, pl->n, 1}, Wa, pl->m, (int)T, pl->m, pl->n, 1, 0, 0, 0, 1, 0,
+                false, s);
+  HIP_TRY(poetx::launch_widen_i8(Wt, Wq, (long long)pl->m * pl->n, s));
+  return gemm(pl, poetx::GEMM_W0, A, Op{Wq, pl->n, 1}, Wa, pl->m, (int)T, pl->m, pl->n, 1, 0, 0, 0, 1, 0,
+              false, s, qscale(pl, Wt));
 }
 
 // Row-form product with one side's blocks: out[:, blk] = in[:, blk] Q^T
@@ -760,9 +775,7 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
     }
     StageScope sc(POETX_STAGE_W0_FWD, s);
     const Op a = fold ? Op{U, pl->n, 1} : Op{w.GU, pl->n, 1};
-    const Op b = fold ? Op{w.Wf, pl->n, 1} : Op{Wt, pl->n, 1};
-    return gemm(pl, poetx::GEMM_W0, a, b, w.GWa, pl->m, (int)T, pl->m, pl->n, 1, 0, 0, 0, 1, 0, false, s,
-                wq(pl) ? qscale(pl, Wt) : nullptr, wq(pl));
+    return w0_forward_product(pl, a, fold ? w.Wf : Wt, w.Wq, w.GWa, T, s);
   };
   const void* Wa = Wa_saved ? Wa_saved : w.GWa;
   if (!Wa_saved && !fused_r && (st = recompute_wa()) != POETX_OK) return st;
@@ -798,12 +811,15 @@ poetx_status backward_dq(const poetx_plan* pl, long long T, const void* X, const
     const Op a = foldb ? Op{w.GZ, pl->m, 1} : Op{w.GWa, pl->m, 1};
     // B(j, i) = (D_R Wt)[i][j]: WfT[j][i] (K-contiguous) or Wf[i][j]; unfolded
     // B(j, i) = Wt[i][j], read K-contiguous from the kept transpose WtT[j][i]
-    // (qT[j][i] for an INT8 weight)
+    // (qT[j][i] for an INT8 weight, widened exactly to bf16 first; its row
+    // scales are already in G_Wa)
+    if (wq(pl))
+      HIP_TRY(poetx::launch_widen_i8(wqpair(pl) ? qt(pl, Wt) : Wt, w.Wq, (long long)pl->m * pl->n, s));
     const Op b = foldt ? Op{w.Wf, pl->m, 1} : foldb ? Op{w.Wf, 1, pl->n}
                  : wpair(pl) ? Op{wtt(pl, Wt), pl->m, 1}
-                 : wqpair(pl) ? Op{qt(pl, Wt), pl->m, 1} : Op{Wt, 1, pl->n};
+                 : wqpair(pl) ? Op{w.Wq, pl->m, 1} : wq(pl) ? Op{w.Wq, 1, pl->n} : Op{Wt, 1, pl->n};
     if ((st = gemm(pl, poetx::GEMM_W0, a, b, w.GV, pl->n, (int)T, pl->n, pl->m, 1, 0, 0, 0, 1, 0, false,
-                   s, nullptr, wq(pl))) != POETX_OK)
+                   s)) != POETX_OK)
       return st;
   }
   if (!dq_r_now) {
@@ -1414,10 +1430,7 @@ poetx_status poetx_forward(const poetx_plan* pl, int64_t T, const void* X, const
   {
     StageScope sc(POETX_STAGE_W0_FWD, s);
     const Op a = fold ? Op{w.U, pl->n, 1} : Op{w.V, pl->n, 1};
-    const Op b = fold ? Op{w.Wf, pl->n, 1} : Op{Wt, pl->n, 1};
-    if ((st = gemm(pl, poetx::GEMM_W0, a, b, Wa, pl->m, (int)T, pl->m, pl->n, 1, 0, 0, 0, 1, 0, false,
-                   s, wq(pl) ? qscale(pl, Wt) : nullptr, wq(pl))) != POETX_OK)
-      return st;
+    if ((st = w0_forward_product(pl, a, fold ? w.Wf : Wt, w.Wq, Wa, T, s)) != POETX_OK) return st;
   }
   // 4 + 5 fused: Z = Wa D_R^T scattered to Y in one pass over the rows
   if (panel_side(pl, POETX_SIDE_R)) {

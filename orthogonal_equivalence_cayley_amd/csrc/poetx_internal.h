@@ -76,6 +76,8 @@ hipError_t launch_quantize_rows(const void* W0, const int32_t* pi_R, const int32
 hipError_t launch_scale_cols(void* C, const float* scale, long long rows, int cols, long long ld,
                              hipStream_t s);
 // out[i][j] = scale[i] * q[i][j] (fp32)
+// out = bf16(q) elementwise (exact), n int8 values; 16-byte aligned buffers
+hipError_t launch_widen_i8(const void* q, void* out, long long n, hipStream_t s);
 hipError_t launch_dequantize_rows(const int8_t* q, const float* scale, float* out, int m, int n,
                                   hipStream_t s);
 // inv[pi[i]] = i for a permutation pi of 0..n-1
@@ -138,9 +140,6 @@ struct GemmBf16 {
   int groups, splits;
   long long c_ss;
   int tpw;    // output tiles per workgroup (set by the launcher)
-  // B holds int8 values (converted exactly to bf16 on the way into LDS); only
-  // for GEMM_W0 on whole 256 x 256 (or 128 x 128) tiles
-  int b_i8 = 0;
   // bf16 output only: column n of group g is multiplied by col_scale[g * c_gs + n]
   // (fp32, before the rounding) when non-null
   const float* col_scale = nullptr;
