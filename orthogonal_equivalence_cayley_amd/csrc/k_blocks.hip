@@ -41,8 +41,11 @@ __global__ __launch_bounds__(kThreads) void unpack_skew_kernel(
   }
 }
 
-// Newton-Schulz start for N = (I - S)^{-1}: with c = max_i sum_j |S[i][j]| (an
-// upper bound of ||S||_2), X0 = a (I + S) = a (I - S)^T with a = 2 / (2 + c^2).
+// Newton-Schulz start for N = (I - S)^{-1}: with c an upper bound of ||S||_2,
+// the smaller of max_i sum_j |S[i][j]| and, when S2 = S S is given, the square
+// root of max_i sum_j |S2[i][j]| (S2 is symmetric and ||S2||_2 = ||S||_2^2, so
+// its largest row sum bounds ||S||_2^2; for generators of many small entries it
+// is the much tighter bound), X0 = a (I + S) = a (I - S)^T with a = 2 / (2 + c^2).
 // The residual R = I - (I - S) X0 is symmetric with eigenvalues 1 - a (1 + s^2)
 // for the singular values s <= c of S, so ||R||_2 <= r = c^2 / (2 + c^2) < 1,
 // and after j steps X <- X (2I - (I - S) X) it is R^(2^j). iters[block] = the
@@ -53,18 +56,12 @@ __global__ __launch_bounds__(kThreads) void unpack_skew_kernel(
 // them; the block is read from L2 by all but the first), then writes its share
 // of the rows of X0; the first also writes iters.
 constexpr int kNsParts = 8;
-__global__ __launch_bounds__(kThreads) void ns_init_kernel(const float* __restrict__ S, int b,
-                                                           float* __restrict__ X0,
-                                                           int32_t* __restrict__ iters, int jmax) {
-  __shared__ float red[kThreads];
-  const int blk = blockIdx.x / kNsParts, part = blockIdx.x - blk * kNsParts;
-  const long long bb = (long long)b * b;
-  const float* Sg = S + blk * bb;
-  float* Xg = X0 + blk * bb;
+// largest row sum of |M| over the b x b block M (every thread of the workgroup)
+__device__ float max_abs_row_sum(const float* __restrict__ M, int b, float* red) {
   const bool vec = (b % 4) == 0;   // then every row starts on a 16-byte boundary
   float mx = 0.0f;
   for (int r = threadIdx.x; r < b; r += kThreads) {
-    const float* row = Sg + (long long)r * b;
+    const float* row = M + (long long)r * b;
     float sum = 0.0f;
     if (vec) {
       for (int c = 0; c < b; c += 4) {
@@ -85,7 +82,21 @@ __global__ __launch_bounds__(kThreads) void ns_init_kernel(const float* __restri
     if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
     __syncthreads();
   }
-  const double c = red[0];
+  const float m = red[0];
+  __syncthreads();   // red is reused by the next call
+  return m;
+}
+__global__ __launch_bounds__(kThreads) void ns_init_kernel(const float* __restrict__ S,
+                                                           const float* __restrict__ S2, int b,
+                                                           float* __restrict__ X0,
+                                                           int32_t* __restrict__ iters, int jmax) {
+  __shared__ float red[kThreads];
+  const int blk = blockIdx.x / kNsParts, part = blockIdx.x - blk * kNsParts;
+  const long long bb = (long long)b * b;
+  const float* Sg = S + blk * bb;
+  float* Xg = X0 + blk * bb;
+  double c = max_abs_row_sum(Sg, b, red);
+  if (S2) c = fmin(c, sqrt((double)max_abs_row_sum(S2 + blk * bb, b, red)));
   const float a = (float)(2.0 / (2.0 + c * c));
   const int r0 = (int)((long long)b * part / kNsParts), r1 = (int)((long long)b * (part + 1) / kNsParts);
   for (long long e = (long long)r0 * b + threadIdx.x; e < (long long)r1 * b; e += kThreads) {
@@ -239,10 +250,11 @@ hipError_t launch_unpack_skew(const float* theta, const Seg& g, float* S, float*
   return hipGetLastError();
 }
 
-hipError_t launch_ns_init(const float* S, int b, int count, float* X0, int32_t* iters, int jmax,
-                          hipStream_t s) {
+hipError_t launch_ns_init(const float* S, const float* S2, int b, int count, float* X0, int32_t* iters,
+                          int jmax, hipStream_t s) {
   if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ns_init_kernel, dim3(count * kNsParts), dim3(kThreads), 0, s, S, b, X0, iters, jmax);
+  hipLaunchKernelGGL(ns_init_kernel, dim3(count * kNsParts), dim3(kThreads), 0, s, S, S2, b, X0, iters,
+                     jmax);
   return hipGetLastError();
 }
 

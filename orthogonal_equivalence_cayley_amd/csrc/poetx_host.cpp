@@ -450,10 +450,18 @@ poetx_status exact_cayley_runs(std::vector<ExactRun>& runs, hipStream_t s) {
       ExactRun& r = *rs[i];
       // the unpack takes base pointers and applies the segment offset
       HIP_TRY(poetx::launch_unpack_skew(r.theta, r.g, r.S - r.g.q_off, nullptr, 0.0f, s));
-      HIP_TRY(poetx::launch_ns_init(r.S, b, r.g.count, r.X0, r.iters, kNsMaxSteps, s));
     }
+    // S^2 (in P1, free until the iterations) for the tighter bound of ||S||_2:
+    // at generators of many small entries it asks for fewer steps than the row
+    // sums of S alone, for one product
     std::vector<poetx::GemmF32Run> v(n);
+    for (size_t i = 0; i < n; ++i) v[i] = poetx::GemmF32Run{rs[i]->S, rs[i]->S, rs[i]->P1, nullptr, rs[i]->g.count};
     poetx_status st;
+    if ((st = f32_runs(b, b, 1, 1, b, v, 0.0f, s)) != POETX_OK) return st;
+    for (size_t i = 0; i < n; ++i) {
+      ExactRun& r = *rs[i];
+      HIP_TRY(poetx::launch_ns_init(r.S, r.P1, b, r.g.count, r.X0, r.iters, kNsMaxSteps, s));
+    }
     for (int it = 0; it < kNsMaxSteps; ++it) {
       // Y = 2I - (I - S) X = S X - X + 2I (in P1), then X' = X Y
       for (size_t i = 0; i < n; ++i) {

@@ -44,10 +44,12 @@ hipError_t launch_transpose_blocks(const void* Q, void* QT, int count, hipStream
 hipError_t launch_unpack_skew(const float* theta, const Seg& g, float* S, float* Q, float c1,
                               hipStream_t s);
 // Newton-Schulz inverse of I - S for count b x b blocks: X0 = a (I + S) with
-// a = 2 / (2 + c^2), c = max row sum of |S| (>= ||S||_2); iters[g] = steps
-// X <- X (2I - (I - S) X) block g needs for a residual below 2^-30 (<= jmax).
-hipError_t launch_ns_init(const float* S, int b, int count, float* X0, int32_t* iters, int jmax,
-                          hipStream_t s);
+// a = 2 / (2 + c^2), c = the smaller of the max row sum of |S| and the square
+// root of the max row sum of |S2| (S2 = S S, or null: both bound ||S||_2);
+// iters[g] = steps X <- X (2I - (I - S) X) block g needs for a residual below
+// 2^-30 (<= jmax).
+hipError_t launch_ns_init(const float* S, const float* S2, int b, int count, float* X0, int32_t* iters,
+                          int jmax, hipStream_t s);
 // N = the iterate of block g (X0 if iters[g] is even, else X1); Q = 2 N - I.
 hipError_t launch_ns_final(const float* X0, const float* X1, const int32_t* iters, int b, int count,
                            float* N, float* Q, hipStream_t s);
